@@ -1,0 +1,220 @@
+"""Seeded synthetic inputs for the MoE FFN layer.
+
+This module only draws random numbers and lays them out; it holds none of
+the layer's arithmetic.  Both the HIP path and the float64 oracle receive
+exactly the arrays made here.
+
+Recipe (per tensor an independent stream):
+  * Small tensors -- x, token ids, RMSNorm weight, router, selection bias,
+    hash table, and every expert of the tiny layer -- come from numpy
+    ``Generator(Philox(key=[seed, tensor_id << 32 | index]))`` on the host,
+    so any process regenerates them bit for bit.
+  * Full-size expert weights (256 experts x 3 matrices of 2048 x 4096, 12 GiB
+    in bf16) come from torch's Philox generator on the target device, one
+    ``manual_seed`` per (tensor, expert); the oracle receives host copies of
+    the experts it needs.
+  * Normal samples are drawn in float32, scaled by the stated standard
+    deviation and rounded to bf16 with round-to-nearest-even.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+LAYER_SCORE = 0
+LAYER_HASH = 1
+
+# tensor ids of the per-tensor streams
+_T_X, _T_TOK, _T_NORM, _T_ROUTER, _T_BIAS, _T_TABLE, _T_HOT = 1, 2, 3, 4, 5, 6, 7
+_T_GATE, _T_UP, _T_DOWN, _T_SGATE, _T_SUP, _T_SDOWN = 10, 11, 12, 13, 14, 15
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    rows: int
+    hidden: int
+    experts: int
+    top_k: int
+    inter: int
+    layer_kind: int
+    router_std: float
+    table_rows: int = 0          # hash table rows (token-id range)
+    hot_experts: int = 0         # experts whose bias is exactly +hot_bias
+    hot_bias: float = 2.0
+    weight_std: float = 0.02
+    bias_std: float = 0.1
+    norm_std: float = 0.05
+    eps: float = 1e-6
+    seed: int = 1000
+
+    @property
+    def routed_slots(self) -> int:
+        return self.rows * self.top_k
+
+
+def _cfg(i, **kw):
+    return Config(seed=1000 + i, **kw)
+
+
+# The five workloads: tiny CPU-seconds layer; full-size decode (score route);
+# the B=4 decode cohort on a hash layer; 512-row prefill; 8192-row prefill
+# with 16 hot experts.
+CONFIGS = [
+    _cfg(0, name="tiny-h512-e32-r8-score", rows=8, hidden=512, experts=32, top_k=6,
+         inter=256, layer_kind=LAYER_SCORE, router_std=1.0 / np.sqrt(512.0), table_rows=1024),
+    _cfg(1, name="decode-r1-score", rows=1, hidden=4096, experts=256, top_k=6, inter=2048,
+         layer_kind=LAYER_SCORE, router_std=1.0 / 64.0),
+    _cfg(2, name="decode-cohort-r4-hash", rows=4, hidden=4096, experts=256, top_k=6,
+         inter=2048, layer_kind=LAYER_HASH, router_std=1.0 / 64.0, table_rows=131072),
+    _cfg(3, name="prefill-r512-score", rows=512, hidden=4096, experts=256, top_k=6,
+         inter=2048, layer_kind=LAYER_SCORE, router_std=1.0 / 64.0, table_rows=131072),
+    _cfg(4, name="prefill-r8192-score-skewed", rows=8192, hidden=4096, experts=256, top_k=6,
+         inter=2048, layer_kind=LAYER_SCORE, router_std=1.0 / 64.0, table_rows=131072,
+         hot_experts=16),
+]
+
+
+def config(i_or_name) -> Config:
+    if isinstance(i_or_name, int):
+        return CONFIGS[i_or_name]
+    for c in CONFIGS:
+        if c.name == i_or_name:
+            return c
+    raise KeyError(i_or_name)
+
+
+def _rng(seed: int, tensor: int, index: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.Philox(key=[int(seed), (int(tensor) << 32) | int(index)]))
+
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round float32 to bf16 (round to nearest, ties to even); uint16 bits."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def _normal_bf16(seed, tensor, index, shape, std) -> np.ndarray:
+    a = _rng(seed, tensor, index).standard_normal(shape, dtype=np.float32)
+    a *= np.float32(std)
+    return f32_to_bf16_bits(a)
+
+
+@dataclasses.dataclass
+class HostInputs:
+    """Everything but the full-size expert weights, as numpy arrays."""
+    x: np.ndarray            # f32 [rows, hidden]
+    token_ids: np.ndarray    # i32 [rows]
+    norm_w: np.ndarray       # f32 [hidden]
+    router: np.ndarray       # bf16 bits [experts, hidden]
+    sel_bias: np.ndarray     # f32 [experts]
+    tid2eid: np.ndarray | None  # i32 [table_rows, top_k]
+    hot: np.ndarray          # i32 [hot_experts]
+
+
+def host_inputs(cfg: Config, layer: int = 0, rows: int | None = None) -> HostInputs:
+    """Activations, token ids and the small per-layer parameters.
+
+    ``layer`` selects an independent set of layer parameters (router, bias,
+    norm weight, table) while x and token ids stay the same.
+    """
+    s = cfg.seed
+    ls = s + 7919 * layer
+    R = cfg.rows if rows is None else rows
+    x = _rng(s, _T_X).standard_normal((R, cfg.hidden), dtype=np.float32)
+    tok = _rng(s, _T_TOK).integers(0, max(cfg.table_rows, 1), size=R, dtype=np.int64).astype(np.int32)
+    norm_w = (1.0 + cfg.norm_std * _rng(ls, _T_NORM).standard_normal(cfg.hidden, dtype=np.float32)).astype(np.float32)
+    router = _normal_bf16(ls, _T_ROUTER, 0, (cfg.experts, cfg.hidden), cfg.router_std)
+    bias = (cfg.bias_std * _rng(ls, _T_BIAS).standard_normal(cfg.experts, dtype=np.float32)).astype(np.float32)
+    hot = np.zeros(0, dtype=np.int32)
+    if cfg.hot_experts:
+        hot = np.sort(_rng(ls, _T_HOT).choice(cfg.experts, cfg.hot_experts, replace=False)).astype(np.int32)
+        bias[hot] = np.float32(cfg.hot_bias)
+    table = None
+    if cfg.table_rows:
+        table = distinct_table(ls, cfg.table_rows, cfg.experts, cfg.top_k)
+    return HostInputs(x=x, token_ids=tok, norm_w=norm_w, router=router, sel_bias=bias,
+                      tid2eid=table, hot=hot)
+
+
+def distinct_table(seed: int, table_rows: int, experts: int, top_k: int) -> np.ndarray:
+    """``table_rows`` rows of ``top_k`` distinct experts in random order."""
+    out = np.empty((table_rows, top_k), dtype=np.int32)
+    rng = _rng(seed, _T_TABLE)
+    chunk = 8192
+    for r0 in range(0, table_rows, chunk):
+        n = min(chunk, table_rows - r0)
+        keys = rng.random((n, experts), dtype=np.float32)
+        part = np.argpartition(keys, top_k - 1, axis=1)[:, :top_k]
+        order = np.argsort(np.take_along_axis(keys, part, axis=1), axis=1, kind="stable")
+        out[r0:r0 + n] = np.take_along_axis(part, order, axis=1)
+    return out
+
+
+def expert_host(cfg: Config, e: int, layer: int = 0):
+    """bf16 bits ``(gate [I,H], up [I,H], down [H,I])`` of routed expert e,
+    drawn on the host (used for the tiny layer)."""
+    ls = cfg.seed + 7919 * layer
+    I, H = cfg.inter, cfg.hidden
+    return (_normal_bf16(ls, _T_GATE, e, (I, H), cfg.weight_std),
+            _normal_bf16(ls, _T_UP, e, (I, H), cfg.weight_std),
+            _normal_bf16(ls, _T_DOWN, e, (H, I), cfg.weight_std))
+
+
+def shared_host(cfg: Config, layer: int = 0):
+    ls = cfg.seed + 7919 * layer
+    I, H = cfg.inter, cfg.hidden
+    return (_normal_bf16(ls, _T_SGATE, 0, (I, H), cfg.weight_std),
+            _normal_bf16(ls, _T_SUP, 0, (I, H), cfg.weight_std),
+            _normal_bf16(ls, _T_SDOWN, 0, (H, I), cfg.weight_std))
+
+
+def all_experts_host(cfg: Config, layer: int = 0):
+    """Stacked host arrays ``(gate [E,I,H], up [E,I,H], down [E,H,I])``."""
+    trip = [expert_host(cfg, e, layer) for e in range(cfg.experts)]
+    return tuple(np.stack([t[j] for t in trip]) for j in range(3))
+
+
+def expert_weights_device(cfg: Config, device, layer: int = 0):
+    """Full-size expert weights drawn directly on ``device`` with torch.
+
+    Returns bf16 tensors ``gate [E,I,H], up [E,I,H], down [E,H,I]`` and the
+    shared triple ``[I,H], [I,H], [H,I]``.  One generator seed per (tensor,
+    expert) keeps every expert reproducible on its own.
+    """
+    import torch
+
+    ls = cfg.seed + 7919 * layer
+    I, H, E = cfg.inter, cfg.hidden, cfg.experts
+    gen = torch.Generator(device=device)
+
+    def fill(dst, tensor_id, e):
+        gen.manual_seed((ls * 1_000_003 + tensor_id * 65_537 + e) & 0x7FFF_FFFF_FFFF_FFFF)
+        tmp = torch.randn(dst.shape, generator=gen, device=device, dtype=torch.float32)
+        tmp.mul_(cfg.weight_std)
+        dst.copy_(tmp.to(torch.bfloat16))
+
+    gate = torch.empty((E, I, H), dtype=torch.bfloat16, device=device)
+    up = torch.empty((E, I, H), dtype=torch.bfloat16, device=device)
+    down = torch.empty((E, H, I), dtype=torch.bfloat16, device=device)
+    for e in range(E):
+        fill(gate[e], _T_GATE, e)
+        fill(up[e], _T_UP, e)
+        fill(down[e], _T_DOWN, e)
+    sg = torch.empty((I, H), dtype=torch.bfloat16, device=device)
+    su = torch.empty((I, H), dtype=torch.bfloat16, device=device)
+    sd = torch.empty((H, I), dtype=torch.bfloat16, device=device)
+    fill(sg, _T_SGATE, 0)
+    fill(su, _T_SUP, 0)
+    fill(sd, _T_SDOWN, 0)
+    return (gate, up, down), (sg, su, sd)
+
+
+def bf16_tensor_bits(t) -> np.ndarray:
+    """Host uint16 copy of a bf16 torch tensor's bits."""
+    import torch
+
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

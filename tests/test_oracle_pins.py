@@ -1,0 +1,399 @@
+"""Pins of the float64 oracle against facts fixed outside the oracle itself:
+a hand-worked example, closed forms, brute force on tiny inputs, invariants
+and textbook routines.  CPU only.
+
+Each ``check_*`` raises AssertionError on failure; the tests call them, and
+``test_pins_catch_planted_mistakes`` plants plausible mistakes in the oracle
+(on the CPU) to show that at least one check fails for each.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from mixture_experts_ffn_rmsnorm_amd import inputs as gen
+from oracle import moe_ref as ref
+from tests.oracle_fixtures import micro_weights, read_golden, tiny_weights, weights_from_arrays
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- checks ---
+def check_bf16_widening():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x3E80, 0x0001, 0x7F7F, 0x4049], dtype=np.uint16)
+    want = [1.0, -2.0, 0.0, -0.0, 0.25, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127, 3.140625]
+    got = ref.bf16_to_f64(bits)
+    assert got.dtype == np.float64
+    assert list(got) == want
+
+
+def check_matmul_triple_loop():
+    rng = np.random.default_rng(7)
+    R, H, I, E = 3, 5, 4, 6
+    xn = rng.standard_normal((R, H))
+    Wr = gen.f32_to_bf16_bits(rng.standard_normal((E, H)).astype(np.float32))
+    Wg = gen.f32_to_bf16_bits(rng.standard_normal((I, H)).astype(np.float32))
+    Wu = gen.f32_to_bf16_bits(rng.standard_normal((I, H)).astype(np.float32))
+    Wd = gen.f32_to_bf16_bits(rng.standard_normal((H, I)).astype(np.float32))
+    f = lambda b: [[float(np.float32(np.uint32(int(v) << 16).view(np.float32))) for v in row] for row in b]
+    wr, wg, wu, wd = f(Wr), f(Wg), f(Wu), f(Wd)
+    logits = ref.router_logits(xn, Wr)
+    h, d = ref.expert_ffn(xn, Wg, Wu, Wd)
+    for r in range(R):
+        for e in range(E):
+            s = sum(xn[r, j] * wr[e][j] for j in range(H))
+            assert math.isclose(logits[r, e], s, rel_tol=1e-13, abs_tol=1e-13)
+        hh = []
+        for i in range(I):
+            g = sum(wg[i][j] * xn[r, j] for j in range(H))
+            u = sum(wu[i][j] * xn[r, j] for j in range(H))
+            hh.append(g / (1.0 + math.exp(-g)) * u)
+            assert math.isclose(h[r, i], hh[i], rel_tol=1e-12, abs_tol=1e-13)
+        for j in range(H):
+            s = sum(wd[j][i] * hh[i] for i in range(I))
+            assert math.isclose(d[r, j], s, rel_tol=1e-12, abs_tol=1e-13)
+
+
+def check_micro_example():
+    g = read_golden("micro_h2.txt")
+    inp, exp = g["inputs"], g["expected"]
+    W = micro_weights(g)
+    x = inp["x"].reshape(2, 2)
+    res = ref.forward(x, None, ref.LAYER_SCORE, W, top_k=int(inp["top_k"][0]), eps=float(inp["eps"][0]))
+    np.testing.assert_array_equal(res["xn"].ravel(), exp["xn"])
+    np.testing.assert_array_equal(res["logits"].ravel(), exp["logits"])
+    np.testing.assert_array_equal(res["idx"].ravel(), exp["idx"].astype(np.int32))
+    np.testing.assert_allclose(res["w"].ravel(), exp["w"], rtol=2e-16, atol=0)
+    np.testing.assert_allclose(res["out"].ravel(), exp["out"], rtol=4e-16, atol=4e-16)
+
+
+def _rank_select(key, K):
+    """Brute-force definition: e is chosen iff fewer than K experts beat it,
+    where j beats e if key_j > key_e or (key_j == key_e and j < e)."""
+    E = len(key)
+    chosen = []
+    for e in range(E):
+        beats = sum(1 for j in range(E) if key[j] > key[e] or (key[j] == key[e] and j < e))
+        if beats < K:
+            chosen.append((beats, e))
+    return [e for _, e in sorted(chosen)]
+
+
+def check_topk_rank_definition():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        E = int(rng.integers(6, 40))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        logits = rng.standard_normal(E) * 2
+        bias = rng.standard_normal(E) * 0.1
+        if trial % 3 == 0:  # engineered exact ties in logits and bias
+            logits = np.round(logits)
+            bias = np.round(bias * 4) / 4
+        idx, w, _ = ref.score_route(logits[None], bias.astype(np.float32), K)
+        sig = 1.0 / (1.0 + np.exp(-logits))
+        key = sig + bias.astype(np.float32).astype(np.float64)
+        assert list(idx[0]) == _rank_select(list(key), K)
+
+
+def check_topk_subset_enumeration():
+    rng = np.random.default_rng(12)
+    for trial in range(60):
+        E = int(rng.integers(6, 11))
+        K = int(rng.integers(1, 7))
+        logits = np.round(rng.standard_normal(E) * 2) if trial % 2 else rng.standard_normal(E)
+        bias = np.zeros(E, dtype=np.float32) if trial % 4 == 1 else (0.1 * rng.standard_normal(E)).astype(np.float32)
+        key = 1.0 / (1.0 + np.exp(-logits)) + bias.astype(np.float64)
+        # the chosen set is the unique K-subset that no outside expert beats
+        good = []
+        for S in itertools.combinations(range(E), K):
+            out = [j for j in range(E) if j not in S]
+            if all(key[e] > key[j] or (key[e] == key[j] and e < j) for e in S for j in out):
+                good.append(set(S))
+        assert len(good) == 1
+        idx, _, _ = ref.score_route(logits[None], bias, K)
+        assert set(idx[0].tolist()) == good[0]
+        # within the set: key descending, equal keys by index
+        ks = [key[e] for e in idx[0]]
+        assert all(ks[i] > ks[i + 1] or (ks[i] == ks[i + 1] and idx[0][i] < idx[0][i + 1]) for i in range(K - 1))
+
+
+def check_engineered_ties():
+    E, K = 32, 6
+    idx, w, _ = ref.score_route(np.zeros((1, E)), np.zeros(E, np.float32), K)
+    assert idx[0].tolist() == [0, 1, 2, 3, 4, 5]
+    assert np.all(w == 1.0 / 6.0)
+    b = np.zeros(E, np.float32)
+    b[[30, 7, 19]] = 0.5
+    idx, _, _ = ref.score_route(np.zeros((1, E)), b, K)
+    assert idx[0].tolist() == [7, 19, 30, 0, 1, 2]
+
+
+def check_weights_sum_to_one():
+    hi, W, _ = tiny_weights()
+    cfg = gen.config(0)
+    xn = ref.rms_norm(hi.x, hi.norm_w, cfg.eps)
+    lg = ref.router_logits(xn, hi.router)
+    _, w, _ = ref.score_route(lg, hi.sel_bias, cfg.top_k)
+    assert np.max(np.abs(w.sum(1) - 1)) <= 1e-12
+    assert np.all(w > 0)
+    tok = np.array([3, 5, 1000, 7, 0, 1023, 2, 9], np.int32)
+    table = hi.tid2eid.copy()
+    table[5, 2] = 99  # an invalid entry: that slot is dropped, the rest renormalised
+    _, w, valid = ref.hash_route(lg, tok, table, cfg.top_k)
+    assert np.max(np.abs(w.sum(1) - 1)) <= 1e-12
+    assert (w[valid] > 0).all() and (w[~valid] == 0).all()
+
+
+def check_hash_equals_score():
+    hi, W, _ = tiny_weights()
+    cfg = gen.config(0)
+    res_s = ref.forward(hi.x, None, ref.LAYER_SCORE, W, cfg.top_k, cfg.eps)
+    tok = np.arange(cfg.rows, dtype=np.int32) * 37 + 5
+    table = np.full((1024, cfg.top_k), 0, np.int32)
+    table[tok] = res_s["idx"]
+    Wh = ref.Weights(W.norm_w, W.router, None, table, W.expert, W.shared)
+    res_h = ref.forward(hi.x, tok, ref.LAYER_HASH, Wh, cfg.top_k, cfg.eps)
+    np.testing.assert_array_equal(res_h["idx"], res_s["idx"])
+    np.testing.assert_array_equal(res_h["w"], res_s["w"])
+    np.testing.assert_array_equal(res_h["out"], res_s["out"])
+
+
+def check_zero_input_closed_form():
+    hi, W, _ = tiny_weights()
+    cfg = gen.config(0)
+    x = np.zeros((3, cfg.hidden), np.float32)
+    res = ref.forward(x, None, ref.LAYER_SCORE, W, cfg.top_k, cfg.eps)
+    assert np.all(res["xn"] == 0) and np.all(res["logits"] == 0)
+    want = np.argsort(-hi.sel_bias.astype(np.float64), kind="stable")[:cfg.top_k]
+    assert all(res["idx"][r].tolist() == want.tolist() for r in range(3))
+    assert np.all(res["w"] == 1.0 / cfg.top_k)
+    assert np.all(res["out"] == 0.0)
+
+
+def check_rmsnorm_identities():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((5, 64)) * rng.uniform(0.01, 100, (5, 1))
+    g = 1 + 0.05 * rng.standard_normal(64)
+    for eps in (0.0, 1e-6, 0.5):
+        xn = ref.rms_norm(x, g, eps)
+        ms = np.mean(x * x, axis=1)
+        np.testing.assert_allclose(np.mean((xn / g) ** 2, axis=1), ms / (ms + eps), rtol=1e-12)
+    # constant vector: x = c  ->  xn = c / sqrt(c^2 + eps) * g
+    c = 3.0
+    np.testing.assert_allclose(ref.rms_norm(np.full((1, 8), c), g[:8], 1e-6)[0], c / math.sqrt(c * c + 1e-6) * g[:8],
+                               rtol=1e-15)
+
+
+def check_scale_invariance():
+    hi, W, _ = tiny_weights()
+    cfg = gen.config(0)
+    base = ref.forward(hi.x, None, ref.LAYER_SCORE, W, cfg.top_k, cfg.eps)
+    for c in (0.5, 3.0, 40.0):
+        res = ref.forward(hi.x * c, None, ref.LAYER_SCORE, W, cfg.top_k, cfg.eps)
+        np.testing.assert_array_equal(res["idx"], base["idx"])
+        np.testing.assert_allclose(res["out"], base["out"], rtol=1e-5, atol=1e-5 * np.abs(base["out"]).max())
+
+
+def check_row_independence():
+    hi, W, _ = tiny_weights()
+    cfg = gen.config(0)
+    full = ref.forward(hi.x, None, ref.LAYER_SCORE, W, cfg.top_k, cfg.eps)
+    for r in (0, 3, 7):
+        one = ref.forward(hi.x[r:r + 1], None, ref.LAYER_SCORE, W, cfg.top_k, cfg.eps)
+        # BLAS may block a 1-row product differently from an 8-row one, so
+        # equality holds to rounding, not bitwise
+        np.testing.assert_allclose(one["out"][0], full["out"][r], rtol=0, atol=1e-13 * np.abs(full["out"][r]).max())
+        np.testing.assert_array_equal(one["idx"][0], full["idx"][r])
+
+
+def check_expert_relabelling():
+    hi, W, (G, U, D) = tiny_weights()
+    cfg = gen.config(0)
+    base = ref.forward(hi.x, None, ref.LAYER_SCORE, W, cfg.top_k, cfg.eps)
+    perm = np.random.default_rng(14).permutation(cfg.experts)   # new id of old expert e is perm[e]
+    inv = np.argsort(perm)
+    Wp = weights_from_arrays(hi.norm_w, hi.router[inv], hi.sel_bias[inv], None, G[inv], U[inv], D[inv], W.shared)
+    res = ref.forward(hi.x, None, ref.LAYER_SCORE, Wp, cfg.top_k, cfg.eps)
+    np.testing.assert_array_equal(res["idx"], perm[base["idx"]])
+    np.testing.assert_allclose(res["out"], base["out"], rtol=1e-13, atol=1e-13)
+
+
+def check_identical_experts():
+    hi, W, (G, U, D) = tiny_weights()
+    cfg = gen.config(0)
+    E = cfg.experts
+    Wi = weights_from_arrays(hi.norm_w, hi.router, hi.sel_bias, None, np.repeat(G[:1], E, 0),
+                             np.repeat(U[:1], E, 0), np.repeat(D[:1], E, 0), W.shared)
+    res = ref.forward(hi.x, None, ref.LAYER_SCORE, Wi, cfg.top_k, cfg.eps)
+    xn = ref.rms_norm(hi.x, hi.norm_w, cfg.eps)
+    _, d0 = ref.expert_ffn(xn, G[0], U[0], D[0])
+    _, ds = ref.expert_ffn(xn, *W.shared)
+    np.testing.assert_allclose(res["out"], d0 + ds, rtol=1e-12, atol=1e-13)
+
+
+def check_invalid_masking():
+    hi, W, _ = tiny_weights()
+    cfg = gen.config(0)
+    tok = np.array([1, -5, 1024, 3, 4, 5, 6, 7], np.int32)  # rows 1, 2: ids out of range
+    table = hi.tid2eid.copy()
+    table[3, 0] = cfg.experts          # row 3: one bad entry
+    table[4, :] = -1                   # row 4: every entry bad
+    Wh = ref.Weights(W.norm_w, W.router, None, table, W.expert, W.shared)
+    res = ref.forward(hi.x, tok, ref.LAYER_HASH, Wh, cfg.top_k, cfg.eps)
+    xn = res["xn"]
+    _, ds = ref.expert_ffn(xn, *W.shared)
+    for r in (1, 2, 4):
+        assert not res["valid"][r].any() and np.all(res["w"][r] == 0)
+        np.testing.assert_array_equal(res["out"][r], ds[r])
+    assert res["idx"][1].tolist() == [-1] * 6
+    assert res["valid"][3].tolist() == [False] + [True] * 5
+    # row 3 equals a 5-slot route over its valid entries
+    ent = table[3, 1:]
+    s = 1.0 / (1.0 + np.exp(-res["logits"][3, ent]))
+    w5 = s / s.sum()
+    out3 = ds[3].copy()
+    for k, e in enumerate(ent):
+        _, d = ref.expert_ffn(xn[3:4], *W.expert(e))
+        out3 += w5[k] * d[0]
+    np.testing.assert_allclose(res["out"][3], out3, rtol=1e-13, atol=1e-14)
+    safe, ok = ref.sanitize(np.array([[-1, 0, 31, 32, 5]]), 32)
+    assert safe.tolist() == [[0, 0, 31, 0, 5]] and ok.tolist() == [[False, True, True, False, True]]
+
+
+def check_special_functions():
+    assert ref.sigmoid(0.0) == 0.5
+    v = np.linspace(-30, 30, 61)
+    np.testing.assert_allclose(ref.sigmoid(v) + ref.sigmoid(-v), 1.0, rtol=0, atol=1e-15)
+    assert ref.silu(0.0) == 0.0
+    assert ref.sigmoid(-1000.0) == 0.0 and ref.sigmoid(1000.0) == 1.0
+    np.testing.assert_allclose(ref.swiglu([2.0], [3.0]), [3.0 * 2.0 / (1 + math.exp(-2.0))], rtol=1e-15)
+
+
+ALL_CHECKS = [check_bf16_widening, check_matmul_triple_loop, check_micro_example, check_topk_rank_definition,
+              check_topk_subset_enumeration, check_engineered_ties, check_weights_sum_to_one,
+              check_hash_equals_score, check_zero_input_closed_form, check_rmsnorm_identities,
+              check_scale_invariance, check_row_independence, check_expert_relabelling,
+              check_identical_experts, check_invalid_masking, check_special_functions]
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
+def test_pin(check):
+    check()
+
+
+# ------------------------------------------------- planted mistakes (CPU) ---
+def _mut_eps_outside(x, g, eps):
+    x = np.asarray(x, np.float64)
+    return x / (np.sqrt(np.mean(x * x, -1, keepdims=True)) + eps) * np.asarray(g, np.float64)
+
+
+def _mut_one_plus_g(x, g, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, -1, keepdims=True) + eps) * (1 + np.asarray(g, np.float64))
+
+
+def _mut_sum_not_mean(x, g, eps):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.sum(x * x, -1, keepdims=True) + eps) * np.asarray(g, np.float64)
+
+
+_orig_score = ref.score_route
+_orig_hash = ref.hash_route
+_orig_ffn = ref.expert_ffn
+_orig_fgr = ref.forward_given_routing
+
+
+def _mut_biased_weights(logits, bias, top_k):
+    idx, w, v = _orig_score(logits, bias, top_k)
+    key = ref.sigmoid(np.atleast_2d(logits)) + np.asarray(bias, np.float64)
+    kk = np.take_along_axis(key, idx.astype(np.int64), 1)
+    return idx, kk / kk.sum(1, keepdims=True), v
+
+
+def _mut_ties_high(logits, bias, top_k):
+    logits = np.atleast_2d(np.asarray(logits, np.float64))
+    key = ref.sigmoid(logits) + np.asarray(bias, np.float64)
+    idx = np.empty((len(key), top_k), np.int32)
+    w = np.empty((len(key), top_k))
+    for r in range(len(key)):
+        o = (len(key[r]) - 1 - np.argsort(-key[r][::-1], kind="stable"))[:top_k]
+        idx[r] = o
+        s = ref.sigmoid(logits[r, o])
+        w[r] = s / s.sum()
+    return idx, w, np.ones_like(idx, bool)
+
+
+def _mut_unnormalised(logits, bias, top_k):
+    idx, w, v = _orig_score(logits, bias, top_k)
+    s = ref.sigmoid(np.take_along_axis(np.atleast_2d(logits), idx.astype(np.int64), 1))
+    return idx, s, v
+
+
+def _mut_ascending(logits, bias, top_k):
+    logits = np.atleast_2d(np.asarray(logits, np.float64))
+    sig = ref.sigmoid(logits)
+    key = sig + np.asarray(bias, np.float64)
+    idx = np.argsort(key, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+    s = np.take_along_axis(sig, idx.astype(np.int64), 1)
+    return idx, s / s.sum(1, keepdims=True), np.ones_like(idx, bool)
+
+
+def _mut_swap_gate_up(xn, g, u, d):
+    return _orig_ffn(xn, u, g, d)
+
+
+def _mut_down_transposed(xn, g, u, d):
+    h, _ = _orig_ffn(xn, g, u, d)
+    return h, h @ ref.bf16_to_f64(d)
+
+
+def _mut_silu_sign(xn, g, u, d):
+    xn = np.asarray(xn, np.float64)
+    gg = xn @ ref.bf16_to_f64(g).T
+    uu = xn @ ref.bf16_to_f64(u).T
+    h = gg * ref.sigmoid(-gg) * uu
+    return h, h @ ref.bf16_to_f64(d).T
+
+
+def _mut_no_shared(xn, idx, w, valid, weights):
+    out = _orig_fgr(xn, idx, w, valid, weights)
+    _, ds = _orig_ffn(np.asarray(xn, np.float64), *weights.shared)
+    return out - ds
+
+
+def _mut_hash_ignores_validity(logits, token_ids, tid2eid, top_k):
+    idx, w, valid = _orig_hash(logits, token_ids, tid2eid, top_k)
+    return idx, w, np.ones_like(valid)
+
+
+MUTANTS = {
+    "rmsnorm_eps_outside_root": ("rms_norm", _mut_eps_outside),
+    "rmsnorm_one_plus_g": ("rms_norm", _mut_one_plus_g),
+    "rmsnorm_sum_not_mean": ("rms_norm", _mut_sum_not_mean),
+    "weights_from_biased_keys": ("score_route", _mut_biased_weights),
+    "ties_to_higher_index": ("score_route", _mut_ties_high),
+    "weights_not_renormalised": ("score_route", _mut_unnormalised),
+    "ascending_selection": ("score_route", _mut_ascending),
+    "gate_up_swapped": ("expert_ffn", _mut_swap_gate_up),
+    "down_transposed": ("expert_ffn", _mut_down_transposed),
+    "silu_sign_flipped": ("expert_ffn", _mut_silu_sign),
+    "shared_expert_dropped": ("forward_given_routing", _mut_no_shared),
+    "hash_invalid_not_masked": ("hash_route", _mut_hash_ignores_validity),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistakes(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(ref, attr, fn)
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check()
+        except Exception:  # an assertion or a shape error both count as caught
+            failed.append(check.__name__)
+    assert failed, f"planted mistake {name} passed every pin"
