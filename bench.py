@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE FFN layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers L]
+
+A step is one moe_ffn_forward call (RMSNorm, router, routing, sort, gate/up +
+SwiGLU, down, weighted reduce + shared expert) over one batch of synthetic
+rows with every input already in HBM.  Steps cycle over L independently drawn
+layers of weights so that a step never finds the previous step's experts in
+the 256 MB Infinity Cache.  Kernel durations come from HIP start/stop events
+the library records at each kernel's own start and end during the timed
+steps; the dominant kernel is reported against the MI355X roofline.  The
+float64 CPU oracle is timed on a bounded sample beside it.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer rows/sec at 1/4/512/8192 rows; HBM GB/s and MFMA % of peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix cores
+EXPERT_BYTES = lambda H, I: 3 * H * I * 2  # gate + up + down, bf16
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def alg_bytes(kernel, cfg, U, R):
+    """Algorithmic HBM bytes of one launch: every touched weight once, plus
+    activations in and out (U = distinct routed experts of the step)."""
+    H, I, E, K = cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
+    x = R * H * 4
+    if kernel == "dec_router_shared":
+        return E * H * 2 + 2 * I * H * 2 + x + H * 4 + R * E * 4 + R * I * 4
+    if kernel == "dec_gateup":
+        return U * 2 * I * H * 2 + R * H * 4 + min(R * K, U * R) * I * 4
+    if kernel == "dec_down_reduce":
+        return (U + 1) * H * I * 2 + (min(R * K, U * R) + R) * I * 4 + R * H * 4
+    if kernel == "gemm_gateup_swiglu":
+        S = R * K
+        return (U + 1) * 2 * I * H * 2 + (S + R) * H * 2 + (S + R) * I * 2
+    if kernel == "gemm_down":
+        S = R * K
+        return (U + 1) * H * I * 2 + (S + R) * I * 2 + (S + R) * H * 4
+    return None
+
+
+def alg_flops(kernel, cfg, R):
+    H, I, K = cfg.hidden, cfg.inter, cfg.top_k
+    rows = R * K + R  # routed slots + shared-expert rows
+    if kernel == "gemm_gateup_swiglu":
+        return 2 * rows * 2 * I * H
+    if kernel == "gemm_down":
+        return 2 * rows * H * I
+    return None
+
+
+def step_bytes(cfg, U, R):
+    H, I, E = cfg.hidden, cfg.inter, cfg.experts
+    return (U + 1) * EXPERT_BYTES(H, I) + E * H * 2 + 2 * R * H * 4 + H * 4 + E * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode-r1-score")
+    ap.add_argument("--layers", type=int, default=None, help="distinct weight sets cycled (default 4 decode, 1 prefill)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_ffn_rmsnorm_amd import inputs as gen
+    from mixture_experts_ffn_rmsnorm_amd import moe
+
+    moe.lib()  # fail loudly if the HIP library is missing
+    cfg = gen.config(args.workload)
+    R = cfg.rows
+    decode = R <= 4
+    L = args.layers or (4 if decode else 1)
+    log(f"workload {cfg.name}: rows={R} layers={L}; drawing weights on the GPU")
+    torch.cuda.set_device(0)
+    dims = moe.dims_of(cfg)
+    layers = []
+    for l in range(L):
+        hi = gen.host_inputs(cfg, layer=l)
+        (g, u, d), (gs, us, ds) = gen.expert_weights_device(cfg, "cuda", layer=l)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        keep = [t(hi.norm_w), t(hi.router.view(np.int16)).view(torch.bfloat16), t(hi.sel_bias),
+                t(hi.tid2eid) if hi.tid2eid is not None else None, g, u, d, gs, us, ds]
+        layers.append((hi, keep, moe.make_weights(*keep)))
+        log(f"layer {l} ready")
+    hi0 = layers[0][0]
+    x = torch.from_numpy(hi0.x).cuda()
+    tok = torch.from_numpy(hi0.token_ids).cuda()
+    out = torch.empty_like(x)
+    ws = [moe.alloc_workspace(dims, R) for _ in range(L)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        l = i % L
+        moe.forward(dims, x, tok, cfg.layer_kind, layers[l][2], out, ws[l])
+
+    log(f"warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # distinct routed experts of each layer's step, from its routing
+    U = []
+    for l in range(L):
+        step(l)
+        torch.cuda.synchronize()
+        idx = moe.routing_view(dims, R, ws[l])[1].cpu().numpy()
+        U.append(len(np.unique(idx[(idx >= 0) & (idx < cfg.experts)])))
+    log(f"distinct routed experts per layer: {U}")
+
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    moe.stage_timing_begin()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = moe.stage_timing_end()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = R / (ms_per_step / 1e3)
+    u_mean = float(np.mean([U[i % L] for i in range(args.steps)]))
+
+    kernels = {}
+    for name, (ms, n) in stages.items():
+        kernels[name] = {"avg_us": ms * 1e3 / n, "launches": n}
+    dom = max(stages, key=lambda k: stages[k][0])
+    avg_s = stages[dom][0] / stages[dom][1] / 1e3
+    flops = alg_flops(dom, cfg, R)
+    if flops is not None and not decode:
+        ach = flops / avg_s / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": None}
+    else:
+        b = alg_bytes(dom, cfg, u_mean, R)
+        ach = b / avg_s / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBPS, "traffic": None}
+    sb = step_bytes(cfg, u_mean, R)
+    res = {
+        "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if decode else "f16", "data": "synthetic",
+        "config": {"workload": cfg.name, "rows": R, "hidden": cfg.hidden, "experts": cfg.experts,
+                   "top_k": cfg.top_k, "inter": cfg.inter, "shared_experts": 1,
+                   "layer_kind": "hash" if cfg.layer_kind == 1 else "score", "layers_cycled": L,
+                   "distinct_routed_experts": u_mean},
+        "roofline": roof,
+        "step_hbm_GBps": sb / (ms_per_step / 1e3) / 1e9,
+        "step_hbm_frac": sb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS,
+        "kernels": kernels,
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds, log)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, layer, budget_s, log):
+    """The float64 oracle on a bounded sample of the same workload."""
+    import numpy as np
+
+    from mixture_experts_ffn_rmsnorm_amd import inputs as gen
+    from oracle import moe_ref as ref
+
+    hi, keep, _ = layer
+    g, u, d, gs, us, ds = keep[4:]
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = tuple(gen.bf16_tensor_bits(m[e]) for m in (g, u, d))
+        return cache[e]
+
+    W = ref.Weights(hi.norm_w, hi.router, hi.sel_bias, hi.tid2eid, expert,
+                    tuple(gen.bf16_tensor_bits(m) for m in (gs, us, ds)))
+    per = min(cfg.rows, 4)
+    # fetch the experts of the sample rows before timing
+    xs, ts = hi.x[:per], hi.token_ids[:per]
+    res = ref.forward(xs, ts, cfg.layer_kind, W, cfg.top_k, cfg.eps)
+    log(f"cpu baseline: timing the oracle on {per}-row samples for ~{budget_s:.0f}s")
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        ref.forward(xs, ts, cfg.layer_kind, W, cfg.top_k, cfg.eps)
+        done += per
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    return {"value": done / el, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {per} row(s) of the workload through the float64 oracle, repeated "
+                      f"{done // per}x in {el:.1f}s (BLAS threads = cores)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * moe_ffn.h -- C ABI of the routed mixture-of-experts FFN layer with RMSNorm
+ * for AMD Instinct MI355X (gfx950), library libmoeffn.so.
+ *
+ * The layer is the one `forward_ffn_rows` encodes on the docs.rs source page
+ * "hf2q 0.1.3 -- src/inference/models/deepseek4/ffn_forward.rs": RMSNorm of
+ * the FFN input, router matmul ("MoE gate"), score route (sigmoid score +
+ * selection bias) or hash route (token-id -> expert table), index
+ * sanitising, routed and shared gate/up projections, SwiGLU, down
+ * projections and the weighted reduce of routed plus shared outputs.  The
+ * hyper-connection prelude and post-mix that wrap it on that page are not
+ * part of this ABI: `x` here is the page's `ffn_input`, `out` its
+ * `ffn_output`.
+ *
+ * Conventions shared by every entry point:
+ *   - Return value: 0 (MOE_OK) or a positive moe_status code; moe_strerror()
+ *     names it.  Argument errors are detected on the host BEFORE any HIP
+ *     call, so they never leave work on the stream.
+ *   - Pointers documented "device" are HIP device (or managed) memory owned
+ *     by the caller; the library neither allocates nor frees on the call
+ *     path and keeps no reference after the call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work; they do not synchronise (except moe_ffn_status and
+ *     moe_ffn_stage_timing_end, which say so).
+ *   - All matrices are row-major; weight matrices are [out][in].
+ *   - Thread safety: the library is stateless apart from the optional stage
+ *     timer.  Concurrent calls on different streams must use different
+ *     workspaces; calls that share a workspace race.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,       /* bad argument: rows <= 0, NULL pointer, unknown
+                           layer kind, missing bias (score) or table (hash) */
+  MOE_EUNSUPPORTED = 2, /* dims with no compiled kernels (see moe_dims_t)    */
+  MOE_EOVERFLOW = 3,    /* rows * top_k (or a buffer size) overflows         */
+  MOE_EWORKSPACE = 4,   /* workspace NULL, misaligned or too small           */
+  MOE_EHIP = 5,         /* a HIP launch or runtime call failed               */
+  MOE_EOVERLAP = 6      /* x and out overlap                                 */
+};
+
+/* ---- layer kinds (ffn_forward.rs: the hash table is bound for layers below
+ * hash_layer_count, the selection bias for the layers after them) -------- */
+enum { MOE_LAYER_SCORE = 0, MOE_LAYER_HASH = 1 };
+
+/* ---- device status bits, read with moe_ffn_status ----------------------- */
+enum {
+  MOE_FLAG_BAD_TOKEN = 1u,      /* a hash-layer token id outside [0, table_rows):
+                                   all of that row's slots were masked      */
+  MOE_FLAG_BAD_TABLE_ENTRY = 2u /* a table entry outside [0, experts): that
+                                   slot was masked                          */
+};
+
+/* Layer dimensions.  ffn_forward.rs guards the native path with fixed
+ * constants (hidden 4096, 256 experts, top-6, inter 2048); this library
+ * compiles kernels for exactly two shapes and rejects others with
+ * MOE_EUNSUPPORTED:
+ *     hidden 4096, experts 256, top_k 6, inter 2048, n_shared 1   (full)
+ *     hidden  512, experts  32, top_k 6, inter  256, n_shared 1   (tiny)
+ * table_rows is the number of tid2eid rows (the token-id range of a hash
+ * layer; ignored for score layers).  eps is the RMSNorm epsilon (> 0 or 0). */
+typedef struct moe_dims {
+  int32_t hidden;
+  int32_t experts;
+  int32_t top_k;
+  int32_t inter;
+  int32_t n_shared;
+  int32_t reserved0;  /* must be 0 */
+  int64_t table_rows;
+  float eps;
+  int32_t reserved1;  /* must be 0 */
+} moe_dims_t;
+
+/* One layer's parameters, all DEVICE pointers, caller-owned, read-only.
+ * Names follow the GGUF tensors ffn_forward.rs binds for block L:
+ *   norm_w    blk.L.ffn_norm.weight        f32  [hidden]
+ *   router    blk.L.ffn_gate_inp.weight    bf16 [experts][hidden]
+ *   sel_bias  blk.L.exp_probs_b.bias       f32  [experts]        (score layers)
+ *   tid2eid   blk.L.ffn_gate_tid2eid       i32  [table_rows][top_k] (hash layers)
+ *   gate_exps blk.L.ffn_gate_exps.weight   bf16 [experts][inter][hidden]
+ *   up_exps   blk.L.ffn_up_exps.weight     bf16 [experts][inter][hidden]
+ *   down_exps blk.L.ffn_down_exps.weight   bf16 [experts][hidden][inter]
+ *   gate_sh   blk.L.ffn_gate_shexp.weight  bf16 [inter][hidden]
+ *   up_sh     blk.L.ffn_up_shexp.weight    bf16 [inter][hidden]
+ *   down_sh   blk.L.ffn_down_shexp.weight  bf16 [hidden][inter]
+ * bf16 values are passed as their 16-bit patterns.  Every pointer must be
+ * 16-byte aligned.  sel_bias may be NULL for hash layers, tid2eid for score
+ * layers. */
+typedef struct moe_weights {
+  const float* norm_w;
+  const uint16_t* router;
+  const float* sel_bias;
+  const int32_t* tid2eid;
+  const uint16_t* gate_exps;
+  const uint16_t* up_exps;
+  const uint16_t* down_exps;
+  const uint16_t* gate_sh;
+  const uint16_t* up_sh;
+  const uint16_t* down_sh;
+} moe_weights_t;
+
+/* Workspace size in bytes that moe_ffn_forward needs for `rows` rows of a
+ * layer with dims *d (the page allocates the same intermediates per call:
+ * logits, indices, safe indices, weights, routed and shared gate/up/
+ * activation/down buffers; here the caller provides one block for them).
+ * Host-only, no HIP call.  Errors: MOE_EINVAL, MOE_EUNSUPPORTED,
+ * MOE_EOVERFLOW. */
+int moe_ffn_workspace_bytes(const moe_dims_t* d, int64_t rows, size_t* bytes);
+
+/* The whole layer for `rows` rows (ffn_forward.rs, forward_ffn_rows from
+ * the FFN RMSNorm through the weighted reduce):
+ *   x          device f32 [rows][hidden]  FFN input (the page's ffn_input)
+ *   token_ids  device i32 [rows]          token id per row; required for
+ *                                          MOE_LAYER_HASH, may be NULL for
+ *                                          MOE_LAYER_SCORE
+ *   layer_kind MOE_LAYER_SCORE or MOE_LAYER_HASH
+ *   w          the layer's parameters (see moe_weights_t)
+ *   out        device f32 [rows][hidden]  fully overwritten; must not
+ *                                          overlap x
+ *   workspace  device, >= moe_ffn_workspace_bytes(d, rows), 256-byte
+ *              aligned; contents on entry are ignored.  After the call it
+ *              holds the routing (see moe_ffn_routing_view) and the status
+ *              word (see moe_ffn_status) until the next call that uses it.
+ * Token ids and table entries are device data, so a bad one is not a host
+ * error: the affected slots are masked (they contribute nothing and the
+ * row's other weights are renormalised over its valid slots) and a status
+ * bit is set.  The result is bitwise reproducible for equal inputs.
+ * Errors (host-checked): MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EOVERFLOW,
+ * MOE_EWORKSPACE, MOE_EOVERLAP; MOE_EHIP if a launch fails. */
+int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,
+                    int layer_kind, const moe_weights_t* w, float* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Routing alone, from caller-given logits (ffn_forward.rs: the score-route
+ * and hash-route dispatches that turn the F32 logits into I32 indices and
+ * F32 weights), using the same device routine as moe_ffn_forward:
+ *   logits     device f32 [rows][experts]
+ *   token_ids  device i32 [rows] (hash layers; NULL ok for score layers)
+ *   w          only sel_bias (score) or tid2eid (hash) is read
+ *   idx        device i32 [rows][top_k]  score: experts by key
+ *              sigmoid(logit)+bias descending, equal keys to the lower
+ *              index, key evaluated in float64; hash: the table row in
+ *              column order, -1 for every slot of a bad token id and the
+ *              raw entry for a bad table entry
+ *   wout       device f32 [rows][top_k]  unbiased sigmoid scores of the
+ *              chosen experts over their sum (0 for masked slots)
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EOVERFLOW, MOE_EHIP. */
+int moe_route(const moe_dims_t* d, const float* logits, const int32_t* token_ids, int64_t rows,
+              int layer_kind, const moe_weights_t* w, int32_t* idx, float* wout, void* stream);
+
+/* Device pointers, inside `workspace`, to the last moe_ffn_forward's router
+ * logits (f32 [rows][experts]), indices (i32 [rows][top_k]) and routing
+ * weights (f32 [rows][top_k]) for a call with the same dims and rows.  Any
+ * output pointer may be NULL.  Host-only arithmetic, no HIP call.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EOVERFLOW, MOE_EWORKSPACE. */
+int moe_ffn_routing_view(const moe_dims_t* d, int64_t rows, void* workspace, size_t workspace_bytes,
+                         const float** logits, const int32_t** idx, const float** wout);
+
+/* Synchronises `stream`, then copies the status word of the last
+ * moe_ffn_forward that used `workspace` (OR of MOE_FLAG_* bits) to *flags.
+ * Errors: MOE_EINVAL, MOE_EHIP. */
+int moe_ffn_status(const void* workspace, void* stream, uint32_t* flags);
+
+/* Static English text for a status code. */
+const char* moe_strerror(int code);
+
+/* ---- stage timing (replaces the page's env-flagged profile_stage_boundary
+ * markers between the router, gate/up, activation and down stages) ------
+ * moe_ffn_stage_timing_begin() makes every following moe_ffn_forward launch
+ * its kernels with HIP start/stop events taken at the kernels' own start
+ * and end.  moe_ffn_stage_timing_end() synchronises those events, writes up
+ * to `max` per-kernel totals (name, summed milliseconds, launch count) and
+ * stops timing.  *n gets the number of distinct kernels seen.  Not for use
+ * under HIP graph capture.  Errors: MOE_EINVAL, MOE_EHIP. */
+int moe_ffn_stage_timing_begin(void);
+int moe_ffn_stage_timing_end(int max, const char** names, double* total_ms, int64_t* launches, int* n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

@@ -1,0 +1,283 @@
+// C ABI of libmoeffn.so (declared in include/moe_ffn.h).
+//
+// Argument checks mirror the bails of forward_ffn_rows on the hf2q
+// ffn_forward.rs page (layer/rows range, routed-row overflow, fixed MoE
+// shape, state dtype/shape, "no routing source") and run on the host before
+// any HIP call, so a rejected call leaves nothing on the stream and can be
+// exercised without a GPU.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <mutex>
+#include <string.h>
+#include <vector>
+
+#include "kernels.h"
+#include "layout.h"
+#include "moe_ffn.h"
+
+namespace moe {
+namespace {
+
+bool dims_supported(const moe_dims_t* d) {
+  if (d->reserved0 != 0 || d->reserved1 != 0 || d->n_shared != 1) return false;
+  if (!(d->eps >= 0.0f) || !isfinite(d->eps)) return false;
+  const bool full = d->hidden == 4096 && d->experts == 256 && d->top_k == 6 && d->inter == 2048;
+  const bool tiny = d->hidden == 512 && d->experts == 32 && d->top_k == 6 && d->inter == 256;
+  return full || tiny;
+}
+
+constexpr int64_t kMaxRows = (int64_t)1 << 24;  // keeps rows*top_k and every index within int32
+
+int check_dims_rows(const moe_dims_t* d, int64_t rows) {
+  if (!d) return MOE_EINVAL;
+  if (rows <= 0) return MOE_EINVAL;
+  if (!dims_supported(d)) return MOE_EUNSUPPORTED;
+  if (rows > kMaxRows) return MOE_EOVERFLOW;
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_weights(const moe_dims_t* d, int layer_kind, const moe_weights_t* w, const int32_t* token_ids,
+                  bool need_experts) {
+  if (!w) return MOE_EINVAL;
+  if (layer_kind != MOE_LAYER_SCORE && layer_kind != MOE_LAYER_HASH) return MOE_EINVAL;
+  if (layer_kind == MOE_LAYER_SCORE && !w->sel_bias) return MOE_EINVAL;
+  if (layer_kind == MOE_LAYER_HASH && (!w->tid2eid || !token_ids || d->table_rows <= 0)) return MOE_EINVAL;
+  if (need_experts) {
+    const void* req[] = {w->norm_w, w->router, w->gate_exps, w->up_exps, w->down_exps,
+                         w->gate_sh, w->up_sh, w->down_sh};
+    for (const void* p : req)
+      if (!p || !aligned(p, 16)) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+struct TimerRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+
+struct StageTimer {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<TimerRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+StageTimer& timer() {
+  static StageTimer t;
+  return t;
+}
+
+}  // namespace
+
+hipError_t launch(const char* name, const void* fn, dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                  void* args) {
+  void* argv[1] = {args};
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  StageTimer& T = timer();
+  std::unique_lock<std::mutex> lk(T.mu);
+  if (T.enabled) {
+    e0 = T.get();
+    e1 = T.get();
+  } else {
+    lk.unlock();
+  }
+  hipError_t err = hipExtLaunchKernel(fn, grid, block, argv, shmem, stream, e0, e1, 0);
+  if (e0 && e1) T.recs.push_back({name, e0, e1});
+  return err;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_ffn_workspace_bytes(const moe_dims_t* d, int64_t rows, size_t* bytes) {
+  int rc = check_dims_rows(d, rows);
+  if (rc) return rc;
+  if (!bytes) return MOE_EINVAL;
+  Layout L;
+  if (!make_layout(rows, d->hidden, d->experts, d->top_k, d->inter, &L)) return MOE_EOVERFLOW;
+  *bytes = L.total;
+  return MOE_OK;
+}
+
+int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
+                    const moe_weights_t* w, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims_rows(d, rows);
+  if (rc) return rc;
+  if (!x || !out || !aligned(x, 16) || !aligned(out, 16)) return MOE_EINVAL;
+  rc = check_weights(d, layer_kind, w, token_ids, true);
+  if (rc) return rc;
+  Layout L;
+  if (!make_layout(rows, d->hidden, d->experts, d->top_k, d->inter, &L)) return MOE_EOVERFLOW;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
+  const size_t nbytes = (size_t)rows * d->hidden * sizeof(float);
+  const uintptr_t xb = (uintptr_t)x, ob = (uintptr_t)out;
+  if (xb < ob + nbytes && ob < xb + nbytes) return MOE_EOVERLAP;
+
+  char* ws = (char*)workspace;
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.R = (int)rows;
+  a.H = d->hidden;
+  a.E = d->experts;
+  a.K = d->top_k;
+  a.I = d->inter;
+  a.eps = d->eps;
+  a.layer_kind = layer_kind;
+  a.table_rows = d->table_rows;
+  a.x = x;
+  a.token_ids = token_ids;
+  a.norm_w = w->norm_w;
+  a.router = w->router;
+  a.bias = w->sel_bias;
+  a.table = w->tid2eid;
+  a.gate = w->gate_exps;
+  a.up = w->up_exps;
+  a.down = w->down_exps;
+  a.gate_sh = w->gate_sh;
+  a.up_sh = w->up_sh;
+  a.down_sh = w->down_sh;
+  a.out = out;
+  a.status = (uint32_t*)(ws + L.status);
+  a.logits = (float*)(ws + L.logits);
+  a.idx = (int32_t*)(ws + L.idx);
+  a.wts = (float*)(ws + L.wts);
+  a.rowflags = (uint32_t*)(ws + L.rowflags);
+  const bool decode = rows <= kDecodeMaxRows;
+  if (decode) {
+    a.xn32 = (float*)(ws + L.xn32);
+    a.plan = (DecodePlan*)(ws + L.plan);
+    a.h32 = (float*)(ws + L.h32);
+  } else {
+    a.xn16 = (_Float16*)(ws + L.xn16);
+    a.cnt = (int32_t*)(ws + L.cnt);
+    a.base = (int32_t*)(ws + L.base);
+    a.slot_rank = (int32_t*)(ws + L.slot_rank);
+    a.perm = (int32_t*)(ws + L.perm);
+    a.h16 = (_Float16*)(ws + L.h16);
+    a.dbuf = (float*)(ws + L.dbuf);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = decode ? run_decode(a, s) : run_prefill(a, s);
+  return err == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_route(const moe_dims_t* d, const float* logits, const int32_t* token_ids, int64_t rows, int layer_kind,
+              const moe_weights_t* w, int32_t* idx, float* wout, void* stream) {
+  int rc = check_dims_rows(d, rows);
+  if (rc) return rc;
+  if (!logits || !idx || !wout) return MOE_EINVAL;
+  rc = check_weights(d, layer_kind, w, token_ids, false);
+  if (rc) return rc;
+  RouteArgs a;
+  a.R = (int)rows;
+  a.E = d->experts;
+  a.K = d->top_k;
+  a.layer_kind = layer_kind;
+  a.table_rows = d->table_rows;
+  a.logits = logits;
+  a.token_ids = token_ids;
+  a.bias = w->sel_bias;
+  a.table = w->tid2eid;
+  a.idx = idx;
+  a.w = wout;
+  return run_route(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_ffn_routing_view(const moe_dims_t* d, int64_t rows, void* workspace, size_t workspace_bytes,
+                         const float** logits, const int32_t** idx, const float** wout) {
+  int rc = check_dims_rows(d, rows);
+  if (rc) return rc;
+  Layout L;
+  if (!make_layout(rows, d->hidden, d->experts, d->top_k, d->inter, &L)) return MOE_EOVERFLOW;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
+  char* ws = (char*)workspace;
+  if (logits) *logits = (const float*)(ws + L.logits);
+  if (idx) *idx = (const int32_t*)(ws + L.idx);
+  if (wout) *wout = (const float*)(ws + L.wts);
+  return MOE_OK;
+}
+
+int moe_ffn_status(const void* workspace, void* stream, uint32_t* flags) {
+  if (!workspace || !flags) return MOE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_EHIP;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_EHIP;
+  *flags = v;
+  return MOE_OK;
+}
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported layer dimensions";
+    case MOE_EOVERFLOW: return "size overflow";
+    case MOE_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_EHIP: return "HIP launch or runtime error";
+    case MOE_EOVERLAP: return "x and out overlap";
+    default: return "unknown status";
+  }
+}
+
+int moe_ffn_stage_timing_begin(void) {
+  StageTimer& T = timer();
+  std::lock_guard<std::mutex> lk(T.mu);
+  T.enabled = true;
+  return MOE_OK;
+}
+
+int moe_ffn_stage_timing_end(int max, const char** names, double* total_ms, int64_t* launches, int* n) {
+  if (max < 0 || !n || (max > 0 && (!names || !total_ms || !launches))) return MOE_EINVAL;
+  StageTimer& T = timer();
+  std::lock_guard<std::mutex> lk(T.mu);
+  T.enabled = false;
+  std::vector<const char*> nm;
+  std::vector<double> ms;
+  std::vector<int64_t> cnt;
+  int rc = MOE_OK;
+  for (auto& r : T.recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) rc = MOE_EHIP;
+    float el = 0.f;
+    if (rc == MOE_OK && hipEventElapsedTime(&el, r.start, r.stop) != hipSuccess) rc = MOE_EHIP;
+    size_t i = 0;
+    while (i < nm.size() && strcmp(nm[i], r.name) != 0) ++i;
+    if (i == nm.size()) {
+      nm.push_back(r.name);
+      ms.push_back(0.0);
+      cnt.push_back(0);
+    }
+    ms[i] += el;
+    cnt[i] += 1;
+    T.pool.push_back(r.start);
+    T.pool.push_back(r.stop);
+  }
+  T.recs.clear();
+  *n = (int)nm.size();
+  for (int i = 0; i < max && i < (int)nm.size(); ++i) {
+    names[i] = nm[i];
+    total_ms[i] = ms[i];
+    launches[i] = cnt[i];
+  }
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Host-side interface between the C ABI (abi.hip) and the kernel files.
+// Every kernel takes one argument struct by value; launch() sends it with
+// hipExtLaunchKernel so the optional stage timer can bracket the kernel's
+// own execution with start/stop events.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace moe {
+
+// Launch `fn(args)` on `stream`; returns the launch status.
+hipError_t launch(const char* name, const void* fn, dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                  void* args);
+
+// Everything one forward call needs, resolved to device pointers.
+struct FwdArgs {
+  // problem
+  int R, H, E, K, I;
+  float eps;
+  int layer_kind;
+  int64_t table_rows;
+  // inputs / outputs
+  const float* x;
+  const int32_t* token_ids;
+  const float* norm_w;
+  const uint16_t* router;
+  const float* bias;
+  const int32_t* table;
+  const uint16_t* gate;
+  const uint16_t* up;
+  const uint16_t* down;
+  const uint16_t* gate_sh;
+  const uint16_t* up_sh;
+  const uint16_t* down_sh;
+  float* out;
+  // workspace pieces
+  uint32_t* status;
+  float* logits;
+  int32_t* idx;
+  float* wts;
+  uint32_t* rowflags;
+  float* xn32;
+  DecodePlan* plan;
+  float* h32;
+  _Float16* xn16;
+  int32_t* cnt;
+  int32_t* base;
+  int32_t* slot_rank;
+  int32_t* perm;
+  _Float16* h16;
+  float* dbuf;
+};
+
+hipError_t run_decode(const FwdArgs& a, hipStream_t s);
+hipError_t run_prefill(const FwdArgs& a, hipStream_t s);
+
+struct RouteArgs {
+  int R, E, K, layer_kind;
+  int64_t table_rows;
+  const float* logits;
+  const int32_t* token_ids;
+  const float* bias;
+  const int32_t* table;
+  int32_t* idx;
+  float* w;
+};
+hipError_t run_route(const RouteArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,99 @@
+// Workspace layout of moe_ffn_forward: one caller-provided device block is
+// carved into the per-call intermediates.  ffn_forward.rs (forward_ffn_rows)
+// allocates the same set per call -- logits, I32 indices, U32 safe
+// indices, weights, routed/shared gate, up, activation and down buffers;
+// here they live at fixed offsets so a call allocates nothing.
+//
+// Pure host/device arithmetic, no HIP calls: the CPU-side validation and the
+// kernels use the same offsets.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Rows up to this count take the decode path (weight-streaming GEMV with
+// f32 activations); larger batches take the grouped-GEMM prefill path.
+constexpr int kDecodeMaxRows = 4;
+constexpr int kMaxTopK = 8;
+constexpr int kDecodeMaxSlots = kDecodeMaxRows * kMaxTopK;  // 32
+constexpr int kMaxExperts = 256;
+
+// Routing plan of a decode call: the distinct experts of the batch, each
+// with the distinct rows that chose it and the summed weight of those
+// slots.  Written by the routing prologue of the gate/up kernel, read by the
+// down kernel.
+struct DecodePlan {
+  int32_t ngroups;                            // distinct routed experts
+  int32_t nentries;                           // distinct (expert, row) pairs
+  int32_t group_expert[kDecodeMaxSlots];
+  int32_t group_begin[kDecodeMaxSlots + 1];   // entry range of each group
+  int32_t entry_row[kDecodeMaxSlots];
+  float entry_w[kDecodeMaxSlots];
+};
+
+struct Layout {
+  size_t status;     // u32 status word (+ padding)
+  size_t logits;     // f32 [R][E]
+  size_t sig;        // f64 [R][E]   sigmoid of the logits (decode path)
+  size_t idx;        // i32 [R][K]
+  size_t wts;        // f32 [R][K]
+  size_t rowflags;   // u32 [R]
+  size_t xn32;       // f32 [R][H]   (decode)
+  size_t plan;       // DecodePlan    (decode)
+  size_t h32;        // f32 [kDecodeMaxSlots + R][I]   (decode)
+  size_t xn16;       // f16 [R][H]   (prefill)
+  size_t cnt;        // i32 [E + 1]  rows per group (routed experts, then shared)
+  size_t base;       // i32 [E + 2]  exclusive prefix of cnt
+  size_t slot_rank;  // i32 [R][K]   rank of the slot's row inside its expert
+  size_t perm;       // i32 [E][R]   rows of each expert in ascending order
+  size_t h16;        // f16 [S + R][I]   SwiGLU output, grouped order
+  size_t dbuf;       // f32 [S + R][H]   down output, grouped order
+  size_t total;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Returns false on size overflow.
+inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
+  const unsigned __int128 lim = (unsigned __int128)1 << 62;
+  unsigned __int128 r = (unsigned __int128)R;
+  unsigned __int128 S = r * K;
+  if (R <= 0 || S >= lim) return false;
+  const bool decode = R <= kDecodeMaxRows;
+  unsigned __int128 off = 0;
+  auto take = [&](unsigned __int128 bytes) -> size_t {
+    off = (off + 255) / 256 * 256;
+    size_t at = (size_t)off;
+    off += bytes;
+    return at;
+  };
+  L->status = take(256);
+  L->logits = take(r * E * 4);
+  L->sig = take(r * E * 8);
+  L->idx = take(S * 4);
+  L->wts = take(S * 4);
+  L->rowflags = take(r * 4);
+  if (decode) {
+    L->xn32 = take(r * H * 4);
+    L->plan = take(sizeof(DecodePlan));
+    L->h32 = take((unsigned __int128)(kDecodeMaxSlots + R) * I * 4);
+    L->xn16 = L->cnt = L->base = L->slot_rank = L->perm = L->h16 = L->dbuf = 0;
+  } else {
+    L->xn32 = L->plan = L->h32 = 0;
+    L->xn16 = take(r * H * 2);
+    L->cnt = take((unsigned __int128)(E + 1) * 4);
+    L->base = take((unsigned __int128)(E + 2) * 4);
+    L->slot_rank = take(S * 4);
+    L->perm = take((unsigned __int128)E * r * 4);
+    L->h16 = take((S + r) * I * 2);
+    L->dbuf = take((S + r) * H * 4);
+  }
+  off = (off + 255) / 256 * 256;
+  if (off >= lim) return false;
+  L->total = (size_t)off;
+  return true;
+}
+
+}  // namespace moe

@@ -48,7 +48,8 @@ class Config:
     bias_std: float = 0.1
     norm_std: float = 0.05
     eps: float = 1e-6
-    seed: int = 1000
+    seed: int = 1000             # activations and token ids
+    param_seed: int = 1000       # layer parameters (shared by the full-size workloads)
 
     @property
     def routed_slots(self) -> int:
@@ -56,7 +57,8 @@ class Config:
 
 
 def _cfg(i, **kw):
-    return Config(seed=1000 + i, **kw)
+    # the four full-size workloads share one set of layer parameters
+    return Config(seed=1000 + i, param_seed=1000 if i == 0 else 1001, **kw)
 
 
 # The five workloads: tiny CPU-seconds layer; full-size decode (score route);
@@ -122,7 +124,7 @@ def host_inputs(cfg: Config, layer: int = 0, rows: int | None = None) -> HostInp
     norm weight, table) while x and token ids stay the same.
     """
     s = cfg.seed
-    ls = s + 7919 * layer
+    ls = cfg.param_seed + 7919 * layer
     R = cfg.rows if rows is None else rows
     x = _rng(s, _T_X).standard_normal((R, cfg.hidden), dtype=np.float32)
     tok = _rng(s, _T_TOK).integers(0, max(cfg.table_rows, 1), size=R, dtype=np.int64).astype(np.int32)
@@ -131,7 +133,8 @@ def host_inputs(cfg: Config, layer: int = 0, rows: int | None = None) -> HostInp
     bias = (cfg.bias_std * _rng(ls, _T_BIAS).standard_normal(cfg.experts, dtype=np.float32)).astype(np.float32)
     hot = np.zeros(0, dtype=np.int32)
     if cfg.hot_experts:
-        hot = np.sort(_rng(ls, _T_HOT).choice(cfg.experts, cfg.hot_experts, replace=False)).astype(np.int32)
+        hot = np.sort(_rng(s + 7919 * layer, _T_HOT).choice(cfg.experts, cfg.hot_experts,
+                                                              replace=False)).astype(np.int32)
         bias[hot] = np.float32(cfg.hot_bias)
     table = None
     if cfg.table_rows:
@@ -157,7 +160,7 @@ def distinct_table(seed: int, table_rows: int, experts: int, top_k: int) -> np.n
 def expert_host(cfg: Config, e: int, layer: int = 0):
     """bf16 bits ``(gate [I,H], up [I,H], down [H,I])`` of routed expert e,
     drawn on the host (used for the tiny layer)."""
-    ls = cfg.seed + 7919 * layer
+    ls = cfg.param_seed + 7919 * layer
     I, H = cfg.inter, cfg.hidden
     return (_normal_bf16(ls, _T_GATE, e, (I, H), cfg.weight_std),
             _normal_bf16(ls, _T_UP, e, (I, H), cfg.weight_std),
@@ -165,7 +168,7 @@ def expert_host(cfg: Config, e: int, layer: int = 0):
 
 
 def shared_host(cfg: Config, layer: int = 0):
-    ls = cfg.seed + 7919 * layer
+    ls = cfg.param_seed + 7919 * layer
     I, H = cfg.inter, cfg.hidden
     return (_normal_bf16(ls, _T_SGATE, 0, (I, H), cfg.weight_std),
             _normal_bf16(ls, _T_SUP, 0, (I, H), cfg.weight_std),
@@ -187,7 +190,7 @@ def expert_weights_device(cfg: Config, device, layer: int = 0):
     """
     import torch
 
-    ls = cfg.seed + 7919 * layer
+    ls = cfg.param_seed + 7919 * layer
     I, H, E = cfg.inter, cfg.hidden, cfg.experts
     gen = torch.Generator(device=device)
 

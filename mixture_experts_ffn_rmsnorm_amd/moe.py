@@ -1,0 +1,172 @@
+"""Thin Python binding of libmoeffn.so (include/moe_ffn.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+Tensors are torch device tensors; the binding passes their data pointers and
+the current HIP stream.  If the library is missing this module raises on
+first use -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoeffn.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EOVERFLOW, MOE_EWORKSPACE, MOE_EHIP, MOE_EOVERLAP = range(7)
+LAYER_SCORE, LAYER_HASH = 0, 1
+FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY = 1, 2
+
+# Function names the header declares (checked against the library's exports).
+EXPORTS = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_route", "moe_ffn_routing_view", "moe_ffn_status",
+           "moe_strerror", "moe_ffn_stage_timing_begin", "moe_ffn_stage_timing_end")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {strerror(code)} (code {code})")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("table_rows", ctypes.c_int64), ("eps", ctypes.c_float), ("reserved1", ctypes.c_int32)]
+
+
+class WeightsC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("norm_w", "router", "sel_bias", "tid2eid", "gate_exps", "up_exps",
+                                               "down_exps", "gate_sh", "up_sh", "down_sh")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixture_experts_ffn_rmsnorm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(Dims), I64, ctypes.POINTER(SZ)]
+        L.moe_ffn_forward.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, SZ, P]
+        L.moe_route.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, P]
+        L.moe_ffn_routing_view.argtypes = [ctypes.POINTER(Dims), I64, P, SZ, ctypes.POINTER(P), ctypes.POINTER(P),
+                                           ctypes.POINTER(P)]
+        L.moe_ffn_status.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
+        L.moe_strerror.argtypes = [I32]
+        L.moe_strerror.restype = ctypes.c_char_p
+        L.moe_ffn_stage_timing_begin.argtypes = []
+        L.moe_ffn_stage_timing_end.argtypes = [I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                               ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(I32)]
+        for n in EXPORTS:
+            if n != "moe_strerror":
+                getattr(L, n).restype = I32
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().moe_strerror(int(code)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != MOE_OK:
+        raise MoeError(rc, what)
+
+
+def make_dims(hidden, experts, top_k, inter, table_rows=0, eps=1e-6, n_shared=1) -> Dims:
+    return Dims(hidden, experts, top_k, inter, n_shared, 0, int(table_rows), float(eps), 0)
+
+
+def dims_of(cfg) -> Dims:
+    """Dims of an ``inputs.Config``."""
+    return make_dims(cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.table_rows, cfg.eps)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_weights(norm_w, router, sel_bias, tid2eid, gate, up, down, gate_sh, up_sh, down_sh) -> WeightsC:
+    """Pack device tensors (bf16 matrices, f32 vectors, i32 table) into the
+    C struct.  The tensors must outlive every call that uses the struct."""
+    return WeightsC(*[None if t is None else t.data_ptr()
+                      for t in (norm_w, router, sel_bias, tid2eid, gate, up, down, gate_sh, up_sh, down_sh)])
+
+
+def workspace_bytes(dims: Dims, rows: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_ffn_workspace_bytes(ctypes.byref(dims), int(rows), ctypes.byref(n)), "moe_ffn_workspace_bytes")
+    return n.value
+
+
+def alloc_workspace(dims: Dims, rows: int, device="cuda"):
+    import torch
+
+    return torch.empty(workspace_bytes(dims, rows), dtype=torch.uint8, device=device)
+
+
+def forward(dims: Dims, x, token_ids, layer_kind: int, weights: WeightsC, out, workspace, stream=None):
+    """``out[rows, hidden] = MoE-FFN(x)``; enqueue only."""
+    rows = x.shape[0]
+    rc = lib().moe_ffn_forward(ctypes.byref(dims), _ptr(x), _ptr(token_ids), rows, int(layer_kind),
+                               ctypes.byref(weights), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(rc, "moe_ffn_forward")
+    return out
+
+
+def route(dims: Dims, logits, token_ids, layer_kind: int, weights: WeightsC, idx, w, stream=None):
+    rc = lib().moe_route(ctypes.byref(dims), _ptr(logits), _ptr(token_ids), logits.shape[0], int(layer_kind),
+                         ctypes.byref(weights), _ptr(idx), _ptr(w), _stream(stream))
+    _check(rc, "moe_route")
+    return idx, w
+
+
+def routing_view(dims: Dims, rows: int, workspace):
+    """Device tensors (views into ``workspace``) of the last forward's
+    logits [rows, E], indices [rows, K] and weights [rows, K]."""
+    import torch
+
+    lp, ip, wp = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib().moe_ffn_routing_view(ctypes.byref(dims), int(rows), _ptr(workspace), workspace.numel(),
+                                      ctypes.byref(lp), ctypes.byref(ip), ctypes.byref(wp)), "moe_ffn_routing_view")
+    base = workspace.data_ptr()
+    E, K = dims.experts, dims.top_k
+
+    def view(p, n, dt):
+        off = p.value - base
+        return workspace[off:off + n * torch.tensor([], dtype=dt).element_size()].view(dt)
+
+    return (view(lp, rows * E, torch.float32).view(rows, E), view(ip, rows * K, torch.int32).view(rows, K),
+            view(wp, rows * K, torch.float32).view(rows, K))
+
+
+def status(workspace, stream=None) -> int:
+    f = ctypes.c_uint32(0)
+    _check(lib().moe_ffn_status(_ptr(workspace), _stream(stream), ctypes.byref(f)), "moe_ffn_status")
+    return f.value
+
+
+def stage_timing_begin():
+    _check(lib().moe_ffn_stage_timing_begin(), "moe_ffn_stage_timing_begin")
+
+
+def stage_timing_end(max_kernels: int = 32) -> dict:
+    """{kernel name: (total ms, launches)} since stage_timing_begin()."""
+    names = (ctypes.c_char_p * max_kernels)()
+    ms = (ctypes.c_double * max_kernels)()
+    cnt = (ctypes.c_int64 * max_kernels)()
+    n = ctypes.c_int(0)
+    _check(lib().moe_ffn_stage_timing_end(max_kernels, names, ms, cnt, ctypes.byref(n)), "moe_ffn_stage_timing_end")
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(min(n.value, max_kernels))}

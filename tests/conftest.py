@@ -16,3 +16,11 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def root_dir():
     return ROOT
+
+
+def pytest_sessionstart(session):
+    """Build the HIP library only if nothing is built yet."""
+    from mixture_experts_ffn_rmsnorm_amd import build, moe
+
+    if not os.path.exists(moe.LIB_PATH):
+        build.build(verbose=False)

@@ -1,0 +1,144 @@
+"""Shared helpers of the GPU parity tests: layers on the device, the
+oracle's view of the same weights, and the comparison rules."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from mixture_experts_ffn_rmsnorm_amd import inputs as gen
+from mixture_experts_ffn_rmsnorm_amd import moe
+from oracle import moe_ref as ref
+
+# spec bar for the layer output (bf16 weights, f32 accumulate)
+REL_L2 = 2e-3
+MAXABS = 1e-2
+# near-tie rule: a row whose GPU expert set differs from the oracle's is
+# accepted only if every swapped pair is within this oracle-key gap and the
+# row matches the oracle run with the GPU's routing
+TAU = 1e-5
+
+
+class Layer:
+    """One layer's parameters on the device plus the oracle view of them."""
+
+    def __init__(self, cfg: gen.Config, layer: int = 0, table=None, share=None):
+        """``share``: a Layer of the same parameters whose device expert
+        weights are reused instead of drawn again."""
+        import torch
+
+        self.cfg = cfg
+        self.layer = layer
+        dev = "cuda"
+        hi = gen.host_inputs(cfg, layer=layer)
+        self.host = hi
+        if table is not None:
+            hi.tid2eid = table
+        t = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        self.norm_w = t(hi.norm_w)
+        self.router = t(hi.router.view(np.int16)).view(torch.bfloat16)
+        self.bias = t(hi.sel_bias)
+        self.table = t(hi.tid2eid) if hi.tid2eid is not None else None
+        if cfg.hidden == 4096:
+            if share is not None:
+                assert share.cfg.param_seed == cfg.param_seed and share.layer == layer
+                self.gate, self.up, self.down = share.gate, share.up, share.down
+                self.gs, self.us, self.ds = share.gs, share.us, share.ds
+                self._cache = share._cache
+            else:
+                (self.gate, self.up, self.down), (self.gs, self.us, self.ds) = \
+                    gen.expert_weights_device(cfg, dev, layer)
+                self._cache = {}
+
+            def expert(e):
+                if e not in self._cache:
+                    self._cache[e] = tuple(gen.bf16_tensor_bits(m[e]) for m in (self.gate, self.up, self.down))
+                return self._cache[e]
+
+            shared = tuple(gen.bf16_tensor_bits(m) for m in (self.gs, self.us, self.ds))
+        else:
+            G, U, D = gen.all_experts_host(cfg, layer)
+            sh = gen.shared_host(cfg, layer)
+            b16 = lambda a: t(a.view(np.int16)).view(torch.bfloat16)
+            self.gate, self.up, self.down = b16(G), b16(U), b16(D)
+            self.gs, self.us, self.ds = (b16(m) for m in sh)
+            expert = lambda e: (G[e], U[e], D[e])
+            shared = sh
+        self.oracle_w = ref.Weights(hi.norm_w, hi.router, hi.sel_bias, hi.tid2eid, expert, shared)
+        self.dims = moe.dims_of(cfg)
+        self.cw = moe.make_weights(self.norm_w, self.router, self.bias, self.table, self.gate, self.up, self.down,
+                                   self.gs, self.us, self.ds)
+
+    def with_table(self, table_np):
+        """Same layer, another hash table (device + oracle)."""
+        import torch
+
+        self.table = torch.from_numpy(np.ascontiguousarray(table_np, dtype=np.int32)).cuda()
+        self.cw = moe.make_weights(self.norm_w, self.router, self.bias, self.table, self.gate, self.up, self.down,
+                                   self.gs, self.us, self.ds)
+        w = self.oracle_w
+        self.oracle_w = ref.Weights(w.norm_w, w.router, w.sel_bias, table_np, w.expert, w.shared)
+        return self
+
+    def run(self, x_np, tok_np, kind, workspace=None):
+        """GPU forward; returns (out, logits, idx, w, status) as numpy."""
+        import torch
+
+        R = x_np.shape[0]
+        x = torch.from_numpy(np.ascontiguousarray(x_np, dtype=np.float32)).cuda()
+        tok = torch.from_numpy(np.ascontiguousarray(tok_np, dtype=np.int32)).cuda() if tok_np is not None else None
+        out = torch.full((R, self.cfg.hidden), float("nan"), dtype=torch.float32, device="cuda")
+        ws = moe.alloc_workspace(self.dims, R) if workspace is None else workspace
+        moe.forward(self.dims, x, tok, kind, self.cw, out, ws)
+        lg, idx, w = moe.routing_view(self.dims, R, ws)
+        st = moe.status(ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), st
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def check_output(out, ref_out, rel=REL_L2, maxabs=MAXABS, what=""):
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    r = rel_l2(out, ref_out)
+    m = float(np.abs(out - ref_out).max() / max(np.abs(ref_out).max(), 1e-300))
+    assert r <= rel and m <= maxabs, f"{what}: relL2 {r:.3e} (bar {rel:.1e}) maxabs/max|ref| {m:.3e} (bar {maxabs:.1e})"
+    return r, m
+
+
+def check_routing_exact(layer: Layer, lg_gpu, idx_gpu, w_gpu, tok, kind, rows=None):
+    """The GPU routing equals the oracle's routing of the GPU's own logits:
+    indices bit-exact, weights to f32 rounding."""
+    K = layer.cfg.top_k
+    sel = slice(None) if rows is None else rows
+    o_idx, o_w, o_valid = ref.route(lg_gpu[sel].astype(np.float64), None if tok is None else tok[sel], kind,
+                                    layer.oracle_w, K)
+    np.testing.assert_array_equal(idx_gpu[sel], o_idx)
+    np.testing.assert_allclose(w_gpu[sel], o_w, rtol=2e-7, atol=1e-9)
+
+
+def check_forward(layer: Layer, x, tok, kind, out, lg, idx, w, rows=None, rel=REL_L2, maxabs=MAXABS,
+                  logit_atol=2e-5):
+    """End-to-end comparison on `rows` (all if None) with the near-tie rule."""
+    cfg = layer.cfg
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    res = ref.forward(x[rows], None if tok is None else tok[rows], kind, layer.oracle_w, cfg.top_k, cfg.eps)
+    np.testing.assert_allclose(lg[rows], res["logits"], rtol=0, atol=logit_atol)
+    check_routing_exact(layer, lg, idx, w, tok, kind, rows)
+    ref_out = res["out"].copy()
+    near = 0
+    for j, r in enumerate(rows):
+        if set(idx[r].tolist()) != set(res["idx"][j].tolist()):
+            assert kind == ref.LAYER_SCORE
+            sig = ref.sigmoid(res["logits"][j])
+            key = sig + layer.oracle_w.sel_bias.astype(np.float64)
+            a, b = set(idx[r].tolist()), set(res["idx"][j].tolist())
+            for e1 in a - b:
+                for e2 in b - a:
+                    assert abs(key[e1] - key[e2]) <= TAU, f"row {r}: expert set differs beyond a near tie"
+            ref_out[j] = ref.forward_given_routing(res["xn"][j:j + 1], idx[r:r + 1], w[r:r + 1].astype(np.float64),
+                                                   np.ones((1, cfg.top_k), bool), layer.oracle_w)[0]
+            near += 1
+    check_output(out[rows], ref_out, rel, maxabs, what=f"{cfg.name} rows={len(rows)}")
+    return near
