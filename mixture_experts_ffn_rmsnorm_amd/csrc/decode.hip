@@ -27,13 +27,16 @@ constexpr int kTileRows = 16;  // weight rows per block for gate/up (per matrix)
 
 // Per-lane partial dot products of NW bf16 weight rows against up to 4
 // activation rows (f32, LDS or global).  Lane l covers 8 consecutive
-// columns of every 512-column chunk.
+// columns of every 512-column chunk; when LEN is not a multiple of 512 the
+// lanes past the end of the last chunk sit it out.
 template <int NW, int LEN>
 __device__ __forceinline__ void wave_gemv(const uint16_t* const (&w)[NW], const float* const (&xr)[4], int nr,
                                           float (&acc)[NW][4]) {
+  static_assert(LEN % 256 == 0, "row length must be a multiple of 256");
   const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
   for (int c = 0; c < LEN; c += 512) {
+    if (LEN % 512 != 0 && c + lane * 8 >= LEN) break;
     uint4 q[NW];
 #pragma unroll
     for (int n = 0; n < NW; ++n) q[n] = load_stream(w[n] + c + lane * 8);
