@@ -38,15 +38,19 @@ def log(msg):
 
 def alg_bytes(kernel, cfg, U, R):
     """Algorithmic HBM bytes of one launch: every touched weight once, plus
-    activations in and out (U = distinct routed experts of the step)."""
+    activations in and out (U = distinct routed experts of the step; a
+    routed (expert, row) pair per slot, R*K of them)."""
     H, I, E, K = cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
     x = R * H * 4
-    if kernel == "dec_router_shared":
-        return E * H * 2 + 2 * I * H * 2 + x + H * 4 + R * E * 4 + R * I * 4
-    if kernel == "dec_gateup":
-        return U * 2 * I * H * 2 + R * H * 4 + min(R * K, U * R) * I * 4
-    if kernel == "dec_down_reduce":
-        return (U + 1) * H * I * 2 + (min(R * K, U * R) + R) * I * 4 + R * H * 4
+    ent = R * K + R  # routed (expert, row) pairs + shared rows
+    if kernel == "dec_router_shared":  # router + routing/plan + shared gate/up
+        return E * H * 2 + 2 * I * H * 2 + 2 * x + H * 4 + R * E * 12 + R * (H + I) * 4
+    if kernel == "dec_gateup":          # routed experts' gate/up
+        return U * 2 * I * H * 2 + R * K * (H + I) * 4
+    if kernel == "dec_down":            # routed + shared down
+        return (U + 1) * H * I * 2 + ent * (I + H) * 4
+    if kernel == "dec_reduce":
+        return ent * H * 4 + x
     if kernel == "gemm_gateup_swiglu":
         S = R * K
         return (U + 1) * 2 * I * H * 2 + (S + R) * H * 2 + (S + R) * I * 2
@@ -133,18 +137,25 @@ def main():
         U.append(len(np.unique(idx[(idx >= 0) & (idx < cfg.experts)])))
     log(f"distinct routed experts per layer: {U}")
 
+    # throughput pass: the timed region, plain launches
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
-    moe.stage_timing_begin()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    stages = moe.stage_timing_end()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = R / (ms_per_step / 1e3)
     u_mean = float(np.mean([U[i % L] for i in range(args.steps)]))
+    # kernel pass: the same steps again, each kernel bracketed by HIP
+    # start/stop events taken at the kernel's own start and end
+    log("timing kernels")
+    moe.stage_timing_begin()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    stages = moe.stage_timing_end()
 
     kernels = {}
     for name, (ms, n) in stages.items():

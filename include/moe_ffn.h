@@ -57,8 +57,11 @@ enum { MOE_LAYER_SCORE = 0, MOE_LAYER_HASH = 1 };
 enum {
   MOE_FLAG_BAD_TOKEN = 1u,      /* a hash-layer token id outside [0, table_rows):
                                    all of that row's slots were masked      */
-  MOE_FLAG_BAD_TABLE_ENTRY = 2u /* a table entry outside [0, experts): that
-                                   slot was masked                          */
+  MOE_FLAG_BAD_TABLE_ENTRY = 2u, /* a table entry outside [0, experts): that
+                                    slot was masked                         */
+  MOE_FLAG_SYNC_TIMEOUT = 4u     /* an in-kernel wait for other workgroups
+                                    gave up (only if the GPU could not run
+                                    the whole grid); the output is invalid  */
 };
 
 /* Layer dimensions.  ffn_forward.rs guards the native path with fixed

@@ -8,6 +8,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <math.h>
 #include <mutex>
 #include <string.h>
@@ -80,6 +82,16 @@ struct StageTimer {
 StageTimer& timer() {
   static StageTimer t;
   return t;
+}
+
+// Per-call tag the decode router blocks publish when their logits are
+// written: a process-wide counter seeded from the clock, never 0, so a flag
+// left in the workspace by an earlier call (or by anything else) does not
+// match the current call.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> ctr{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
+  uint32_t e = ctr.fetch_add(1, std::memory_order_relaxed);
+  return e ? e : ctr.fetch_add(1, std::memory_order_relaxed);
 }
 
 }  // namespace
@@ -156,7 +168,10 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
   a.down_sh = w->down_sh;
   a.out = out;
   a.status = (uint32_t*)(ws + L.status);
+  a.route_flags = (uint32_t*)(ws + L.status + 64);
+  a.epoch = next_epoch();
   a.logits = (float*)(ws + L.logits);
+  a.key = (double*)(ws + L.key);
   a.idx = (int32_t*)(ws + L.idx);
   a.wts = (float*)(ws + L.wts);
   a.rowflags = (uint32_t*)(ws + L.rowflags);
@@ -165,6 +180,7 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
     a.xn32 = (float*)(ws + L.xn32);
     a.plan = (DecodePlan*)(ws + L.plan);
     a.h32 = (float*)(ws + L.h32);
+    a.d32 = (float*)(ws + L.d32);
   } else {
     a.xn16 = (_Float16*)(ws + L.xn16);
     a.cnt = (int32_t*)(ws + L.cnt);

@@ -1,21 +1,27 @@
-// Decode path (1..4 rows): the layer is a stream of expert weights read once
-// from HBM, so every projection is a wavefront GEMV with f32 activations
-// held in LDS and bf16 weights widened in registers.
+// Decode path (1..4 rows).  The layer is a stream of expert weights read
+// once from HBM: every projection is a wavefront GEMV whose f32 activations
+// sit in LDS while bf16 weight rows stream through registers, each row read
+// front to back with the next rows already requested (activation reads use
+// the LDS counter, so they never wait behind the weight loads).
 //
-//   k_dec_router_shared  RMSNorm + router logits (one expert per wave) and,
-//                        in the same grid, the shared expert's gate/up +
-//                        SwiGLU (it needs no routing)
-//   k_dec_gateup         routing prologue (top-k or hash, distinct experts
-//                        of the batch), then gate/up + SwiGLU of the routed
-//                        experts, one (expert, 16 inter rows) tile per block
-//   k_dec_down           down projections of routed + shared experts with
-//                        the weighted reduce fused: each block owns 16 output
-//                        columns and sums every expert's contribution in a
-//                        fixed order, so no atomics and bitwise-stable output
+//   k_dec_router   blocks [0, E/4): RMSNorm (f32) and router logits, one
+//                  expert per wave, plus the score layer's float64 selection
+//                  keys sigmoid(l) + bias.  Then the shared expert's gate/up
+//                  + SwiGLU, which needs no routing and covers the router's
+//                  latency.  A last block waits for the router blocks' flags,
+//                  routes the batch (top-k over the keys, or the hash table)
+//                  and writes the plan of distinct (expert, row) pairs
+//   k_dec_gateup   routed gate/up + SwiGLU, one (expert, 16 inter rows) tile
+//                  per block
+//   k_dec_down     down projection of one group (shared or routed expert)
+//                  for 32 hidden rows -> f32 per (expert, row) pair
+//   k_dec_reduce   out[r] = sum of weight * down over r's pairs + shared
+//                  down, in a fixed order (no atomics)
 //
 // Stage order follows forward_ffn_rows on the hf2q ffn_forward.rs page
 // (rms_norm -> MoE gate -> route -> sanitize -> routed/shared gate, up ->
-// swiglu -> routed/shared down -> weighted reduce).
+// swiglu -> routed/shared down -> weighted reduce); the page's rows*top_k
+// one-expert matvecs become one pass over the batch's distinct experts.
 #include "device.h"
 #include "kernels.h"
 
@@ -23,39 +29,66 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileRows = 16;  // weight rows per block for gate/up (per matrix) and down
+constexpr int kGuRows = 16;     // inter rows per routed gate/up block (x2 matrices): 4 waves x 4
+constexpr int kShRows = 8;      // inter rows per shared gate/up block: 4 waves x 2
+constexpr int kRedCols = 1024;  // output columns per reduce block
+constexpr int kDnRows = 32;     // hidden rows per down block: 4 waves x 8
 
-// Per-lane partial dot products of NW bf16 weight rows against up to 4
-// activation rows (f32, LDS or global).  Lane l covers 8 consecutive
-// columns of every 512-column chunk; when LEN is not a multiple of 512 the
-// lanes past the end of the last chunk sit it out.
-template <int NW, int LEN>
-__device__ __forceinline__ void wave_gemv(const uint16_t* const (&w)[NW], const float* const (&xr)[4], int nr,
-                                          float (&acc)[NW][4]) {
+// One wavefront walks a sequence of whole bf16 weight rows (global) and dots
+// each with up to 4 f32 activation rows in LDS (row r at act + r*LEN).  Each
+// row is read front to back as contiguous 1 KiB wave loads; NBUF rows are in
+// flight (the next ones load while the current one is multiplied), which
+// keeps the DRAM streams long.  Lane l covers 8 consecutive columns of every
+// 512-column chunk; lanes past the end of a partial chunk (LEN not a
+// multiple of 512) neither load nor add.  rowptr(j) gives row j's address;
+// pre() runs once after the first NBUF rows are requested (staging the
+// activations there overlaps it with the first weight fetch; it must end
+// with a barrier if it fills LDS); sink(j, part) receives each lane's
+// partial sums part[0..nr) of row j (reduce them with wave_sum).
+template <int LEN, int NBUF, class RowPtr, class Pre, class Sink>
+__device__ __forceinline__ void stream_rows(int nrows, RowPtr rowptr, const float* act, int nr, Pre pre, Sink sink) {
   static_assert(LEN % 256 == 0, "row length must be a multiple of 256");
+  constexpr int NCH = (LEN + 511) / 512;
   const int lane = threadIdx.x & (kWave - 1);
+  const bool full = LEN % 512 == 0 || lane * 8 < LEN % 512;  // active in the last chunk
+  uint4 q[NBUF][NCH];
+  auto load_row = [&](int b, int j) {
+    const uint16_t* p = rowptr(j) + lane * 8;
 #pragma unroll
-  for (int c = 0; c < LEN; c += 512) {
-    if (LEN % 512 != 0 && c + lane * 8 >= LEN) break;
-    uint4 q[NW];
+    for (int c = 0; c < NCH; ++c)
+      if (c < NCH - 1 || full) q[b][c] = load_stream(p + c * 512);
+  };
 #pragma unroll
-    for (int n = 0; n < NW; ++n) q[n] = load_stream(w[n] + c + lane * 8);
+  for (int b = 0; b < NBUF; ++b)
+    if (b < nrows) load_row(b, b);
+  pre();
+#pragma unroll 1
+  for (int j0 = 0; j0 < nrows; j0 += NBUF) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (r < nr) {
-        const float4* xp = (const float4*)(xr[r] + c + lane * 8);
-        const float4 a = xp[0], b = xp[1];
+    for (int b = 0; b < NBUF; ++b) {
+      const int j = j0 + b;
+      if (j < nrows) {
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int n = 0; n < NW; ++n) {
-          float f[8];
-          unpack8(q[n], f);
-          float s = acc[n][r];
-          s = fmaf(f[0], a.x, s); s = fmaf(f[1], a.y, s);
-          s = fmaf(f[2], a.z, s); s = fmaf(f[3], a.w, s);
-          s = fmaf(f[4], b.x, s); s = fmaf(f[5], b.y, s);
-          s = fmaf(f[6], b.z, s); s = fmaf(f[7], b.w, s);
-          acc[n][r] = s;
+        for (int c = 0; c < NCH; ++c) {
+          if (c < NCH - 1 || full) {
+            float f[8];
+            unpack8(q[b][c], f);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (r < nr) {
+                const float4* xp = (const float4*)(act + r * LEN + c * 512 + lane * 8);
+                const float4 u = xp[0], v = xp[1];
+                float s = part[r];
+                s = fmaf(f[0], u.x, s); s = fmaf(f[1], u.y, s); s = fmaf(f[2], u.z, s); s = fmaf(f[3], u.w, s);
+                s = fmaf(f[4], v.x, s); s = fmaf(f[5], v.y, s); s = fmaf(f[6], v.z, s); s = fmaf(f[7], v.w, s);
+                part[r] = s;
+              }
+            }
+          }
         }
+        if (j + NBUF < nrows) load_row(b, j + NBUF);
+        sink(j, part);
       }
     }
   }
@@ -102,62 +135,52 @@ __device__ __forceinline__ void norm_rows_to_lds(const float* __restrict__ x, co
   __syncthreads();
 }
 
-// ---------------------------------------------------------------------------
-// Router logits + shared-expert gate/up.  Blocks [0, nrb) compute logits for
-// 4 experts each (one per wave); blocks [nrb, nrb + I/16) compute 16 rows of
-// the shared expert's SwiGLU output for every batch row.
-template <int H, int I>
-__global__ __launch_bounds__(kThreads) void k_dec_router_shared(const FwdArgs a) {
-  extern __shared__ float xs[];  // [R][H]
-  const int R = a.R;
-  norm_rows_to_lds<H>(a.x, a.norm_w, R, a.eps, xs);
+// Copy `nr` rows of LEN floats (global rows src[j]) into LDS rows dst + j*LEN.
+template <int LEN>
+__device__ __forceinline__ void stage_rows(float* dst, const float* const (&src)[4], int nr) {
+#pragma unroll 1
+  for (int j = 0; j < nr; ++j)
+    for (int i = threadIdx.x; i < LEN / 4; i += kThreads) ((float4*)(dst + j * LEN))[i] = ((const float4*)src[j])[i];
+  __syncthreads();
+}
+
+// Gate/up + SwiGLU of PAIRS inter rows of one expert for the `nr` activation
+// rows in LDS: tile x of `tiles` takes rows x, x + tiles, x + 2*tiles, ...,
+// so the blocks working on one expert at the same time read neighbouring
+// rows; wave w streams gate_i then up_i for every fourth of them.  h32 rows
+// hout..hout+nr-1 receive silu(gate . x) * (up . x).
+template <int H, int I, int PAIRS, class Pre>
+__device__ __forceinline__ void gateup_tile(const uint16_t* gbase, const uint16_t* ubase, const float* xs, int nr,
+                                            int x, int tiles, float* h32, int hout, Pre pre) {
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int nrb = (a.E + 3) / 4;
-  if (blockIdx.x == 0) {  // publish xn for the routed gate/up kernel
-    for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
-  }
-  const float* xr[4] = {xs, xs + (R > 1 ? H : 0), xs + (R > 2 ? 2 * H : 0), xs + (R > 3 ? 3 * H : 0)};
-  if ((int)blockIdx.x < nrb) {
-    const int e = blockIdx.x * 4 + wv;
-    if (e >= a.E) return;
-    const uint16_t* w[1] = {a.router + (int64_t)e * H};
-    float acc[1][4] = {};
-    wave_gemv<1, H>(w, xr, R, acc);
+  constexpr int W = kThreads / kWave;
+  float g[4];
+  auto row_of = [&](int j) { return x + (wv + (j >> 1) * W) * tiles; };
+  auto rowptr = [&](int j) { return ((j & 1) ? ubase : gbase) + (int64_t)row_of(j) * H; };
+  auto sink = [&](int j, const float (&part)[4]) {
+    if (!(j & 1)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) g[r] = part[r];
+      return;
+    }
+    const int i = row_of(j);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if (r < R) {
-        float v = wave_sum(acc[0][r]);
-        if (lane == 0) a.logits[(int64_t)r * a.E + e] = v;
+      if (r < nr) {
+        const float gs = wave_sum(g[r]);
+        const float us = wave_sum(part[r]);
+        if (lane == 0) h32[(int64_t)(hout + r) * I + i] = swiglu_f32(gs, us);
       }
     }
-    return;
-  }
-  const int i0 = (blockIdx.x - nrb) * kTileRows + wv * 4;
-  const uint16_t* w[8];
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    w[n] = a.gate_sh + (int64_t)(i0 + n) * H;
-    w[4 + n] = a.up_sh + (int64_t)(i0 + n) * H;
-  }
-  float acc[8][4] = {};
-  wave_gemv<8, H>(w, xr, R, acc);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (r < R) {
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        float g = wave_sum(acc[n][r]);
-        float u = wave_sum(acc[4 + n][r]);
-        if (lane == 0) a.h32[(int64_t)(kDecodeMaxSlots + r) * I + i0 + n] = swiglu_f32(g, u);
-      }
-    }
-  }
+  };
+  stream_rows<H, 2>(2 * (PAIRS / W), rowptr, xs, nr, pre, sink);
 }
 
 // Distinct (expert, row) pairs of the batch, grouped by expert (ascending),
 // rows ascending inside a group; duplicate slots of one row (possible only
 // with a malformed hash table) merge by summing their weights.  Runs on
-// wave 0; inputs in LDS.
+// wave 0 with lane s holding slot s; every comparison walks the S slots with
+// uniform readlane broadcasts.
 __device__ void build_plan(const int* s_idx, const float* s_w, const unsigned char* s_valid, int R, int K, int E,
                            DecodePlan* P) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -176,28 +199,30 @@ __device__ void build_plan(const int* s_idx, const float* s_w, const unsigned ch
   bool first = v;
   float wsum = 0.f;
   for (int t = 0; t < S; ++t) {
-    int kt = __shfl(key, t, kWave);
-    float wt = __shfl(w, t, kWave);
+    const int kt = __builtin_amdgcn_readlane(key, t);
+    const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), t));
     if (v && kt == key) {
       wsum += wt;
       if (t < lane) first = false;
     }
   }
-  int pos = 0, gidx = 0;
+  const uint64_t fmask = __ballot(first);
+  int pos = 0;
   bool efirst = first;
   for (int t = 0; t < S; ++t) {
-    int ft = __shfl((int)first, t, kWave);
-    int kt = __shfl(key, t, kWave);
-    if (ft && kt < key) ++pos;
-    if (ft && (kt >> 3) == (key >> 3) && kt < key) efirst = false;
+    if (!((fmask >> t) & 1)) continue;
+    const int kt = __builtin_amdgcn_readlane(key, t);
+    if (kt < key) ++pos;
+    if ((kt >> 3) == (key >> 3) && kt < key) efirst = false;
   }
+  const uint64_t emask = __ballot(efirst);
+  int gidx = 0;
   for (int t = 0; t < S; ++t) {
-    int eft = __shfl((int)efirst, t, kWave);
-    int kt = __shfl(key, t, kWave);
-    if (eft && (kt >> 3) < (key >> 3)) ++gidx;
+    if (!((emask >> t) & 1)) continue;
+    if ((__builtin_amdgcn_readlane(key, t) >> 3) < (key >> 3)) ++gidx;
   }
-  const int ngroups = __popcll(__ballot(efirst));
-  const int nentries = __popcll(__ballot(first));
+  const int ngroups = __popcll(emask);
+  const int nentries = __popcll(fmask);
   if (first) {
     P->entry_row[pos] = r;
     P->entry_w[pos] = wsum;
@@ -213,87 +238,279 @@ __device__ void build_plan(const int* s_idx, const float* s_w, const unsigned ch
   }
 }
 
+// Routing of the batch into LDS: wave w < R routes row w from the logits
+// (and, for score layers, the keys) that the router waves wrote through to
+// memory; they are read with agent-scope loads, which do not hit stale lines.
+__device__ void route_rows(const FwdArgs& a, int* s_idx, float* s_w, unsigned char* s_valid, uint32_t* s_flags) {
+  const int R = a.R, K = a.K, E = a.E;
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  if (wv >= R) return;
+  RowRoute rr;
+  float lgv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + kWave * j;
+    lgv[j] = (e < E) ? __hip_atomic_load(&a.logits[(int64_t)wv * E + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     : 0.f;
+  }
+  if (a.layer_kind == MOE_LAYER_HASH) {
+    rr = hash_route_lanes(lgv, E, K, a.table, a.table_rows, a.token_ids[wv]);
+  } else {
+    double key[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + kWave * j;
+      key[j] = (e < E) ? __hip_atomic_load(&a.key[(int64_t)wv * E + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : 0.0;
+    }
+    rr = score_route_keys(key, lgv, E, K);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+      if (k < K) {
+        s_idx[wv * K + k] = rr.idx[k];
+        s_w[wv * K + k] = rr.w[k];
+        s_valid[wv * K + k] = rr.valid[k];
+      }
+    }
+    s_flags[wv] = rr.flags;
+  }
+}
+
+// Spin limit of the plan block's wait for the router blocks' flags (each
+// poll is a device-scope load, about a microsecond: roughly 0.25 s in all);
+// reaching it sets MOE_FLAG_SYNC_TIMEOUT instead of hanging.
+constexpr int kMaxPolls = 1 << 18;
+
 // ---------------------------------------------------------------------------
-// Routing prologue + routed gate/up + SwiGLU.  grid = (I/16, max groups).
+// Router + plan + shared gate/up.  grid = E/4 router blocks, I/8 shared
+// blocks, then one plan block.
+//   Router wave (expert e = 4b + w): reads its router row, x and g directly
+//   and forms logit[r,e] = (sum_j W[e,j] x[r,j] g[j]) * (mean_j x[r,j]^2 +
+//   eps)^-1/2 -- the RMSNorm factor is per row, so it is applied after the
+//   dot product and the wave needs no block-wide norm.  It stores the logits
+//   and (score layers) the float64 keys sigmoid(logit) + bias with
+//   write-through (agent-scope) stores, waits for them to complete and only
+//   then stores flag[e] = this call's epoch.
+//   Shared blocks: RMSNorm into LDS, then 8 inter rows of the shared
+//   expert's SwiGLU output for every row; block nrb also publishes xn.
+//   Plan block (dispatched last, so every router block is already running):
+//   waits until all flags carry the epoch, routes the batch from the logits
+//   and keys (read write-through), publishes indices, weights, row flags,
+//   status and the plan, and clears the flags so a replay of the same launch
+//   waits again.
 template <int H, int I>
-__global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
+__global__ __launch_bounds__(kThreads) void k_dec_router(const FwdArgs a) {
+  extern __shared__ float xs[];  // [R][H]
   __shared__ int s_idx[kDecodeMaxSlots];
   __shared__ float s_w[kDecodeMaxSlots];
   __shared__ unsigned char s_valid[kDecodeMaxSlots];
   __shared__ uint32_t s_flags[kDecodeMaxRows];
   __shared__ DecodePlan P;
-  const int R = a.R, K = a.K;
+  __shared__ uint32_t s_timeout;
+  const int R = a.R, E = a.E, K = a.K;
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  if (wv < R) {
-    const int32_t tok = (a.layer_kind == MOE_LAYER_HASH) ? a.token_ids[wv] : 0;
-    RowRoute rr = route_row(a.logits + (int64_t)wv * a.E, a.E, K, a.layer_kind, a.bias, a.table, a.table_rows, tok);
-    if (lane == 0) {
+  const int nrb = (E + 3) / 4;
+  if ((int)blockIdx.x == (int)gridDim.x - 1) {  // the plan block
+    if (wv == 0) {
+      bool ready = false;
+      int polls = 0;
+      while (!ready) {
+        bool mine = true;
 #pragma unroll
-      for (int k = 0; k < kMaxTopK; ++k) {
-        if (k < K) {
-          s_idx[wv * K + k] = rr.idx[k];
-          s_w[wv * K + k] = rr.w[k];
-          s_valid[wv * K + k] = rr.valid[k];
+        for (int j = 0; j < kMaxExperts / kWave; ++j) {
+          const int e = lane + kWave * j;
+          if (e < E) mine &= __hip_atomic_load(&a.route_flags[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+        }
+        ready = __ballot(!mine) == 0;
+        if (!ready) {
+          if (++polls >= kMaxPolls) break;
+          __builtin_amdgcn_s_sleep(1);
         }
       }
-      s_flags[wv] = rr.flags;
+      if (lane == 0) s_timeout = ready ? 0u : (uint32_t)MOE_FLAG_SYNC_TIMEOUT;
     }
-  }
-  __syncthreads();
-  if (wv == 0) build_plan(s_idx, s_w, s_valid, R, K, a.E, &P);
-  __syncthreads();
-  const int u = blockIdx.y;
-  if (blockIdx.x == 0 && u == 0) {  // publish routing, plan and status once
+    __syncthreads();
+    route_rows(a, s_idx, s_w, s_valid, s_flags);
+    __syncthreads();
+    if (wv == 0) build_plan(s_idx, s_w, s_valid, R, K, E, &P);
+    __syncthreads();
     for (int s = threadIdx.x; s < R * K; s += kThreads) {
       a.idx[s] = s_idx[s];
       a.wts[s] = s_w[s];
     }
     if (threadIdx.x < R) a.rowflags[threadIdx.x] = s_flags[threadIdx.x];
     if (threadIdx.x == 0) {
-      uint32_t f = 0;
+      uint32_t f = s_timeout;
       for (int r = 0; r < R; ++r) f |= s_flags[r];
       a.status[0] = f;
     }
-    const int* src = (const int*)&P;
-    int* dst = (int*)a.plan;
-    for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += kThreads) dst[i] = src[i];
+    for (int e = threadIdx.x; e < E; e += kThreads)
+      __hip_atomic_store(&a.route_flags[e], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int* ps = (const int*)&P;
+    int* pd = (int*)a.plan;
+    for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += kThreads) pd[i] = ps[i];
+    return;
   }
-  if (u >= P.ngroups) return;
-  const int e = P.group_expert[u];
-  const int b = P.group_begin[u], nr = P.group_begin[u + 1] - b;
-  // activations of this group's rows straight from xn32 (L2-resident)
-  const float* xr[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) xr[j] = a.xn32 + (int64_t)P.entry_row[b + (j < nr ? j : 0)] * H;
-  const int i0 = blockIdx.x * kTileRows + wv * 4;
-  const uint16_t* w[8];
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    w[n] = a.gate + ((int64_t)e * I + i0 + n) * H;
-    w[4 + n] = a.up + ((int64_t)e * I + i0 + n) * H;
+  if ((int)blockIdx.x >= nrb) {
+    auto stage = [&]() {
+      norm_rows_to_lds<H>(a.x, a.norm_w, R, a.eps, xs);
+      if ((int)blockIdx.x == nrb)
+        for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
+    };
+    gateup_tile<H, I, kShRows>(a.gate_sh, a.up_sh, xs, R, blockIdx.x - nrb, I / kShRows, a.h32, kDecodeMaxSlots,
+                               stage);
+    return;
   }
-  float acc[8][4] = {};
-  wave_gemv<8, H>(w, xr, nr, acc);
+  // router wave: whole row of W[e] (8 loads) plus x and g straight from memory
+  const int e = blockIdx.x * 4 + wv;
+  if (e >= E) return;
+  constexpr int NCH = (H + 511) / 512;
+  const bool full = H % 512 == 0 || lane * 8 < H % 512;
+  uint4 q[NCH];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (j < nr) {
+  for (int c = 0; c < NCH; ++c)
+    if (c < NCH - 1 || full) q[c] = load_stream(a.router + (int64_t)e * H + c * 512 + lane * 8);
+  float dot[kDecodeMaxRows] = {0.f, 0.f, 0.f, 0.f}, ss[kDecodeMaxRows] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        float g = wave_sum(acc[n][j]);
-        float uu = wave_sum(acc[4 + n][j]);
-        if (lane == 0) a.h32[(int64_t)(b + j) * I + i0 + n] = swiglu_f32(g, uu);
+  for (int c = 0; c < NCH; ++c) {
+    if (c < NCH - 1 || full) {
+      const int col = c * 512 + lane * 8;
+      const float4 g0 = *(const float4*)(a.norm_w + col), g1 = *(const float4*)(a.norm_w + col + 4);
+      float f[8];
+      unpack8(q[c], f);
+      const float wg[8] = {f[0] * g0.x, f[1] * g0.y, f[2] * g0.z, f[3] * g0.w,
+                           f[4] * g1.x, f[5] * g1.y, f[6] * g1.z, f[7] * g1.w};
+#pragma unroll
+      for (int r = 0; r < kDecodeMaxRows; ++r) {
+        if (r < R) {
+          const float4 x0 = *(const float4*)(a.x + (int64_t)r * H + col);
+          const float4 x1 = *(const float4*)(a.x + (int64_t)r * H + col + 4);
+          const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            dot[r] = fmaf(wg[i], xv[i], dot[r]);
+            ss[r] = fmaf(xv[i], xv[i], ss[r]);
+          }
+        }
       }
     }
   }
+#pragma unroll
+  for (int r = 0; r < kDecodeMaxRows; ++r) {
+    if (r < R) {
+      const float d = wave_sum(dot[r]);
+      const float q2 = wave_sum(ss[r]);
+      if (lane == 0) {
+        const float v = d * (1.0f / sqrtf(q2 / (float)H + a.eps));
+        __hip_atomic_store(&a.logits[(int64_t)r * E + e], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (a.layer_kind == MOE_LAYER_SCORE)
+          __hip_atomic_store(&a.key[(int64_t)r * E + e], score_key(v, a.bias[e]), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if (lane == 0) {
+    // the write-through stores above have completed before the flag is stored
+    __builtin_amdgcn_s_waitcnt(0);
+    __hip_atomic_store(&a.route_flags[e], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The plan as read by the later kernels, every field clamped to its range
+// so that no value can index outside the buffers.
+struct PlanGroup {
+  int expert, begin, nr;
+};
+__device__ __forceinline__ int plan_ngroups(const DecodePlan* P) {
+  const int n = P->ngroups;
+  return n < 0 ? 0 : (n > kDecodeMaxSlots ? kDecodeMaxSlots : n);
+}
+__device__ __forceinline__ PlanGroup plan_group(const DecodePlan* P, int u, int E) {
+  PlanGroup g;
+  const int e = P->group_expert[u];
+  g.expert = e < 0 ? 0 : (e >= E ? E - 1 : e);
+  int b = P->group_begin[u], n = P->group_begin[u + 1];
+  b = b < 0 ? 0 : (b > kDecodeMaxSlots - 1 ? kDecodeMaxSlots - 1 : b);
+  n = n - b;  // n <= 0 (only from a corrupt plan) just means no rows
+  n = n > kDecodeMaxRows ? kDecodeMaxRows : n;
+  if (b + n > kDecodeMaxSlots) n = kDecodeMaxSlots - b;
+  g.begin = b;
+  g.nr = n;
+  return g;
+}
+__device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R) {
+  const int r = P->entry_row[j];
+  return r < 0 ? 0 : (r >= R ? R - 1 : r);
 }
 
 // ---------------------------------------------------------------------------
-// Down projections + weighted reduce.  grid = H/16; each wave owns 4 output
-// columns and, per lane, accumulates weight * partial dot over every group
-// (routed experts in ascending id, then the shared expert with weight 1),
-// reducing across the wave once at the end.
+// Routed gate/up + SwiGLU.  grid = (I/16, max distinct routed experts); block
+// (x, u) handles inter rows 16x..16x+15 of the plan's u-th expert.
+template <int H, int I>
+__global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
+  extern __shared__ float xs[];  // [nr][H]
+  const DecodePlan* P = a.plan;
+  const int u = blockIdx.y;
+  if (u >= plan_ngroups(P)) return;
+  const PlanGroup g = plan_group(P, u, a.E);
+  const float* src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) src[j] = a.xn32 + (int64_t)plan_row(P, g.begin + (j < g.nr ? j : 0), a.R) * H;
+  gateup_tile<H, I, kGuRows>(a.gate + (int64_t)g.expert * I * H, a.up + (int64_t)g.expert * I * H, xs, g.nr,
+                             blockIdx.x, I / kGuRows, a.h32, g.begin, [&]() { stage_rows<H>(xs, src, g.nr); });
+}
+
+// ---------------------------------------------------------------------------
+// Down projection of one group for 32 hidden rows.  grid = (H/32, 1 + max
+// distinct routed experts); y = 0 is the shared expert.  Output
+// d32[entry][H].
 template <int H, int I>
 __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
+  __shared__ float hs[kDecodeMaxRows * I];
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const uint16_t* wbase;
+  int nr, ent;
+  if (blockIdx.y == 0) {
+    wbase = a.down_sh;
+    nr = a.R;
+    ent = kDecodeMaxSlots;
+  } else {
+    const DecodePlan* P = a.plan;
+    const int u = blockIdx.y - 1;
+    if (u >= plan_ngroups(P)) return;
+    const PlanGroup g = plan_group(P, u, a.E);
+    wbase = a.down + (int64_t)g.expert * H * I;
+    ent = g.begin;
+    nr = g.nr;
+  }
+  const float* src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(ent + (j < nr ? j : 0)) * I;
+  // tile x takes hidden rows x, x + H/32, ...: concurrent blocks read
+  // neighbouring rows
+  constexpr int tiles = H / kDnRows;
+  auto row_of = [&](int j) { return (int)blockIdx.x + (wv + j * 4) * tiles; };
+  auto rowptr = [&](int j) { return wbase + (int64_t)row_of(j) * I; };
+  auto sink = [&](int j, const float (&part)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r < nr) {
+        const float v = wave_sum(part[r]);
+        if (lane == 0) a.d32[(int64_t)(ent + r) * H + row_of(j)] = v;
+      }
+    }
+  };
+  stream_rows<I, 2>(kDnRows / 4, rowptr, hs, nr, [&]() { stage_rows<I>(hs, src, nr); }, sink);
+}
+
+// ---------------------------------------------------------------------------
+// Weighted reduce: out[r] = sum over the plan's (expert, r) entries, experts
+// ascending, of weight * down, then + shared down -- a fixed order, so the
+// output is bitwise reproducible.  grid = (ceil(H/1024), R).
+template <int H>
+__global__ __launch_bounds__(kThreads) void k_dec_reduce(const FwdArgs a) {
   __shared__ DecodePlan P;
   {
     const int* src = (const int*)a.plan;
@@ -301,68 +518,38 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
     for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += kThreads) dst[i] = src[i];
   }
   __syncthreads();
-  const int R = a.R;
-  const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int h0 = blockIdx.x * kTileRows + wv * 4;
-  float acc[4][4] = {};
-  const int ng = P.ngroups;
-  for (int g = 0; g <= ng; ++g) {
-    const bool shared = g == ng;
-    const uint16_t* wbase = shared ? a.down_sh : a.down + (int64_t)P.group_expert[g] * H * I;
-    const int b = shared ? 0 : P.group_begin[g];
-    const int nr = shared ? R : P.group_begin[g + 1] - b;
-    const uint16_t* w[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) w[n] = wbase + (int64_t)(h0 + n) * I;
-    const float* xr[4];
-    int rowj[4];
-    float wj[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int jj = j < nr ? j : 0;
-      xr[j] = a.h32 + (int64_t)(shared ? kDecodeMaxSlots + jj : b + jj) * I;
-      rowj[j] = shared ? jj : P.entry_row[b + jj];
-      wj[j] = shared ? 1.0f : P.entry_w[b + jj];
-    }
-    float p[4][4] = {};
-    wave_gemv<4, I>(w, xr, nr, p);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < nr) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float sc = (rr == rowj[j]) ? wj[j] : 0.0f;
-#pragma unroll
-          for (int n = 0; n < 4; ++n) acc[n][rr] = fmaf(sc, p[n][j], acc[n][rr]);
-        }
-      }
-    }
+  const int r = blockIdx.y;
+  const int c = blockIdx.x * kRedCols + threadIdx.x * 4;
+  if (c >= H) return;
+  int ne = P.nentries;
+  ne = ne < 0 ? 0 : (ne > kDecodeMaxSlots ? kDecodeMaxSlots : ne);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < ne; ++j) {
+    if (P.entry_row[j] != r) continue;
+    const float wj = P.entry_w[j];
+    const float4 d = *(const float4*)(a.d32 + (int64_t)j * H + c);
+    acc.x = fmaf(wj, d.x, acc.x); acc.y = fmaf(wj, d.y, acc.y);
+    acc.z = fmaf(wj, d.z, acc.z); acc.w = fmaf(wj, d.w, acc.w);
   }
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    if (rr < R) {
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        float v = wave_sum(acc[n][rr]);
-        if (lane == 0) a.out[(int64_t)rr * H + h0 + n] = v;
-      }
-    }
-  }
+  const float4 s = *(const float4*)(a.d32 + (int64_t)(kDecodeMaxSlots + r) * H + c);
+  acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
+  *(float4*)(a.out + (int64_t)r * H + c) = acc;
 }
 
 template <int H, int I>
 hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   FwdArgs args = a;
-  const int nrb = (a.E + 3) / 4;
-  hipError_t err = launch("dec_router_shared", (const void*)k_dec_router_shared<H, I>,
-                          dim3(nrb + I / kTileRows), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
-  if (err != hipSuccess) return err;
   const int gmax = a.R * a.K < a.E ? a.R * a.K : a.E;
-  err = launch("dec_gateup", (const void*)k_dec_gateup<H, I>, dim3(I / kTileRows, gmax), dim3(kThreads), 0, s,
-               &args);
+  hipError_t err = launch("dec_router_shared", (const void*)k_dec_router<H, I>,
+                          dim3((a.E + 3) / 4 + I / kShRows + 1), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  return launch("dec_down_reduce", (const void*)k_dec_down<H, I>, dim3(H / kTileRows), dim3(kThreads), 0, s,
-                &args);
+  err = launch("dec_gateup", (const void*)k_dec_gateup<H, I>, dim3(I / kGuRows, gmax), dim3(kThreads),
+               (size_t)a.R * H * 4, s, &args);
+  if (err != hipSuccess) return err;
+  err = launch("dec_down", (const void*)k_dec_down<H, I>, dim3(H / kDnRows, 1 + gmax), dim3(kThreads), 0, s, &args);
+  if (err != hipSuccess) return err;
+  return launch("dec_reduce", (const void*)k_dec_reduce<H>, dim3((H + kRedCols - 1) / kRedCols, a.R),
+                dim3(kThreads), 0, s, &args);
 }
 
 }  // namespace

@@ -65,90 +65,197 @@ struct RowRoute {
   uint32_t flags;
 };
 
-// Routes one row with one wavefront; every lane returns the same result.
-//   score layer: top-K experts by key sigmoid(logit) + bias (float64),
-//     descending, equal keys to the lower index; weights are the unbiased
-//     sigmoids of the chosen experts over their sum.
-//   hash layer: the table row of the token id in column order, weighted by
-//     the renormalised sigmoids of those experts; a token id outside
-//     [0, table_rows) masks the whole row, a table entry outside
-//     [0, E) masks its slot.
-// `logits` is the row's f32 logits [E] (global memory).
+// Selection key of the score route: sigmoid(logit) + bias, in float64.
+__device__ __forceinline__ double score_key(float logit, float bias) { return sigmoid_f64(logit) + (double)bias; }
+
+// Order-preserving map of a float64 key onto uint64 (larger key -> larger
+// integer); finite keys map to values >= 1, so 0 can mark "no candidate".
+__device__ __forceinline__ uint64_t ordered_key(double k) {
+  const uint64_t b = (uint64_t)__double_as_longlong(k);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// max(v, v from the lane `CTRL` selects within its 16-lane row), 0 for lanes
+// whose source falls outside the row.
+template <int CTRL>
+__device__ __forceinline__ uint64_t umax_dpp(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, true);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Maximum of a uint64 over the wavefront, returned to every lane: shifts by
+// 1, 2, 4, 8 lanes inside each 16-lane row leave the row maximum in its lane
+// 15; the four row maxima are read back as scalars.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = umax_dpp<0x111>(v);  // row_shr:1
+  v = umax_dpp<0x112>(v);  // row_shr:2
+  v = umax_dpp<0x114>(v);  // row_shr:4
+  v = umax_dpp<0x118>(v);  // row_shr:8
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r + 15);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r + 15);
+    const uint64_t x = ((uint64_t)hi << 32) | lo;
+    m = x > m ? x : m;
+  }
+  return m;
+}
+
+// Top-K of one row's keys with one wavefront: lane l holds the keys of
+// experts l, l+64, l+128, l+192 (key[j]; experts >= E absent).  Larger key
+// first; equal keys go to the lower expert id.  Every lane gets the same K
+// indices in idx and, in lg_sel, the f32 logit lg[j] of each chosen expert.
+__device__ __forceinline__ void select_topk(const double (&key)[4], const float (&lg)[4], int E, int K,
+                                            int (&idx)[kMaxTopK], float (&lg_sel)[kMaxTopK]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t u[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) u[j] = (lane + kWave * j < E) ? ordered_key(key[j]) : 0ull;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    idx[k] = -1;
+    lg_sel[k] = 0.f;
+    if (k >= K) continue;
+    uint64_t lm = u[0];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) lm = u[j] > lm ? u[j] : lm;
+    const uint64_t m = wave_max_u64(lm);
+    // the lowest expert id holding the maximum: experts are ordered by
+    // (j, lane), so scan j upwards and take the lowest lane
+    int e = 0;
+    float l = lg[0];
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (found) continue;
+      const uint64_t mask = __ballot(u[j] == m && m != 0ull);
+      if (mask) {
+        const int wl = __ffsll((unsigned long long)mask) - 1;
+        e = wl + kWave * j;
+        l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lg[j]), wl));
+        if (lane == wl) u[j] = 0ull;
+        found = true;
+      }
+    }
+    idx[k] = found ? e : 0;
+    lg_sel[k] = l;
+  }
+}
+
+// Score route of one row given its keys and logits (lane layout of
+// select_topk): indices by select_topk, weights the unbiased sigmoids of the
+// chosen logits over their sum.
+__device__ __forceinline__ RowRoute score_route_keys(const double (&key)[4], const float (&lg)[4], int E, int K) {
+  RowRoute rr;
+  rr.flags = 0;
+  float ls[kMaxTopK];
+  select_topk(key, lg, E, K, rr.idx, ls);
+  double s[kMaxTopK], tot = 0.0;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    s[k] = (k < K) ? sigmoid_f64(ls[k]) : 0.0;
+    tot += s[k];
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    rr.valid[k] = k < K;
+    rr.w[k] = (k < K) ? (float)(s[k] / tot) : 0.0f;
+  }
+  return rr;
+}
+
+// Hash route of one row: the table row of the token id in column order,
+// weighted by the renormalised sigmoids of those experts' logits.  A token
+// id outside [0, table_rows) masks the whole row (indices -1); an entry
+// outside [0, E) masks its slot (raw entry kept).
+__device__ __forceinline__ RowRoute hash_route_row(const float* __restrict__ logits, int E, int K,
+                                                   const int32_t* __restrict__ table, int64_t table_rows,
+                                                   int32_t token) {
+  RowRoute rr;
+  rr.flags = 0;
+  const bool tok_ok = token >= 0 && (int64_t)token < table_rows;
+  double s[kMaxTopK];
+  double tot = 0.0;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (k >= K) {
+      rr.idx[k] = -1;
+      rr.valid[k] = false;
+      s[k] = 0.0;
+      continue;
+    }
+    const int e = tok_ok ? table[(int64_t)token * K + k] : -1;
+    const bool ok = tok_ok && e >= 0 && e < E;
+    rr.idx[k] = e;
+    rr.valid[k] = ok;
+    s[k] = ok ? sigmoid_f64(logits[e]) : 0.0;
+    tot += s[k];
+    if (tok_ok && !ok) rr.flags |= MOE_FLAG_BAD_TABLE_ENTRY;
+  }
+  if (!tok_ok) rr.flags |= MOE_FLAG_BAD_TOKEN;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) rr.w[k] = (rr.valid[k] && tot > 0.0) ? (float)(s[k] / tot) : 0.0f;
+  return rr;
+}
+
+// Hash route of one row whose logits are held in the select_topk lane
+// layout (lane l: experts l, l+64, l+128, l+192); same result as
+// hash_route_row.
+__device__ __forceinline__ RowRoute hash_route_lanes(const float (&lg)[4], int E, int K,
+                                                     const int32_t* __restrict__ table, int64_t table_rows,
+                                                     int32_t token) {
+  RowRoute rr;
+  rr.flags = 0;
+  const bool tok_ok = token >= 0 && (int64_t)token < table_rows;
+  double s[kMaxTopK];
+  double tot = 0.0;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (k >= K) {
+      rr.idx[k] = -1;
+      rr.valid[k] = false;
+      s[k] = 0.0;
+      continue;
+    }
+    const int e = tok_ok ? table[(int64_t)token * K + k] : -1;
+    const bool ok = tok_ok && e >= 0 && e < E;
+    rr.idx[k] = e;
+    rr.valid[k] = ok;
+    float l = 0.f;
+    if (ok) {
+      const int j = e / kWave, src = e % kWave;
+      const float v = j == 0 ? lg[0] : j == 1 ? lg[1] : j == 2 ? lg[2] : lg[3];
+      l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+    }
+    s[k] = ok ? sigmoid_f64(l) : 0.0;
+    tot += s[k];
+    if (tok_ok && !ok) rr.flags |= MOE_FLAG_BAD_TABLE_ENTRY;
+  }
+  if (!tok_ok) rr.flags |= MOE_FLAG_BAD_TOKEN;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) rr.w[k] = (rr.valid[k] && tot > 0.0) ? (float)(s[k] / tot) : 0.0f;
+  return rr;
+}
+
+// Routes one row with one wavefront from its f32 logits (keys computed here);
+// every lane returns the same result.
 __device__ __forceinline__ RowRoute route_row(const float* __restrict__ logits, int E, int K, int layer_kind,
                                               const float* __restrict__ bias, const int32_t* __restrict__ table,
                                               int64_t table_rows, int32_t token) {
+  if (layer_kind == MOE_LAYER_HASH) return hash_route_row(logits, E, K, table, table_rows, token);
   const int lane = threadIdx.x & (kWave - 1);
-  RowRoute rr;
-  rr.flags = 0;
-  if (layer_kind == 1) {  // hash
-    const bool tok_ok = token >= 0 && (int64_t)token < table_rows;
-    double s[kMaxTopK];
-    double tot = 0.0;
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-      if (k >= K) { rr.idx[k] = -1; rr.valid[k] = false; s[k] = 0.0; continue; }
-      int e = tok_ok ? table[(int64_t)token * K + k] : -1;
-      bool ok = tok_ok && e >= 0 && e < E;
-      rr.idx[k] = e;
-      rr.valid[k] = ok;
-      s[k] = ok ? sigmoid_f64(logits[e]) : 0.0;
-      tot += s[k];
-      if (tok_ok && !ok) rr.flags |= MOE_FLAG_BAD_TABLE_ENTRY;
-    }
-    if (!tok_ok) rr.flags |= MOE_FLAG_BAD_TOKEN;
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) rr.w[k] = (rr.valid[k] && tot > 0.0) ? (float)(s[k] / tot) : 0.0f;
-    return rr;
-  }
-  // score layer: each lane owns experts lane, lane+64, lane+128, lane+192
-  double key[4], sg[4];
-  bool taken[4];
+  double key[4];
+  float lg[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int e = lane + kWave * j;
-    taken[j] = e >= E;
-    sg[j] = (e < E) ? sigmoid_f64(logits[e]) : 0.0;
-    key[j] = (e < E) ? sg[j] + (double)bias[e] : 0.0;
+    const int e = lane + kWave * j;
+    lg[j] = (e < E) ? logits[e] : 0.f;
+    key[j] = (e < E) ? score_key(lg[j], bias[e]) : 0.0;
   }
-  double tot = 0.0;
-  double s[kMaxTopK];
-#pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) {
-    if (k >= K) { rr.idx[k] = -1; rr.valid[k] = false; s[k] = 0.0; continue; }
-    double bk = 0.0, bsg = 0.0;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int e = lane + kWave * j;
-      if (!taken[j] && (be == 0x7fffffff || ranks_before(key[j], e, bk, be))) {
-        bk = key[j];
-        be = e;
-        bsg = sg[j];
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      double ok_ = __shfl_xor(bk, o, kWave);
-      int oe = __shfl_xor(be, o, kWave);
-      double osg = __shfl_xor(bsg, o, kWave);
-      bool take = (oe != 0x7fffffff) && (be == 0x7fffffff || ranks_before(ok_, oe, bk, be));
-      if (take) {
-        bk = ok_;
-        be = oe;
-        bsg = osg;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + kWave * j == be) taken[j] = true;
-    rr.idx[k] = be;
-    rr.valid[k] = true;
-    s[k] = bsg;
-    tot += bsg;
-  }
-#pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) rr.w[k] = (k < K) ? (float)(s[k] / tot) : 0.0f;
-  return rr;
+  return score_route_keys(key, lg, E, K);
 }
 
 }  // namespace moe

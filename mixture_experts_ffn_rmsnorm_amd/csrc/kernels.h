@@ -22,6 +22,7 @@ struct FwdArgs {
   float eps;
   int layer_kind;
   int64_t table_rows;
+  uint32_t epoch;  // per-call tag written by the decode router blocks
   // inputs / outputs
   const float* x;
   const int32_t* token_ids;
@@ -38,13 +39,16 @@ struct FwdArgs {
   float* out;
   // workspace pieces
   uint32_t* status;
+  uint32_t* route_flags;
   float* logits;
+  double* key;
   int32_t* idx;
   float* wts;
   uint32_t* rowflags;
   float* xn32;
   DecodePlan* plan;
   float* h32;
+  float* d32;
   _Float16* xn16;
   int32_t* cnt;
   int32_t* base;

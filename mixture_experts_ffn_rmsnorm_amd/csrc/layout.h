@@ -34,15 +34,16 @@ struct DecodePlan {
 };
 
 struct Layout {
-  size_t status;     // u32 status word (+ padding)
+  size_t status;     // u32 status word; at +64: u32 [kMaxExperts] router flags (decode)
   size_t logits;     // f32 [R][E]
-  size_t sig;        // f64 [R][E]   sigmoid of the logits (decode path)
+  size_t key;        // f64 [R][E]   selection keys sigmoid(logit) + bias (decode path)
   size_t idx;        // i32 [R][K]
   size_t wts;        // f32 [R][K]
   size_t rowflags;   // u32 [R]
   size_t xn32;       // f32 [R][H]   (decode)
   size_t plan;       // DecodePlan    (decode)
   size_t h32;        // f32 [kDecodeMaxSlots + R][I]   (decode)
+  size_t d32;        // f32 [kDecodeMaxSlots + R][H]   (decode) down output per entry
   size_t xn16;       // f16 [R][H]   (prefill)
   size_t cnt;        // i32 [E + 1]  rows per group (routed experts, then shared)
   size_t base;       // i32 [E + 2]  exclusive prefix of cnt
@@ -69,9 +70,9 @@ inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
     off += bytes;
     return at;
   };
-  L->status = take(256);
+  L->status = take(64 + kMaxExperts * 4);
   L->logits = take(r * E * 4);
-  L->sig = take(r * E * 8);
+  L->key = take(r * E * 8);
   L->idx = take(S * 4);
   L->wts = take(S * 4);
   L->rowflags = take(r * 4);
@@ -79,9 +80,10 @@ inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
     L->xn32 = take(r * H * 4);
     L->plan = take(sizeof(DecodePlan));
     L->h32 = take((unsigned __int128)(kDecodeMaxSlots + R) * I * 4);
+    L->d32 = take((unsigned __int128)(kDecodeMaxSlots + R) * H * 4);
     L->xn16 = L->cnt = L->base = L->slot_rank = L->perm = L->h16 = L->dbuf = 0;
   } else {
-    L->xn32 = L->plan = L->h32 = 0;
+    L->xn32 = L->plan = L->h32 = L->d32 = 0;
     L->xn16 = take(r * H * 2);
     L->cnt = take((unsigned __int128)(E + 1) * 4);
     L->base = take((unsigned __int128)(E + 2) * 4);
