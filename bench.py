@@ -43,14 +43,12 @@ def alg_bytes(kernel, cfg, U, R):
     H, I, E, K = cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
     x = R * H * 4
     ent = R * K + R  # routed (expert, row) pairs + shared rows
-    if kernel == "dec_router_shared":  # router + routing/plan + shared gate/up
+    if kernel == "dec_head":         # router + routing plan + shared gate/up
         return E * H * 2 + 2 * I * H * 2 + 2 * x + H * 4 + R * E * 12 + R * (H + I) * 4
-    if kernel == "dec_gateup":          # routed experts' gate/up
-        return U * 2 * I * H * 2 + R * K * (H + I) * 4
-    if kernel == "dec_down":            # routed + shared down
-        return (U + 1) * H * I * 2 + ent * (I + H) * 4
-    if kernel == "dec_reduce":
-        return ent * H * 4 + x
+    if kernel == "dec_gateup":       # shared down + routed gate/up
+        return H * I * 2 + U * 2 * I * H * 2 + R * (I + H) * 4 + R * K * (H + I) * 4
+    if kernel == "dec_down_reduce":  # routed down + weighted reduce
+        return U * H * I * 2 + R * K * (I + 2 * H) * 4 + R * H * 4 + x
     if kernel == "gemm_gateup_swiglu":
         S = R * K
         return (U + 1) * 2 * I * H * 2 + (S + R) * H * 2 + (S + R) * I * 2

@@ -168,7 +168,7 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
   a.down_sh = w->down_sh;
   a.out = out;
   a.status = (uint32_t*)(ws + L.status);
-  a.route_flags = (uint32_t*)(ws + L.status + 64);
+  a.sync = (DecodeSync*)(ws + L.status + 64);  // both paths: the status block
   a.epoch = next_epoch();
   a.logits = (float*)(ws + L.logits);
   a.key = (double*)(ws + L.key);
@@ -236,7 +236,11 @@ int moe_ffn_status(const void* workspace, void* stream, uint32_t* flags) {
   hipStream_t s = (hipStream_t)stream;
   if (hipStreamSynchronize(s) != hipSuccess) return MOE_EHIP;
   uint32_t v = 0;
+  DecodeSync sy;
   if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_EHIP;
+  if (hipMemcpy(&sy, (const char*)workspace + 64, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return MOE_EHIP;
+  if (sy.last_epoch != 0 && sy.timeout_epoch == sy.last_epoch) v |= MOE_FLAG_SYNC_TIMEOUT;
   *flags = v;
   return MOE_OK;
 }

@@ -4,19 +4,16 @@
 // front to back with the next rows already requested (activation reads use
 // the LDS counter, so they never wait behind the weight loads).
 //
-//   k_dec_router   blocks [0, E/4): RMSNorm (f32) and router logits, one
-//                  expert per wave, plus the score layer's float64 selection
-//                  keys sigmoid(l) + bias.  Then the shared expert's gate/up
-//                  + SwiGLU, which needs no routing and covers the router's
-//                  latency.  A last block waits for the router blocks' flags,
-//                  routes the batch (top-k over the keys, or the hash table)
-//                  and writes the plan of distinct (expert, row) pairs
-//   k_dec_gateup   routed gate/up + SwiGLU, one (expert, 16 inter rows) tile
+//   k_dec_head     router logits (+ float64 selection keys), the routing
+//                  plan of distinct (expert, row) pairs, and the shared
+//                  expert's gate/up + SwiGLU, whose streaming covers the
+//                  router's latency
+//   k_dec_gateup   the shared expert's down projection (first blocks), then
+//                  routed gate/up + SwiGLU, one (expert, 16 inter rows) tile
 //                  per block
-//   k_dec_down     down projection of one group (shared or routed expert)
-//                  for 32 hidden rows -> f32 per (expert, row) pair
-//   k_dec_reduce   out[r] = sum of weight * down over r's pairs + shared
-//                  down, in a fixed order (no atomics)
+//   k_dec_down     routed down projections for 32 hidden rows per block; the
+//                  last block of each column tile forms out = sum of weight
+//                  * down + shared in a fixed order
 //
 // Stage order follows forward_ffn_rows on the hf2q ffn_forward.rs page
 // (rms_norm -> MoE gate -> route -> sanitize -> routed/shared gate, up ->
@@ -33,6 +30,10 @@ constexpr int kGuRows = 16;     // inter rows per routed gate/up block (x2 matri
 constexpr int kShRows = 8;      // inter rows per shared gate/up block: 4 waves x 2
 constexpr int kRedCols = 1024;  // output columns per reduce block
 constexpr int kDnRows = 32;     // hidden rows per down block: 4 waves x 8
+// Spin limit of an in-kernel wait on another workgroup's flag or counter
+// (each poll is a device-scope load, about a microsecond: roughly 0.25 s in
+// all); reaching it sets MOE_FLAG_SYNC_TIMEOUT instead of hanging.
+constexpr int kMaxPolls = 1 << 18;
 
 // One wavefront walks a sequence of whole bf16 weight rows (global) and dots
 // each with up to 4 f32 activation rows in LDS (row r at act + r*LEN).  Each
@@ -144,6 +145,46 @@ __device__ __forceinline__ void stage_rows(float* dst, const float* const (&src)
   __syncthreads();
 }
 
+// Write-through (agent-scope) store / load of one float: data that another
+// workgroup of the same kernel reads after a flag or counter says so.  The
+// writer waits for these stores to complete (sync_stores) before raising
+// the flag; the reader's loads bypass stale cache lines.
+__device__ __forceinline__ void store_wt(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_wt(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_flag(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_flag(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every store this thread issued has completed.
+__device__ __forceinline__ void sync_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Wave 0 waits until n flags equal `want` (bounded); the other waves wait at
+// the barrier.  Returns false on timeout.
+__device__ __forceinline__ bool wait_flags(const uint32_t* flags, int n, uint32_t want) {
+  __shared__ int s_ok;
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    bool ready = false;
+    int polls = 0;
+    while (true) {
+      bool mine = true;
+      for (int i = lane; i < n; i += kWave) mine &= load_flag(&flags[i]) == want;
+      ready = __ballot(!mine) == 0;
+      if (ready || ++polls >= kMaxPolls) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (lane == 0) s_ok = ready;
+  }
+  __syncthreads();
+  return s_ok;
+}
+
 // Gate/up + SwiGLU of PAIRS inter rows of one expert for the `nr` activation
 // rows in LDS: tile x of `tiles` takes rows x, x + tiles, x + 2*tiles, ...,
 // so the blocks working on one expert at the same time read neighbouring
@@ -169,7 +210,7 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* gbase, const uint16_
       if (r < nr) {
         const float gs = wave_sum(g[r]);
         const float us = wave_sum(part[r]);
-        if (lane == 0) h32[(int64_t)(hout + r) * I + i] = swiglu_f32(gs, us);
+        if (lane == 0) store_wt(&h32[(int64_t)(hout + r) * I + i], swiglu_f32(gs, us));
       }
     }
   };
@@ -278,60 +319,90 @@ __device__ void route_rows(const FwdArgs& a, int* s_idx, float* s_w, unsigned ch
   }
 }
 
-// Spin limit of the plan block's wait for the router blocks' flags (each
-// poll is a device-scope load, about a microsecond: roughly 0.25 s in all);
-// reaching it sets MOE_FLAG_SYNC_TIMEOUT instead of hanging.
-constexpr int kMaxPolls = 1 << 18;
+// The plan as read by the tail kernel, every field clamped to its range so
+// that no value can index outside the buffers.
+struct PlanGroup {
+  int expert, begin, nr;
+};
+__device__ __forceinline__ int plan_ngroups(const DecodePlan* P) {
+  const int n = P->ngroups;
+  return n < 0 ? 0 : (n > kDecodeMaxSlots ? kDecodeMaxSlots : n);
+}
+__device__ __forceinline__ PlanGroup plan_group(const DecodePlan* P, int u, int E) {
+  PlanGroup g;
+  const int e = P->group_expert[u];
+  g.expert = e < 0 ? 0 : (e >= E ? E - 1 : e);
+  int b = P->group_begin[u], n = P->group_begin[u + 1];
+  b = b < 0 ? 0 : (b > kDecodeMaxSlots - 1 ? kDecodeMaxSlots - 1 : b);
+  n = n - b;  // n <= 0 (only from a corrupt plan) just means no rows
+  n = n > kDecodeMaxRows ? kDecodeMaxRows : n;
+  if (b + n > kDecodeMaxSlots) n = kDecodeMaxSlots - b;
+  g.begin = b;
+  g.nr = n;
+  return g;
+}
+__device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R) {
+  const int r = P->entry_row[j];
+  return r < 0 ? 0 : (r >= R ? R - 1 : r);
+}
+
+// Down projection of 32 hidden rows of one expert (wbase [H][I]) for the nr
+// activation rows staged in hs; tile x of H/32 takes rows x, x + H/32, ...
+// so concurrent blocks read neighbouring rows.  d32 rows ent..ent+nr-1
+// receive the results (written through).
+template <int H, int I, class Pre>
+__device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs, int nr, int x, float* d32, int ent,
+                                          Pre pre) {
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  constexpr int tiles = H / kDnRows;
+  auto row_of = [&](int j) { return x + (wv + j * 4) * tiles; };
+  auto rowptr = [&](int j) { return wbase + (int64_t)row_of(j) * I; };
+  auto sink = [&](int j, const float (&part)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r < nr) {
+        const float v = wave_sum(part[r]);
+        if (lane == 0) store_wt(&d32[(int64_t)(ent + r) * H + row_of(j)], v);
+      }
+    }
+  };
+  stream_rows<I, 2>(kDnRows / 4, rowptr, hs, nr, pre, sink);
+}
 
 // ---------------------------------------------------------------------------
-// Router + plan + shared gate/up.  grid = E/4 router blocks, I/8 shared
-// blocks, then one plan block.
+// Head kernel: router, routing plan and the shared expert's gate/up.
+// grid = E/4 router blocks, I/8 shared gate/up blocks, then one plan block
+// (a block only waits for blocks before it, which the hardware has
+// dispatched already).
 //   Router wave (expert e = 4b + w): reads its router row, x and g directly
 //   and forms logit[r,e] = (sum_j W[e,j] x[r,j] g[j]) * (mean_j x[r,j]^2 +
 //   eps)^-1/2 -- the RMSNorm factor is per row, so it is applied after the
-//   dot product and the wave needs no block-wide norm.  It stores the logits
-//   and (score layers) the float64 keys sigmoid(logit) + bias with
-//   write-through (agent-scope) stores, waits for them to complete and only
-//   then stores flag[e] = this call's epoch.
-//   Shared blocks: RMSNorm into LDS, then 8 inter rows of the shared
-//   expert's SwiGLU output for every row; block nrb also publishes xn.
-//   Plan block (dispatched last, so every router block is already running):
-//   waits until all flags carry the epoch, routes the batch from the logits
-//   and keys (read write-through), publishes indices, weights, row flags,
-//   status and the plan, and clears the flags so a replay of the same launch
-//   waits again.
+//   dot product and the wave needs no block-wide norm.  It writes the logits
+//   and (score layers) the float64 keys sigmoid(logit) + bias through to
+//   memory and then raises route_flags[e] to the call's epoch.
+//   Shared gate/up block: RMSNorm into LDS, then 8 inter rows of the shared
+//   expert's SwiGLU output for every row (its streaming covers the router's
+//   and the plan's latency).  The first of these blocks publishes xn.
+//   Plan block: waits for every router wave, routes the batch, publishes
+//   indices, weights, row flags, status and the plan, and clears the down
+//   kernel's tile counters and the router flags.  A wait that gives up
+//   records the call's epoch in timeout_epoch (reported as
+//   MOE_FLAG_SYNC_TIMEOUT by moe_ffn_status).
 template <int H, int I>
-__global__ __launch_bounds__(kThreads) void k_dec_router(const FwdArgs a) {
+__global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   extern __shared__ float xs[];  // [R][H]
   __shared__ int s_idx[kDecodeMaxSlots];
   __shared__ float s_w[kDecodeMaxSlots];
   __shared__ unsigned char s_valid[kDecodeMaxSlots];
   __shared__ uint32_t s_flags[kDecodeMaxRows];
   __shared__ DecodePlan P;
-  __shared__ uint32_t s_timeout;
   const int R = a.R, E = a.E, K = a.K;
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const int nrb = (E + 3) / 4;
-  if ((int)blockIdx.x == (int)gridDim.x - 1) {  // the plan block
-    if (wv == 0) {
-      bool ready = false;
-      int polls = 0;
-      while (!ready) {
-        bool mine = true;
-#pragma unroll
-        for (int j = 0; j < kMaxExperts / kWave; ++j) {
-          const int e = lane + kWave * j;
-          if (e < E) mine &= __hip_atomic_load(&a.route_flags[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
-        }
-        ready = __ballot(!mine) == 0;
-        if (!ready) {
-          if (++polls >= kMaxPolls) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-      if (lane == 0) s_timeout = ready ? 0u : (uint32_t)MOE_FLAG_SYNC_TIMEOUT;
-    }
-    __syncthreads();
+  DecodeSync* sy = a.sync;
+  const int nrb = (E + 3) / 4, nsh = I / kShRows;
+  const int b = blockIdx.x;
+  if (b == nrb + nsh) {  // plan block
+    const bool ok = wait_flags(sy->route_flags, E, a.epoch);
     route_rows(a, s_idx, s_w, s_valid, s_flags);
     __syncthreads();
     if (wv == 0) build_plan(s_idx, s_w, s_valid, R, K, E, &P);
@@ -342,29 +413,31 @@ __global__ __launch_bounds__(kThreads) void k_dec_router(const FwdArgs a) {
     }
     if (threadIdx.x < R) a.rowflags[threadIdx.x] = s_flags[threadIdx.x];
     if (threadIdx.x == 0) {
-      uint32_t f = s_timeout;
+      uint32_t f = 0;
       for (int r = 0; r < R; ++r) f |= s_flags[r];
       a.status[0] = f;
+      sy->last_epoch = a.epoch;
+      if (!ok) store_flag(&sy->timeout_epoch, a.epoch);
     }
-    for (int e = threadIdx.x; e < E; e += kThreads)
-      __hip_atomic_store(&a.route_flags[e], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < kDecodeMaxTiles; i += kThreads) sy->tile_cnt[i] = 0;
+    for (int i = threadIdx.x; i < kMaxExperts; i += kThreads) store_flag(&sy->route_flags[i], 0u);
     const int* ps = (const int*)&P;
     int* pd = (int*)a.plan;
     for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += kThreads) pd[i] = ps[i];
     return;
   }
-  if ((int)blockIdx.x >= nrb) {
+  if (b >= nrb) {  // shared gate/up block
+    const int x = b - nrb;
     auto stage = [&]() {
       norm_rows_to_lds<H>(a.x, a.norm_w, R, a.eps, xs);
-      if ((int)blockIdx.x == nrb)
+      if (x == 0)
         for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
     };
-    gateup_tile<H, I, kShRows>(a.gate_sh, a.up_sh, xs, R, blockIdx.x - nrb, I / kShRows, a.h32, kDecodeMaxSlots,
-                               stage);
+    gateup_tile<H, I, kShRows>(a.gate_sh, a.up_sh, xs, R, x, nsh, a.h32, kDecodeMaxSlots, stage);
     return;
   }
   // router wave: whole row of W[e] (8 loads) plus x and g straight from memory
-  const int e = blockIdx.x * 4 + wv;
+  const int e = b * 4 + wv;
   if (e >= E) return;
   constexpr int NCH = (H + 511) / 512;
   const bool full = H % 512 == 0 || lane * 8 < H % 512;
@@ -404,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_router(const FwdArgs a) {
       const float q2 = wave_sum(ss[r]);
       if (lane == 0) {
         const float v = d * (1.0f / sqrtf(q2 / (float)H + a.eps));
-        __hip_atomic_store(&a.logits[(int64_t)r * E + e], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        store_wt(&a.logits[(int64_t)r * E + e], v);
         if (a.layer_kind == MOE_LAYER_SCORE)
           __hip_atomic_store(&a.key[(int64_t)r * E + e], score_key(v, a.bias[e]), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -412,144 +485,109 @@ __global__ __launch_bounds__(kThreads) void k_dec_router(const FwdArgs a) {
     }
   }
   if (lane == 0) {
-    // the write-through stores above have completed before the flag is stored
-    __builtin_amdgcn_s_waitcnt(0);
-    __hip_atomic_store(&a.route_flags[e], a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sync_stores();
+    store_flag(&sy->route_flags[e], a.epoch);
   }
 }
 
-// The plan as read by the later kernels, every field clamped to its range
-// so that no value can index outside the buffers.
-struct PlanGroup {
-  int expert, begin, nr;
-};
-__device__ __forceinline__ int plan_ngroups(const DecodePlan* P) {
-  const int n = P->ngroups;
-  return n < 0 ? 0 : (n > kDecodeMaxSlots ? kDecodeMaxSlots : n);
-}
-__device__ __forceinline__ PlanGroup plan_group(const DecodePlan* P, int u, int E) {
-  PlanGroup g;
-  const int e = P->group_expert[u];
-  g.expert = e < 0 ? 0 : (e >= E ? E - 1 : e);
-  int b = P->group_begin[u], n = P->group_begin[u + 1];
-  b = b < 0 ? 0 : (b > kDecodeMaxSlots - 1 ? kDecodeMaxSlots - 1 : b);
-  n = n - b;  // n <= 0 (only from a corrupt plan) just means no rows
-  n = n > kDecodeMaxRows ? kDecodeMaxRows : n;
-  if (b + n > kDecodeMaxSlots) n = kDecodeMaxSlots - b;
-  g.begin = b;
-  g.nr = n;
-  return g;
-}
-__device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R) {
-  const int r = P->entry_row[j];
-  return r < 0 ? 0 : (r >= R ? R - 1 : r);
-}
-
 // ---------------------------------------------------------------------------
-// Routed gate/up + SwiGLU.  grid = (I/16, max distinct routed experts); block
-// (x, u) handles inter rows 16x..16x+15 of the plan's u-th expert.
+// Shared down + routed gate/up.  grid = H/32 shared-down blocks (dispatched
+// first: the shared h is complete, and their streaming covers the routed
+// blocks' plan read and staging), then G * I/16 routed gate/up blocks (G =
+// max distinct routed experts).  Shared-down block x: hidden rows x,
+// x + H/32, ... of the shared expert's down projection -> d32 shared rows.
+// Gate/up block (u, x): inter rows x, x + I/16, ... of the plan's u-th
+// expert -> h32.
 template <int H, int I>
 __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
-  extern __shared__ float xs[];  // [nr][H]
+  extern __shared__ float xs[];  // [nr][H] activations, or [R][I] shared h
+  constexpr int nsd = H / kDnRows, gut = I / kGuRows;
+  const int b = blockIdx.x;
+  if (b < nsd) {
+    const float* src[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(kDecodeMaxSlots + (j < a.R ? j : 0)) * I;
+    down_tile<H, I>(a.down_sh, xs, a.R, b, a.d32, kDecodeMaxSlots, [&]() { stage_rows<I>(xs, src, a.R); });
+    return;
+  }
   const DecodePlan* P = a.plan;
-  const int u = blockIdx.y;
+  const int u = (b - nsd) / gut, x = (b - nsd) % gut;
   if (u >= plan_ngroups(P)) return;
   const PlanGroup g = plan_group(P, u, a.E);
   const float* src[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) src[j] = a.xn32 + (int64_t)plan_row(P, g.begin + (j < g.nr ? j : 0), a.R) * H;
-  gateup_tile<H, I, kGuRows>(a.gate + (int64_t)g.expert * I * H, a.up + (int64_t)g.expert * I * H, xs, g.nr,
-                             blockIdx.x, I / kGuRows, a.h32, g.begin, [&]() { stage_rows<H>(xs, src, g.nr); });
+  gateup_tile<H, I, kGuRows>(a.gate + (int64_t)g.expert * I * H, a.up + (int64_t)g.expert * I * H, xs, g.nr, x, gut,
+                             a.h32, g.begin, [&]() { stage_rows<H>(xs, src, g.nr); });
 }
 
 // ---------------------------------------------------------------------------
-// Down projection of one group for 32 hidden rows.  grid = (H/32, 1 + max
-// distinct routed experts); y = 0 is the shared expert.  Output
-// d32[entry][H].
+// Routed down + weighted reduce.  grid = (H/32, max distinct routed
+// experts).  Block (x, u) computes hidden rows x, x + H/32, ... of the plan's
+// u-th expert's down projection for its rows and writes them through to
+// d32; it then counts itself in tile_cnt[x].  The block that completes the
+// count (every routed group of the tile has written) forms, for those 32
+// columns, out[r] = sum over r's (expert, row) pairs in plan order (experts
+// ascending) of weight * down, then + shared down -- a fixed order, so the
+// output is bitwise reproducible.  No block waits for another.  With no
+// valid routed expert at all, the u = 0 blocks write out = shared down.
 template <int H, int I>
 __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   __shared__ float hs[kDecodeMaxRows * I];
-  const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  const uint16_t* wbase;
-  int nr, ent;
-  if (blockIdx.y == 0) {
-    wbase = a.down_sh;
-    nr = a.R;
-    ent = kDecodeMaxSlots;
-  } else {
-    const DecodePlan* P = a.plan;
-    const int u = blockIdx.y - 1;
-    if (u >= plan_ngroups(P)) return;
+  __shared__ int s_last;
+  const int R = a.R;
+  const DecodePlan* P = a.plan;
+  const int ng = plan_ngroups(P);
+  const int x = blockIdx.x, u = blockIdx.y;
+  constexpr int dnt = H / kDnRows;
+  if (ng > 0) {
+    if (u >= ng) return;
     const PlanGroup g = plan_group(P, u, a.E);
-    wbase = a.down + (int64_t)g.expert * H * I;
-    ent = g.begin;
-    nr = g.nr;
-  }
-  const float* src[4];
+    const float* src[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(ent + (j < nr ? j : 0)) * I;
-  // tile x takes hidden rows x, x + H/32, ...: concurrent blocks read
-  // neighbouring rows
-  constexpr int tiles = H / kDnRows;
-  auto row_of = [&](int j) { return (int)blockIdx.x + (wv + j * 4) * tiles; };
-  auto rowptr = [&](int j) { return wbase + (int64_t)row_of(j) * I; };
-  auto sink = [&](int j, const float (&part)[4]) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (r < nr) {
-        const float v = wave_sum(part[r]);
-        if (lane == 0) a.d32[(int64_t)(ent + r) * H + row_of(j)] = v;
-      }
+    for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
+    down_tile<H, I>(a.down + (int64_t)g.expert * H * I, hs, g.nr, x, a.d32, g.begin,
+                    [&]() { stage_rows<I>(hs, src, g.nr); });
+    sync_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t prev =
+          __hip_atomic_fetch_add(&a.sync->tile_cnt[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev + 1 == (uint32_t)ng;
     }
-  };
-  stream_rows<I, 2>(kDnRows / 4, rowptr, hs, nr, [&]() { stage_rows<I>(hs, src, nr); }, sink);
-}
-
-// ---------------------------------------------------------------------------
-// Weighted reduce: out[r] = sum over the plan's (expert, r) entries, experts
-// ascending, of weight * down, then + shared down -- a fixed order, so the
-// output is bitwise reproducible.  grid = (ceil(H/1024), R).
-template <int H>
-__global__ __launch_bounds__(kThreads) void k_dec_reduce(const FwdArgs a) {
-  __shared__ DecodePlan P;
-  {
-    const int* src = (const int*)a.plan;
-    int* dst = (int*)&P;
-    for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += kThreads) dst[i] = src[i];
+    __syncthreads();
+    if (!s_last) return;
+  } else if (u != 0) {
+    return;
   }
-  __syncthreads();
-  const int r = blockIdx.y;
-  const int c = blockIdx.x * kRedCols + threadIdx.x * 4;
-  if (c >= H) return;
-  int ne = P.nentries;
+  // reduce this tile: thread t -> (row r = t / 32, hidden row x + (t % 32) * H/32)
+  const int t = threadIdx.x;
+  if (t >= R * kDnRows) return;
+  const int r = t / kDnRows;
+  const int h = x + (t % kDnRows) * dnt;
+  int ne = P->nentries;
   ne = ne < 0 ? 0 : (ne > kDecodeMaxSlots ? kDecodeMaxSlots : ne);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < ne; ++j) {
-    if (P.entry_row[j] != r) continue;
-    const float wj = P.entry_w[j];
-    const float4 d = *(const float4*)(a.d32 + (int64_t)j * H + c);
-    acc.x = fmaf(wj, d.x, acc.x); acc.y = fmaf(wj, d.y, acc.y);
-    acc.z = fmaf(wj, d.z, acc.z); acc.w = fmaf(wj, d.w, acc.w);
-  }
-  const float4 s = *(const float4*)(a.d32 + (int64_t)(kDecodeMaxSlots + r) * H + c);
-  acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
-  *(float4*)(a.out + (int64_t)r * H + c) = acc;
+  float o = 0.f;
+  if (ng > 0)
+    for (int j = 0; j < ne; ++j)
+      if (P->entry_row[j] == r) o = fmaf(P->entry_w[j], load_wt(&a.d32[(int64_t)j * H + h]), o);
+  o += a.d32[(int64_t)(kDecodeMaxSlots + r) * H + h];
+  a.out[(int64_t)r * H + h] = o;
 }
 
 template <int H, int I>
 hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
+  static_assert(H / kDnRows <= kDecodeMaxTiles && I / kShRows <= kDecodeMaxTiles, "too many tiles");
   FwdArgs args = a;
   const int gmax = a.R * a.K < a.E ? a.R * a.K : a.E;
-  hipError_t err = launch("dec_router_shared", (const void*)k_dec_router<H, I>,
-                          dim3((a.E + 3) / 4 + I / kShRows + 1), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
+  hipError_t err = launch("dec_head", (const void*)k_dec_head<H, I>, dim3((a.E + 3) / 4 + I / kShRows + 1),
+                          dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  err = launch("dec_gateup", (const void*)k_dec_gateup<H, I>, dim3(I / kGuRows, gmax), dim3(kThreads),
-               (size_t)a.R * H * 4, s, &args);
+  err = launch("dec_gateup", (const void*)k_dec_gateup<H, I>, dim3(H / kDnRows + gmax * (I / kGuRows)),
+               dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  err = launch("dec_down", (const void*)k_dec_down<H, I>, dim3(H / kDnRows, 1 + gmax), dim3(kThreads), 0, s, &args);
-  if (err != hipSuccess) return err;
-  return launch("dec_reduce", (const void*)k_dec_reduce<H>, dim3((H + kRedCols - 1) / kRedCols, a.R),
-                dim3(kThreads), 0, s, &args);
+  return launch("dec_down_reduce", (const void*)k_dec_down<H, I>, dim3(H / kDnRows, gmax), dim3(kThreads), 0, s,
+                &args);
 }
 
 }  // namespace

@@ -39,7 +39,7 @@ struct FwdArgs {
   float* out;
   // workspace pieces
   uint32_t* status;
-  uint32_t* route_flags;
+  DecodeSync* sync;
   float* logits;
   double* key;
   int32_t* idx;

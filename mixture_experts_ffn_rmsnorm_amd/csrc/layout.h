@@ -33,8 +33,20 @@ struct DecodePlan {
   float entry_w[kDecodeMaxSlots];
 };
 
+// Cross-workgroup signalling words of the decode path, after the status word.
+// Flags carry the call's epoch when set; counters are zeroed by the first
+// kernel of the call for the second.
+constexpr int kDecodeMaxTiles = 256;  // down column tiles (hidden/32) and shared gate/up tiles (inter/8)
+struct DecodeSync {
+  uint32_t last_epoch;                   // epoch of the last decode call (0 after a prefill call)
+  uint32_t timeout_epoch;                // epoch of a call in which an in-kernel wait gave up
+  uint32_t pad[14];
+  uint32_t route_flags[kMaxExperts];     // router wave e done
+  uint32_t tile_cnt[kDecodeMaxTiles];    // groups finished per down column tile
+};
+
 struct Layout {
-  size_t status;     // u32 status word; at +64: u32 [kMaxExperts] router flags (decode)
+  size_t status;     // u32 status word, then the decode path's sync words (DecodeSync)
   size_t logits;     // f32 [R][E]
   size_t key;        // f64 [R][E]   selection keys sigmoid(logit) + bias (decode path)
   size_t idx;        // i32 [R][K]
@@ -70,7 +82,7 @@ inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
     off += bytes;
     return at;
   };
-  L->status = take(64 + kMaxExperts * 4);
+  L->status = take(64 + sizeof(DecodeSync));
   L->logits = take(r * E * 4);
   L->key = take(r * E * 8);
   L->idx = take(S * 4);

@@ -167,6 +167,7 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
       uint32_t tot = 0;
       for (int w = 0; w < kThreads / kWave; ++w) tot |= (uint32_t)s_wsum[w];
       a.status[0] = tot;
+      a.sync->last_epoch = 0;  // no decode-path wait in this call
       a.cnt[E] = (int)R;
     }
     return;
