@@ -42,29 +42,35 @@ def alg_bytes(kernel, cfg, U, R):
     routed (expert, row) pair per slot, R*K of them)."""
     H, I, E, K = cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
     x = R * H * 4
-    ent = R * K + R  # routed (expert, row) pairs + shared rows
+    S = R * K
     if kernel == "dec_head":         # router + routing plan + shared gate/up
         return E * H * 2 + 2 * I * H * 2 + 2 * x + H * 4 + R * E * 12 + R * (H + I) * 4
     if kernel == "dec_gateup":       # shared down + routed gate/up
         return H * I * 2 + U * 2 * I * H * 2 + R * (I + H) * 4 + R * K * (H + I) * 4
     if kernel == "dec_down_reduce":  # routed down + weighted reduce
         return U * H * I * 2 + R * K * (I + 2 * H) * 4 + R * H * 4 + x
+    if kernel == "pre_router":       # x in, xn16 + logits + routing out, router weights once
+        return E * H * 2 + x + R * H * 2 + R * E * 4 + S * 12
     if kernel == "gemm_gateup_swiglu":
-        S = R * K
         return (U + 1) * 2 * I * H * 2 + (S + R) * H * 2 + (S + R) * I * 2
-    if kernel == "gemm_down":
-        S = R * K
-        return (U + 1) * H * I * 2 + (S + R) * I * 2 + (S + R) * H * 4
+    if kernel == "gemm_down":        # routed experts: h16 in, d16 out
+        return U * H * I * 2 + S * I * 2 + S * H * 2
+    if kernel == "gemm_down_shared_reduce":  # shared expert + weighted reduce of d16
+        return H * I * 2 + R * I * 2 + S * H * 2 + R * H * 4 + S * 12
     return None
 
 
 def alg_flops(kernel, cfg, R):
-    H, I, K = cfg.hidden, cfg.inter, cfg.top_k
-    rows = R * K + R  # routed slots + shared-expert rows
+    H, I, E, K = cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
+    S = R * K
+    if kernel == "pre_router":       # hi and lo passes
+        return 2 * 2 * R * E * H
     if kernel == "gemm_gateup_swiglu":
-        return 2 * rows * 2 * I * H
+        return 2 * (S + R) * 2 * I * H
     if kernel == "gemm_down":
-        return 2 * rows * H * I
+        return 2 * S * H * I
+    if kernel == "gemm_down_shared_reduce":
+        return 2 * R * H * I
     return None
 
 
@@ -161,15 +167,23 @@ def main():
     dom = max(stages, key=lambda k: stages[k][0])
     avg_s = stages[dom][0] / stages[dom][1] / 1e3
     flops = alg_flops(dom, cfg, R)
-    if flops is not None and not decode:
+    b = alg_bytes(dom, cfg, u_mean, R)
+    # the kernel's roofline: whichever of HBM and the matrix cores bounds it
+    if flops is not None and flops / (MFMA_F16_PEAK_TFLOPS * 1e12) > b / (HBM_PEAK_GBPS * 1e9):
         ach = flops / avg_s / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": None}
     else:
-        b = alg_bytes(dom, cfg, u_mean, R)
         ach = b / avg_s / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBPS, "traffic": None}
+    for name, k in kernels.items():
+        kb, kf = alg_bytes(name, cfg, u_mean, R), alg_flops(name, cfg, R)
+        secs = k["avg_us"] * 1e-6
+        if kb is not None:
+            k["hbm_frac"] = kb / secs / 1e9 / HBM_PEAK_GBPS
+        if kf is not None:
+            k["mfma_frac"] = kf / secs / 1e12 / MFMA_F16_PEAK_TFLOPS
     sb = step_bytes(cfg, u_mean, R)
     res = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,

@@ -183,12 +183,13 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
     a.d32 = (float*)(ws + L.d32);
   } else {
     a.xn16 = (_Float16*)(ws + L.xn16);
+    a.xlo16 = (_Float16*)(ws + L.xlo16);
     a.cnt = (int32_t*)(ws + L.cnt);
-    a.base = (int32_t*)(ws + L.base);
+    a.mask = (uint32_t*)(ws + L.mask);
     a.slot_rank = (int32_t*)(ws + L.slot_rank);
     a.perm = (int32_t*)(ws + L.perm);
     a.h16 = (_Float16*)(ws + L.h16);
-    a.dbuf = (float*)(ws + L.dbuf);
+    a.d16 = (_Float16*)(ws + L.d16);
   }
   hipStream_t s = (hipStream_t)stream;
   hipError_t err = decode ? run_decode(a, s) : run_prefill(a, s);

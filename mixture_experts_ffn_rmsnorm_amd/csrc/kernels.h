@@ -50,12 +50,13 @@ struct FwdArgs {
   float* h32;
   float* d32;
   _Float16* xn16;
+  _Float16* xlo16;
+  uint32_t* mask;
   int32_t* cnt;
-  int32_t* base;
   int32_t* slot_rank;
   int32_t* perm;
   _Float16* h16;
-  float* dbuf;
+  _Float16* d16;
 };
 
 hipError_t run_decode(const FwdArgs& a, hipStream_t s);

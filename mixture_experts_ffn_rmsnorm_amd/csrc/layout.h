@@ -19,6 +19,9 @@ constexpr int kDecodeMaxRows = 4;
 constexpr int kMaxTopK = 8;
 constexpr int kDecodeMaxSlots = kDecodeMaxRows * kMaxTopK;  // 32
 constexpr int kMaxExperts = 256;
+// Rows per prefill router block: the routing of a block's rows is handed to
+// the sort as one 32-bit row mask per expert.
+constexpr int kPrefillBlockRows = 32;
 
 // Routing plan of a decode call: the distinct experts of the batch, each
 // with the distinct rows that chose it and the summed weight of those
@@ -56,13 +59,14 @@ struct Layout {
   size_t plan;       // DecodePlan    (decode)
   size_t h32;        // f32 [kDecodeMaxSlots + R][I]   (decode)
   size_t d32;        // f32 [kDecodeMaxSlots + R][H]   (decode) down output per entry
-  size_t xn16;       // f16 [R][H]   (prefill)
+  size_t xn16;       // f16 [R][H]   normalised activations, rounded (prefill)
+  size_t xlo16;      // f16 [R][H]   their rounding remainders (prefill router)
+  size_t mask;       // u32 [E][ceil(R/32)]  bit j of word b: row 32b+j chose the expert (prefill)
   size_t cnt;        // i32 [E + 1]  rows per group (routed experts, then shared)
-  size_t base;       // i32 [E + 2]  exclusive prefix of cnt
-  size_t slot_rank;  // i32 [R][K]   rank of the slot's row inside its expert
+  size_t slot_rank;  // i32 [R][K]   rank of the slot's row inside its expert, -1 if masked
   size_t perm;       // i32 [E][R]   rows of each expert in ascending order
   size_t h16;        // f16 [S + R][I]   SwiGLU output, grouped order
-  size_t dbuf;       // f32 [S + R][H]   down output, grouped order
+  size_t d16;        // f16 [S][H]   routed down output, grouped order
   size_t total;
 };
 
@@ -93,16 +97,17 @@ inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
     L->plan = take(sizeof(DecodePlan));
     L->h32 = take((unsigned __int128)(kDecodeMaxSlots + R) * I * 4);
     L->d32 = take((unsigned __int128)(kDecodeMaxSlots + R) * H * 4);
-    L->xn16 = L->cnt = L->base = L->slot_rank = L->perm = L->h16 = L->dbuf = 0;
+    L->xn16 = L->xlo16 = L->mask = L->cnt = L->slot_rank = L->perm = L->h16 = L->d16 = 0;
   } else {
     L->xn32 = L->plan = L->h32 = L->d32 = 0;
     L->xn16 = take(r * H * 2);
+    L->xlo16 = take(r * H * 2);
+    L->mask = take((unsigned __int128)E * ((r + kPrefillBlockRows - 1) / kPrefillBlockRows) * 4);
     L->cnt = take((unsigned __int128)(E + 1) * 4);
-    L->base = take((unsigned __int128)(E + 2) * 4);
     L->slot_rank = take(S * 4);
     L->perm = take((unsigned __int128)E * r * 4);
     L->h16 = take((S + r) * I * 2);
-    L->dbuf = take((S + r) * H * 4);
+    L->d16 = take(S * H * 2);
   }
   off = (off + 255) / 256 * 256;
   if (off >= lim) return false;

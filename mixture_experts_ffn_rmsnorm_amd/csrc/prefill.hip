@@ -1,17 +1,17 @@
 // Prefill path (more than 4 rows): routed rows are grouped by expert and
 // every projection is a grouped GEMM on the fp16 matrix cores.
 //
-//   k_pre_router   RMSNorm (f32) -> xn16 (fp16 GEMM operand); router logits
-//                  on f32 activations; routing of each row (score top-k or
-//                  hash) in the same block
-//   k_pre_sort     counting sort of the (row, expert) pairs: per expert the
-//                  ascending list of rows that chose it, plus each slot's
-//                  rank in that list (one block per expert, stable)
+//   k_pre_router   RMSNorm -> xn16 (fp16 GEMM operand); router logits on the
+//                  matrix cores (hi/lo split activations); routing of each
+//                  row; per expert a mask of the block's rows that chose it
+//   k_pre_sort     per expert the ascending list of rows that chose it, plus
+//                  each slot's rank in that list (one block per expert)
 //   k_gemm<0>      gate/up GEMM of every (expert, row-tile, column-tile),
 //                  the shared expert being one more group, with SwiGLU in
 //                  the epilogue -> h16
-//   k_gemm<1>      down GEMM -> per-(expert,row) outputs in f32
-//   k_pre_reduce   out[r] = sum_k w[r,k] * down_k + shared, slots in k order
+//   k_gemm<1>      routed down GEMM -> per-(expert,row) outputs in fp16
+//   k_gemm<2>      shared down GEMM whose epilogue adds the weighted routed
+//                  outputs, slots in k order -> out
 //
 // Steps and their order follow forward_ffn_rows on the hf2q ffn_forward.rs
 // page; its "slotted" indexed matmul over [rows, top_k] becomes the sort +
@@ -30,135 +30,261 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// ===========================================================================
-// Router: 16 rows per block.
-constexpr int kRB = 16;  // rows per block
-constexpr int kKT = 32;  // router k-tile
+__device__ __forceinline__ uint2 bf16x4_to_f16x4(uint32_t lo, uint32_t hi) {
+  // bf16 -> f32 -> f16 (round toward zero; exact whenever the value is an
+  // fp16 normal, since bf16 carries fewer mantissa bits)
+  auto p0 = __builtin_amdgcn_cvt_pkrtz(bf16lo(lo), bf16hi(lo));
+  auto p1 = __builtin_amdgcn_cvt_pkrtz(bf16lo(hi), bf16hi(hi));
+  uint2 r;
+  r.x = *(uint32_t*)&p0;
+  r.y = *(uint32_t*)&p1;
+  return r;
+}
 
-template <int H>
-__global__ __launch_bounds__(kThreads) void k_pre_router(const FwdArgs a) {
-  __shared__ float s_rs[kRB];
-  __shared__ float As[kKT][kRB];
-  __shared__ float Bs[kKT * kMaxExperts];  // [kKT][E]; reused as logits [kRB][E]
-  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
-  const int E = a.E, K = a.K;
-  const int64_t r0 = (int64_t)blockIdx.x * kRB;
-  const int nrows = (int)((a.R - r0) < kRB ? (a.R - r0) : kRB);
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& q) {
+  const uint2 lo = bf16x4_to_f16x4(q.x, q.y);
+  const uint2 hi = bf16x4_to_f16x4(q.z, q.w);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
 
-  // 1. RMSNorm factors, and xn16 for the matrix-core GEMM
-  for (int j = wv; j < kRB; j += kThreads / kWave) {
-    if (j >= nrows) break;
-    const float4* xr = (const float4*)(a.x + (r0 + j) * H);
-    float ss = 0.f;
-    for (int i = lane; i < H / 4; i += kWave) {
-      float4 v = xr[i];
-      ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss);
-      ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
-    }
-    ss = wave_sum(ss);
-    const float rs = 1.0f / sqrtf(ss / (float)H + a.eps);
-    if (lane == 0) s_rs[j] = rs;
-    half4* dst = (half4*)(a.xn16 + (r0 + j) * H);
-    for (int i = lane; i < H / 4; i += kWave) {
-      float4 v = xr[i];
-      float4 g = ((const float4*)a.norm_w)[i];
-      half4 o;
-      o.x = (_Float16)(v.x * rs * g.x); o.y = (_Float16)(v.y * rs * g.y);
-      o.z = (_Float16)(v.z * rs * g.z); o.w = (_Float16)(v.w * rs * g.w);
-      dst[i] = o;
-    }
-  }
-  __syncthreads();
+// chunk swizzle of a 128-byte LDS row
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-  // 2. logits[16][E] = xn[16][H] . Wr[E][H]^T on f32 FMA.  Thread t owns
-  //    rows 4*(t/64)..+4 and experts 4*(t%64)..+4.
-  const int rg = (t / 64) * 4, eg = (t % 64) * 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < H; k0 += kKT) {
-    {  // A tile: 16 rows x 32 k, normalised on the fly
-      const int row = t / 16, kk = (t % 16) * 2;
-      float v0 = 0.f, v1 = 0.f;
-      if (row < nrows) {
-        const float2 xv = *(const float2*)(a.x + (r0 + row) * H + k0 + kk);
-        const float2 gv = *(const float2*)(a.norm_w + k0 + kk);
-        v0 = xv.x * s_rs[row] * gv.x;
-        v1 = xv.y * s_rs[row] * gv.y;
-      }
-      As[kk][row] = v0;
-      As[kk + 1][row] = v1;
-    }
-    if (t < E) {  // B tile: expert t, 32 k
-      const uint4* src = (const uint4*)(a.router + (int64_t)t * H + k0);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float f[8];
-        unpack8(src[q], f);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) Bs[(q * 8 + u) * E + t] = f[u];
-      }
-    }
-    __syncthreads();
-    if (eg < E) {
-#pragma unroll 8
-      for (int kk = 0; kk < kKT; ++kk) {
-        const float4 av = *(const float4*)&As[kk][rg];
-        const float4 bv = *(const float4*)&Bs[kk * E + eg];
-        const float ar[4] = {av.x, av.y, av.z, av.w};
-        const float br[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ar[i], br[j], acc[i][j]);
-      }
-    }
-    __syncthreads();
-  }
-  // 3. logits to LDS and workspace, then route each row with one wave
-  if (eg < E) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rg + i;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) Bs[row * E + eg + j] = acc[i][j];
-      if (row < nrows) {
-        float4 o = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-        *(float4*)(a.logits + (r0 + row) * E + eg) = o;
-      }
-    }
-  }
-  __syncthreads();
-  for (int j = wv; j < nrows; j += kThreads / kWave) {
-    const int64_t r = r0 + j;
-    const int32_t tok = (a.layer_kind == MOE_LAYER_HASH) ? a.token_ids[r] : 0;
-    RowRoute rr = route_row(Bs + j * E, E, K, a.layer_kind, a.bias, a.table, a.table_rows, tok);
-    if (lane < K) {
-      int iv = 0;
-      float wv_ = 0.f;
-#pragma unroll
-      for (int k = 0; k < kMaxTopK; ++k)
-        if (k == lane) { iv = rr.idx[k]; wv_ = rr.w[k]; }
-      a.idx[r * K + lane] = iv;
-      a.wts[r * K + lane] = wv_;
-    }
-    if (lane == 0) a.rowflags[r] = rr.flags;
-  }
+// 16 bytes per lane from global memory into LDS, lanes filling consecutive
+// 16-byte slots from the wave-uniform LDS byte address `lds`.  Completion is
+// counted by vmcnt like any vector load.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // ===========================================================================
-// Counting sort: block e < E collects the rows that chose expert e (each row
-// once, even if a malformed table lists e twice), in ascending row order,
-// and the rank of each such slot.  Block E records the shared group's row
-// count and folds the per-row status bits into the status word.
-constexpr int kSortPer = 16;  // slots per thread per pass
+// Router on the matrix cores.  A block takes 32 rows and every expert.
+//  1. RMSNorm: per row rs = rsqrt(mean(x^2) + eps) and xn = x * rs * g (f32),
+//     split into hi = fp16(xn) and lo = fp16(xn - hi), which together carry
+//     about 22 significant bits.  hi is the fp16 operand the expert GEMMs
+//     take (xn16); lo goes to xlo16 for step 2.
+//  2. logits = hi.W + lo.W on the 32x32x16 fp16 MFMA with f32 accumulation;
+//     the bf16 router weights convert to fp16 exactly (for magnitudes in the
+//     fp16 normal range).  Operand tiles reach LDS by direct global->LDS
+//     loads through a 3-stage ring.
+//  3. Selection keys sigmoid(l) + bias (float64) of all 32 x E logits, by all
+//     threads at once; then one wave per row picks its top-k (or looks up
+//     its hash row), and the block publishes, per expert, the 32-bit mask
+//     of its rows that chose the expert, which is all the sort needs.
+constexpr int kRR = kPrefillBlockRows;  // rows per router block (one MFMA row fragment)
+constexpr int kRK = 64;                 // k-tile (one 128-byte row per operand row)
+constexpr int kRStages = 3;
 
+template <int H, int E>
+__global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
+  constexpr int NF = E / 32;                  // 32-expert fragments
+  constexpr int FPW = (NF + 3) / 4;           // fragments per wave
+  constexpr int NK = H / kRK;
+  constexpr int A_ST = kRR * kRK * 2;         // one of the hi / lo tiles
+  constexpr int B_ST = E * kRK * 2;
+  constexpr int ST = 2 * A_ST + B_ST;
+  constexpr int BI = B_ST / 16 / kThreads;    // B DMA instructions per thread per k-tile
+  constexpr int LPS = 2 + BI;                 // vector-memory ops per thread per k-tile
+  constexpr int V4 = H / 4 / kWave;           // float4 of a row per lane
+  static_assert(E % 32 == 0 && BI >= 1 && BI * kThreads * 16 == B_ST && A_ST == kThreads * 16, "router tiling");
+  static_assert(kRR * E * 4 + kRR * E * 8 <= kRStages * ST, "logits and keys reuse the ring");
+  static_assert(NK >= 2 && H % (4 * kWave) == 0, "router k loop");
+  __shared__ __align__(16) unsigned char s_ring[kRStages * ST];
+  __shared__ uint32_t s_mask[E];
+  __shared__ uint32_t s_flags;
+  float* s_logit = reinterpret_cast<float*>(s_ring);                 // [kRR][E] after the k loop
+  double* s_key = reinterpret_cast<double*>(s_ring + kRR * E * 4);   // [kRR][E]
+
+  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
+  const int K = a.K;
+  const int64_t r0 = (int64_t)blockIdx.x * kRR;
+  const int nrows = (int)((a.R - r0) < kRR ? (a.R - r0) : kRR);
+  const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)s_ring;
+
+  // 1. RMSNorm, hi/lo split: one wave per row, 8 rows per wave.  Rows past
+  //    the batch end are written as zeros of their own (never read back
+  //    except by this block's MFMAs, whose results for them are dropped).
+  for (int e = t; e < E; e += kThreads) s_mask[e] = 0;
+  if (t == 0) s_flags = 0;
+  {
+    float4 g[V4];
+#pragma unroll
+    for (int i = 0; i < V4; ++i) g[i] = ((const float4*)a.norm_w)[i * kWave + lane];
+#pragma unroll 1
+    for (int j = wv * (kRR / 4); j < (wv + 1) * (kRR / 4); ++j) {
+      if (j >= nrows) break;
+      const int64_t r = r0 + j;
+      const float4* xr = (const float4*)(a.x + r * H);
+      float4 v[V4];
+#pragma unroll
+      for (int i = 0; i < V4; ++i) v[i] = xr[i * kWave + lane];
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < V4; ++i) {
+        ss = fmaf(v[i].x, v[i].x, ss); ss = fmaf(v[i].y, v[i].y, ss);
+        ss = fmaf(v[i].z, v[i].z, ss); ss = fmaf(v[i].w, v[i].w, ss);
+      }
+      ss = wave_sum(ss);
+      const float rs = 1.0f / sqrtf(ss / (float)H + a.eps);
+      half4* hp = (half4*)(a.xn16 + r * H);
+      half4* lp = (half4*)(a.xlo16 + r * H);
+#pragma unroll
+      for (int i = 0; i < V4; ++i) {
+        float xn[4] = {v[i].x * rs * g[i].x, v[i].y * rs * g[i].y, v[i].z * rs * g[i].z, v[i].w * rs * g[i].w};
+        half4 h, l;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // xn is pinned as an f32 value first: hi must be the rounding of
+          // the same f32 xn that lo is taken from (a multiply fused with the
+          // fp16 rounding can round a tie the other way)
+          asm volatile("" : "+v"(xn[u]));
+          h[u] = (_Float16)xn[u];
+          l[u] = (_Float16)(xn[u] - (float)h[u]);
+        }
+        hp[i * kWave + lane] = h;
+        lp[i * kWave + lane] = l;
+      }
+    }
+  }
+  wait_vmcnt<0>();  // this block's xn16 / xlo16 stores have reached L2
+  __syncthreads();
+
+  // 2. logits[32][E].  DMA: the hi and lo tiles take one instruction each
+  //    (wave w: rows 8w..8w+7), the router tile BI (rows (w*BI + i)*8 + lane/8);
+  //    chunk (lane & 7) ^ swz(row) of each 128-byte row.
+  const int chunk_even = ((lane & 7) ^ (lane >> 3)) * 16, chunk_odd = chunk_even ^ 16;
+  const int arow_l = wv * 8 + (lane >> 3);
+  const int64_t arow_g = r0 + (arow_l < nrows ? arow_l : nrows - 1);
+  const unsigned char* ahi = (const unsigned char*)(a.xn16 + arow_g * H) + ((wv & 1) ? chunk_odd : chunk_even);
+  const unsigned char* alo = (const unsigned char*)(a.xlo16 + arow_g * H) + ((wv & 1) ? chunk_odd : chunk_even);
+  const unsigned char* bsrc = (const unsigned char*)(a.router + (int64_t)(wv * BI * 8 + (lane >> 3)) * H);
+  const uint32_t a_wave = __builtin_amdgcn_readfirstlane(wv * 1024);
+  const uint32_t b_wave = __builtin_amdgcn_readfirstlane(2 * A_ST + wv * BI * 1024);
+  auto issue = [&](int kt) {
+    const uint32_t base = ring + (uint32_t)(kt % kRStages) * ST;
+    dma16(ahi + kt * (kRK * 2), base + a_wave);
+    dma16(alo + kt * (kRK * 2), base + A_ST + a_wave);
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      dma16(bsrc + (int64_t)i * 8 * H * 2 + kt * (kRK * 2) + (((wv * BI + i) & 1) ? chunk_odd : chunk_even),
+            base + b_wave + i * 1024);
+  };
+  // fragment rows: A row lane & 31; B rows of fragment f: f*32 + lane & 31
+  // (fragments past NF, on the small shapes, repeat fragment f % NF and are
+  // not stored)
+  int bro[FPW];
+#pragma unroll
+  for (int q = 0; q < FPW; ++q) bro[q] = ((wv + 4 * q) % NF) * 32 + (lane & 31);
+  const int aro = lane & 31;
+  floatx16 acc_hi[FPW], acc_lo[FPW];
+#pragma unroll
+  for (int q = 0; q < FPW; ++q) { acc_hi[q] = floatx16{}; acc_lo[q] = floatx16{}; }
+  issue(0);
+  issue(1);
+#pragma unroll 1
+  for (int kt = 0; kt < NK; ++kt) {
+    if (kt + 1 < NK) wait_vmcnt<LPS>(); else wait_vmcnt<0>();
+    __syncthreads();  // k-tile kt landed for every wave; the buffer of kt-1 is free
+    if (kt + 2 < NK) issue(kt + 2);
+    const unsigned char* S = s_ring + (kt % kRStages) * ST;
+#pragma unroll
+    for (int st = 0; st < kRK / 16; ++st) {
+      const int c = 2 * st + (lane >> 5);
+      const int ao = aro * 128 + ((c ^ swz(aro)) << 4);
+      const half8 ah = *(const half8*)(S + ao);
+      const half8 al = *(const half8*)(S + A_ST + ao);
+#pragma unroll
+      for (int q = 0; q < FPW; ++q) {
+        const uint4 raw = *(const uint4*)(S + 2 * A_ST + bro[q] * 128 + ((c ^ swz(bro[q])) << 4));
+        const uint4 cv = bf16x8_to_f16x8(raw);
+        const half8 bf = *(const half8*)&cv;
+        acc_hi[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bf, acc_hi[q], 0, 0, 0);
+        acc_lo[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bf, acc_lo[q], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // the ring becomes the logit and key tiles
+
+  // 3. logits to LDS (D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2),
+  //    register 4*(i/8) + i%4) and to the workspace; keys; routing
+#pragma unroll
+  for (int q = 0; q < FPW; ++q) {
+    const int f = wv + 4 * q;
+    if (f < NF) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        s_logit[i * E + f * 32 + (lane & 31)] = acc_hi[q][v] + acc_lo[q][v];
+      }
+    }
+  }
+  __syncthreads();
+  for (int v = t; v < nrows * E / 4; v += kThreads)
+    ((float4*)(a.logits + r0 * E))[v] = ((const float4*)s_logit)[v];
+  const bool score = a.layer_kind != MOE_LAYER_HASH;
+  if (score) {
+    for (int q = t; q < nrows * E; q += kThreads) s_key[q] = score_key(s_logit[q], a.bias[q % E]);
+    __syncthreads();
+  }
+  for (int j = wv; j < nrows; j += kThreads / kWave) {
+    const int64_t r = r0 + j;
+    RowRoute rr;
+    if (score) {
+      double key[4];
+      float lg[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int e = lane + kWave * jj;
+        key[jj] = e < E ? s_key[j * E + e] : 0.0;
+        lg[jj] = e < E ? s_logit[j * E + e] : 0.f;
+      }
+      rr = score_route_keys(key, lg, E, K);
+    } else {
+      rr = hash_route_row(s_logit + j * E, E, K, a.table, a.table_rows, a.token_ids[r]);
+    }
+    if (lane < K) {
+      int iv = 0;
+      float wv_ = 0.f;
+      bool ok = false;
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k)
+        if (k == lane) { iv = rr.idx[k]; wv_ = rr.w[k]; ok = rr.valid[k]; }
+      a.idx[r * K + lane] = iv;
+      a.wts[r * K + lane] = wv_;
+      if (ok) atomicOr(&s_mask[iv], 1u << j);
+      else a.slot_rank[r * K + lane] = -1;
+    }
+    if (lane == 0 && rr.flags) atomicOr(&s_flags, rr.flags);
+  }
+  __syncthreads();
+  const int64_t nb = (a.R + kRR - 1) / kRR;
+  for (int e = t; e < E; e += kThreads) a.mask[(int64_t)e * nb + blockIdx.x] = s_mask[e];
+  if (t == 0) a.rowflags[blockIdx.x] = s_flags;
+}
+
+// ===========================================================================
+// Sort: block e < E turns the router blocks' row masks for expert e into the
+// ascending list of rows that chose e (perm) and each such slot's rank in
+// it (slot_rank; a row listed twice by a malformed table gets one rank for
+// both slots).  Thread t owns a contiguous run of masks, so one block-wide
+// scan of the per-thread popcounts places every row.  Block E records the
+// shared group's row count and folds the router blocks' status bits into
+// the status word.
 __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
   __shared__ int s_wsum[kThreads / kWave];
   const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
   const int e = blockIdx.x, E = a.E, K = a.K;
-  const int64_t R = a.R, S = R * K;
+  const int64_t R = a.R, nb = (R + kRR - 1) / kRR;
   if (e == E) {
     uint32_t f = 0;
-    for (int64_t r = t; r < R; r += kThreads) f |= a.rowflags[r];
+    for (int64_t b = t; b < nb; b += kThreads) f |= a.rowflags[b];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, kWave);
     if (lane == 0) s_wsum[wv] = (int)f;
@@ -172,113 +298,116 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
     }
     return;
   }
-  int running = 0;
-  for (int64_t c0 = 0; c0 < S; c0 += (int64_t)kThreads * kSortPer) {
-    const int64_t s0 = c0 + (int64_t)t * kSortPer;
-    unsigned flags = 0;
+  const uint32_t* m = a.mask + (int64_t)e * nb;
+  const int64_t per = (nb + kThreads - 1) / kThreads;
+  const int64_t b0 = (int64_t)t * per, b1 = (b0 + per < nb) ? b0 + per : nb;
+  int mine = 0;
+  for (int64_t b = b0; b < b1; ++b) mine += __popc(m[b]);
+  int incl = mine;
 #pragma unroll
-    for (int q = 0; q < kSortPer; ++q) {
-      const int64_t s = s0 + q;
-      if (s < S && a.idx[s] == e) {
-        // count a row once: skip if an earlier slot of the row has e too
-        const int64_t rb = s - s % K;
-        bool dup = false;
-        for (int64_t p = rb; p < s; ++p) dup |= (a.idx[p] == e);
-        if (!dup) flags |= 1u << q;
-      }
-    }
-    const int mine = __popc(flags);
-    // block-wide exclusive scan of `mine`
-    int incl = mine;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      int v = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += v;
-    }
-    if (lane == kWave - 1) s_wsum[wv] = incl;
-    __syncthreads();
-    int before = running, total = running;
-#pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) {
-      const int v = s_wsum[w];
-      if (w < wv) before += v;
-      total += v;
-    }
-    before += incl - mine;
-    int rank = before;
-#pragma unroll
-    for (int q = 0; q < kSortPer; ++q) {
-      if (flags & (1u << q)) {
-        const int64_t s = s0 + q;
-        a.perm[(int64_t)e * R + rank] = (int)(s / K);
-        a.slot_rank[s] = rank;
-        ++rank;
-      }
-    }
-    running = total;
-    __syncthreads();
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
   }
-  if (t == 0) a.cnt[e] = running;
+  if (lane == kWave - 1) s_wsum[wv] = incl;
+  __syncthreads();
+  int rank = incl - mine, total = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    const int v = s_wsum[w];
+    if (w < wv) rank += v;
+    total += v;
+  }
+  int32_t* perm = a.perm + (int64_t)e * R;
+  for (int64_t b = b0; b < b1; ++b) {
+    uint32_t bits = m[b];
+    while (bits) {
+      const int j = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int64_t row = b * kRR + j;
+      perm[rank] = (int32_t)row;
+      for (int k = 0; k < K; ++k)
+        if (a.idx[row * K + k] == e) a.slot_rank[row * K + k] = rank;
+      ++rank;
+    }
+  }
+  if (t == 0) a.cnt[e] = total;
 }
 
 // ===========================================================================
-// Grouped GEMM on fp16 MFMA.  Tile 128 (rows) x 128 (output columns) x 64
-// (k), 4 waves in a 2 x 2 arrangement, each wave 64 x 64 from 32x32x16
-// MFMAs.  MODE 0 (gate/up): the B tile holds 128 gate rows and the matching
-// 128 up rows, and the epilogue writes silu(gate) * up as fp16.  MODE 1
-// (down): the B tile holds 128 down rows, epilogue writes f32.
-constexpr int BM = 128, BN = 128, BK = 64, LDSK = BK + 8;
+// Grouped GEMM on fp16 MFMA.  Block tile 256 (rows) x 256 (B rows), 4 waves
+// in a 2 x 2 arrangement, each wave 128 x 128 from 32x32x16 MFMAs (4 A
+// fragments x 4 B fragments, 256 accumulators per lane).  Groups are the
+// routed experts (rows listed by the sort) and the shared expert (every
+// row).  Three modes:
+//   0  gate/up, every group: the B tile holds 128 gate rows and the matching
+//      128 up rows; the epilogue writes silu(gate) * up as fp16 (h16)
+//   1  down, routed groups: fp16 output per (expert, row) pair (d16)
+//   2  down, shared group: the epilogue forms the layer output
+//      out[r] = sum_k w[r,k] * d16[pair (idx[r,k], r)] + shared down(r),
+//      slots in k order
+// Operands travel global -> LDS directly (global_load_lds_dwordx4, no
+// register round trip) in k-tiles of 64 through a 2-stage ring: the next
+// k-tile loads while the current one is multiplied.  A tile row is 64 k =
+// 128 bytes, one cache line; its eight 16-byte chunks are stored
+// XOR-swizzled by the row index so the fragment reads of consecutive rows
+// hit distinct LDS banks.  B stays bf16 in LDS and is converted to fp16
+// after the fragment read, interleaved with the MFMAs of the previous
+// k-step.
+// The grid is persistent (one block per compute unit); tiles are ordered
+// group, column tile, row tile, and handed out so that each XCD takes a
+// contiguous run of them: the row tiles that share a weight slice run at
+// the same time behind the same L2.
+constexpr int BM = 256, BROWS = 256, BK = 64;
+constexpr int WM = 4, WN = 4;  // A and B fragments per wave
+constexpr int kStages = 2;
+constexpr int kSlab = 64;      // epilogue rows staged per pass
 
+// output columns per block tile
 template <int MODE>
-struct GemmShape;
-template <>
-struct GemmShape<0> {
-  static constexpr int BROWS = 2 * BN;
+struct GemmShape {
+  static constexpr int BN = MODE == 0 ? BROWS / 2 : BROWS;
 };
-template <>
-struct GemmShape<1> {
-  static constexpr int BROWS = BN;
-};
-
-__device__ __forceinline__ uint2 bf16x4_to_f16x4(uint32_t lo, uint32_t hi) {
-  // bf16 -> f32 -> f16 (round toward zero; exact whenever the value is an
-  // fp16 normal, since bf16 carries fewer mantissa bits)
-  auto p0 = __builtin_amdgcn_cvt_pkrtz(bf16lo(lo), bf16hi(lo));
-  auto p1 = __builtin_amdgcn_cvt_pkrtz(bf16lo(hi), bf16hi(hi));
-  uint2 r;
-  r.x = *(uint32_t*)&p0;
-  r.y = *(uint32_t*)&p1;
-  return r;
-}
 
 template <int MODE, int KD, int ND>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
-  constexpr int BROWS = GemmShape<MODE>::BROWS;
-  constexpr int NT = ND / BN;       // column tiles per group
-  constexpr int NK = KD / BK;       // k tiles
-  constexpr int AV = BM * BK / 8 / kThreads;     // 16B A vectors per thread (4)
-  constexpr int BV = BROWS * BK / 8 / kThreads;  // 16B B vectors per thread (8 or 4)
-  __shared__ _Float16 As[2][BM][LDSK];
-  __shared__ _Float16 Bs[2][BROWS][LDSK];
+  constexpr int BN = GemmShape<MODE>::BN;
+  constexpr int NT = ND / BN;                // column tiles per group
+  constexpr int NK = KD / BK;                // k slices
+  constexpr int A_ST = BM * BK * 2, B_ST = BROWS * BK * 2, ST = A_ST + B_ST;
+  constexpr int AI = A_ST / 16 / kThreads;  // A DMA instructions per thread per k-tile (8)
+  constexpr int BI = B_ST / 16 / kThreads;  // B DMA instructions per thread per k-tile (8)
+  // epilogue staging per 64-row slab, reusing the ring: f32 [64][BROWS + 4]
+  // (gate/up: gate columns, then up columns)
+  constexpr int CPITCH = BROWS + 4;
+  static_assert(kSlab * CPITCH * 4 <= kStages * ST, "staging fits");
+  static_assert(NK >= 2 && ND % BN == 0, "tiling");
+  __shared__ __align__(16) unsigned char s_ring[kStages * ST];
   __shared__ int s_tbase[kMaxExperts + 2];
   __shared__ int s_rbase[kMaxExperts + 2];
   __shared__ int s_cnt[kMaxExperts + 1];
+  __shared__ int s_pos[MODE == 2 ? BM * kMaxTopK : 1];
+  __shared__ float s_w[MODE == 2 ? BM * kMaxTopK : 1];
 
   const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
-  const int E = a.E, G = E + 1;
+  const int E = a.E, G = E + 1, K = a.K;
   const int64_t R = a.R;
+  const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)s_ring;
+  const uint32_t a_wave = __builtin_amdgcn_readfirstlane(wv * AI * 1024);
+  const uint32_t b_wave = __builtin_amdgcn_readfirstlane(A_ST + wv * BI * 1024);
 
-  // group prefix sums (rows and tiles), computed by wave 0
+  // row bases of every group, and tile bases of the groups this mode covers
   if (wv == 0) {
     int rrun = 0, trun = 0;
     for (int g0 = 0; g0 < G; g0 += kWave) {
       const int g = g0 + lane;
       const int c = g < G ? a.cnt[g] : 0;
-      const int tm = (c + BM - 1) / BM * NT;
+      const bool mine = MODE == 0 ? g < G : MODE == 1 ? g < E : g == E;
+      const int tm = mine ? (c + BM - 1) / BM * NT : 0;
       int ci = c, ti = tm;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
-        int v1 = __shfl_up(ci, o, kWave), v2 = __shfl_up(ti, o, kWave);
+        const int v1 = __shfl_up(ci, o, kWave), v2 = __shfl_up(ti, o, kWave);
         if (lane >= o) { ci += v1; ti += v2; }
       }
       if (g < G) {
@@ -295,14 +424,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
     }
   }
   __syncthreads();
-  if (MODE == 0 && blockIdx.x == 0) {
-    for (int g = t; g <= G; g += kThreads) a.base[g] = s_rbase[g];
-  }
   const int total = s_tbase[G];
   const int wm = wv >> 1, wn = wv & 1;
+  int first = blockIdx.x;
+  if (gridDim.x % 8 == 0) first = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    // locate the group: largest g with s_tbase[g] <= tile
+  // fragment rows of this lane (tile-relative) and their swizzles
+  int arow[WM], brow[WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i) arow[i] = wm * (WM * 32) + i * 32 + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < WN; ++j)
+    brow[j] = (MODE == 0 ? (j < WN / 2 ? 0 : BROWS / 2) + wn * (WN / 2) * 32 + (j % (WN / 2)) * 32
+                         : wn * (WN * 32) + j * 32) + (lane & 31);
+  // DMA: instruction i of a wave fills 8 tile rows, (wave * count + i) * 8 +
+  // lane / 8; the lane moves chunk (lane & 7) ^ swz(row) = (lane & 7) ^
+  // (lane / 8) ^ (i & 1) of its row
+  const int chunk0 = ((lane & 7) ^ (lane >> 3)) * 16;  // bytes, even i
+  const int chunk1 = chunk0 ^ 16;                       // odd i
+
+  for (int tile = first; tile < total; tile += gridDim.x) {
+    // locate the group: largest g with s_tbase[g] <= tile (empty groups
+    // share their successor's base and lose the search)
     int lo = 0, hi = G - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -316,168 +459,189 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
     const int m0 = mt * BM, n0 = nt * BN;
     const bool shared = g == E;
 
-    // A row sources for this thread's vectors
-    const _Float16* arow[AV];
-#pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const int v = t + kThreads * i;
-      const int m = m0 + (v >> 3);
-      if (m < cntg) {
-        if (MODE == 0) {
-          const int64_t r = shared ? (int64_t)m : (int64_t)a.perm[(int64_t)g * R + m];
-          arow[i] = a.xn16 + r * KD + (v & 7) * 8;
-        } else {
-          arow[i] = a.h16 + (int64_t)(s_rbase[g] + m) * KD + (v & 7) * 8;
+    if (MODE == 2) {
+      // slots of this tile's rows: position of each (expert, row) pair in
+      // d16, and its weight
+      for (int q = t; q < BM * K; q += kThreads) {
+        const int rl = q / K, k = q - rl * K;
+        const int64_t r = (int64_t)m0 + rl;
+        int pos = -1;
+        float w = 0.f;
+        if (r < R) {
+          const int e = a.idx[r * K + k];
+          const int rank = a.slot_rank[r * K + k];
+          if (e >= 0 && e < E && rank >= 0) {
+            pos = s_rbase[e] + rank;
+            w = a.wts[r * K + k];
+          }
         }
-      } else {
-        arow[i] = nullptr;
+        s_pos[rl * kMaxTopK + k] = pos;
+        s_w[rl * kMaxTopK + k] = w;
       }
     }
-    const uint16_t* brow[BV];
+
+    // DMA sources.  Rows past the group's end read its last row; their
+    // results are never stored.
+    const unsigned char* asrc[AI];
 #pragma unroll
-    for (int i = 0; i < BV; ++i) {
-      const int v = t + kThreads * i;
-      const int br = v >> 3;
-      const uint16_t* basep;
-      int64_t row;
+    for (int i = 0; i < AI; ++i) {
+      const int row = (wv * AI + i) * 8 + (lane >> 3);
+      const int m = (m0 + row < cntg) ? m0 + row : cntg - 1;
+      int64_t r;
+      if (MODE == 0) r = shared ? (int64_t)m : (int64_t)a.perm[(int64_t)g * R + m];
+      else r = (int64_t)s_rbase[g] + m;
+      asrc[i] = (MODE == 0 ? (const unsigned char*)a.xn16 : (const unsigned char*)a.h16) + r * (KD * 2) +
+                ((i & 1) ? chunk1 : chunk0);
+    }
+    // B: each wave's rows are all gate or all up rows
+    const unsigned char* bsrc[BI];
+    {
+      const int bw_row = wv * BI * 8;  // first tile B row of this wave
+      const uint16_t* bmat;
+      int brow0;
       if (MODE == 0) {
-        const bool is_up = br >= BN;
-        basep = shared ? (is_up ? a.up_sh : a.gate_sh) : (is_up ? a.up : a.gate) + (int64_t)g * ND * KD;
-        row = n0 + (is_up ? br - BN : br);
+        const bool is_up = bw_row >= BN;
+        bmat = shared ? (is_up ? a.up_sh : a.gate_sh) : (is_up ? a.up : a.gate) + (int64_t)g * ND * KD;
+        brow0 = n0 + (is_up ? bw_row - BN : bw_row) + (lane >> 3);
       } else {
-        basep = shared ? a.down_sh : a.down + (int64_t)g * ND * KD;
-        row = n0 + br;
+        bmat = shared ? a.down_sh : a.down + (int64_t)g * ND * KD;
+        brow0 = n0 + bw_row + (lane >> 3);
       }
-      brow[i] = basep + row * KD + (v & 7) * 8;
+#pragma unroll
+      for (int i = 0; i < BI; ++i)
+        bsrc[i] = (const unsigned char*)bmat + (int64_t)(brow0 + i * 8) * (KD * 2) + ((i & 1) ? chunk1 : chunk0);
     }
-
-    uint4 ra[AV], rb[BV];
-    auto gload = [&](int kt) {
+    auto issue = [&](int kt) {
+      const uint32_t base = ring + (uint32_t)(kt % kStages) * ST;
 #pragma unroll
-      for (int i = 0; i < AV; ++i)
-        ra[i] = arow[i] ? *(const uint4*)(arow[i] + kt * BK) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < AI; ++i) dma16(asrc[i] + kt * (BK * 2), base + a_wave + i * 1024);
 #pragma unroll
-      for (int i = 0; i < BV; ++i) rb[i] = *(const uint4*)(brow[i] + kt * BK);
+      for (int i = 0; i < BI; ++i) dma16(bsrc[i] + kt * (BK * 2), base + b_wave + i * 1024);
     };
-    auto sstore = [&](int buf) {
+    // fragment reads of k-step `st` (16 k) from ring buffer `buf`
+    auto read_step = [&](int buf, int st, half8 (&af)[WM], uint4 (&rb)[WN]) {
+      const unsigned char* As = s_ring + buf * ST;
+      const unsigned char* Bs = As + A_ST;
+      const int c = 2 * st + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < AV; ++i) {
-        const int v = t + kThreads * i;
-        *(uint4*)&As[buf][v >> 3][(v & 7) * 8] = ra[i];
-      }
+      for (int i = 0; i < WM; ++i) af[i] = *(const half8*)(As + arow[i] * 128 + ((c ^ swz(arow[i])) << 4));
 #pragma unroll
-      for (int i = 0; i < BV; ++i) {
-        const int v = t + kThreads * i;
-        const uint2 lo = bf16x4_to_f16x4(rb[i].x, rb[i].y);
-        const uint2 hi = bf16x4_to_f16x4(rb[i].z, rb[i].w);
-        *(uint4*)&Bs[buf][v >> 3][(v & 7) * 8] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      for (int j = 0; j < WN; ++j) rb[j] = *(const uint4*)(Bs + brow[j] * 128 + ((c ^ swz(brow[j])) << 4));
+    };
+    auto convert = [&](const uint4 (&rb)[WN], half8 (&bf)[WN]) {
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const uint4 cv = bf16x8_to_f16x8(rb[j]);
+        bf[j] = *(const half8*)&cv;
       }
     };
 
-    constexpr int NB = (MODE == 0) ? 4 : 2;  // B fragments per wave (gate 2 + up 2, or 2)
-    floatx16 acc[2][NB];
+    floatx16 acc[WM][WN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = floatx16{};
+      for (int j = 0; j < WN; ++j) acc[i][j] = floatx16{};
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
+    // Two-stage ring: k-tile kt+1 loads while kt is multiplied.  Within a
+    // k-tile, the next k-step's fragments are read and converted while the
+    // 16 MFMAs of the current step run.
+    constexpr int NS = BK / 16;  // k-steps per k-tile
+    issue(0);
+#pragma unroll 1
     for (int kt = 0; kt < NK; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < NK) gload(kt + 1);
+      wait_vmcnt<0>();
+      __syncthreads();  // k-tile kt landed for every wave; buffer of kt-1 is free
+      if (kt + 1 < NK) issue(kt + 1);
+      const int buf = kt % kStages;
+      half8 af[WM], bf[WN], afn[WM], bfn[WN];
+      uint4 rb[WN];
+      read_step(buf, 0, af, rb);
+      convert(rb, bf);
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int kof = kk * 16 + (lane >> 5) * 8;
-        half8 af[2], bfr[NB];
+      for (int st = 0; st < NS; ++st) {
+        if (st + 1 < NS) read_step(buf, st + 1, afn, rb);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = *(const half8*)&As[buf][wm * 64 + i * 32 + (lane & 31)][kof];
+        for (int j = 0; j < WN; ++j)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          int brow_l;
-          if (MODE == 0) brow_l = (j < 2 ? 0 : BN) + wn * 64 + (j & 1) * 32 + (lane & 31);
-          else brow_l = wn * 64 + j * 32 + (lane & 31);
-          bfr[j] = *(const half8*)&Bs[buf][brow_l][kof];
+          for (int i = 0; i < WM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        if (st + 1 < NS) {
+          convert(rb, bfn);
+          // one MFMA, then three VALU (the conversions), sixteen times
+#pragma unroll
+          for (int q = 0; q < WM * WN; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < WM; ++i) af[i] = afn[i];
+#pragma unroll
+          for (int j = 0; j < WN; ++j) bf[j] = bfn[j];
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < NK) sstore(buf ^ 1);
+    }
+    __syncthreads();  // every wave is done with the ring before it becomes staging
+
+    // epilogue, through LDS in 64-row slabs: D[i][j] of a 32x32 tile sits in
+    // lane j + 32*((i/4)%2), register 4*(i/8) + i%4
+    constexpr int CH = BN / 8;  // 8-column chunks per row
+    // unrolled: the accumulator indices must stay compile-time constants
+#pragma unroll
+    for (int sl = 0; sl < BM / kSlab; ++sl) {
+      __syncthreads();  // the ring (or the previous slab) is free
+      __builtin_amdgcn_sched_barrier(0);  // keep each slab's accumulator reads in place
+      if (wm == sl / 2) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = (sl & 1) * 2 + ii;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rl = ii * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+#pragma unroll
+            for (int j = 0; j < WN; ++j) ((float*)s_ring)[rl * CPITCH + brow[j]] = acc[i][j][v];
+          }
+        }
+      }
       __syncthreads();
-    }
-
-    // epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2),
-    // register 4*(i/8) + i%4
-    const int rb0 = s_rbase[g];
+#pragma unroll 1
+      for (int q = t; q < kSlab * CH; q += kThreads) {
+        const int rl = q / CH, cc = (q % CH) * 8;
+        const int m = m0 + sl * kSlab + rl;
+        if (m >= cntg) continue;
+        if (MODE != 2) {
+          const float* sv = &((const float*)s_ring)[rl * CPITCH + cc];
+          half8 h;
+          if (MODE == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+            for (int u = 0; u < 8; ++u) h[u] = (_Float16)swiglu_f32(sv[u], sv[BN + u]);
+          } else {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int mrow = m0 + wm * 64 + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v & 3);
-        if (mrow >= cntg) continue;
-        const int64_t orow = (int64_t)(rb0 + mrow);
-        if (MODE == 0) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-            const float gv = acc[i][j][v], uv = acc[i][j + 2][v];
-            a.h16[orow * ND + col] = (_Float16)swiglu_f32(gv, uv);
+            for (int u = 0; u < 8; ++u) h[u] = (_Float16)sv[u];
           }
+          _Float16* dst = MODE == 0 ? a.h16 : a.d16;
+          *(half8*)(dst + (int64_t)(s_rbase[g] + m) * ND + n0 + cc) = h;
         } else {
+          const int tr = sl * kSlab + rl;  // tile row
+          float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          for (int k = 0; k < K; ++k) {
+            const int pos = s_pos[tr * kMaxTopK + k];
+            if (pos < 0) continue;
+            const float w = s_w[tr * kMaxTopK + k];
+            const half8 d = *(const half8*)(a.d16 + (int64_t)pos * ND + n0 + cc);
 #pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-            a.dbuf[orow * ND + col] = acc[i][j][v];
+            for (int u = 0; u < 8; ++u) o[u] = fmaf(w, (float)d[u], o[u]);
           }
+          const float* sh = &((const float*)s_ring)[rl * CPITCH + cc];
+          float4 o0, o1;
+          o0.x = o[0] + sh[0]; o0.y = o[1] + sh[1]; o0.z = o[2] + sh[2]; o0.w = o[3] + sh[3];
+          o1.x = o[4] + sh[4]; o1.y = o[5] + sh[5]; o1.z = o[6] + sh[6]; o1.w = o[7] + sh[7];
+          float* dst = a.out + (int64_t)m * ND + n0 + cc;
+          *(float4*)dst = o0;
+          *(float4*)(dst + 4) = o1;
         }
       }
     }
-  }
-}
-
-// ===========================================================================
-// Weighted reduce: out[r] = sum_k w[r,k] * down(expert idx[r,k]) + shared,
-// slots in k order; masked slots skipped.  One block per row.
-template <int H>
-__global__ __launch_bounds__(kThreads) void k_pre_reduce(const FwdArgs a) {
-  const int64_t r = blockIdx.x;
-  const int K = a.K, E = a.E, t = threadIdx.x;
-  int pos[kMaxTopK];
-  float wk[kMaxTopK];
-#pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) {
-    pos[k] = -1;
-    wk[k] = 0.f;
-    if (k < K) {
-      const int e = a.idx[r * K + k];
-      if (e >= 0 && e < E) {
-        int kf = k;  // first slot of this row with the same expert
-        for (int p = k - 1; p >= 0; --p)
-          if (a.idx[r * K + p] == e) kf = p;
-        pos[k] = a.base[e] + a.slot_rank[r * K + kf];
-        wk[k] = a.wts[r * K + k];
-      }
-    }
-  }
-  const int64_t shpos = (int64_t)a.base[E] + r;
-#pragma unroll
-  for (int c = t; c < H / 4; c += kThreads) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-      if (pos[k] >= 0) {
-        const float4 d = ((const float4*)(a.dbuf + (int64_t)pos[k] * H))[c];
-        acc.x = fmaf(wk[k], d.x, acc.x); acc.y = fmaf(wk[k], d.y, acc.y);
-        acc.z = fmaf(wk[k], d.z, acc.z); acc.w = fmaf(wk[k], d.w, acc.w);
-      }
-    }
-    const float4 s = ((const float4*)(a.dbuf + shpos * H))[c];
-    acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
-    ((float4*)(a.out + r * H))[c] = acc;
+    __syncthreads();  // staging and s_pos are rewritten by the next tile
   }
 }
 
@@ -511,11 +675,11 @@ int gemm_grid() {
   return cus;
 }
 
-template <int H, int I>
+template <int H, int I, int E>
 hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   FwdArgs args = a;
-  hipError_t err = launch("pre_router", (const void*)k_pre_router<H>, dim3((a.R + kRB - 1) / kRB), dim3(kThreads), 0,
-                          s, &args);
+  const int nb = (a.R + kRR - 1) / kRR;
+  hipError_t err = launch("pre_router", (const void*)k_pre_router<H, E>, dim3(nb), dim3(kThreads), 0, s, &args);
   if (err != hipSuccess) return err;
   err = launch("pre_sort", (const void*)k_pre_sort, dim3(a.E + 1), dim3(kThreads), 0, s, &args);
   if (err != hipSuccess) return err;
@@ -524,14 +688,17 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   err = launch("gemm_down", (const void*)k_gemm<1, I, H>, dim3(grid), dim3(kThreads), 0, s, &args);
   if (err != hipSuccess) return err;
-  return launch("pre_reduce", (const void*)k_pre_reduce<H>, dim3(a.R), dim3(kThreads), 0, s, &args);
+  const int64_t sh_tiles = (a.R + BM - 1) / BM * (H / GemmShape<2>::BN);
+  const int sh_grid = sh_tiles < grid ? (int)sh_tiles : grid;
+  return launch("gemm_down_shared_reduce", (const void*)k_gemm<2, I, H>, dim3(sh_grid), dim3(kThreads), 0, s,
+                &args);
 }
 
 }  // namespace
 
 hipError_t run_prefill(const FwdArgs& a, hipStream_t s) {
-  if (a.H == 4096 && a.I == 2048) return run_prefill_t<4096, 2048>(a, s);
-  if (a.H == 512 && a.I == 256) return run_prefill_t<512, 256>(a, s);
+  if (a.H == 4096 && a.I == 2048 && a.E == 256) return run_prefill_t<4096, 2048, 256>(a, s);
+  if (a.H == 512 && a.I == 256 && a.E == 32) return run_prefill_t<512, 256, 32>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -163,8 +163,9 @@ def test_workspace_bytes():
     assert all(s % 256 == 0 and s > 0 for s in sizes)
     assert sizes[0] < sizes[1] < sizes[2] < sizes[3]
     assert sizes[4] < sizes[5] < sizes[6]
-    # prefill at 8192 rows holds at least the grouped down output in f32
-    assert sizes[6] >= (8192 * 6 + 8192) * 4096 * 4
+    # prefill at 8192 rows holds at least the grouped SwiGLU output and the
+    # routed down output, both fp16
+    assert sizes[6] >= (8192 * 6 + 8192) * 2048 * 2 + 8192 * 6 * 4096 * 2
     n = ctypes.c_size_t(0)
     assert moe.lib().moe_ffn_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(n)) == moe.MOE_EINVAL
     assert moe.lib().moe_ffn_workspace_bytes(ctypes.byref(d), 4, None) == moe.MOE_EINVAL
