@@ -65,6 +65,98 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // ===========================================================================
+// Routing of one row by 8 consecutive lanes (lane `sub` of the group); the
+// returned slot is slot `sub` (meaningful for sub < K).  Same results as the
+// one-wave routines: score route by key sigmoid(logit) + bias (float64)
+// descending, equal keys to the lower expert, weights the unbiased sigmoids
+// of the chosen logits over their sum in slot order; hash route by the token
+// id's table row with invalid ids / entries masked.
+struct RowPick {
+  int idx;
+  float w;
+  bool valid;
+  uint32_t flags;
+};
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((int)(uint32_t)v, m, kWave);
+  const uint32_t hi = __shfl_xor((int)(uint32_t)(v >> 32), m, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// weights of the K picks: s_k = sigmoid(l_k) (0 if masked), w_k = s_k / sum
+// with the sum taken in slot order; lane `sub` holds slot sub's s
+__device__ __forceinline__ float weight_8(double s_mine, int K, int sub) {
+  const int base = (threadIdx.x & (kWave - 1)) & ~7;
+  double tot = 0.0;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    const double sk = __shfl(s_mine, base + k, kWave);
+    if (k < K) tot += sk;
+  }
+  return (sub < K && tot > 0.0) ? (float)(s_mine / tot) : 0.0f;
+}
+
+template <int EMAX>
+__device__ __forceinline__ RowPick pick_score_8_t(const double* key, const float* lg, int E, int K, int sub) {
+  constexpr int PER = EMAX / 8;  // experts per lane: e = sub + 8 i
+  uint64_t u[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = sub + 8 * i;
+    u[i] = e < E ? ordered_key(key[e]) : 0ull;
+  }
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (k >= K) break;
+    uint64_t bu = 0ull;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (u[i] > bu) { bu = u[i]; be = sub + 8 * i; }
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+      const uint64_t ou = shfl_xor_u64(bu, m);
+      const int oe = __shfl_xor(be, m, kWave);
+      if (ou > bu || (ou == bu && oe < be)) { bu = ou; be = oe; }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (sub + 8 * i == be) u[i] = 0ull;
+    if (k == sub) mine = be;
+  }
+  RowPick rp;
+  rp.idx = mine;
+  rp.valid = sub < K;
+  rp.flags = 0;
+  rp.w = weight_8(sub < K ? sigmoid_f64(lg[mine]) : 0.0, K, sub);
+  return rp;
+}
+
+__device__ __forceinline__ RowPick pick_score_8(const double* key, const float* lg, int E, int K, int sub) {
+  return E <= 32 ? pick_score_8_t<32>(key, lg, E, K, sub) : pick_score_8_t<kMaxExperts>(key, lg, E, K, sub);
+}
+
+__device__ __forceinline__ RowPick pick_hash_8(const float* lg, int E, int K, const int32_t* __restrict__ table,
+                                              int64_t table_rows, int32_t token, int sub) {
+  RowPick rp;
+  const bool tok_ok = token >= 0 && (int64_t)token < table_rows;
+  const int e = (tok_ok && sub < K) ? table[(int64_t)token * K + sub] : -1;
+  rp.idx = e;
+  rp.valid = tok_ok && sub < K && e >= 0 && e < E;
+  rp.flags = !tok_ok ? (uint32_t)MOE_FLAG_BAD_TOKEN : 0u;
+  // a bad entry anywhere in the row flags the row (each slot reports its own)
+  const bool bad_entry = tok_ok && sub < K && !rp.valid;
+  uint32_t any_bad = bad_entry ? 1u : 0u;
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) any_bad |= (uint32_t)__shfl_xor((int)any_bad, m, kWave);
+  if (any_bad) rp.flags |= MOE_FLAG_BAD_TABLE_ENTRY;
+  rp.w = weight_8(rp.valid ? sigmoid_f64(lg[e]) : 0.0, K, sub);
+  return rp;
+}
+
+// ===========================================================================
 // Router on the matrix cores.  A block takes 32 rows and every expert.
 //  1. RMSNorm: per row rs = rsqrt(mean(x^2) + eps) and xn = x * rs * g (f32),
 //     split into hi = fp16(xn) and lo = fp16(xn - hi), which together carry
@@ -117,14 +209,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
     float4 g[V4];
 #pragma unroll
     for (int i = 0; i < V4; ++i) g[i] = ((const float4*)a.norm_w)[i * kWave + lane];
-#pragma unroll 1
-    for (int j = wv * (kRR / 4); j < (wv + 1) * (kRR / 4); ++j) {
-      if (j >= nrows) break;
-      const int64_t r = r0 + j;
-      const float4* xr = (const float4*)(a.x + r * H);
-      float4 v[V4];
+    // the next row's loads are issued before the current row is reduced
+    const int j0 = wv * (kRR / 4), j1 = (wv + 1) * (kRR / 4) < nrows ? (wv + 1) * (kRR / 4) : nrows;
+    float4 v[V4], vn[V4];
+    if (j0 < j1) {
 #pragma unroll
-      for (int i = 0; i < V4; ++i) v[i] = xr[i * kWave + lane];
+      for (int i = 0; i < V4; ++i) v[i] = ((const float4*)(a.x + (r0 + j0) * H))[i * kWave + lane];
+    }
+#pragma unroll 1
+    for (int j = j0; j < j1; ++j) {
+      const int64_t r = r0 + j;
+      const int jn = j + 1 < j1 ? j + 1 : j;
+#pragma unroll
+      for (int i = 0; i < V4; ++i) vn[i] = ((const float4*)(a.x + (r0 + jn) * H))[i * kWave + lane];
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < V4; ++i) {
@@ -151,6 +248,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
         hp[i * kWave + lane] = h;
         lp[i * kWave + lane] = l;
       }
+#pragma unroll
+      for (int i = 0; i < V4; ++i) v[i] = vn[i];
     }
   }
   wait_vmcnt<0>();  // this block's xn16 / xlo16 stores have reached L2
@@ -233,35 +332,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
     for (int q = t; q < nrows * E; q += kThreads) s_key[q] = score_key(s_logit[q], a.bias[q % E]);
     __syncthreads();
   }
-  for (int j = wv; j < nrows; j += kThreads / kWave) {
-    const int64_t r = r0 + j;
-    RowRoute rr;
-    if (score) {
-      double key[4];
-      float lg[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int e = lane + kWave * jj;
-        key[jj] = e < E ? s_key[j * E + e] : 0.0;
-        lg[jj] = e < E ? s_logit[j * E + e] : 0.f;
+  // one row per 8 consecutive lanes: all 32 rows at once
+  {
+    const int j = t >> 3, sub = t & 7;
+    if (j < nrows) {
+      const int64_t r = r0 + j;
+      RowPick rp = score ? pick_score_8(s_key + j * E, s_logit + j * E, E, K, sub)
+                         : pick_hash_8(s_logit + j * E, E, K, a.table, a.table_rows, a.token_ids[r], sub);
+      if (sub < K) {
+        a.idx[r * K + sub] = rp.idx;
+        a.wts[r * K + sub] = rp.w;
+        if (rp.valid) atomicOr(&s_mask[rp.idx], 1u << j);
+        else a.slot_rank[r * K + sub] = -1;
       }
-      rr = score_route_keys(key, lg, E, K);
-    } else {
-      rr = hash_route_row(s_logit + j * E, E, K, a.table, a.table_rows, a.token_ids[r]);
+      if (sub == 0 && rp.flags) atomicOr(&s_flags, rp.flags);
     }
-    if (lane < K) {
-      int iv = 0;
-      float wv_ = 0.f;
-      bool ok = false;
-#pragma unroll
-      for (int k = 0; k < kMaxTopK; ++k)
-        if (k == lane) { iv = rr.idx[k]; wv_ = rr.w[k]; ok = rr.valid[k]; }
-      a.idx[r * K + lane] = iv;
-      a.wts[r * K + lane] = wv_;
-      if (ok) atomicOr(&s_mask[iv], 1u << j);
-      else a.slot_rank[r * K + lane] = -1;
-    }
-    if (lane == 0 && rr.flags) atomicOr(&s_flags, rr.flags);
   }
   __syncthreads();
   const int64_t nb = (a.R + kRR - 1) / kRR;
@@ -511,12 +596,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
       for (int i = 0; i < BI; ++i)
         bsrc[i] = (const unsigned char*)bmat + (int64_t)(brow0 + i * 8) * (KD * 2) + ((i & 1) ? chunk1 : chunk0);
     }
-    auto issue = [&](int kt) {
-      const uint32_t base = ring + (uint32_t)(kt % kStages) * ST;
+    // k-tile `src` into ring buffer `buf`
+    auto issue = [&](int src, int buf) {
+      const uint32_t base = ring + (uint32_t)buf * ST;
 #pragma unroll
-      for (int i = 0; i < AI; ++i) dma16(asrc[i] + kt * (BK * 2), base + a_wave + i * 1024);
+      for (int i = 0; i < AI; ++i) dma16(asrc[i] + src * (BK * 2), base + a_wave + i * 1024);
 #pragma unroll
-      for (int i = 0; i < BI; ++i) dma16(bsrc[i] + kt * (BK * 2), base + b_wave + i * 1024);
+      for (int i = 0; i < BI; ++i) dma16(bsrc[i] + src * (BK * 2), base + b_wave + i * 1024);
     };
     // fragment reads of k-step `st` (16 k) from ring buffer `buf`
     auto read_step = [&](int buf, int st, half8 (&af)[WM], uint4 (&rb)[WN]) {
@@ -542,45 +628,74 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < WN; ++j) acc[i][j] = floatx16{};
 
-    // Two-stage ring: k-tile kt+1 loads while kt is multiplied.  Within a
-    // k-tile, the next k-step's fragments are read and converted while the
-    // 16 MFMAs of the current step run.
+    // Two-stage ring: k-tile kt+1 loads while kt is multiplied.  The next
+    // k-step's fragments are read and converted while the 16 MFMAs of the
+    // current step run, across k-tile boundaries too: before the last step
+    // of k-tile kt (its fragments already in registers) every wave waits
+    // for k-tile kt+1, passes the barrier, reads kt+1's first step and
+    // refills kt's buffer with kt+2.  The loop body has no branches: past
+    // the end the refill re-loads the last k-tile into the dead buffer and
+    // the read repeats it.
     constexpr int NS = BK / 16;  // k-steps per k-tile
-    issue(0);
+    half8 af[WM], bf[WN];
+    issue(0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    issue(1, 1);
+    {
+      uint4 rb[WN];
+      read_step(0, 0, af, rb);
+      convert(rb, bf);
+    }
+    // one B fragment's four MFMAs
+    auto mfma_j = [&](int j) {
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    };
+    auto conv1 = [&](const uint4& raw, half8& out) {
+      const uint4 cv = bf16x8_to_f16x8(raw);
+      out = *(const half8*)&cv;
+    };
+    // The schedule inside a k-step is pinned with scheduling fences: the
+    // next step's fragment reads go first, then each B fragment's MFMAs run
+    // while the next step's fragment of the previous column converts.
 #pragma unroll 1
     for (int kt = 0; kt < NK; ++kt) {
-      wait_vmcnt<0>();
-      __syncthreads();  // k-tile kt landed for every wave; buffer of kt-1 is free
-      if (kt + 1 < NK) issue(kt + 1);
-      const int buf = kt % kStages;
-      half8 af[WM], bf[WN], afn[WM], bfn[WN];
-      uint4 rb[WN];
-      read_step(buf, 0, af, rb);
-      convert(rb, bf);
+      const int buf = kt & 1;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        if (st + 1 < NS) read_step(buf, st + 1, afn, rb);
-#pragma unroll
-        for (int j = 0; j < WN; ++j)
-#pragma unroll
-          for (int i = 0; i < WM; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        half8 afn[WM], bfn[WN];
+        uint4 rb[WN];
         if (st + 1 < NS) {
-          convert(rb, bfn);
-          // one MFMA, then three VALU (the conversions), sixteen times
-#pragma unroll
-          for (int q = 0; q < WM * WN; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-          }
-#pragma unroll
-          for (int i = 0; i < WM; ++i) af[i] = afn[i];
-#pragma unroll
-          for (int j = 0; j < WN; ++j) bf[j] = bfn[j];
+          read_step(buf, st + 1, afn, rb);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_j(0);
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          wait_vmcnt<0>();
+          __syncthreads();  // k-tile kt+1 landed; every wave is done reading buffer `buf`
+          read_step(buf ^ 1, 0, afn, rb);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_j(0);
+          issue(kt + 2 < NK ? kt + 2 : NK - 1, buf);
+          __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int j = 1; j < WN; ++j) {
+          conv1(rb[j - 1], bfn[j - 1]);
+          mfma_j(j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        conv1(rb[WN - 1], bfn[WN - 1]);
+#pragma unroll
+        for (int i = 0; i < WM; ++i) af[i] = afn[i];
+#pragma unroll
+        for (int j = 0; j < WN; ++j) bf[j] = bfn[j];
       }
     }
-    __syncthreads();  // every wave is done with the ring before it becomes staging
+    wait_vmcnt<0>();  // the trailing refill lands before the ring turns into staging
+    __syncthreads();
 
     // epilogue, through LDS in 64-row slabs: D[i][j] of a 32x32 tile sits in
     // lane j + 32*((i/4)%2), register 4*(i/8) + i%4
