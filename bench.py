@@ -177,6 +177,13 @@ def main():
         ach = b / avg_s / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBPS, "traffic": None}
+    # HBM bytes per launch of the dominant kernel, from the committed counter
+    # summary of the same workload, if it was measured on these sources
+    from mixture_experts_ffn_rmsnorm_amd import profiling
+
+    measured = profiling.read_traffic(cfg.name)
+    if measured and dom in measured:
+        roof["traffic"] = measured[dom]
     for name, k in kernels.items():
         kb, kf = alg_bytes(name, cfg, u_mean, R), alg_flops(name, cfg, R)
         secs = k["avg_us"] * 1e-6
