@@ -22,6 +22,8 @@
 // to fp16 (exact for |w| >= 2^-14, nearly so below), accumulating in f32 on
 // v_mfma_f32_32x32x16_f16.  fp16 keeps 3 more mantissa bits than bf16 at the
 // same matrix-core rate.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -54,7 +56,9 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 // 16-byte slots from the wave-uniform LDS byte address `lds`.  Completion is
 // counted by vmcnt like any vector load.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone
@@ -597,20 +601,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
         bsrc[i] = (const unsigned char*)bmat + (int64_t)(brow0 + i * 8) * (KD * 2) + ((i & 1) ? chunk1 : chunk0);
     }
     // k-tile `src` into ring buffer `buf`
+    // (A row groups wholly past the group's end are not loaded: the ring
+    // waits with vmcnt(0), so the number of loads may differ per wave)
     auto issue = [&](int src, int buf) {
       const uint32_t base = ring + (uint32_t)buf * ST;
 #pragma unroll
-      for (int i = 0; i < AI; ++i) dma16(asrc[i] + src * (BK * 2), base + a_wave + i * 1024);
+      for (int i = 0; i < AI; ++i)
+        if (m0 + (wv * AI + i) * 8 < cntg) dma16(asrc[i] + src * (BK * 2), base + a_wave + i * 1024);
 #pragma unroll
       for (int i = 0; i < BI; ++i) dma16(bsrc[i] + src * (BK * 2), base + b_wave + i * 1024);
     };
     // fragment reads of k-step `st` (16 k) from ring buffer `buf`
-    auto read_step = [&](int buf, int st, half8 (&af)[WM], uint4 (&rb)[WN]) {
+    auto read_step = [&](int buf, int st, half8 (&af)[WM], uint4 (&rb)[WN], int nv) {
       const unsigned char* As = s_ring + buf * ST;
       const unsigned char* Bs = As + A_ST;
       const int c = 2 * st + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < WM; ++i) af[i] = *(const half8*)(As + arow[i] * 128 + ((c ^ swz(arow[i])) << 4));
+      for (int i = 0; i < WM; ++i)
+        if (i < nv) af[i] = *(const half8*)(As + arow[i] * 128 + ((c ^ swz(arow[i])) << 4));
 #pragma unroll
       for (int j = 0; j < WN; ++j) rb[j] = *(const uint4*)(Bs + brow[j] * 128 + ((c ^ swz(brow[j])) << 4));
     };
@@ -637,6 +645,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
     // the end the refill re-loads the last k-tile into the dead buffer and
     // the read repeats it.
     constexpr int NS = BK / 16;  // k-steps per k-tile
+    // The k loop is instantiated per count NV of this wave's A fragments
+    // that hold rows of the group (a partly filled row tile runs only the
+    // MFMAs of its filled fragments); every variant passes the same barriers.
+    auto kloop = [&](auto nv_c) {
+    constexpr int NV = decltype(nv_c)::value;
     half8 af[WM], bf[WN];
     issue(0, 0);
     wait_vmcnt<0>();
@@ -644,13 +657,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
     issue(1, 1);
     {
       uint4 rb[WN];
-      read_step(0, 0, af, rb);
+      read_step(0, 0, af, rb, NV);
       convert(rb, bf);
     }
     // one B fragment's four MFMAs
     auto mfma_j = [&](int j) {
 #pragma unroll
-      for (int i = 0; i < WM; ++i)
+      for (int i = 0; i < NV; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     };
     auto conv1 = [&](const uint4& raw, half8& out) {
@@ -668,14 +681,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
         half8 afn[WM], bfn[WN];
         uint4 rb[WN];
         if (st + 1 < NS) {
-          read_step(buf, st + 1, afn, rb);
+          read_step(buf, st + 1, afn, rb, NV);
           __builtin_amdgcn_sched_barrier(0);
           mfma_j(0);
           __builtin_amdgcn_sched_barrier(0);
         } else {
           wait_vmcnt<0>();
           __syncthreads();  // k-tile kt+1 landed; every wave is done reading buffer `buf`
-          read_step(buf ^ 1, 0, afn, rb);
+          read_step(buf ^ 1, 0, afn, rb, NV);
           __builtin_amdgcn_sched_barrier(0);
           mfma_j(0);
           issue(kt + 2 < NK ? kt + 2 : NK - 1, buf);
@@ -689,9 +702,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
         }
         conv1(rb[WN - 1], bfn[WN - 1]);
 #pragma unroll
-        for (int i = 0; i < WM; ++i) af[i] = afn[i];
+        for (int i = 0; i < NV; ++i) af[i] = afn[i];
 #pragma unroll
         for (int j = 0; j < WN; ++j) bf[j] = bfn[j];
+      }
+    }
+    };
+    {
+      const int rows_left = cntg - m0 - wm * (WM * 32);
+      const int nv = rows_left <= 0 ? 0 : (rows_left >= WM * 32 ? WM : (rows_left + 31) / 32);
+      switch (nv) {
+        case 4: kloop(std::integral_constant<int, 4>{}); break;
+        case 3: kloop(std::integral_constant<int, 3>{}); break;
+        case 2: kloop(std::integral_constant<int, 2>{}); break;
+        case 1: kloop(std::integral_constant<int, 1>{}); break;
+        default: kloop(std::integral_constant<int, 0>{}); break;
       }
     }
     wait_vmcnt<0>();  // the trailing refill lands before the ring turns into staging
@@ -737,14 +762,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
           *(half8*)(dst + (int64_t)(s_rbase[g] + m) * ND + n0 + cc) = h;
         } else {
           const int tr = sl * kSlab + rl;  // tile row
-          float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          for (int k = 0; k < K; ++k) {
-            const int pos = s_pos[tr * kMaxTopK + k];
-            if (pos < 0) continue;
-            const float w = s_w[tr * kMaxTopK + k];
-            const half8 d = *(const half8*)(a.d16 + (int64_t)pos * ND + n0 + cc);
+          // all K gathers in flight before the sum (masked slots load row 0
+          // and are dropped by a select, never multiplied)
+          half8 d[kMaxTopK];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) o[u] = fmaf(w, (float)d[u], o[u]);
+          for (int k = 0; k < kMaxTopK; ++k) {
+            if (k < K) {
+              const int pos = s_pos[tr * kMaxTopK + k];
+              d[k] = *(const half8*)(a.d16 + (int64_t)(pos >= 0 ? pos : 0) * ND + n0 + cc);
+            }
+          }
+          float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < kMaxTopK; ++k) {
+            if (k < K && s_pos[tr * kMaxTopK + k] >= 0) {
+              const float w = s_w[tr * kMaxTopK + k];
+#pragma unroll
+              for (int u = 0; u < 8; ++u) o[u] = fmaf(w, (float)d[k][u], o[u]);
+            }
           }
           const float* sh = &((const float*)s_ring)[rl * CPITCH + cc];
           float4 o0, o1;
