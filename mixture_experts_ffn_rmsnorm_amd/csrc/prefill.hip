@@ -448,7 +448,9 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
 // contiguous run of them: the row tiles that share a weight slice run at
 // the same time behind the same L2.
 constexpr int BM = 256, BROWS = 256, BK = 64;
-constexpr int WM = 4, WN = 4;  // A and B fragments per wave
+constexpr int kGT = 512;       // threads per GEMM block: 8 waves, 2 per SIMD
+constexpr int GWN = 4;         // waves along the B rows (2 x 4 wave grid)
+constexpr int WM = 4, WN = 2;  // A and B fragments per wave
 constexpr int kStages = 2;
 constexpr int kSlab = 64;      // epilogue rows staged per pass
 
@@ -459,13 +461,14 @@ struct GemmShape {
 };
 
 template <int MODE, int KD, int ND>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
+__global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
   constexpr int BN = GemmShape<MODE>::BN;
   constexpr int NT = ND / BN;                // column tiles per group
   constexpr int NK = KD / BK;                // k slices
   constexpr int A_ST = BM * BK * 2, B_ST = BROWS * BK * 2, ST = A_ST + B_ST;
-  constexpr int AI = A_ST / 16 / kThreads;  // A DMA instructions per thread per k-tile (8)
-  constexpr int BI = B_ST / 16 / kThreads;  // B DMA instructions per thread per k-tile (8)
+  constexpr int AI = A_ST / 16 / kGT;  // A DMA instructions per thread per k-tile (4)
+  constexpr int BI = B_ST / 16 / kGT;  // B DMA instructions per thread per k-tile (4)
+  static_assert(AI % 2 == 0 && BI % 2 == 0, "chunk parity alternates with the instruction index");
   // epilogue staging per 64-row slab, reusing the ring: f32 [64][BROWS + 4]
   // (gate/up: gate columns, then up columns)
   constexpr int CPITCH = BROWS + 4;
@@ -514,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
   }
   __syncthreads();
   const int total = s_tbase[G];
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / GWN, wn = wv % GWN;
   int first = blockIdx.x;
   if (gridDim.x % 8 == 0) first = (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
 
@@ -551,7 +554,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
     if (MODE == 2) {
       // slots of this tile's rows: position of each (expert, row) pair in
       // d16, and its weight
-      for (int q = t; q < BM * K; q += kThreads) {
+      for (int q = t; q < BM * K; q += kGT) {
         const int rl = q / K, k = q - rl * K;
         const int64_t r = (int64_t)m0 + rl;
         int pos = -1;
@@ -744,7 +747,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const FwdArgs a) {
       }
       __syncthreads();
 #pragma unroll 1
-      for (int q = t; q < kSlab * CH; q += kThreads) {
+      for (int q = t; q < kSlab * CH; q += kGT) {
         const int rl = q / CH, cc = (q % CH) * 8;
         const int m = m0 + sl * kSlab + rl;
         if (m >= cntg) continue;
@@ -834,13 +837,13 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   err = launch("pre_sort", (const void*)k_pre_sort, dim3(a.E + 1), dim3(kThreads), 0, s, &args);
   if (err != hipSuccess) return err;
   const int grid = gemm_grid();
-  err = launch("gemm_gateup_swiglu", (const void*)k_gemm<0, H, I>, dim3(grid), dim3(kThreads), 0, s, &args);
+  err = launch("gemm_gateup_swiglu", (const void*)k_gemm<0, H, I>, dim3(grid), dim3(kGT), 0, s, &args);
   if (err != hipSuccess) return err;
-  err = launch("gemm_down", (const void*)k_gemm<1, I, H>, dim3(grid), dim3(kThreads), 0, s, &args);
+  err = launch("gemm_down", (const void*)k_gemm<1, I, H>, dim3(grid), dim3(kGT), 0, s, &args);
   if (err != hipSuccess) return err;
   const int64_t sh_tiles = (a.R + BM - 1) / BM * (H / GemmShape<2>::BN);
   const int sh_grid = sh_tiles < grid ? (int)sh_tiles : grid;
-  return launch("gemm_down_shared_reduce", (const void*)k_gemm<2, I, H>, dim3(sh_grid), dim3(kThreads), 0, s,
+  return launch("gemm_down_shared_reduce", (const void*)k_gemm<2, I, H>, dim3(sh_grid), dim3(kGT), 0, s,
                 &args);
 }
 
