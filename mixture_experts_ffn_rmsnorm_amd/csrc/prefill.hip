@@ -49,6 +49,12 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& q) {
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// SwiGLU for an fp16 result: silu(g) * u with the hardware exp2 and
+// reciprocal (relative error ~1e-6, far below the fp16 rounding that follows)
+__device__ __forceinline__ float swiglu_fast(float g, float u) {
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
 // chunk swizzle of a 128-byte LDS row
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -443,10 +449,10 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
 // hit distinct LDS banks.  B stays bf16 in LDS and is converted to fp16
 // after the fragment read, interleaved with the MFMAs of the previous
 // k-step.
-// The grid is persistent (one block per compute unit); tiles are ordered
-// group, column tile, row tile, and handed out so that each XCD takes a
-// contiguous run of them: the row tiles that share a weight slice run at
-// the same time behind the same L2.
+// The grid is persistent (one block per compute unit); tiles are ordered by
+// group, then in blocks of 4 row tiles x 8 column tiles, and handed out so
+// that each XCD takes a contiguous run of them: the tiles that share
+// activation tiles and weight slices run at the same time behind one L2.
 constexpr int BM = 256, BROWS = 256, BK = 64;
 constexpr int kGT = 512;       // threads per GEMM block: 8 waves, 2 per SIMD
 constexpr int GWN = 4;         // waves along the B rows (2 x 4 wave grid)
@@ -547,7 +553,15 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     const int cntg = s_cnt[g];
     const int tm = (cntg + BM - 1) / BM;
     const int local = tile - s_tbase[g];
-    const int mt = local % tm, nt = local / tm;
+    // within the group, tiles go in bands of SN column tiles, each band in
+    // blocks of SM row tiles x SN column tiles (row tile fastest): an XCD's
+    // 32 concurrent tiles then share 4 activation tiles and 8 weight slices
+    constexpr int SN = NT < 8 ? NT : 8, SM = 4;
+    static_assert(NT % SN == 0, "column bands");
+    const int band = local / (tm * SN), inband = local - band * tm * SN;
+    const int mb = inband / (SM * SN), ms = (tm - mb * SM) < SM ? (tm - mb * SM) : SM;
+    const int ib = inband - mb * SM * SN;
+    const int mt = mb * SM + ib % ms, nt = band * SN + ib / ms;
     const int m0 = mt * BM, n0 = nt * BN;
     const bool shared = g == E;
 
@@ -756,7 +770,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
           half8 h;
           if (MODE == 0) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) h[u] = (_Float16)swiglu_f32(sv[u], sv[BN + u]);
+            for (int u = 0; u < 8; ++u) h[u] = (_Float16)swiglu_fast(sv[u], sv[BN + u]);
           } else {
 #pragma unroll
             for (int u = 0; u < 8; ++u) h[u] = (_Float16)sv[u];
