@@ -84,10 +84,9 @@ StageTimer& timer() {
   return t;
 }
 
-// Per-call tag the decode router blocks publish when their logits are
-// written: a process-wide counter seeded from the clock, never 0, so a flag
-// left in the workspace by an earlier call (or by anything else) does not
-// match the current call.
+// Per-call tag of the decode path's tagged words: a process-wide counter
+// seeded from the clock, never 0, so a word left in the workspace by an
+// earlier call (or by anything else) does not match the current call.
 uint32_t next_epoch() {
   static std::atomic<uint32_t> ctr{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
   uint32_t e = ctr.fetch_add(1, std::memory_order_relaxed);
@@ -171,7 +170,6 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
   a.sync = (DecodeSync*)(ws + L.status + 64);  // both paths: the status block
   a.epoch = next_epoch();
   a.logits = (float*)(ws + L.logits);
-  a.key = (double*)(ws + L.key);
   a.idx = (int32_t*)(ws + L.idx);
   a.wts = (float*)(ws + L.wts);
   a.rowflags = (uint32_t*)(ws + L.rowflags);
@@ -237,11 +235,10 @@ int moe_ffn_status(const void* workspace, void* stream, uint32_t* flags) {
   hipStream_t s = (hipStream_t)stream;
   if (hipStreamSynchronize(s) != hipSuccess) return MOE_EHIP;
   uint32_t v = 0;
-  DecodeSync sy;
+  uint32_t ep[2];  // DecodeSync: last_epoch, timeout_epoch
   if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_EHIP;
-  if (hipMemcpy(&sy, (const char*)workspace + 64, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
-    return MOE_EHIP;
-  if (sy.last_epoch != 0 && sy.timeout_epoch == sy.last_epoch) v |= MOE_FLAG_SYNC_TIMEOUT;
+  if (hipMemcpy(ep, (const char*)workspace + 64, sizeof(ep), hipMemcpyDeviceToHost) != hipSuccess) return MOE_EHIP;
+  if (ep[0] != 0 && ep[1] == ep[0]) v |= MOE_FLAG_SYNC_TIMEOUT;
   *flags = v;
   return MOE_OK;
 }

@@ -279,44 +279,148 @@ __device__ void build_plan(const int* s_idx, const float* s_w, const unsigned ch
   }
 }
 
-// Routing of the batch into LDS: wave w < R routes row w from the logits
-// (and, for score layers, the keys) that the router waves wrote through to
-// memory; they are read with agent-scope loads, which do not hit stale lines.
-__device__ void route_rows(const FwdArgs& a, int* s_idx, float* s_w, unsigned char* s_valid, uint32_t* s_flags) {
+// Route of one row by one wavefront, slot-parallel: lane k < K returns
+// slot k (index, weight, valid); flags (the row's status bits) are the same
+// in every lane.  lg holds the logits in the select_topk lane layout (lane
+// l: experts l, l+64, l+128, l+192).  Score layers: the K largest keys
+// sigmoid(logit) + bias (bias bs0..bs3 in the same layout), larger first,
+// equal keys to the lower expert id;
+// hash layers: `ent`, lane k's entry of the token's table row (tok_ok false
+// for a token id outside the table).  Weights are the chosen experts'
+// sigmoids over their sum, summed in slot order.  Same results, in the same
+// order of operations, as select_topk + score_route_keys and
+// hash_route_entries; written with one copy of each step (keys, selection,
+// weights), which keeps the kernel small.
+struct SlotRoute {
+  int idx;
+  float w;
+  bool valid;
+  uint32_t flags;
+};
+__device__ __forceinline__ SlotRoute route_slots(float lg0, float lg1, float lg2, float lg3, float bs0, float bs1,
+                                                 float bs2, float bs3, int E, int K, bool hash, bool tok_ok, int ent) {
+  const int lane = threadIdx.x & (kWave - 1);
+  SlotRoute o;
+  o.flags = 0;
+  float lsel = 0.f;  // this lane's slot: the logit its weight comes from
+  bool use = false;  // ... and whether the slot is valid
+  if (!hash) {
+    uint64_t u0 = 0, u1 = 0, u2 = 0, u3 = 0;
+#pragma unroll 1
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + kWave * j;
+      const float l = j == 0 ? lg0 : j == 1 ? lg1 : j == 2 ? lg2 : lg3;
+      const float bj = j == 0 ? bs0 : j == 1 ? bs1 : j == 2 ? bs2 : bs3;
+      const uint64_t k = e < E ? ordered_key(score_key(l, bj)) : 0ull;
+      u0 = j == 0 ? k : u0;
+      u1 = j == 1 ? k : u1;
+      u2 = j == 2 ? k : u2;
+      u3 = j == 3 ? k : u3;
+    }
+    o.idx = -1;
+#pragma unroll 1
+    for (int k = 0; k < K; ++k) {
+      uint64_t lm = u0 > u1 ? u0 : u1;
+      lm = u2 > lm ? u2 : lm;
+      lm = u3 > lm ? u3 : lm;
+      const uint64_t m = wave_max_u64(lm);
+      // the lowest expert id holding the maximum: experts are ordered by
+      // (j, lane), so take the lowest j, then the lowest lane
+      const uint64_t b0 = __ballot(u0 == m && m != 0ull), b1 = __ballot(u1 == m && m != 0ull);
+      const uint64_t b2 = __ballot(u2 == m && m != 0ull), b3 = __ballot(u3 == m && m != 0ull);
+      const int j = b0 ? 0 : b1 ? 1 : b2 ? 2 : b3 ? 3 : -1;
+      const uint64_t bm = j == 0 ? b0 : j == 1 ? b1 : j == 2 ? b2 : b3;
+      int e = 0;
+      float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lg0), 0));
+      if (j >= 0) {
+        const int wl = __ffsll((unsigned long long)bm) - 1;
+        e = wl + kWave * j;
+        const float lj = j == 0 ? lg0 : j == 1 ? lg1 : j == 2 ? lg2 : lg3;
+        l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lj), wl));
+        if (lane == wl) {
+          u0 = j == 0 ? 0ull : u0;
+          u1 = j == 1 ? 0ull : u1;
+          u2 = j == 2 ? 0ull : u2;
+          u3 = j == 3 ? 0ull : u3;
+        }
+      }
+      if (lane == k) {
+        o.idx = e;
+        lsel = l;
+      }
+    }
+    use = lane < K;
+  } else {
+    const int e = (tok_ok && lane < K) ? ent : -1;
+    use = tok_ok && lane < K && e >= 0 && e < E;
+    const int src = use ? (e & (kWave - 1)) : 0, j = use ? e / kWave : 0;
+    const float v0 = __shfl(lg0, src), v1 = __shfl(lg1, src), v2 = __shfl(lg2, src), v3 = __shfl(lg3, src);
+    lsel = j == 0 ? v0 : j == 1 ? v1 : j == 2 ? v2 : v3;
+    o.idx = lane < K ? e : -1;
+    if (__ballot(tok_ok && lane < K && !use)) o.flags |= MOE_FLAG_BAD_TABLE_ENTRY;
+    if (!tok_ok) o.flags |= MOE_FLAG_BAD_TOKEN;
+  }
+  const double sg = use ? sigmoid_f64(lsel) : 0.0;
+  double tot = 0.0;
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const int lo = __builtin_amdgcn_readlane((int)(uint32_t)__double_as_longlong(sg), k);
+    const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(__double_as_longlong(sg) >> 32), k);
+    tot += __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
+  }
+  o.valid = use;
+  o.w = (use && (!hash || tot > 0.0)) ? (float)(sg / tot) : 0.0f;
+  return o;
+}
+
+// Routing of the batch into LDS: wave r < R routes row r.  It first reads
+// what the route needs besides the logits (bias, or the token's table row),
+// then polls the row's tagged logits until every one carries the call's
+// epoch (bounded; returns false on timeout).
+__device__ bool route_rows(const FwdArgs& a, int* s_idx, float* s_w, unsigned char* s_valid, uint32_t* s_flags) {
   const int R = a.R, K = a.K, E = a.E;
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  if (wv >= R) return;
-  RowRoute rr;
-  float lgv[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + kWave * j;
-    lgv[j] = (e < E) ? __hip_atomic_load(&a.logits[(int64_t)wv * E + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                     : 0.f;
-  }
-  if (a.layer_kind == MOE_LAYER_HASH) {
-    rr = hash_route_lanes(lgv, E, K, a.table, a.table_rows, a.token_ids[wv]);
+  if (wv >= R) return true;
+  const bool hash = a.layer_kind == MOE_LAYER_HASH;
+  int ent = -1;
+  bool tok_ok = false;
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (hash) {
+    const int32_t tok = a.token_ids[wv];
+    tok_ok = tok >= 0 && (int64_t)tok < a.table_rows;
+    if (tok_ok && lane < K) ent = a.table[(int64_t)tok * K + lane];
   } else {
-    double key[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bias[j] = (lane + kWave * j < E) ? a.bias[lane + kWave * j] : 0.f;
+  }
+  const uint64_t* tags = a.sync->logit_tag + wv * E;
+  float lgv[4];
+  bool ready = false;
+  for (int polls = 0;; ++polls) {
+    bool mine = true;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = lane + kWave * j;
-      key[j] = (e < E) ? __hip_atomic_load(&a.key[(int64_t)wv * E + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                       : 0.0;
-    }
-    rr = score_route_keys(key, lgv, E, K);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-      if (k < K) {
-        s_idx[wv * K + k] = rr.idx[k];
-        s_w[wv * K + k] = rr.w[k];
-        s_valid[wv * K + k] = rr.valid[k];
+      lgv[j] = 0.f;
+      if (e < E) {
+        const uint64_t w = __hip_atomic_load(&tags[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mine &= (uint32_t)(w >> 32) == a.epoch;
+        lgv[j] = __uint_as_float((uint32_t)w);
       }
     }
-    s_flags[wv] = rr.flags;
+    ready = __ballot(!mine) == 0;
+    if (ready || polls >= kMaxPolls) break;
+    __builtin_amdgcn_s_sleep(1);
   }
+  const SlotRoute sr =
+      route_slots(lgv[0], lgv[1], lgv[2], lgv[3], bias[0], bias[1], bias[2], bias[3], E, K, hash, tok_ok, ent);
+  if (lane < K) {
+    s_idx[wv * K + lane] = sr.idx;
+    s_w[wv * K + lane] = sr.w;
+    s_valid[wv * K + lane] = sr.valid;
+  }
+  if (lane == 0) s_flags[wv] = sr.flags;
+  return ready;
 }
 
 // The plan as read by the tail kernel, every field clamped to its range so
@@ -377,20 +481,21 @@ __device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs
 //   Router wave (expert e = 4b + w): reads its router row, x and g directly
 //   and forms logit[r,e] = (sum_j W[e,j] x[r,j] g[j]) * (mean_j x[r,j]^2 +
 //   eps)^-1/2 -- the RMSNorm factor is per row, so it is applied after the
-//   dot product and the wave needs no block-wide norm.  It writes the logits
-//   and (score layers) the float64 keys sigmoid(logit) + bias through to
-//   memory and then raises route_flags[e] to the call's epoch.
+//   dot product and the wave needs no block-wide norm.  It writes the
+//   logits, and each one tagged with the call's epoch to logit_tag.
 //   Shared gate/up block: RMSNorm into LDS, then 8 inter rows of the shared
 //   expert's SwiGLU output for every row (its streaming covers the router's
-//   and the plan's latency).  The first of these blocks publishes xn.
-//   Plan block: waits for every router wave, routes the batch, publishes
-//   indices, weights, row flags, status and the plan, and clears the down
-//   kernel's tile counters and the router flags.  A wait that gives up
-//   records the call's epoch in timeout_epoch (reported as
-//   MOE_FLAG_SYNC_TIMEOUT by moe_ffn_status).
+//   and the plan's latency).  The norm comes before the block requests its
+//   weights, which lets the router's weight rows reach the memory queues
+//   first.  The first of these blocks publishes xn.
+//   Plan block: routes the batch (wave r polls row r's tagged logits),
+//   publishes indices, weights, row flags, status and the plan, and clears
+//   the down kernel's tile counters.  A wait that gives up records the
+//   call's epoch in timeout_epoch (reported as MOE_FLAG_SYNC_TIMEOUT by
+//   moe_ffn_status).
 template <int H, int I>
 __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
-  extern __shared__ float xs[];  // [R][H]
+  extern __shared__ __attribute__((aligned(16))) float xs[];  // [R][H]
   __shared__ int s_idx[kDecodeMaxSlots];
   __shared__ float s_w[kDecodeMaxSlots];
   __shared__ unsigned char s_valid[kDecodeMaxSlots];
@@ -402,9 +507,12 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   const int nrb = (E + 3) / 4, nsh = I / kShRows;
   const int b = blockIdx.x;
   if (b == nrb + nsh) {  // plan block
-    const bool ok = wait_flags(sy->route_flags, E, a.epoch);
-    route_rows(a, s_idx, s_w, s_valid, s_flags);
+    __shared__ int s_ok;
+    if (threadIdx.x == 0) s_ok = 1;
     __syncthreads();
+    if (!route_rows(a, s_idx, s_w, s_valid, s_flags) && lane == 0) s_ok = 0;
+    __syncthreads();
+    const bool ok = s_ok;
     if (wv == 0) build_plan(s_idx, s_w, s_valid, R, K, E, &P);
     __syncthreads();
     for (int s = threadIdx.x; s < R * K; s += kThreads) {
@@ -420,7 +528,6 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
       if (!ok) store_flag(&sy->timeout_epoch, a.epoch);
     }
     for (int i = threadIdx.x; i < kDecodeMaxTiles; i += kThreads) sy->tile_cnt[i] = 0;
-    for (int i = threadIdx.x; i < kMaxExperts; i += kThreads) store_flag(&sy->route_flags[i], 0u);
     const int* ps = (const int*)&P;
     int* pd = (int*)a.plan;
     for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += kThreads) pd[i] = ps[i];
@@ -433,7 +540,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
       if (x == 0)
         for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
     };
-    gateup_tile<H, I, kShRows>(a.gate_sh, a.up_sh, xs, R, x, nsh, a.h32, kDecodeMaxSlots, stage);
+    stage();
+    gateup_tile<H, I, kShRows>(a.gate_sh, a.up_sh, xs, R, x, nsh, a.h32, kDecodeMaxSlots, [] {});
     return;
   }
   // router wave: whole row of W[e] (8 loads) plus x and g straight from memory
@@ -477,16 +585,11 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
       const float q2 = wave_sum(ss[r]);
       if (lane == 0) {
         const float v = d * (1.0f / sqrtf(q2 / (float)H + a.eps));
-        store_wt(&a.logits[(int64_t)r * E + e], v);
-        if (a.layer_kind == MOE_LAYER_SCORE)
-          __hip_atomic_store(&a.key[(int64_t)r * E + e], score_key(v, a.bias[e]), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        a.logits[(int64_t)r * E + e] = v;
+        __hip_atomic_store(&sy->logit_tag[r * E + e], ((uint64_t)a.epoch << 32) | __float_as_uint(v),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-  }
-  if (lane == 0) {
-    sync_stores();
-    store_flag(&sy->route_flags[e], a.epoch);
   }
 }
 
@@ -500,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
 // expert -> h32.
 template <int H, int I>
 __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
-  extern __shared__ float xs[];  // [nr][H] activations, or [R][I] shared h
+  extern __shared__ __attribute__((aligned(16))) float xs[];  // [nr][H] activations, or [R][I] shared h
   constexpr int nsd = H / kDnRows, gut = I / kGuRows;
   const int b = blockIdx.x;
   if (b < nsd) {

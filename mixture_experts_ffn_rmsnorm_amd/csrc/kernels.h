@@ -22,7 +22,7 @@ struct FwdArgs {
   float eps;
   int layer_kind;
   int64_t table_rows;
-  uint32_t epoch;  // per-call tag written by the decode router blocks
+  uint32_t epoch;  // per-call tag of the decode path's tagged words
   // inputs / outputs
   const float* x;
   const int32_t* token_ids;
@@ -41,7 +41,6 @@ struct FwdArgs {
   uint32_t* status;
   DecodeSync* sync;
   float* logits;
-  double* key;
   int32_t* idx;
   float* wts;
   uint32_t* rowflags;

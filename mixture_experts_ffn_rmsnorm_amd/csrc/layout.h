@@ -37,21 +37,22 @@ struct DecodePlan {
 };
 
 // Cross-workgroup signalling words of the decode path, after the status word.
-// Flags carry the call's epoch when set; counters are zeroed by the first
-// kernel of the call for the second.
+// A tagged word carries the call's epoch in its upper half and a 32-bit
+// value in its lower half, written and read whole, so its reader polls the
+// data itself; counters are zeroed by the first kernel of the call for the
+// later ones.
 constexpr int kDecodeMaxTiles = 256;  // down column tiles (hidden/32) and shared gate/up tiles (inter/8)
 struct DecodeSync {
   uint32_t last_epoch;                   // epoch of the last decode call (0 after a prefill call)
   uint32_t timeout_epoch;                // epoch of a call in which an in-kernel wait gave up
   uint32_t pad[14];
-  uint32_t route_flags[kMaxExperts];     // router wave e done
+  uint64_t logit_tag[kDecodeMaxRows * kMaxExperts];  // router wave -> plan block: epoch | f32 logit bits
   uint32_t tile_cnt[kDecodeMaxTiles];    // groups finished per down column tile
 };
 
 struct Layout {
   size_t status;     // u32 status word, then the decode path's sync words (DecodeSync)
   size_t logits;     // f32 [R][E]
-  size_t key;        // f64 [R][E]   selection keys sigmoid(logit) + bias (decode path)
   size_t idx;        // i32 [R][K]
   size_t wts;        // f32 [R][K]
   size_t rowflags;   // u32 [R]
@@ -88,7 +89,6 @@ inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
   };
   L->status = take(64 + sizeof(DecodeSync));
   L->logits = take(r * E * 4);
-  L->key = take(r * E * 8);
   L->idx = take(S * 4);
   L->wts = take(S * 4);
   L->rowflags = take(r * 4);
