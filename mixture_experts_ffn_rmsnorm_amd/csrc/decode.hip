@@ -45,7 +45,10 @@ constexpr int kMaxPolls = 1 << 18;
 // pre() runs once after the first NBUF rows are requested (staging the
 // activations there overlaps it with the first weight fetch; it must end
 // with a barrier if it fills LDS); sink(j, part) receives each lane's
-// partial sums part[0..nr) of row j (reduce them with wave_sum).
+// partial sums part[0..nr) of row j (reduce them with wave_sum); it must not
+// store to global memory: loads and stores share one wait counter, and a
+// store among the weight loads makes every later wait drain them all.
+// nrows is a positive multiple of NBUF.
 template <int LEN, int NBUF, class RowPtr, class Pre, class Sink>
 __device__ __forceinline__ void stream_rows(int nrows, RowPtr rowptr, const float* act, int nr, Pre pre, Sink sink) {
   static_assert(LEN % 256 == 0, "row length must be a multiple of 256");
@@ -59,39 +62,53 @@ __device__ __forceinline__ void stream_rows(int nrows, RowPtr rowptr, const floa
     for (int c = 0; c < NCH; ++c)
       if (c < NCH - 1 || full) q[b][c] = load_stream(p + c * 512);
   };
+  auto dot_row = [&](int b, float (&part)[4]) {
 #pragma unroll
-  for (int b = 0; b < NBUF; ++b)
-    if (b < nrows) load_row(b, b);
-  pre();
-#pragma unroll 1
-  for (int j0 = 0; j0 < nrows; j0 += NBUF) {
+    for (int r = 0; r < 4; ++r) part[r] = 0.f;
 #pragma unroll
-    for (int b = 0; b < NBUF; ++b) {
-      const int j = j0 + b;
-      if (j < nrows) {
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NCH; ++c) {
+      if (c < NCH - 1 || full) {
+        float f[8];
+        unpack8(q[b][c], f);
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          if (c < NCH - 1 || full) {
-            float f[8];
-            unpack8(q[b][c], f);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (r < nr) {
-                const float4* xp = (const float4*)(act + r * LEN + c * 512 + lane * 8);
-                const float4 u = xp[0], v = xp[1];
-                float s = part[r];
-                s = fmaf(f[0], u.x, s); s = fmaf(f[1], u.y, s); s = fmaf(f[2], u.z, s); s = fmaf(f[3], u.w, s);
-                s = fmaf(f[4], v.x, s); s = fmaf(f[5], v.y, s); s = fmaf(f[6], v.z, s); s = fmaf(f[7], v.w, s);
-                part[r] = s;
-              }
-            }
+        for (int r = 0; r < 4; ++r) {
+          if (r < nr) {
+            const float4* xp = (const float4*)(act + r * LEN + c * 512 + lane * 8);
+            const float4 u = xp[0], v = xp[1];
+            float s = part[r];
+            s = fmaf(f[0], u.x, s); s = fmaf(f[1], u.y, s); s = fmaf(f[2], u.z, s); s = fmaf(f[3], u.w, s);
+            s = fmaf(f[4], v.x, s); s = fmaf(f[5], v.y, s); s = fmaf(f[6], v.z, s); s = fmaf(f[7], v.w, s);
+            part[r] = s;
           }
         }
-        if (j + NBUF < nrows) load_row(b, j + NBUF);
-        sink(j, part);
       }
     }
+  };
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) load_row(b, b);
+  pre();
+  // Steady state: every row of the group has a successor NBUF rows on, whose
+  // loads go out as soon as the row is multiplied.  The loads are
+  // unconditional, so the compiler's wait for each chunk counts exactly the
+  // loads issued after it, and NBUF rows stay in flight (a conditional
+  // refill makes every wait assume it did not happen, and each wave then
+  // also waits for the row it has just requested).
+#pragma unroll 1
+  for (int j0 = 0; j0 + NBUF < nrows; j0 += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      float part[4];
+      dot_row(b, part);
+      load_row(b, j0 + b + NBUF);
+      sink(j0 + b, part);
+    }
+  }
+  // last group: no further loads
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) {
+    float part[4];
+    dot_row(b, part);
+    sink(nrows - NBUF + b, part);
   }
 }
 
@@ -193,8 +210,11 @@ __device__ __forceinline__ bool wait_flags(const uint32_t* flags, int n, uint32_
 template <int H, int I, int PAIRS, class Pre>
 __device__ __forceinline__ void gateup_tile(const uint16_t* gbase, const uint16_t* ubase, const float* xs, int nr,
                                             int x, int tiles, float* h32, int hout, Pre pre) {
+  constexpr int W = kThreads / kWave, PPW = PAIRS / W;  // pairs per wave
+  static_assert(PPW * 4 <= kWave, "one lane per result");
+  __shared__ float s_res[W * PPW * 4];  // results wait here until the stream ends
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  constexpr int W = kThreads / kWave;
+  float* res = s_res + wv * PPW * 4;
   float g[4];
   auto row_of = [&](int j) { return x + (wv + (j >> 1) * W) * tiles; };
   auto rowptr = [&](int j) { return ((j & 1) ? ubase : gbase) + (int64_t)row_of(j) * H; };
@@ -204,17 +224,18 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* gbase, const uint16_
       for (int r = 0; r < 4; ++r) g[r] = part[r];
       return;
     }
-    const int i = row_of(j);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (r < nr) {
         const float gs = wave_sum(g[r]);
         const float us = wave_sum(part[r]);
-        if (lane == 0) store_wt(&h32[(int64_t)(hout + r) * I + i], swiglu_f32(gs, us));
+        if (lane == 0) res[(j >> 1) * 4 + r] = swiglu_f32(gs, us);
       }
     }
   };
-  stream_rows<H, 2>(2 * (PAIRS / W), rowptr, xs, nr, pre, sink);
+  stream_rows<H, 2>(2 * PPW, rowptr, xs, nr, pre, sink);
+  const int p = lane >> 2, r = lane & 3;
+  if (p < PPW && r < nr) store_wt(&h32[(int64_t)(hout + r) * I + row_of(2 * p)], res[lane]);
 }
 
 // Distinct (expert, row) pairs of the batch, grouped by expert (ascending),
@@ -457,20 +478,26 @@ __device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R) {
 template <int H, int I, class Pre>
 __device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs, int nr, int x, float* d32, int ent,
                                           Pre pre) {
+  constexpr int W = kThreads / kWave, RPW = kDnRows / W;  // rows per wave
+  static_assert(RPW * 4 <= kWave, "one lane per result");
+  __shared__ float s_res[kDnRows * 4];  // results wait here until the stream ends
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  float* res = s_res + wv * RPW * 4;
   constexpr int tiles = H / kDnRows;
-  auto row_of = [&](int j) { return x + (wv + j * 4) * tiles; };
+  auto row_of = [&](int j) { return x + (wv + j * W) * tiles; };
   auto rowptr = [&](int j) { return wbase + (int64_t)row_of(j) * I; };
   auto sink = [&](int j, const float (&part)[4]) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (r < nr) {
         const float v = wave_sum(part[r]);
-        if (lane == 0) store_wt(&d32[(int64_t)(ent + r) * H + row_of(j)], v);
+        if (lane == 0) res[j * 4 + r] = v;
       }
     }
   };
-  stream_rows<I, 2>(kDnRows / 4, rowptr, hs, nr, pre, sink);
+  stream_rows<I, 2>(RPW, rowptr, hs, nr, pre, sink);
+  const int j = lane >> 2, r = lane & 3;
+  if (j < RPW && r < nr) store_wt(&d32[(int64_t)(ent + r) * H + row_of(j)], res[lane]);
 }
 
 // ---------------------------------------------------------------------------
