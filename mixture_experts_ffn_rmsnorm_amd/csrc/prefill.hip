@@ -453,12 +453,24 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
 // group, then in blocks of 4 row tiles x 8 column tiles, and handed out so
 // that each XCD takes a contiguous run of them: the tiles that share
 // activation tiles and weight slices run at the same time behind one L2.
-constexpr int BM = 256, BROWS = 256, BK = 64;
-constexpr int kGT = 512;       // threads per GEMM block: 8 waves, 2 per SIMD
-constexpr int GWN = 4;         // waves along the B rows (2 x 4 wave grid)
-constexpr int WM = 4, WN = 2;  // A and B fragments per wave
-constexpr int kStages = 2;
-constexpr int kSlab = 64;      // epilogue rows staged per pass
+constexpr int BROWS = 256, BK = 64;
+constexpr int kGT = 512;  // threads per GEMM block: 8 waves, 2 per SIMD
+constexpr int GWN = 4;    // waves along the B rows (2 x 4 wave grid)
+constexpr int WN = 2;     // B fragments per wave
+constexpr int kSlab = 64; // epilogue rows staged per pass
+
+// Row-tile configurations.  Big: 256 rows per tile (4 A fragments per wave)
+// and a 2-stage ring, for groups of many rows.  Small: 64 rows (1 A
+// fragment per wave) and a 3-stage ring, for groups of a few rows: there the
+// kernel mostly streams weights, and with the A tile 4x smaller the ring
+// holds two weight k-tiles in flight per compute unit instead of one.
+template <int BM_, int WM_, int STAGES_>
+struct GemmCfg {
+  static constexpr int BM = BM_, WM = WM_, kStages = STAGES_;
+  static_assert(BM == 2 * WM * 32, "2 x 4 wave grid, 32-row fragments");
+};
+using GemmBig = GemmCfg<256, 4, 2>;
+using GemmSmall = GemmCfg<64, 1, 3>;
 
 // output columns per block tile
 template <int MODE>
@@ -466,15 +478,17 @@ struct GemmShape {
   static constexpr int BN = MODE == 0 ? BROWS / 2 : BROWS;
 };
 
-template <int MODE, int KD, int ND>
+template <int MODE, int KD, int ND, class Cfg>
 __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
+  constexpr int BM = Cfg::BM, WM = Cfg::WM, kStages = Cfg::kStages;
   constexpr int BN = GemmShape<MODE>::BN;
   constexpr int NT = ND / BN;                // column tiles per group
   constexpr int NK = KD / BK;                // k slices
   constexpr int A_ST = BM * BK * 2, B_ST = BROWS * BK * 2, ST = A_ST + B_ST;
-  constexpr int AI = A_ST / 16 / kGT;  // A DMA instructions per thread per k-tile (4)
+  constexpr int AI = A_ST / 16 / kGT;  // A DMA instructions per thread per k-tile (4 or 1)
   constexpr int BI = B_ST / 16 / kGT;  // B DMA instructions per thread per k-tile (4)
-  static_assert(AI % 2 == 0 && BI % 2 == 0, "chunk parity alternates with the instruction index");
+  static_assert(AI >= 1 && BI >= 1 && AI * kGT * 16 == A_ST && BI * kGT * 16 == B_ST, "DMA tiling");
+  static_assert(kStages == 2 || AI == 1, "the ring's wait counts at most one A load per thread and stage");
   // epilogue staging per 64-row slab, reusing the ring: f32 [64][BROWS + 4]
   // (gate/up: gate columns, then up columns)
   constexpr int CPITCH = BROWS + 4;
@@ -537,9 +551,9 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
                          : wn * (WN * 32) + j * 32) + (lane & 31);
   // DMA: instruction i of a wave fills 8 tile rows, (wave * count + i) * 8 +
   // lane / 8; the lane moves chunk (lane & 7) ^ swz(row) = (lane & 7) ^
-  // (lane / 8) ^ (i & 1) of its row
-  const int chunk0 = ((lane & 7) ^ (lane >> 3)) * 16;  // bytes, even i
-  const int chunk1 = chunk0 ^ 16;                       // odd i
+  // (lane / 8) ^ ((wave * count + i) & 1) of its row
+  const int chunk0 = ((lane & 7) ^ (lane >> 3)) * 16;  // bytes, even row group
+  const int chunk1 = chunk0 ^ 16;                       // odd row group
 
   for (int tile = first; tile < total; tile += gridDim.x) {
     // locate the group: largest g with s_tbase[g] <= tile (empty groups
@@ -597,7 +611,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
       if (MODE == 0) r = shared ? (int64_t)m : (int64_t)a.perm[(int64_t)g * R + m];
       else r = (int64_t)s_rbase[g] + m;
       asrc[i] = (MODE == 0 ? (const unsigned char*)a.xn16 : (const unsigned char*)a.h16) + r * (KD * 2) +
-                ((i & 1) ? chunk1 : chunk0);
+                (((wv * AI + i) & 1) ? chunk1 : chunk0);
     }
     // B: each wave's rows are all gate or all up rows
     const unsigned char* bsrc[BI];
@@ -615,8 +629,12 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < BI; ++i)
-        bsrc[i] = (const unsigned char*)bmat + (int64_t)(brow0 + i * 8) * (KD * 2) + ((i & 1) ? chunk1 : chunk0);
+        bsrc[i] = (const unsigned char*)bmat + (int64_t)(brow0 + i * 8) * (KD * 2) +
+                  (((wv * BI + i) & 1) ? chunk1 : chunk0);
     }
+    // whether this wave loads A rows at all (the small configuration's one
+    // A load per thread and k-tile; the big one waits with vmcnt(0))
+    const bool a_loads = m0 + wv * AI * 8 < cntg;
     // k-tile `src` into ring buffer `buf`
     // (A row groups wholly past the group's end are not loaded: the ring
     // waits with vmcnt(0), so the number of loads may differ per wave)
@@ -671,7 +689,8 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     issue(0, 0);
     wait_vmcnt<0>();
     __syncthreads();
-    issue(1, 1);
+#pragma unroll
+    for (int st = 1; st < kStages; ++st) issue(st < NK ? st : NK - 1, st);
     {
       uint4 rb[WN];
       read_step(0, 0, af, rb, NV);
@@ -692,7 +711,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     // while the next step's fragment of the previous column converts.
 #pragma unroll 1
     for (int kt = 0; kt < NK; ++kt) {
-      const int buf = kt & 1;
+      const int buf = kt % kStages, nbuf = (kt + 1) % kStages;
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         half8 afn[WM], bfn[WN];
@@ -703,12 +722,15 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
           mfma_j(0);
           __builtin_amdgcn_sched_barrier(0);
         } else {
-          wait_vmcnt<0>();
-          __syncthreads();  // k-tile kt+1 landed; every wave is done reading buffer `buf`
-          read_step(buf ^ 1, 0, afn, rb, NV);
+          // k-tile kt+1 landed for this wave: only the loads of the
+          // kStages-2 later tiles may still be in flight
+          if (kStages == 2 || !a_loads) wait_vmcnt<(kStages - 2) * BI>();
+          else wait_vmcnt<(kStages - 2) * (BI + 1)>();
+          __syncthreads();  // k-tile kt+1 landed for every wave; every wave is done reading buffer `buf`
+          read_step(nbuf, 0, afn, rb, NV);
           __builtin_amdgcn_sched_barrier(0);
           mfma_j(0);
-          issue(kt + 2 < NK ? kt + 2 : NK - 1, buf);
+          issue(kt + kStages < NK ? kt + kStages : NK - 1, buf);
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -747,13 +769,31 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     for (int sl = 0; sl < BM / kSlab; ++sl) {
       __syncthreads();  // the ring (or the previous slab) is free
       __builtin_amdgcn_sched_barrier(0);  // keep each slab's accumulator reads in place
-      if (wm == sl / 2) {
+      if constexpr (WM * 32 >= kSlab) {
+        // a wave row spans whole slabs: slab sl holds fragments
+        // (sl % S) * F .. + F-1 of wave row sl / S (F per slab, S slabs per row)
+        constexpr int F = kSlab / 32, S = WM / F;
+        if (wm == sl / S) {
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          const int i = (sl & 1) * 2 + ii;
+          for (int ii = 0; ii < F; ++ii) {
+            const int i = (sl % S) * F + ii;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int rl = ii * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+#pragma unroll
+              for (int j = 0; j < WN; ++j) ((float*)s_ring)[rl * CPITCH + brow[j]] = acc[i][j][v];
+            }
+          }
+        }
+      } else {
+        // a slab spans several wave rows: every fragment lands in slab 0
+        static_assert(BM == kSlab, "one slab");
+#pragma unroll
+        for (int i = 0; i < WM; ++i) {
+          const int base = wm * (WM * 32) + i * 32;  // tile row of fragment i
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int rl = ii * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int rl = base + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 #pragma unroll
             for (int j = 0; j < WN; ++j) ((float*)s_ring)[rl * CPITCH + brow[j]] = acc[i][j][v];
           }
@@ -851,13 +891,18 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   err = launch("pre_sort", (const void*)k_pre_sort, dim3(a.E + 1), dim3(kThreads), 0, s, &args);
   if (err != hipSuccess) return err;
   const int grid = gemm_grid();
-  err = launch("gemm_gateup_swiglu", (const void*)k_gemm<0, H, I>, dim3(grid), dim3(kGT), 0, s, &args);
+  // groups of a few rows on average: the small row tile and the deeper ring
+  const bool small = (int64_t)a.R * a.K <= 32LL * a.E;
+  err = launch("gemm_gateup_swiglu",
+               small ? (const void*)k_gemm<0, H, I, GemmSmall> : (const void*)k_gemm<0, H, I, GemmBig>, dim3(grid),
+               dim3(kGT), 0, s, &args);
   if (err != hipSuccess) return err;
-  err = launch("gemm_down", (const void*)k_gemm<1, I, H>, dim3(grid), dim3(kGT), 0, s, &args);
+  err = launch("gemm_down", small ? (const void*)k_gemm<1, I, H, GemmSmall> : (const void*)k_gemm<1, I, H, GemmBig>,
+               dim3(grid), dim3(kGT), 0, s, &args);
   if (err != hipSuccess) return err;
-  const int64_t sh_tiles = (a.R + BM - 1) / BM * (H / GemmShape<2>::BN);
+  const int64_t sh_tiles = (a.R + GemmBig::BM - 1) / GemmBig::BM * (H / GemmShape<2>::BN);
   const int sh_grid = sh_tiles < grid ? (int)sh_tiles : grid;
-  return launch("gemm_down_shared_reduce", (const void*)k_gemm<2, I, H>, dim3(sh_grid), dim3(kGT), 0, s,
+  return launch("gemm_down_shared_reduce", (const void*)k_gemm<2, I, H, GemmBig>, dim3(sh_grid), dim3(kGT), 0, s,
                 &args);
 }
 
