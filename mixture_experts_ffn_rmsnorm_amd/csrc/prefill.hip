@@ -453,42 +453,49 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
 // group, then in blocks of 4 row tiles x 8 column tiles, and handed out so
 // that each XCD takes a contiguous run of them: the tiles that share
 // activation tiles and weight slices run at the same time behind one L2.
-constexpr int BROWS = 256, BK = 64;
 constexpr int kGT = 512;  // threads per GEMM block: 8 waves, 2 per SIMD
 constexpr int GWN = 4;    // waves along the B rows (2 x 4 wave grid)
-constexpr int WN = 2;     // B fragments per wave
 constexpr int kSlab = 64; // epilogue rows staged per pass
 
-// Row-tile configurations.  Big: 256 rows per tile (4 A fragments per wave)
-// and a 2-stage ring, for groups of many rows.  Small: 64 rows (1 A
-// fragment per wave) and a 3-stage ring, for groups of a few rows: there the
-// kernel mostly streams weights, and with the A tile 4x smaller the ring
-// holds two weight k-tiles in flight per compute unit instead of one.
-template <int BM_, int WM_, int STAGES_>
+// Tile configurations: BM tile rows (WM A fragments per wave), BROWS tile B
+// rows (WN B fragments per wave), k-tiles of BK held in LDS as BK/64 halves
+// of 64 k (one 128-byte row each), a ring of STAGES k-tiles.
+//   Big: 256 x 256, BK 64, 2 stages -- groups of many rows.
+//   Small: 64 x 128, BK 128, 3 stages -- groups of a few rows, where the
+//   kernel mostly streams weights: a lane fetches the two adjacent 128-byte
+//   lines of a weight row back to back, so each row is read 256 bytes at a
+//   time (DRAM page locality), and two k-tiles are in flight per compute
+//   unit.
+template <int BM_, int WM_, int BROWS_, int WN_, int BK_, int STAGES_>
 struct GemmCfg {
-  static constexpr int BM = BM_, WM = WM_, kStages = STAGES_;
-  static_assert(BM == 2 * WM * 32, "2 x 4 wave grid, 32-row fragments");
+  static constexpr int BM = BM_, WM = WM_, BROWS = BROWS_, WN = WN_, BK = BK_, kStages = STAGES_;
+  static_assert(BM == 2 * WM * 32 && BROWS == GWN * WN * 32, "2 x 4 wave grid, 32-row fragments");
+  static_assert(BK % 64 == 0, "k-tiles of whole 64-k halves");
 };
-using GemmBig = GemmCfg<256, 4, 2>;
-using GemmSmall = GemmCfg<64, 1, 3>;
+using GemmBig = GemmCfg<256, 4, 256, 2, 64, 2>;
+using GemmSmall = GemmCfg<64, 1, 128, 1, 128, 3>;
 
 // output columns per block tile
-template <int MODE>
+template <int MODE, class Cfg>
 struct GemmShape {
-  static constexpr int BN = MODE == 0 ? BROWS / 2 : BROWS;
+  static constexpr int BN = MODE == 0 ? Cfg::BROWS / 2 : Cfg::BROWS;
 };
 
 template <int MODE, int KD, int ND, class Cfg>
 __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
-  constexpr int BM = Cfg::BM, WM = Cfg::WM, kStages = Cfg::kStages;
-  constexpr int BN = GemmShape<MODE>::BN;
+  constexpr int BM = Cfg::BM, WM = Cfg::WM, BROWS = Cfg::BROWS, WN = Cfg::WN, BK = Cfg::BK;
+  constexpr int kStages = Cfg::kStages;
+  constexpr int BN = GemmShape<MODE, Cfg>::BN;
   constexpr int NT = ND / BN;                // column tiles per group
   constexpr int NK = KD / BK;                // k slices
-  constexpr int A_ST = BM * BK * 2, B_ST = BROWS * BK * 2, ST = A_ST + B_ST;
-  constexpr int AI = A_ST / 16 / kGT;  // A DMA instructions per thread per k-tile (4 or 1)
-  constexpr int BI = B_ST / 16 / kGT;  // B DMA instructions per thread per k-tile (4)
-  static_assert(AI >= 1 && BI >= 1 && AI * kGT * 16 == A_ST && BI * kGT * 16 == B_ST, "DMA tiling");
-  static_assert(kStages == 2 || AI == 1, "the ring's wait counts at most one A load per thread and stage");
+  constexpr int NH = BK / 64;              // 64-k halves per k-tile
+  constexpr int HA = BM * 128, HB = BROWS * 128;  // bytes of one half of the A / B tile
+  constexpr int A_ST = NH * HA, B_ST = NH * HB, ST = A_ST + B_ST;
+  constexpr int AI = A_ST / 16 / kGT;  // A DMA instructions per thread per k-tile
+  constexpr int BI = B_ST / 16 / kGT;  // B DMA instructions per thread per k-tile
+  constexpr int AG = AI / NH, BG = BI / NH;  // 8-row groups per wave (A, B)
+  static_assert(AG >= 1 && BG >= 1 && AI * kGT * 16 == A_ST && BI * kGT * 16 == B_ST, "DMA tiling");
+  static_assert(kStages == 2 || AG == 1, "the ring's wait counts at most one A row group per wave");
   // epilogue staging per 64-row slab, reusing the ring: f32 [64][BROWS + 4]
   // (gate/up: gate columns, then up columns)
   constexpr int CPITCH = BROWS + 4;
@@ -505,8 +512,8 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
   const int E = a.E, G = E + 1, K = a.K;
   const int64_t R = a.R;
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)s_ring;
-  const uint32_t a_wave = __builtin_amdgcn_readfirstlane(wv * AI * 1024);
-  const uint32_t b_wave = __builtin_amdgcn_readfirstlane(A_ST + wv * BI * 1024);
+  const uint32_t a_wave = __builtin_amdgcn_readfirstlane(wv * AG * 1024);
+  const uint32_t b_wave = __builtin_amdgcn_readfirstlane(A_ST + wv * BG * 1024);
 
   // row bases of every group, and tile bases of the groups this mode covers
   if (wv == 0) {
@@ -547,11 +554,12 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
   for (int i = 0; i < WM; ++i) arow[i] = wm * (WM * 32) + i * 32 + (lane & 31);
 #pragma unroll
   for (int j = 0; j < WN; ++j)
-    brow[j] = (MODE == 0 ? (j < WN / 2 ? 0 : BROWS / 2) + wn * (WN / 2) * 32 + (j % (WN / 2)) * 32
-                         : wn * (WN * 32) + j * 32) + (lane & 31);
-  // DMA: instruction i of a wave fills 8 tile rows, (wave * count + i) * 8 +
-  // lane / 8; the lane moves chunk (lane & 7) ^ swz(row) = (lane & 7) ^
-  // (lane / 8) ^ ((wave * count + i) & 1) of its row
+    brow[j] = (MODE == 0 && WN >= 2 ? (j < WN / 2 ? 0 : BROWS / 2) + wn * (WN / 2) * 32 + (j % (WN / 2 > 0 ? WN / 2 : 1)) * 32
+                                    : wn * (WN * 32) + j * 32) + (lane & 31);
+  // DMA: row group q of a wave (8 tile rows, (wave * groups + q) * 8 +
+  // lane / 8) is filled half by half, the halves of a row back to back; the
+  // lane moves chunk (lane & 7) ^ swz(row) = (lane & 7) ^ (lane / 8) ^
+  // ((wave * groups + q) & 1) of its row
   const int chunk0 = ((lane & 7) ^ (lane >> 3)) * 16;  // bytes, even row group
   const int chunk1 = chunk0 ^ 16;                       // odd row group
 
@@ -602,21 +610,21 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
 
     // DMA sources.  Rows past the group's end read its last row; their
     // results are never stored.
-    const unsigned char* asrc[AI];
+    const unsigned char* asrc[AG];
 #pragma unroll
-    for (int i = 0; i < AI; ++i) {
-      const int row = (wv * AI + i) * 8 + (lane >> 3);
+    for (int i = 0; i < AG; ++i) {
+      const int row = (wv * AG + i) * 8 + (lane >> 3);
       const int m = (m0 + row < cntg) ? m0 + row : cntg - 1;
       int64_t r;
       if (MODE == 0) r = shared ? (int64_t)m : (int64_t)a.perm[(int64_t)g * R + m];
       else r = (int64_t)s_rbase[g] + m;
       asrc[i] = (MODE == 0 ? (const unsigned char*)a.xn16 : (const unsigned char*)a.h16) + r * (KD * 2) +
-                (((wv * AI + i) & 1) ? chunk1 : chunk0);
+                (((wv * AG + i) & 1) ? chunk1 : chunk0);
     }
     // B: each wave's rows are all gate or all up rows
-    const unsigned char* bsrc[BI];
+    const unsigned char* bsrc[BG];
     {
-      const int bw_row = wv * BI * 8;  // first tile B row of this wave
+      const int bw_row = wv * BG * 8;  // first tile B row of this wave
       const uint16_t* bmat;
       int brow0;
       if (MODE == 0) {
@@ -628,29 +636,33 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
         brow0 = n0 + bw_row + (lane >> 3);
       }
 #pragma unroll
-      for (int i = 0; i < BI; ++i)
+      for (int i = 0; i < BG; ++i)
         bsrc[i] = (const unsigned char*)bmat + (int64_t)(brow0 + i * 8) * (KD * 2) +
-                  (((wv * BI + i) & 1) ? chunk1 : chunk0);
+                  (((wv * BG + i) & 1) ? chunk1 : chunk0);
     }
     // whether this wave loads A rows at all (the small configuration's one
-    // A load per thread and k-tile; the big one waits with vmcnt(0))
-    const bool a_loads = m0 + wv * AI * 8 < cntg;
+    // A row group per wave; the big one waits with vmcnt(0))
+    const bool a_loads = m0 + wv * AG * 8 < cntg;
     // k-tile `src` into ring buffer `buf`
     // (A row groups wholly past the group's end are not loaded: the ring
     // waits with vmcnt(0), so the number of loads may differ per wave)
     auto issue = [&](int src, int buf) {
       const uint32_t base = ring + (uint32_t)buf * ST;
 #pragma unroll
-      for (int i = 0; i < AI; ++i)
-        if (m0 + (wv * AI + i) * 8 < cntg) dma16(asrc[i] + src * (BK * 2), base + a_wave + i * 1024);
+      for (int i = 0; i < AG; ++i)
+        if (m0 + (wv * AG + i) * 8 < cntg)
 #pragma unroll
-      for (int i = 0; i < BI; ++i) dma16(bsrc[i] + src * (BK * 2), base + b_wave + i * 1024);
+          for (int h = 0; h < NH; ++h) dma16(asrc[i] + src * (BK * 2) + h * 128, base + a_wave + h * HA + i * 1024);
+#pragma unroll
+      for (int i = 0; i < BG; ++i)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) dma16(bsrc[i] + src * (BK * 2) + h * 128, base + b_wave + h * HB + i * 1024);
     };
     // fragment reads of k-step `st` (16 k) from ring buffer `buf`
     auto read_step = [&](int buf, int st, half8 (&af)[WM], uint4 (&rb)[WN], int nv) {
-      const unsigned char* As = s_ring + buf * ST;
-      const unsigned char* Bs = As + A_ST;
-      const int c = 2 * st + (lane >> 5);
+      const unsigned char* As = s_ring + buf * ST + (st >> 2) * HA;
+      const unsigned char* Bs = s_ring + buf * ST + A_ST + (st >> 2) * HB;
+      const int c = 2 * (st & 3) + (lane >> 5);
 #pragma unroll
       for (int i = 0; i < WM; ++i)
         if (i < nv) af[i] = *(const half8*)(As + arow[i] * 128 + ((c ^ swz(arow[i])) << 4));
@@ -725,7 +737,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
           // k-tile kt+1 landed for this wave: only the loads of the
           // kStages-2 later tiles may still be in flight
           if (kStages == 2 || !a_loads) wait_vmcnt<(kStages - 2) * BI>();
-          else wait_vmcnt<(kStages - 2) * (BI + 1)>();
+          else wait_vmcnt<(kStages - 2) * (BI + NH)>();
           __syncthreads();  // k-tile kt+1 landed for every wave; every wave is done reading buffer `buf`
           read_step(nbuf, 0, afn, rb, NV);
           __builtin_amdgcn_sched_barrier(0);
@@ -900,7 +912,7 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   err = launch("gemm_down", small ? (const void*)k_gemm<1, I, H, GemmSmall> : (const void*)k_gemm<1, I, H, GemmBig>,
                dim3(grid), dim3(kGT), 0, s, &args);
   if (err != hipSuccess) return err;
-  const int64_t sh_tiles = (a.R + GemmBig::BM - 1) / GemmBig::BM * (H / GemmShape<2>::BN);
+  const int64_t sh_tiles = (a.R + GemmBig::BM - 1) / GemmBig::BM * (H / GemmShape<2, GemmBig>::BN);
   const int sh_grid = sh_tiles < grid ? (int)sh_tiles : grid;
   return launch("gemm_down_shared_reduce", (const void*)k_gemm<2, I, H, GemmBig>, dim3(sh_grid), dim3(kGT), 0, s,
                 &args);
