@@ -912,10 +912,16 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   err = launch("gemm_down", small ? (const void*)k_gemm<1, I, H, GemmSmall> : (const void*)k_gemm<1, I, H, GemmBig>,
                dim3(grid), dim3(kGT), 0, s, &args);
   if (err != hipSuccess) return err;
-  const int64_t sh_tiles = (a.R + GemmBig::BM - 1) / GemmBig::BM * (H / GemmShape<2, GemmBig>::BN);
+  // the shared down covers R rows only: small tiles when big ones would
+  // leave compute units idle
+  const int64_t big_tiles = (a.R + GemmBig::BM - 1) / GemmBig::BM * (H / GemmShape<2, GemmBig>::BN);
+  const bool sh_small = big_tiles < grid;
+  const int64_t sh_tiles =
+      sh_small ? (a.R + GemmSmall::BM - 1) / GemmSmall::BM * (H / GemmShape<2, GemmSmall>::BN) : big_tiles;
   const int sh_grid = sh_tiles < grid ? (int)sh_tiles : grid;
-  return launch("gemm_down_shared_reduce", (const void*)k_gemm<2, I, H, GemmBig>, dim3(sh_grid), dim3(kGT), 0, s,
-                &args);
+  return launch("gemm_down_shared_reduce",
+                sh_small ? (const void*)k_gemm<2, I, H, GemmSmall> : (const void*)k_gemm<2, I, H, GemmBig>,
+                dim3(sh_grid), dim3(kGT), 0, s, &args);
 }
 
 }  // namespace
