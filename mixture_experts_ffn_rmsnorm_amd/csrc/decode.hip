@@ -113,21 +113,36 @@ __device__ __forceinline__ void stream_rows(int nrows, RowPtr rowptr, const floa
 }
 
 // RMSNorm of R (<= 4) rows into LDS: xs[r*H + j] = x[r,j] * (mean x^2 + eps)^-1/2 * g[j].
-// The first floats of xs double as the cross-wave reduction scratch.
+// Every row's loads go out before the first reduction (one memory round
+// trip for the batch, not one per row), and the values stay in registers
+// for the scaled write.  The first floats of xs double as the cross-wave
+// reduction scratch.
 template <int H>
 __device__ __forceinline__ void norm_rows_to_lds(const float* __restrict__ x, const float* __restrict__ g, int R,
                                                  float eps, float* xs) {
   const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
-  constexpr int V = H / 4;  // float4 per row
-  for (int r = 0; r < R; ++r) {
-    float ss = 0.f;
-    for (int i = t; i < V; i += kThreads) {
-      float4 v = ((const float4*)(x + (int64_t)r * H))[i];
-      ss = fmaf(v.x, v.x, ss); ss = fmaf(v.y, v.y, ss);
-      ss = fmaf(v.z, v.z, ss); ss = fmaf(v.w, v.w, ss);
+  constexpr int V = H / 4;                            // float4 per row
+  constexpr int NPT = (V + kThreads - 1) / kThreads;  // float4 per thread and row
+  float4 v[kDecodeMaxRows][NPT];
+#pragma unroll
+  for (int r = 0; r < kDecodeMaxRows; ++r)
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int i = t + k * kThreads;
+      v[r][k] = (r < R && i < V) ? ((const float4*)(x + (int64_t)r * H))[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    ss = wave_sum(ss);
-    if (lane == 0) xs[wv * kDecodeMaxRows + r] = ss;
+#pragma unroll
+  for (int r = 0; r < kDecodeMaxRows; ++r) {
+    if (r < R) {
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < NPT; ++k) {
+        ss = fmaf(v[r][k].x, v[r][k].x, ss); ss = fmaf(v[r][k].y, v[r][k].y, ss);
+        ss = fmaf(v[r][k].z, v[r][k].z, ss); ss = fmaf(v[r][k].w, v[r][k].w, ss);
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) xs[wv * kDecodeMaxRows + r] = ss;
+    }
   }
   __syncthreads();
   float rs[kDecodeMaxRows];
@@ -140,25 +155,50 @@ __device__ __forceinline__ void norm_rows_to_lds(const float* __restrict__ x, co
   }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < kDecodeMaxRows; ++r) {
-    if (r >= R) break;
-    for (int i = t; i < V; i += kThreads) {
-      float4 v = ((const float4*)(x + (int64_t)r * H))[i];
-      float4 gg = ((const float4*)g)[i];
-      float4 o;
-      o.x = v.x * rs[r] * gg.x; o.y = v.y * rs[r] * gg.y; o.z = v.z * rs[r] * gg.z; o.w = v.w * rs[r] * gg.w;
-      ((float4*)(xs + r * H))[i] = o;
+  for (int k = 0; k < NPT; ++k) {
+    const int i = t + k * kThreads;
+    if (i < V) {
+      const float4 gg = ((const float4*)g)[i];
+#pragma unroll
+      for (int r = 0; r < kDecodeMaxRows; ++r) {
+        if (r < R) {
+          float4 o;
+          o.x = v[r][k].x * rs[r] * gg.x; o.y = v[r][k].y * rs[r] * gg.y;
+          o.z = v[r][k].z * rs[r] * gg.z; o.w = v[r][k].w * rs[r] * gg.w;
+          ((float4*)(xs + r * H))[i] = o;
+        }
+      }
     }
   }
   __syncthreads();
 }
 
-// Copy `nr` rows of LEN floats (global rows src[j]) into LDS rows dst + j*LEN.
+// Copy `nr` rows of LEN floats (global rows src[j]) into LDS rows dst + j*LEN,
+// two rows per memory round trip (both rows' loads issued before their
+// stores).
 template <int LEN>
 __device__ __forceinline__ void stage_rows(float* dst, const float* const (&src)[4], int nr) {
-#pragma unroll 1
-  for (int j = 0; j < nr; ++j)
-    for (int i = threadIdx.x; i < LEN / 4; i += kThreads) ((float4*)(dst + j * LEN))[i] = ((const float4*)src[j])[i];
+  constexpr int V = LEN / 4;
+  constexpr int NPT = (V + kThreads - 1) / kThreads;
+#pragma unroll
+  for (int j0 = 0; j0 < kDecodeMaxRows; j0 += 2) {
+    if (j0 >= nr) break;
+    float4 v[2][NPT];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int k = 0; k < NPT; ++k) {
+        const int i = threadIdx.x + k * kThreads;
+        v[j][k] = (j0 + j < nr && i < V) ? ((const float4*)src[j0 + j])[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int k = 0; k < NPT; ++k) {
+        const int i = threadIdx.x + k * kThreads;
+        if (j0 + j < nr && i < V) ((float4*)(dst + (j0 + j) * LEN))[i] = v[j][k];
+      }
+  }
   __syncthreads();
 }
 
@@ -207,7 +247,7 @@ __device__ __forceinline__ bool wait_flags(const uint32_t* flags, int n, uint32_
 // so the blocks working on one expert at the same time read neighbouring
 // rows; wave w streams gate_i then up_i for every fourth of them.  h32 rows
 // hout..hout+nr-1 receive silu(gate . x) * (up . x).
-template <int H, int I, int PAIRS, class Pre>
+template <int H, int I, int PAIRS, int NBUF, class Pre>
 __device__ __forceinline__ void gateup_tile(const uint16_t* gbase, const uint16_t* ubase, const float* xs, int nr,
                                             int x, int tiles, float* h32, int hout, Pre pre) {
   constexpr int W = kThreads / kWave, PPW = PAIRS / W;  // pairs per wave
@@ -233,18 +273,23 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* gbase, const uint16_
       }
     }
   };
-  stream_rows<H, 2>(2 * PPW, rowptr, xs, nr, pre, sink);
+  static_assert((2 * PPW) % NBUF == 0, "whole groups of rows in flight");
+  stream_rows<H, NBUF>(2 * PPW, rowptr, xs, nr, pre, sink);
   const int p = lane >> 2, r = lane & 3;
   if (p < PPW && r < nr) store_wt(&h32[(int64_t)(hout + r) * I + row_of(2 * p)], res[lane]);
 }
 
 // Distinct (expert, row) pairs of the batch, grouped by expert (ascending),
 // rows ascending inside a group; duplicate slots of one row (possible only
-// with a malformed hash table) merge by summing their weights.  Runs on
-// wave 0 with lane s holding slot s; every comparison walks the S slots with
-// uniform readlane broadcasts.
-__device__ void build_plan(const int* s_idx, const float* s_w, const unsigned char* s_valid, int R, int K, int E,
-                           DecodePlan* P) {
+// with a malformed hash table) merge by summing their weights in slot order.
+// Runs on wave 0 with lane s holding slot s: the slots' keys and weights go
+// through LDS once, and every lane then walks them 8 at a time (same-address
+// broadcast reads) comparing in registers.  Loops, not straight-line code:
+// this runs once per call, on a cold instruction cache.
+__device__ __forceinline__ void build_plan(const int* s_idx, const float* s_w, const unsigned char* s_valid,
+                                           int R, int K, int E, DecodePlan* P) {
+  __shared__ __attribute__((aligned(16))) int s_key[kDecodeMaxSlots];
+  __shared__ __attribute__((aligned(16))) float s_kw[kDecodeMaxSlots];
   const int lane = threadIdx.x & (kWave - 1);
   const int S = R * K;
   int e = -1, r = 0;
@@ -258,30 +303,52 @@ __device__ void build_plan(const int* s_idx, const float* s_w, const unsigned ch
   }
   const int kNone = 0x7fffffff;
   const int key = v ? e * 8 + r : kNone;
+  if (lane < kDecodeMaxSlots) {
+    s_key[lane] = key;
+    s_kw[lane] = w;
+  }
+  __builtin_amdgcn_wave_barrier();
+  auto keys8 = [&](int t0, int (&kk)[8]) {
+    const int4 a = *(const int4*)(s_key + t0), b = *(const int4*)(s_key + t0 + 4);
+    kk[0] = a.x; kk[1] = a.y; kk[2] = a.z; kk[3] = a.w; kk[4] = b.x; kk[5] = b.y; kk[6] = b.z; kk[7] = b.w;
+  };
   bool first = v;
   float wsum = 0.f;
-  for (int t = 0; t < S; ++t) {
-    const int kt = __builtin_amdgcn_readlane(key, t);
-    const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), t));
-    if (v && kt == key) {
-      wsum += wt;
-      if (t < lane) first = false;
+#pragma unroll 1
+  for (int t0 = 0; t0 < S; t0 += 8) {
+    int kk[8];
+    keys8(t0, kk);
+    const float4 a = *(const float4*)(s_kw + t0), b = *(const float4*)(s_kw + t0 + 4);
+    const float kw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool eq = v && kk[i] == key;
+      if (eq) wsum += kw[i];
+      first = first && !(eq && t0 + i < lane);
     }
   }
   const uint64_t fmask = __ballot(first);
   int pos = 0;
   bool efirst = first;
-  for (int t = 0; t < S; ++t) {
-    if (!((fmask >> t) & 1)) continue;
-    const int kt = __builtin_amdgcn_readlane(key, t);
-    if (kt < key) ++pos;
-    if ((kt >> 3) == (key >> 3) && kt < key) efirst = false;
+#pragma unroll 1
+  for (int t0 = 0; t0 < S; t0 += 8) {
+    int kk[8];
+    keys8(t0, kk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ft = (fmask >> (t0 + i)) & 1;
+      pos += (ft && kk[i] < key) ? 1 : 0;
+      efirst = efirst && !(ft && (kk[i] >> 3) == (key >> 3) && kk[i] < key);
+    }
   }
   const uint64_t emask = __ballot(efirst);
   int gidx = 0;
-  for (int t = 0; t < S; ++t) {
-    if (!((emask >> t) & 1)) continue;
-    if ((__builtin_amdgcn_readlane(key, t) >> 3) < (key >> 3)) ++gidx;
+#pragma unroll 1
+  for (int t0 = 0; t0 < S; t0 += 8) {
+    int kk[8];
+    keys8(t0, kk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gidx += (((emask >> (t0 + i)) & 1) && (kk[i] >> 3) < (key >> 3)) ? 1 : 0;
   }
   const int ngroups = __popcll(emask);
   const int nentries = __popcll(fmask);
@@ -568,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
         for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
     };
     stage();
-    gateup_tile<H, I, kShRows>(a.gate_sh, a.up_sh, xs, R, x, nsh, a.h32, kDecodeMaxSlots, [] {});
+    gateup_tile<H, I, kShRows, 2>(a.gate_sh, a.up_sh, xs, R, x, nsh, a.h32, kDecodeMaxSlots, [] {});
     return;
   }
   // router wave: whole row of W[e] (8 loads) plus x and g straight from memory
@@ -647,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
   const float* src[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) src[j] = a.xn32 + (int64_t)plan_row(P, g.begin + (j < g.nr ? j : 0), a.R) * H;
-  gateup_tile<H, I, kGuRows>(a.gate + (int64_t)g.expert * I * H, a.up + (int64_t)g.expert * I * H, xs, g.nr, x, gut,
+  gateup_tile<H, I, kGuRows, 2>(a.gate + (int64_t)g.expert * I * H, a.up + (int64_t)g.expert * I * H, xs, g.nr, x, gut,
                              a.h32, g.begin, [&]() { stage_rows<H>(xs, src, g.nr); });
 }
 
