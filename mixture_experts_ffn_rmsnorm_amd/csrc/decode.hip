@@ -572,11 +572,10 @@ __device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs
 // grid = E/4 router blocks, I/8 shared gate/up blocks, then one plan block
 // (a block only waits for blocks before it, which the hardware has
 // dispatched already).
-//   Router wave (expert e = 4b + w): reads its router row, x and g directly
-//   and forms logit[r,e] = (sum_j W[e,j] x[r,j] g[j]) * (mean_j x[r,j]^2 +
-//   eps)^-1/2 -- the RMSNorm factor is per row, so it is applied after the
-//   dot product and the wave needs no block-wide norm.  It writes the
-//   logits, and each one tagged with the call's epoch to logit_tag.
+//   Router block (experts 4b .. 4b+3, one per wave): requests its router
+//   rows, normalises the batch rows into LDS, and forms logit[r,e] =
+//   sum_j W[e,j] xn[r,j].  It writes the logits, and each one tagged with
+//   the call's epoch to logit_tag.
 //   Shared gate/up block: RMSNorm into LDS, then 8 inter rows of the shared
 //   expert's SwiGLU output for every row (its streaming covers the router's
 //   and the plan's latency).  The norm comes before the block requests its
@@ -638,36 +637,34 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
     gateup_tile<H, I, kShRows, 2>(a.gate_sh, a.up_sh, xs, R, x, nsh, a.h32, kDecodeMaxSlots, [] {});
     return;
   }
-  // router wave: whole row of W[e] (8 loads) plus x and g straight from memory
+  // router block: expert e = 4b + w per wave.  The weight row's loads go out
+  // first; the block then normalises its rows into LDS (one round trip for
+  // the batch) and each wave dots its row with them.
   const int e = b * 4 + wv;
-  if (e >= E) return;
   constexpr int NCH = (H + 511) / 512;
   const bool full = H % 512 == 0 || lane * 8 < H % 512;
   uint4 q[NCH];
+  if (e < E) {
 #pragma unroll
-  for (int c = 0; c < NCH; ++c)
-    if (c < NCH - 1 || full) q[c] = load_stream(a.router + (int64_t)e * H + c * 512 + lane * 8);
-  float dot[kDecodeMaxRows] = {0.f, 0.f, 0.f, 0.f}, ss[kDecodeMaxRows] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NCH; ++c)
+      if (c < NCH - 1 || full) q[c] = load_stream(a.router + (int64_t)e * H + c * 512 + lane * 8);
+  }
+  norm_rows_to_lds<H>(a.x, a.norm_w, R, a.eps, xs);
+  if (e >= E) return;
+  float dot[kDecodeMaxRows] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     if (c < NCH - 1 || full) {
       const int col = c * 512 + lane * 8;
-      const float4 g0 = *(const float4*)(a.norm_w + col), g1 = *(const float4*)(a.norm_w + col + 4);
       float f[8];
       unpack8(q[c], f);
-      const float wg[8] = {f[0] * g0.x, f[1] * g0.y, f[2] * g0.z, f[3] * g0.w,
-                           f[4] * g1.x, f[5] * g1.y, f[6] * g1.z, f[7] * g1.w};
 #pragma unroll
       for (int r = 0; r < kDecodeMaxRows; ++r) {
         if (r < R) {
-          const float4 x0 = *(const float4*)(a.x + (int64_t)r * H + col);
-          const float4 x1 = *(const float4*)(a.x + (int64_t)r * H + col + 4);
+          const float4 x0 = *(const float4*)(xs + r * H + col), x1 = *(const float4*)(xs + r * H + col + 4);
           const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            dot[r] = fmaf(wg[i], xv[i], dot[r]);
-            ss[r] = fmaf(xv[i], xv[i], ss[r]);
-          }
+          for (int i = 0; i < 8; ++i) dot[r] = fmaf(f[i], xv[i], dot[r]);
         }
       }
     }
@@ -675,10 +672,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
 #pragma unroll
   for (int r = 0; r < kDecodeMaxRows; ++r) {
     if (r < R) {
-      const float d = wave_sum(dot[r]);
-      const float q2 = wave_sum(ss[r]);
+      const float v = wave_sum(dot[r]);
       if (lane == 0) {
-        const float v = d * (1.0f / sqrtf(q2 / (float)H + a.eps));
         a.logits[(int64_t)r * E + e] = v;
         __hip_atomic_store(&sy->logit_tag[r * E + e], ((uint64_t)a.epoch << 32) | __float_as_uint(v),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
