@@ -49,8 +49,10 @@ def alg_bytes(kernel, cfg, U, R):
         return H * I * 2 + U * 2 * I * H * 2 + R * (I + H) * 4 + R * K * (H + I) * 4
     if kernel == "dec_down_reduce":  # routed down + weighted reduce
         return U * H * I * 2 + R * K * (I + 2 * H) * 4 + R * H * 4 + x
-    if kernel == "pre_router":       # x in, xn16 + logits + routing out, router weights once
-        return E * H * 2 + x + R * H * 2 + R * E * 4 + S * 12
+    if kernel == "pre_norm":         # x in, xn16 + xlo16 out
+        return x + 2 * R * H * 2
+    if kernel == "pre_router":       # xn16 + xlo16 in, logits + routing out, router weights once
+        return E * H * 2 + 2 * R * H * 2 + R * E * 4 + S * 12
     if kernel == "gemm_gateup_swiglu":
         return (U + 1) * 2 * I * H * 2 + (S + R) * H * 2 + (S + R) * I * 2
     if kernel == "gemm_down":        # routed experts: h16 in, d16 out

@@ -51,6 +51,7 @@ struct FwdArgs {
   _Float16* xn16;
   _Float16* xlo16;
   uint32_t* mask;
+  uint32_t* rcnt;
   int32_t* cnt;
   int32_t* slot_rank;
   int32_t* perm;

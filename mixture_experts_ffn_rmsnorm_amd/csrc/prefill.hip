@@ -1,9 +1,12 @@
 // Prefill path (more than 4 rows): routed rows are grouped by expert and
 // every projection is a grouped GEMM on the fp16 matrix cores.
 //
-//   k_pre_router   RMSNorm -> xn16 (fp16 GEMM operand); router logits on the
-//                  matrix cores (hi/lo split activations); routing of each
-//                  row; per expert a mask of the block's rows that chose it
+//   k_pre_norm     RMSNorm -> xn16 (fp16 GEMM operand) and its rounding
+//                  remainder xlo16, one wave per row
+//   k_pre_router   router logits on the matrix cores (hi/lo split
+//                  activations), experts sliced over blocks for small
+//                  batches; routing of each row; per expert a mask of the
+//                  group's rows that chose it
 //   k_pre_sort     per expert the ascending list of rows that chose it, plus
 //                  each slot's rank in that list (one block per expert)
 //   k_gemm<0>      gate/up GEMM of every (expert, row-tile, column-tile),
@@ -167,117 +170,132 @@ __device__ __forceinline__ RowPick pick_hash_8(const float* lg, int E, int K, co
 }
 
 // ===========================================================================
-// Router on the matrix cores.  A block takes 32 rows and every expert.
-//  1. RMSNorm: per row rs = rsqrt(mean(x^2) + eps) and xn = x * rs * g (f32),
-//     split into hi = fp16(xn) and lo = fp16(xn - hi), which together carry
-//     about 22 significant bits.  hi is the fp16 operand the expert GEMMs
-//     take (xn16); lo goes to xlo16 for step 2.
-//  2. logits = hi.W + lo.W on the 32x32x16 fp16 MFMA with f32 accumulation;
+// RMSNorm of the batch, one wave per row: rs = rsqrt(mean(x^2) + eps) and
+// xn = x * rs * g (f32), split into hi = fp16(xn) and lo = fp16(xn - hi),
+// which together carry about 22 significant bits.  hi is the fp16 operand
+// the expert GEMMs take (xn16); lo (xlo16) joins it in the router GEMM.
+// Block 0 also clears the router's per-group arrival counters.
+constexpr int kRR = kPrefillBlockRows;  // rows per router group (one MFMA row fragment)
+
+template <int H>
+__global__ __launch_bounds__(kThreads) void k_pre_norm(const FwdArgs a) {
+  constexpr int V4 = H / 4 / kWave;  // float4 of a row per lane
+  static_assert(H % (4 * kWave) == 0, "row split over the lanes");
+  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
+  if (blockIdx.x == 0) {
+    const int64_t nb = (a.R + kRR - 1) / kRR;
+    for (int64_t i = t; i < nb; i += kThreads) a.rcnt[i] = 0;
+  }
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / kWave) + wv;
+  if (r >= a.R) return;
+  float4 v[V4], g[V4];
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    v[i] = ((const float4*)(a.x + r * H))[i * kWave + lane];
+    g[i] = ((const float4*)a.norm_w)[i * kWave + lane];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    ss = fmaf(v[i].x, v[i].x, ss); ss = fmaf(v[i].y, v[i].y, ss);
+    ss = fmaf(v[i].z, v[i].z, ss); ss = fmaf(v[i].w, v[i].w, ss);
+  }
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / (float)H + a.eps);
+  half4* hp = (half4*)(a.xn16 + r * H);
+  half4* lp = (half4*)(a.xlo16 + r * H);
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    float xn[4] = {v[i].x * rs * g[i].x, v[i].y * rs * g[i].y, v[i].z * rs * g[i].z, v[i].w * rs * g[i].w};
+    half4 h, l;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // xn is pinned as an f32 value first: hi must be the rounding of the
+      // same f32 xn that lo is taken from (a multiply fused with the fp16
+      // rounding can round a tie the other way)
+      asm volatile("" : "+v"(xn[u]));
+      h[u] = (_Float16)xn[u];
+      l[u] = (_Float16)(xn[u] - (float)h[u]);
+    }
+    hp[i * kWave + lane] = h;
+    lp[i * kWave + lane] = l;
+  }
+}
+
+// ===========================================================================
+// Router on the matrix cores.  Block (s, b) takes the 32 rows of group b and
+// experts s*E/S .. (s+1)*E/S - 1 (S expert slices; more slices when the
+// batch has few groups, so that small batches still spread over the chip).
+//  1. logits = hi.W + lo.W on the 32x32x16 fp16 MFMA with f32 accumulation;
 //     the bf16 router weights convert to fp16 exactly (for magnitudes in the
 //     fp16 normal range).  Operand tiles reach LDS by direct global->LDS
-//     loads through a 3-stage ring.
+//     loads through a ring as deep as LDS allows (a narrower expert slice
+//     leaves room for more k-tiles in flight).  Every logit is the same
+//     k-ordered sum whatever the slicing.
+//  2. With S > 1 a block writes its logit columns through to the workspace
+//     and counts itself in the group's arrival counter; the group's last
+//     block reads all E logits of its rows back and routes them.
 //  3. Selection keys sigmoid(l) + bias (float64) of all 32 x E logits, by all
 //     threads at once; then one wave per row picks its top-k (or looks up
 //     its hash row), and the block publishes, per expert, the 32-bit mask
 //     of its rows that chose the expert, which is all the sort needs.
-constexpr int kRR = kPrefillBlockRows;  // rows per router block (one MFMA row fragment)
 constexpr int kRK = 64;                 // k-tile (one 128-byte row per operand row)
-constexpr int kRStages = 3;
+constexpr int kRBudget = 144 * 1024;    // LDS bytes of the router ring
 
-template <int H, int E>
+template <int E, int S>
+struct RouterShape {
+  static constexpr int EL = E / S;                             // experts per block
+  static constexpr int ST = 2 * kRR * kRK * 2 + EL * kRK * 2;  // hi + lo + router tile
+  static constexpr int NSTG = kRBudget / ST < 12 ? kRBudget / ST : 12;
+};
+
+template <int H, int E, int S>
 __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
-  constexpr int NF = E / 32;                  // 32-expert fragments
+  constexpr int EL = RouterShape<E, S>::EL;
+  constexpr int NF = EL / 32;                 // 32-expert fragments
   constexpr int FPW = (NF + 3) / 4;           // fragments per wave
   constexpr int NK = H / kRK;
   constexpr int A_ST = kRR * kRK * 2;         // one of the hi / lo tiles
-  constexpr int B_ST = E * kRK * 2;
-  constexpr int ST = 2 * A_ST + B_ST;
+  constexpr int B_ST = EL * kRK * 2;
+  constexpr int ST = RouterShape<E, S>::ST;
+  constexpr int NSTG = RouterShape<E, S>::NSTG;
   constexpr int BI = B_ST / 16 / kThreads;    // B DMA instructions per thread per k-tile
   constexpr int LPS = 2 + BI;                 // vector-memory ops per thread per k-tile
-  constexpr int V4 = H / 4 / kWave;           // float4 of a row per lane
-  static_assert(E % 32 == 0 && BI >= 1 && BI * kThreads * 16 == B_ST && A_ST == kThreads * 16, "router tiling");
-  static_assert(kRR * E * 4 + kRR * E * 8 <= kRStages * ST, "logits and keys reuse the ring");
-  static_assert(NK >= 2 && H % (4 * kWave) == 0, "router k loop");
-  __shared__ __align__(16) unsigned char s_ring[kRStages * ST];
+  static_assert(EL % 32 == 0 && BI >= 1 && BI * kThreads * 16 == B_ST && A_ST == kThreads * 16, "router tiling");
+  static_assert(NSTG >= 3 && (NSTG - 2) * LPS < 64, "router ring");
+  static_assert(kRR * E * 4 + kRR * E * 8 <= NSTG * ST, "logits and keys reuse the ring");
+  static_assert(NK >= 2, "router k loop");
+  __shared__ __align__(16) unsigned char s_ring[NSTG * ST];
   __shared__ uint32_t s_mask[E];
   __shared__ uint32_t s_flags;
+  __shared__ int s_last;
   float* s_logit = reinterpret_cast<float*>(s_ring);                 // [kRR][E] after the k loop
   double* s_key = reinterpret_cast<double*>(s_ring + kRR * E * 4);   // [kRR][E]
 
   const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
   const int K = a.K;
-  const int64_t r0 = (int64_t)blockIdx.x * kRR;
+  const int64_t nb = (a.R + kRR - 1) / kRR;
+  const int64_t rb = blockIdx.x % nb;  // row group; its S slices are nb blocks apart
+  const int e0 = (int)(blockIdx.x / nb) * EL;
+  const int64_t r0 = rb * kRR;
   const int nrows = (int)((a.R - r0) < kRR ? (a.R - r0) : kRR);
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)s_ring;
-
-  // 1. RMSNorm, hi/lo split: one wave per row, 8 rows per wave.  Rows past
-  //    the batch end are written as zeros of their own (never read back
-  //    except by this block's MFMAs, whose results for them are dropped).
   for (int e = t; e < E; e += kThreads) s_mask[e] = 0;
   if (t == 0) s_flags = 0;
-  {
-    float4 g[V4];
-#pragma unroll
-    for (int i = 0; i < V4; ++i) g[i] = ((const float4*)a.norm_w)[i * kWave + lane];
-    // the next row's loads are issued before the current row is reduced
-    const int j0 = wv * (kRR / 4), j1 = (wv + 1) * (kRR / 4) < nrows ? (wv + 1) * (kRR / 4) : nrows;
-    float4 v[V4], vn[V4];
-    if (j0 < j1) {
-#pragma unroll
-      for (int i = 0; i < V4; ++i) v[i] = ((const float4*)(a.x + (r0 + j0) * H))[i * kWave + lane];
-    }
-#pragma unroll 1
-    for (int j = j0; j < j1; ++j) {
-      const int64_t r = r0 + j;
-      const int jn = j + 1 < j1 ? j + 1 : j;
-#pragma unroll
-      for (int i = 0; i < V4; ++i) vn[i] = ((const float4*)(a.x + (r0 + jn) * H))[i * kWave + lane];
-      float ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < V4; ++i) {
-        ss = fmaf(v[i].x, v[i].x, ss); ss = fmaf(v[i].y, v[i].y, ss);
-        ss = fmaf(v[i].z, v[i].z, ss); ss = fmaf(v[i].w, v[i].w, ss);
-      }
-      ss = wave_sum(ss);
-      const float rs = 1.0f / sqrtf(ss / (float)H + a.eps);
-      half4* hp = (half4*)(a.xn16 + r * H);
-      half4* lp = (half4*)(a.xlo16 + r * H);
-#pragma unroll
-      for (int i = 0; i < V4; ++i) {
-        float xn[4] = {v[i].x * rs * g[i].x, v[i].y * rs * g[i].y, v[i].z * rs * g[i].z, v[i].w * rs * g[i].w};
-        half4 h, l;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          // xn is pinned as an f32 value first: hi must be the rounding of
-          // the same f32 xn that lo is taken from (a multiply fused with the
-          // fp16 rounding can round a tie the other way)
-          asm volatile("" : "+v"(xn[u]));
-          h[u] = (_Float16)xn[u];
-          l[u] = (_Float16)(xn[u] - (float)h[u]);
-        }
-        hp[i * kWave + lane] = h;
-        lp[i * kWave + lane] = l;
-      }
-#pragma unroll
-      for (int i = 0; i < V4; ++i) v[i] = vn[i];
-    }
-  }
-  wait_vmcnt<0>();  // this block's xn16 / xlo16 stores have reached L2
-  __syncthreads();
 
-  // 2. logits[32][E].  DMA: the hi and lo tiles take one instruction each
-  //    (wave w: rows 8w..8w+7), the router tile BI (rows (w*BI + i)*8 + lane/8);
-  //    chunk (lane & 7) ^ swz(row) of each 128-byte row.
+  // 1. logits[32][e0 .. e0+EL).  DMA: the hi and lo tiles take one
+  //    instruction each (wave w: rows 8w..8w+7), the router tile BI (rows
+  //    (w*BI + i)*8 + lane/8); chunk (lane & 7) ^ swz(row) of each 128-byte row.
   const int chunk_even = ((lane & 7) ^ (lane >> 3)) * 16, chunk_odd = chunk_even ^ 16;
   const int arow_l = wv * 8 + (lane >> 3);
   const int64_t arow_g = r0 + (arow_l < nrows ? arow_l : nrows - 1);
   const unsigned char* ahi = (const unsigned char*)(a.xn16 + arow_g * H) + ((wv & 1) ? chunk_odd : chunk_even);
   const unsigned char* alo = (const unsigned char*)(a.xlo16 + arow_g * H) + ((wv & 1) ? chunk_odd : chunk_even);
-  const unsigned char* bsrc = (const unsigned char*)(a.router + (int64_t)(wv * BI * 8 + (lane >> 3)) * H);
+  const unsigned char* bsrc = (const unsigned char*)(a.router + (int64_t)(e0 + wv * BI * 8 + (lane >> 3)) * H);
   const uint32_t a_wave = __builtin_amdgcn_readfirstlane(wv * 1024);
   const uint32_t b_wave = __builtin_amdgcn_readfirstlane(2 * A_ST + wv * BI * 1024);
   auto issue = [&](int kt) {
-    const uint32_t base = ring + (uint32_t)(kt % kRStages) * ST;
+    const uint32_t base = ring + (uint32_t)(kt % NSTG) * ST;
     dma16(ahi + kt * (kRK * 2), base + a_wave);
     dma16(alo + kt * (kRK * 2), base + A_ST + a_wave);
 #pragma unroll
@@ -295,23 +313,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
   floatx16 acc_hi[FPW], acc_lo[FPW];
 #pragma unroll
   for (int q = 0; q < FPW; ++q) { acc_hi[q] = floatx16{}; acc_lo[q] = floatx16{}; }
-  issue(0);
-  issue(1);
+  // NSTG-1 k-tiles in flight; past the end the refill re-loads the last
+  // k-tile into the buffer just freed, so every wait counts the same loads
+#pragma unroll
+  for (int st = 0; st + 1 < NSTG; ++st) issue(st < NK ? st : NK - 1);
 #pragma unroll 1
   for (int kt = 0; kt < NK; ++kt) {
-    if (kt + 1 < NK) wait_vmcnt<LPS>(); else wait_vmcnt<0>();
+    wait_vmcnt<(NSTG - 2) * LPS>();
     __syncthreads();  // k-tile kt landed for every wave; the buffer of kt-1 is free
-    if (kt + 2 < NK) issue(kt + 2);
-    const unsigned char* S = s_ring + (kt % kRStages) * ST;
+    issue(kt + NSTG - 1 < NK ? kt + NSTG - 1 : NK - 1);
+    const unsigned char* Sb = s_ring + (kt % NSTG) * ST;
 #pragma unroll
     for (int st = 0; st < kRK / 16; ++st) {
       const int c = 2 * st + (lane >> 5);
       const int ao = aro * 128 + ((c ^ swz(aro)) << 4);
-      const half8 ah = *(const half8*)(S + ao);
-      const half8 al = *(const half8*)(S + A_ST + ao);
+      const half8 ah = *(const half8*)(Sb + ao);
+      const half8 al = *(const half8*)(Sb + A_ST + ao);
 #pragma unroll
       for (int q = 0; q < FPW; ++q) {
-        const uint4 raw = *(const uint4*)(S + 2 * A_ST + bro[q] * 128 + ((c ^ swz(bro[q])) << 4));
+        const uint4 raw = *(const uint4*)(Sb + 2 * A_ST + bro[q] * 128 + ((c ^ swz(bro[q])) << 4));
         const uint4 cv = bf16x8_to_f16x8(raw);
         const half8 bf = *(const half8*)&cv;
         acc_hi[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bf, acc_hi[q], 0, 0, 0);
@@ -319,24 +339,57 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
       }
     }
   }
+  wait_vmcnt<0>();   // the trailing refills land before the ring is reused
   __syncthreads();  // the ring becomes the logit and key tiles
 
-  // 3. logits to LDS (D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2),
-  //    register 4*(i/8) + i%4) and to the workspace; keys; routing
+  // logits (D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2), register
+  // 4*(i/8) + i%4)
+  if constexpr (S == 1) {
 #pragma unroll
-  for (int q = 0; q < FPW; ++q) {
-    const int f = wv + 4 * q;
-    if (f < NF) {
+    for (int q = 0; q < FPW; ++q) {
+      const int f = wv + 4 * q;
+      if (f < NF) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        s_logit[i * E + f * 32 + (lane & 31)] = acc_hi[q][v] + acc_lo[q][v];
+        for (int v = 0; v < 16; ++v) {
+          const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          s_logit[i * E + f * 32 + (lane & 31)] = acc_hi[q][v] + acc_lo[q][v];
+        }
       }
     }
+    __syncthreads();
+    for (int v = t; v < nrows * E / 4; v += kThreads)
+      ((float4*)(a.logits + r0 * E))[v] = ((const float4*)s_logit)[v];
+  } else {
+    // 2. this block's columns, written through; the group's last block
+    //    routes
+#pragma unroll
+    for (int q = 0; q < FPW; ++q) {
+      const int f = wv + 4 * q;
+      if (f < NF) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (i < nrows)
+            __hip_atomic_store(&a.logits[(r0 + i) * E + e0 + f * 32 + (lane & 31)], acc_hi[q][v] + acc_lo[q][v],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    __threadfence();  // release: the columns are visible device-wide before the count
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(&a.rcnt[rb], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev + 1 == (uint32_t)S;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();  // acquire: every slice's columns are visible to the loads below
+    for (int v = t; v < nrows * E / 4; v += kThreads)
+      ((float4*)s_logit)[v] = ((const float4*)(a.logits + r0 * E))[v];
+    __syncthreads();
   }
-  __syncthreads();
-  for (int v = t; v < nrows * E / 4; v += kThreads)
-    ((float4*)(a.logits + r0 * E))[v] = ((const float4*)s_logit)[v];
+
+  // 3. keys; routing
   const bool score = a.layer_kind != MOE_LAYER_HASH;
   if (score) {
     for (int q = t; q < nrows * E; q += kThreads) s_key[q] = score_key(s_logit[q], a.bias[q % E]);
@@ -359,9 +412,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
     }
   }
   __syncthreads();
-  const int64_t nb = (a.R + kRR - 1) / kRR;
-  for (int e = t; e < E; e += kThreads) a.mask[(int64_t)e * nb + blockIdx.x] = s_mask[e];
-  if (t == 0) a.rowflags[blockIdx.x] = s_flags;
+  for (int e = t; e < E; e += kThreads) a.mask[(int64_t)e * nb + rb] = s_mask[e];
+  if (t == 0) a.rowflags[rb] = s_flags;
 }
 
 // ===========================================================================
@@ -894,15 +946,31 @@ int gemm_grid() {
   return cus;
 }
 
+template <int H, int E, int S>
+const void* router_fn() {
+  if constexpr (E / S >= 32) return (const void*)k_pre_router<H, E, S>;
+  else return (const void*)k_pre_router<H, E, 1>;
+}
+
 template <int H, int I, int E>
 hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   FwdArgs args = a;
   const int nb = (a.R + kRR - 1) / kRR;
-  hipError_t err = launch("pre_router", (const void*)k_pre_router<H, E>, dim3(nb), dim3(kThreads), 0, s, &args);
+  hipError_t err = launch("pre_norm", (const void*)k_pre_norm<H>, dim3((a.R + 3) / 4), dim3(kThreads), 0, s, &args);
+  if (err != hipSuccess) return err;
+  // expert slices: as many as keep the router blocks within one per compute
+  // unit, up to 8 (32 experts, one fragment, per block)
+  const int grid = gemm_grid();
+  int S = 1;
+  while (S < 8 && E / (2 * S) >= 32 && (int64_t)nb * 2 * S <= grid) S *= 2;
+  const void* router = S == 8   ? router_fn<H, E, 8>()
+                       : S == 4 ? router_fn<H, E, 4>()
+                       : S == 2 ? router_fn<H, E, 2>()
+                                : router_fn<H, E, 1>();
+  err = launch("pre_router", router, dim3(nb * S), dim3(kThreads), 0, s, &args);
   if (err != hipSuccess) return err;
   err = launch("pre_sort", (const void*)k_pre_sort, dim3(a.E + 1), dim3(kThreads), 0, s, &args);
   if (err != hipSuccess) return err;
-  const int grid = gemm_grid();
   // groups of a few rows on average: the small row tile and the deeper ring
   const bool small = (int64_t)a.R * a.K <= 32LL * a.E;
   err = launch("gemm_gateup_swiglu",

@@ -61,7 +61,7 @@ def short_name(kernel: str) -> str:
 # launch names used by the stage timer / bench, by kernel template
 LAUNCH_NAMES = [
     ("k_dec_head", "dec_head"), ("k_dec_gateup", "dec_gateup"), ("k_dec_down", "dec_down_reduce"),
-    ("k_pre_router", "pre_router"), ("k_pre_sort", "pre_sort"), ("k_gemm<0,", "gemm_gateup_swiglu"),
+    ("k_pre_norm", "pre_norm"), ("k_pre_router", "pre_router"), ("k_pre_sort", "pre_sort"), ("k_gemm<0,", "gemm_gateup_swiglu"),
     ("k_gemm<1,", "gemm_down"), ("k_gemm<2,", "gemm_down_shared_reduce"), ("k_route", "route"),
 ]
 
