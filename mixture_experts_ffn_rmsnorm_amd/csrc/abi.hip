@@ -185,6 +185,7 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
     a.cnt = (int32_t*)(ws + L.cnt);
     a.mask = (uint32_t*)(ws + L.mask);
     a.rcnt = (uint32_t*)(ws + L.rcnt);
+    a.gctr = (uint32_t*)(ws + L.gctr);
     a.slot_rank = (int32_t*)(ws + L.slot_rank);
     a.perm = (int32_t*)(ws + L.perm);
     a.h16 = (_Float16*)(ws + L.h16);

@@ -52,6 +52,7 @@ struct FwdArgs {
   _Float16* xlo16;
   uint32_t* mask;
   uint32_t* rcnt;
+  uint32_t* gctr;
   int32_t* cnt;
   int32_t* slot_rank;
   int32_t* perm;

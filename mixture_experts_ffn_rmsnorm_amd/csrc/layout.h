@@ -64,6 +64,7 @@ struct Layout {
   size_t xlo16;      // f16 [R][H]   their rounding remainders (prefill router)
   size_t mask;       // u32 [E][ceil(R/32)]  bit j of word b: row 32b+j chose the expert (prefill)
   size_t rcnt;       // u32 [ceil(R/32)]  router blocks finished per 32-row group (prefill)
+  size_t gctr;       // u32 [4]      tail-tile counters of the three GEMM launches (prefill)
   size_t cnt;        // i32 [E + 1]  rows per group (routed experts, then shared)
   size_t slot_rank;  // i32 [R][K]   rank of the slot's row inside its expert, -1 if masked
   size_t perm;       // i32 [E][R]   rows of each expert in ascending order
@@ -98,13 +99,14 @@ inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
     L->plan = take(sizeof(DecodePlan));
     L->h32 = take((unsigned __int128)(kDecodeMaxSlots + R) * I * 4);
     L->d32 = take((unsigned __int128)(kDecodeMaxSlots + R) * H * 4);
-    L->xn16 = L->xlo16 = L->mask = L->rcnt = L->cnt = L->slot_rank = L->perm = L->h16 = L->d16 = 0;
+    L->xn16 = L->xlo16 = L->mask = L->rcnt = L->gctr = L->cnt = L->slot_rank = L->perm = L->h16 = L->d16 = 0;
   } else {
     L->xn32 = L->plan = L->h32 = L->d32 = 0;
     L->xn16 = take(r * H * 2);
     L->xlo16 = take(r * H * 2);
     L->mask = take((unsigned __int128)E * ((r + kPrefillBlockRows - 1) / kPrefillBlockRows) * 4);
     L->rcnt = take((r + kPrefillBlockRows - 1) / kPrefillBlockRows * 4);
+    L->gctr = take(16);
     L->cnt = take((unsigned __int128)(E + 1) * 4);
     L->slot_rank = take(S * 4);
     L->perm = take((unsigned __int128)E * r * 4);

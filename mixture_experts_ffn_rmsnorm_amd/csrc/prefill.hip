@@ -174,7 +174,8 @@ __device__ __forceinline__ RowPick pick_hash_8(const float* lg, int E, int K, co
 // xn = x * rs * g (f32), split into hi = fp16(xn) and lo = fp16(xn - hi),
 // which together carry about 22 significant bits.  hi is the fp16 operand
 // the expert GEMMs take (xn16); lo (xlo16) joins it in the router GEMM.
-// Block 0 also clears the router's per-group arrival counters.
+// Block 0 also clears the router's per-group arrival counters and the
+// GEMM launches' tail-tile counters.
 constexpr int kRR = kPrefillBlockRows;  // rows per router group (one MFMA row fragment)
 
 template <int H>
@@ -185,6 +186,7 @@ __global__ __launch_bounds__(kThreads) void k_pre_norm(const FwdArgs a) {
   if (blockIdx.x == 0) {
     const int64_t nb = (a.R + kRR - 1) / kRR;
     for (int64_t i = t; i < nb; i += kThreads) a.rcnt[i] = 0;
+    if (t < 4) a.gctr[t] = 0;
   }
   const int64_t r = (int64_t)blockIdx.x * (kThreads / kWave) + wv;
   if (r >= a.R) return;
@@ -615,7 +617,24 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
   const int chunk0 = ((lane & 7) ^ (lane >> 3)) * 16;  // bytes, even row group
   const int chunk1 = chunk0 ^ 16;                       // odd row group
 
-  for (int tile = first; tile < total; tile += gridDim.x) {
+  // Tiles: all but the last two rounds are dealt statically (first, first
+  // + grid, ...; an XCD's blocks get neighbouring tiles); the rest go to
+  // whichever block asks next, through a counter per launch, so that blocks
+  // that ran fast take the tail.
+  __shared__ int s_next;
+  const int grid = (int)gridDim.x, rounds = total / grid;
+  const int nstatic = total <= grid ? total : (rounds > 3 ? rounds - 2 : 1) * grid;
+  auto grab = [&]() { return nstatic + (int)__hip_atomic_fetch_add(&a.gctr[MODE], 1u, __ATOMIC_RELAXED,
+                                                                      __HIP_MEMORY_SCOPE_AGENT); };
+  int tile = first;
+  if (tile >= nstatic) {
+    if (t == 0) s_next = nstatic < total ? grab() : total;
+    __syncthreads();
+    tile = s_next;
+  }
+  while (tile < total) {
+    const bool dyn_next = tile + grid >= nstatic;  // the next tile comes from the counter
+    int next_dyn = total;
     // locate the group: largest g with s_tbase[g] <= tile (empty groups
     // share their successor's base and lose the search)
     int lo = 0, hi = G - 1;
@@ -823,6 +842,8 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
       }
     }
     wait_vmcnt<0>();  // the trailing refill lands before the ring turns into staging
+    // the next tile's number is requested now; the epilogue covers the wait
+    if (t == 0 && dyn_next && nstatic < total) next_dyn = grab();
     __syncthreads();
 
     // epilogue, through LDS in 64-row slabs: D[i][j] of a 32x32 tile sits in
@@ -912,7 +933,9 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
         }
       }
     }
+    if (t == 0) s_next = dyn_next ? next_dyn : tile + grid;
     __syncthreads();  // staging and s_pos are rewritten by the next tile
+    tile = s_next;
   }
 }
 
