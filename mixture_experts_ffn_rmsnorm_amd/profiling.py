@@ -51,6 +51,11 @@ def sources_digest() -> str:
     return h.hexdigest()
 
 
+PROFILED_NOTE = ("Under kernel tracing the bench's own per-kernel event timings (`kernels`, and the roofline "
+                 "figure derived from them) include the tracer's per-dispatch overhead; the rocprofv3 durations in "
+                 "the table are the reference, and the unprofiled bench's event timings agree with them.")
+
+
 def short_name(kernel: str) -> str:
     """k_dec_gateup<4096, 2048> style names for this library's kernels."""
     s = re.sub(r"\(moe::\w+\)", "", kernel)
@@ -124,6 +129,7 @@ def cmd_stats(args, extra):
             f.write(f"| {s} | {ln} | {c} | {a:.1f} | {mn:.1f} | {mx:.1f} |\n")
         if json_line:
             f.write("\nbench.py output of the same run:\n\n```\n" + json_line + "\n```\n")
+            f.write("\n" + PROFILED_NOTE + "\n")
     print(open(path).read())
     return 0
 
