@@ -212,6 +212,36 @@ def test_full_ragged_rows(full, rows):
     check_routing_exact(full, lg, idx, w, None, SCORE)
 
 
+@pytest.mark.parametrize("rows", [1500, 3000])
+def test_full_prefill_router_slices(full, rows):
+    """Batches whose router splits the experts over 4 (1500 rows) and 2 (3000
+    rows) blocks per 32-row group, each with a ragged last group: every row's
+    logits against the oracle router, every row's routing exact, sampled
+    outputs end to end."""
+    cfg = full.cfg
+    x = _x(cfg, rows, seed=70 + rows)
+    out, lg, idx, w, st = full.run(x, None, SCORE)
+    assert st == 0
+    xn = ref.rms_norm(x, full.host.norm_w, cfg.eps)
+    np.testing.assert_allclose(lg, ref.router_logits(xn, full.host.router), rtol=0, atol=LOGIT_ATOL_PREFILL)
+    check_routing_exact(full, lg, idx, w, None, SCORE)
+    check_forward(full, x, None, SCORE, out, lg, idx, w, rows=[0, 31, 32, rows // 2, rows - 2, rows - 1])
+
+
+def test_full_prefill_hash(full):
+    """A hash-routed layer through the prefill path (700 rows: 22 groups, the
+    last one ragged, experts sliced 8 ways in the router)."""
+    cfg = gen.config(2)
+    lay = Layer(cfg, share=full)
+    rows = 700
+    x = _x(cfg, rows, seed=77)
+    tok = _tok(cfg, rows, seed=78)
+    out, lg, idx, w, st = lay.run(x, tok, HASH)
+    assert st == 0
+    check_routing_exact(lay, lg, idx, w, tok, HASH)
+    check_forward(lay, x, tok, HASH, out, lg, idx, w, rows=[0, 5, 350, 671, 672, 699])
+
+
 def test_full_prefill_config3(full):
     cfg = gen.config(3)
     lay = Layer(cfg, share=full)
