@@ -467,17 +467,40 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
     if (w < wv) rank += v;
     total += v;
   }
+  // rows of each mask word in ascending order, 8 at a time: their slots'
+  // expert indices are all requested before any is compared (one memory
+  // round trip per 8 rows, not one per slot)
   int32_t* perm = a.perm + (int64_t)e * R;
+  constexpr int kB = 8;
   for (int64_t b = b0; b < b1; ++b) {
     uint32_t bits = m[b];
     while (bits) {
-      const int j = __ffs(bits) - 1;
-      bits &= bits - 1;
-      const int64_t row = b * kRR + j;
-      perm[rank] = (int32_t)row;
-      for (int k = 0; k < K; ++k)
-        if (a.idx[row * K + k] == e) a.slot_rank[row * K + k] = rank;
-      ++rank;
+      int64_t rows[kB];
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < kB; ++q) {
+        rows[q] = -1;
+        if (bits) {
+          rows[q] = b * kRR + (__ffs(bits) - 1);
+          bits &= bits - 1;
+          n = q + 1;
+        }
+      }
+      int ids[kB][kMaxTopK];
+#pragma unroll
+      for (int q = 0; q < kB; ++q)
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) ids[q][k] = (rows[q] >= 0 && k < K) ? a.idx[rows[q] * K + k] : -1;
+#pragma unroll
+      for (int q = 0; q < kB; ++q) {
+        if (q < n) {
+          perm[rank + q] = (int32_t)rows[q];
+#pragma unroll
+          for (int k = 0; k < kMaxTopK; ++k)
+            if (k < K && ids[q][k] == e) a.slot_rank[rows[q] * K + k] = rank + q;
+        }
+      }
+      rank += n;
     }
   }
   if (t == 0) a.cnt[e] = total;
