@@ -232,8 +232,9 @@ __global__ __launch_bounds__(kThreads) void k_pre_norm(const FwdArgs a) {
 //     the bf16 router weights convert to fp16 exactly (for magnitudes in the
 //     fp16 normal range).  Operand tiles reach LDS by direct global->LDS
 //     loads through a ring as deep as LDS allows (a narrower expert slice
-//     leaves room for more k-tiles in flight).  Every logit is the same
-//     k-ordered sum whatever the slicing.
+//     leaves room for more k-tiles in flight).  With fewer 32-expert
+//     fragments than waves, the waves of a fragment split its k-steps and
+//     add their partial sums in a fixed order.
 //  2. With S > 1 a block writes its logit columns through to the workspace
 //     and counts itself in the group's arrival counter; the group's last
 //     block reads all E logits of its rows back and routes them.
@@ -266,6 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
   static_assert(EL % 32 == 0 && BI >= 1 && BI * kThreads * 16 == B_ST && A_ST == kThreads * 16, "router tiling");
   static_assert(NSTG >= 3 && (NSTG - 2) * LPS < 64, "router ring");
   static_assert(kRR * E * 4 + kRR * E * 8 <= NSTG * ST, "logits and keys reuse the ring");
+  static_assert(kRR * E * 12 + 4 * 16 * kWave * 4 <= NSTG * ST, "partial sums after the logits and keys");
   static_assert(NK >= 2, "router k loop");
   __shared__ __align__(16) unsigned char s_ring[NSTG * ST];
   __shared__ uint32_t s_mask[E];
@@ -315,34 +317,84 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
   floatx16 acc_hi[FPW], acc_lo[FPW];
 #pragma unroll
   for (int q = 0; q < FPW; ++q) { acc_hi[q] = floatx16{}; acc_lo[q] = floatx16{}; }
+  // With fewer fragments than waves, the WPF waves of one fragment split each
+  // k-tile's k-steps (wave split s takes steps s, s + WPF, ...) and their
+  // partial sums are added at the end in split order.
+  constexpr int WPF = NF < 4 ? 4 / NF : 1;
+  constexpr int NSW = (kRK / 16) / WPF;  // k-steps per k-tile of one wave
+  static_assert(NF >= 4 || 4 % NF == 0, "fragments share the waves evenly");
+  const int split = NF < 4 ? wv / NF : 0;
+  auto read = [&](int kt, int st, half8& ah, half8& al, uint4 (&bq)[FPW]) {
+    const unsigned char* Sb = s_ring + (kt % NSTG) * ST;
+    const int c = 2 * st + (lane >> 5);
+    const int ao = aro * 128 + ((c ^ swz(aro)) << 4);
+    ah = *(const half8*)(Sb + ao);
+    al = *(const half8*)(Sb + A_ST + ao);
+#pragma unroll
+    for (int q = 0; q < FPW; ++q) bq[q] = *(const uint4*)(Sb + 2 * A_ST + bro[q] * 128 + ((c ^ swz(bro[q])) << 4));
+  };
+  auto mma = [&](const half8& ah, const half8& al, const uint4 (&bq)[FPW]) {
+#pragma unroll
+    for (int q = 0; q < FPW; ++q) {
+      const uint4 cv = bf16x8_to_f16x8(bq[q]);
+      const half8 bf = *(const half8*)&cv;
+      acc_hi[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bf, acc_hi[q], 0, 0, 0);
+      acc_lo[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bf, acc_lo[q], 0, 0, 0);
+    }
+  };
   // NSTG-1 k-tiles in flight; past the end the refill re-loads the last
-  // k-tile into the buffer just freed, so every wait counts the same loads
+  // k-tile into the buffer just freed, so every wait counts the same loads.
+  // A wave's next k-step is read before the current one's MFMAs, across
+  // k-tile boundaries too (the barrier comes before the next tile's read).
 #pragma unroll
   for (int st = 0; st + 1 < NSTG; ++st) issue(st < NK ? st : NK - 1);
+  wait_vmcnt<(NSTG - 2) * LPS>();
+  __syncthreads();  // k-tile 0 landed for every wave
+  issue(NSTG - 1 < NK ? NSTG - 1 : NK - 1);
+  half8 ah, al;
+  uint4 bq[FPW];
+  read(0, split, ah, al, bq);
 #pragma unroll 1
   for (int kt = 0; kt < NK; ++kt) {
-    wait_vmcnt<(NSTG - 2) * LPS>();
-    __syncthreads();  // k-tile kt landed for every wave; the buffer of kt-1 is free
-    issue(kt + NSTG - 1 < NK ? kt + NSTG - 1 : NK - 1);
-    const unsigned char* Sb = s_ring + (kt % NSTG) * ST;
 #pragma unroll
-    for (int st = 0; st < kRK / 16; ++st) {
-      const int c = 2 * st + (lane >> 5);
-      const int ao = aro * 128 + ((c ^ swz(aro)) << 4);
-      const half8 ah = *(const half8*)(Sb + ao);
-      const half8 al = *(const half8*)(Sb + A_ST + ao);
-#pragma unroll
-      for (int q = 0; q < FPW; ++q) {
-        const uint4 raw = *(const uint4*)(Sb + 2 * A_ST + bro[q] * 128 + ((c ^ swz(bro[q])) << 4));
-        const uint4 cv = bf16x8_to_f16x8(raw);
-        const half8 bf = *(const half8*)&cv;
-        acc_hi[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bf, acc_hi[q], 0, 0, 0);
-        acc_lo[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bf, acc_lo[q], 0, 0, 0);
+    for (int i = 0; i < NSW; ++i) {
+      half8 ahn, aln;
+      uint4 bqn[FPW];
+      if (i + 1 < NSW) {
+        read(kt, split + WPF * (i + 1), ahn, aln, bqn);
+      } else if (kt + 1 < NK) {
+        wait_vmcnt<(NSTG - 2) * LPS>();
+        __syncthreads();  // k-tile kt+1 landed for every wave; every wave is done reading kt's buffer
+        issue(kt + NSTG < NK ? kt + NSTG : NK - 1);
+        read(kt + 1, split, ahn, aln, bqn);
       }
+      mma(ah, al, bq);
+      ah = ahn;
+      al = aln;
+#pragma unroll
+      for (int q = 0; q < FPW; ++q) bq[q] = bqn[q];
     }
   }
   wait_vmcnt<0>();   // the trailing refills land before the ring is reused
   __syncthreads();  // the ring becomes the logit and key tiles
+  if constexpr (WPF > 1) {
+    // the partial sums of each fragment, added in split order by the wave
+    // with split 0 (which then holds the fragment's logits in acc_hi)
+    float* s_part = reinterpret_cast<float*>(s_ring + kRR * E * 12);  // [4 waves][16][64]
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s_part[(wv * 16 + v) * kWave + lane] = acc_hi[0][v] + acc_lo[0][v];
+    __syncthreads();
+    if (split == 0) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float sum = s_part[(wv * 16 + v) * kWave + lane];
+        for (int sp = 1; sp < WPF; ++sp) sum += s_part[((wv + sp * NF) * 16 + v) * kWave + lane];
+        acc_hi[0][v] = sum;
+        acc_lo[0][v] = 0.f;
+      }
+    }
+    __syncthreads();
+  }
 
   // logits (D[i][j] of a 32x32 tile sits in lane j + 32*((i/4)%2), register
   // 4*(i/8) + i%4)
@@ -367,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
 #pragma unroll
     for (int q = 0; q < FPW; ++q) {
       const int f = wv + 4 * q;
-      if (f < NF) {
+      if (f < NF) {  // (with split k-steps, f < NF is the split-0 wave)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
