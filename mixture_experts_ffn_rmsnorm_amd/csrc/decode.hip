@@ -30,6 +30,9 @@ constexpr int kGuRows = 16;     // inter rows per routed gate/up block (x2 matri
 constexpr int kShRows = 8;      // inter rows per shared gate/up block: 4 waves x 2
 constexpr int kRedCols = 1024;  // output columns per reduce block
 constexpr int kDnRows = 32;     // hidden rows per down block: 4 waves x 8
+// hidden rows per shared-down block of the gate/up launch (4 waves x 4): its
+// H/16 blocks give every compute unit one of them besides its routed blocks
+constexpr int kSdRows = 16;
 // Spin limit of an in-kernel wait on another workgroup's flag or counter
 // (each poll is a device-scope load, about a microsecond: roughly 0.25 s in
 // all); reaching it sets MOE_FLAG_SYNC_TIMEOUT instead of hanging.
@@ -542,15 +545,15 @@ __device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R) {
 // activation rows staged in hs; tile x of H/32 takes rows x, x + H/32, ...
 // so concurrent blocks read neighbouring rows.  d32 rows ent..ent+nr-1
 // receive the results (written through).
-template <int H, int I, class Pre>
+template <int H, int I, int ROWS, class Pre>
 __device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs, int nr, int x, float* d32, int ent,
                                           Pre pre) {
-  constexpr int W = kThreads / kWave, RPW = kDnRows / W;  // rows per wave
-  static_assert(RPW * 4 <= kWave, "one lane per result");
-  __shared__ float s_res[kDnRows * 4];  // results wait here until the stream ends
+  constexpr int W = kThreads / kWave, RPW = ROWS / W;  // rows per wave
+  static_assert(RPW * 4 <= kWave && RPW % 2 == 0, "one lane per result; whole row pairs in flight");
+  __shared__ float s_res[ROWS * 4];  // results wait here until the stream ends
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   float* res = s_res + wv * RPW * 4;
-  constexpr int tiles = H / kDnRows;
+  constexpr int tiles = H / ROWS;
   auto row_of = [&](int j) { return x + (wv + j * W) * tiles; };
   auto rowptr = [&](int j) { return wbase + (int64_t)row_of(j) * I; };
   auto sink = [&](int j, const float (&part)[4]) {
@@ -683,23 +686,25 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Shared down + routed gate/up.  grid = H/32 shared-down blocks (dispatched
+// Shared down + routed gate/up.  grid = H/16 shared-down blocks (dispatched
 // first: the shared h is complete, and their streaming covers the routed
 // blocks' plan read and staging), then G * I/16 routed gate/up blocks (G =
-// max distinct routed experts).  Shared-down block x: hidden rows x,
-// x + H/32, ... of the shared expert's down projection -> d32 shared rows.
+// max distinct routed experts); with one row, 256 + 6 * 128 blocks put one
+// shared-down and three routed blocks on every compute unit, so no unit
+// has more to stream than another.  Shared-down block x: hidden rows x,
+// x + H/16, ... of the shared expert's down projection -> d32 shared rows.
 // Gate/up block (u, x): inter rows x, x + I/16, ... of the plan's u-th
 // expert -> h32.
 template <int H, int I>
 __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [nr][H] activations, or [R][I] shared h
-  constexpr int nsd = H / kDnRows, gut = I / kGuRows;
+  constexpr int nsd = H / kSdRows, gut = I / kGuRows;
   const int b = blockIdx.x;
   if (b < nsd) {
     const float* src[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(kDecodeMaxSlots + (j < a.R ? j : 0)) * I;
-    down_tile<H, I>(a.down_sh, xs, a.R, b, a.d32, kDecodeMaxSlots, [&]() { stage_rows<I>(xs, src, a.R); });
+    down_tile<H, I, kSdRows>(a.down_sh, xs, a.R, b, a.d32, kDecodeMaxSlots, [&]() { stage_rows<I>(xs, src, a.R); });
     return;
   }
   const DecodePlan* P = a.plan;
@@ -738,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
     const float* src[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
-    down_tile<H, I>(a.down + (int64_t)g.expert * H * I, hs, g.nr, x, a.d32, g.begin,
+    down_tile<H, I, kDnRows>(a.down + (int64_t)g.expert * H * I, hs, g.nr, x, a.d32, g.begin,
                     [&]() { stage_rows<I>(hs, src, g.nr); });
     sync_stores();
     __syncthreads();
@@ -775,7 +780,7 @@ hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   hipError_t err = launch("dec_head", (const void*)k_dec_head<H, I>, dim3((a.E + 3) / 4 + I / kShRows + 1),
                           dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  err = launch("dec_gateup", (const void*)k_dec_gateup<H, I>, dim3(H / kDnRows + gmax * (I / kGuRows)),
+  err = launch("dec_gateup", (const void*)k_dec_gateup<H, I>, dim3(H / kSdRows + gmax * (I / kGuRows)),
                dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
   return launch("dec_down_reduce", (const void*)k_dec_down<H, I>, dim3(H / kDnRows, gmax), dim3(kThreads), 0, s,
