@@ -84,9 +84,12 @@ StageTimer& timer() {
   return t;
 }
 
-// Per-call tag of the decode path's tagged words: a process-wide counter
-// seeded from the clock, never 0, so a word left in the workspace by an
-// earlier call (or by anything else) does not match the current call.
+// Host part of the per-call tag of the decode path's tagged words: a
+// process-wide counter seeded from the clock, so a word left in the
+// workspace by an earlier call (or by anything else) does not match the
+// current call.  The kernels add the workspace's device-side call count, so
+// that the replays of a captured graph (whose arguments are fixed) differ
+// as well.
 uint32_t next_epoch() {
   static std::atomic<uint32_t> ctr{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
   uint32_t e = ctr.fetch_add(1, std::memory_order_relaxed);

@@ -464,11 +464,21 @@ __device__ __forceinline__ SlotRoute route_slots(float lg0, float lg1, float lg2
   return o;
 }
 
+// The call's tag for the decode path's tagged words: the host's per-call
+// value plus the workspace's device-side call count, which the gate/up
+// launch advances -- distinct for every call, also for every replay of a
+// captured graph, whose launch arguments are fixed.  Never 0.
+__device__ __forceinline__ uint32_t call_epoch(const FwdArgs& a) {
+  const uint32_t e = a.epoch + a.sync->call_seq;
+  return e ? e : 1u;
+}
+
 // Routing of the batch into LDS: wave r < R routes row r.  It first reads
 // what the route needs besides the logits (bias, or the token's table row),
 // then polls the row's tagged logits until every one carries the call's
 // epoch (bounded; returns false on timeout).
-__device__ bool route_rows(const FwdArgs& a, int* s_idx, float* s_w, unsigned char* s_valid, uint32_t* s_flags) {
+__device__ bool route_rows(const FwdArgs& a, uint32_t epoch, int* s_idx, float* s_w, unsigned char* s_valid,
+                           uint32_t* s_flags) {
   const int R = a.R, K = a.K, E = a.E;
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   if (wv >= R) return true;
@@ -495,7 +505,7 @@ __device__ bool route_rows(const FwdArgs& a, int* s_idx, float* s_w, unsigned ch
       lgv[j] = 0.f;
       if (e < E) {
         const uint64_t w = __hip_atomic_load(&tags[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        mine &= (uint32_t)(w >> 32) == a.epoch;
+        mine &= (uint32_t)(w >> 32) == epoch;
         lgv[j] = __uint_as_float((uint32_t)w);
       }
     }
@@ -600,13 +610,14 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   const int R = a.R, E = a.E, K = a.K;
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   DecodeSync* sy = a.sync;
+  const uint32_t epoch = call_epoch(a);
   const int nrb = (E + 3) / 4, nsh = I / kShRows;
   const int b = blockIdx.x;
   if (b == nrb + nsh) {  // plan block
     __shared__ int s_ok;
     if (threadIdx.x == 0) s_ok = 1;
     __syncthreads();
-    if (!route_rows(a, s_idx, s_w, s_valid, s_flags) && lane == 0) s_ok = 0;
+    if (!route_rows(a, epoch, s_idx, s_w, s_valid, s_flags) && lane == 0) s_ok = 0;
     __syncthreads();
     const bool ok = s_ok;
     if (wv == 0) build_plan(s_idx, s_w, s_valid, R, K, E, &P);
@@ -620,8 +631,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
       uint32_t f = 0;
       for (int r = 0; r < R; ++r) f |= s_flags[r];
       a.status[0] = f;
-      sy->last_epoch = a.epoch;
-      if (!ok) store_flag(&sy->timeout_epoch, a.epoch);
+      sy->last_epoch = epoch;
+      if (!ok) store_flag(&sy->timeout_epoch, epoch);
     }
     for (int i = threadIdx.x; i < kDecodeMaxTiles; i += kThreads) sy->tile_cnt[i] = 0;
     const int* ps = (const int*)&P;
@@ -678,7 +689,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
       const float v = wave_sum(dot[r]);
       if (lane == 0) {
         a.logits[(int64_t)r * E + e] = v;
-        __hip_atomic_store(&sy->logit_tag[r * E + e], ((uint64_t)a.epoch << 32) | __float_as_uint(v),
+        __hip_atomic_store(&sy->logit_tag[r * E + e], ((uint64_t)epoch << 32) | __float_as_uint(v),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -700,6 +711,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [nr][H] activations, or [R][I] shared h
   constexpr int nsd = H / kSdRows, gut = I / kGuRows;
   const int b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) a.sync->call_seq = a.sync->call_seq + 1;  // the head has read it
   if (b < nsd) {
     const float* src[4];
 #pragma unroll

@@ -22,7 +22,7 @@ struct FwdArgs {
   float eps;
   int layer_kind;
   int64_t table_rows;
-  uint32_t epoch;  // per-call tag of the decode path's tagged words
+  uint32_t epoch;  // host part of the per-call tag of the decode path's tagged words
   // inputs / outputs
   const float* x;
   const int32_t* token_ids;

@@ -45,7 +45,8 @@ constexpr int kDecodeMaxTiles = 256;  // down column tiles (hidden/32) and share
 struct DecodeSync {
   uint32_t last_epoch;                   // epoch of the last decode call (0 after a prefill call)
   uint32_t timeout_epoch;                // epoch of a call in which an in-kernel wait gave up
-  uint32_t pad[14];
+  uint32_t call_seq;                     // decode calls made on this workspace (device side)
+  uint32_t pad[13];
   uint64_t logit_tag[kDecodeMaxRows * kMaxExperts];  // router wave -> plan block: epoch | f32 logit bits
   uint32_t tile_cnt[kDecodeMaxTiles];    // groups finished per down column tile
 };
