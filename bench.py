@@ -90,6 +90,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="distinct weight sets cycled (default 4 decode, 1 prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the L layers chained (each layer's output the next one's input) "
+                         "as one captured HIP graph, replayed --steps times; reported under 'graph'")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -208,9 +211,43 @@ def main():
         "kernels": kernels,
     }
 
+    if args.graph:
+        res["graph"] = graph_chain(dims, cfg, layers, x, tok, ws, args.steps, log)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds, log)
     print(json.dumps(res), flush=True)
+
+
+def graph_chain(dims, cfg, layers, x, tok, ws, reps, log):
+    """The L layers back to back as a model runs them (layer l's output is
+    layer l+1's input), captured once as a HIP graph and replayed: per-layer
+    time without host launches between the kernels."""
+    import torch
+
+    from mixture_experts_ffn_rmsnorm_amd import moe
+
+    L = len(layers)
+    bufs = [x] + [torch.empty_like(x) for _ in range(L)]
+
+    def chain():
+        for l in range(L):
+            moe.forward(dims, bufs[l], tok, cfg.layer_kind, layers[l][2], bufs[l + 1], ws[l])
+
+    chain()  # outside the graph first
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    log(f"graph: {L} layers, {reps} replays")
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_layer = (time.perf_counter() - t0) * 1e3 / (reps * L)
+    return {"layers": L, "replays": reps, "ms_per_layer": ms_layer, "rows_per_s": cfg.rows / (ms_layer / 1e3)}
 
 
 def cpu_baseline(cfg, layer, budget_s, log):
