@@ -76,6 +76,13 @@ def alg_flops(kernel, cfg, R):
     return None
 
 
+def step_flops(cfg, R):
+    """Algorithmic flops of one layer call: the router plus 7 expert units
+    (6 routed slots and the shared expert) of 2*3*H*I per row."""
+    H, I, E, K = cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
+    return R * (2 * E * H + (K + 1) * 2 * 3 * H * I)
+
+
 def step_bytes(cfg, U, R):
     H, I, E = cfg.hidden, cfg.inter, cfg.experts
     return (U + 1) * EXPERT_BYTES(H, I) + E * H * 2 + 2 * R * H * 4 + H * 4 + E * 4
@@ -165,6 +172,16 @@ def main():
         step(i)
     torch.cuda.synchronize()
     stages = moe.stage_timing_end()
+    # latency pass: each step bracketed by events on the stream the kernels use
+    lat = []
+    for i in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step(i)
+        e1.record()
+        lat.append((e0, e1))
+    torch.cuda.synchronize()
+    lat_us = np.array([a.elapsed_time(b) * 1e3 for a, b in lat])
 
     kernels = {}
     for name, (ms, n) in stages.items():
@@ -197,6 +214,13 @@ def main():
         if kf is not None:
             k["mfma_frac"] = kf / secs / 1e12 / MFMA_F16_PEAK_TFLOPS
     sb = step_bytes(cfg, u_mean, R)
+    sf = step_flops(cfg, R)
+    # one call of layer 0 for the parity sample and the status word
+    step(0)
+    torch.cuda.synchronize()
+    per = min(R, 4)
+    gpu0 = (out[:per].cpu().numpy().copy(), moe.routing_view(dims, R, ws[0])[1][:per].cpu().numpy().copy())
+    status_flags = moe.status(ws[0])
     res = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -206,15 +230,22 @@ def main():
                    "layer_kind": "hash" if cfg.layer_kind == 1 else "score", "layers_cycled": L,
                    "distinct_routed_experts": u_mean},
         "roofline": roof,
+        "latency_us": {"median": float(np.median(lat_us)), "p10": float(np.percentile(lat_us, 10)),
+                       "p90": float(np.percentile(lat_us, 90))},
+        "step_alg_bytes": sb,
         "step_hbm_GBps": sb / (ms_per_step / 1e3) / 1e9,
         "step_hbm_frac": sb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS,
+        "step_alg_flops": sf,
+        "step_TFLOPs": sf / (ms_per_step / 1e3) / 1e12,
+        "step_mfma_frac": sf / (ms_per_step / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "status_flags": status_flags,
         "kernels": kernels,
     }
 
     if args.graph:
         res["graph"] = graph_chain(dims, cfg, layers, x, tok, ws, args.steps, log)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds, log)
+        res["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds, log, gpu0)
     print(json.dumps(res), flush=True)
 
 
@@ -250,8 +281,10 @@ def graph_chain(dims, cfg, layers, x, tok, ws, reps, log):
     return {"layers": L, "replays": reps, "ms_per_layer": ms_layer, "rows_per_s": cfg.rows / (ms_layer / 1e3)}
 
 
-def cpu_baseline(cfg, layer, budget_s, log):
-    """The float64 oracle on a bounded sample of the same workload."""
+def cpu_baseline(cfg, layer, budget_s, log, gpu=None):
+    """The float64 oracle on a bounded sample of the same workload; with the
+    GPU's output and expert indices for the same rows (`gpu`), also their
+    agreement with the oracle on that sample."""
     import numpy as np
 
     from mixture_experts_ffn_rmsnorm_amd import inputs as gen
@@ -287,9 +320,20 @@ def cpu_baseline(cfg, layer, budget_s, log):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = 1
-    return {"value": done / el, "unit": "rows/s", "cores": cores, "kind": "oracle",
+    base = {"value": done / el, "unit": "rows/s", "cores": cores, "kind": "oracle",
             "sample": f"the first {per} row(s) of the workload through the float64 oracle, repeated "
                       f"{done // per}x in {el:.1f}s (BLAS threads = cores)"}
+    if gpu is not None:
+        out_g, idx_g = gpu
+        ref_out = res["out"]
+        same = [set(idx_g[r].tolist()) == set(res["idx"][r].tolist()) for r in range(per)]
+        base["parity"] = {
+            "rows": per,
+            "relL2": float(np.linalg.norm(out_g - ref_out) / max(np.linalg.norm(ref_out), 1e-300)),
+            "maxabs_ratio": float(np.abs(out_g - ref_out).max() / max(np.abs(ref_out).max(), 1e-300)),
+            "index_match_rows": int(sum(same)),
+        }
+    return base
 
 
 if __name__ == "__main__":
