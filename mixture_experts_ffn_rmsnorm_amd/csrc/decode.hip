@@ -28,7 +28,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kGuRows = 16;     // inter rows per routed gate/up block (x2 matrices): 4 waves x 4
 constexpr int kShRows = 8;      // inter rows per shared gate/up block: 4 waves x 2
-constexpr int kRedCols = 1024;  // output columns per reduce block
 constexpr int kDnRows = 32;     // hidden rows per down block: 4 waves x 8
 // hidden rows per shared-down block of the gate/up launch (4 waves x 4): its
 // H/16 blocks give every compute unit one of them besides its routed blocks
@@ -218,32 +217,8 @@ __device__ __forceinline__ float load_wt(const float* p) {
 __device__ __forceinline__ void store_flag(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t load_flag(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // Every store this thread issued has completed.
 __device__ __forceinline__ void sync_stores() { __builtin_amdgcn_s_waitcnt(0); }
-
-// Wave 0 waits until n flags equal `want` (bounded); the other waves wait at
-// the barrier.  Returns false on timeout.
-__device__ __forceinline__ bool wait_flags(const uint32_t* flags, int n, uint32_t want) {
-  __shared__ int s_ok;
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    bool ready = false;
-    int polls = 0;
-    while (true) {
-      bool mine = true;
-      for (int i = lane; i < n; i += kWave) mine &= load_flag(&flags[i]) == want;
-      ready = __ballot(!mine) == 0;
-      if (ready || ++polls >= kMaxPolls) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    if (lane == 0) s_ok = ready;
-  }
-  __syncthreads();
-  return s_ok;
-}
 
 // Gate/up + SwiGLU of PAIRS inter rows of one expert for the `nr` activation
 // rows in LDS: tile x of `tiles` takes rows x, x + tiles, x + 2*tiles, ...,
@@ -626,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
       a.idx[s] = s_idx[s];
       a.wts[s] = s_w[s];
     }
-    if (threadIdx.x < R) a.rowflags[threadIdx.x] = s_flags[threadIdx.x];
+    if ((int)threadIdx.x < R) a.rowflags[threadIdx.x] = s_flags[threadIdx.x];
     if (threadIdx.x == 0) {
       uint32_t f = 0;
       for (int r = 0; r < R; ++r) f |= s_flags[r];

@@ -367,6 +367,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
         __syncthreads();  // k-tile kt+1 landed for every wave; every wave is done reading kt's buffer
         issue(kt + NSTG < NK ? kt + NSTG : NK - 1);
         read(kt + 1, split, ahn, aln, bqn);
+      } else {  // the last step: nothing follows
+        ahn = ah;
+        aln = al;
+#pragma unroll
+        for (int q = 0; q < FPW; ++q) bqn[q] = bq[q];
       }
       mma(ah, al, bq);
       ah = ahn;
