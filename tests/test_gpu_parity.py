@@ -242,6 +242,30 @@ def test_full_prefill_hash(full):
     check_forward(lay, x, tok, HASH, out, lg, idx, w, rows=[0, 5, 350, 671, 672, 699])
 
 
+def test_full_prefill_hash_invalid(full):
+    """Bad token ids and bad table entries through the full-size prefill path
+    (40 rows: two 32-row groups, experts sliced 8 ways): masked slots,
+    status bits, and the weights renormalised over the slots left."""
+    cfg = gen.config(2)
+    rows = 40
+    table = gen.host_inputs(cfg).tid2eid.copy()
+    tok = _tok(cfg, rows, seed=81)
+    tok[0] = -7                    # bad token id: the whole row is masked
+    tok[33] = cfg.table_rows       # one past the end, in the second group
+    bad = int(tok[5])
+    table[bad, 1] = cfg.experts    # a bad entry: that slot is masked
+    table[bad, 3] = -2
+    lay = Layer(cfg, table=table, share=full)
+    x = _x(cfg, rows, seed=82)
+    out, lg, idx, w, st = lay.run(x, tok, HASH)
+    assert st == moe.FLAG_BAD_TOKEN | moe.FLAG_BAD_TABLE_ENTRY
+    assert (idx[0] == -1).all() and (w[0] == 0).all() and (idx[33] == -1).all()
+    # a bad entry keeps its raw value as the index, with weight 0
+    assert idx[5, 1] == cfg.experts and idx[5, 3] == -2 and w[5, 1] == 0 and w[5, 3] == 0
+    assert abs(float(w[5].sum()) - 1.0) < 1e-5
+    check_forward(lay, x, tok, HASH, out, lg, idx, w, rows=[0, 5, 6, 33, 39])
+
+
 def test_full_prefill_config3(full):
     cfg = gen.config(3)
     lay = Layer(cfg, share=full)
