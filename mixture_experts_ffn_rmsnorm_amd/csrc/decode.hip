@@ -718,20 +718,29 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
 template <int H, int I>
 __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   __shared__ float hs[kDecodeMaxRows * I];
+  __shared__ int s_er[kDecodeMaxSlots];    // the plan's entry rows and weights, for the reduce
+  __shared__ float s_ew[kDecodeMaxSlots];
   __shared__ int s_last;
   const int R = a.R;
   const DecodePlan* P = a.plan;
   const int ng = plan_ngroups(P);
   const int x = blockIdx.x, u = blockIdx.y;
   constexpr int dnt = H / kDnRows;
+  int ne = P->nentries;
+  ne = ne < 0 ? 0 : (ne > kDecodeMaxSlots ? kDecodeMaxSlots : ne);
   if (ng > 0) {
     if (u >= ng) return;
     const PlanGroup g = plan_group(P, u, a.E);
     const float* src[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
-    down_tile<H, I, kDnRows>(a.down + (int64_t)g.expert * H * I, hs, g.nr, x, a.d32, g.begin,
-                    [&]() { stage_rows<I>(hs, src, g.nr); });
+    down_tile<H, I, kDnRows>(a.down + (int64_t)g.expert * H * I, hs, g.nr, x, a.d32, g.begin, [&]() {
+      if (threadIdx.x < kDecodeMaxSlots) {
+        s_er[threadIdx.x] = P->entry_row[threadIdx.x];
+        s_ew[threadIdx.x] = P->entry_w[threadIdx.x];
+      }
+      stage_rows<I>(hs, src, g.nr);  // ends with a barrier
+    });
     sync_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -749,13 +758,20 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   if (t >= R * kDnRows) return;
   const int r = t / kDnRows;
   const int h = x + (t % kDnRows) * dnt;
-  int ne = P->nentries;
-  ne = ne < 0 ? 0 : (ne > kDecodeMaxSlots ? kDecodeMaxSlots : ne);
+  const float sh = a.d32[(int64_t)(kDecodeMaxSlots + r) * H + h];
   float o = 0.f;
-  if (ng > 0)
-    for (int j = 0; j < ne; ++j)
-      if (P->entry_row[j] == r) o = fmaf(P->entry_w[j], load_wt(&a.d32[(int64_t)j * H + h]), o);
-  o += a.d32[(int64_t)(kDecodeMaxSlots + r) * H + h];
+  if (ng > 0 && ne > 0) {
+    // every entry's partial is requested at once (one memory round trip; the
+    // index is clamped, so the loads past ne re-read a valid row), then the
+    // row's own entries are added in plan order
+    float v[kDecodeMaxSlots];
+#pragma unroll
+    for (int j = 0; j < kDecodeMaxSlots; ++j) v[j] = load_wt(&a.d32[(int64_t)(j < ne ? j : ne - 1) * H + h]);
+#pragma unroll
+    for (int j = 0; j < kDecodeMaxSlots; ++j)
+      if (j < ne && s_er[j] == r) o = fmaf(s_ew[j], v[j], o);
+  }
+  o += sh;
   a.out[(int64_t)r * H + h] = o;
 }
 
