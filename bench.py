@@ -97,6 +97,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="distinct weight sets cycled (default 4 decode, 1 prefill)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the device-ceiling microbenchmarks (HBM read, fp16 MFMA) reported as measured_peaks")
     ap.add_argument("--graph", action="store_true",
                     help="also time the L layers chained (each layer's output the next one's input) "
                          "as one captured HIP graph, replayed --steps times; reported under 'graph'")
@@ -244,6 +246,16 @@ def main():
 
     if args.graph:
         res["graph"] = graph_chain(dims, cfg, layers, x, tok, ws, args.steps, log)
+    if not args.no_peaks:
+        # the published peaks above are the roofline's; these are the same
+        # two ceilings measured on this device, after the timed passes
+        from mixture_experts_ffn_rmsnorm_amd import device_peaks
+
+        log("measuring device ceilings")
+        pk = device_peaks.measure()
+        top = pk["hbm_read_GBps"] if roof["unit"] == "GB/s" else pk["mfma_f16_TFLOPs"]
+        pk["roofline_frac_of_measured"] = roof["achieved"] / top
+        res["measured_peaks"] = pk
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds, log, gpu0)
     print(json.dumps(res), flush=True)

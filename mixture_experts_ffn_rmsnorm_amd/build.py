@@ -1,11 +1,12 @@
-"""Build libmoeffn.so in-tree with hipcc for gfx950.
+"""Build libmoeffn.so (and libmoepeaks.so) in-tree with hipcc for gfx950.
 
     python -m mixture_experts_ffn_rmsnorm_amd.build
 
 Each ``csrc/*.hip`` compiles to an object under ``_build/`` in parallel, then
-everything links into ``mixture_experts_ffn_rmsnorm_amd/libmoeffn.so``.  The
-build always recompiles (it is the "does it build" check); loading code
-never builds.
+everything links into ``mixture_experts_ffn_rmsnorm_amd/libmoeffn.so``;
+``peaks/peaks.hip`` (the device-ceiling microbenchmarks) becomes
+``mixture_experts_ffn_rmsnorm_amd/libmoepeaks.so``.  The build always
+recompiles (it is the "does it build" check); loading code never builds.
 """
 
 from __future__ import annotations
@@ -23,6 +24,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoeffn.so")
+PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(PKG, "libmoepeaks.so")
 ARCH = os.environ.get("MOEFFN_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -48,19 +51,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
-        raise RuntimeError(f"link failed:\n{p.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {lib} failed:\n{p.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        objs = list(ex.map(_compile, srcs + [PEAKS_SRC]))
+    _link(objs[-1:], PEAKS_LIB)
+    objs = objs[:-1]
+    _link(objs, LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 

@@ -155,7 +155,7 @@ def _pmc_pass(counter, cmd, out_dir):
 
 def cmd_traffic(args, extra):
     copy_cmd = [sys.executable, "-m", "mixture_experts_ffn_rmsnorm_amd.profiling", "child-copy"]
-    bench = _bench_cmd(args.workload, ["--steps", "5", "--warmup", "2", "--no-cpu-baseline"])
+    bench = _bench_cmd(args.workload, ["--steps", "5", "--warmup", "2", "--no-cpu-baseline", "--no-peaks"])
     res = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         copy = _pmc_pass(counter, copy_cmd, os.path.join(args.scratch, f"copy_{counter}"))
@@ -171,7 +171,7 @@ def cmd_traffic(args, extra):
         f.write(f"# HBM traffic per dispatch, workload {args.workload}, from rocprofv3 counters\n")
         f.write(f"# command: python3 -m mixture_experts_ffn_rmsnorm_amd.profiling traffic --workload {args.workload}\n")
         f.write("# passes: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, each over\n")
-        f.write(f"#   python3 bench.py --workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline\n")
+        f.write(f"#   python3 bench.py --workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline --no-peaks\n")
         f.write("#   and over a 1 GiB device-to-device copy (calibration: factor = bytes / counter bytes)\n")
         f.write(f"sources_sha256: {sources_digest()}\n")
         f.write(f"copy_kernel: {short_name(cf_name)}\n")

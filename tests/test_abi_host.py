@@ -217,3 +217,25 @@ def test_strerror():
     for c in range(7):
         assert moe.strerror(c) and moe.strerror(c) != "unknown status"
     assert moe.strerror(99) == "unknown status"
+
+
+def test_peaks_library_exports_and_rejects_bad_arguments():
+    """The device-ceiling microbenchmarks (libmoepeaks.so) load, export their
+    functions, and reject malformed arguments before any launch."""
+    from mixture_experts_ffn_rmsnorm_amd import device_peaks
+
+    L = device_peaks.lib()
+    nm = subprocess.run(["nm", "-D", "--defined-only", device_peaks.LIB_PATH], capture_output=True, text=True,
+                        check=True)
+    syms = set(re.findall(r"\b(moe_\w+)\b", nm.stdout))
+    assert set(device_peaks.EXPORTS) <= syms
+    assert L.moe_peaks_mfma_chains() >= 1 and L.moe_peaks_mfma_threads() % 64 == 0
+    invalid = 1  # hipErrorInvalidValue
+    sink = ctypes.c_void_p(FAKE)
+    assert L.moe_peaks_read(None, 1 << 20, sink, 16, None) == invalid
+    assert L.moe_peaks_read(ctypes.c_void_p(FAKE), (1 << 20) + 4, sink, 16, None) == invalid  # not whole 16-B chunks
+    assert L.moe_peaks_read(ctypes.c_void_p(FAKE + 8), 1 << 20, sink, 16, None) == invalid  # misaligned
+    assert L.moe_peaks_read(ctypes.c_void_p(FAKE), 1 << 20, sink, 0, None) == invalid
+    assert L.moe_peaks_mfma(0, 16, sink, None) == invalid
+    assert L.moe_peaks_mfma(16, 0, sink, None) == invalid
+    assert L.moe_peaks_mfma(16, 16, None, None) == invalid
