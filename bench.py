@@ -49,6 +49,12 @@ def alg_bytes(kernel, cfg, U, R):
         return H * I * 2 + U * 2 * I * H * 2 + R * (I + H) * 4 + R * K * (H + I) * 4
     if kernel == "dec_down_reduce":  # routed down + weighted reduce
         return U * H * I * 2 + R * K * (I + 2 * H) * 4 + R * H * 4 + x
+    if kernel == "dec1_router":      # one-row path: router, logits + xn out
+        return E * H * 2 + x + H * 4 + R * E * 4 + R * H * 4
+    if kernel == "dec1_gateup":      # shared + routed gate/up, routing from the logits
+        return (U + 1) * 2 * I * H * 2 + R * E * 4 + R * H * 4 + (R * K + R) * I * 4 + R * K * 12
+    if kernel == "dec1_down_reduce":  # routed + shared down + weighted reduce
+        return (U + 1) * H * I * 2 + (R * K + R) * I * 4 + (R * K + R) * 2 * H * 4 + R * H * 4
     if kernel == "pre_norm":         # x in, xn16 + xlo16 out
         return x + 2 * R * H * 2
     if kernel == "pre_router":       # xn16 + xlo16 in, logits + routing out, router weights once

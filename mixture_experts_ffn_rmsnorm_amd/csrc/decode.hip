@@ -15,6 +15,15 @@
 //                  last block of each column tile forms out = sum of weight
 //                  * down + shared in a fixed order
 //
+// With one row the launches divide the work differently, and no workgroup
+// ever waits for another:
+//   k_dec_head<true>  router only; each router wave also stores its expert's
+//                     selection key and float64 sigmoid
+//   k_dec1_gateup     shared gate/up blocks, and routed gate/up blocks that
+//                     each route the row from those keys before streaming
+//   k_dec_down<true>  routed down, plus the shared down in two half-blocks
+//                     per column tile, and the same reduce
+//
 // Stage order follows forward_ffn_rows on the hf2q ffn_forward.rs page
 // (rms_norm -> MoE gate -> route -> sanitize -> routed/shared gate, up ->
 // swiglu -> routed/shared down -> weighted reduce); the page's rows*top_k
@@ -439,6 +448,84 @@ __device__ __forceinline__ SlotRoute route_slots(float lg0, float lg1, float lg2
   return o;
 }
 
+// route_slots for one row from per-expert values the router launch stored:
+// key[j] = ordered_key(score_key(logit, bias)) and sig[j] = sigmoid_f64(logit)
+// of expert lane + 64j (the same functions route_slots applies to the
+// logits, so the same bits).  The selection loop, its tie-break and the
+// weights are route_slots'; the sigmoid of a chosen expert is read from its
+// lane instead of recomputed.
+__device__ __forceinline__ double lane_f64(double v, int src) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)b, src);
+  const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+  return __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ SlotRoute route_slots_keyed(const uint64_t (&key)[4], const double (&sig)[4], int E, int K,
+                                                       bool hash, bool tok_ok, int ent) {
+  const int lane = threadIdx.x & (kWave - 1);
+  SlotRoute o;
+  o.flags = 0;
+  double sg = 0.0;
+  bool use = false;
+  if (!hash) {
+    uint64_t u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u[j] = lane + kWave * j < E ? key[j] : 0ull;
+    o.idx = -1;
+#pragma unroll 1
+    for (int k = 0; k < K; ++k) {
+      uint64_t lm = u[0] > u[1] ? u[0] : u[1];
+      lm = u[2] > lm ? u[2] : lm;
+      lm = u[3] > lm ? u[3] : lm;
+      const uint64_t m = wave_max_u64(lm);
+      const uint64_t b0 = __ballot(u[0] == m && m != 0ull), b1 = __ballot(u[1] == m && m != 0ull);
+      const uint64_t b2 = __ballot(u[2] == m && m != 0ull), b3 = __ballot(u[3] == m && m != 0ull);
+      const int j = b0 ? 0 : b1 ? 1 : b2 ? 2 : b3 ? 3 : -1;
+      const uint64_t bm = j == 0 ? b0 : j == 1 ? b1 : j == 2 ? b2 : b3;
+      int e = 0;
+      double v = lane_f64(sig[0], 0);
+      if (j >= 0) {
+        const int wl = __ffsll((unsigned long long)bm) - 1;
+        e = wl + kWave * j;
+        v = lane_f64(j == 0 ? sig[0] : j == 1 ? sig[1] : j == 2 ? sig[2] : sig[3], wl);
+        if (lane == wl) {
+          u[0] = j == 0 ? 0ull : u[0];
+          u[1] = j == 1 ? 0ull : u[1];
+          u[2] = j == 2 ? 0ull : u[2];
+          u[3] = j == 3 ? 0ull : u[3];
+        }
+      }
+      if (lane == k) {
+        o.idx = e;
+        sg = v;
+      }
+    }
+    use = lane < K;
+  } else {
+    const int e = (tok_ok && lane < K) ? ent : -1;
+    use = tok_ok && lane < K && e >= 0 && e < E;
+    const int src = use ? (e & (kWave - 1)) : 0, j = use ? e / kWave : 0;
+    double v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const long long b = __double_as_longlong(sig[q]);
+      const int lo = __shfl((int)(uint32_t)b, src), hi = __shfl((int)(uint32_t)(b >> 32), src);
+      v[q] = __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
+    }
+    sg = use ? (j == 0 ? v[0] : j == 1 ? v[1] : j == 2 ? v[2] : v[3]) : 0.0;
+    o.idx = lane < K ? e : -1;
+    if (__ballot(tok_ok && lane < K && !use)) o.flags |= MOE_FLAG_BAD_TABLE_ENTRY;
+    if (!tok_ok) o.flags |= MOE_FLAG_BAD_TOKEN;
+  }
+  if (!use) sg = 0.0;
+  double tot = 0.0;
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) tot += lane_f64(sg, k);
+  o.valid = use;
+  o.w = (use && (!hash || tot > 0.0)) ? (float)(sg / tot) : 0.0f;
+  return o;
+}
+
 // The call's tag for the decode path's tagged words: the host's per-call
 // value plus the workspace's device-side call count, which the gate/up
 // launch advances -- distinct for every call, also for every replay of a
@@ -451,9 +538,10 @@ __device__ __forceinline__ uint32_t call_epoch(const FwdArgs& a) {
 // Routing of the batch into LDS: wave r < R routes row r.  It first reads
 // what the route needs besides the logits (bias, or the token's table row),
 // then polls the row's tagged logits until every one carries the call's
-// epoch (bounded; returns false on timeout).
-__device__ bool route_rows(const FwdArgs& a, uint32_t epoch, int* s_idx, float* s_w, unsigned char* s_valid,
-                           uint32_t* s_flags) {
+// epoch (bounded; returns false on timeout).  `plain` (one row, after the
+// router launch): it reads the stored keys and sigmoids instead, no waiting.
+__device__ bool route_rows(const FwdArgs& a, uint32_t epoch, bool plain, int* s_idx, float* s_w,
+                           unsigned char* s_valid, uint32_t* s_flags) {
   const int R = a.R, K = a.K, E = a.E;
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   if (wv >= R) return true;
@@ -468,6 +556,24 @@ __device__ bool route_rows(const FwdArgs& a, uint32_t epoch, int* s_idx, float* 
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) bias[j] = (lane + kWave * j < E) ? a.bias[lane + kWave * j] : 0.f;
+  }
+  if (plain) {  // one row: the router launch's keys and sigmoids, plain loads
+    uint64_t key[4];
+    double sig[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + kWave * j;
+      key[j] = e < E ? a.sync->route_key[e] : 0ull;
+      sig[j] = e < E ? a.sync->route_sig[e] : 0.0;
+    }
+    const SlotRoute sr = route_slots_keyed(key, sig, E, K, hash, tok_ok, ent);
+    if (lane < K) {
+      s_idx[lane] = sr.idx;
+      s_w[lane] = sr.w;
+      s_valid[lane] = sr.valid;
+    }
+    if (lane == 0) s_flags[0] = sr.flags;
+    return true;
   }
   const uint64_t* tags = a.sync->logit_tag + wv * E;
   float lgv[4];
@@ -499,6 +605,32 @@ __device__ bool route_rows(const FwdArgs& a, uint32_t epoch, int* s_idx, float* 
   return ready;
 }
 
+// Writes the block's routing (indices, weights, row flags, status word) and
+// the plan (from LDS) to the workspace for the later launches and the
+// caller, and clears the down launch's tile counters.  `epoch` is the call's
+// tag (0 for a call whose kernels never wait), `ok` false if a wait gave up.
+__device__ void publish_routing(const FwdArgs& a, uint32_t epoch, bool ok, const int* s_idx, const float* s_w,
+                                const uint32_t* s_flags, const DecodePlan* P) {
+  const int R = a.R;
+  DecodeSync* sy = a.sync;
+  for (int s = threadIdx.x; s < R * a.K; s += kThreads) {
+    a.idx[s] = s_idx[s];
+    a.wts[s] = s_w[s];
+  }
+  if ((int)threadIdx.x < R) a.rowflags[threadIdx.x] = s_flags[threadIdx.x];
+  if (threadIdx.x == 0) {
+    uint32_t f = 0;
+    for (int r = 0; r < R; ++r) f |= s_flags[r];
+    a.status[0] = f;
+    sy->last_epoch = epoch;
+    if (!ok) store_flag(&sy->timeout_epoch, epoch);
+  }
+  for (int i = threadIdx.x; i < kDecodeMaxTiles; i += kThreads) sy->tile_cnt[i] = 0;
+  const int* ps = (const int*)P;
+  int* pd = (int*)a.plan;
+  for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += kThreads) pd[i] = ps[i];
+}
+
 // The plan as read by the tail kernel, every field clamped to its range so
 // that no value can index outside the buffers.
 struct PlanGroup {
@@ -526,20 +658,20 @@ __device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R) {
   return r < 0 ? 0 : (r >= R ? R - 1 : r);
 }
 
-// Down projection of 32 hidden rows of one expert (wbase [H][I]) for the nr
-// activation rows staged in hs; tile x of H/32 takes rows x, x + H/32, ...
-// so concurrent blocks read neighbouring rows.  d32 rows ent..ent+nr-1
-// receive the results (written through).
+// Down projection of ROWS hidden rows of one expert (wbase [H][I]) for the
+// nr activation rows staged in hs: the block's i-th row (i = wave + 4j) is
+// x + (i * mul + add) * stride, so concurrent blocks read neighbouring rows
+// (x, x + stride, ... for mul 1; every other one of them, from `add`, for
+// mul 2).  d32 rows ent..ent+nr-1 receive the results (written through).
 template <int H, int I, int ROWS, class Pre>
-__device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs, int nr, int x, float* d32, int ent,
-                                          Pre pre) {
+__device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs, int nr, int x, int stride, int mul,
+                                          int add, float* d32, int ent, Pre pre) {
   constexpr int W = kThreads / kWave, RPW = ROWS / W;  // rows per wave
   static_assert(RPW * 4 <= kWave && RPW % 2 == 0, "one lane per result; whole row pairs in flight");
   __shared__ float s_res[ROWS * 4];  // results wait here until the stream ends
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   float* res = s_res + wv * RPW * 4;
-  constexpr int tiles = H / ROWS;
-  auto row_of = [&](int j) { return x + (wv + j * W) * tiles; };
+  auto row_of = [&](int j) { return x + ((wv + j * W) * mul + add) * stride; };
   auto rowptr = [&](int j) { return wbase + (int64_t)row_of(j) * I; };
   auto sink = [&](int j, const float (&part)[4]) {
 #pragma unroll
@@ -574,7 +706,7 @@ __device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs
 //   the down kernel's tile counters.  A wait that gives up records the
 //   call's epoch in timeout_epoch (reported as MOE_FLAG_SYNC_TIMEOUT by
 //   moe_ffn_status).
-template <int H, int I>
+template <int H, int I, bool kRouterOnly>
 __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [R][H]
   __shared__ int s_idx[kDecodeMaxSlots];
@@ -588,34 +720,19 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   const uint32_t epoch = call_epoch(a);
   const int nrb = (E + 3) / 4, nsh = I / kShRows;
   const int b = blockIdx.x;
-  if (b == nrb + nsh) {  // plan block
+  if (!kRouterOnly && b == nrb + nsh) {  // plan block
     __shared__ int s_ok;
     if (threadIdx.x == 0) s_ok = 1;
     __syncthreads();
-    if (!route_rows(a, epoch, s_idx, s_w, s_valid, s_flags) && lane == 0) s_ok = 0;
+    if (!route_rows(a, epoch, false, s_idx, s_w, s_valid, s_flags) && lane == 0) s_ok = 0;
     __syncthreads();
     const bool ok = s_ok;
     if (wv == 0) build_plan(s_idx, s_w, s_valid, R, K, E, &P);
     __syncthreads();
-    for (int s = threadIdx.x; s < R * K; s += kThreads) {
-      a.idx[s] = s_idx[s];
-      a.wts[s] = s_w[s];
-    }
-    if ((int)threadIdx.x < R) a.rowflags[threadIdx.x] = s_flags[threadIdx.x];
-    if (threadIdx.x == 0) {
-      uint32_t f = 0;
-      for (int r = 0; r < R; ++r) f |= s_flags[r];
-      a.status[0] = f;
-      sy->last_epoch = epoch;
-      if (!ok) store_flag(&sy->timeout_epoch, epoch);
-    }
-    for (int i = threadIdx.x; i < kDecodeMaxTiles; i += kThreads) sy->tile_cnt[i] = 0;
-    const int* ps = (const int*)&P;
-    int* pd = (int*)a.plan;
-    for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += kThreads) pd[i] = ps[i];
+    publish_routing(a, epoch, ok, s_idx, s_w, s_flags, &P);
     return;
   }
-  if (b >= nrb) {  // shared gate/up block
+  if (!kRouterOnly && b >= nrb) {  // shared gate/up block
     const int x = b - nrb;
     auto stage = [&]() {
       norm_rows_to_lds<H>(a.x, a.norm_w, R, a.eps, xs);
@@ -639,6 +756,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
       if (c < NCH - 1 || full) q[c] = load_stream(a.router + (int64_t)e * H + c * 512 + lane * 8);
   }
   norm_rows_to_lds<H>(a.x, a.norm_w, R, a.eps, xs);
+  if (kRouterOnly && b == 0)  // the later launches stage the normalised rows from xn
+    for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
   if (e >= E) return;
   float dot[kDecodeMaxRows] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -664,8 +783,14 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
       const float v = wave_sum(dot[r]);
       if (lane == 0) {
         a.logits[(int64_t)r * E + e] = v;
-        __hip_atomic_store(&sy->logit_tag[r * E + e], ((uint64_t)epoch << 32) | __float_as_uint(v),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (kRouterOnly) {  // one row: what the gate/up blocks' routing needs of this expert
+          const double sg = sigmoid_f64(v);
+          sy->route_sig[e] = sg;
+          sy->route_key[e] = a.layer_kind == MOE_LAYER_HASH ? 0ull : ordered_key(score_key(v, a.bias[e]));
+        }
+        if (!kRouterOnly)
+          __hip_atomic_store(&sy->logit_tag[r * E + e], ((uint64_t)epoch << 32) | __float_as_uint(v),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -691,7 +816,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
     const float* src[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(kDecodeMaxSlots + (j < a.R ? j : 0)) * I;
-    down_tile<H, I, kSdRows>(a.down_sh, xs, a.R, b, a.d32, kDecodeMaxSlots, [&]() { stage_rows<I>(xs, src, a.R); });
+    down_tile<H, I, kSdRows>(a.down_sh, xs, a.R, b, H / kSdRows, 1, 0, a.d32, kDecodeMaxSlots,
+                             [&]() { stage_rows<I>(xs, src, a.R); });
     return;
   }
   const DecodePlan* P = a.plan;
@@ -706,16 +832,63 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Routed down + weighted reduce.  grid = (H/32, max distinct routed
-// experts).  Block (x, u) computes hidden rows x, x + H/32, ... of the plan's
-// u-th expert's down projection for its rows and writes them through to
-// d32; it then counts itself in tile_cnt[x].  The block that completes the
-// count (every routed group of the tile has written) forms, for those 32
+// One-row gate/up launch: grid = I/8 shared gate/up blocks, then
+// G * I/16 routed gate/up blocks (G = top_k).  The router launch before it
+// has written the logits and xn.  A routed block routes the row itself --
+// wave 0 reads the logits and picks the slots as the head's plan block
+// does, then builds the plan in LDS -- and streams the rows of the plan's
+// u-th expert; the u = 0, x = 0 block also publishes the routing and the
+// plan.  No block waits for another: with one row the routing is a few
+// microseconds of work that every block repeats, against the
+// cross-workgroup round trips of a shared plan.  At full size this is 256 +
+// 6 * 128 blocks, one shared and three routed per compute unit.
+template <int H, int I>
+__global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float xs[];  // [H] normalised row
+  __shared__ int s_idx[kDecodeMaxSlots];
+  __shared__ float s_w[kDecodeMaxSlots];
+  __shared__ unsigned char s_valid[kDecodeMaxSlots];
+  __shared__ uint32_t s_flags[kDecodeMaxRows];
+  __shared__ DecodePlan P;
+  constexpr int nsh = I / kShRows, gut = I / kGuRows;
+  const int b = blockIdx.x;
+  const float* src[4] = {a.xn32, a.xn32, a.xn32, a.xn32};
+  if (b < nsh) {  // shared gate/up block
+    // the row count stays a run-time value (a.R = 1 here): with a constant 1
+    // the compiler keeps the whole activation row in registers
+    gateup_tile<H, I, kShRows, 2>(a.gate_sh, a.up_sh, xs, a.R, b, nsh, a.h32, kDecodeMaxSlots,
+                                  [&]() { stage_rows<H>(xs, src, a.R); });
+    return;
+  }
+  const int u = (b - nsh) / gut, x = (b - nsh) % gut;
+  route_rows(a, 0, true, s_idx, s_w, s_valid, s_flags);  // wave 0 (the row)
+  __syncthreads();
+  if (threadIdx.x < kWave) build_plan(s_idx, s_w, s_valid, 1, a.K, a.E, &P);
+  __syncthreads();
+  if (u == 0 && x == 0) publish_routing(a, 0u, true, s_idx, s_w, s_flags, &P);
+  if (u >= plan_ngroups(&P)) return;
+  const PlanGroup g = plan_group(&P, u, a.E);
+  const int nr = g.nr < a.R ? g.nr : a.R;  // LDS holds a.R rows
+  gateup_tile<H, I, kGuRows, 2>(a.gate + (int64_t)g.expert * I * H, a.up + (int64_t)g.expert * I * H, xs, nr, x, gut,
+                                a.h32, g.begin, [&]() { stage_rows<H>(xs, src, nr); });
+}
+
+// ---------------------------------------------------------------------------
+// Routed down + weighted reduce.  grid = (H/32, G) with G the most distinct
+// routed experts, plus two rows of shared-down blocks when kShared (the
+// one-row path, whose shared h is computed by the launch before).  Block
+// (x, u < G) computes hidden rows x, x + H/32, ... of the plan's u-th
+// expert's down projection for its rows and writes them through to d32;
+// shared block (x, G + h) computes every other one of those rows, from the
+// h-th, of the shared down projection.  Each then counts itself in
+// tile_cnt[x].  The block that completes the count (every routed group of
+// the tile, and both shared halves, have written) forms, for those 32
 // columns, out[r] = sum over r's (expert, row) pairs in plan order (experts
 // ascending) of weight * down, then + shared down -- a fixed order, so the
-// output is bitwise reproducible.  No block waits for another.  With no
-// valid routed expert at all, the u = 0 blocks write out = shared down.
-template <int H, int I>
+// output is bitwise reproducible.  No block waits for another.  Without
+// kShared and with no valid routed expert at all, the u = 0 blocks write
+// out = shared down.
+template <int H, int I, bool kShared>
 __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   __shared__ float hs[kDecodeMaxRows * I];
   __shared__ int s_er[kDecodeMaxSlots];    // the plan's entry rows and weights, for the reduce
@@ -728,25 +901,40 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   constexpr int dnt = H / kDnRows;
   int ne = P->nentries;
   ne = ne < 0 ? 0 : (ne > kDecodeMaxSlots ? kDecodeMaxSlots : ne);
-  if (ng > 0) {
-    if (u >= ng) return;
-    const PlanGroup g = plan_group(P, u, a.E);
-    const float* src[4];
+  const int G = kShared ? (int)gridDim.y - 2 : (int)gridDim.y;
+  const int expect = ng + (kShared ? 2 : 0);  // blocks that write into tile x
+  auto stage_entries = [&]() {
+    if (threadIdx.x < kDecodeMaxSlots) {
+      s_er[threadIdx.x] = P->entry_row[threadIdx.x];
+      s_ew[threadIdx.x] = P->entry_w[threadIdx.x];
+    }
+  };
+  if (expect > 0) {
+    if (kShared && u >= G) {  // shared half-block
+      const float* src[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
-    down_tile<H, I, kDnRows>(a.down + (int64_t)g.expert * H * I, hs, g.nr, x, a.d32, g.begin, [&]() {
-      if (threadIdx.x < kDecodeMaxSlots) {
-        s_er[threadIdx.x] = P->entry_row[threadIdx.x];
-        s_ew[threadIdx.x] = P->entry_w[threadIdx.x];
-      }
-      stage_rows<I>(hs, src, g.nr);  // ends with a barrier
-    });
+      for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(kDecodeMaxSlots + (j < R ? j : 0)) * I;
+      down_tile<H, I, kDnRows / 2>(a.down_sh, hs, R, x, dnt, 2, u - G, a.d32, kDecodeMaxSlots, [&]() {
+        stage_entries();
+        stage_rows<I>(hs, src, R);  // ends with a barrier
+      });
+    } else {
+      if (u >= ng) return;
+      const PlanGroup g = plan_group(P, u, a.E);
+      const float* src[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
+      down_tile<H, I, kDnRows>(a.down + (int64_t)g.expert * H * I, hs, g.nr, x, dnt, 1, 0, a.d32, g.begin, [&]() {
+        stage_entries();
+        stage_rows<I>(hs, src, g.nr);  // ends with a barrier
+      });
+    }
     sync_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
       const uint32_t prev =
           __hip_atomic_fetch_add(&a.sync->tile_cnt[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = prev + 1 == (uint32_t)ng;
+      s_last = prev + 1 == (uint32_t)expect;
     }
     __syncthreads();
     if (!s_last) return;
@@ -780,14 +968,27 @@ hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   static_assert(H / kDnRows <= kDecodeMaxTiles && I / kShRows <= kDecodeMaxTiles, "too many tiles");
   FwdArgs args = a;
   const int gmax = a.R * a.K < a.E ? a.R * a.K : a.E;
-  hipError_t err = launch("dec_head", (const void*)k_dec_head<H, I>, dim3((a.E + 3) / 4 + I / kShRows + 1),
-                          dim3(kThreads), (size_t)a.R * H * 4, s, &args);
+  hipError_t err;
+  if (a.R == 1) {
+    // one row: router launch, then gate/up blocks that route for
+    // themselves, then routed + shared down with the reduce
+    err = launch("dec1_router", (const void*)k_dec_head<H, I, true>, dim3((a.E + 3) / 4), dim3(kThreads),
+                 (size_t)H * 4, s, &args);
+    if (err != hipSuccess) return err;
+    err = launch("dec1_gateup", (const void*)k_dec1_gateup<H, I>, dim3(I / kShRows + gmax * (I / kGuRows)),
+                 dim3(kThreads), (size_t)H * 4, s, &args);
+    if (err != hipSuccess) return err;
+    return launch("dec1_down_reduce", (const void*)k_dec_down<H, I, true>, dim3(H / kDnRows, gmax + 2),
+                  dim3(kThreads), 0, s, &args);
+  }
+  err = launch("dec_head", (const void*)k_dec_head<H, I, false>, dim3((a.E + 3) / 4 + I / kShRows + 1),
+               dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
   err = launch("dec_gateup", (const void*)k_dec_gateup<H, I>, dim3(H / kSdRows + gmax * (I / kGuRows)),
                dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  return launch("dec_down_reduce", (const void*)k_dec_down<H, I>, dim3(H / kDnRows, gmax), dim3(kThreads), 0, s,
-                &args);
+  return launch("dec_down_reduce", (const void*)k_dec_down<H, I, false>, dim3(H / kDnRows, gmax), dim3(kThreads), 0,
+                s, &args);
 }
 
 }  // namespace

@@ -48,6 +48,10 @@ struct DecodeSync {
   uint32_t call_seq;                     // decode calls made on this workspace (device side)
   uint32_t pad[13];
   uint64_t logit_tag[kDecodeMaxRows * kMaxExperts];  // router wave -> plan block: epoch | f32 logit bits
+  // one-row path: each expert's ordered selection key and float64 sigmoid,
+  // written by the router launch for the gate/up blocks that route
+  uint64_t route_key[kMaxExperts];
+  double route_sig[kMaxExperts];
   uint32_t tile_cnt[kDecodeMaxTiles];    // groups finished per down column tile
 };
 

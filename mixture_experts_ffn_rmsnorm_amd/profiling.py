@@ -73,6 +73,13 @@ LAUNCH_NAMES = [
 
 def launch_name(kernel: str) -> str | None:
     k = short_name(kernel).replace(" ", "")
+    # the one-row decode path: router-only head, self-routing gate/up, down with the shared expert
+    if k.startswith("k_dec_head") and k.endswith("true>"):
+        return "dec1_router"
+    if k.startswith("k_dec1_gateup"):
+        return "dec1_gateup"
+    if k.startswith("k_dec_down") and k.endswith("true>"):
+        return "dec1_down_reduce"
     for key, name in LAUNCH_NAMES:
         if k.startswith(key.replace(" ", "")):
             return name

@@ -228,6 +228,24 @@ def test_full_prefill_router_slices(full, rows):
     check_forward(full, x, None, SCORE, out, lg, idx, w, rows=[0, 31, 32, rows // 2, rows - 2, rows - 1])
 
 
+def test_full_decode_one_row_hash(full):
+    """One hash-routed row at full size (the one-row path: keys and sigmoids
+    from the router launch, routing inside every routed gate/up block), a
+    normal token and then a bad one."""
+    cfg = gen.config(2)
+    lay = Layer(cfg, share=full)
+    x = _x(cfg, 1, seed=91)
+    tok = _tok(cfg, 1, seed=92)
+    out, lg, idx, w, st = lay.run(x, tok, HASH)
+    assert st == 0
+    check_routing_exact(lay, lg, idx, w, tok, HASH)
+    check_forward(lay, x, tok, HASH, out, lg, idx, w)
+    tok_bad = np.array([-1], dtype=np.int32)
+    out, lg, idx, w, st = lay.run(x, tok_bad, HASH)
+    assert st == moe.FLAG_BAD_TOKEN and (idx == -1).all() and (w == 0).all()
+    check_forward(lay, x, tok_bad, HASH, out, lg, idx, w)
+
+
 def test_full_prefill_hash(full):
     """A hash-routed layer through the prefill path (700 rows: 22 groups, the
     last one ragged, experts sliced 8 ways in the router)."""
