@@ -706,6 +706,64 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
   const int nstatic = total <= grid ? total : (rounds > 3 ? rounds - 2 : 1) * grid;
   auto grab = [&]() { return nstatic + (int)__hip_atomic_fetch_add(&a.gctr[MODE], 1u, __ATOMIC_RELAXED,
                                                                       __HIP_MEMORY_SCOPE_AGENT); };
+  // group and position of a tile: largest g with s_tbase[g] <= tl (empty
+  // groups share their successor's base and lose the search); within the
+  // group, tiles go in bands of SN column tiles, each band in blocks of SM
+  // row tiles x SN column tiles (row tile fastest): an XCD's 32 concurrent
+  // tiles then share 4 activation tiles and 8 weight slices
+  auto locate = [&](int tl, int& g, int& cntg, int& m0, int& n0) {
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tbase[mid] <= tl) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    cntg = s_cnt[g];
+    const int tm = (cntg + BM - 1) / BM;
+    const int local = tl - s_tbase[g];
+    constexpr int SN = NT < 8 ? NT : 8, SM = 4;
+    static_assert(NT % SN == 0, "column bands");
+    const int band = local / (tm * SN), inband = local - band * tm * SN;
+    const int mb = inband / (SM * SN), ms = (tm - mb * SM) < SM ? (tm - mb * SM) : SM;
+    const int ib = inband - mb * SM * SN;
+    m0 = (mb * SM + ib % ms) * BM;
+    n0 = (band * SN + ib / ms) * BN;
+  };
+  // DMA source of A row group i / B row group i of this wave for a tile.
+  // Rows past the group's end read its last row; their results are never
+  // stored.  B: each wave's rows are all gate or all up rows.
+  auto a_src = [&](int g, int cntg, int m0, int i) {
+    const int row = (wv * AG + i) * 8 + (lane >> 3);
+    const int m = (m0 + row < cntg) ? m0 + row : cntg - 1;
+    int64_t r;
+    if (MODE == 0) r = g == E ? (int64_t)m : (int64_t)a.perm[(int64_t)g * R + m];
+    else r = (int64_t)s_rbase[g] + m;
+    return (MODE == 0 ? (const unsigned char*)a.xn16 : (const unsigned char*)a.h16) + r * (KD * 2) +
+           (((wv * AG + i) & 1) ? chunk1 : chunk0);
+  };
+  auto b_src = [&](int g, int n0, int i) {
+    const int bw_row = wv * BG * 8;  // first tile B row of this wave
+    const bool sh = g == E;
+    const uint16_t* bmat;
+    int brow0;
+    if (MODE == 0) {
+      const bool is_up = bw_row >= BN;
+      bmat = sh ? (is_up ? a.up_sh : a.gate_sh) : (is_up ? a.up : a.gate) + (int64_t)g * ND * KD;
+      brow0 = n0 + (is_up ? bw_row - BN : bw_row) + (lane >> 3);
+    } else {
+      bmat = sh ? a.down_sh : a.down + (int64_t)g * ND * KD;
+      brow0 = n0 + bw_row + (lane >> 3);
+    }
+    return (const unsigned char*)bmat + (int64_t)(brow0 + i * 8) * (KD * 2) + (((wv * BG + i) & 1) ? chunk1 : chunk0);
+  };
+  // With three or more stages and a slab that fits in one stage, the
+  // epilogue stages through the ring's last buffer, and a statically dealt
+  // next tile's first k-tile is requested into buffer 0 before the
+  // epilogue, so that its latency overlaps the epilogue (not for the shared
+  // expert's down + reduce, whose per-tile slot table lives in LDS).
+  constexpr bool kPre = MODE != 2 && kStages >= 3 && kSlab * CPITCH * 4 <= ST;
+  unsigned char* const s_stage = s_ring + (kPre ? (kStages - 1) * ST : 0);
+  bool pre = false;  // the current tile's first k-tile was requested by the previous tile
   int tile = first;
   if (tile >= nstatic) {
     if (t == 0) s_next = nstatic < total ? grab() : total;
@@ -715,28 +773,8 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
   while (tile < total) {
     const bool dyn_next = tile + grid >= nstatic;  // the next tile comes from the counter
     int next_dyn = total;
-    // locate the group: largest g with s_tbase[g] <= tile (empty groups
-    // share their successor's base and lose the search)
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_tbase[mid] <= tile) lo = mid; else hi = mid - 1;
-    }
-    const int g = lo;
-    const int cntg = s_cnt[g];
-    const int tm = (cntg + BM - 1) / BM;
-    const int local = tile - s_tbase[g];
-    // within the group, tiles go in bands of SN column tiles, each band in
-    // blocks of SM row tiles x SN column tiles (row tile fastest): an XCD's
-    // 32 concurrent tiles then share 4 activation tiles and 8 weight slices
-    constexpr int SN = NT < 8 ? NT : 8, SM = 4;
-    static_assert(NT % SN == 0, "column bands");
-    const int band = local / (tm * SN), inband = local - band * tm * SN;
-    const int mb = inband / (SM * SN), ms = (tm - mb * SM) < SM ? (tm - mb * SM) : SM;
-    const int ib = inband - mb * SM * SN;
-    const int mt = mb * SM + ib % ms, nt = band * SN + ib / ms;
-    const int m0 = mt * BM, n0 = nt * BN;
-    const bool shared = g == E;
+    int g, cntg, m0, n0;
+    locate(tile, g, cntg, m0, n0);
 
     if (MODE == 2) {
       // slots of this tile's rows: position of each (expert, row) pair in
@@ -759,38 +797,13 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
       }
     }
 
-    // DMA sources.  Rows past the group's end read its last row; their
-    // results are never stored.
+    // DMA sources
     const unsigned char* asrc[AG];
 #pragma unroll
-    for (int i = 0; i < AG; ++i) {
-      const int row = (wv * AG + i) * 8 + (lane >> 3);
-      const int m = (m0 + row < cntg) ? m0 + row : cntg - 1;
-      int64_t r;
-      if (MODE == 0) r = shared ? (int64_t)m : (int64_t)a.perm[(int64_t)g * R + m];
-      else r = (int64_t)s_rbase[g] + m;
-      asrc[i] = (MODE == 0 ? (const unsigned char*)a.xn16 : (const unsigned char*)a.h16) + r * (KD * 2) +
-                (((wv * AG + i) & 1) ? chunk1 : chunk0);
-    }
-    // B: each wave's rows are all gate or all up rows
+    for (int i = 0; i < AG; ++i) asrc[i] = a_src(g, cntg, m0, i);
     const unsigned char* bsrc[BG];
-    {
-      const int bw_row = wv * BG * 8;  // first tile B row of this wave
-      const uint16_t* bmat;
-      int brow0;
-      if (MODE == 0) {
-        const bool is_up = bw_row >= BN;
-        bmat = shared ? (is_up ? a.up_sh : a.gate_sh) : (is_up ? a.up : a.gate) + (int64_t)g * ND * KD;
-        brow0 = n0 + (is_up ? bw_row - BN : bw_row) + (lane >> 3);
-      } else {
-        bmat = shared ? a.down_sh : a.down + (int64_t)g * ND * KD;
-        brow0 = n0 + bw_row + (lane >> 3);
-      }
 #pragma unroll
-      for (int i = 0; i < BG; ++i)
-        bsrc[i] = (const unsigned char*)bmat + (int64_t)(brow0 + i * 8) * (KD * 2) +
-                  (((wv * BG + i) & 1) ? chunk1 : chunk0);
-    }
+    for (int i = 0; i < BG; ++i) bsrc[i] = b_src(g, n0, i);
     // whether this wave loads A rows at all (the small configuration's one
     // A row group per wave; the big one waits with vmcnt(0))
     const bool a_loads = m0 + wv * AG * 8 < cntg;
@@ -849,7 +862,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     auto kloop = [&](auto nv_c) {
     constexpr int NV = decltype(nv_c)::value;
     half8 af[WM], bf[WN];
-    issue(0, 0);
+    if (!pre) issue(0, 0);
     wait_vmcnt<0>();
     __syncthreads();
 #pragma unroll
@@ -925,6 +938,26 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     // the next tile's number is requested now; the epilogue covers the wait
     if (t == 0 && dyn_next && nstatic < total) next_dyn = grab();
     __syncthreads();
+    // the next tile's first k-tile into buffer 0 (free: every wave is past
+    // the k loop and the trailing refills have landed)
+    pre = kPre && !dyn_next && tile + grid < total;
+    if (pre) {
+      int ng, ncnt, nm0, nn0;
+      locate(tile + grid, ng, ncnt, nm0, nn0);
+#pragma unroll
+      for (int i = 0; i < AG; ++i)
+        if (nm0 + (wv * AG + i) * 8 < ncnt) {
+          const unsigned char* src = a_src(ng, ncnt, nm0, i);
+#pragma unroll
+          for (int h = 0; h < NH; ++h) dma16(src + h * 128, ring + a_wave + h * HA + i * 1024);
+        }
+#pragma unroll
+      for (int i = 0; i < BG; ++i) {
+        const unsigned char* src = b_src(ng, nn0, i);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) dma16(src + h * 128, ring + b_wave + h * HB + i * 1024);
+      }
+    }
 
     // epilogue, through LDS in 64-row slabs: D[i][j] of a 32x32 tile sits in
     // lane j + 32*((i/4)%2), register 4*(i/8) + i%4
@@ -946,7 +979,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
             for (int v = 0; v < 16; ++v) {
               const int rl = ii * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 #pragma unroll
-              for (int j = 0; j < WN; ++j) ((float*)s_ring)[rl * CPITCH + brow[j]] = acc[i][j][v];
+              for (int j = 0; j < WN; ++j) ((float*)s_stage)[rl * CPITCH + brow[j]] = acc[i][j][v];
             }
           }
         }
@@ -960,7 +993,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
           for (int v = 0; v < 16; ++v) {
             const int rl = base + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 #pragma unroll
-            for (int j = 0; j < WN; ++j) ((float*)s_ring)[rl * CPITCH + brow[j]] = acc[i][j][v];
+            for (int j = 0; j < WN; ++j) ((float*)s_stage)[rl * CPITCH + brow[j]] = acc[i][j][v];
           }
         }
       }
@@ -971,7 +1004,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
         const int m = m0 + sl * kSlab + rl;
         if (m >= cntg) continue;
         if (MODE != 2) {
-          const float* sv = &((const float*)s_ring)[rl * CPITCH + cc];
+          const float* sv = &((const float*)s_stage)[rl * CPITCH + cc];
           half8 h;
           if (MODE == 0) {
 #pragma unroll
@@ -1003,7 +1036,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
               for (int u = 0; u < 8; ++u) o[u] = fmaf(w, (float)d[k][u], o[u]);
             }
           }
-          const float* sh = &((const float*)s_ring)[rl * CPITCH + cc];
+          const float* sh = &((const float*)s_stage)[rl * CPITCH + cc];
           float4 o0, o1;
           o0.x = o[0] + sh[0]; o0.y = o[1] + sh[1]; o0.z = o[2] + sh[2]; o0.w = o[3] + sh[3];
           o1.x = o[4] + sh[4]; o1.y = o[5] + sh[5]; o1.z = o[6] + sh[6]; o1.w = o[7] + sh[7];
