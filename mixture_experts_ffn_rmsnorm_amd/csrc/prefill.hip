@@ -756,14 +756,17 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     }
     return (const unsigned char*)bmat + (int64_t)(brow0 + i * 8) * (KD * 2) + (((wv * BG + i) & 1) ? chunk1 : chunk0);
   };
-  // With three or more stages and a slab that fits in one stage, the
-  // epilogue stages through the ring's last buffer, and a statically dealt
-  // next tile's first k-tile is requested into buffer 0 before the
-  // epilogue, so that its latency overlaps the epilogue (not for the shared
-  // expert's down + reduce, whose per-tile slot table lives in LDS).
-  constexpr bool kPre = MODE != 2 && kStages >= 3 && kSlab * CPITCH * 4 <= ST;
-  unsigned char* const s_stage = s_ring + (kPre ? (kStages - 1) * ST : 0);
-  bool pre = false;  // the current tile's first k-tile was requested by the previous tile
+  // With three stages and a slab that fits in one stage, the k-tiles of
+  // consecutive statically dealt tiles form one stream: the last two
+  // refills of a tile's k loop request the next tile's first two k-tiles
+  // (instead of re-loading a dead one), so the next tile starts with them
+  // landed; the epilogue stages through the buffer of the tile's last
+  // k-tile, the one buffer left free.  k-tile kt of a tile sits in buffer
+  // (off + kt) % kStages.  Not for the shared expert's down + reduce, whose
+  // per-tile slot table lives in LDS.
+  constexpr bool kPre = MODE != 2 && kStages == 3 && kSlab * CPITCH * 4 <= ST;
+  int off = 0;   // ring offset of the current tile
+  int npre = 0;  // its first k-tiles the previous tile requested (0 or 2)
   int tile = first;
   if (tile >= nstatic) {
     if (t == 0) s_next = nstatic < total ? grab() : total;
@@ -807,6 +810,23 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     // whether this wave loads A rows at all (the small configuration's one
     // A row group per wave; the big one waits with vmcnt(0))
     const bool a_loads = m0 + wv * AG * 8 < cntg;
+    // the next statically dealt tile, whose first k-tiles this tile's k loop
+    // requests: its DMA sources now (their row-list loads land under the k
+    // loop's first full wait)
+    const bool pref = kPre && !dyn_next && tile + grid < total;
+    const unsigned char* nasrc[AG];
+    const unsigned char* nbsrc[BG];
+    bool na_loads = false;
+    int nm0 = 0, ncnt = 0;
+    if (kPre && pref) {
+      int ng, nn0;
+      locate(tile + grid, ng, ncnt, nm0, nn0);
+#pragma unroll
+      for (int i = 0; i < AG; ++i) nasrc[i] = a_src(ng, ncnt, nm0, i);
+#pragma unroll
+      for (int i = 0; i < BG; ++i) nbsrc[i] = b_src(ng, nn0, i);
+      na_loads = nm0 + wv * AG * 8 < ncnt;
+    }
     // k-tile `src` into ring buffer `buf`
     // (A row groups wholly past the group's end are not loaded: the ring
     // waits with vmcnt(0), so the number of loads may differ per wave)
@@ -822,6 +842,20 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
 #pragma unroll
         for (int h = 0; h < NH; ++h) dma16(bsrc[i] + src * (BK * 2) + h * 128, base + b_wave + h * HB + i * 1024);
     };
+    // the same for k-tile `src` of the next tile
+    auto issue_next = [&](int src, int buf) {
+      const uint32_t base = ring + (uint32_t)buf * ST;
+#pragma unroll
+      for (int i = 0; i < AG; ++i)
+        if (nm0 + (wv * AG + i) * 8 < ncnt)
+#pragma unroll
+          for (int h = 0; h < NH; ++h) dma16(nasrc[i] + src * (BK * 2) + h * 128, base + a_wave + h * HA + i * 1024);
+#pragma unroll
+      for (int i = 0; i < BG; ++i)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) dma16(nbsrc[i] + src * (BK * 2) + h * 128, base + b_wave + h * HB + i * 1024);
+    };
+    auto ring_buf = [&](int kt) { return kPre ? (off + kt) % kStages : kt % kStages; };
     // fragment reads of k-step `st` (16 k) from ring buffer `buf`
     auto read_step = [&](int buf, int st, half8 (&af)[WM], uint4 (&rb)[WN], int nv) {
       const unsigned char* As = s_ring + buf * ST + (st >> 2) * HA;
@@ -862,14 +896,23 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     auto kloop = [&](auto nv_c) {
     constexpr int NV = decltype(nv_c)::value;
     half8 af[WM], bf[WN];
-    if (!pre) issue(0, 0);
-    wait_vmcnt<0>();
-    __syncthreads();
+    if constexpr (kPre) {
+      if (npre == 0) issue(0, ring_buf(0));
+      wait_vmcnt<0>();
+      __syncthreads();
 #pragma unroll
-    for (int st = 1; st < kStages; ++st) issue(st < NK ? st : NK - 1, st);
+      for (int st = 1; st < kStages; ++st)
+        if (st >= npre) issue(st < NK ? st : NK - 1, ring_buf(st));
+    } else {
+      issue(0, 0);
+      wait_vmcnt<0>();
+      __syncthreads();
+#pragma unroll
+      for (int st = 1; st < kStages; ++st) issue(st < NK ? st : NK - 1, st);
+    }
     {
       uint4 rb[WN];
-      read_step(0, 0, af, rb, NV);
+      read_step(ring_buf(0), 0, af, rb, NV);
       convert(rb, bf);
     }
     // one B fragment's four MFMAs
@@ -887,7 +930,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     // while the next step's fragment of the previous column converts.
 #pragma unroll 1
     for (int kt = 0; kt < NK; ++kt) {
-      const int buf = kt % kStages, nbuf = (kt + 1) % kStages;
+      const int buf = ring_buf(kt), nbuf = ring_buf(kt + 1);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         half8 afn[WM], bfn[WN];
@@ -899,14 +942,22 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         } else {
           // k-tile kt+1 landed for this wave: only the loads of the
-          // kStages-2 later tiles may still be in flight
-          if (kStages == 2 || !a_loads) wait_vmcnt<(kStages - 2) * BI>();
+          // kStages-2 later tiles may still be in flight (with three
+          // stages, k-tile kt+2: the next tile's first when kt+2 >= NK)
+          const bool later_a = (kPre && pref && kt + 2 >= NK) ? na_loads : a_loads;
+          if (kStages == 2 || !later_a) wait_vmcnt<(kStages - 2) * BI>();
           else wait_vmcnt<(kStages - 2) * (BI + NH)>();
           __syncthreads();  // k-tile kt+1 landed for every wave; every wave is done reading buffer `buf`
           read_step(nbuf, 0, afn, rb, NV);
           __builtin_amdgcn_sched_barrier(0);
           mfma_j(0);
-          issue(kt + kStages < NK ? kt + kStages : NK - 1, buf);
+          if constexpr (!kPre) {
+            issue(kt + kStages < NK ? kt + kStages : NK - 1, buf);
+          } else {
+            if (kt + kStages < NK) issue(kt + kStages, buf);
+            else if (!pref) issue(NK - 1, buf);  // dead refill: the loop body stays the same
+            else if (kt + kStages - NK < kStages - 1) issue_next(kt + kStages - NK, buf);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -934,30 +985,14 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
         default: kloop(std::integral_constant<int, 0>{}); break;
       }
     }
-    wait_vmcnt<0>();  // the trailing refill lands before the ring turns into staging
+    // the trailing refills land before the ring turns into staging (with the
+    // cross-tile stream there are none: the staging buffer gets no refill,
+    // and the next tile's k-tiles may stay in flight)
+    if (!kPre || !pref) wait_vmcnt<0>();
     // the next tile's number is requested now; the epilogue covers the wait
     if (t == 0 && dyn_next && nstatic < total) next_dyn = grab();
     __syncthreads();
-    // the next tile's first k-tile into buffer 0 (free: every wave is past
-    // the k loop and the trailing refills have landed)
-    pre = kPre && !dyn_next && tile + grid < total;
-    if (pre) {
-      int ng, ncnt, nm0, nn0;
-      locate(tile + grid, ng, ncnt, nm0, nn0);
-#pragma unroll
-      for (int i = 0; i < AG; ++i)
-        if (nm0 + (wv * AG + i) * 8 < ncnt) {
-          const unsigned char* src = a_src(ng, ncnt, nm0, i);
-#pragma unroll
-          for (int h = 0; h < NH; ++h) dma16(src + h * 128, ring + a_wave + h * HA + i * 1024);
-        }
-#pragma unroll
-      for (int i = 0; i < BG; ++i) {
-        const unsigned char* src = b_src(ng, nn0, i);
-#pragma unroll
-        for (int h = 0; h < NH; ++h) dma16(src + h * 128, ring + b_wave + h * HB + i * 1024);
-      }
-    }
+    unsigned char* const s_stage = s_ring + (kPre ? ring_buf(NK - 1) * ST : 0);
 
     // epilogue, through LDS in 64-row slabs: D[i][j] of a 32x32 tile sits in
     // lane j + 32*((i/4)%2), register 4*(i/8) + i%4
@@ -1047,6 +1082,10 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
       }
     }
     if (t == 0) s_next = dyn_next ? next_dyn : tile + grid;
+    if constexpr (kPre) {
+      off = pref ? ring_buf(NK) : 0;
+      npre = pref ? kStages - 1 : 0;
+    }
     __syncthreads();  // staging and s_pos are rewritten by the next tile
     tile = s_next;
   }
