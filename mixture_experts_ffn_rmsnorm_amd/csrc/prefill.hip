@@ -881,14 +881,15 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < WN; ++j) acc[i][j] = floatx16{};
 
-    // Two-stage ring: k-tile kt+1 loads while kt is multiplied.  The next
-    // k-step's fragments are read and converted while the 16 MFMAs of the
-    // current step run, across k-tile boundaries too: before the last step
-    // of k-tile kt (its fragments already in registers) every wave waits
-    // for k-tile kt+1, passes the barrier, reads kt+1's first step and
-    // refills kt's buffer with kt+2.  The loop body has no branches: past
-    // the end the refill re-loads the last k-tile into the dead buffer and
-    // the read repeats it.
+    // Ring of kStages buffers: later k-tiles load while kt is multiplied.
+    // The next k-step's fragments are read and converted while the MFMAs of
+    // the current step run, across k-tile boundaries too: before the last
+    // step of k-tile kt (its fragments already in registers) every wave
+    // waits for k-tile kt+1, passes the barrier, reads kt+1's first step and
+    // refills kt's buffer with kt+kStages.  Past the end the refill re-loads
+    // the last k-tile into the dead buffer and the read repeats it -- or,
+    // with the cross-tile stream, requests the next tile's first k-tiles
+    // (and the read past the end reads the next tile's first, unused).
     constexpr int NS = BK / 16;  // k-steps per k-tile
     // The k loop is instantiated per count NV of this wave's A fragments
     // that hold rows of the group (a partly filled row tile runs only the
