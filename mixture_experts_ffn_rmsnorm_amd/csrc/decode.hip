@@ -834,11 +834,11 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
 // ---------------------------------------------------------------------------
 // One-row gate/up launch: grid = I/8 shared gate/up blocks, then
 // G * I/16 routed gate/up blocks (G = top_k).  The router launch before it
-// has written the logits and xn.  A routed block routes the row itself --
-// wave 0 reads the logits and picks the slots as the head's plan block
-// does, then builds the plan in LDS -- and streams the rows of the plan's
-// u-th expert; the u = 0, x = 0 block also publishes the routing and the
-// plan.  No block waits for another: with one row the routing is a few
+// has written the logits, each expert's selection key and sigmoid, and xn.
+// A routed block routes the row itself -- wave 0 reads the keys and
+// sigmoids and picks the slots with the head plan block's selection, then
+// builds the plan in LDS -- and streams the rows of the plan's u-th expert;
+// the u = 0, x = 0 block also publishes the routing and the plan.  No block waits for another: with one row the routing is a few
 // microseconds of work that every block repeats, against the
 // cross-workgroup round trips of a shared plan.  At full size this is 256 +
 // 6 * 128 blocks, one shared and three routed per compute unit.
