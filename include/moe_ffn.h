@@ -61,7 +61,8 @@ enum {
                                     slot was masked                         */
   MOE_FLAG_SYNC_TIMEOUT = 4u     /* an in-kernel wait for other workgroups
                                     gave up (only if the GPU could not run
-                                    the whole grid); the output is invalid  */
+                                    the whole grid); the output is invalid.
+                                    Only calls of 2 to 4 rows wait at all   */
 };
 
 /* Layer dimensions.  ffn_forward.rs guards the native path with fixed
