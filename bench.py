@@ -351,6 +351,18 @@ def cpu_baseline(cfg, layer, budget_s, log, gpu=None):
             "maxabs_ratio": float(np.abs(out_g - ref_out).max() / max(np.abs(ref_out).max(), 1e-300)),
             "index_match_rows": int(sum(same)),
         }
+        # rows whose K-th and (K+1)-th selection keys (oracle, float64) lie
+        # closer than float32 rounding of the logits could reorder: there an
+        # index mismatch is a legitimate tie, not an error (hash layers select
+        # from the table and have none)
+        gap_tol = 1e-6
+        near = 0
+        if cfg.layer_kind == ref.LAYER_SCORE and cfg.experts > cfg.top_k:
+            keys = ref.sigmoid(res["logits"]) + np.asarray(hi.sel_bias, dtype=np.float64)
+            top = -np.sort(-keys, axis=1)
+            near = int(np.sum(top[:, cfg.top_k - 1] - top[:, cfg.top_k] < gap_tol))
+        base["parity"]["near_tie_rows"] = near
+        base["parity"]["near_tie_gap"] = gap_tol
     return base
 
 
