@@ -59,6 +59,8 @@ def alg_bytes(kernel, cfg, U, R):
         return x + 2 * R * H * 2
     if kernel == "pre_router":       # xn16 + xlo16 in, logits + routing out, router weights once
         return E * H * 2 + 2 * R * H * 2 + R * E * 4 + S * 12
+    if kernel == "pre_sort":         # row masks in; row lists, slot ranks and counts out
+        return E * ((R + 31) // 32) * 4 + S * 4 * 2 + (E + 1) * 4
     if kernel == "gemm_gateup_swiglu":
         return (U + 1) * 2 * I * H * 2 + (S + R) * H * 2 + (S + R) * I * 2
     if kernel == "gemm_down":        # routed experts: h16 in, d16 out

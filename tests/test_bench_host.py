@@ -41,3 +41,36 @@ def test_step_bytes_match_the_paths():
     for U in (6, 23):
         for path in PATHS.values():
             assert abs(_sum(path, cfg, U, 0) - bench.step_bytes(cfg, U, 0)) <= cfg.hidden * 4 + cfg.experts * 4
+
+
+def test_profiled_kernel_names_map_to_launch_names():
+    """rocprofv3 reports demangled template names; each of the library's
+    kernels maps to the launch name the stage timer and bench.py use."""
+    from mixture_experts_ffn_rmsnorm_amd import profiling
+
+    ns = "void moe::(anonymous namespace)::"
+    cases = {
+        "k_dec_head<4096, 2048, false>(moe::FwdArgs)": "dec_head",
+        "k_dec_head<4096, 2048, true>(moe::FwdArgs)": "dec1_router",
+        "k_dec_gateup<4096, 2048>(moe::FwdArgs)": "dec_gateup",
+        "k_dec1_gateup<512, 256>(moe::FwdArgs)": "dec1_gateup",
+        "k_dec_down<4096, 2048, false>(moe::FwdArgs)": "dec_down_reduce",
+        "k_dec_down<512, 256, true>(moe::FwdArgs)": "dec1_down_reduce",
+        "k_pre_norm<4096>(moe::FwdArgs)": "pre_norm",
+        "k_pre_router<4096, 256, 8>(moe::FwdArgs)": "pre_router",
+        "k_pre_sort(moe::FwdArgs)": "pre_sort",
+        "k_gemm<0, 4096, 2048, moe::(anonymous namespace)::GemmCfg<64, 1, 128, 1, 128, 3> >(moe::FwdArgs)":
+            "gemm_gateup_swiglu",
+        "k_gemm<1, 2048, 4096, moe::(anonymous namespace)::GemmCfg<256, 4, 256, 2, 64, 2> >(moe::FwdArgs)":
+            "gemm_down",
+        "k_gemm<2, 2048, 4096, moe::(anonymous namespace)::GemmCfg<256, 4, 256, 2, 64, 2> >(moe::FwdArgs)":
+            "gemm_down_shared_reduce",
+        "k_route(moe::RouteArgs)": "route",
+    }
+    for kernel, name in cases.items():
+        assert profiling.launch_name(ns + kernel) == name, kernel
+    assert profiling.launch_name("__amd_rocclr_copyBuffer") is None
+    # every launch name has an algorithmic byte count in bench.py (route aside)
+    cfg = gen.config(1)
+    for name in set(cases.values()) - {"route"}:
+        assert bench.alg_bytes(name, cfg, 6, 4) is not None, name
