@@ -59,10 +59,21 @@ enum {
                                    all of that row's slots were masked      */
   MOE_FLAG_BAD_TABLE_ENTRY = 2u, /* a table entry outside [0, experts): that
                                     slot was masked                         */
-  MOE_FLAG_SYNC_TIMEOUT = 4u     /* an in-kernel wait for other workgroups
+  MOE_FLAG_SYNC_TIMEOUT = 4u,    /* an in-kernel wait for other workgroups
                                     gave up (only if the GPU could not run
-                                    the whole grid); the output is invalid.
-                                    Only calls of 2 to 4 rows wait at all   */
+                                    the whole grid); the output is invalid
+                                    and the workspace must be zero-filled
+                                    again before its next use.  Only calls
+                                    of 2 to 4 rows wait at all              */
+  MOE_FLAG_F16_RANGE = 8u        /* calls of more than 4 rows only (the
+                                    matrix-core path, whose operands are
+                                    fp16): a router logit, SwiGLU output,
+                                    routed down output or layer output was
+                                    not finite -- an activation or weight
+                                    beyond fp16's range (|v| > 65504), or a
+                                    non-finite input; the output is not
+                                    valid.  Calls of 1 to 4 rows compute in
+                                    f32 and never set it                    */
 };
 
 /* Layer dimensions.  ffn_forward.rs guards the native path with fixed
@@ -132,13 +143,35 @@ int moe_ffn_workspace_bytes(const moe_dims_t* d, int64_t rows, size_t* bytes);
  *   out        device f32 [rows][hidden]  fully overwritten; must not
  *                                          overlap x
  *   workspace  device, >= moe_ffn_workspace_bytes(d, rows), 256-byte
- *              aligned; contents on entry are ignored.  After the call it
- *              holds the routing (see moe_ffn_routing_view) and the status
- *              word (see moe_ffn_status) until the next call that uses it.
+ *              aligned, zero-filled before its first use (e.g. by
+ *              hipMemset); after that every call leaves it valid for the
+ *              next, whatever the row count.  Calls of 2 to 4 rows hand the
+ *              router logits between workgroups in words tagged with a
+ *              nonzero per-call value, and set each word back to 0 once
+ *              consumed, so a word never carries a tag its call did not
+ *              write (graph replays and eager calls may share a workspace
+ *              in any order).  After the call the workspace holds the
+ *              routing (see moe_ffn_routing_view) and the status word (see
+ *              moe_ffn_status) until the next call that uses it.
  * Token ids and table entries are device data, so a bad one is not a host
  * error: the affected slots are masked (they contribute nothing and the
  * row's other weights are renormalised over its valid slots) and a status
  * bit is set.  The result is bitwise reproducible for equal inputs.
+ * Precision (the page keeps every activation in F32):
+ *   rows <= 4  f32 activations, bf16 weights widened exactly, f32 FMA
+ *              accumulation; no range limit beyond f32's.
+ *   rows > 4   the normalised input and the SwiGLU output are rounded to
+ *              fp16 (the router also adds the input's fp16 rounding
+ *              remainder, about 22 significant bits in all), weights
+ *              converted bf16 -> fp16, f32 accumulation on the matrix
+ *              cores; routed down outputs are kept in fp16 until the
+ *              f32 weighted reduce.  Domain: every such operand must stay
+ *              within fp16's range (|v| <= 65504), else the output is not
+ *              finite and MOE_FLAG_F16_RANGE is set; values below 2^-14
+ *              are fp16 subnormals, carried within 2^-25 absolute, so a
+ *              layer whose SwiGLU outputs are mostly that small (weights
+ *              ~100x smaller than the N(0, 0.02) the accuracy is stated
+ *              for) loses relative accuracy on this path. 
  * Errors (host-checked): MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EOVERFLOW,
  * MOE_EWORKSPACE, MOE_EOVERLAP; MOE_EHIP if a launch fails. */
 int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,

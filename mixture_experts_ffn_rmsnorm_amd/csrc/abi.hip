@@ -85,11 +85,10 @@ StageTimer& timer() {
 }
 
 // Host part of the per-call tag of the decode path's tagged words: a
-// process-wide counter seeded from the clock, so a word left in the
-// workspace by an earlier call (or by anything else) does not match the
-// current call.  The kernels add the workspace's device-side call count, so
-// that the replays of a captured graph (whose arguments are fixed) differ
-// as well.
+// process-wide counter seeded from the clock.  Words consumed by a call are
+// set back to 0 on the device, so the tag only has to differ from 0 and from
+// whatever a fresh workspace happens to hold; the kernels add the
+// workspace's device-side call count to it.
 uint32_t next_epoch() {
   static std::atomic<uint32_t> ctr{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
   uint32_t e = ctr.fetch_add(1, std::memory_order_relaxed);
@@ -240,10 +239,7 @@ int moe_ffn_status(const void* workspace, void* stream, uint32_t* flags) {
   hipStream_t s = (hipStream_t)stream;
   if (hipStreamSynchronize(s) != hipSuccess) return MOE_EHIP;
   uint32_t v = 0;
-  uint32_t ep[2];  // DecodeSync: last_epoch, timeout_epoch
   if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_EHIP;
-  if (hipMemcpy(ep, (const char*)workspace + 64, sizeof(ep), hipMemcpyDeviceToHost) != hipSuccess) return MOE_EHIP;
-  if (ep[0] != 0 && ep[1] == ep[0]) v |= MOE_FLAG_SYNC_TIMEOUT;
   *flags = v;
   return MOE_OK;
 }

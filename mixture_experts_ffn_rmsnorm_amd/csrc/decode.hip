@@ -223,9 +223,6 @@ __device__ __forceinline__ void store_wt(float* p, float v) {
 __device__ __forceinline__ float load_wt(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store_flag(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // Every store this thread issued has completed.
 __device__ __forceinline__ void sync_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -528,8 +525,12 @@ __device__ __forceinline__ SlotRoute route_slots_keyed(const uint64_t (&key)[4],
 
 // The call's tag for the decode path's tagged words: the host's per-call
 // value plus the workspace's device-side call count, which the gate/up
-// launch advances -- distinct for every call, also for every replay of a
-// captured graph, whose launch arguments are fixed.  Never 0.
+// launch advances.  Never 0.  Tags of different calls may repeat (the
+// replays of a captured graph keep the host values they were captured
+// with); what makes a word's tag mean "written by this call" is that the
+// plan block of every call sets each word it consumed back to 0 once it has
+// seen the call's tag on it: a later call on the same workspace starts with
+// those words at 0, and only its own router waves tag them again.
 __device__ __forceinline__ uint32_t call_epoch(const FwdArgs& a) {
   const uint32_t e = a.epoch + a.sync->call_seq;
   return e ? e : 1u;
@@ -538,7 +539,9 @@ __device__ __forceinline__ uint32_t call_epoch(const FwdArgs& a) {
 // Routing of the batch into LDS: wave r < R routes row r.  It first reads
 // what the route needs besides the logits (bias, or the token's table row),
 // then polls the row's tagged logits until every one carries the call's
-// epoch (bounded; returns false on timeout).  `plain` (one row, after the
+// epoch (bounded; returns false on timeout), and sets those words back to 0:
+// each is written once per call, by this call's router, so once all of them
+// carry the tag no write to them is pending.  `plain` (one row, after the
 // router launch): it reads the stored keys and sigmoids instead, no waiting.
 __device__ bool route_rows(const FwdArgs& a, uint32_t epoch, bool plain, int* s_idx, float* s_w,
                            unsigned char* s_valid, uint32_t* s_flags) {
@@ -575,7 +578,7 @@ __device__ bool route_rows(const FwdArgs& a, uint32_t epoch, bool plain, int* s_
     if (lane == 0) s_flags[0] = sr.flags;
     return true;
   }
-  const uint64_t* tags = a.sync->logit_tag + wv * E;
+  uint64_t* tags = a.sync->logit_tag + wv * E;
   float lgv[4];
   bool ready = false;
   for (int polls = 0;; ++polls) {
@@ -594,6 +597,11 @@ __device__ bool route_rows(const FwdArgs& a, uint32_t epoch, bool plain, int* s_
     if (ready || polls >= kMaxPolls) break;
     __builtin_amdgcn_s_sleep(1);
   }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + kWave * j;
+    if (e < E) __hip_atomic_store(&tags[e], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   const SlotRoute sr =
       route_slots(lgv[0], lgv[1], lgv[2], lgv[3], bias[0], bias[1], bias[2], bias[3], E, K, hash, tok_ok, ent);
   if (lane < K) {
@@ -607,9 +615,9 @@ __device__ bool route_rows(const FwdArgs& a, uint32_t epoch, bool plain, int* s_
 
 // Writes the block's routing (indices, weights, row flags, status word) and
 // the plan (from LDS) to the workspace for the later launches and the
-// caller, and clears the down launch's tile counters.  `epoch` is the call's
-// tag (0 for a call whose kernels never wait), `ok` false if a wait gave up.
-__device__ void publish_routing(const FwdArgs& a, uint32_t epoch, bool ok, const int* s_idx, const float* s_w,
+// caller, and clears the down launch's tile counters.  `ok` false if a wait
+// gave up (MOE_FLAG_SYNC_TIMEOUT in the status word).
+__device__ void publish_routing(const FwdArgs& a, bool ok, const int* s_idx, const float* s_w,
                                 const uint32_t* s_flags, const DecodePlan* P) {
   const int R = a.R;
   DecodeSync* sy = a.sync;
@@ -619,11 +627,9 @@ __device__ void publish_routing(const FwdArgs& a, uint32_t epoch, bool ok, const
   }
   if ((int)threadIdx.x < R) a.rowflags[threadIdx.x] = s_flags[threadIdx.x];
   if (threadIdx.x == 0) {
-    uint32_t f = 0;
+    uint32_t f = ok ? 0u : (uint32_t)MOE_FLAG_SYNC_TIMEOUT;
     for (int r = 0; r < R; ++r) f |= s_flags[r];
     a.status[0] = f;
-    sy->last_epoch = epoch;
-    if (!ok) store_flag(&sy->timeout_epoch, epoch);
   }
   for (int i = threadIdx.x; i < kDecodeMaxTiles; i += kThreads) sy->tile_cnt[i] = 0;
   const int* ps = (const int*)P;
@@ -701,11 +707,10 @@ __device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs
 //   and the plan's latency).  The norm comes before the block requests its
 //   weights, which lets the router's weight rows reach the memory queues
 //   first.  The first of these blocks publishes xn.
-//   Plan block: routes the batch (wave r polls row r's tagged logits),
-//   publishes indices, weights, row flags, status and the plan, and clears
-//   the down kernel's tile counters.  A wait that gives up records the
-//   call's epoch in timeout_epoch (reported as MOE_FLAG_SYNC_TIMEOUT by
-//   moe_ffn_status).
+//   Plan block: routes the batch (wave r polls row r's tagged logits and
+//   then zeroes them), publishes indices, weights, row flags, status and the
+//   plan, and clears the down kernel's tile counters.  A wait that gives up
+//   sets MOE_FLAG_SYNC_TIMEOUT in the status word.
 template <int H, int I, bool kRouterOnly>
 __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [R][H]
@@ -729,7 +734,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
     const bool ok = s_ok;
     if (wv == 0) build_plan(s_idx, s_w, s_valid, R, K, E, &P);
     __syncthreads();
-    publish_routing(a, epoch, ok, s_idx, s_w, s_flags, &P);
+    publish_routing(a, ok, s_idx, s_w, s_flags, &P);
     return;
   }
   if (!kRouterOnly && b >= nrb) {  // shared gate/up block
@@ -865,7 +870,7 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
   __syncthreads();
   if (threadIdx.x < kWave) build_plan(s_idx, s_w, s_valid, 1, a.K, a.E, &P);
   __syncthreads();
-  if (u == 0 && x == 0) publish_routing(a, 0u, true, s_idx, s_w, s_flags, &P);
+  if (u == 0 && x == 0) publish_routing(a, true, s_idx, s_w, s_flags, &P);
   if (u >= plan_ngroups(&P)) return;
   const PlanGroup g = plan_group(&P, u, a.E);
   const int nr = g.nr < a.R ? g.nr : a.R;  // LDS holds a.R rows
@@ -946,7 +951,9 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   if (t >= R * kDnRows) return;
   const int r = t / kDnRows;
   const int h = x + (t % kDnRows) * dnt;
-  const float sh = a.d32[(int64_t)(kDecodeMaxSlots + r) * H + h];
+  // written through by other blocks of this launch when kShared (the shared
+  // half-blocks), so read past any stale cache line like the partials below
+  const float sh = load_wt(&a.d32[(int64_t)(kDecodeMaxSlots + r) * H + h]);
   float o = 0.f;
   if (ng > 0 && ne > 0) {
     // every entry's partial is requested at once (one memory round trip; the

@@ -37,17 +37,16 @@ struct DecodePlan {
 };
 
 // Cross-workgroup signalling words of the decode path, after the status word.
-// A tagged word carries the call's epoch in its upper half and a 32-bit
-// value in its lower half, written and read whole, so its reader polls the
-// data itself; counters are zeroed by the first kernel of the call for the
-// later ones.
+// A tagged word carries the call's tag in its upper half and a 32-bit value
+// in its lower half, written and read whole, so its reader polls the data
+// itself; the reader sets every word it consumed back to 0 (no tag is 0), so
+// no completed call leaves a tagged word behind for a later one.  Counters
+// are zeroed by the first kernel of the call for the later ones.
 constexpr int kDecodeMaxTiles = 256;  // down column tiles (hidden/32) and shared gate/up tiles (inter/8)
 struct DecodeSync {
-  uint32_t last_epoch;                   // epoch of the last decode call (0 after a prefill call)
-  uint32_t timeout_epoch;                // epoch of a call in which an in-kernel wait gave up
-  uint32_t call_seq;                     // decode calls made on this workspace (device side)
-  uint32_t pad[13];
-  uint64_t logit_tag[kDecodeMaxRows * kMaxExperts];  // router wave -> plan block: epoch | f32 logit bits
+  uint32_t call_seq;                     // two- to four-row calls made on this workspace (device side)
+  uint32_t pad[15];
+  uint64_t logit_tag[kDecodeMaxRows * kMaxExperts];  // router wave -> plan block: tag | f32 logit bits
   // one-row path: each expert's ordered selection key and float64 sigmoid,
   // written by the router launch for the gate/up blocks that route
   uint64_t route_key[kMaxExperts];

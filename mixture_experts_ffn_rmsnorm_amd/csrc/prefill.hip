@@ -22,9 +22,12 @@
 //
 // Matrix-core precision: weights are bf16; activations (xn, and the SwiGLU
 // output h) are rounded to fp16 and multiplied by the bf16 weights converted
-// to fp16 (exact for |w| >= 2^-14, nearly so below), accumulating in f32 on
-// v_mfma_f32_32x32x16_f16.  fp16 keeps 3 more mantissa bits than bf16 at the
-// same matrix-core rate.
+// to fp16 (exact for 2^-14 <= |w| <= 65504, within 2^-25 below), accumulating
+// in f32 on v_mfma_f32_32x32x16_f16.  fp16 keeps 3 more mantissa bits than
+// bf16 at the same matrix-core rate, at the price of its range: an operand
+// beyond 65504 in magnitude becomes infinite, and the router (non-finite
+// logit) or a GEMM epilogue (non-finite h, routed down output or layer
+// output) then sets MOE_FLAG_F16_RANGE in the status word.
 #include <type_traits>
 
 #include "device.h"
@@ -35,14 +38,23 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t f32x2_to_f16x2(float a, float b) {
+  // one v_cvt_pk_f16_f32: round to nearest even, so a magnitude beyond
+  // fp16's range becomes infinite (and is reported) instead of clamped
+  const half2v h = __builtin_convertvector((float2v){a, b}, half2v);
+  return *(const uint32_t*)&h;
+}
+
 __device__ __forceinline__ uint2 bf16x4_to_f16x4(uint32_t lo, uint32_t hi) {
-  // bf16 -> f32 -> f16 (round toward zero; exact whenever the value is an
-  // fp16 normal, since bf16 carries fewer mantissa bits)
-  auto p0 = __builtin_amdgcn_cvt_pkrtz(bf16lo(lo), bf16hi(lo));
-  auto p1 = __builtin_amdgcn_cvt_pkrtz(bf16lo(hi), bf16hi(hi));
+  // bf16 -> f32 -> f16: exact for every bf16 value in fp16's normal range
+  // (bf16 carries fewer mantissa bits), within 2^-25 below it (subnormal),
+  // infinite above 65504
   uint2 r;
-  r.x = *(uint32_t*)&p0;
-  r.y = *(uint32_t*)&p1;
+  r.x = f32x2_to_f16x2(bf16lo(lo), bf16hi(lo));
+  r.y = f32x2_to_f16x2(bf16lo(hi), bf16hi(hi));
   return r;
 }
 
@@ -64,11 +76,17 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 // 16 bytes per lane from global memory into LDS, lanes filling consecutive
 // 16-byte slots from the wave-uniform LDS byte address `lds`.  Completion is
 // counted by vmcnt like any vector load.
+// m0 is a reserved register the compiler may assume unchanged; none of the
+// code generated for these kernels reads or writes it other than here (the
+// kernels' assembly holds no other m0 access), so clobbering it is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt vmcnt(N) with the other counters left alone
 template <int N>
@@ -448,10 +466,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
     __syncthreads();
   }
 
-  // 3. keys; routing
+  // 3. keys; routing.  A non-finite logit (an fp16 operand beyond range,
+  //    or a non-finite input) is reported in the status word.
   const bool score = a.layer_kind != MOE_LAYER_HASH;
-  if (score) {
-    for (int q = t; q < nrows * E; q += kThreads) s_key[q] = score_key(s_logit[q], a.bias[q % E]);
+  {
+    bool bad = false;
+    for (int q = t; q < nrows * E; q += kThreads) {
+      const float l = s_logit[q];
+      bad |= !__builtin_isfinite(l);
+      if (score) s_key[q] = score_key(l, a.bias[q % E]);
+    }
+    if (bad) atomicOr(&s_flags, (uint32_t)MOE_FLAG_F16_RANGE);
     __syncthreads();
   }
   // one row per 8 consecutive lanes: all 32 rows at once
@@ -499,7 +524,6 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
       uint32_t tot = 0;
       for (int w = 0; w < kThreads / kWave; ++w) tot |= (uint32_t)s_wsum[w];
       a.status[0] = tot;
-      a.sync->last_epoch = 0;  // no decode-path wait in this call
       a.cnt[E] = (int)R;
     }
     return;
@@ -767,6 +791,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
   constexpr bool kPre = MODE != 2 && kStages == 3 && kSlab * CPITCH * 4 <= ST;
   int off = 0;   // ring offset of the current tile
   int npre = 0;  // its first k-tiles the previous tile requested (0 or 2)
+  bool range_bad = false;  // a non-finite value written by this thread's epilogues
   int tile = first;
   if (tile >= nstatic) {
     if (t == 0) s_next = nstatic < total ? grab() : total;
@@ -1049,6 +1074,8 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) h[u] = (_Float16)sv[u];
           }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) range_bad |= !__builtin_isfinite((float)h[u]);
           _Float16* dst = MODE == 0 ? a.h16 : a.d16;
           *(half8*)(dst + (int64_t)(s_rbase[g] + m) * ND + n0 + cc) = h;
         } else {
@@ -1076,6 +1103,9 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
           float4 o0, o1;
           o0.x = o[0] + sh[0]; o0.y = o[1] + sh[1]; o0.z = o[2] + sh[2]; o0.w = o[3] + sh[3];
           o1.x = o[4] + sh[4]; o1.y = o[5] + sh[5]; o1.z = o[6] + sh[6]; o1.w = o[7] + sh[7];
+          range_bad |= !(__builtin_isfinite(o0.x) && __builtin_isfinite(o0.y) && __builtin_isfinite(o0.z) &&
+                         __builtin_isfinite(o0.w) && __builtin_isfinite(o1.x) && __builtin_isfinite(o1.y) &&
+                         __builtin_isfinite(o1.z) && __builtin_isfinite(o1.w));
           float* dst = a.out + (int64_t)m * ND + n0 + cc;
           *(float4*)dst = o0;
           *(float4*)(dst + 4) = o1;
@@ -1090,6 +1120,8 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     __syncthreads();  // staging and s_pos are rewritten by the next tile
     tile = s_next;
   }
+  // the sort has written the status word; this launch only adds to it
+  if (range_bad) atomicOr(a.status, (uint32_t)MOE_FLAG_F16_RANGE);
 }
 
 // ===========================================================================

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoeffn.s
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EOVERFLOW, MOE_EWORKSPACE, MOE_EHIP, MOE_EOVERLAP = range(7)
 LAYER_SCORE, LAYER_HASH = 0, 1
-FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY = 1, 2
+FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY, FLAG_SYNC_TIMEOUT, FLAG_F16_RANGE = 1, 2, 4, 8
 
 # Function names the header declares (checked against the library's exports).
 EXPORTS = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_route", "moe_ffn_routing_view", "moe_ffn_status",
@@ -112,9 +112,10 @@ def workspace_bytes(dims: Dims, rows: int) -> int:
 
 
 def alloc_workspace(dims: Dims, rows: int, device="cuda"):
+    """A zero-filled workspace (the ABI asks for zeros before first use)."""
     import torch
 
-    return torch.empty(workspace_bytes(dims, rows), dtype=torch.uint8, device=device)
+    return torch.zeros(workspace_bytes(dims, rows), dtype=torch.uint8, device=device)
 
 
 def forward(dims: Dims, x, token_ids, layer_kind: int, weights: WeightsC, out, workspace, stream=None):
