@@ -46,8 +46,15 @@ enum moe_status {
   MOE_EOVERFLOW = 3,    /* rows * top_k (or a buffer size) overflows         */
   MOE_EWORKSPACE = 4,   /* workspace NULL, misaligned or too small           */
   MOE_EHIP = 5,         /* a HIP launch or runtime call failed               */
-  MOE_EOVERLAP = 6      /* x and out overlap                                 */
+  MOE_EOVERLAP = 6,     /* x and out overlap                                 */
+  MOE_ESCRATCH = 7      /* moe_ffn_forward_noalloc: the call needs more
+                           intermediate memory than its built-in scratch of
+                           MOE_NOALLOC_SCRATCH_BYTES holds                 */
 };
+
+/* Size of the device array that holds moe_ffn_forward_noalloc's
+ * intermediates, one per GPU the library runs on (64 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ull << 20)
 
 /* ---- layer kinds (ffn_forward.rs: the hash table is bound for layers below
  * hash_layer_count, the selection bias for the layers after them) -------- */
@@ -177,6 +184,34 @@ int moe_ffn_workspace_bytes(const moe_dims_t* d, int64_t rows, size_t* bytes);
 int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,
                     int layer_kind, const moe_weights_t* w, float* out, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* moe_ffn_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, kernels and
+ * results as moe_ffn_forward (bitwise), except that the intermediates live
+ * in a library-owned device array of MOE_NOALLOC_SCRATCH_BYTES per GPU
+ * (a file-scope device variable, held until the process ends), so the
+ * call allocates and frees nothing.
+ *   Limit: a call whose moe_ffn_workspace_bytes exceeds the array is
+ *   rejected with MOE_ESCRATCH before any HIP call -- at the full shape
+ *   (hidden 4096, 256 experts, inter 2048) that is more than 696 rows, at
+ *   the tiny shape more than 5539 rows; decode calls (1 to 4 rows) always
+ *   fit.
+ *   Sharing: every call on one GPU uses that GPU's array, which keeps the
+ *   last call's contents.  Calls on one stream (or otherwise ordered) are
+ *   fine in any mix with moe_ffn_forward; calls that overlap in time on one
+ *   GPU race and give wrong results.
+ *   Set-up: the first call on each GPU looks up the array's device address
+ *   (hipGetSymbolAddress, with that GPU current); until one call has run
+ *   outside stream capture, a call also enqueues a small kernel that zeroes
+ *   the array's handoff words before the forward (inside a capture it
+ *   becomes part of the graph, harmless on every replay).
+ *   The status word and routing of these calls are not exposed (there is no
+ *   workspace pointer to read them from).
+ * Errors: those of moe_ffn_forward except MOE_EWORKSPACE, plus
+ * MOE_ESCRATCH; MOE_EHIP if the set-up or a launch fails. */
+int moe_ffn_forward_noalloc(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,
+                            int layer_kind, const moe_weights_t* w, float* out, void* stream);
 
 /* Routing alone, from caller-given logits (ffn_forward.rs: the score-route
  * and hash-route dispatches that turn the F32 logits into I32 indices and

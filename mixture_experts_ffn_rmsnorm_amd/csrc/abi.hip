@@ -130,20 +130,32 @@ int moe_ffn_workspace_bytes(const moe_dims_t* d, int64_t rows, size_t* bytes) {
   return MOE_OK;
 }
 
-int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
-                    const moe_weights_t* w, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+// Host checks of a forward call that need no workspace: dims, rows,
+// pointers, layer kind, overlap of x and out.  Fills *L with the workspace
+// layout for `rows`.
+int check_forward_args(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
+                       const moe_weights_t* w, const float* out, Layout* L) {
   int rc = check_dims_rows(d, rows);
   if (rc) return rc;
   if (!x || !out || !aligned(x, 16) || !aligned(out, 16)) return MOE_EINVAL;
   rc = check_weights(d, layer_kind, w, token_ids, true);
   if (rc) return rc;
-  Layout L;
-  if (!make_layout(rows, d->hidden, d->experts, d->top_k, d->inter, &L)) return MOE_EOVERFLOW;
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
+  if (!make_layout(rows, d->hidden, d->experts, d->top_k, d->inter, L)) return MOE_EOVERFLOW;
   const size_t nbytes = (size_t)rows * d->hidden * sizeof(float);
   const uintptr_t xb = (uintptr_t)x, ob = (uintptr_t)out;
   if (xb < ob + nbytes && ob < xb + nbytes) return MOE_EOVERLAP;
+  return MOE_OK;
+}
 
+// The forward with its intermediates carved from `workspace` (already
+// checked: at least L.total bytes, 256-byte aligned).
+int forward_in(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
+               const moe_weights_t* w, float* out, void* workspace, const Layout& L, void* stream) {
   char* ws = (char*)workspace;
   FwdArgs a;
   memset(&a, 0, sizeof(a));
@@ -196,6 +208,95 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
   hipStream_t s = (hipStream_t)stream;
   hipError_t err = decode ? run_decode(a, s) : run_prefill(a, s);
   return err == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// ---- the allocation-free entry point's scratch ---------------------------
+// The intermediates of moe_ffn_forward_noalloc live in this array, one copy
+// per GPU (each device that loads the library's code holds its own, until
+// the process ends).  In host code `scratch` names a host-side stand-in, not
+// the device array: its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// ever passed to a kernel.
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  void* ptr = nullptr;   // device address of this device's `scratch`
+  bool zeroed = false;   // its handoff words were zeroed by a call that ran (not only captured)
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxDevices];
+
+__global__ void k_zero_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// Device address of the scratch on the device `stream` belongs to.  Until
+// a call on that device has run outside stream capture, the call first
+// enqueues a fill kernel that zeroes the status block (the decode path's
+// handoff words must start at 0); inside a capture the fill becomes part of
+// the graph and runs before the forward on every replay, which is harmless.
+int scratch_for(hipStream_t stream, size_t zero_bytes, void** out) {
+  int dev = 0, cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return MOE_EHIP;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return MOE_EHIP;
+  } else {
+    dev = cur;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchSlot& sl = g_scratch[dev];
+  if (!sl.ptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return MOE_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p || !aligned(p, 256)) return MOE_EHIP;
+    sl.ptr = p;
+  }
+  if (!sl.zeroed) {
+    const int n = (int)(zero_bytes / 4);
+    void* argv[2];
+    uint32_t* wp = (uint32_t*)sl.ptr;
+    int nn = n;
+    argv[0] = &wp;
+    argv[1] = &nn;
+    if (hipLaunchKernel((const void*)k_zero_words, dim3((n + 255) / 256), dim3(256), argv, 0, stream) != hipSuccess)
+      return MOE_EHIP;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return MOE_EHIP;
+    if (cs == hipStreamCaptureStatusNone) sl.zeroed = true;
+  }
+  *out = sl.ptr;
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
+                    const moe_weights_t* w, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  Layout L;
+  const int rc = check_forward_args(d, x, token_ids, rows, layer_kind, w, out, &L);
+  if (rc) return rc;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
+  return forward_in(d, x, token_ids, rows, layer_kind, w, out, workspace, L, stream);
+}
+
+int moe_ffn_forward_noalloc(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,
+                            int layer_kind, const moe_weights_t* w, float* out, void* stream) {
+  Layout L;
+  int rc = check_forward_args(d, x, token_ids, rows, layer_kind, w, out, &L);
+  if (rc) return rc;
+  if (L.total > kScratchBytes) return MOE_ESCRATCH;
+  void* ws = nullptr;
+  rc = scratch_for((hipStream_t)stream, L.logits, &ws);  // the status block precedes the logits
+  if (rc) return rc;
+  return forward_in(d, x, token_ids, rows, layer_kind, w, out, ws, L, stream);
 }
 
 int moe_route(const moe_dims_t* d, const float* logits, const int32_t* token_ids, int64_t rows, int layer_kind,
@@ -253,6 +354,7 @@ const char* moe_strerror(int code) {
     case MOE_EWORKSPACE: return "workspace missing, misaligned or too small";
     case MOE_EHIP: return "HIP launch or runtime error";
     case MOE_EOVERLAP: return "x and out overlap";
+    case MOE_ESCRATCH: return "rows need more intermediate memory than the allocation-free entry point's scratch holds";
     default: return "unknown status";
   }
 }

@@ -13,13 +13,15 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoeffn.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EOVERFLOW, MOE_EWORKSPACE, MOE_EHIP, MOE_EOVERLAP = range(7)
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EOVERFLOW, MOE_EWORKSPACE, MOE_EHIP, MOE_EOVERLAP, MOE_ESCRATCH = range(8)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 LAYER_SCORE, LAYER_HASH = 0, 1
 FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY, FLAG_SYNC_TIMEOUT, FLAG_F16_RANGE = 1, 2, 4, 8
 
 # Function names the header declares (checked against the library's exports).
-EXPORTS = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_route", "moe_ffn_routing_view", "moe_ffn_status",
-           "moe_strerror", "moe_ffn_stage_timing_begin", "moe_ffn_stage_timing_end")
+EXPORTS = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_route",
+           "moe_ffn_routing_view", "moe_ffn_status", "moe_strerror", "moe_ffn_stage_timing_begin",
+           "moe_ffn_stage_timing_end")
 
 
 class MoeError(RuntimeError):
@@ -53,6 +55,7 @@ def lib() -> ctypes.CDLL:
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         L.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(Dims), I64, ctypes.POINTER(SZ)]
         L.moe_ffn_forward.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, SZ, P]
+        L.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P]
         L.moe_route.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, P]
         L.moe_ffn_routing_view.argtypes = [ctypes.POINTER(Dims), I64, P, SZ, ctypes.POINTER(P), ctypes.POINTER(P),
                                            ctypes.POINTER(P)]
@@ -124,6 +127,15 @@ def forward(dims: Dims, x, token_ids, layer_kind: int, weights: WeightsC, out, w
     rc = lib().moe_ffn_forward(ctypes.byref(dims), _ptr(x), _ptr(token_ids), rows, int(layer_kind),
                                ctypes.byref(weights), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "moe_ffn_forward")
+    return out
+
+
+def forward_noalloc(dims: Dims, x, token_ids, layer_kind: int, weights: WeightsC, out, stream=None):
+    """``forward`` with the library's built-in per-GPU scratch instead of a
+    workspace (allocates nothing); enqueue only."""
+    rc = lib().moe_ffn_forward_noalloc(ctypes.byref(dims), _ptr(x), _ptr(token_ids), x.shape[0], int(layer_kind),
+                                       ctypes.byref(weights), _ptr(out), _stream(stream))
+    _check(rc, "moe_ffn_forward_noalloc")
     return out
 
 

@@ -214,7 +214,7 @@ def test_status_and_timer_host_paths():
 
 
 def test_strerror():
-    for c in range(7):
+    for c in range(8):
         assert moe.strerror(c) and moe.strerror(c) != "unknown status"
     assert moe.strerror(99) == "unknown status"
 
@@ -239,3 +239,33 @@ def test_peaks_library_exports_and_rejects_bad_arguments():
     assert L.moe_peaks_mfma(0, 16, sink, None) == invalid
     assert L.moe_peaks_mfma(16, 0, sink, None) == invalid
     assert L.moe_peaks_mfma(16, 16, None, None) == invalid
+
+
+def _noalloc(dims, x=FAKE, tok=FAKE, rows=4, kind=moe.LAYER_SCORE, w=None, out=FAKE + (1 << 30)):
+    w = _weights() if w is None else w
+    d = None if dims is None else ctypes.byref(dims)
+    return moe.lib().moe_ffn_forward_noalloc(d, x, tok, rows, kind, ctypes.byref(w), out, None)
+
+
+def test_noalloc_rejects_on_host():
+    """The allocation-free entry point checks its arguments like
+    moe_ffn_forward, and a call whose intermediates exceed the built-in
+    scratch is rejected with MOE_ESCRATCH -- all before any HIP call."""
+    d = moe.make_dims(**FULL, table_rows=131072)
+    assert _noalloc(None) == moe.MOE_EINVAL
+    assert _noalloc(d, rows=0) == moe.MOE_EINVAL
+    assert _noalloc(d, x=None) == moe.MOE_EINVAL
+    assert _noalloc(d, out=None) == moe.MOE_EINVAL
+    assert _noalloc(d, kind=5) == moe.MOE_EINVAL
+    assert _noalloc(d, kind=moe.LAYER_HASH, tok=None) == moe.MOE_EINVAL
+    assert _noalloc(moe.make_dims(4096, 128, 6, 2048)) == moe.MOE_EUNSUPPORTED
+    assert _noalloc(d, rows=(1 << 24) + 1) == moe.MOE_EOVERFLOW
+    assert _noalloc(d, rows=8, out=FAKE + 64) == moe.MOE_EOVERLAP
+    # the size limit: 696 full-shape rows fit in 64 MiB, 697 do not
+    assert moe.workspace_bytes(d, 696) <= moe.NOALLOC_SCRATCH_BYTES < moe.workspace_bytes(d, 697)
+    assert _noalloc(d, rows=697) == moe.MOE_ESCRATCH
+    assert _noalloc(d, rows=8192) == moe.MOE_ESCRATCH
+    t = moe.make_dims(**TINY)
+    assert moe.workspace_bytes(t, 5539) <= moe.NOALLOC_SCRATCH_BYTES < moe.workspace_bytes(t, 5540)
+    assert _noalloc(t, rows=5540) == moe.MOE_ESCRATCH
+    assert "scratch" in moe.strerror(moe.MOE_ESCRATCH)
