@@ -1,16 +1,24 @@
 #!/usr/bin/env python3
 """Throughput of the routed MoE FFN layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers L]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--only] [--layers L] [--graph]
 
 A step is one moe_ffn_forward call (RMSNorm, router, routing, sort, gate/up +
 SwiGLU, down, weighted reduce + shared expert) over one batch of synthetic
 rows with every input already in HBM.  Steps cycle over L independently drawn
-layers of weights so that a step never finds the previous step's experts in
-the 256 MB Infinity Cache.  Kernel durations come from HIP start/stop events
-the library records at each kernel's own start and end during the timed
-steps; the dominant kernel is reported against the MI355X roofline.  The
-float64 CPU oracle is timed on a bounded sample beside it.
+layers of weights (4 for decode, 1 for prefill) on one workspace, so that a
+decode step never finds the previous step's experts in the 256 MB Infinity
+Cache.  Kernel durations come from HIP start/stop events the library records
+at each kernel's own start and end; the dominant kernel is reported against
+the MI355X roofline.
+
+The headline (`value`, `roofline`, ...) is the named workload, by default the
+one-row score-routed decode.  Unless --only is given, the same JSON line also
+carries `workloads`: one record per other full-size workload (the 4-row hash
+cohort, 512-row prefill, 8192-row skewed prefill) with its rows/s, dominant
+kernel roofline, step fractions and per-kernel timings, and its float64
+oracle run over the whole batch with the GPU's agreement on every row.  The
+headline's `cpu_baseline` times the oracle on a bounded sample beside it.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -96,95 +104,91 @@ def step_bytes(cfg, U, R):
     return (U + 1) * EXPERT_BYTES(H, I) + E * H * 2 + 2 * R * H * 4 + H * 4 + E * 4
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode-r1-score")
-    ap.add_argument("--layers", type=int, default=None, help="distinct weight sets cycled (default 4 decode, 1 prefill)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline sample")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-peaks", action="store_true",
-                    help="skip the device-ceiling microbenchmarks (HBM read, fp16 MFMA) reported as measured_peaks")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the L layers chained (each layer's output the next one's input) "
-                         "as one captured HIP graph, replayed --steps times; reported under 'graph'")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1).", file=sys.stderr)
-        sys.exit(2)
+SUB_WORKLOADS = ("decode-cohort-r4-hash", "prefill-r512-score", "prefill-r8192-score-skewed")
 
+
+def draw_layers(cfg, L):
+    """Device expert weights of L independently drawn layers (the full-size
+    workloads share one parameter seed, so one set serves all of them)."""
+    from mixture_experts_ffn_rmsnorm_amd import inputs as gen
+
+    out = []
+    for l in range(L):
+        out.append(gen.expert_weights_device(cfg, "cuda", layer=l))
+        log(f"layer {l} weights ready")
+    return out
+
+
+def bind_layers(cfg, big, L):
+    """Per workload: small per-layer parameters (router, bias with the hot
+    experts, norm weight, table) on the device, bound with the big weights."""
     import numpy as np
     import torch
 
     from mixture_experts_ffn_rmsnorm_amd import inputs as gen
     from mixture_experts_ffn_rmsnorm_amd import moe
 
-    moe.lib()  # fail loudly if the HIP library is missing
-    cfg = gen.config(args.workload)
-    R = cfg.rows
-    decode = R <= 4
-    L = args.layers or (4 if decode else 1)
-    log(f"workload {cfg.name}: rows={R} layers={L}; drawing weights on the GPU")
-    torch.cuda.set_device(0)
-    dims = moe.dims_of(cfg)
     layers = []
     for l in range(L):
         hi = gen.host_inputs(cfg, layer=l)
-        (g, u, d), (gs, us, ds) = gen.expert_weights_device(cfg, "cuda", layer=l)
+        (g, u, d), (gs, us, ds) = big[l]
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         keep = [t(hi.norm_w), t(hi.router.view(np.int16)).view(torch.bfloat16), t(hi.sel_bias),
                 t(hi.tid2eid) if hi.tid2eid is not None else None, g, u, d, gs, us, ds]
         layers.append((hi, keep, moe.make_weights(*keep)))
-        log(f"layer {l} ready")
+    return layers
+
+
+def time_workload(cfg, layers, steps, warmup, graph=False):
+    """One workload on the device: throughput, per-kernel event timings and
+    their rooflines, latency, and layer 0's output for the parity check."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_ffn_rmsnorm_amd import moe
+
+    R = cfg.rows
+    L = len(layers)
+    dims = moe.dims_of(cfg)
     hi0 = layers[0][0]
     x = torch.from_numpy(hi0.x).cuda()
     tok = torch.from_numpy(hi0.token_ids).cuda()
     out = torch.empty_like(x)
-    ws = [moe.alloc_workspace(dims, R) for _ in range(L)]
+    ws = moe.alloc_workspace(dims, R)  # one workspace for every layer, as a model runs them
     torch.cuda.synchronize()
 
     def step(i):
-        l = i % L
-        moe.forward(dims, x, tok, cfg.layer_kind, layers[l][2], out, ws[l])
+        moe.forward(dims, x, tok, cfg.layer_kind, layers[i % L][2], out, ws)
 
-    log(f"warmup {args.warmup}")
-    for i in range(args.warmup):
+    log(f"{cfg.name}: warmup {warmup}")
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # distinct routed experts of each layer's step, from its routing
-    U = []
+    U = []  # distinct routed experts of each layer's step, from its routing
     for l in range(L):
         step(l)
         torch.cuda.synchronize()
-        idx = moe.routing_view(dims, R, ws[l])[1].cpu().numpy()
+        idx = moe.routing_view(dims, R, ws)[1].cpu().numpy()
         U.append(len(np.unique(idx[(idx >= 0) & (idx < cfg.experts)])))
-    log(f"distinct routed experts per layer: {U}")
-
-    # throughput pass: the timed region, plain launches
-    log(f"timing {args.steps} steps")
+    log(f"{cfg.name}: distinct routed experts per layer {U}; timing {steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    value = R / (ms_per_step / 1e3)
-    u_mean = float(np.mean([U[i % L] for i in range(args.steps)]))
-    # kernel pass: the same steps again, each kernel bracketed by HIP
-    # start/stop events taken at the kernel's own start and end
-    log("timing kernels")
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    u_mean = float(np.mean([U[i % L] for i in range(steps)]))
+    # kernel pass: each kernel bracketed by HIP events taken at its own start
+    # and end, on the stream it runs on
     moe.stage_timing_begin()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     stages = moe.stage_timing_end()
-    # latency pass: each step bracketed by events on the stream the kernels use
+    # latency pass: each step between events on the launch stream
     lat = []
-    for i in range(args.steps):
+    for i in range(steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         step(i)
@@ -200,7 +204,6 @@ def main():
     avg_s = stages[dom][0] / stages[dom][1] / 1e3
     flops = alg_flops(dom, cfg, R)
     b = alg_bytes(dom, cfg, u_mean, R)
-    # the kernel's roofline: whichever of HBM and the matrix cores bounds it
     if flops is not None and flops / (MFMA_F16_PEAK_TFLOPS * 1e12) > b / (HBM_PEAK_GBPS * 1e9):
         ach = flops / avg_s / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -223,37 +226,92 @@ def main():
             k["hbm_frac"] = kb / secs / 1e9 / HBM_PEAK_GBPS
         if kf is not None:
             k["mfma_frac"] = kf / secs / 1e12 / MFMA_F16_PEAK_TFLOPS
-    sb = step_bytes(cfg, u_mean, R)
-    sf = step_flops(cfg, R)
-    # one call of layer 0 for the parity sample and the status word
-    step(0)
-    torch.cuda.synchronize()
-    per = min(R, 4)
-    gpu0 = (out[:per].cpu().numpy().copy(), moe.routing_view(dims, R, ws[0])[1][:per].cpu().numpy().copy())
-    status_flags = moe.status(ws[0])
-    res = {
-        "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if decode else "f16", "data": "synthetic",
-        "config": {"workload": cfg.name, "rows": R, "hidden": cfg.hidden, "experts": cfg.experts,
-                   "top_k": cfg.top_k, "inter": cfg.inter, "shared_experts": 1,
-                   "layer_kind": "hash" if cfg.layer_kind == 1 else "score", "layers_cycled": L,
-                   "distinct_routed_experts": u_mean},
-        "roofline": roof,
+    sb, sf = step_bytes(cfg, u_mean, R), step_flops(cfg, R)
+    step_s = ms_per_step / 1e3
+    rec = {
+        "rows": R, "rows_per_s": R / step_s, "ms_per_step": ms_per_step, "layers_cycled": L,
+        "distinct_routed_experts": u_mean,
         "latency_us": {"median": float(np.median(lat_us)), "p10": float(np.percentile(lat_us, 10)),
                        "p90": float(np.percentile(lat_us, 90))},
-        "step_alg_bytes": sb,
-        "step_hbm_GBps": sb / (ms_per_step / 1e3) / 1e9,
-        "step_hbm_frac": sb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS,
-        "step_alg_flops": sf,
-        "step_TFLOPs": sf / (ms_per_step / 1e3) / 1e12,
-        "step_mfma_frac": sf / (ms_per_step / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-        "status_flags": status_flags,
-        "kernels": kernels,
+        "step_alg_bytes": sb, "step_hbm_GBps": sb / step_s / 1e9, "step_hbm_frac": sb / step_s / 1e9 / HBM_PEAK_GBPS,
+        "step_alg_flops": sf, "step_TFLOPs": sf / step_s / 1e12,
+        "step_mfma_frac": sf / step_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "roofline": roof, "kernels": kernels,
     }
+    if graph:
+        rec["graph"] = graph_chain(dims, cfg, layers, x, tok, ws, steps, ms_per_step)
+    # one call of layer 0 for the parity check and the status word
+    moe.forward(dims, x, tok, cfg.layer_kind, layers[0][2], out, ws)
+    torch.cuda.synchronize()
+    rec["status_flags"] = moe.status(ws)
+    gpu0 = (out.cpu().numpy(), moe.routing_view(dims, R, ws)[1].cpu().numpy())
+    del x, tok, out, ws
+    return rec, gpu0
 
-    if args.graph:
-        res["graph"] = graph_chain(dims, cfg, layers, x, tok, ws, args.steps, log)
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode-r1-score")
+    ap.add_argument("--only", action="store_true",
+                    help="time the named workload alone (no sub-records of the other full-size workloads)")
+    ap.add_argument("--layers", type=int, default=None, help="distinct weight sets cycled (default 4 decode, 1 prefill)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the headline's oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the device-ceiling microbenchmarks (HBM read, fp16 MFMA) reported as measured_peaks")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the L decode layers chained (each layer's output the next one's input) on one "
+                         "workspace as one captured HIP graph against the same chain launched eagerly")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_ffn_rmsnorm_amd import inputs as gen
+    from mixture_experts_ffn_rmsnorm_amd import moe
+
+    moe.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    cfg = gen.config(args.workload)
+    subs = [] if (args.only or cfg.hidden != 4096) else [gen.config(n) for n in SUB_WORKLOADS if n != cfg.name]
+    nl = lambda c: args.layers or (4 if c.rows <= 4 else 1)
+    L = max([nl(cfg)] + [nl(c) for c in subs])
+    log(f"workload {cfg.name} (+ {len(subs)} more): drawing {L} layers of weights on the GPU")
+    big = draw_layers(cfg, L)
+    layers = bind_layers(cfg, big, nl(cfg))
+    rec, gpu0 = time_workload(cfg, layers, args.steps, args.warmup, graph=args.graph and cfg.rows <= 4)
+    R = cfg.rows
+    res = {
+        "metric": METRIC, "value": rec["rows_per_s"], "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if R <= 4 else "f16", "data": "synthetic",
+        "config": {"workload": cfg.name, "rows": R, "hidden": cfg.hidden, "experts": cfg.experts,
+                   "top_k": cfg.top_k, "inter": cfg.inter, "shared_experts": 1,
+                   "layer_kind": "hash" if cfg.layer_kind == 1 else "score", "layers_cycled": rec["layers_cycled"],
+                   "distinct_routed_experts": rec["distinct_routed_experts"]},
+        "roofline": rec["roofline"],
+    }
+    for k in ("latency_us", "step_alg_bytes", "step_hbm_GBps", "step_hbm_frac", "step_alg_flops", "step_TFLOPs",
+              "step_mfma_frac", "status_flags", "kernels", "graph"):
+        if k in rec:
+            res[k] = rec[k]
+    sub_gpu = {}
+    if subs:
+        res["workloads"] = {}
+    for c in subs:
+        lay_c = bind_layers(c, big, nl(c))
+        r_c, g_c = time_workload(c, lay_c, args.steps, args.warmup, graph=args.graph and c.rows <= 4)
+        r_c["dtype"] = "f32" if c.rows <= 4 else "f16"
+        r_c["layer_kind"] = "hash" if c.layer_kind == 1 else "score"
+        res["workloads"][c.name] = r_c
+        sub_gpu[c.name] = (lay_c[0], g_c)
+        torch.cuda.empty_cache()
     if not args.no_peaks:
         # the published peaks above are the roofline's; these are the same
         # two ceilings measured on this device, after the timed passes
@@ -261,18 +319,23 @@ def main():
 
         log("measuring device ceilings")
         pk = device_peaks.measure()
+        roof = res["roofline"]
         top = pk["hbm_read_GBps"] if roof["unit"] == "GB/s" else pk["mfma_f16_TFLOPs"]
         pk["roofline_frac_of_measured"] = roof["achieved"] / top
         res["measured_peaks"] = pk
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds, log, gpu0)
+        res["cpu_baseline"] = cpu_baseline(cfg, layers[0], args.cpu_seconds, gpu0)
+        for c in subs:
+            lay0, g_c = sub_gpu[c.name]
+            res["workloads"][c.name]["cpu_baseline"] = oracle_full_batch(c, lay0, g_c)
     print(json.dumps(res), flush=True)
 
 
-def graph_chain(dims, cfg, layers, x, tok, ws, reps, log):
+def graph_chain(dims, cfg, layers, x, tok, ws, reps, eager_ms):
     """The L layers back to back as a model runs them (layer l's output is
-    layer l+1's input), captured once as a HIP graph and replayed: per-layer
-    time without host launches between the kernels."""
+    layer l+1's input), every layer on the one workspace `ws`: launched
+    eagerly, then captured once as a HIP graph and replayed.  Per-layer
+    times of both."""
     import torch
 
     from mixture_experts_ffn_rmsnorm_amd import moe
@@ -282,31 +345,36 @@ def graph_chain(dims, cfg, layers, x, tok, ws, reps, log):
 
     def chain():
         for l in range(L):
-            moe.forward(dims, bufs[l], tok, cfg.layer_kind, layers[l][2], bufs[l + 1], ws[l])
+            moe.forward(dims, bufs[l], tok, cfg.layer_kind, layers[l][2], bufs[l + 1], ws)
 
-    chain()  # outside the graph first
+    for _ in range(3):
+        chain()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        chain()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) * 1e3 / (reps * L)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         chain()
     for _ in range(3):
         g.replay()
     torch.cuda.synchronize()
-    log(f"graph: {L} layers, {reps} replays")
+    log(f"graph: {L} layers on one workspace, {reps} replays")
     t0 = time.perf_counter()
     for _ in range(reps):
         g.replay()
     torch.cuda.synchronize()
     ms_layer = (time.perf_counter() - t0) * 1e3 / (reps * L)
-    return {"layers": L, "replays": reps, "ms_per_layer": ms_layer, "rows_per_s": cfg.rows / (ms_layer / 1e3)}
+    return {"layers": L, "replays": reps, "workspaces": 1, "us_per_layer_graph": ms_layer * 1e3,
+            "us_per_layer_eager_chain": eager * 1e3, "us_per_step_independent": eager_ms * 1e3,
+            "rows_per_s_graph": cfg.rows / (ms_layer / 1e3)}
 
 
-def cpu_baseline(cfg, layer, budget_s, log, gpu=None):
-    """The float64 oracle on a bounded sample of the same workload; with the
-    GPU's output and expert indices for the same rows (`gpu`), also their
-    agreement with the oracle on that sample."""
-    import numpy as np
-
+def _oracle_weights(cfg, layer):
+    """The oracle's view of one bench layer: small parameters from the host
+    inputs, expert matrices copied from the device when first needed."""
     from mixture_experts_ffn_rmsnorm_amd import inputs as gen
     from oracle import moe_ref as ref
 
@@ -319,12 +387,56 @@ def cpu_baseline(cfg, layer, budget_s, log, gpu=None):
             cache[e] = tuple(gen.bf16_tensor_bits(m[e]) for m in (g, u, d))
         return cache[e]
 
-    W = ref.Weights(hi.norm_w, hi.router, hi.sel_bias, hi.tid2eid, expert,
-                    tuple(gen.bf16_tensor_bits(m) for m in (gs, us, ds)))
+    return ref.Weights(hi.norm_w, hi.router, hi.sel_bias, hi.tid2eid, expert,
+                       tuple(gen.bf16_tensor_bits(m) for m in (gs, us, ds))), cache
+
+
+def _threads():
+    """(threads the oracle's BLAS runs on, cores this process may use)."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    return blas, len(os.sched_getaffinity(0))
+
+
+def _parity(cfg, hi, res, out_g, idx_g):
+    """Agreement of the GPU's output and expert sets with the oracle's on the
+    rows of `res`: relL2, max-abs ratio, rows whose expert set matches, and
+    rows whose oracle 6th and 7th selection keys lie within 1e-6 (where a
+    set mismatch would be a float32 tie, not an error; hash layers select
+    from the table and have none)."""
+    import numpy as np
+
+    from oracle import moe_ref as ref
+
+    n = res["out"].shape[0]
+    ref_out = res["out"]
+    same = sum(set(idx_g[r].tolist()) == set(res["idx"][r].tolist()) for r in range(n))
+    gap_tol = 1e-6
+    near = 0
+    if cfg.layer_kind == ref.LAYER_SCORE and cfg.experts > cfg.top_k:
+        keys = ref.sigmoid(res["logits"]) + np.asarray(hi.sel_bias, dtype=np.float64)
+        top = -np.sort(-keys, axis=1)
+        near = int(np.sum(top[:, cfg.top_k - 1] - top[:, cfg.top_k] < gap_tol))
+    return {"rows": n, "relL2": float(np.linalg.norm(out_g - ref_out) / max(np.linalg.norm(ref_out), 1e-300)),
+            "maxabs_ratio": float(np.abs(out_g - ref_out).max() / max(np.abs(ref_out).max(), 1e-300)),
+            "index_match_rows": int(same), "near_tie_rows": near, "near_tie_gap": gap_tol}
+
+
+def cpu_baseline(cfg, layer, budget_s, gpu):
+    """The float64 oracle on a bounded sample of the headline workload (its
+    first <= 4 rows, repeated for ~budget_s), with the GPU's agreement on
+    those rows."""
+    from oracle import moe_ref as ref
+
+    hi = layer[0]
+    W, _ = _oracle_weights(cfg, layer)
     per = min(cfg.rows, 4)
-    # fetch the experts of the sample rows before timing
     xs, ts = hi.x[:per], hi.token_ids[:per]
-    res = ref.forward(xs, ts, cfg.layer_kind, W, cfg.top_k, cfg.eps)
+    res = ref.forward(xs, ts, cfg.layer_kind, W, cfg.top_k, cfg.eps)  # fetches the experts before timing
     log(f"cpu baseline: timing the oracle on {per}-row samples for ~{budget_s:.0f}s")
     t0 = time.perf_counter()
     done = 0
@@ -334,38 +446,43 @@ def cpu_baseline(cfg, layer, budget_s, log, gpu=None):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
-    base = {"value": done / el, "unit": "rows/s", "cores": cores, "kind": "oracle",
+    blas, host = _threads()
+    out_g, idx_g = gpu
+    return {"value": done / el, "unit": "rows/s", "cores": blas, "host_cores": host, "kind": "oracle",
             "sample": f"the first {per} row(s) of the workload through the float64 oracle, repeated "
-                      f"{done // per}x in {el:.1f}s (BLAS threads = cores)"}
-    if gpu is not None:
-        out_g, idx_g = gpu
-        ref_out = res["out"]
-        same = [set(idx_g[r].tolist()) == set(res["idx"][r].tolist()) for r in range(per)]
-        base["parity"] = {
-            "rows": per,
-            "relL2": float(np.linalg.norm(out_g - ref_out) / max(np.linalg.norm(ref_out), 1e-300)),
-            "maxabs_ratio": float(np.abs(out_g - ref_out).max() / max(np.abs(ref_out).max(), 1e-300)),
-            "index_match_rows": int(sum(same)),
-        }
-        # rows whose K-th and (K+1)-th selection keys (oracle, float64) lie
-        # closer than float32 rounding of the logits could reorder: there an
-        # index mismatch is a legitimate tie, not an error (hash layers select
-        # from the table and have none)
-        gap_tol = 1e-6
-        near = 0
-        if cfg.layer_kind == ref.LAYER_SCORE and cfg.experts > cfg.top_k:
-            keys = ref.sigmoid(res["logits"]) + np.asarray(hi.sel_bias, dtype=np.float64)
-            top = -np.sort(-keys, axis=1)
-            near = int(np.sum(top[:, cfg.top_k - 1] - top[:, cfg.top_k] < gap_tol))
-        base["parity"]["near_tie_rows"] = near
-        base["parity"]["near_tie_gap"] = gap_tol
-    return base
+                      f"{done // per}x in {el:.1f}s on {blas} BLAS threads ({host} cores available)",
+            "parity": _parity(cfg, hi, res, out_g[:per], idx_g[:per])}
+
+
+def oracle_full_batch(cfg, layer, gpu, min_s=3.0):
+    """The float64 oracle over the workload's whole batch (repeated until
+    min_s when one pass is shorter), timed after the experts it needs have
+    been copied to the host, and the GPU's agreement on every row."""
+    from oracle import moe_ref as ref
+
+    hi = layer[0]
+    W, cache = _oracle_weights(cfg, layer)
+    R = cfg.rows
+    log(f"{cfg.name}: oracle over all {R} rows")
+    idx = ref.forward(hi.x, hi.token_ids, cfg.layer_kind, W, cfg.top_k, cfg.eps)["idx"] if R <= 4 else gpu[1]
+    for e in set(int(v) for v in idx.reshape(-1) if 0 <= v < cfg.experts):
+        W.expert(e)  # host copies outside the timed region
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        res = ref.forward(hi.x, hi.token_ids, cfg.layer_kind, W, cfg.top_k, cfg.eps)
+        passes += 1
+        if time.perf_counter() - t0 >= min_s:
+            break
+    el = (time.perf_counter() - t0) / passes
+    blas, host = _threads()
+    rec = {"value": R / el, "unit": "rows/s", "cores": blas, "host_cores": host, "kind": "oracle",
+           "oracle_s_per_batch": el,
+           "sample": f"all {R} rows of the workload through the float64 oracle, {passes} pass(es) of {el:.2f}s "
+                     f"on {blas} BLAS threads ({host} cores available); expert copies to the host not timed",
+           "parity": _parity(cfg, hi, res, gpu[0], gpu[1])}
+    cache.clear()
+    return rec
 
 
 if __name__ == "__main__":

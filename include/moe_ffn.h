@@ -240,10 +240,21 @@ int moe_ffn_routing_view(const moe_dims_t* d, int64_t rows, void* workspace, siz
 
 /* Synchronises `stream`, then copies the status word of the last
  * moe_ffn_forward that used `workspace` (OR of MOE_FLAG_* bits) to *flags.
+ * ffn_forward.rs runs deepseek_moe_sanitize_indices between the route and
+ * the expert matmuls, turning the I32 indices into U32 safe indices while
+ * the weighted reduce still receives the raw ones; what that step found
+ * (a token id outside the table, a table entry outside [0, experts)) is
+ * device data the host cannot see at call time, so it is reported here
+ * after the fact instead of as an error return.
  * Errors: MOE_EINVAL, MOE_EHIP. */
 int moe_ffn_status(const void* workspace, void* stream, uint32_t* flags);
 
-/* Static English text for a status code. */
+/* Static English text for a status code.  forward_ffn_rows on the
+ * ffn_forward.rs page reports its argument failures as anyhow errors from
+ * bail! checks (layer and rows range, routed-row overflow, the fixed MoE
+ * shape, state dtype and shape, a layer with neither a tid2eid table nor a
+ * selection bias); here each becomes a moe_status code checked on the host,
+ * and this gives its text. */
 const char* moe_strerror(int code);
 
 /* ---- stage timing (replaces the page's env-flagged profile_stage_boundary

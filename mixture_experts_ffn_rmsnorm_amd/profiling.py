@@ -94,7 +94,7 @@ def _run(cmd, log):
 
 
 def _bench_cmd(workload, extra):
-    return [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload] + list(extra)
+    return [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--only"] + list(extra)
 
 
 def cmd_stats(args, extra):
@@ -126,7 +126,7 @@ def cmd_stats(args, extra):
         f.write(f"# Kernel durations, workload {args.workload}\n\n")
         f.write("Command (from the repository root, on one MI355X):\n\n")
         f.write(f"    {cmdline}\n\nwhich runs\n\n    rocprofv3 --kernel-trace --stats --output-format csv "
-                f"-d <scratch> -o run -- python3 bench.py --workload {args.workload}"
+                f"-d <scratch> -o run -- python3 bench.py --workload {args.workload} --only"
                 + ("" if not extra else " " + " ".join(extra)) + "\n\n")
         f.write(f"Kernel sources digest: `{sources_digest()}`\n\n")
         f.write("rocprofv3 kernel statistics for this library's kernels (every call of the run: warm-up, "
@@ -178,7 +178,7 @@ def cmd_traffic(args, extra):
         f.write(f"# HBM traffic per dispatch, workload {args.workload}, from rocprofv3 counters\n")
         f.write(f"# command: python3 -m mixture_experts_ffn_rmsnorm_amd.profiling traffic --workload {args.workload}\n")
         f.write("# passes: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, each over\n")
-        f.write(f"#   python3 bench.py --workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline --no-peaks\n")
+        f.write(f"#   python3 bench.py --workload {args.workload} --only --steps 5 --warmup 2 --no-cpu-baseline --no-peaks\n")
         f.write("#   and over a 1 GiB device-to-device copy (calibration: factor = bytes / counter bytes)\n")
         f.write(f"sources_sha256: {sources_digest()}\n")
         f.write(f"copy_kernel: {short_name(cf_name)}\n")
