@@ -57,10 +57,10 @@ def alg_bytes(kernel, cfg, U, R):
         return H * I * 2 + U * 2 * I * H * 2 + R * (I + H) * 4 + R * K * (H + I) * 4
     if kernel == "dec_down_reduce":  # routed down + weighted reduce
         return U * H * I * 2 + R * K * (I + 2 * H) * 4 + R * H * 4 + x
-    if kernel == "dec1_router":      # one-row path: router, logits + xn out
-        return E * H * 2 + x + H * 4 + R * E * 4 + R * H * 4
-    if kernel == "dec1_gateup":      # shared + routed gate/up, routing from the logits
-        return (U + 1) * 2 * I * H * 2 + R * E * 4 + R * H * 4 + (R * K + R) * I * 4 + R * K * 12
+    if kernel == "dec1_router":      # one-row path: router, logits + keys + sigmoids + xn out
+        return E * H * 2 + x + H * 4 + R * E * 4 + R * H * 4 + R * E * 16
+    if kernel == "dec1_gateup":      # shared + routed gate/up, routing from the keys
+        return (U + 1) * 2 * I * H * 2 + R * E * 16 + R * H * 4 + (R * K + R) * I * 4 + R * K * 12
     if kernel == "dec1_down_reduce":  # routed + shared down + weighted reduce
         return (U + 1) * H * I * 2 + (R * K + R) * I * 4 + (R * K + R) * 2 * H * 4 + R * H * 4
     if kernel == "pre_norm":         # x in, xn16 + xlo16 out
@@ -204,7 +204,10 @@ def time_workload(cfg, layers, steps, warmup, graph=False):
     avg_s = stages[dom][0] / stages[dom][1] / 1e3
     flops = alg_flops(dom, cfg, R)
     b = alg_bytes(dom, cfg, u_mean, R)
-    if flops is not None and flops / (MFMA_F16_PEAK_TFLOPS * 1e12) > b / (HBM_PEAK_GBPS * 1e9):
+    if b is None and flops is None:  # a kernel this accounting does not know
+        roof = {"kernel": dom, "bound": None, "achieved": None, "peak": None, "unit": None, "frac": None,
+                "traffic": None}
+    elif flops is not None and (b is None or flops / (MFMA_F16_PEAK_TFLOPS * 1e12) > b / (HBM_PEAK_GBPS * 1e9)):
         ach = flops / avg_s / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_F16_PEAK_TFLOPS, "traffic": None}

@@ -66,12 +66,9 @@ enum {
                                    all of that row's slots were masked      */
   MOE_FLAG_BAD_TABLE_ENTRY = 2u, /* a table entry outside [0, experts): that
                                     slot was masked                         */
-  MOE_FLAG_SYNC_TIMEOUT = 4u,    /* an in-kernel wait for other workgroups
-                                    gave up (only if the GPU could not run
-                                    the whole grid); the output is invalid
-                                    and the workspace must be zero-filled
-                                    again before its next use.  Only calls
-                                    of 2 to 4 rows wait at all              */
+  MOE_FLAG_SYNC_TIMEOUT = 4u,    /* reserved, never set: no workgroup of
+                                    any call waits for another (kept so the
+                                    bit values stay stable)                 */
   MOE_FLAG_F16_RANGE = 8u        /* calls of more than 4 rows only (the
                                     matrix-core path, whose operands are
                                     fp16): a router logit, SwiGLU output,
@@ -152,14 +149,14 @@ int moe_ffn_workspace_bytes(const moe_dims_t* d, int64_t rows, size_t* bytes);
  *   workspace  device, >= moe_ffn_workspace_bytes(d, rows), 256-byte
  *              aligned, zero-filled before its first use (e.g. by
  *              hipMemset); after that every call leaves it valid for the
- *              next, whatever the row count.  Calls of 2 to 4 rows hand the
- *              router logits between workgroups in words tagged with a
- *              nonzero per-call value, and set each word back to 0 once
- *              consumed, so a word never carries a tag its call did not
- *              write (graph replays and eager calls may share a workspace
- *              in any order).  After the call the workspace holds the
- *              routing (see moe_ffn_routing_view) and the status word (see
- *              moe_ffn_status) until the next call that uses it.
+ *              next, whatever the row count, in any order of eager calls
+ *              and graph replays.  (Calls of 2 to 4 rows keep an arrival
+ *              count of their router workgroups in it, which must read 0
+ *              when a call starts; the workgroup that completes the count
+ *              routes the batch and sets it back to 0.)  After the call the
+ *              workspace holds the routing (see moe_ffn_routing_view) and
+ *              the status word (see moe_ffn_status) until the next call
+ *              that uses it.
  * Token ids and table entries are device data, so a bad one is not a host
  * error: the affected slots are masked (they contribute nothing and the
  * row's other weights are renormalised over its valid slots) and a status
@@ -195,7 +192,7 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
  *   Limit: a call whose moe_ffn_workspace_bytes exceeds the array is
  *   rejected with MOE_ESCRATCH before any HIP call -- at the full shape
  *   (hidden 4096, 256 experts, inter 2048) that is more than 696 rows, at
- *   the tiny shape more than 5539 rows; decode calls (1 to 4 rows) always
+ *   the tiny shape more than 5540 rows; decode calls (1 to 4 rows) always
  *   fit.
  *   Sharing: every call on one GPU uses that GPU's array, which keeps the
  *   last call's contents.  Calls on one stream (or otherwise ordered) are

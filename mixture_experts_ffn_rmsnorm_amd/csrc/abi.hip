@@ -8,8 +8,6 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
-#include <atomic>
-#include <chrono>
 #include <math.h>
 #include <mutex>
 #include <string.h>
@@ -82,17 +80,6 @@ struct StageTimer {
 StageTimer& timer() {
   static StageTimer t;
   return t;
-}
-
-// Host part of the per-call tag of the decode path's tagged words: a
-// process-wide counter seeded from the clock.  Words consumed by a call are
-// set back to 0 on the device, so the tag only has to differ from 0 and from
-// whatever a fresh workspace happens to hold; the kernels add the
-// workspace's device-side call count to it.
-uint32_t next_epoch() {
-  static std::atomic<uint32_t> ctr{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
-  uint32_t e = ctr.fetch_add(1, std::memory_order_relaxed);
-  return e ? e : ctr.fetch_add(1, std::memory_order_relaxed);
 }
 
 }  // namespace
@@ -182,7 +169,6 @@ int forward_in(const moe_dims_t* d, const float* x, const int32_t* token_ids, in
   a.out = out;
   a.status = (uint32_t*)(ws + L.status);
   a.sync = (DecodeSync*)(ws + L.status + 64);  // both paths: the status block
-  a.epoch = next_epoch();
   a.logits = (float*)(ws + L.logits);
   a.idx = (int32_t*)(ws + L.idx);
   a.wts = (float*)(ws + L.wts);

@@ -523,31 +523,46 @@ __device__ __forceinline__ SlotRoute route_slots_keyed(const uint64_t (&key)[4],
   return o;
 }
 
-// The call's tag for the decode path's tagged words: the host's per-call
-// value plus the workspace's device-side call count, which the gate/up
-// launch advances.  Never 0.  Tags of different calls may repeat (the
-// replays of a captured graph keep the host values they were captured
-// with); what makes a word's tag mean "written by this call" is that the
-// plan block of every call sets each word it consumed back to 0 once it has
-// seen the call's tag on it: a later call on the same workspace starts with
-// those words at 0, and only its own router waves tag them again.
-__device__ __forceinline__ uint32_t call_epoch(const FwdArgs& a) {
-  const uint32_t e = a.epoch + a.sync->call_seq;
-  return e ? e : 1u;
+// Routing of the one row by wave 0 of a one-row gate/up block, from the
+// selection keys and float64 sigmoids the router launch stored (plain loads:
+// written by the launch before).
+__device__ void route_one_row(const FwdArgs& a, int* s_idx, float* s_w, unsigned char* s_valid, uint32_t* s_flags) {
+  const int K = a.K, E = a.E;
+  const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  if (wv != 0) return;
+  const bool hash = a.layer_kind == MOE_LAYER_HASH;
+  int ent = -1;
+  bool tok_ok = false;
+  if (hash) {
+    const int32_t tok = a.token_ids[0];
+    tok_ok = tok >= 0 && (int64_t)tok < a.table_rows;
+    if (tok_ok && lane < K) ent = a.table[(int64_t)tok * K + lane];
+  }
+  uint64_t key[4];
+  double sig[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + kWave * j;
+    key[j] = e < E ? a.sync->route_key[e] : 0ull;
+    sig[j] = e < E ? a.sync->route_sig[e] : 0.0;
+  }
+  const SlotRoute sr = route_slots_keyed(key, sig, E, K, hash, tok_ok, ent);
+  if (lane < K) {
+    s_idx[lane] = sr.idx;
+    s_w[lane] = sr.w;
+    s_valid[lane] = sr.valid;
+  }
+  if (lane == 0) s_flags[0] = sr.flags;
 }
 
-// Routing of the batch into LDS: wave r < R routes row r.  It first reads
-// what the route needs besides the logits (bias, or the token's table row),
-// then polls the row's tagged logits until every one carries the call's
-// epoch (bounded; returns false on timeout), and sets those words back to 0:
-// each is written once per call, by this call's router, so once all of them
-// carry the tag no write to them is pending.  `plain` (one row, after the
-// router launch): it reads the stored keys and sigmoids instead, no waiting.
-__device__ bool route_rows(const FwdArgs& a, uint32_t epoch, bool plain, int* s_idx, float* s_w,
-                           unsigned char* s_valid, uint32_t* s_flags) {
+// Routing of the batch by the router launch's last block: wave r < R
+// routes row r from the logits the router blocks published (read past any
+// stale cache line: other workgroups wrote them) into LDS.  It first reads
+// what the route needs besides the logits (bias, or the token's table row).
+__device__ void route_batch(const FwdArgs& a, int* s_idx, float* s_w, unsigned char* s_valid, uint32_t* s_flags) {
   const int R = a.R, K = a.K, E = a.E;
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  if (wv >= R) return true;
+  if (wv >= R) return;
   const bool hash = a.layer_kind == MOE_LAYER_HASH;
   int ent = -1;
   bool tok_ok = false;
@@ -560,65 +575,27 @@ __device__ bool route_rows(const FwdArgs& a, uint32_t epoch, bool plain, int* s_
 #pragma unroll
     for (int j = 0; j < 4; ++j) bias[j] = (lane + kWave * j < E) ? a.bias[lane + kWave * j] : 0.f;
   }
-  if (plain) {  // one row: the router launch's keys and sigmoids, plain loads
-    uint64_t key[4];
-    double sig[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + kWave * j;
-      key[j] = e < E ? a.sync->route_key[e] : 0ull;
-      sig[j] = e < E ? a.sync->route_sig[e] : 0.0;
-    }
-    const SlotRoute sr = route_slots_keyed(key, sig, E, K, hash, tok_ok, ent);
-    if (lane < K) {
-      s_idx[lane] = sr.idx;
-      s_w[lane] = sr.w;
-      s_valid[lane] = sr.valid;
-    }
-    if (lane == 0) s_flags[0] = sr.flags;
-    return true;
-  }
-  uint64_t* tags = a.sync->logit_tag + wv * E;
-  float lgv[4];
-  bool ready = false;
-  for (int polls = 0;; ++polls) {
-    bool mine = true;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + kWave * j;
-      lgv[j] = 0.f;
-      if (e < E) {
-        const uint64_t w = __hip_atomic_load(&tags[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        mine &= (uint32_t)(w >> 32) == epoch;
-        lgv[j] = __uint_as_float((uint32_t)w);
-      }
-    }
-    ready = __ballot(!mine) == 0;
-    if (ready || polls >= kMaxPolls) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
+  float lg[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + kWave * j;
-    if (e < E) __hip_atomic_store(&tags[e], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lg[j] = e < E ? load_wt(&a.logits[(int64_t)wv * E + e]) : 0.f;
   }
-  const SlotRoute sr =
-      route_slots(lgv[0], lgv[1], lgv[2], lgv[3], bias[0], bias[1], bias[2], bias[3], E, K, hash, tok_ok, ent);
+  const SlotRoute sr = route_slots(lg[0], lg[1], lg[2], lg[3], bias[0], bias[1], bias[2], bias[3], E, K, hash, tok_ok,
+                                   ent);
   if (lane < K) {
     s_idx[wv * K + lane] = sr.idx;
     s_w[wv * K + lane] = sr.w;
     s_valid[wv * K + lane] = sr.valid;
   }
   if (lane == 0) s_flags[wv] = sr.flags;
-  return ready;
 }
 
 // Writes the block's routing (indices, weights, row flags, status word) and
 // the plan (from LDS) to the workspace for the later launches and the
-// caller, and clears the down launch's tile counters.  `ok` false if a wait
-// gave up (MOE_FLAG_SYNC_TIMEOUT in the status word).
-__device__ void publish_routing(const FwdArgs& a, bool ok, const int* s_idx, const float* s_w,
-                                const uint32_t* s_flags, const DecodePlan* P) {
+// caller, and clears the down launch's tile counters.
+__device__ void publish_routing(const FwdArgs& a, const int* s_idx, const float* s_w, const uint32_t* s_flags,
+                                const DecodePlan* P) {
   const int R = a.R;
   DecodeSync* sy = a.sync;
   for (int s = threadIdx.x; s < R * a.K; s += kThreads) {
@@ -627,7 +604,7 @@ __device__ void publish_routing(const FwdArgs& a, bool ok, const int* s_idx, con
   }
   if ((int)threadIdx.x < R) a.rowflags[threadIdx.x] = s_flags[threadIdx.x];
   if (threadIdx.x == 0) {
-    uint32_t f = ok ? 0u : (uint32_t)MOE_FLAG_SYNC_TIMEOUT;
+    uint32_t f = 0;
     for (int r = 0; r < R; ++r) f |= s_flags[r];
     a.status[0] = f;
   }
@@ -695,22 +672,18 @@ __device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs
 
 // ---------------------------------------------------------------------------
 // Head kernel: router, routing plan and the shared expert's gate/up.
-// grid = E/4 router blocks, I/8 shared gate/up blocks, then one plan block
-// (a block only waits for blocks before it, which the hardware has
-// dispatched already).
+// grid = E/4 router blocks, then I/8 shared gate/up blocks.
 //   Router block (experts 4b .. 4b+3, one per wave): requests its router
-//   rows, normalises the batch rows into LDS, and forms logit[r,e] =
-//   sum_j W[e,j] xn[r,j].  It writes the logits, and each one tagged with
-//   the call's epoch to logit_tag.
+//   rows, normalises the batch rows into LDS, forms logit[r,e] = sum_j
+//   W[e,j] xn[r,j] and writes it through.  Then it counts itself in; the
+//   block that completes the count -- every logit is written by then --
+//   routes the batch (wave r row r), builds the plan
+//   of distinct (expert, row) pairs, publishes indices, weights, row flags,
+//   status and the plan, clears the down launch's tile counters and resets
+//   the count for the next call.  No workgroup waits for another.
 //   Shared gate/up block: RMSNorm into LDS, then 8 inter rows of the shared
-//   expert's SwiGLU output for every row (its streaming covers the router's
-//   and the plan's latency).  The norm comes before the block requests its
-//   weights, which lets the router's weight rows reach the memory queues
-//   first.  The first of these blocks publishes xn.
-//   Plan block: routes the batch (wave r polls row r's tagged logits and
-//   then zeroes them), publishes indices, weights, row flags, status and the
-//   plan, and clears the down kernel's tile counters.  A wait that gives up
-//   sets MOE_FLAG_SYNC_TIMEOUT in the status word.
+//   expert's SwiGLU output for every row; its streaming covers the router's
+//   latency and the routing.  The first of these blocks publishes xn.
 template <int H, int I, bool kRouterOnly>
 __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [R][H]
@@ -719,24 +692,12 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   __shared__ unsigned char s_valid[kDecodeMaxSlots];
   __shared__ uint32_t s_flags[kDecodeMaxRows];
   __shared__ DecodePlan P;
+  __shared__ int s_last;
   const int R = a.R, E = a.E, K = a.K;
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   DecodeSync* sy = a.sync;
-  const uint32_t epoch = call_epoch(a);
   const int nrb = (E + 3) / 4, nsh = I / kShRows;
   const int b = blockIdx.x;
-  if (!kRouterOnly && b == nrb + nsh) {  // plan block
-    __shared__ int s_ok;
-    if (threadIdx.x == 0) s_ok = 1;
-    __syncthreads();
-    if (!route_rows(a, epoch, false, s_idx, s_w, s_valid, s_flags) && lane == 0) s_ok = 0;
-    __syncthreads();
-    const bool ok = s_ok;
-    if (wv == 0) build_plan(s_idx, s_w, s_valid, R, K, E, &P);
-    __syncthreads();
-    publish_routing(a, ok, s_idx, s_w, s_flags, &P);
-    return;
-  }
   if (!kRouterOnly && b >= nrb) {  // shared gate/up block
     const int x = b - nrb;
     auto stage = [&]() {
@@ -761,44 +722,59 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
       if (c < NCH - 1 || full) q[c] = load_stream(a.router + (int64_t)e * H + c * 512 + lane * 8);
   }
   norm_rows_to_lds<H>(a.x, a.norm_w, R, a.eps, xs);
-  if (kRouterOnly && b == 0)  // the later launches stage the normalised rows from xn
+  if (kRouterOnly && b == 0)  // the later launches stage the normalised row from xn
     for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
-  if (e >= E) return;
-  float dot[kDecodeMaxRows] = {0.f, 0.f, 0.f, 0.f};
+  if (e < E) {
+    float dot[kDecodeMaxRows] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    if (c < NCH - 1 || full) {
-      const int col = c * 512 + lane * 8;
-      float f[8];
-      unpack8(q[c], f);
+    for (int c = 0; c < NCH; ++c) {
+      if (c < NCH - 1 || full) {
+        const int col = c * 512 + lane * 8;
+        float f[8];
+        unpack8(q[c], f);
 #pragma unroll
-      for (int r = 0; r < kDecodeMaxRows; ++r) {
-        if (r < R) {
-          const float4 x0 = *(const float4*)(xs + r * H + col), x1 = *(const float4*)(xs + r * H + col + 4);
-          const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        for (int r = 0; r < kDecodeMaxRows; ++r) {
+          if (r < R) {
+            const float4 x0 = *(const float4*)(xs + r * H + col), x1 = *(const float4*)(xs + r * H + col + 4);
+            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) dot[r] = fmaf(f[i], xv[i], dot[r]);
+            for (int i = 0; i < 8; ++i) dot[r] = fmaf(f[i], xv[i], dot[r]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kDecodeMaxRows; ++r) {
+      if (r < R) {
+        const float v = wave_sum(dot[r]);
+        if (lane == 0) {
+          if (kRouterOnly) {  // one row: what the gate/up blocks' routing needs of this expert
+            a.logits[e] = v;
+            sy->route_sig[e] = sigmoid_f64(v);
+            sy->route_key[e] = a.layer_kind == MOE_LAYER_HASH ? 0ull : ordered_key(score_key(v, a.bias[e]));
+          } else {
+            store_wt(&a.logits[(int64_t)r * E + e], v);
+          }
         }
       }
     }
   }
-#pragma unroll
-  for (int r = 0; r < kDecodeMaxRows; ++r) {
-    if (r < R) {
-      const float v = wave_sum(dot[r]);
-      if (lane == 0) {
-        a.logits[(int64_t)r * E + e] = v;
-        if (kRouterOnly) {  // one row: what the gate/up blocks' routing needs of this expert
-          const double sg = sigmoid_f64(v);
-          sy->route_sig[e] = sg;
-          sy->route_key[e] = a.layer_kind == MOE_LAYER_HASH ? 0ull : ordered_key(score_key(v, a.bias[e]));
-        }
-        if (!kRouterOnly)
-          __hip_atomic_store(&sy->logit_tag[r * E + e], ((uint64_t)epoch << 32) | __float_as_uint(v),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+  if (kRouterOnly) return;
+  // count in once the logits are written through (like the down launch's
+  // partials: no cache-wide fence); the last router block routes, reading
+  // them with write-through loads
+  sync_stores();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&sy->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == (uint32_t)nrb;
+  __syncthreads();
+  if (!s_last) return;
+  route_batch(a, s_idx, s_w, s_valid, s_flags);
+  __syncthreads();
+  if (wv == 0) build_plan(s_idx, s_w, s_valid, R, K, E, &P);
+  __syncthreads();
+  publish_routing(a, s_idx, s_w, s_flags, &P);
+  if (threadIdx.x == 0) sy->arrive = 0;  // every router block of this call has counted in
 }
 
 // ---------------------------------------------------------------------------
@@ -816,7 +792,6 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [nr][H] activations, or [R][I] shared h
   constexpr int nsd = H / kSdRows, gut = I / kGuRows;
   const int b = blockIdx.x;
-  if (b == 0 && threadIdx.x == 0) a.sync->call_seq = a.sync->call_seq + 1;  // the head has read it
   if (b < nsd) {
     const float* src[4];
 #pragma unroll
@@ -866,11 +841,11 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
     return;
   }
   const int u = (b - nsh) / gut, x = (b - nsh) % gut;
-  route_rows(a, 0, true, s_idx, s_w, s_valid, s_flags);  // wave 0 (the row)
+  route_one_row(a, s_idx, s_w, s_valid, s_flags);  // wave 0 (the row)
   __syncthreads();
   if (threadIdx.x < kWave) build_plan(s_idx, s_w, s_valid, 1, a.K, a.E, &P);
   __syncthreads();
-  if (u == 0 && x == 0) publish_routing(a, true, s_idx, s_w, s_flags, &P);
+  if (u == 0 && x == 0) publish_routing(a, s_idx, s_w, s_flags, &P);
   if (u >= plan_ngroups(&P)) return;
   const PlanGroup g = plan_group(&P, u, a.E);
   const int nr = g.nr < a.R ? g.nr : a.R;  // LDS holds a.R rows
@@ -972,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
 
 template <int H, int I>
 hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
-  static_assert(H / kDnRows <= kDecodeMaxTiles && I / kShRows <= kDecodeMaxTiles, "too many tiles");
+  static_assert(H / kDnRows <= kDecodeMaxTiles, "too many down tiles");
   FwdArgs args = a;
   const int gmax = a.R * a.K < a.E ? a.R * a.K : a.E;
   hipError_t err;
@@ -988,7 +963,7 @@ hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
     return launch("dec1_down_reduce", (const void*)k_dec_down<H, I, true>, dim3(H / kDnRows, gmax + 2),
                   dim3(kThreads), 0, s, &args);
   }
-  err = launch("dec_head", (const void*)k_dec_head<H, I, false>, dim3((a.E + 3) / 4 + I / kShRows + 1),
+  err = launch("dec_head", (const void*)k_dec_head<H, I, false>, dim3((a.E + 3) / 4 + I / kShRows),
                dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
   err = launch("dec_gateup", (const void*)k_dec_gateup<H, I>, dim3(H / kSdRows + gmax * (I / kGuRows)),

@@ -22,7 +22,6 @@ struct FwdArgs {
   float eps;
   int layer_kind;
   int64_t table_rows;
-  uint32_t epoch;  // host part of the per-call tag of the decode path's tagged words
   // inputs / outputs
   const float* x;
   const int32_t* token_ids;

@@ -36,22 +36,19 @@ struct DecodePlan {
   float entry_w[kDecodeMaxSlots];
 };
 
-// Cross-workgroup signalling words of the decode path, after the status word.
-// A tagged word carries the call's tag in its upper half and a 32-bit value
-// in its lower half, written and read whole, so its reader polls the data
-// itself; the reader sets every word it consumed back to 0 (no tag is 0), so
-// no completed call leaves a tagged word behind for a later one.  Counters
-// are zeroed by the first kernel of the call for the later ones.
+// Cross-workgroup counters of the decode path, after the status word.  The
+// arrival count starts every call at 0: the router block that completes it
+// resets it (the workspace is zero-filled before its first use); the tile
+// counters are cleared by the head launch for the down launch.
 constexpr int kDecodeMaxTiles = 256;  // down column tiles (hidden/32) and shared gate/up tiles (inter/8)
 struct DecodeSync {
-  uint32_t call_seq;                     // two- to four-row calls made on this workspace (device side)
+  uint32_t arrive;                       // router blocks of the current call that have written their logits
   uint32_t pad[15];
-  uint64_t logit_tag[kDecodeMaxRows * kMaxExperts];  // router wave -> plan block: tag | f32 logit bits
+  uint32_t tile_cnt[kDecodeMaxTiles];    // groups finished per down column tile
   // one-row path: each expert's ordered selection key and float64 sigmoid,
   // written by the router launch for the gate/up blocks that route
   uint64_t route_key[kMaxExperts];
   double route_sig[kMaxExperts];
-  uint32_t tile_cnt[kDecodeMaxTiles];    // groups finished per down column tile
 };
 
 struct Layout {

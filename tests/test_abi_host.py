@@ -266,6 +266,6 @@ def test_noalloc_rejects_on_host():
     assert _noalloc(d, rows=697) == moe.MOE_ESCRATCH
     assert _noalloc(d, rows=8192) == moe.MOE_ESCRATCH
     t = moe.make_dims(**TINY)
-    assert moe.workspace_bytes(t, 5539) <= moe.NOALLOC_SCRATCH_BYTES < moe.workspace_bytes(t, 5540)
-    assert _noalloc(t, rows=5540) == moe.MOE_ESCRATCH
+    assert moe.workspace_bytes(t, 5540) <= moe.NOALLOC_SCRATCH_BYTES < moe.workspace_bytes(t, 5541)
+    assert _noalloc(t, rows=5541) == moe.MOE_ESCRATCH
     assert "scratch" in moe.strerror(moe.MOE_ESCRATCH)
