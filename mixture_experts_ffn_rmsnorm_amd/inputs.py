@@ -15,6 +15,10 @@ Recipe (per tensor an independent stream):
     the experts it needs.
   * Normal samples are drawn in float32, scaled by the stated standard
     deviation and rounded to bf16 with round-to-nearest-even.
+  * Block-scaled (MXFP8) expert weights, the layer's second weight format:
+    E4M3 codes of N(0,1) * 8 samples (rounded to E4M3 by torch) and one
+    E8M0 scale per 32 inputs drawn from 2^-10, 2^-9, 2^-8, from torch's
+    generator with one seed per (tensor, expert) as above.
 """
 
 from __future__ import annotations
@@ -214,6 +218,61 @@ def expert_weights_device(cfg: Config, device, layer: int = 0):
     fill(su, _T_SUP, 0)
     fill(sd, _T_SDOWN, 0)
     return (gate, up, down), (sg, su, sd)
+
+
+# --------------------------------------------------------------------------
+# block-scaled 8-bit expert weights (OCP MXFP8: E4M3 codes, one E8M0 scale
+# per MX_BLOCK elements along the input dimension)
+# --------------------------------------------------------------------------
+MX_BLOCK = 32
+_T_MX = 20  # tensor-id offset of the MX weight streams
+
+
+def _mx_matrix(gen, out, inn, device):
+    """Codes: N(0,1) * 8 (within E4M3's +-448) rounded to E4M3 by torch;
+    scales: 2^-10, 2^-9 or 2^-8 per block, so the weights have a standard
+    deviation of 0.008-0.03 like the bf16 workloads' 0.02."""
+    import torch
+
+    v = torch.randn((out, inn), generator=gen, device=device, dtype=torch.float32).mul_(8.0).clamp_(-448.0, 448.0)
+    codes = v.to(torch.float8_e4m3fn).view(torch.uint8)
+    sc = torch.randint(117, 120, (out, inn // MX_BLOCK), generator=gen, device=device, dtype=torch.int32)
+    return codes, sc.to(torch.uint8)
+
+
+def mx_expert_weights(cfg: Config, device, layer: int = 0):
+    """MXFP8 expert weights drawn on ``device`` (host for ``"cpu"``): returns
+    ``(gate, up, down)`` and the shared ``(gate, up, down)``, each matrix a
+    ``(codes uint8 [..., out, in], scales uint8 [..., out, in/32])`` pair of
+    torch tensors (routed: a leading expert dimension).  One generator seed
+    per (tensor, expert)."""
+    import torch
+
+    ls = cfg.param_seed + 7919 * layer
+    I, H, E = cfg.inter, cfg.hidden, cfg.experts
+    gen = torch.Generator(device=device)
+
+    def mat(tensor_id, e, out, inn):
+        gen.manual_seed((ls * 1_000_003 + (_T_MX + tensor_id) * 65_537 + e) & 0x7FFF_FFFF_FFFF_FFFF)
+        return _mx_matrix(gen, out, inn, device)
+
+    def stack(tensor_id, out, inn):
+        q = torch.empty((E, out, inn), dtype=torch.uint8, device=device)
+        s = torch.empty((E, out, inn // MX_BLOCK), dtype=torch.uint8, device=device)
+        for e in range(E):
+            q[e], s[e] = mat(tensor_id, e, out, inn)
+        return q, s
+
+    routed = (stack(_T_GATE, I, H), stack(_T_UP, I, H), stack(_T_DOWN, H, I))
+    shared = (mat(_T_SGATE, 0, I, H), mat(_T_SUP, 0, I, H), mat(_T_SDOWN, 0, H, I))
+    return routed, shared
+
+
+def mx_host(pair):
+    """Host numpy copy ``(codes, scales)`` of one MX matrix (or one expert's
+    slice of a stacked one)."""
+    q, s = pair
+    return q.detach().contiguous().cpu().numpy(), s.detach().contiguous().cpu().numpy()
 
 
 def bf16_tensor_bits(t) -> np.ndarray:

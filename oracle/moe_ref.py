@@ -47,12 +47,20 @@ the design notes of the repository):
   * Weights are bf16 bit patterns, widened exactly to float64; every
     activation stays in float64.
 
+Block-scaled weights: an expert matrix may be given as OCP MXFP8 codes and
+scales instead of bf16 bits; ``mx_dequant`` decodes it exactly (FP8 E4M3 and
+E8M0 values are all exact in float64) and the layer is then computed the
+same way.
+
 Parity pins (tests/test_oracle_pins.py): brute-force top-k ranks and subset
 enumeration, sum-to-one weights, hash == score when the table holds the score
 route's choice, the closed form at x = 0, a hand-worked micro example
 (tests/golden/micro_h2.txt), RMSNorm scale invariance and mean-square identity,
 row independence, expert relabelling, identical experts, matmul against a
-plain triple loop, and bf16 widening of known bit patterns.
+plain triple loop, bf16 widening of known bit patterns, and the MX decoders
+against hand-derived codes (tests/golden/mx_codes.txt), against torch's
+float8 E4M3 / E8M0 types for all 256 codes, and through a whole layer whose
+MX weights hold the same values as a bf16 layer.
 """
 
 from __future__ import annotations
@@ -75,6 +83,54 @@ def bf16_to_f64(bits) -> np.ndarray:
     """
     b = np.ascontiguousarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# block-scaled 8-bit weights (OCP Microscaling "MXFP8": FP8 E4M3 elements,
+# one E8M0 power-of-two scale per 32 consecutive elements of a row).  The
+# FFN page binds its expert matrices as GGML-typed raw matrices without
+# naming the type; the only MXFP8 on the pages (the attention page's
+# activation fake-quant) uses blocks of 64.  Weights here follow the OCP
+# layout: blocks of MX_BLOCK along the input dimension of each row.
+# --------------------------------------------------------------------------
+MX_BLOCK = 32
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> float64.  Bit 7 is the sign, bits 6..3
+    the exponent (bias 7), bits 2..0 the mantissa.  Exponent 0 encodes
+    subnormals m/8 * 2^-6; exponent 15 with mantissa 7 is NaN; the format has
+    no infinities (so 448 = 2^8 * 1.75 is the largest finite value)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign, ex, man = c >> 7, (c >> 3) & 15, c & 7
+    mag = np.where(ex == 0, man / 8.0 * 2.0 ** -6, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
+    mag = np.where((ex == 15) & (man == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+def e8m0_to_f64(scales) -> np.ndarray:
+    """E8M0 scale codes (uint8) -> float64: 2^(s - 127); 255 is NaN."""
+    s = np.asarray(scales, dtype=np.uint8).astype(np.int64)
+    return np.where(s == 255, np.nan, np.exp2(s - 127.0))
+
+
+def mx_dequant(codes, scales, block: int = MX_BLOCK) -> np.ndarray:
+    """Decode an MX matrix exactly: ``w[..., o, i] = e4m3(codes[..., o, i]) *
+    e8m0(scales[..., o, i // block])``."""
+    v = e4m3_to_f64(codes)
+    sc = e8m0_to_f64(scales)
+    assert sc.shape[-1] * block == v.shape[-1], "one scale per block of the input dimension"
+    return v * np.repeat(sc, block, axis=-1)
+
+
+def weight_f64(w) -> np.ndarray:
+    """One weight matrix in float64: bf16 bit patterns (uint16) widened
+    exactly, an MX matrix given as ``(codes, scales)`` decoded exactly, or an
+    array of values taken as they are."""
+    if isinstance(w, tuple):
+        return mx_dequant(*w)
+    w = np.asarray(w)
+    return bf16_to_f64(w) if w.dtype == np.uint16 else w.astype(np.float64)
 
 
 # --------------------------------------------------------------------------
@@ -195,14 +251,15 @@ def swiglu(gate, up) -> np.ndarray:
 def expert_ffn(xn_rows, gate_bits, up_bits, down_bits):
     """One expert on a block of rows: ``down @ (silu(gate @ xn) * (up @ xn))``.
 
-    ``gate_bits``/``up_bits`` are bf16 ``[inter, hidden]``, ``down_bits`` is
-    bf16 ``[hidden, inter]`` (row-major [out][in]).  Returns ``(h, d)``.
+    ``gate_bits``/``up_bits`` are ``[inter, hidden]``, ``down_bits`` is
+    ``[hidden, inter]`` (row-major [out][in]), each as bf16 bits or an MX
+    ``(codes, scales)`` pair (see ``weight_f64``).  Returns ``(h, d)``.
     """
     xn_rows = np.asarray(xn_rows, dtype=np.float64)
-    g = xn_rows @ bf16_to_f64(gate_bits).T
-    u = xn_rows @ bf16_to_f64(up_bits).T
+    g = xn_rows @ weight_f64(gate_bits).T
+    u = xn_rows @ weight_f64(up_bits).T
     h = swiglu(g, u)
-    d = h @ bf16_to_f64(down_bits).T
+    d = h @ weight_f64(down_bits).T
     return h, d
 
 
@@ -212,9 +269,10 @@ def expert_ffn(xn_rows, gate_bits, up_bits, down_bits):
 class Weights:
     """Host view of one layer's parameters.
 
-    ``expert(e)`` returns bf16 bit arrays ``(gate [I,H], up [I,H], down [H,I])``
-    of routed expert e; it may fetch lazily, so a full-size layer need not be
-    held in host memory.  ``shared`` is the same triple for the shared expert.
+    ``expert(e)`` returns ``(gate [I,H], up [I,H], down [H,I])`` of routed
+    expert e, each bf16 bits or an MX ``(codes, scales)`` pair; it may fetch
+    lazily, so a full-size layer need not be held in host memory.  ``shared``
+    is the same triple for the shared expert.  The router is bf16 bits.
     """
 
     def __init__(self, norm_w, router, sel_bias, tid2eid, expert, shared):

@@ -273,11 +273,82 @@ def check_special_functions():
     np.testing.assert_allclose(ref.swiglu([2.0], [3.0]), [3.0 * 2.0 / (1 + math.exp(-2.0))], rtol=1e-15)
 
 
+def check_mx_golden_codes():
+    """E4M3 and E8M0 codes against values worked by hand from the OCP MX
+    definitions (tests/golden/mx_codes.txt)."""
+    g = read_golden("mx_codes.txt")
+    for table, fn in (("e4m3", ref.e4m3_to_f64), ("e8m0", ref.e8m0_to_f64)):
+        for key, (code, want) in g[table].items():
+            got = float(fn(np.array([int(code)], np.uint8))[0])
+            if math.isnan(want):
+                assert math.isnan(got), (table, key)
+            else:
+                assert got == want and math.copysign(1, got) == math.copysign(1, want), (table, key, got, want)
+
+
+def check_mx_against_torch():
+    """All 256 E4M3 and E8M0 codes against torch's float8_e4m3fn and
+    float8_e8m0fnu conversions (a library routine, not the oracle's)."""
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    t = torch.from_numpy(codes)
+    for fn, dt in ((ref.e4m3_to_f64, torch.float8_e4m3fn), (ref.e8m0_to_f64, torch.float8_e8m0fnu)):
+        want = t.view(dt).to(torch.float64).numpy()
+        got = fn(codes)
+        assert np.array_equal(np.isnan(got), np.isnan(want))
+        ok = ~np.isnan(want)
+        assert np.array_equal(got[ok], want[ok]) and np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def check_mx_block_broadcast():
+    """A hand-built 2 x 64 MX matrix: every element is its code's value times
+    the scale of its own 32-element block of its own row."""
+    q = np.zeros((2, 64), np.uint8)
+    q[0, 0], q[0, 31], q[0, 32], q[0, 63] = 0x38, 0x40, 0x38, 0xC0    # 1, 2, 1, -2
+    q[1, 5], q[1, 40] = 0x3C, 0x01                                  # 1.5, 2^-9
+    sc = np.array([[127, 125], [130, 0]], np.uint8)                 # 1, 1/4 ; 8, 2^-127
+    w = ref.mx_dequant(q, sc)
+    want = np.zeros((2, 64))
+    want[0, 0], want[0, 31], want[0, 32], want[0, 63] = 1.0, 2.0, 0.25, -0.5
+    want[1, 5], want[1, 40] = 12.0, 2.0 ** -9 * 2.0 ** -127
+    assert np.array_equal(w, want)
+
+
+def check_mx_layer_equals_bf16_layer():
+    """A tiny layer whose experts are MX matrices gives bitwise the output of
+    the same layer with bf16 experts holding the same values.  The bf16 bits
+    are made by torch (E4M3 -> float32, times the power-of-two scale, ->
+    bfloat16: all exact here), independently of the oracle's decoders."""
+    import torch
+
+    cfg = gen.config(0)
+    hi, W, _ = tiny_weights(cfg)
+    (G, U, D), (sg, su, sd) = gen.mx_expert_weights(cfg, "cpu")
+
+    def bits(pair):
+        q, s = pair
+        v = q.view(torch.float8_e4m3fn).to(torch.float32)
+        scale = torch.exp2(s.to(torch.float32) - 127.0).repeat_interleave(gen.MX_BLOCK, dim=-1)
+        return gen.bf16_tensor_bits((v * scale).to(torch.bfloat16))
+
+    mx = lambda e: tuple(gen.mx_host((m[0][e], m[1][e])) for m in (G, U, D))
+    b16 = lambda e: tuple(bits((m[0][e], m[1][e])) for m in (G, U, D))
+    Wm = ref.Weights(hi.norm_w, hi.router, hi.sel_bias, None, mx, tuple(gen.mx_host(m) for m in (sg, su, sd)))
+    Wb = ref.Weights(hi.norm_w, hi.router, hi.sel_bias, None, b16, tuple(bits(m) for m in (sg, su, sd)))
+    x = np.random.default_rng(17).standard_normal((5, cfg.hidden))
+    a = ref.forward(x, None, ref.LAYER_SCORE, Wm, cfg.top_k, cfg.eps)["out"]
+    b = ref.forward(x, None, ref.LAYER_SCORE, Wb, cfg.top_k, cfg.eps)["out"]
+    assert np.array_equal(a, b) and np.abs(a).max() > 0
+
+
 ALL_CHECKS = [check_bf16_widening, check_matmul_triple_loop, check_micro_example, check_topk_rank_definition,
               check_topk_subset_enumeration, check_engineered_ties, check_weights_sum_to_one,
               check_hash_equals_score, check_zero_input_closed_form, check_rmsnorm_identities,
               check_scale_invariance, check_row_independence, check_expert_relabelling,
-              check_identical_experts, check_invalid_masking, check_special_functions]
+              check_identical_experts, check_invalid_masking, check_special_functions,
+              check_mx_golden_codes, check_mx_against_torch, check_mx_block_broadcast,
+              check_mx_layer_equals_bf16_layer]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -370,7 +441,52 @@ def _mut_hash_ignores_validity(logits, token_ids, tid2eid, top_k):
     return idx, w, np.ones_like(valid)
 
 
+def _mut_e4m3_bias8(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign, ex, man = c >> 7, (c >> 3) & 15, c & 7
+    mag = np.where(ex == 0, man / 8.0 * 2.0 ** -7, (1.0 + man / 8.0) * np.exp2(ex - 8.0))
+    mag = np.where((ex == 15) & (man == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+def _mut_e4m3_no_subnormals(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign, ex, man = c >> 7, (c >> 3) & 15, c & 7
+    mag = (1.0 + man / 8.0) * np.exp2(ex - 7.0)
+    mag = np.where((ex == 15) & (man == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+def _mut_e4m3_unsigned(codes):
+    return np.abs(_orig_e4m3(codes))
+
+
+def _mut_mx_block_64(codes, scales, block=32):
+    v = ref.e4m3_to_f64(codes)
+    sc = ref.e8m0_to_f64(scales)
+    return v * np.repeat(sc, 64, axis=-1)[..., :v.shape[-1]]
+
+
+def _mut_mx_scale_per_column(codes, scales, block=32):
+    v = ref.e4m3_to_f64(codes)
+    sc = ref.e8m0_to_f64(scales)
+    return v * np.tile(sc, (1,) * (sc.ndim - 1) + (block,))
+
+
+def _mut_e8m0_bias_128(scales):
+    s = np.asarray(scales, dtype=np.uint8).astype(np.int64)
+    return np.where(s == 255, np.nan, np.exp2(s - 128.0))
+
+
+_orig_e4m3 = ref.e4m3_to_f64
+
 MUTANTS = {
+    "e4m3_exponent_bias_8": ("e4m3_to_f64", _mut_e4m3_bias8),
+    "e4m3_subnormals_as_normals": ("e4m3_to_f64", _mut_e4m3_no_subnormals),
+    "e4m3_sign_dropped": ("e4m3_to_f64", _mut_e4m3_unsigned),
+    "e8m0_bias_128": ("e8m0_to_f64", _mut_e8m0_bias_128),
+    "mx_blocks_of_64": ("mx_dequant", _mut_mx_block_64),
+    "mx_scale_per_column_block": ("mx_dequant", _mut_mx_scale_per_column),
     "rmsnorm_eps_outside_root": ("rms_norm", _mut_eps_outside),
     "rmsnorm_one_plus_g": ("rms_norm", _mut_one_plus_g),
     "rmsnorm_sum_not_mean": ("rms_norm", _mut_sum_not_mean),
