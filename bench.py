@@ -37,7 +37,9 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer rows/sec at 1/4/512/8192 rows; HBM GB/s and MFMA % of peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix cores
-EXPERT_BYTES = lambda H, I: 3 * H * I * 2  # gate + up + down, bf16
+# bytes per expert weight: bf16, or an MXFP8 code plus 1/32 of its block's E8M0 scale
+WEIGHT_BYTES = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32}
+EXPERT_BYTES = lambda H, I, wb=2.0: 3 * H * I * wb  # gate + up + down
 
 
 def log(msg):
@@ -47,22 +49,26 @@ def log(msg):
 def alg_bytes(kernel, cfg, U, R):
     """Algorithmic HBM bytes of one launch: every touched weight once, plus
     activations in and out (U = distinct routed experts of the step; a
-    routed (expert, row) pair per slot, R*K of them)."""
+    routed (expert, row) pair per slot, R*K of them).  Launch names ending in
+    "_mx" read MXFP8 expert weights (the router stays bf16)."""
     H, I, E, K = cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
+    wb = WEIGHT_BYTES["bf16"]
+    if kernel.endswith("_mx"):
+        kernel, wb = kernel[:-3], WEIGHT_BYTES["mxfp8"]
     x = R * H * 4
     S = R * K
     if kernel == "dec_head":         # router + routing plan + shared gate/up
-        return E * H * 2 + 2 * I * H * 2 + 2 * x + H * 4 + R * E * 12 + R * (H + I) * 4
+        return E * H * 2 + 2 * I * H * wb + 2 * x + H * 4 + R * E * 12 + R * (H + I) * 4
     if kernel == "dec_gateup":       # shared down + routed gate/up
-        return H * I * 2 + U * 2 * I * H * 2 + R * (I + H) * 4 + R * K * (H + I) * 4
+        return H * I * wb + U * 2 * I * H * wb + R * (I + H) * 4 + R * K * (H + I) * 4
     if kernel == "dec_down_reduce":  # routed down + weighted reduce
-        return U * H * I * 2 + R * K * (I + 2 * H) * 4 + R * H * 4 + x
+        return U * H * I * wb + R * K * (I + 2 * H) * 4 + R * H * 4 + x
     if kernel == "dec1_router":      # one-row path: router, logits + keys + sigmoids + xn out
         return E * H * 2 + x + H * 4 + R * E * 4 + R * H * 4 + R * E * 16
     if kernel == "dec1_gateup":      # shared + routed gate/up, routing from the keys
-        return (U + 1) * 2 * I * H * 2 + R * E * 16 + R * H * 4 + (R * K + R) * I * 4 + R * K * 12
+        return (U + 1) * 2 * I * H * wb + R * E * 16 + R * H * 4 + (R * K + R) * I * 4 + R * K * 12
     if kernel == "dec1_down_reduce":  # routed + shared down + weighted reduce
-        return (U + 1) * H * I * 2 + (R * K + R) * I * 4 + (R * K + R) * 2 * H * 4 + R * H * 4
+        return (U + 1) * H * I * wb + (R * K + R) * I * 4 + (R * K + R) * 2 * H * 4 + R * H * 4
     if kernel == "pre_norm":         # x in, xn16 + xlo16 out
         return x + 2 * R * H * 2
     if kernel == "pre_router":       # xn16 + xlo16 in, logits + routing out, router weights once
@@ -70,15 +76,17 @@ def alg_bytes(kernel, cfg, U, R):
     if kernel == "pre_sort":         # row masks in; row lists, slot ranks and counts out
         return E * ((R + 31) // 32) * 4 + S * 4 * 2 + (E + 1) * 4
     if kernel == "gemm_gateup_swiglu":
-        return (U + 1) * 2 * I * H * 2 + (S + R) * H * 2 + (S + R) * I * 2
+        return (U + 1) * 2 * I * H * wb + (S + R) * H * 2 + (S + R) * I * 2
     if kernel == "gemm_down":        # routed experts: h16 in, d16 out
-        return U * H * I * 2 + S * I * 2 + S * H * 2
+        return U * H * I * wb + S * I * 2 + S * H * 2
     if kernel == "gemm_down_shared_reduce":  # shared expert + weighted reduce of d16
-        return H * I * 2 + R * I * 2 + S * H * 2 + R * H * 4 + S * 12
+        return H * I * wb + R * I * 2 + S * H * 2 + R * H * 4 + S * 12
     return None
 
 
 def alg_flops(kernel, cfg, R):
+    if kernel.endswith("_mx"):
+        kernel = kernel[:-3]
     H, I, E, K = cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
     S = R * K
     if kernel == "pre_router":       # hi and lo passes
@@ -99,12 +107,14 @@ def step_flops(cfg, R):
     return R * (2 * E * H + (K + 1) * 2 * 3 * H * I)
 
 
-def step_bytes(cfg, U, R):
+def step_bytes(cfg, U, R, fmt="bf16"):
     H, I, E = cfg.hidden, cfg.inter, cfg.experts
-    return (U + 1) * EXPERT_BYTES(H, I) + E * H * 2 + 2 * R * H * 4 + H * 4 + E * 4
+    return (U + 1) * EXPERT_BYTES(H, I, WEIGHT_BYTES[fmt]) + E * H * 2 + 2 * R * H * 4 + H * 4 + E * 4
 
 
 SUB_WORKLOADS = ("decode-cohort-r4-hash", "prefill-r512-score", "prefill-r8192-score-skewed")
+# the same workloads with MXFP8 expert weights (moe_ffn_forward_mxfp8)
+MX_WORKLOADS = ("decode-r1-score", "decode-cohort-r4-hash")
 
 
 def draw_layers(cfg, L):
@@ -119,9 +129,21 @@ def draw_layers(cfg, L):
     return out
 
 
-def bind_layers(cfg, big, L):
+def draw_layers_mx(cfg, L):
+    """Device MXFP8 expert weights of L layers ((codes, scales) per matrix)."""
+    from mixture_experts_ffn_rmsnorm_amd import inputs as gen
+
+    out = []
+    for l in range(L):
+        out.append(gen.mx_expert_weights(cfg, "cuda", layer=l))
+        log(f"layer {l} MXFP8 weights ready")
+    return out
+
+
+def bind_layers(cfg, big, L, fmt="bf16"):
     """Per workload: small per-layer parameters (router, bias with the hot
-    experts, norm weight, table) on the device, bound with the big weights."""
+    experts, norm weight, table) on the device, bound with the big weights.
+    Each layer is (host inputs, kept tensors, C weight struct, format)."""
     import numpy as np
     import torch
 
@@ -135,8 +157,15 @@ def bind_layers(cfg, big, L):
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         keep = [t(hi.norm_w), t(hi.router.view(np.int16)).view(torch.bfloat16), t(hi.sel_bias),
                 t(hi.tid2eid) if hi.tid2eid is not None else None, g, u, d, gs, us, ds]
-        layers.append((hi, keep, moe.make_weights(*keep)))
+        cw = moe.make_weights(*keep) if fmt == "bf16" else moe.make_mx_weights(*keep)
+        layers.append((hi, keep, cw, fmt))
     return layers
+
+
+def forward_fn(fmt):
+    from mixture_experts_ffn_rmsnorm_amd import moe
+
+    return moe.forward if fmt == "bf16" else moe.forward_mxfp8
 
 
 def time_workload(cfg, layers, steps, warmup, graph=False):
@@ -157,8 +186,11 @@ def time_workload(cfg, layers, steps, warmup, graph=False):
     ws = moe.alloc_workspace(dims, R)  # one workspace for every layer, as a model runs them
     torch.cuda.synchronize()
 
+    fmt = layers[0][3]
+    fwd = forward_fn(fmt)
+
     def step(i):
-        moe.forward(dims, x, tok, cfg.layer_kind, layers[i % L][2], out, ws)
+        fwd(dims, x, tok, cfg.layer_kind, layers[i % L][2], out, ws)
 
     log(f"{cfg.name}: warmup {warmup}")
     for i in range(warmup):
@@ -229,10 +261,10 @@ def time_workload(cfg, layers, steps, warmup, graph=False):
             k["hbm_frac"] = kb / secs / 1e9 / HBM_PEAK_GBPS
         if kf is not None:
             k["mfma_frac"] = kf / secs / 1e12 / MFMA_F16_PEAK_TFLOPS
-    sb, sf = step_bytes(cfg, u_mean, R), step_flops(cfg, R)
+    sb, sf = step_bytes(cfg, u_mean, R, fmt), step_flops(cfg, R)
     step_s = ms_per_step / 1e3
     rec = {
-        "rows": R, "rows_per_s": R / step_s, "ms_per_step": ms_per_step, "layers_cycled": L,
+        "rows": R, "rows_per_s": R / step_s, "ms_per_step": ms_per_step, "layers_cycled": L, "weights": fmt,
         "distinct_routed_experts": u_mean,
         "latency_us": {"median": float(np.median(lat_us)), "p10": float(np.percentile(lat_us, 10)),
                        "p90": float(np.percentile(lat_us, 90))},
@@ -244,7 +276,7 @@ def time_workload(cfg, layers, steps, warmup, graph=False):
     if graph:
         rec["graph"] = graph_chain(dims, cfg, layers, x, tok, ws, steps, ms_per_step)
     # one call of layer 0 for the parity check and the status word
-    moe.forward(dims, x, tok, cfg.layer_kind, layers[0][2], out, ws)
+    fwd(dims, x, tok, cfg.layer_kind, layers[0][2], out, ws)
     torch.cuda.synchronize()
     rec["status_flags"] = moe.status(ws)
     gpu0 = (out.cpu().numpy(), moe.routing_view(dims, R, ws)[1].cpu().numpy())
@@ -261,6 +293,8 @@ def main():
     ap.add_argument("--only", action="store_true",
                     help="time the named workload alone (no sub-records of the other full-size workloads)")
     ap.add_argument("--layers", type=int, default=None, help="distinct weight sets cycled (default 4 decode, 1 prefill)")
+    ap.add_argument("--weights", choices=("bf16", "mxfp8"), default="bf16",
+                    help="expert weight format of the named workload (the headline is bf16)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the headline's oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
@@ -286,8 +320,8 @@ def main():
     nl = lambda c: args.layers or (4 if c.rows <= 4 else 1)
     L = max([nl(cfg)] + [nl(c) for c in subs])
     log(f"workload {cfg.name} (+ {len(subs)} more): drawing {L} layers of weights on the GPU")
-    big = draw_layers(cfg, L)
-    layers = bind_layers(cfg, big, nl(cfg))
+    big = draw_layers(cfg, L) if args.weights == "bf16" else draw_layers_mx(cfg, L)
+    layers = bind_layers(cfg, big, nl(cfg), args.weights)
     rec, gpu0 = time_workload(cfg, layers, args.steps, args.warmup, graph=args.graph and cfg.rows <= 4)
     R = cfg.rows
     res = {
@@ -296,7 +330,8 @@ def main():
         "vs_baseline": None, "dtype": "f32" if R <= 4 else "f16", "data": "synthetic",
         "config": {"workload": cfg.name, "rows": R, "hidden": cfg.hidden, "experts": cfg.experts,
                    "top_k": cfg.top_k, "inter": cfg.inter, "shared_experts": 1,
-                   "layer_kind": "hash" if cfg.layer_kind == 1 else "score", "layers_cycled": rec["layers_cycled"],
+                   "layer_kind": "hash" if cfg.layer_kind == 1 else "score", "weights": args.weights,
+                   "layers_cycled": rec["layers_cycled"],
                    "distinct_routed_experts": rec["distinct_routed_experts"]},
         "roofline": rec["roofline"],
     }
@@ -315,6 +350,18 @@ def main():
         res["workloads"][c.name] = r_c
         sub_gpu[c.name] = (lay_c[0], g_c)
         torch.cuda.empty_cache()
+    mx_gpu = {}
+    if subs:
+        mx_cfgs = [gen.config(n) for n in MX_WORKLOADS]
+        if mx_cfgs:
+            big_mx = draw_layers_mx(cfg, max(nl(c) for c in mx_cfgs))
+            for c in mx_cfgs:
+                lay_c = bind_layers(c, big_mx, nl(c), "mxfp8")
+                r_c, g_c = time_workload(c, lay_c, args.steps, args.warmup, graph=args.graph and c.rows <= 4)
+                r_c["dtype"] = "f32"
+                r_c["layer_kind"] = "hash" if c.layer_kind == 1 else "score"
+                res["workloads"][c.name + "-mxfp8"] = r_c
+                mx_gpu[c.name + "-mxfp8"] = (c, lay_c[0], g_c)
     if not args.no_peaks:
         # the published peaks above are the roofline's; these are the same
         # two ceilings measured on this device, after the timed passes
@@ -331,6 +378,8 @@ def main():
         for c in subs:
             lay0, g_c = sub_gpu[c.name]
             res["workloads"][c.name]["cpu_baseline"] = oracle_full_batch(c, lay0, g_c)
+        for name, (c, lay0, g_c) in mx_gpu.items():
+            res["workloads"][name]["cpu_baseline"] = oracle_full_batch(c, lay0, g_c)
     print(json.dumps(res), flush=True)
 
 
@@ -346,9 +395,11 @@ def graph_chain(dims, cfg, layers, x, tok, ws, reps, eager_ms):
     L = len(layers)
     bufs = [x] + [torch.empty_like(x) for _ in range(L)]
 
+    fwd = forward_fn(layers[0][3])
+
     def chain():
         for l in range(L):
-            moe.forward(dims, bufs[l], tok, cfg.layer_kind, layers[l][2], bufs[l + 1], ws)
+            fwd(dims, bufs[l], tok, cfg.layer_kind, layers[l][2], bufs[l + 1], ws)
 
     for _ in range(3):
         chain()
@@ -381,17 +432,23 @@ def _oracle_weights(cfg, layer):
     from mixture_experts_ffn_rmsnorm_amd import inputs as gen
     from oracle import moe_ref as ref
 
-    hi, keep, _ = layer
+    hi, keep, _, fmt = layer
     g, u, d, gs, us, ds = keep[4:]
     cache = {}
+    if fmt == "bf16":
+        host = gen.bf16_tensor_bits
+        pick = lambda m, e: m[e]
+    else:  # MXFP8: (codes, scales) pairs
+        host = gen.mx_host
+        pick = lambda m, e: (m[0][e], m[1][e])
 
     def expert(e):
         if e not in cache:
-            cache[e] = tuple(gen.bf16_tensor_bits(m[e]) for m in (g, u, d))
+            cache[e] = tuple(host(pick(m, e)) for m in (g, u, d))
         return cache[e]
 
     return ref.Weights(hi.norm_w, hi.router, hi.sel_bias, hi.tid2eid, expert,
-                       tuple(gen.bf16_tensor_bits(m) for m in (gs, us, ds))), cache
+                       tuple(host(m) for m in (gs, us, ds))), cache
 
 
 def _threads():

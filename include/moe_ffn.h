@@ -182,6 +182,45 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
                     int layer_kind, const moe_weights_t* w, float* out, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* ---- block-scaled 8-bit expert weights (OCP Microscaling MXFP8) --------
+ * ffn_forward.rs binds the expert matrices (ffn_{gate,up,down}_exps,
+ * ffn_{gate,up,down}_shexp) as GGML-typed raw matrices, i.e. in whatever
+ * quantised type the model file holds; the library's second weight format
+ * is OCP MXFP8: one FP8 E4M3 code per weight and one E8M0 power-of-two
+ * scale per MOE_MX_BLOCK consecutive weights of a row (along the input
+ * dimension), value = e4m3(code) * 2^(scale - 127).  (The pages' only MXFP8
+ * step, the attention page's fake quantisation of activations, uses blocks
+ * of 64; these are weights, in the OCP block of 32.)  The router stays
+ * bf16. */
+#define MOE_MX_BLOCK 32
+
+typedef struct moe_mx_matrix {
+  const uint8_t* codes;   /* E4M3 codes, [out][in] (routed: [experts][out][in]) */
+  const uint8_t* scales;  /* E8M0 codes, [out][in / 32] (routed: [experts][out][in / 32]) */
+} moe_mx_matrix_t;
+
+/* The parameters of moe_weights_t with the six expert matrices in MXFP8.
+ * All DEVICE pointers, caller-owned, read-only, 16-byte aligned; shapes as
+ * in moe_weights_t (gate/up [inter][hidden], down [hidden][inter]). */
+typedef struct moe_mx_weights {
+  const float* norm_w;
+  const uint16_t* router;
+  const float* sel_bias;
+  const int32_t* tid2eid;
+  moe_mx_matrix_t gate_exps, up_exps, down_exps;
+  moe_mx_matrix_t gate_sh, up_sh, down_sh;
+} moe_mx_weights_t;
+
+/* moe_ffn_forward with MXFP8 expert weights: same arguments, workspace
+ * (moe_ffn_workspace_bytes), routing, status and bitwise reproducibility;
+ * each weight is its decoded value exactly (E4M3 and E8M0 values are exact
+ * in f32).  Reads half the expert bytes of the bf16 layer.
+ * Errors: as moe_ffn_forward; MOE_EINVAL also for a missing or misaligned
+ * code or scale array; MOE_EUNSUPPORTED for rows > 4 (decode shapes only). */
+int moe_ffn_forward_mxfp8(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,
+                          int layer_kind, const moe_mx_weights_t* w, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* moe_ffn_forward without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Same arguments, kernels and

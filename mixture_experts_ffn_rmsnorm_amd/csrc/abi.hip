@@ -55,6 +55,22 @@ int check_weights(const moe_dims_t* d, int layer_kind, const moe_weights_t* w, c
   return MOE_OK;
 }
 
+// The block-scaled weight struct checked like the bf16 one: the small
+// parameters are shared, every code and scale array must be present and
+// 16-byte aligned.  *common receives the small parameters (and the code
+// arrays in the expert slots, only for the presence checks).
+int check_mx_weights(const moe_mx_weights_t* w, moe_weights_t* common) {
+  if (!w) return MOE_EINVAL;
+  const moe_mx_matrix_t* m[] = {&w->gate_exps, &w->up_exps, &w->down_exps, &w->gate_sh, &w->up_sh, &w->down_sh};
+  for (const moe_mx_matrix_t* p : m)
+    if (!p->codes || !p->scales || !aligned(p->codes, 16) || !aligned(p->scales, 16)) return MOE_EINVAL;
+  *common = moe_weights_t{w->norm_w, w->router, w->sel_bias, w->tid2eid,
+                          (const uint16_t*)w->gate_exps.codes, (const uint16_t*)w->up_exps.codes,
+                          (const uint16_t*)w->down_exps.codes, (const uint16_t*)w->gate_sh.codes,
+                          (const uint16_t*)w->up_sh.codes, (const uint16_t*)w->down_sh.codes};
+  return MOE_OK;
+}
+
 struct TimerRec {
   const char* name;
   hipEvent_t start, stop;
@@ -140,9 +156,12 @@ int check_forward_args(const moe_dims_t* d, const float* x, const int32_t* token
 }
 
 // The forward with its intermediates carved from `workspace` (already
-// checked: at least L.total bytes, 256-byte aligned).
+// checked: at least L.total bytes, 256-byte aligned).  With `mx` the expert
+// matrices are the block-scaled ones there (w then supplies only the small
+// parameters).
 int forward_in(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
-               const moe_weights_t* w, float* out, void* workspace, const Layout& L, void* stream) {
+               const moe_weights_t* w, const moe_mx_weights_t* mx, float* out, void* workspace, const Layout& L,
+               void* stream) {
   char* ws = (char*)workspace;
   FwdArgs a;
   memset(&a, 0, sizeof(a));
@@ -166,6 +185,22 @@ int forward_in(const moe_dims_t* d, const float* x, const int32_t* token_ids, in
   a.gate_sh = w->gate_sh;
   a.up_sh = w->up_sh;
   a.down_sh = w->down_sh;
+  if (mx) {
+    a.gate = a.up = a.down = a.gate_sh = a.up_sh = a.down_sh = nullptr;
+    a.mx = 1;
+    a.gate_q = mx->gate_exps.codes;
+    a.up_q = mx->up_exps.codes;
+    a.down_q = mx->down_exps.codes;
+    a.gate_sh_q = mx->gate_sh.codes;
+    a.up_sh_q = mx->up_sh.codes;
+    a.down_sh_q = mx->down_sh.codes;
+    a.gate_s = mx->gate_exps.scales;
+    a.up_s = mx->up_exps.scales;
+    a.down_s = mx->down_exps.scales;
+    a.gate_sh_s = mx->gate_sh.scales;
+    a.up_sh_s = mx->up_sh.scales;
+    a.down_sh_s = mx->down_sh.scales;
+  }
   a.out = out;
   a.status = (uint32_t*)(ws + L.status);
   a.sync = (DecodeSync*)(ws + L.status + 64);  // both paths: the status block
@@ -270,7 +305,7 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
   const int rc = check_forward_args(d, x, token_ids, rows, layer_kind, w, out, &L);
   if (rc) return rc;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
-  return forward_in(d, x, token_ids, rows, layer_kind, w, out, workspace, L, stream);
+  return forward_in(d, x, token_ids, rows, layer_kind, w, nullptr, out, workspace, L, stream);
 }
 
 int moe_ffn_forward_noalloc(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,
@@ -282,7 +317,23 @@ int moe_ffn_forward_noalloc(const moe_dims_t* d, const float* x, const int32_t* 
   void* ws = nullptr;
   rc = scratch_for((hipStream_t)stream, L.logits, &ws);  // the status block precedes the logits
   if (rc) return rc;
-  return forward_in(d, x, token_ids, rows, layer_kind, w, out, ws, L, stream);
+  return forward_in(d, x, token_ids, rows, layer_kind, w, nullptr, out, ws, L, stream);
+}
+
+int moe_ffn_forward_mxfp8(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
+                          const moe_mx_weights_t* w, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  moe_weights_t common;
+  int rc = check_dims_rows(d, rows);
+  if (rc) return rc;
+  rc = check_mx_weights(w, &common);
+  if (rc) return rc;
+  Layout L;
+  rc = check_forward_args(d, x, token_ids, rows, layer_kind, &common, out, &L);
+  if (rc) return rc;
+  if (rows > kDecodeMaxRows) return MOE_EUNSUPPORTED;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
+  return forward_in(d, x, token_ids, rows, layer_kind, &common, w, out, workspace, L, stream);
 }
 
 int moe_route(const moe_dims_t* d, const float* logits, const int32_t* token_ids, int64_t rows, int layer_kind,

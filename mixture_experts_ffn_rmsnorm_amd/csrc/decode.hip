@@ -28,6 +28,8 @@
 // (rms_norm -> MoE gate -> route -> sanitize -> routed/shared gate, up ->
 // swiglu -> routed/shared down -> weighted reduce); the page's rows*top_k
 // one-expert matvecs become one pass over the batch's distinct experts.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -41,60 +43,148 @@ constexpr int kDnRows = 32;     // hidden rows per down block: 4 waves x 8
 // hidden rows per shared-down block of the gate/up launch (4 waves x 4): its
 // H/16 blocks give every compute unit one of them besides its routed blocks
 constexpr int kSdRows = 16;
-// Spin limit of an in-kernel wait on another workgroup's flag or counter
-// (each poll is a device-scope load, about a microsecond: roughly 0.25 s in
-// all); reaching it sets MOE_FLAG_SYNC_TIMEOUT instead of hanging.
-constexpr int kMaxPolls = 1 << 18;
+// Weight rows in flight per wave: two, multiplied as a pair (one LDS read
+// of an activation value serves both weight rows).  Measured against one
+// row at a time: bf16 one row 71.5-72.1 vs 72.9-73.9 us, four rows 209.6
+// vs 213.6-216.0 us; 8-bit weights four rows 172.9 us with two rows in
+// flight vs 177.7 us with four (four in flight without pairs: 83 us at one
+// row).
+template <bool MX> constexpr int kNbuf = 2;
+template <bool MX> constexpr bool kPair = true;
 
-// One wavefront walks a sequence of whole bf16 weight rows (global) and dots
-// each with up to 4 f32 activation rows in LDS (row r at act + r*LEN).  Each
-// row is read front to back as contiguous 1 KiB wave loads; NBUF rows are in
-// flight (the next ones load while the current one is multiplied), which
-// keeps the DRAM streams long.  Lane l covers 8 consecutive columns of every
-// 512-column chunk; lanes past the end of a partial chunk (LEN not a
-// multiple of 512) neither load nor add.  rowptr(j) gives row j's address;
-// pre() runs once after the first NBUF rows are requested (staging the
-// activations there overlaps it with the first weight fetch; it must end
-// with a barrier if it fills LDS); sink(j, part) receives each lane's
-// partial sums part[0..nr) of row j (reduce them with wave_sum); it must not
-// store to global memory: loads and stores share one wait counter, and a
-// store among the weight loads makes every later wait drain them all.
-// nrows is a positive multiple of NBUF.
-template <int LEN, int NBUF, class RowPtr, class Pre, class Sink>
-__device__ __forceinline__ void stream_rows(int nrows, RowPtr rowptr, const float* act, int nr, Pre pre, Sink sink) {
+// An expert matrix [out][LEN] in either weight format: bf16 values, or
+// block-scaled 8-bit values (E4M3 codes [out][LEN] with one E8M0 scale per
+// 32 columns, [out][LEN/32]).  WRow is one row of it.
+struct WMat {
+  const void* w;
+  const uint8_t* s;  // MX only
+};
+struct WRow {
+  const void* w;
+  const uint8_t* s;
+};
+template <bool MX, int LEN>
+__device__ __forceinline__ WRow wrow(const WMat& m, int64_t i) {
+  if constexpr (MX) return WRow{(const uint8_t*)m.w + i * LEN, m.s + i * (LEN / 32)};
+  else return WRow{(const uint16_t*)m.w + i * LEN, nullptr};
+}
+// Expert e's matrix of `elems` values from the forward's arguments.
+template <bool MX>
+__device__ __forceinline__ WMat expert_mat(const uint16_t* bf, const uint8_t* q, const uint8_t* s, int64_t e,
+                                           int64_t elems) {
+  if constexpr (MX) return WMat{q + e * elems, s + e * (elems / 32)};
+  else return WMat{bf + e * elems, nullptr};
+}
+
+// E8M0 scale code -> f32: 2^(c-127) (the f32 exponent field itself for c in
+// 1..254; 2^-127, a subnormal, for 0; NaN for 255).
+__device__ __forceinline__ float e8m0_f32(uint32_t c) {
+  return c == 0 ? __uint_as_float(0x00400000u) : (c == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(c << 23));
+}
+// Eight E4M3 codes (little-endian bytes of q) -> eight floats, exactly.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void unpack8_e4m3(const uint2& q, float* f) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.x, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
+  f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y; f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load_stream8(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
+  return make_uint2(v.x, v.y);
+}
+
+// One wavefront walks a sequence of whole weight rows (global) and dots each
+// with up to 4 f32 activation rows in LDS (row r at act + r*LEN).  Each row
+// is read front to back as contiguous wave loads (1 KiB for bf16, 512 B for
+// 8-bit codes); NBUF rows are in flight (the next ones load while the
+// current one is multiplied), which keeps the DRAM streams long.  Lane l
+// covers 8 consecutive columns of every 512-column chunk; lanes past the end
+// of a partial chunk (LEN not a multiple of 512) neither load nor add.  With
+// MX the row's scale bytes come with one 4-byte load per lane, and chunk c's
+// lane takes the scale of its 32-column block from the lane holding it
+// (columns c*512 + 8l.. lie in block 16c + l/4); the lane's 8-term partial
+// of the chunk is multiplied by it (a power of two: exact) and added.
+// rowsrc(j) gives row j (WRow); pre() runs once after the first NBUF rows
+// are requested (staging the activations there overlaps it with the first
+// weight fetch; it must end with a barrier if it fills LDS); sink(j, part)
+// receives each lane's partial sums part[0..nr) of row j (reduce them with
+// wave_sum); it must not store to global memory: loads and stores share one
+// wait counter, and a store among the weight loads makes every later wait
+// drain them all.  nrows is a positive multiple of NBUF.
+// With PAIR rows are multiplied two at a time, so each activation value read
+// from LDS serves both (with several activation rows and half-size 8-bit
+// weight rows the LDS reads, not the weight stream, bound the loop
+// otherwise).
+template <int LEN, int NBUF, bool MX, bool PAIR, class RowSrc, class Pre, class Sink>
+__device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const float* act, int nr, Pre pre, Sink sink) {
   static_assert(LEN % 256 == 0, "row length must be a multiple of 256");
+  static_assert(!PAIR || NBUF % 2 == 0, "pairs of rows in flight");
   constexpr int NCH = (LEN + 511) / 512;
   const int lane = threadIdx.x & (kWave - 1);
   const bool full = LEN % 512 == 0 || lane * 8 < LEN % 512;  // active in the last chunk
-  uint4 q[NBUF][NCH];
+  using Chunk = typename std::conditional<MX, uint2, uint4>::type;
+  Chunk q[NBUF][NCH];
+  uint32_t sw[NBUF];  // MX: this lane's 4 scale bytes of the row
   auto load_row = [&](int b, int j) {
-    const uint16_t* p = rowptr(j) + lane * 8;
+    const WRow src = rowsrc(j);
+    if constexpr (MX) {
+      const uint8_t* p = (const uint8_t*)src.w + lane * 8;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      if (c < NCH - 1 || full) q[b][c] = load_stream(p + c * 512);
+      for (int c = 0; c < NCH; ++c)
+        if (c < NCH - 1 || full) q[b][c] = load_stream8(p + c * 512);
+      sw[b] = lane * 4 < LEN / 32 ? *(const uint32_t*)(src.s + lane * 4) : 0u;
+    } else {
+      const uint16_t* p = (const uint16_t*)src.w + lane * 8;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        if (c < NCH - 1 || full) q[b][c] = load_stream(p + c * 512);
+    }
   };
-  auto dot_row = [&](int b, float (&part)[4]) {
+  // rows b .. b+NR-1 (NR = 1, or 2 with PAIR) against the activations
+  auto dot_rows = [&](int b, auto nr_c, float (&part)[2][4]) {
+    constexpr int NR = decltype(nr_c)::value;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part[r] = 0.f;
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[i][r] = 0.f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
+      float sc[NR];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        sc[i] = 1.f;
+        if constexpr (MX) {  // every lane takes part in the shuffle
+          const uint32_t w = (uint32_t)__shfl((int)sw[b + i], c * 4 + (lane >> 4), kWave);
+          sc[i] = e8m0_f32((w >> (8 * ((lane >> 2) & 3))) & 255u);
+        }
+      }
       if (c < NCH - 1 || full) {
-        float f[8];
-        unpack8(q[b][c], f);
+        float f[NR][8];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          if constexpr (MX) unpack8_e4m3(q[b + i][c], f[i]);
+          else unpack8(q[b + i][c], f[i]);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (r < nr) {
             const float4* xp = (const float4*)(act + r * LEN + c * 512 + lane * 8);
             const float4 u = xp[0], v = xp[1];
-            float s = part[r];
-            s = fmaf(f[0], u.x, s); s = fmaf(f[1], u.y, s); s = fmaf(f[2], u.z, s); s = fmaf(f[3], u.w, s);
-            s = fmaf(f[4], v.x, s); s = fmaf(f[5], v.y, s); s = fmaf(f[6], v.z, s); s = fmaf(f[7], v.w, s);
-            part[r] = s;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+              float s = MX ? 0.f : part[i][r];
+              s = fmaf(f[i][0], u.x, s); s = fmaf(f[i][1], u.y, s); s = fmaf(f[i][2], u.z, s); s = fmaf(f[i][3], u.w, s);
+              s = fmaf(f[i][4], v.x, s); s = fmaf(f[i][5], v.y, s); s = fmaf(f[i][6], v.z, s); s = fmaf(f[i][7], v.w, s);
+              part[i][r] = MX ? fmaf(sc[i], s, part[i][r]) : s;
+            }
           }
         }
       }
     }
   };
+  constexpr int STEP = PAIR ? 2 : 1;
+  using StepC = std::integral_constant<int, STEP>;
 #pragma unroll
   for (int b = 0; b < NBUF; ++b) load_row(b, b);
   pre();
@@ -107,19 +197,22 @@ __device__ __forceinline__ void stream_rows(int nrows, RowPtr rowptr, const floa
 #pragma unroll 1
   for (int j0 = 0; j0 + NBUF < nrows; j0 += NBUF) {
 #pragma unroll
-    for (int b = 0; b < NBUF; ++b) {
-      float part[4];
-      dot_row(b, part);
-      load_row(b, j0 + b + NBUF);
-      sink(j0 + b, part);
+    for (int b = 0; b < NBUF; b += STEP) {
+      float part[2][4];
+      dot_rows(b, StepC{}, part);
+#pragma unroll
+      for (int i = 0; i < STEP; ++i) load_row(b + i, j0 + b + i + NBUF);
+#pragma unroll
+      for (int i = 0; i < STEP; ++i) sink(j0 + b + i, part[i]);
     }
   }
   // last group: no further loads
 #pragma unroll
-  for (int b = 0; b < NBUF; ++b) {
-    float part[4];
-    dot_row(b, part);
-    sink(nrows - NBUF + b, part);
+  for (int b = 0; b < NBUF; b += STEP) {
+    float part[2][4];
+    dot_rows(b, StepC{}, part);
+#pragma unroll
+    for (int i = 0; i < STEP; ++i) sink(nrows - NBUF + b + i, part[i]);
   }
 }
 
@@ -231,9 +324,9 @@ __device__ __forceinline__ void sync_stores() { __builtin_amdgcn_s_waitcnt(0); }
 // so the blocks working on one expert at the same time read neighbouring
 // rows; wave w streams gate_i then up_i for every fourth of them.  h32 rows
 // hout..hout+nr-1 receive silu(gate . x) * (up . x).
-template <int H, int I, int PAIRS, int NBUF, class Pre>
-__device__ __forceinline__ void gateup_tile(const uint16_t* gbase, const uint16_t* ubase, const float* xs, int nr,
-                                            int x, int tiles, float* h32, int hout, Pre pre) {
+template <int H, int I, int PAIRS, int NBUF, bool MX, bool PAIR, class Pre>
+__device__ __forceinline__ void gateup_tile(const WMat& gm, const WMat& um, const float* xs, int nr, int x, int tiles,
+                                            float* h32, int hout, Pre pre) {
   constexpr int W = kThreads / kWave, PPW = PAIRS / W;  // pairs per wave
   static_assert(PPW * 4 <= kWave, "one lane per result");
   __shared__ float s_res[W * PPW * 4];  // results wait here until the stream ends
@@ -241,7 +334,7 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* gbase, const uint16_
   float* res = s_res + wv * PPW * 4;
   float g[4];
   auto row_of = [&](int j) { return x + (wv + (j >> 1) * W) * tiles; };
-  auto rowptr = [&](int j) { return ((j & 1) ? ubase : gbase) + (int64_t)row_of(j) * H; };
+  auto rowsrc = [&](int j) { return wrow<MX, H>((j & 1) ? um : gm, row_of(j)); };
   auto sink = [&](int j, const float (&part)[4]) {
     if (!(j & 1)) {
 #pragma unroll
@@ -258,7 +351,7 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* gbase, const uint16_
     }
   };
   static_assert((2 * PPW) % NBUF == 0, "whole groups of rows in flight");
-  stream_rows<H, NBUF>(2 * PPW, rowptr, xs, nr, pre, sink);
+  stream_rows<H, NBUF, MX, PAIR>(2 * PPW, rowsrc, xs, nr, pre, sink);
   const int p = lane >> 2, r = lane & 3;
   if (p < PPW && r < nr) store_wt(&h32[(int64_t)(hout + r) * I + row_of(2 * p)], res[lane]);
 }
@@ -646,16 +739,16 @@ __device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R) {
 // x + (i * mul + add) * stride, so concurrent blocks read neighbouring rows
 // (x, x + stride, ... for mul 1; every other one of them, from `add`, for
 // mul 2).  d32 rows ent..ent+nr-1 receive the results (written through).
-template <int H, int I, int ROWS, class Pre>
-__device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs, int nr, int x, int stride, int mul,
-                                          int add, float* d32, int ent, Pre pre) {
+template <int H, int I, int ROWS, int NBUF, bool MX, bool PAIR, class Pre>
+__device__ __forceinline__ void down_tile(const WMat& wm, const float* hs, int nr, int x, int stride, int mul, int add,
+                                          float* d32, int ent, Pre pre) {
   constexpr int W = kThreads / kWave, RPW = ROWS / W;  // rows per wave
-  static_assert(RPW * 4 <= kWave && RPW % 2 == 0, "one lane per result; whole row pairs in flight");
+  static_assert(RPW * 4 <= kWave && RPW % NBUF == 0, "one lane per result; whole row groups in flight");
   __shared__ float s_res[ROWS * 4];  // results wait here until the stream ends
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   float* res = s_res + wv * RPW * 4;
   auto row_of = [&](int j) { return x + ((wv + j * W) * mul + add) * stride; };
-  auto rowptr = [&](int j) { return wbase + (int64_t)row_of(j) * I; };
+  auto rowsrc = [&](int j) { return wrow<MX, I>(wm, row_of(j)); };
   auto sink = [&](int j, const float (&part)[4]) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -665,7 +758,7 @@ __device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs
       }
     }
   };
-  stream_rows<I, 2>(RPW, rowptr, hs, nr, pre, sink);
+  stream_rows<I, NBUF, MX, PAIR>(RPW, rowsrc, hs, nr, pre, sink);
   const int j = lane >> 2, r = lane & 3;
   if (j < RPW && r < nr) store_wt(&d32[(int64_t)(ent + r) * H + row_of(j)], res[lane]);
 }
@@ -684,7 +777,7 @@ __device__ __forceinline__ void down_tile(const uint16_t* wbase, const float* hs
 //   Shared gate/up block: RMSNorm into LDS, then 8 inter rows of the shared
 //   expert's SwiGLU output for every row; its streaming covers the router's
 //   latency and the routing.  The first of these blocks publishes xn.
-template <int H, int I, bool kRouterOnly>
+template <int H, int I, bool kRouterOnly, bool MX>
 __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [R][H]
   __shared__ int s_idx[kDecodeMaxSlots];
@@ -706,7 +799,9 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
         for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
     };
     stage();
-    gateup_tile<H, I, kShRows, 2>(a.gate_sh, a.up_sh, xs, R, x, nsh, a.h32, kDecodeMaxSlots, [] {});
+    gateup_tile<H, I, kShRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.gate_sh, a.gate_sh_q, a.gate_sh_s, 0, (int64_t)I * H),
+                                      expert_mat<MX>(a.up_sh, a.up_sh_q, a.up_sh_s, 0, (int64_t)I * H), xs, R, x, nsh,
+                                      a.h32, kDecodeMaxSlots, [] {});
     return;
   }
   // router block: expert e = 4b + w per wave.  The weight row's loads go out
@@ -787,7 +882,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
 // x + H/16, ... of the shared expert's down projection -> d32 shared rows.
 // Gate/up block (u, x): inter rows x, x + I/16, ... of the plan's u-th
 // expert -> h32.
-template <int H, int I>
+template <int H, int I, bool MX>
 __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [nr][H] activations, or [R][I] shared h
   constexpr int nsd = H / kSdRows, gut = I / kGuRows;
@@ -796,7 +891,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
     const float* src[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(kDecodeMaxSlots + (j < a.R ? j : 0)) * I;
-    down_tile<H, I, kSdRows>(a.down_sh, xs, a.R, b, H / kSdRows, 1, 0, a.d32, kDecodeMaxSlots,
+    down_tile<H, I, kSdRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down_sh, a.down_sh_q, a.down_sh_s, 0, (int64_t)H * I), xs, a.R, b,
+                                 H / kSdRows, 1, 0, a.d32, kDecodeMaxSlots,
                              [&]() { stage_rows<I>(xs, src, a.R); });
     return;
   }
@@ -807,7 +903,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
   const float* src[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) src[j] = a.xn32 + (int64_t)plan_row(P, g.begin + (j < g.nr ? j : 0), a.R) * H;
-  gateup_tile<H, I, kGuRows, 2>(a.gate + (int64_t)g.expert * I * H, a.up + (int64_t)g.expert * I * H, xs, g.nr, x, gut,
+  gateup_tile<H, I, kGuRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.gate, a.gate_q, a.gate_s, g.expert, (int64_t)I * H),
+                                    expert_mat<MX>(a.up, a.up_q, a.up_s, g.expert, (int64_t)I * H), xs, g.nr, x, gut,
                              a.h32, g.begin, [&]() { stage_rows<H>(xs, src, g.nr); });
 }
 
@@ -822,7 +919,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
 // microseconds of work that every block repeats, against the
 // cross-workgroup round trips of a shared plan.  At full size this is 256 +
 // 6 * 128 blocks, one shared and three routed per compute unit.
-template <int H, int I>
+template <int H, int I, bool MX>
 __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [H] normalised row
   __shared__ int s_idx[kDecodeMaxSlots];
@@ -836,7 +933,9 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
   if (b < nsh) {  // shared gate/up block
     // the row count stays a run-time value (a.R = 1 here): with a constant 1
     // the compiler keeps the whole activation row in registers
-    gateup_tile<H, I, kShRows, 2>(a.gate_sh, a.up_sh, xs, a.R, b, nsh, a.h32, kDecodeMaxSlots,
+    gateup_tile<H, I, kShRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.gate_sh, a.gate_sh_q, a.gate_sh_s, 0, (int64_t)I * H),
+                                      expert_mat<MX>(a.up_sh, a.up_sh_q, a.up_sh_s, 0, (int64_t)I * H), xs, a.R, b, nsh,
+                                      a.h32, kDecodeMaxSlots,
                                   [&]() { stage_rows<H>(xs, src, a.R); });
     return;
   }
@@ -849,7 +948,8 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
   if (u >= plan_ngroups(&P)) return;
   const PlanGroup g = plan_group(&P, u, a.E);
   const int nr = g.nr < a.R ? g.nr : a.R;  // LDS holds a.R rows
-  gateup_tile<H, I, kGuRows, 2>(a.gate + (int64_t)g.expert * I * H, a.up + (int64_t)g.expert * I * H, xs, nr, x, gut,
+  gateup_tile<H, I, kGuRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.gate, a.gate_q, a.gate_s, g.expert, (int64_t)I * H),
+                                    expert_mat<MX>(a.up, a.up_q, a.up_s, g.expert, (int64_t)I * H), xs, nr, x, gut,
                                 a.h32, g.begin, [&]() { stage_rows<H>(xs, src, nr); });
 }
 
@@ -868,7 +968,7 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
 // output is bitwise reproducible.  No block waits for another.  Without
 // kShared and with no valid routed expert at all, the u = 0 blocks write
 // out = shared down.
-template <int H, int I, bool kShared>
+template <int H, int I, bool kShared, bool MX>
 __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   __shared__ float hs[kDecodeMaxRows * I];
   __shared__ int s_er[kDecodeMaxSlots];    // the plan's entry rows and weights, for the reduce
@@ -894,7 +994,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
       const float* src[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(kDecodeMaxSlots + (j < R ? j : 0)) * I;
-      down_tile<H, I, kDnRows / 2>(a.down_sh, hs, R, x, dnt, 2, u - G, a.d32, kDecodeMaxSlots, [&]() {
+      down_tile<H, I, kDnRows / 2, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down_sh, a.down_sh_q, a.down_sh_s, 0, (int64_t)H * I), hs, R, x,
+                                       dnt, 2, u - G, a.d32, kDecodeMaxSlots, [&]() {
         stage_entries();
         stage_rows<I>(hs, src, R);  // ends with a barrier
       });
@@ -904,7 +1005,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
       const float* src[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
-      down_tile<H, I, kDnRows>(a.down + (int64_t)g.expert * H * I, hs, g.nr, x, dnt, 1, 0, a.d32, g.begin, [&]() {
+      down_tile<H, I, kDnRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down, a.down_q, a.down_s, g.expert, (int64_t)H * I), hs, g.nr, x,
+                                   dnt, 1, 0, a.d32, g.begin, [&]() {
         stage_entries();
         stage_rows<I>(hs, src, g.nr);  // ends with a barrier
       });
@@ -945,7 +1047,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   a.out[(int64_t)r * H + h] = o;
 }
 
-template <int H, int I>
+template <int H, int I, bool MX>
 hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   static_assert(H / kDnRows <= kDecodeMaxTiles, "too many down tiles");
   FwdArgs args = a;
@@ -954,30 +1056,30 @@ hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   if (a.R == 1) {
     // one row: router launch, then gate/up blocks that route for
     // themselves, then routed + shared down with the reduce
-    err = launch("dec1_router", (const void*)k_dec_head<H, I, true>, dim3((a.E + 3) / 4), dim3(kThreads),
-                 (size_t)H * 4, s, &args);
-    if (err != hipSuccess) return err;
-    err = launch("dec1_gateup", (const void*)k_dec1_gateup<H, I>, dim3(I / kShRows + gmax * (I / kGuRows)),
+    err = launch(MX ? "dec1_router_mx" : "dec1_router", (const void*)k_dec_head<H, I, true, MX>, dim3((a.E + 3) / 4),
                  dim3(kThreads), (size_t)H * 4, s, &args);
     if (err != hipSuccess) return err;
-    return launch("dec1_down_reduce", (const void*)k_dec_down<H, I, true>, dim3(H / kDnRows, gmax + 2),
-                  dim3(kThreads), 0, s, &args);
+    err = launch(MX ? "dec1_gateup_mx" : "dec1_gateup", (const void*)k_dec1_gateup<H, I, MX>,
+                 dim3(I / kShRows + gmax * (I / kGuRows)), dim3(kThreads), (size_t)H * 4, s, &args);
+    if (err != hipSuccess) return err;
+    return launch(MX ? "dec1_down_reduce_mx" : "dec1_down_reduce", (const void*)k_dec_down<H, I, true, MX>,
+                  dim3(H / kDnRows, gmax + 2), dim3(kThreads), 0, s, &args);
   }
-  err = launch("dec_head", (const void*)k_dec_head<H, I, false>, dim3((a.E + 3) / 4 + I / kShRows),
-               dim3(kThreads), (size_t)a.R * H * 4, s, &args);
+  err = launch(MX ? "dec_head_mx" : "dec_head", (const void*)k_dec_head<H, I, false, MX>,
+               dim3((a.E + 3) / 4 + I / kShRows), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  err = launch("dec_gateup", (const void*)k_dec_gateup<H, I>, dim3(H / kSdRows + gmax * (I / kGuRows)),
-               dim3(kThreads), (size_t)a.R * H * 4, s, &args);
+  err = launch(MX ? "dec_gateup_mx" : "dec_gateup", (const void*)k_dec_gateup<H, I, MX>,
+               dim3(H / kSdRows + gmax * (I / kGuRows)), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  return launch("dec_down_reduce", (const void*)k_dec_down<H, I, false>, dim3(H / kDnRows, gmax), dim3(kThreads), 0,
-                s, &args);
+  return launch(MX ? "dec_down_reduce_mx" : "dec_down_reduce", (const void*)k_dec_down<H, I, false, MX>,
+                dim3(H / kDnRows, gmax), dim3(kThreads), 0, s, &args);
 }
 
 }  // namespace
 
 hipError_t run_decode(const FwdArgs& a, hipStream_t s) {
-  if (a.H == 4096 && a.I == 2048) return run_decode_t<4096, 2048>(a, s);
-  if (a.H == 512 && a.I == 256) return run_decode_t<512, 256>(a, s);
+  if (a.H == 4096 && a.I == 2048) return a.mx ? run_decode_t<4096, 2048, true>(a, s) : run_decode_t<4096, 2048, false>(a, s);
+  if (a.H == 512 && a.I == 256) return a.mx ? run_decode_t<512, 256, true>(a, s) : run_decode_t<512, 256, false>(a, s);
   return hipErrorInvalidValue;
 }
 

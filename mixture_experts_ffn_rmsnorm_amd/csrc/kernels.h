@@ -35,6 +35,11 @@ struct FwdArgs {
   const uint16_t* gate_sh;
   const uint16_t* up_sh;
   const uint16_t* down_sh;
+  // block-scaled 8-bit expert weights (moe_ffn_forward_mxfp8; mx != 0): E4M3
+  // codes [out][in] and E8M0 scales [out][in/32] of the same six matrices
+  int mx;
+  const uint8_t *gate_q, *up_q, *down_q, *gate_sh_q, *up_sh_q, *down_sh_q;
+  const uint8_t *gate_s, *up_s, *down_s, *gate_sh_s, *up_sh_s, *down_sh_s;
   float* out;
   // workspace pieces
   uint32_t* status;

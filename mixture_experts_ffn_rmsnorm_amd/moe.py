@@ -19,7 +19,8 @@ LAYER_SCORE, LAYER_HASH = 0, 1
 FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY, FLAG_SYNC_TIMEOUT, FLAG_F16_RANGE = 1, 2, 4, 8
 
 # Function names the header declares (checked against the library's exports).
-EXPORTS = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_route",
+EXPORTS = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp8", "moe_ffn_forward_noalloc",
+           "moe_route",
            "moe_ffn_routing_view", "moe_ffn_status", "moe_strerror", "moe_ffn_stage_timing_begin",
            "moe_ffn_stage_timing_end")
 
@@ -41,6 +42,16 @@ class WeightsC(ctypes.Structure):
                                                "down_exps", "gate_sh", "up_sh", "down_sh")]
 
 
+class MxMatrixC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class MxWeightsC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("norm_w", "router", "sel_bias", "tid2eid")] + \
+               [(n, MxMatrixC) for n in ("gate_exps", "up_exps", "down_exps", "gate_sh", "up_sh", "down_sh")]
+
+
+MX_BLOCK = 32
 _lib = None
 
 
@@ -55,6 +66,8 @@ def lib() -> ctypes.CDLL:
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         L.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(Dims), I64, ctypes.POINTER(SZ)]
         L.moe_ffn_forward.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, SZ, P]
+        L.moe_ffn_forward_mxfp8.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(MxWeightsC), P, P, SZ,
+                                            P]
         L.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P]
         L.moe_route.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, P]
         L.moe_ffn_routing_view.argtypes = [ctypes.POINTER(Dims), I64, P, SZ, ctypes.POINTER(P), ctypes.POINTER(P),
@@ -106,6 +119,26 @@ def make_weights(norm_w, router, sel_bias, tid2eid, gate, up, down, gate_sh, up_
     C struct.  The tensors must outlive every call that uses the struct."""
     return WeightsC(*[None if t is None else t.data_ptr()
                       for t in (norm_w, router, sel_bias, tid2eid, gate, up, down, gate_sh, up_sh, down_sh)])
+
+
+def make_mx_weights(norm_w, router, sel_bias, tid2eid, gate, up, down, gate_sh, up_sh, down_sh) -> MxWeightsC:
+    """Pack device tensors into the MXFP8 weight struct: the small parameters
+    as in ``make_weights``, each expert matrix a ``(codes, scales)`` pair of
+    uint8 tensors.  The tensors must outlive every call that uses it."""
+    p = lambda t: None if t is None else t.data_ptr()
+    mat = lambda m: MxMatrixC(m[0].data_ptr(), m[1].data_ptr())
+    return MxWeightsC(p(norm_w), p(router), p(sel_bias), p(tid2eid), mat(gate), mat(up), mat(down), mat(gate_sh),
+                      mat(up_sh), mat(down_sh))
+
+
+def forward_mxfp8(dims: Dims, x, token_ids, layer_kind: int, weights: MxWeightsC, out, workspace, stream=None):
+    """``forward`` with MXFP8 expert weights; enqueue only."""
+    rows = x.shape[0]
+    rc = lib().moe_ffn_forward_mxfp8(ctypes.byref(dims), _ptr(x), _ptr(token_ids), rows, int(layer_kind),
+                                     ctypes.byref(weights), _ptr(out), _ptr(workspace), workspace.numel(),
+                                     _stream(stream))
+    _check(rc, "moe_ffn_forward_mxfp8")
+    return out
 
 
 def workspace_bytes(dims: Dims, rows: int) -> int:

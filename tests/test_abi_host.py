@@ -269,3 +269,58 @@ def test_noalloc_rejects_on_host():
     assert moe.workspace_bytes(t, 5540) <= moe.NOALLOC_SCRATCH_BYTES < moe.workspace_bytes(t, 5541)
     assert _noalloc(t, rows=5541) == moe.MOE_ESCRATCH
     assert "scratch" in moe.strerror(moe.MOE_ESCRATCH)
+
+
+def test_mx_struct_layout_matches_header():
+    src = r"""
+    #include <stdio.h>
+    #include <stddef.h>
+    #include "moe_ffn.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu %d\n", sizeof(moe_mx_weights_t), offsetof(moe_mx_weights_t, gate_exps),
+             offsetof(moe_mx_weights_t, down_sh), offsetof(moe_mx_matrix_t, scales), MOE_MX_BLOCK);
+      return 0;
+    }"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        got = list(map(int, subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()))
+    assert got == [ctypes.sizeof(moe.MxWeightsC), moe.MxWeightsC.gate_exps.offset, moe.MxWeightsC.down_sh.offset,
+                   moe.MxMatrixC.scales.offset, moe.MX_BLOCK]
+
+
+def _mx_weights(drop=None, misalign=None):
+    mats = {n: moe.MxMatrixC(FAKE, FAKE + (1 << 32)) for n in
+            ("gate_exps", "up_exps", "down_exps", "gate_sh", "up_sh", "down_sh")}
+    if drop:
+        setattr(mats[drop[0]], drop[1], None)
+    if misalign:
+        setattr(mats[misalign[0]], misalign[1], getattr(mats[misalign[0]], misalign[1]) + 4)
+    return moe.MxWeightsC(FAKE, FAKE, FAKE, FAKE, *mats.values())
+
+
+def test_mxfp8_forward_rejects_on_host():
+    """The MXFP8 entry point checks its weights (every code and scale array
+    present and 16-byte aligned) and the shared arguments before any HIP
+    call; more than 4 rows are not supported."""
+    d = moe.make_dims(**FULL, table_rows=131072)
+    L = moe.lib()
+
+    def call(w, rows=4, dims=d, x=FAKE, kind=moe.LAYER_SCORE):
+        return L.moe_ffn_forward_mxfp8(None if dims is None else ctypes.byref(dims), x, FAKE, rows, kind,
+                                       None if w is None else ctypes.byref(w), FAKE + (1 << 30), FAKE + (2 << 30),
+                                       1 << 40, None)
+
+    assert call(None) == moe.MOE_EINVAL
+    assert call(_mx_weights(), dims=None) == moe.MOE_EINVAL
+    assert call(_mx_weights(drop=("down_sh", "scales"))) == moe.MOE_EINVAL
+    assert call(_mx_weights(drop=("gate_exps", "codes"))) == moe.MOE_EINVAL
+    assert call(_mx_weights(misalign=("up_exps", "codes"))) == moe.MOE_EINVAL
+    assert call(_mx_weights(misalign=("gate_sh", "scales"))) == moe.MOE_EINVAL
+    assert call(_mx_weights(), rows=0) == moe.MOE_EINVAL
+    assert call(_mx_weights(), x=None) == moe.MOE_EINVAL
+    assert call(_mx_weights(), kind=9) == moe.MOE_EINVAL
+    assert call(_mx_weights(), dims=moe.make_dims(4096, 128, 6, 2048)) == moe.MOE_EUNSUPPORTED
+    assert call(_mx_weights(), rows=5) == moe.MOE_EUNSUPPORTED
