@@ -114,7 +114,7 @@ def step_bytes(cfg, U, R, fmt="bf16"):
 
 SUB_WORKLOADS = ("decode-cohort-r4-hash", "prefill-r512-score", "prefill-r8192-score-skewed")
 # the same workloads with MXFP8 expert weights (moe_ffn_forward_mxfp8)
-MX_WORKLOADS = ("decode-r1-score", "decode-cohort-r4-hash")
+MX_WORKLOADS = ("decode-r1-score", "decode-cohort-r4-hash", "prefill-r512-score", "prefill-r8192-score-skewed")
 
 
 def draw_layers(cfg, L):
@@ -358,7 +358,7 @@ def main():
             for c in mx_cfgs:
                 lay_c = bind_layers(c, big_mx, nl(c), "mxfp8")
                 r_c, g_c = time_workload(c, lay_c, args.steps, args.warmup, graph=args.graph and c.rows <= 4)
-                r_c["dtype"] = "f32"
+                r_c["dtype"] = "f32" if c.rows <= 4 else "f16"
                 r_c["layer_kind"] = "hash" if c.layer_kind == 1 else "score"
                 res["workloads"][c.name + "-mxfp8"] = r_c
                 mx_gpu[c.name + "-mxfp8"] = (c, lay_c[0], g_c)

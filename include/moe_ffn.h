@@ -212,11 +212,16 @@ typedef struct moe_mx_weights {
 } moe_mx_weights_t;
 
 /* moe_ffn_forward with MXFP8 expert weights: same arguments, workspace
- * (moe_ffn_workspace_bytes), routing, status and bitwise reproducibility;
- * each weight is its decoded value exactly (E4M3 and E8M0 values are exact
- * in f32).  Reads half the expert bytes of the bf16 layer.
+ * (moe_ffn_workspace_bytes), routing, status and bitwise reproducibility.
+ * Reads about half the expert bytes of the bf16 layer.  Precision:
+ *   rows <= 4  each weight is its decoded value exactly (E4M3 and E8M0
+ *              values are exact in f32), f32 accumulation.
+ *   rows > 4   each weight is its decoded value rounded to nearest even
+ *              fp16 (exact for 2^-14 <= |w| <= 65504, within 2^-25
+ *              below, infinite beyond), then as moe_ffn_forward's fp16
+ *              path, with its domain and MOE_FLAG_F16_RANGE.
  * Errors: as moe_ffn_forward; MOE_EINVAL also for a missing or misaligned
- * code or scale array; MOE_EUNSUPPORTED for rows > 4 (decode shapes only). */
+ * code or scale array. */
 int moe_ffn_forward_mxfp8(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,
                           int layer_kind, const moe_mx_weights_t* w, float* out, void* workspace,
                           size_t workspace_bytes, void* stream);

@@ -331,7 +331,6 @@ int moe_ffn_forward_mxfp8(const moe_dims_t* d, const float* x, const int32_t* to
   Layout L;
   rc = check_forward_args(d, x, token_ids, rows, layer_kind, &common, out, &L);
   if (rc) return rc;
-  if (rows > kDecodeMaxRows) return MOE_EUNSUPPORTED;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
   return forward_in(d, x, token_ids, rows, layer_kind, &common, w, out, workspace, L, stream);
 }

@@ -20,10 +20,13 @@
 // page; its "slotted" indexed matmul over [rows, top_k] becomes the sort +
 // grouped GEMM here.
 //
-// Matrix-core precision: weights are bf16; activations (xn, and the SwiGLU
-// output h) are rounded to fp16 and multiplied by the bf16 weights converted
-// to fp16 (exact for 2^-14 <= |w| <= 65504, within 2^-25 below), accumulating
-// in f32 on v_mfma_f32_32x32x16_f16.  fp16 keeps 3 more mantissa bits than
+// Matrix-core precision: weights are bf16, or block-scaled 8-bit codes
+// (E4M3 with an E8M0 scale per 32 inputs, OCP MX); activations (xn, and the
+// SwiGLU output h) are rounded to fp16 and multiplied by the weights
+// converted to fp16 (bf16: exact for 2^-14 <= |w| <= 65504, within 2^-25
+// below; MX: the decoded value code * 2^(scale-127) rounded to nearest even
+// fp16, so exact in the same range), accumulating in f32 on
+// v_mfma_f32_32x32x16_f16.  fp16 keeps 3 more mantissa bits than
 // bf16 at the same matrix-core rate, at the price of its range: an operand
 // beyond 65504 in magnitude becomes infinite, and the router (non-finite
 // logit) or a GEMM epilogue (non-finite h, routed down output or layer
@@ -72,6 +75,15 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 
 // chunk swizzle of a 128-byte LDS row
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// chunk swizzle of an 8-bit weight row in LDS: 8 chunks (one 128-byte row
+// per line) as above; 4 chunks (two 64-byte rows per line) by (row / 4) & 3,
+// so that 16 consecutive rows read at one chunk hit 16 distinct 16-byte bank
+// groups
+__device__ __forceinline__ int mxsw(int row, int cpr) { return cpr == 8 ? swz(row) : (row >> 2) & 3; }
+// dword swizzle of a scale row of `dpr` dwords: the rows that share a
+// 256-byte span rotate their dwords, so 32 consecutive rows reading one
+// dword hit 32 distinct banks
+__device__ __forceinline__ int ssw(int row, int dpr) { return (row / (64 / dpr)) & (dpr - 1); }
 
 // 16 bytes per lane from global memory into LDS, lanes filling consecutive
 // 16-byte slots from the wave-uniform LDS byte address `lds`.  Completion is
@@ -86,7 +98,34 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
+// 4 bytes per lane, lanes filling consecutive 4-byte slots from `lds`
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// An E8M0 block scale 2^(c-127) as an f32 operand of the scaled conversions
+// (c = 0 is the subnormal 2^-127, c = 255 is NaN).
+__device__ __forceinline__ float e8m0_scale(uint32_t c) {
+  return c == 0 ? __uint_as_float(0x00400000u) : (c == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(c << 23));
+}
+
+// Eight E4M3 codes (little-endian bytes of lo, hi) times `scale`, rounded to
+// nearest even fp16, in k order: v_cvt_scalef32_pk_f16_fp8 converts the two
+// codes of one 16-bit half of its source.  Each result is taken as a whole
+// 32-bit word: extracting the halves of the builtin's vector result
+// duplicates its low half (measured: every odd code read back as its even
+// neighbour), while the word itself holds both conversions exactly.
+__device__ __forceinline__ uint4 fp8x8_to_f16x8(uint32_t lo, uint32_t hi, float scale) {
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, scale, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, scale, true));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, scale, false));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, scale, true));
+  return r;
+}
 
 // s_waitcnt vmcnt(N) with the other counters left alone
 template <int N>
@@ -607,6 +646,15 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
 // hit distinct LDS banks.  B stays bf16 in LDS and is converted to fp16
 // after the fragment read, interleaved with the MFMAs of the previous
 // k-step.
+// Block-scaled 8-bit weights (MX) travel the same way as 8-bit codes, a
+// k-tile row of BK bytes (BK 128: one 128-byte row; BK 64: two rows per
+// 128-byte line, 16-byte chunks swizzled by (row / 4) & 3); each tile's
+// block scales (one byte per 32 inputs) land in LDS once per tile.  The k
+// order inside a pair of k-steps is permuted so that a lane's 16 codes of
+// the pair are contiguous and share one scale: k-step 2p + o takes k =
+// 32p + 16 * (lane / 32) + 8o + 0..7 (the A fragments follow the same map),
+// and one 16-byte read per pair feeds both steps through
+// v_cvt_scalef32_pk_f16_fp8.
 // The grid is persistent (one block per compute unit); tiles are ordered by
 // group, then in blocks of 4 row tiles x 8 column tiles, and handed out so
 // that each XCD takes a contiguous run of them: the tiles that share
@@ -639,7 +687,7 @@ struct GemmShape {
   static constexpr int BN = MODE == 0 ? Cfg::BROWS / 2 : Cfg::BROWS;
 };
 
-template <int MODE, int KD, int ND, class Cfg>
+template <int MODE, int KD, int ND, class Cfg, bool MX>
 __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
   constexpr int BM = Cfg::BM, WM = Cfg::WM, BROWS = Cfg::BROWS, WN = Cfg::WN, BK = Cfg::BK;
   constexpr int kStages = Cfg::kStages;
@@ -647,19 +695,45 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
   constexpr int NT = ND / BN;                // column tiles per group
   constexpr int NK = KD / BK;                // k slices
   constexpr int NH = BK / 64;              // 64-k halves per k-tile
-  constexpr int HA = BM * 128, HB = BROWS * 128;  // bytes of one half of the A / B tile
-  constexpr int A_ST = NH * HA, B_ST = NH * HB, ST = A_ST + B_ST;
-  constexpr int AI = A_ST / 16 / kGT;  // A DMA instructions per thread per k-tile
-  constexpr int BI = B_ST / 16 / kGT;  // B DMA instructions per thread per k-tile
-  constexpr int AG = AI / NH, BG = BI / NH;  // 8-row groups per wave (A, B)
-  static_assert(AG >= 1 && BG >= 1 && AI * kGT * 16 == A_ST && BI * kGT * 16 == B_ST, "DMA tiling");
-  static_assert(kStages == 2 || AG == 1, "the ring's wait counts at most one A row group per wave");
+  constexpr int HA = BM * 128, HB = BROWS * 128;  // bytes of one half of the A / B tile (bf16 B)
   // epilogue staging per 64-row slab, reusing the ring: f32 [64][BROWS + 4]
   // (gate/up: gate columns, then up columns)
   constexpr int CPITCH = BROWS + 4;
-  static_assert(kSlab * CPITCH * 4 <= kStages * ST, "staging fits");
+  constexpr int SLAB = kSlab * CPITCH * 4;
+  // MX: the B tile holds BK bytes per row; with three stages they are
+  // padded to a slab so that the epilogue can stage through one of them
+  constexpr int A_ST = NH * HA, B_ST = MX ? BROWS * BK : NH * HB;
+  constexpr bool kPad = MX && kStages == 3 && MODE != 2 && A_ST + B_ST < SLAB;
+  constexpr int ST = kPad ? (SLAB + 1023) / 1024 * 1024 : A_ST + B_ST;
+  constexpr int AI = A_ST / 16 / kGT;  // A DMA instructions per thread per k-tile
+  constexpr int BI = B_ST / 16 / kGT;  // B DMA instructions per thread per k-tile
+  constexpr int AG = AI / NH, BG = MX ? BI : BI / NH;  // 8-line groups per wave (A, B)
+  static_assert(AG >= 1 && BG >= 1 && AI * kGT * 16 == A_ST && BI * kGT * 16 == B_ST, "DMA tiling");
+  static_assert(kStages == 2 || AG == 1, "the ring's wait counts at most one A row group per wave");
+  static_assert(SLAB <= kStages * ST, "staging fits");
   static_assert(NK >= 2 && ND % BN == 0, "tiling");
+  // MX B rows: RPL rows per 128-byte line, CPR 16-byte chunks per row
+  constexpr int RPL = MX ? 128 / BK : 1, CPR = MX ? BK / 16 : 8;
+  static_assert(!MX || ((BK == 64 || BK == 128) && BROWS % (8 * RPL) == 0), "MX B layout");
+  // MX block scales of the tile's B rows: SR bytes per row (DPR dwords),
+  // dword w of row r stored at slot w ^ ssw(r); one buffer padded to whole
+  // rounds of 4-byte DMA, SCI per thread
+  constexpr int SR = KD / 32, DPR = SR / 4;
+  static_assert(!MX || (KD % 128 == 0 && DPR <= 64 && (DPR & (DPR - 1)) == 0), "MX scale rows");
+  constexpr int SCL = MX ? (BROWS * SR + kGT * 4 - 1) / (kGT * 4) * (kGT * 4) : 0;
+  constexpr int SCI = SCL / (kGT * 4);
+  // With three stages and a slab that fits in one stage, the k-tiles of
+  // consecutive statically dealt tiles form one stream: the last two
+  // refills of a tile's k loop request the next tile's first two k-tiles
+  // (instead of re-loading a dead one), so the next tile starts with them
+  // landed; the epilogue stages through the buffer of the tile's last
+  // k-tile, the one buffer left free.  k-tile kt of a tile sits in buffer
+  // (off + kt) % kStages.  Not for the shared expert's down + reduce, whose
+  // per-tile slot table lives in LDS.  MX: the next tile's scales land in
+  // the second scale buffer along with them.
+  constexpr bool kPre = MODE != 2 && kStages == 3 && SLAB <= ST;
   __shared__ __align__(16) unsigned char s_ring[kStages * ST];
+  __shared__ __align__(16) unsigned char s_scl[MX ? (kPre ? 2 : 1) * SCL : 16];
   __shared__ int s_tbase[kMaxExperts + 2];
   __shared__ int s_rbase[kMaxExperts + 2];
   __shared__ int s_cnt[kMaxExperts + 1];
@@ -670,6 +744,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
   const int E = a.E, G = E + 1, K = a.K;
   const int64_t R = a.R;
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)s_ring;
+  const uint32_t scl = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)s_scl;
   const uint32_t a_wave = __builtin_amdgcn_readfirstlane(wv * AG * 1024);
   const uint32_t b_wave = __builtin_amdgcn_readfirstlane(A_ST + wv * BG * 1024);
 
@@ -780,17 +855,46 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     }
     return (const unsigned char*)bmat + (int64_t)(brow0 + i * 8) * (KD * 2) + (((wv * BG + i) & 1) ? chunk1 : chunk0);
   };
-  // With three stages and a slab that fits in one stage, the k-tiles of
-  // consecutive statically dealt tiles form one stream: the last two
-  // refills of a tile's k loop request the next tile's first two k-tiles
-  // (instead of re-loading a dead one), so the next tile starts with them
-  // landed; the epilogue stages through the buffer of the tile's last
-  // k-tile, the one buffer left free.  k-tile kt of a tile sits in buffer
-  // (off + kt) % kStages.  Not for the shared expert's down + reduce, whose
-  // per-tile slot table lives in LDS.
-  constexpr bool kPre = MODE != 2 && kStages == 3 && kSlab * CPITCH * 4 <= ST;
+  // MX: codes (or scales) of tile B row `r` (0 <= r < BROWS)
+  auto mx_row = [&](int g, int n0, int r, bool scales) {
+    const bool sh = g == E;
+    const uint8_t* m;
+    int row;
+    if (MODE == 0) {
+      const bool is_up = r >= BN;
+      m = scales ? (sh ? (is_up ? a.up_sh_s : a.gate_sh_s) : (is_up ? a.up_s : a.gate_s))
+                 : (sh ? (is_up ? a.up_sh_q : a.gate_sh_q) : (is_up ? a.up_q : a.gate_q));
+      row = n0 + (is_up ? r - BN : r);
+    } else {
+      m = scales ? (sh ? a.down_sh_s : a.down_s) : (sh ? a.down_sh_q : a.down_q);
+      row = n0 + r;
+    }
+    const int64_t rows_before = sh ? 0 : (int64_t)g * ND;
+    return m + (rows_before + row) * (scales ? SR : KD);
+  };
+  // MX B DMA: instruction i of the wave fills 1024 bytes of the B tile,
+  // lane l the 16-byte slot l & 7 of line (wave * BI + i) * 8 + l / 8: row
+  // line * RPL + slot / CPR, chunk (slot % CPR) ^ mxsw(row)
+  auto b_src_mx = [&](int g, int n0, int i) {
+    const int line = (wv * BI + i) * 8 + (lane >> 3), slot = lane & 7;
+    const int r = line * RPL + slot / CPR;
+    return mx_row(g, n0, r, false) + ((slot % CPR) ^ mxsw(r, CPR)) * 16;
+  };
+  // MX scales of a tile into scale buffer `sb`: dword d of the buffer (row
+  // d / DPR, slot d % DPR) holds source dword slot ^ ssw(row); rows past the
+  // tile (padding) re-read its last row.  Not unrolled: unrolled, the
+  // tile-invariant offsets of every round were kept live across the k loop
+  // and spilled.
+  auto issue_scales = [&](int g, int n0, int sb) {
+#pragma unroll 1
+    for (int u = 0; u < SCI; ++u) {
+      const int d = u * kGT + t, r = d / DPR < BROWS ? d / DPR : BROWS - 1;
+      dma4(mx_row(g, n0, r, true) + (((d % DPR) ^ ssw(r, DPR)) << 2), scl + (uint32_t)(sb * SCL + (u * kGT + wv * kWave) * 4));
+    }
+  };
   int off = 0;   // ring offset of the current tile
   int npre = 0;  // its first k-tiles the previous tile requested (0 or 2)
+  int sb = 0;    // MX: the scale buffer of the current tile
   bool range_bad = false;  // a non-finite value written by this thread's epilogues
   int tile = first;
   if (tile >= nstatic) {
@@ -831,7 +935,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     for (int i = 0; i < AG; ++i) asrc[i] = a_src(g, cntg, m0, i);
     const unsigned char* bsrc[BG];
 #pragma unroll
-    for (int i = 0; i < BG; ++i) bsrc[i] = b_src(g, n0, i);
+    for (int i = 0; i < BG; ++i) bsrc[i] = MX ? b_src_mx(g, n0, i) : b_src(g, n0, i);
     // whether this wave loads A rows at all (the small configuration's one
     // A row group per wave; the big one waits with vmcnt(0))
     const bool a_loads = m0 + wv * AG * 8 < cntg;
@@ -842,14 +946,13 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     const unsigned char* nasrc[AG];
     const unsigned char* nbsrc[BG];
     bool na_loads = false;
-    int nm0 = 0, ncnt = 0;
+    int nm0 = 0, ncnt = 0, ng = 0, nn0 = 0;
     if (kPre && pref) {
-      int ng, nn0;
       locate(tile + grid, ng, ncnt, nm0, nn0);
 #pragma unroll
       for (int i = 0; i < AG; ++i) nasrc[i] = a_src(ng, ncnt, nm0, i);
 #pragma unroll
-      for (int i = 0; i < BG; ++i) nbsrc[i] = b_src(ng, nn0, i);
+      for (int i = 0; i < BG; ++i) nbsrc[i] = MX ? b_src_mx(ng, nn0, i) : b_src(ng, nn0, i);
       na_loads = nm0 + wv * AG * 8 < ncnt;
     }
     // k-tile `src` into ring buffer `buf`
@@ -862,10 +965,15 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
         if (m0 + (wv * AG + i) * 8 < cntg)
 #pragma unroll
           for (int h = 0; h < NH; ++h) dma16(asrc[i] + src * (BK * 2) + h * 128, base + a_wave + h * HA + i * 1024);
+      if constexpr (MX) {
 #pragma unroll
-      for (int i = 0; i < BG; ++i)
+        for (int i = 0; i < BG; ++i) dma16(bsrc[i] + src * BK, base + b_wave + i * 1024);
+      } else {
 #pragma unroll
-        for (int h = 0; h < NH; ++h) dma16(bsrc[i] + src * (BK * 2) + h * 128, base + b_wave + h * HB + i * 1024);
+        for (int i = 0; i < BG; ++i)
+#pragma unroll
+          for (int h = 0; h < NH; ++h) dma16(bsrc[i] + src * (BK * 2) + h * 128, base + b_wave + h * HB + i * 1024);
+      }
     };
     // the same for k-tile `src` of the next tile
     auto issue_next = [&](int src, int buf) {
@@ -875,29 +983,48 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
         if (nm0 + (wv * AG + i) * 8 < ncnt)
 #pragma unroll
           for (int h = 0; h < NH; ++h) dma16(nasrc[i] + src * (BK * 2) + h * 128, base + a_wave + h * HA + i * 1024);
+      if constexpr (MX) {
 #pragma unroll
-      for (int i = 0; i < BG; ++i)
+        for (int i = 0; i < BG; ++i) dma16(nbsrc[i] + src * BK, base + b_wave + i * 1024);
+      } else {
 #pragma unroll
-        for (int h = 0; h < NH; ++h) dma16(nbsrc[i] + src * (BK * 2) + h * 128, base + b_wave + h * HB + i * 1024);
+        for (int i = 0; i < BG; ++i)
+#pragma unroll
+          for (int h = 0; h < NH; ++h) dma16(nbsrc[i] + src * (BK * 2) + h * 128, base + b_wave + h * HB + i * 1024);
+      }
     };
     auto ring_buf = [&](int kt) { return kPre ? (off + kt) % kStages : kt % kStages; };
-    // fragment reads of k-step `st` (16 k) from ring buffer `buf`
-    auto read_step = [&](int buf, int st, half8 (&af)[WM], uint4 (&rb)[WN], int nv) {
+    // fragment reads of k-step `st` (16 k) of k-tile `kt` from ring buffer
+    // `buf`.  MX: the B codes of a step pair and their scale are read at its
+    // even step and kept for the odd one.
+    auto read_step = [&](int buf, int st, half8 (&af)[WM], uint4 (&rb)[WN], float (&sc)[WN], int nv, int kt) {
       const unsigned char* As = s_ring + buf * ST + (st >> 2) * HA;
-      const unsigned char* Bs = s_ring + buf * ST + A_ST + (st >> 2) * HB;
-      const int c = 2 * (st & 3) + (lane >> 5);
+      const int c = MX ? 4 * ((st >> 1) & 1) + 2 * (lane >> 5) + (st & 1) : 2 * (st & 3) + (lane >> 5);
 #pragma unroll
       for (int i = 0; i < WM; ++i)
         if (i < nv) af[i] = *(const half8*)(As + arow[i] * 128 + ((c ^ swz(arow[i])) << 4));
+      if constexpr (!MX) {
+        const unsigned char* Bs = s_ring + buf * ST + A_ST + (st >> 2) * HB;
 #pragma unroll
-      for (int j = 0; j < WN; ++j) rb[j] = *(const uint4*)(Bs + brow[j] * 128 + ((c ^ swz(brow[j])) << 4));
-    };
-    auto convert = [&](const uint4 (&rb)[WN], half8 (&bf)[WN]) {
+        for (int j = 0; j < WN; ++j) rb[j] = *(const uint4*)(Bs + brow[j] * 128 + ((c ^ swz(brow[j])) << 4));
+      } else if ((st & 1) == 0) {
+        const unsigned char* Bs = s_ring + buf * ST + A_ST;
+        const int q = 2 * (st >> 1) + (lane >> 5);
+        const int b = kt * (BK / 32) + (st >> 1);  // 32-k block of the pair
+        const unsigned char* Ss = s_scl + sb * SCL + (b & 3);
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const uint4 cv = bf16x8_to_f16x8(rb[j]);
-        bf[j] = *(const half8*)&cv;
+        for (int j = 0; j < WN; ++j) {
+          rb[j] = *(const uint4*)(Bs + (brow[j] / RPL) * 128 + (brow[j] % RPL) * BK + ((q ^ mxsw(brow[j], CPR)) << 4));
+          sc[j] = e8m0_scale(Ss[brow[j] * SR + (((b >> 2) ^ ssw(brow[j], DPR)) << 2)]);
+        }
       }
+    };
+    // B fragment j of k-step `st` in fp16
+    auto conv1 = [&](int j, int st, const uint4 (&rb)[WN], const float (&sc)[WN], half8& out) {
+      uint4 cv;
+      if constexpr (MX) cv = (st & 1) ? fp8x8_to_f16x8(rb[j].z, rb[j].w, sc[j]) : fp8x8_to_f16x8(rb[j].x, rb[j].y, sc[j]);
+      else cv = bf16x8_to_f16x8(rb[j]);
+      out = __builtin_bit_cast(half8, cv);
     };
 
     floatx16 acc[WM][WN];
@@ -923,33 +1050,34 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     constexpr int NV = decltype(nv_c)::value;
     half8 af[WM], bf[WN];
     if constexpr (kPre) {
-      if (npre == 0) issue(0, ring_buf(0));
+      if (npre == 0) {
+        if constexpr (MX) issue_scales(g, n0, sb);
+        issue(0, ring_buf(0));
+      }
       wait_vmcnt<0>();
       __syncthreads();
 #pragma unroll
       for (int st = 1; st < kStages; ++st)
         if (st >= npre) issue(st < NK ? st : NK - 1, ring_buf(st));
     } else {
+      if constexpr (MX) issue_scales(g, n0, 0);
       issue(0, 0);
       wait_vmcnt<0>();
       __syncthreads();
 #pragma unroll
       for (int st = 1; st < kStages; ++st) issue(st < NK ? st : NK - 1, st);
     }
-    {
-      uint4 rb[WN];
-      read_step(ring_buf(0), 0, af, rb, NV);
-      convert(rb, bf);
-    }
+    // raw B fragments (MX: of the current step pair) and their scales
+    uint4 rb[WN];
+    float sc[WN];
+    read_step(ring_buf(0), 0, af, rb, sc, NV, 0);
+#pragma unroll
+    for (int j = 0; j < WN; ++j) conv1(j, 0, rb, sc, bf[j]);
     // one B fragment's four MFMAs
     auto mfma_j = [&](int j) {
 #pragma unroll
       for (int i = 0; i < NV; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    };
-    auto conv1 = [&](const uint4& raw, half8& out) {
-      const uint4 cv = bf16x8_to_f16x8(raw);
-      out = *(const half8*)&cv;
     };
     // The schedule inside a k-step is pinned with scheduling fences: the
     // next step's fragment reads go first, then each B fragment's MFMAs run
@@ -960,9 +1088,8 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         half8 afn[WM], bfn[WN];
-        uint4 rb[WN];
         if (st + 1 < NS) {
-          read_step(buf, st + 1, afn, rb, NV);
+          read_step(buf, st + 1, afn, rb, sc, NV, kt);
           __builtin_amdgcn_sched_barrier(0);
           mfma_j(0);
           __builtin_amdgcn_sched_barrier(0);
@@ -974,7 +1101,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
           if (kStages == 2 || !later_a) wait_vmcnt<(kStages - 2) * BI>();
           else wait_vmcnt<(kStages - 2) * (BI + NH)>();
           __syncthreads();  // k-tile kt+1 landed for every wave; every wave is done reading buffer `buf`
-          read_step(nbuf, 0, afn, rb, NV);
+          read_step(nbuf, 0, afn, rb, sc, NV, kt + 1 < NK ? kt + 1 : NK - 1);
           __builtin_amdgcn_sched_barrier(0);
           mfma_j(0);
           if constexpr (!kPre) {
@@ -982,17 +1109,21 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
           } else {
             if (kt + kStages < NK) issue(kt + kStages, buf);
             else if (!pref) issue(NK - 1, buf);  // dead refill: the loop body stays the same
-            else if (kt + kStages - NK < kStages - 1) issue_next(kt + kStages - NK, buf);
+            else if (kt + kStages - NK < kStages - 1) {
+              // MX: the next tile's scales go ahead of its first k-tile
+              if (MX && kt + kStages == NK) issue_scales(ng, nn0, sb ^ 1);
+              issue_next(kt + kStages - NK, buf);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int j = 1; j < WN; ++j) {
-          conv1(rb[j - 1], bfn[j - 1]);
+          conv1(j - 1, (st + 1) % NS, rb, sc, bfn[j - 1]);
           mfma_j(j);
           __builtin_amdgcn_sched_barrier(0);
         }
-        conv1(rb[WN - 1], bfn[WN - 1]);
+        conv1(WN - 1, (st + 1) % NS, rb, sc, bfn[WN - 1]);
 #pragma unroll
         for (int i = 0; i < NV; ++i) af[i] = afn[i];
 #pragma unroll
@@ -1116,6 +1247,7 @@ __global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
     if constexpr (kPre) {
       off = pref ? ring_buf(NK) : 0;
       npre = pref ? kStages - 1 : 0;
+      if (MX && pref) sb ^= 1;
     }
     __syncthreads();  // staging and s_pos are rewritten by the next tile
     tile = s_next;
@@ -1160,7 +1292,7 @@ const void* router_fn() {
   else return (const void*)k_pre_router<H, E, 1>;
 }
 
-template <int H, int I, int E>
+template <int H, int I, int E, bool MX>
 hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   FwdArgs args = a;
   const int nb = (a.R + kRR - 1) / kRR;
@@ -1181,11 +1313,12 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   // groups of a few rows on average: the small row tile and the deeper ring
   const bool small = (int64_t)a.R * a.K <= 32LL * a.E;
-  err = launch("gemm_gateup_swiglu",
-               small ? (const void*)k_gemm<0, H, I, GemmSmall> : (const void*)k_gemm<0, H, I, GemmBig>, dim3(grid),
-               dim3(kGT), 0, s, &args);
+  err = launch(MX ? "gemm_gateup_swiglu_mx" : "gemm_gateup_swiglu",
+               small ? (const void*)k_gemm<0, H, I, GemmSmall, MX> : (const void*)k_gemm<0, H, I, GemmBig, MX>,
+               dim3(grid), dim3(kGT), 0, s, &args);
   if (err != hipSuccess) return err;
-  err = launch("gemm_down", small ? (const void*)k_gemm<1, I, H, GemmSmall> : (const void*)k_gemm<1, I, H, GemmBig>,
+  err = launch(MX ? "gemm_down_mx" : "gemm_down",
+               small ? (const void*)k_gemm<1, I, H, GemmSmall, MX> : (const void*)k_gemm<1, I, H, GemmBig, MX>,
                dim3(grid), dim3(kGT), 0, s, &args);
   if (err != hipSuccess) return err;
   // the shared down covers R rows only: small tiles when big ones would
@@ -1195,16 +1328,18 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   const int64_t sh_tiles =
       sh_small ? (a.R + GemmSmall::BM - 1) / GemmSmall::BM * (H / GemmShape<2, GemmSmall>::BN) : big_tiles;
   const int sh_grid = sh_tiles < grid ? (int)sh_tiles : grid;
-  return launch("gemm_down_shared_reduce",
-                sh_small ? (const void*)k_gemm<2, I, H, GemmSmall> : (const void*)k_gemm<2, I, H, GemmBig>,
+  return launch(MX ? "gemm_down_shared_reduce_mx" : "gemm_down_shared_reduce",
+                sh_small ? (const void*)k_gemm<2, I, H, GemmSmall, MX> : (const void*)k_gemm<2, I, H, GemmBig, MX>,
                 dim3(sh_grid), dim3(kGT), 0, s, &args);
 }
 
 }  // namespace
 
 hipError_t run_prefill(const FwdArgs& a, hipStream_t s) {
-  if (a.H == 4096 && a.I == 2048 && a.E == 256) return run_prefill_t<4096, 2048, 256>(a, s);
-  if (a.H == 512 && a.I == 256 && a.E == 32) return run_prefill_t<512, 256, 32>(a, s);
+  if (a.H == 4096 && a.I == 2048 && a.E == 256)
+    return a.mx ? run_prefill_t<4096, 2048, 256, true>(a, s) : run_prefill_t<4096, 2048, 256, false>(a, s);
+  if (a.H == 512 && a.I == 256 && a.E == 32)
+    return a.mx ? run_prefill_t<512, 256, 32, true>(a, s) : run_prefill_t<512, 256, 32, false>(a, s);
   return hipErrorInvalidValue;
 }
 

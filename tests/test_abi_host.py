@@ -304,7 +304,7 @@ def _mx_weights(drop=None, misalign=None):
 def test_mxfp8_forward_rejects_on_host():
     """The MXFP8 entry point checks its weights (every code and scale array
     present and 16-byte aligned) and the shared arguments before any HIP
-    call; more than 4 rows are not supported."""
+    call."""
     d = moe.make_dims(**FULL, table_rows=131072)
     L = moe.lib()
 
@@ -323,4 +323,4 @@ def test_mxfp8_forward_rejects_on_host():
     assert call(_mx_weights(), x=None) == moe.MOE_EINVAL
     assert call(_mx_weights(), kind=9) == moe.MOE_EINVAL
     assert call(_mx_weights(), dims=moe.make_dims(4096, 128, 6, 2048)) == moe.MOE_EUNSUPPORTED
-    assert call(_mx_weights(), rows=5) == moe.MOE_EUNSUPPORTED
+    assert call(_mx_weights(), rows=(1 << 24) + 1) == moe.MOE_EOVERFLOW

@@ -34,17 +34,19 @@ class MxLayer:
         self.table = t(hi.tid2eid) if hi.tid2eid is not None else None
         routed, shared = gen.mx_expert_weights(cfg, "cuda", layer)
         self.routed, self.shared = routed, shared
-        self._cache = {}
 
-        def expert(e):
-            if e not in self._cache:
-                self._cache[e] = tuple(gen.mx_host((m[0][e], m[1][e])) for m in routed)
-            return self._cache[e]
+        def expert(e):  # fetched per call: the oracle asks once per expert
+            return tuple(gen.mx_host((m[0][e], m[1][e])) for m in self.routed)
 
         self.oracle_w = ref.Weights(hi.norm_w, hi.router, hi.sel_bias, hi.tid2eid, expert,
                                     tuple(gen.mx_host(m) for m in shared))
         self.dims = moe.dims_of(cfg)
         self.cw = moe.make_mx_weights(self.norm_w, self.router, self.bias, self.table, *routed, *shared)
+
+    def set_scale(self, mat, e, row, block, value):
+        """Overwrite one block scale of routed matrix `mat` (0 gate, 1 up,
+        2 down) of expert e on the device (the oracle reads it from there)."""
+        self.routed[mat][1][e, row, block] = value
 
     def run(self, x_np, tok_np, kind):
         import torch
@@ -144,3 +146,100 @@ def test_full_mx_decode_ragged(full_mx, rows):
     out, lg, idx, w, st = full_mx.run(x, None, SCORE)
     near = check_forward(full_mx, x, None, SCORE, out, lg, idx, w, rel=1e-5, maxabs=5e-5)
     report_near_ties(f"mx {rows} rows", near, rows)
+
+
+# ------------------------------------------------------------ prefill ---
+# rows > 4: the grouped GEMM with 8-bit B tiles (37 rows: the small row tile
+# with the cross-tile stream; 300: the big tile), fp16 operands
+PREFILL_TOL = 2e-3
+
+
+@pytest.mark.parametrize("rows", [5, 8, 37, 300])
+def test_tiny_mx_prefill_score(tiny_mx, rows):
+    cfg = tiny_mx.cfg
+    x = _x(cfg, rows, 340 + rows)
+    out, lg, idx, w, st = tiny_mx.run(x, None, SCORE)
+    assert st == 0
+    check_forward(tiny_mx, x, None, SCORE, out, lg, idx, w, rel=PREFILL_TOL, maxabs=PREFILL_TOL * 5)
+
+
+@pytest.mark.parametrize("rows", [8, 37, 300])
+def test_tiny_mx_prefill_hash(tiny_mx, rows):
+    cfg = tiny_mx.cfg
+    x = _x(cfg, rows, 350 + rows)
+    tok = _tok(cfg, rows, 360 + rows)
+    out, lg, idx, w, st = tiny_mx.run(x, tok, HASH)
+    assert st == 0
+    check_forward(tiny_mx, x, tok, HASH, out, lg, idx, w, rel=PREFILL_TOL, maxabs=PREFILL_TOL * 5)
+
+
+@pytest.mark.parametrize("rows", [37, 300])
+def test_tiny_mx_prefill_matches_bf16_twin(tiny_mx, rows):
+    """Both formats give the matrix cores the same fp16 weights (the decoded
+    value fits bf16 exactly and both round it to fp16 the same way); only the
+    k order inside the MFMAs differs, so the outputs agree far below the
+    oracle tolerance, up to the odd 1-ulp flip of an fp16-rounded h."""
+    import torch
+
+    cfg = tiny_mx.cfg
+    twin = tiny_mx.bf16_twin()
+    x = _x(cfg, rows, 370 + rows)
+    out_mx = tiny_mx.run(x, None, SCORE)[0]
+    xd = torch.from_numpy(x).cuda()
+    ob = torch.empty_like(xd)
+    moe.forward(tiny_mx.dims, xd, None, SCORE, twin, ob, moe.alloc_workspace(tiny_mx.dims, rows))
+    torch.cuda.synchronize()
+    check_output(out_mx, ob.cpu().numpy(), rel=1e-4, maxabs=5e-4, what=f"mx vs bf16 twin, {rows} rows")
+
+
+@pytest.mark.parametrize("rows", [3, 37, 300])
+def test_tiny_mx_special_scales(rows):
+    """A block scale of 0 (2^-127: the block's weights vanish below fp16 and
+    f32 resolution) and one of 255 (NaN: every output of the rows routed to
+    that expert is NaN, on the oracle too).  Finite rows match the oracle; the
+    NaN rows are the same rows; the fp16 path reports them."""
+    lay = MxLayer(gen.config(0), layer=3)
+    cfg = lay.cfg
+    x = _x(cfg, rows, 380 + rows)
+    _, _, idx0, _, _ = lay.run(x, None, SCORE)
+    e_nan = int(idx0[0, 0])                              # row 0's first expert
+    e_zero = int(idx0[rows - 1, -1]) if int(idx0[rows - 1, -1]) != e_nan else int(idx0[rows - 1, 0])
+    lay.set_scale(0, e_nan, 5, 1, 255)                  # gate row 5, inputs 32..63
+    lay.set_scale(2, e_zero, 7, 0, 0)                   # down row 7, inputs 0..31
+    out, lg, idx, w, st = lay.run(x, None, SCORE)
+    res = ref.forward(x, None, SCORE, lay.oracle_w, cfg.top_k, cfg.eps)
+    np.testing.assert_array_equal(idx, idx0)  # the router does not see expert weights
+    nan_rows = np.isnan(res["out"]).any(axis=1)
+    assert nan_rows[0] and not nan_rows.all()
+    np.testing.assert_array_equal(np.isnan(out).any(axis=1), nan_rows)
+    assert np.isnan(out[nan_rows]).all()
+    if rows > 4:
+        assert st & moe.FLAG_F16_RANGE
+    tol = 1e-5 if rows <= 4 else PREFILL_TOL
+    check_output(out[~nan_rows], res["out"][~nan_rows], rel=tol, maxabs=tol * 5, what="finite rows")
+
+
+def test_full_mx_prefill_512(full_mx):
+    """Every row of the 512-row prefill with MXFP8 experts."""
+    cfg = gen.config(3)
+    lay = MxLayer(cfg)
+    hi = lay.host
+    out, lg, idx, w, st = lay.run(hi.x, None, SCORE)
+    assert st == 0
+    near = check_forward(lay, hi.x, None, SCORE, out, lg, idx, w)
+    report_near_ties(f"mx {cfg.name}", near, cfg.rows)
+
+
+def test_full_mx_prefill_8192_skewed():
+    """Every row of the 8192-row skewed prefill (16 hot experts: the big
+    tile, dynamically dealt tail tiles) with MXFP8 experts; bitwise
+    reproducible."""
+    cfg = gen.config(4)
+    lay = MxLayer(cfg)
+    hi = lay.host
+    out, lg, idx, w, st = lay.run(hi.x, None, SCORE)
+    assert st == 0
+    assert np.isin(idx, hi.hot).all()
+    near = check_forward(lay, hi.x, None, SCORE, out, lg, idx, w)
+    report_near_ties(f"mx {cfg.name}", near, cfg.rows)
+    np.testing.assert_array_equal(out, lay.run(hi.x, None, SCORE)[0])
