@@ -251,7 +251,7 @@ def time_workload(cfg, layers, steps, warmup, graph=False):
     # summary of the same workload, if it was measured on these sources
     from mixture_experts_ffn_rmsnorm_amd import profiling
 
-    measured = profiling.read_traffic(cfg.name)
+    measured = profiling.read_traffic(profiling.profile_key(cfg.name, layers[0][3]))
     if measured and dom in measured:
         roof["traffic"] = measured[dom]
     for name, k in kernels.items():

@@ -63,50 +63,92 @@ def short_name(kernel: str) -> str:
     return s.strip()
 
 
-# launch names used by the stage timer / bench, by kernel template
-LAUNCH_NAMES = [
-    ("k_dec_head", "dec_head"), ("k_dec_gateup", "dec_gateup"), ("k_dec_down", "dec_down_reduce"),
-    ("k_pre_norm", "pre_norm"), ("k_pre_router", "pre_router"), ("k_pre_sort", "pre_sort"), ("k_gemm<0,", "gemm_gateup_swiglu"),
-    ("k_gemm<1,", "gemm_down"), ("k_gemm<2,", "gemm_down_shared_reduce"), ("k_route", "route"),
-]
+def _template(kernel: str):
+    """(function name, top-level template arguments) of a demangled name."""
+    k = short_name(kernel)
+    k = k.split("(")[0] if "<" not in k.split("(")[0] else k
+    lt = k.find("<")
+    if lt < 0:
+        return k.split("(")[0].strip(), []
+    name, args, depth, cur = k[:lt].strip(), [], 0, ""
+    for ch in k[lt + 1:]:
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            if depth == 0:
+                break
+            depth -= 1
+        if ch == "," and depth == 0:
+            args.append(cur.strip())
+            cur = ""
+        else:
+            cur += ch
+    args.append(cur.strip())
+    return name, args
 
 
 def launch_name(kernel: str) -> str | None:
-    k = short_name(kernel).replace(" ", "")
-    # the one-row decode path: router-only head, self-routing gate/up, down with the shared expert
-    if k.startswith("k_dec_head") and k.endswith("true>"):
-        return "dec1_router"
-    if k.startswith("k_dec1_gateup"):
-        return "dec1_gateup"
-    if k.startswith("k_dec_down") and k.endswith("true>"):
-        return "dec1_down_reduce"
-    for key, name in LAUNCH_NAMES:
-        if k.startswith(key.replace(" ", "")):
-            return name
-    return None
+    """The launch name the stage timer and bench.py use for a kernel, by its
+    template: block-scaled (MX) instances end in "_mx"; the one-row decode
+    path's router-only head and shared-expert down are dec1_*."""
+    name, args = _template(kernel)
+    mx = bool(args) and args[-1] == "true"
+    base = None
+    if name == "k_dec_head" and len(args) == 4:
+        base = "dec1_router" if args[2] == "true" else "dec_head"
+    elif name == "k_dec_gateup" and len(args) == 3:
+        base = "dec_gateup"
+    elif name == "k_dec1_gateup" and len(args) == 3:
+        base = "dec1_gateup"
+    elif name == "k_dec_down" and len(args) == 4:
+        base = "dec1_down_reduce" if args[2] == "true" else "dec_down_reduce"
+    elif name == "k_gemm" and len(args) == 5:
+        base = {"0": "gemm_gateup_swiglu", "1": "gemm_down", "2": "gemm_down_shared_reduce"}.get(args[0])
+    else:
+        mx = False
+        base = {"k_pre_norm": "pre_norm", "k_pre_router": "pre_router", "k_pre_sort": "pre_sort",
+                "k_route": "route"}.get(name)
+    if base is None:
+        return None
+    return base + "_mx" if mx else base
 
 
 def _run(cmd, log):
+    """Run `cmd`; its stderr goes to `log` and, line by line, to ours (the
+    bench's progress lines); returns (returncode, stdout)."""
     print("[profiling] " + " ".join(shlex.quote(c) for c in cmd), file=sys.stderr, flush=True)
-    with open(log, "w") as fh:
-        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=fh, text=True, cwd=ROOT)
-    return r
+    with open(log, "w") as fh, open(log + ".stdout", "w") as fo:
+        p = subprocess.Popen(cmd, stdout=fo, stderr=subprocess.PIPE, text=True, cwd=ROOT)
+        for line in p.stderr:
+            fh.write(line)
+            if line.startswith("[bench]"):
+                sys.stderr.write(line)
+                sys.stderr.flush()
+        rc = p.wait()
+    return rc, open(log + ".stdout").read()
 
 
-def _bench_cmd(workload, extra):
-    return [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--only"] + list(extra)
+def _bench_cmd(workload, extra, weights="bf16"):
+    return ([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--only", "--weights", weights]
+            + list(extra))
+
+
+def profile_key(workload: str, weights: str = "bf16") -> str:
+    """File-name key of a workload's summaries: MXFP8 runs get "-mxfp8"."""
+    return workload if weights == "bf16" else f"{workload}-{weights}"
 
 
 def cmd_stats(args, extra):
-    out_dir = os.path.join(args.scratch, f"stats_{args.workload}")
+    key = profile_key(args.workload, args.weights)
+    out_dir = os.path.join(args.scratch, f"stats_{key}")
     os.makedirs(out_dir, exist_ok=True)
     prof = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", out_dir, "-o", "run", "--"]
-    bench = _bench_cmd(args.workload, extra)
-    r = _run(prof + bench, os.path.join(out_dir, "log.txt"))
-    json_line = next((l for l in r.stdout.splitlines() if l.startswith("{")), None)
-    if r.returncode != 0 and json_line is None:
-        print(f"profiled command failed ({r.returncode}); see {out_dir}/log.txt", file=sys.stderr)
-        return r.returncode
+    bench = _bench_cmd(args.workload, extra, args.weights)
+    rc, stdout = _run(prof + bench, os.path.join(out_dir, "log.txt"))
+    json_line = next((l for l in stdout.splitlines() if l.startswith("{")), None)
+    if rc != 0 and json_line is None:
+        print(f"profiled command failed ({rc}); see {out_dir}/log.txt", file=sys.stderr)
+        return rc
     stats = glob.glob(os.path.join(out_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not stats:
         print("no kernel_stats.csv produced", file=sys.stderr)
@@ -119,14 +161,16 @@ def cmd_stats(args, extra):
                      float(row["AverageNs"]) / 1e3, float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
     rows.sort(key=lambda t: -t[2] * t[3])
     cmdline = "python3 -m mixture_experts_ffn_rmsnorm_amd.profiling stats --workload " + args.workload
+    if args.weights != "bf16":
+        cmdline += " --weights " + args.weights
     if extra:
         cmdline += " -- " + " ".join(shlex.quote(e) for e in extra)
-    path = os.path.join(OUTDIR, f"kernels-{args.workload}.md")
+    path = os.path.join(OUTDIR, f"kernels-{key}.md")
     with open(path, "w") as f:
-        f.write(f"# Kernel durations, workload {args.workload}\n\n")
+        f.write(f"# Kernel durations, workload {args.workload}, {args.weights} expert weights\n\n")
         f.write("Command (from the repository root, on one MI355X):\n\n")
         f.write(f"    {cmdline}\n\nwhich runs\n\n    rocprofv3 --kernel-trace --stats --output-format csv "
-                f"-d <scratch> -o run -- python3 bench.py --workload {args.workload} --only"
+                f"-d <scratch> -o run -- python3 bench.py --workload {args.workload} --only --weights {args.weights}"
                 + ("" if not extra else " " + " ".join(extra)) + "\n\n")
         f.write(f"Kernel sources digest: `{sources_digest()}`\n\n")
         f.write("rocprofv3 kernel statistics for this library's kernels (every call of the run: warm-up, "
@@ -141,13 +185,19 @@ def cmd_stats(args, extra):
     return 0
 
 
-def _pmc_pass(counter, cmd, out_dir):
+# counters are collected on this library's kernels only (the weight
+# generation's torch kernels run unprofiled)
+KERNEL_REGEX = "k_(dec|pre|gemm|route)"
+
+
+def _pmc_pass(counter, cmd, out_dir, include=None):
     os.makedirs(out_dir, exist_ok=True)
-    prof = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", out_dir, "-o", "run", "--"]
-    r = _run(prof + cmd, os.path.join(out_dir, "log.txt"))
+    prof = ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d", out_dir, "-o", "run"]
+    prof += (["--kernel-include-regex", include] if include else []) + ["--"]
+    rc, _ = _run(prof + cmd, os.path.join(out_dir, "log.txt"))
     files = glob.glob(os.path.join(out_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
-        raise RuntimeError(f"{counter}: no counter_collection.csv (rc {r.returncode}); see {out_dir}/log.txt")
+        raise RuntimeError(f"{counter}: no counter_collection.csv (rc {rc}); see {out_dir}/log.txt")
     per = {}
     for f in files:
         for row in csv.DictReader(open(f)):
@@ -162,23 +212,30 @@ def _pmc_pass(counter, cmd, out_dir):
 
 def cmd_traffic(args, extra):
     copy_cmd = [sys.executable, "-m", "mixture_experts_ffn_rmsnorm_amd.profiling", "child-copy"]
-    bench = _bench_cmd(args.workload, ["--steps", "5", "--warmup", "2", "--no-cpu-baseline", "--no-peaks"])
+    key = profile_key(args.workload, args.weights)
+    bench_args = ["--steps", "5", "--warmup", "2", "--layers", "1", "--no-cpu-baseline", "--no-peaks"]
+    bench = _bench_cmd(args.workload, bench_args, args.weights)
     res = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         copy = _pmc_pass(counter, copy_cmd, os.path.join(args.scratch, f"copy_{counter}"))
         big = max(copy.items(), key=lambda kv: kv[1])  # the 1 GiB copy
-        kern = _pmc_pass(counter, bench, os.path.join(args.scratch, f"{args.workload}_{counter}"))
+        kern = _pmc_pass(counter, bench, os.path.join(args.scratch, f"{key}_{counter}"), KERNEL_REGEX)
         res[counter] = (big, kern)
     (cf_name, cf), _ = res["FETCH_SIZE"]
     (cw_name, cw), _ = res["WRITE_SIZE"]
     ffac, wfac = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
     names = sorted(set(res["FETCH_SIZE"][1]) | set(res["WRITE_SIZE"][1]))
-    path = os.path.join(OUTDIR, f"traffic-{args.workload}.txt")
+    path = os.path.join(OUTDIR, f"traffic-{key}.txt")
+    wopt = "" if args.weights == "bf16" else f" --weights {args.weights}"
     with open(path, "w") as f:
-        f.write(f"# HBM traffic per dispatch, workload {args.workload}, from rocprofv3 counters\n")
-        f.write(f"# command: python3 -m mixture_experts_ffn_rmsnorm_amd.profiling traffic --workload {args.workload}\n")
-        f.write("# passes: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, each over\n")
-        f.write(f"#   python3 bench.py --workload {args.workload} --only --steps 5 --warmup 2 --no-cpu-baseline --no-peaks\n")
+        f.write(f"# HBM traffic per dispatch, workload {args.workload}, {args.weights} expert weights, "
+                "from rocprofv3 counters\n")
+        f.write(f"# command: python3 -m mixture_experts_ffn_rmsnorm_amd.profiling traffic --workload {args.workload}"
+                f"{wopt}\n")
+        f.write(f"# passes: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, with --kernel-include-regex "
+                f"'{KERNEL_REGEX}', each over\n")
+        f.write(f"#   python3 bench.py --workload {args.workload} --only --weights {args.weights} "
+                + " ".join(bench_args) + "\n")
         f.write("#   and over a 1 GiB device-to-device copy (calibration: factor = bytes / counter bytes)\n")
         f.write(f"sources_sha256: {sources_digest()}\n")
         f.write(f"copy_kernel: {short_name(cf_name)}\n")
@@ -233,6 +290,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("what", choices=["stats", "traffic"])
     ap.add_argument("--workload", default="decode-r1-score")
+    ap.add_argument("--weights", choices=["bf16", "mxfp8"], default="bf16")
     ap.add_argument("--scratch", default="/tmp/moe_prof")
     ap.add_argument("--outdir", default=PROFILES, help="directory for the summaries (default profiles/)")
     argv = sys.argv[1:]
