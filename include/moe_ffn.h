@@ -254,6 +254,76 @@ int moe_ffn_forward_mxfp8(const moe_dims_t* d, const float* x, const int32_t* to
 int moe_ffn_forward_noalloc(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,
                             int layer_kind, const moe_weights_t* w, float* out, void* stream);
 
+/* ---- hyper-connection wrapper -------------------------------------------
+ * forward_ffn_rows on the ffn_forward.rs page takes the residual state as
+ * F32 [rows][hc][hidden] (hc = the model's hyper_connection_count) and
+ * returns a new state of that shape.  Before the FFN it normalises each
+ * row's flattened state without a scale (rms_norm_no_scale_f32 with
+ * rms_norm_eps), multiplies it by hc_ffn_fn into (2 + hc) * hc "mixes"
+ * (the "HC FFN function" matmul), splits those with hc_ffn_scale and
+ * hc_ffn_base into pre [hc], post [hc] and comb [hc][hc]
+ * (dispatch_hc_split_sinkhorn) and mixes the streams into the FFN input
+ * with pre (dispatch_hc_pre); after the weighted reduce, dispatch_hc_post
+ * combines the FFN output and the old state with post and comb.  The page
+ * prints no formula for the split, pre and post steps; this library
+ * computes (the published manifold-constrained hyper-connection maps, which
+ * match those names and shapes):
+ *   mixes  = state_flat * (mean(state_flat^2) + eps)^(-1/2) @ hc_fn^T,
+ *            columns: pre (hc) | post (hc) | comb (hc * hc, row-major
+ *            (output stream j, input stream i))
+ *   pre_i  = sigmoid(hc_scale[0] * mix_pre_i + hc_base[i])
+ *   post_j = 2 * sigmoid(hc_scale[1] * mix_post_j + hc_base[hc + j])
+ *   comb   = exp(hc_scale[2] * mix_comb + hc_base[2hc ..]) after
+ *            sinkhorn_iters rounds of dividing each row by its sum, then
+ *            each column by its sum
+ *   x      = sum_i pre_i * state_i            (the FFN input, moe_ffn_forward)
+ *   new_j  = post_j * ffn(x) + sum_i comb[j][i] * state_i */
+#define MOE_HC_MAX 4
+#define MOE_HC_MAX_ITERS 1000
+
+typedef struct moe_hc_weights {
+  const uint16_t* hc_fn;   /* device bf16 [(2+hc)*hc][hc*hidden] (hc_ffn_fn), 16-byte aligned */
+  const float* hc_scale;   /* device f32 [3]: pre, post, comb (hc_ffn_scale) */
+  const float* hc_base;    /* device f32 [(2+hc)*hc] (hc_ffn_base) */
+  int32_t hc;              /* streams, 1..MOE_HC_MAX */
+  int32_t sinkhorn_iters;  /* Sinkhorn rounds, 1..MOE_HC_MAX_ITERS */
+} moe_hc_weights_t;
+
+/* Workspace bytes of moe_ffn_forward_hc: moe_ffn_workspace_bytes' layout at
+ * offset 0 (so moe_ffn_routing_view and moe_ffn_status read the inner FFN
+ * call's routing and status from it), then the wrapper's intermediates.
+ * Host-only.  Errors: MOE_EINVAL, MOE_EUNSUPPORTED (also hc outside
+ * 1..MOE_HC_MAX), MOE_EOVERFLOW. */
+int moe_ffn_hc_workspace_bytes(const moe_dims_t* d, int32_t hc, int64_t rows, size_t* bytes);
+
+/* The wrapped layer:
+ *   state_in   device f32 [rows][hc][hidden], 16-byte aligned
+ *   state_out  device f32 [rows][hc][hidden], 16-byte aligned, overlapping
+ *              neither state_in nor the workspace
+ *   token_ids, layer_kind, w   as moe_ffn_forward
+ *   hw         the wrapper's parameters (struct read on the host)
+ *   workspace  moe_ffn_hc_workspace_bytes of device memory, 256-byte
+ *              aligned, zero-filled before its first use (as for
+ *              moe_ffn_forward, whose intermediates it holds)
+ * Launches on `stream`: the mixes' partial sums, the split with the FFN
+ * input, moe_ffn_forward on it (same precision, routing and status), the
+ * new state.  The wrapper's arithmetic is f32, sums in a fixed order; the
+ * result is bitwise reproducible.
+ * Errors: those of moe_ffn_forward; MOE_EINVAL also for a missing or
+ * misaligned hc array or a round count outside 1..MOE_HC_MAX_ITERS,
+ * MOE_EUNSUPPORTED for hc outside 1..MOE_HC_MAX. */
+int moe_ffn_forward_hc(const moe_dims_t* d, const float* state_in, const int32_t* token_ids, int64_t rows,
+                       int layer_kind, const moe_weights_t* w, const moe_hc_weights_t* hw, float* state_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device pointers, inside a moe_ffn_forward_hc workspace, to the last
+ * call's mixes and maps (f32 [rows][(2+hc)*hc]; maps: pre | post | comb as
+ * above), FFN input and FFN output (f32 [rows][hidden]).  Any output
+ * pointer may be NULL.  Host-only arithmetic, no HIP call.
+ * Errors: MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EOVERFLOW, MOE_EWORKSPACE. */
+int moe_ffn_hc_view(const moe_dims_t* d, int32_t hc, int64_t rows, void* workspace, size_t workspace_bytes,
+                    const float** mixes, const float** maps, const float** ffn_in, const float** ffn_out);
+
 /* Routing alone, from caller-given logits (ffn_forward.rs: the score-route
  * and hash-route dispatches that turn the F32 logits into I32 indices and
  * F32 weights), using the same device routine as moe_ffn_forward:

@@ -117,6 +117,23 @@ hipError_t launch(const char* name, const void* fn, dim3 grid, dim3 block, size_
   return err;
 }
 
+// The wrapper's parameters: hc streams supported, a positive round count,
+// every array present (hc_fn 16-byte aligned for its 8-byte loads).
+int check_hc_weights(const moe_hc_weights_t* hw) {
+  if (!hw) return MOE_EINVAL;
+  if (hw->hc < 1 || hw->hc > kHcMax) return MOE_EUNSUPPORTED;
+  if (hw->sinkhorn_iters < 1 || hw->sinkhorn_iters > MOE_HC_MAX_ITERS) return MOE_EINVAL;
+  if (!hw->hc_fn || !hw->hc_scale || !hw->hc_base || !aligned(hw->hc_fn, 16) || !aligned(hw->hc_scale, 4) ||
+      !aligned(hw->hc_base, 4))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -355,6 +372,77 @@ int moe_route(const moe_dims_t* d, const float* logits, const int32_t* token_ids
   a.idx = idx;
   a.w = wout;
   return run_route(a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_ffn_hc_workspace_bytes(const moe_dims_t* d, int32_t hc, int64_t rows, size_t* bytes) {
+  int rc = check_dims_rows(d, rows);
+  if (rc) return rc;
+  if (!bytes) return MOE_EINVAL;
+  if (hc < 1 || hc > kHcMax) return MOE_EUNSUPPORTED;
+  HcLayout L;
+  if (!make_hc_layout(rows, d->hidden, d->experts, d->top_k, d->inter, hc, &L)) return MOE_EOVERFLOW;
+  *bytes = L.total;
+  return MOE_OK;
+}
+
+int moe_ffn_forward_hc(const moe_dims_t* d, const float* state_in, const int32_t* token_ids, int64_t rows,
+                       int layer_kind, const moe_weights_t* w, const moe_hc_weights_t* hw, float* state_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_dims_rows(d, rows);
+  if (rc) return rc;
+  rc = check_hc_weights(hw);
+  if (rc) return rc;
+  if (!state_in || !state_out || !aligned(state_in, 16) || !aligned(state_out, 16)) return MOE_EINVAL;
+  rc = check_weights(d, layer_kind, w, token_ids, true);
+  if (rc) return rc;
+  HcLayout L;
+  if (!make_hc_layout(rows, d->hidden, d->experts, d->top_k, d->inter, hw->hc, &L)) return MOE_EOVERFLOW;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
+  const size_t sbytes = (size_t)rows * hw->hc * d->hidden * sizeof(float);
+  if (overlaps(state_in, sbytes, state_out, sbytes) || overlaps(state_out, sbytes, workspace, L.total) ||
+      overlaps(state_in, sbytes, workspace, L.total))
+    return MOE_EOVERLAP;
+  char* ws = (char*)workspace;
+  HcArgs a;
+  memset(&a, 0, sizeof(a));
+  a.R = (int)rows;
+  a.H = d->hidden;
+  a.hc = hw->hc;
+  a.iters = hw->sinkhorn_iters;
+  a.eps = d->eps;
+  a.slices = L.slices;
+  a.state = state_in;
+  a.fn = hw->hc_fn;
+  a.scale = hw->hc_scale;
+  a.base = hw->hc_base;
+  a.mixes = (float*)(ws + L.mixes);
+  a.maps = (float*)(ws + L.maps);
+  a.partial = (float*)(ws + L.partial);
+  a.ffn_in = (float*)(ws + L.ffn_in);
+  a.ffn_out = (float*)(ws + L.ffn_out);
+  a.out = state_out;
+  hipStream_t s = (hipStream_t)stream;
+  if (run_hc_pre(a, s) != hipSuccess) return MOE_EHIP;
+  rc = forward_in(d, a.ffn_in, token_ids, rows, layer_kind, w, nullptr, (float*)(ws + L.ffn_out), workspace, L.ffn,
+                  stream);
+  if (rc) return rc;
+  return run_hc_post(a, s) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_ffn_hc_view(const moe_dims_t* d, int32_t hc, int64_t rows, void* workspace, size_t workspace_bytes,
+                    const float** mixes, const float** maps, const float** ffn_in, const float** ffn_out) {
+  int rc = check_dims_rows(d, rows);
+  if (rc) return rc;
+  if (hc < 1 || hc > kHcMax) return MOE_EUNSUPPORTED;
+  HcLayout L;
+  if (!make_hc_layout(rows, d->hidden, d->experts, d->top_k, d->inter, hc, &L)) return MOE_EOVERFLOW;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
+  char* ws = (char*)workspace;
+  if (mixes) *mixes = (const float*)(ws + L.mixes);
+  if (maps) *maps = (const float*)(ws + L.maps);
+  if (ffn_in) *ffn_in = (const float*)(ws + L.ffn_in);
+  if (ffn_out) *ffn_out = (const float*)(ws + L.ffn_out);
+  return MOE_OK;
 }
 
 int moe_ffn_routing_view(const moe_dims_t* d, int64_t rows, void* workspace, size_t workspace_bytes,

@@ -306,19 +306,6 @@ __device__ __forceinline__ void stage_rows(float* dst, const float* const (&src)
   __syncthreads();
 }
 
-// Write-through (agent-scope) store / load of one float: data that another
-// workgroup of the same kernel reads after a flag or counter says so.  The
-// writer waits for these stores to complete (sync_stores) before raising
-// the flag; the reader's loads bypass stale cache lines.
-__device__ __forceinline__ void store_wt(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_wt(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Every store this thread issued has completed.
-__device__ __forceinline__ void sync_stores() { __builtin_amdgcn_s_waitcnt(0); }
-
 // Gate/up + SwiGLU of PAIRS inter rows of one expert for the `nr` activation
 // rows in LDS: tile x of `tiles` takes rows x, x + tiles, x + 2*tiles, ...,
 // so the blocks working on one expert at the same time read neighbouring

@@ -38,6 +38,19 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Write-through (agent-scope) store / load of one float: data that another
+// workgroup of the same kernel reads after a flag or counter says so.  The
+// writer waits for these stores to complete (sync_stores) before raising
+// the flag; the reader's loads bypass stale cache lines.
+__device__ __forceinline__ void store_wt(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_wt(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every store this thread issued has completed.
+__device__ __forceinline__ void sync_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -1,0 +1,216 @@
+// Hyper-connection wrapper around the FFN layer.  forward_ffn_rows on the
+// hf2q ffn_forward.rs page keeps the residual as hc streams, F32
+// [rows, hc, hidden]; before the FFN it normalises each row's flattened
+// state without a scale (rms_norm_no_scale_f32), multiplies it by
+// hc_ffn_fn into (2 + hc) * hc mixes, splits those into pre / post / comb
+// maps (dispatch_hc_split_sinkhorn) and mixes the streams into the FFN
+// input (dispatch_hc_pre); after it, dispatch_hc_post builds the new state.
+// The split, pre and post arithmetic is the reading stated in moe_ffn.h.
+//
+//   k_hc_mix   one block per (row tile, slice of kHcSlice flattened inputs):
+//              the slice's dot products with every hc_fn row and its sum of
+//              squares
+//   k_hc_pre   per (row, hidden chunk): the row's slices added in order,
+//              normalised and split (pre and post by sigmoid, comb by exp
+//              and Sinkhorn rounds with one lane per (output, input) stream
+//              pair), then FFN input = sum_i pre_i * state_i
+//   k_hc_post  new_j = post_j * ffn_output + sum_i comb[j][i] * state_i
+//
+// Everything is f32 with sums in a fixed order (bitwise reproducible).
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kHcThreads = 256;
+constexpr int kHcWaves = kHcThreads / kWave;
+static_assert(kHcSlice == 4 * kHcThreads, "four flattened inputs per thread");
+
+template <int HC>
+__global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
+  constexpr int MW = (2 + HC) * HC, V = MW + 1;  // mixes, then the sum of squares
+  const int tile = blockIdx.x, sl = blockIdx.y;
+  const int t = threadIdx.x, wv = t / kWave, lane = t % kWave;
+  const int64_t r0 = (int64_t)tile * kHcRows;
+  const int nr = a.R - r0 < kHcRows ? (int)(a.R - r0) : kHcRows;
+  const int K = HC * a.H;
+  const int k = sl * kHcSlice + 4 * t;
+
+  float acc[kHcRows][V];
+#pragma unroll
+  for (int r = 0; r < kHcRows; ++r)
+#pragma unroll
+    for (int m = 0; m < V; ++m) acc[r][m] = 0.f;
+  if (k < K) {  // K is a multiple of 4
+    float w[MW][4];
+#pragma unroll
+    for (int m = 0; m < MW; ++m) {
+      const uint2 q = *(const uint2*)(a.fn + (int64_t)m * K + k);
+      w[m][0] = bf16lo(q.x); w[m][1] = bf16hi(q.x); w[m][2] = bf16lo(q.y); w[m][3] = bf16hi(q.y);
+    }
+#pragma unroll
+    for (int r = 0; r < kHcRows; ++r) {
+      if (r < nr) {
+        const float4 s = *(const float4*)(a.state + (r0 + r) * K + k);
+        acc[r][MW] = fmaf(s.x, s.x, fmaf(s.y, s.y, fmaf(s.z, s.z, s.w * s.w)));
+#pragma unroll
+        for (int m = 0; m < MW; ++m) acc[r][m] = fmaf(s.x, w[m][0], fmaf(s.y, w[m][1], fmaf(s.z, w[m][2], s.w * w[m][3])));
+      }
+    }
+  }
+  // block sums: each wave, then the waves in order
+  __shared__ float s_part[kHcWaves][kHcRows * V];
+#pragma unroll
+  for (int r = 0; r < kHcRows; ++r) {
+    if (r < nr) {  // block-uniform
+#pragma unroll
+      for (int m = 0; m < V; ++m) {
+        const float v = wave_sum(acc[r][m]);
+        if (lane == 0) s_part[wv][r * V + m] = v;
+      }
+    }
+  }
+  __syncthreads();
+  float* part = a.partial + ((int64_t)tile * a.slices + sl) * (kHcRows * V);
+  for (int q = t; q < nr * V; q += kHcThreads) {
+    float v = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kHcWaves; ++w2) v += s_part[w2][q];
+    part[q] = v;
+  }
+}
+
+// One row's split, then its FFN input for 4 hidden values per thread.
+// Lane m of wave 0 adds mix m over the row's slices in order; lanes 0-15
+// normalise and split: lane 4j + i holds comb entry (j, i) through the Sinkhorn rounds
+// (row sums over the lanes of one j, column sums over the lanes of one i).
+// Every hidden chunk of a row repeats the split; chunk 0 stores the mixes
+// and maps.
+template <int HC>
+__global__ __launch_bounds__(kHcThreads) void k_hc_pre(const HcArgs a) {
+  constexpr int MW = (2 + HC) * HC, V = MW + 1;
+  const int64_t r = blockIdx.x;
+  const int t = threadIdx.x;
+  __shared__ float s_map[MW];
+  __shared__ float s_sum[V];
+  if (t < V) {  // mix t (t = MW: the sum of squares) over the slices, in order
+    const float* part = a.partial + (r / kHcRows) * a.slices * (kHcRows * V) + (r % kHcRows) * V + t;
+    float v = 0.f;
+#pragma unroll 8
+    for (int64_t s2 = 0; s2 < a.slices; ++s2) v += part[s2 * (kHcRows * V)];
+    s_sum[t] = v;
+  }
+  __syncthreads();
+  if (t < 16) {
+    const int j = t / 4, i = t % 4;
+    float mix[V];  // entries t, t + 16, ... are this lane's to store
+#pragma unroll
+    for (int m = 0; m < V; ++m) mix[m] = s_sum[m];
+    const float rinv = 1.0f / sqrtf(mix[MW] / (float)(HC * a.H) + a.eps);
+#pragma unroll
+    for (int m = 0; m < MW; ++m) mix[m] *= rinv;
+    const bool in = j < HC && i < HC;
+    if (in && i == 0) {  // pre_j and post_j
+      s_map[j] = 1.0f / (1.0f + expf(-(a.scale[0] * mix[j] + a.base[j])));
+      s_map[HC + j] = 2.0f / (1.0f + expf(-(a.scale[1] * mix[HC + j] + a.base[HC + j])));
+    }
+    float c = 0.f;
+    if (in) c = expf(a.scale[2] * mix[2 * HC + j * HC + i] + a.base[2 * HC + j * HC + i]);
+    for (int it = 0; it < a.iters; ++it) {
+      float rs = c + __shfl_xor(c, 1, kWave);
+      rs += __shfl_xor(rs, 2, kWave);
+      c = in ? c / rs : 0.f;
+      float cs = c + __shfl_xor(c, 4, kWave);
+      cs += __shfl_xor(cs, 8, kWave);
+      c = in ? c / cs : 0.f;
+    }
+    if (in) s_map[2 * HC + j * HC + i] = c;
+    if (blockIdx.y == 0) {
+#pragma unroll
+      for (int m = 0; m < MW; ++m)
+        if (m % 16 == t) a.mixes[r * MW + m] = mix[m];
+    }
+  }
+  __syncthreads();
+  if (blockIdx.y == 0)
+    for (int m = t; m < MW; m += kHcThreads) a.maps[r * MW + m] = s_map[m];
+  const int h = (blockIdx.y * kHcThreads + t) * 4;
+  if (h >= a.H) return;
+  const float* st = a.state + r * HC * a.H + h;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < HC; ++i) {
+    const float p = s_map[i];
+    const float4 s = *(const float4*)(st + (int64_t)i * a.H);
+    x.x = fmaf(p, s.x, x.x); x.y = fmaf(p, s.y, x.y); x.z = fmaf(p, s.z, x.z); x.w = fmaf(p, s.w, x.w);
+  }
+  *(float4*)(a.ffn_in + r * a.H + h) = x;
+}
+
+// new state: 4 hidden values of every stream per thread
+template <int HC>
+__global__ __launch_bounds__(kHcThreads) void k_hc_post(const HcArgs a) {
+  constexpr int MW = (2 + HC) * HC;
+  const int64_t r = blockIdx.x;
+  const int h = (blockIdx.y * kHcThreads + threadIdx.x) * 4;
+  if (h >= a.H) return;
+  const float* mp = a.maps + r * MW;
+  float4 s[HC];
+#pragma unroll
+  for (int i = 0; i < HC; ++i) s[i] = *(const float4*)(a.state + (r * HC + i) * a.H + h);
+  const float4 f = *(const float4*)(a.ffn_out + r * a.H + h);
+#pragma unroll
+  for (int j = 0; j < HC; ++j) {
+    const float p = mp[HC + j];
+    float4 o = make_float4(p * f.x, p * f.y, p * f.z, p * f.w);
+#pragma unroll
+    for (int i = 0; i < HC; ++i) {
+      const float c = mp[2 * HC + j * HC + i];
+      o.x = fmaf(c, s[i].x, o.x); o.y = fmaf(c, s[i].y, o.y); o.z = fmaf(c, s[i].z, o.z); o.w = fmaf(c, s[i].w, o.w);
+    }
+    *(float4*)(a.out + (r * HC + j) * a.H + h) = o;
+  }
+}
+
+template <int HC>
+hipError_t run_hc_pre_t(const HcArgs& a, hipStream_t s) {
+  HcArgs args = a;
+  hipError_t err = launch("hc_mix", (const void*)k_hc_mix<HC>,
+                          dim3((unsigned)((a.R + kHcRows - 1) / kHcRows), (unsigned)a.slices), dim3(kHcThreads), 0, s,
+                          &args);
+  if (err != hipSuccess) return err;
+  return launch("hc_pre", (const void*)k_hc_pre<HC>, dim3(a.R, (a.H / 4 + kHcThreads - 1) / kHcThreads),
+                dim3(kHcThreads), 0, s, &args);
+}
+
+template <int HC>
+hipError_t run_hc_post_t(const HcArgs& a, hipStream_t s) {
+  HcArgs args = a;
+  return launch("hc_post", (const void*)k_hc_post<HC>, dim3(a.R, (a.H / 4 + kHcThreads - 1) / kHcThreads),
+                dim3(kHcThreads), 0, s, &args);
+}
+
+}  // namespace
+
+hipError_t run_hc_pre(const HcArgs& a, hipStream_t s) {
+  switch (a.hc) {
+    case 1: return run_hc_pre_t<1>(a, s);
+    case 2: return run_hc_pre_t<2>(a, s);
+    case 3: return run_hc_pre_t<3>(a, s);
+    case 4: return run_hc_pre_t<4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t run_hc_post(const HcArgs& a, hipStream_t s) {
+  switch (a.hc) {
+    case 1: return run_hc_post_t<1>(a, s);
+    case 2: return run_hc_post_t<2>(a, s);
+    case 3: return run_hc_post_t<3>(a, s);
+    case 4: return run_hc_post_t<4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

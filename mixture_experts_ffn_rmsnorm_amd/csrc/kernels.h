@@ -67,6 +67,27 @@ struct FwdArgs {
 hipError_t run_decode(const FwdArgs& a, hipStream_t s);
 hipError_t run_prefill(const FwdArgs& a, hipStream_t s);
 
+// The hyper-connection wrapper's launches (hc.hip).
+struct HcArgs {
+  int R, H, hc, iters;
+  float eps;
+  int64_t slices;
+  const float* state;    // [R][hc][H]
+  const uint16_t* fn;    // bf16 [(2+hc)*hc][hc*H]
+  const float* scale;    // [3]
+  const float* base;     // [(2+hc)*hc]
+  float* mixes;          // [R][(2+hc)*hc]
+  float* maps;           // [R][(2+hc)*hc]
+  float* partial;
+  float* ffn_in;         // [R][H]
+  const float* ffn_out;  // [R][H]
+  float* out;            // [R][hc][H]
+};
+// mixes (one launch), then split and FFN input (one launch), before the FFN
+hipError_t run_hc_pre(const HcArgs& a, hipStream_t s);
+// the new state (after the FFN)
+hipError_t run_hc_post(const HcArgs& a, hipStream_t s);
+
 struct RouteArgs {
   int R, E, K, layer_kind;
   int64_t table_rows;

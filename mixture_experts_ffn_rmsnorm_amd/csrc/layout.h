@@ -120,4 +120,47 @@ inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
   return true;
 }
 
+// Hyper-connection wrapper (moe_ffn_forward_hc): the FFN's layout at offset
+// 0, then the wrapper's intermediates.  The mix launch works on tiles of
+// kHcRows rows x kHcSlice flattened inputs and leaves one partial sum per
+// tile and slice; the next launch adds them.
+constexpr int kHcMax = 4;       // streams
+constexpr int kHcRows = 4;      // rows per mix tile
+constexpr int kHcSlice = 1024;  // flattened state values per mix block
+struct HcLayout {
+  Layout ffn;
+  int64_t tiles, slices;
+  size_t mixes;    // f32 [R][(2+hc)*hc]
+  size_t maps;     // f32 [R][(2+hc)*hc]  pre | post | comb (output stream, input stream)
+  size_t ffn_in;   // f32 [R][H]
+  size_t ffn_out;  // f32 [R][H]
+  size_t partial;  // f32 [tiles][slices][kHcRows][(2+hc)*hc + 1]  partial dots, then the sum of squares
+  size_t total;
+};
+
+inline bool make_hc_layout(int64_t R, int H, int E, int K, int I, int hc, HcLayout* L) {
+  if (hc < 1 || hc > kHcMax || !make_layout(R, H, E, K, I, &L->ffn)) return false;
+  const unsigned __int128 lim = (unsigned __int128)1 << 62;
+  const unsigned __int128 r = (unsigned __int128)R;
+  const int mw = (2 + hc) * hc;
+  L->tiles = (R + kHcRows - 1) / kHcRows;
+  L->slices = ((int64_t)hc * H + kHcSlice - 1) / kHcSlice;
+  unsigned __int128 off = L->ffn.total;
+  auto take = [&](unsigned __int128 bytes) -> size_t {
+    off = (off + 255) / 256 * 256;
+    size_t at = (size_t)off;
+    off += bytes;
+    return at;
+  };
+  L->mixes = take(r * mw * 4);
+  L->maps = take(r * mw * 4);
+  L->ffn_in = take(r * H * 4);
+  L->ffn_out = take(r * H * 4);
+  L->partial = take((unsigned __int128)L->tiles * L->slices * kHcRows * (mw + 1) * 4);
+  off = (off + 255) / 256 * 256;
+  if (off >= lim) return false;
+  L->total = (size_t)off;
+  return true;
+}
+
 }  // namespace moe

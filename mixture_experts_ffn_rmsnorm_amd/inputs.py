@@ -19,6 +19,12 @@ Recipe (per tensor an independent stream):
     E4M3 codes of N(0,1) * 8 samples (rounded to E4M3 by torch) and one
     E8M0 scale per 32 inputs drawn from 2^-10, 2^-9, 2^-8, from torch's
     generator with one seed per (tensor, expert) as above.
+  * Hyper-connection wrapper (hc residual streams): the state is N(0,1) per
+    stream (like x); hc_fn is bf16 N(0, 0.02) [(2+hc)*hc, hc*hidden] (mixes
+    of standard deviation 0.02 * sqrt(hc*hidden), 2.6 at the full shape);
+    hc_scale = (0.25, 0.25, 0.5); hc_base: pre and post offsets N(0, 0.5),
+    comb offsets 2 on the diagonal plus N(0, 0.5) (a residual mix near the
+    identity); 20 Sinkhorn rounds.
 """
 
 from __future__ import annotations
@@ -33,6 +39,9 @@ LAYER_HASH = 1
 # tensor ids of the per-tensor streams
 _T_X, _T_TOK, _T_NORM, _T_ROUTER, _T_BIAS, _T_TABLE, _T_HOT = 1, 2, 3, 4, 5, 6, 7
 _T_GATE, _T_UP, _T_DOWN, _T_SGATE, _T_SUP, _T_SDOWN = 10, 11, 12, 13, 14, 15
+_T_HC_STATE, _T_HC_FN, _T_HC_BASE = 40, 41, 42
+HC_SCALE = (0.25, 0.25, 0.5)
+HC_ITERS = 20
 
 
 @dataclasses.dataclass(frozen=True)
@@ -280,3 +289,27 @@ def bf16_tensor_bits(t) -> np.ndarray:
     import torch
 
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@dataclasses.dataclass
+class HcInputs:
+    """The hyper-connection wrapper's state and parameters, numpy."""
+    state: np.ndarray     # f32 [rows, hc, hidden]
+    hc_fn: np.ndarray     # bf16 bits [(2+hc)*hc, hc*hidden]
+    hc_scale: np.ndarray  # f32 [3]
+    hc_base: np.ndarray   # f32 [(2+hc)*hc]
+    hc: int
+    iters: int
+
+
+def hc_inputs(cfg: Config, hc: int = 4, layer: int = 0, rows: int | None = None) -> HcInputs:
+    """Seeded state and wrapper parameters (recipe in the module docstring)."""
+    ls = cfg.param_seed + 7919 * layer
+    R = cfg.rows if rows is None else rows
+    mw = (2 + hc) * hc
+    state = _rng(cfg.seed, _T_HC_STATE, hc).standard_normal((R, hc, cfg.hidden), dtype=np.float32)
+    fn = _normal_bf16(ls, _T_HC_FN, hc, (mw, hc * cfg.hidden), 0.02)
+    base = (0.5 * _rng(ls, _T_HC_BASE, hc).standard_normal(mw, dtype=np.float32)).astype(np.float32)
+    base[2 * hc:] += (2.0 * np.eye(hc, dtype=np.float32)).reshape(-1)
+    return HcInputs(state=state, hc_fn=fn, hc_scale=np.array(HC_SCALE, dtype=np.float32), hc_base=base, hc=hc,
+                    iters=HC_ITERS)

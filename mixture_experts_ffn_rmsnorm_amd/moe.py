@@ -20,7 +20,7 @@ FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY, FLAG_SYNC_TIMEOUT, FLAG_F16_RANGE = 1, 2, 
 
 # Function names the header declares (checked against the library's exports).
 EXPORTS = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp8", "moe_ffn_forward_noalloc",
-           "moe_route",
+           "moe_ffn_hc_workspace_bytes", "moe_ffn_forward_hc", "moe_ffn_hc_view", "moe_route",
            "moe_ffn_routing_view", "moe_ffn_status", "moe_strerror", "moe_ffn_stage_timing_begin",
            "moe_ffn_stage_timing_end")
 
@@ -51,7 +51,14 @@ class MxWeightsC(ctypes.Structure):
                [(n, MxMatrixC) for n in ("gate_exps", "up_exps", "down_exps", "gate_sh", "up_sh", "down_sh")]
 
 
+class HcWeightsC(ctypes.Structure):
+    _fields_ = [("hc_fn", ctypes.c_void_p), ("hc_scale", ctypes.c_void_p), ("hc_base", ctypes.c_void_p),
+                ("hc", ctypes.c_int32), ("sinkhorn_iters", ctypes.c_int32)]
+
+
 MX_BLOCK = 32
+HC_MAX = 4
+HC_MAX_ITERS = 1000
 _lib = None
 
 
@@ -69,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward_mxfp8.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(MxWeightsC), P, P, SZ,
                                             P]
         L.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P]
+        L.moe_ffn_hc_workspace_bytes.argtypes = [ctypes.POINTER(Dims), I32, I64, ctypes.POINTER(SZ)]
+        L.moe_ffn_forward_hc.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC),
+                                         ctypes.POINTER(HcWeightsC), P, P, SZ, P]
+        L.moe_ffn_hc_view.argtypes = [ctypes.POINTER(Dims), I32, I64, P, SZ] + [ctypes.POINTER(P)] * 4
         L.moe_route.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, P]
         L.moe_ffn_routing_view.argtypes = [ctypes.POINTER(Dims), I64, P, SZ, ctypes.POINTER(P), ctypes.POINTER(P),
                                            ctypes.POINTER(P)]
@@ -170,6 +181,56 @@ def forward_noalloc(dims: Dims, x, token_ids, layer_kind: int, weights: WeightsC
                                        ctypes.byref(weights), _ptr(out), _stream(stream))
     _check(rc, "moe_ffn_forward_noalloc")
     return out
+
+
+def make_hc_weights(hc_fn, hc_scale, hc_base, hc: int, sinkhorn_iters: int) -> HcWeightsC:
+    """The hyper-connection parameters: ``hc_fn`` bf16 [(2+hc)*hc, hc*hidden],
+    ``hc_scale`` f32 [3], ``hc_base`` f32 [(2+hc)*hc] device tensors (they
+    must outlive every call that uses the struct)."""
+    return HcWeightsC(hc_fn.data_ptr(), hc_scale.data_ptr(), hc_base.data_ptr(), int(hc), int(sinkhorn_iters))
+
+
+def hc_workspace_bytes(dims: Dims, hc: int, rows: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_ffn_hc_workspace_bytes(ctypes.byref(dims), int(hc), int(rows), ctypes.byref(n)),
+           "moe_ffn_hc_workspace_bytes")
+    return n.value
+
+
+def alloc_hc_workspace(dims: Dims, hc: int, rows: int, device="cuda"):
+    """A zero-filled workspace for ``forward_hc``."""
+    import torch
+
+    return torch.zeros(hc_workspace_bytes(dims, hc, rows), dtype=torch.uint8, device=device)
+
+
+def forward_hc(dims: Dims, state, token_ids, layer_kind: int, weights: WeightsC, hc_weights: HcWeightsC, out,
+               workspace, stream=None):
+    """``out[rows, hc, hidden]`` = the hyper-connection-wrapped layer of
+    ``state[rows, hc, hidden]``; enqueue only."""
+    rc = lib().moe_ffn_forward_hc(ctypes.byref(dims), _ptr(state), _ptr(token_ids), state.shape[0], int(layer_kind),
+                                  ctypes.byref(weights), ctypes.byref(hc_weights), _ptr(out), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+    _check(rc, "moe_ffn_forward_hc")
+    return out
+
+
+def hc_view(dims: Dims, hc: int, rows: int, workspace):
+    """Device tensors (views into ``workspace``) of the last ``forward_hc``'s
+    mixes and maps [rows, (2+hc)*hc], FFN input and FFN output [rows, hidden]."""
+    import torch
+
+    ps = [ctypes.c_void_p() for _ in range(4)]
+    _check(lib().moe_ffn_hc_view(ctypes.byref(dims), int(hc), int(rows), _ptr(workspace), workspace.numel(),
+                                 *[ctypes.byref(p) for p in ps]), "moe_ffn_hc_view")
+    base, mw, H = workspace.data_ptr(), (2 + hc) * hc, dims.hidden
+
+    def view(p, n, cols):
+        off = p.value - base
+        return workspace[off:off + 4 * n].view(torch.float32).view(rows, cols)
+
+    return (view(ps[0], rows * mw, mw), view(ps[1], rows * mw, mw), view(ps[2], rows * H, H),
+            view(ps[3], rows * H, H))
 
 
 def route(dims: Dims, logits, token_ids, layer_kind: int, weights: WeightsC, idx, w, stream=None):

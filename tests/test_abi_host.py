@@ -324,3 +324,86 @@ def test_mxfp8_forward_rejects_on_host():
     assert call(_mx_weights(), kind=9) == moe.MOE_EINVAL
     assert call(_mx_weights(), dims=moe.make_dims(4096, 128, 6, 2048)) == moe.MOE_EUNSUPPORTED
     assert call(_mx_weights(), rows=(1 << 24) + 1) == moe.MOE_EOVERFLOW
+
+
+def test_hc_struct_layout_matches_header():
+    src = r"""
+    #include <stdio.h>
+    #include <stddef.h>
+    #include "moe_ffn.h"
+    int main(void) {
+      printf("%zu %zu %zu %d %d\n", sizeof(moe_hc_weights_t), offsetof(moe_hc_weights_t, hc),
+             offsetof(moe_hc_weights_t, sinkhorn_iters), MOE_HC_MAX, MOE_HC_MAX_ITERS);
+      return 0;
+    }"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        got = list(map(int, subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()))
+    assert got == [ctypes.sizeof(moe.HcWeightsC), moe.HcWeightsC.hc.offset, moe.HcWeightsC.sinkhorn_iters.offset,
+                   moe.HC_MAX, moe.HC_MAX_ITERS]
+
+
+def test_hc_workspace_bytes_and_view():
+    """The wrapper's workspace holds the FFN's layout at offset 0 plus the
+    mixes, maps, FFN input and output; the view points inside it."""
+    L = moe.lib()
+    for dims, rows in ((moe.make_dims(**FULL, table_rows=131072), 1), (moe.make_dims(**TINY), 37)):
+        n = ctypes.c_size_t(0)
+        for hc in (0, 5):
+            assert L.moe_ffn_hc_workspace_bytes(ctypes.byref(dims), hc, rows, ctypes.byref(n)) == \
+                moe.MOE_EUNSUPPORTED
+        assert L.moe_ffn_hc_workspace_bytes(ctypes.byref(dims), 4, rows, None) == moe.MOE_EINVAL
+        base = moe.workspace_bytes(dims, rows)
+        for hc in (1, 4):
+            total = moe.hc_workspace_bytes(dims, hc, rows)
+            mw, H = (2 + hc) * hc, dims.hidden
+            assert total >= base + rows * (2 * mw + 2 * H) * 4
+            ps = [ctypes.c_void_p() for _ in range(4)]
+            assert L.moe_ffn_hc_view(ctypes.byref(dims), hc, rows, FAKE, total, *[ctypes.byref(p) for p in ps]) == 0
+            offs = [p.value - FAKE for p in ps]
+            assert offs[0] >= base and offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+            assert offs[1] - offs[0] >= rows * mw * 4 and offs[3] - offs[2] >= rows * H * 4
+            assert offs[3] + rows * H * 4 <= total
+            assert L.moe_ffn_hc_view(ctypes.byref(dims), hc, rows, FAKE, total - 1,
+                                     *[ctypes.byref(p) for p in ps]) == moe.MOE_EWORKSPACE
+
+
+def test_hc_forward_rejects_on_host():
+    """Every malformed wrapper call fails on the host with its documented
+    code before any HIP call."""
+    d = moe.make_dims(**FULL, table_rows=131072)
+    L = moe.lib()
+    good = moe.HcWeightsC(FAKE, FAKE + 256, FAKE + 512, 4, 20)
+    S = FAKE + (4 << 30)  # state_out, clear of state_in (FAKE) and the workspace
+
+    def call(hw=good, rows=4, state=FAKE, out=S, ws=FAKE + (8 << 30), wsb=1 << 40, kind=moe.LAYER_SCORE, w=None):
+        w = _weights() if w is None else w
+        return L.moe_ffn_forward_hc(ctypes.byref(d), state, FAKE, rows, kind, ctypes.byref(w),
+                                    None if hw is None else ctypes.byref(hw), out, ws, wsb, None)
+
+    def hw(**kw):
+        f = dict(hc_fn=FAKE, hc_scale=FAKE + 256, hc_base=FAKE + 512, hc=4, sinkhorn_iters=20)
+        f.update(kw)
+        return moe.HcWeightsC(f["hc_fn"], f["hc_scale"], f["hc_base"], f["hc"], f["sinkhorn_iters"])
+
+    assert call(hw=None) == moe.MOE_EINVAL
+    assert call(hw=hw(hc=0)) == moe.MOE_EUNSUPPORTED
+    assert call(hw=hw(hc=5)) == moe.MOE_EUNSUPPORTED
+    assert call(hw=hw(sinkhorn_iters=0)) == moe.MOE_EINVAL
+    assert call(hw=hw(sinkhorn_iters=moe.HC_MAX_ITERS + 1)) == moe.MOE_EINVAL
+    assert call(hw=hw(hc_fn=None)) == moe.MOE_EINVAL
+    assert call(hw=hw(hc_fn=FAKE + 8)) == moe.MOE_EINVAL
+    assert call(hw=hw(hc_base=None)) == moe.MOE_EINVAL
+    assert call(hw=hw(hc_scale=FAKE + 2)) == moe.MOE_EINVAL
+    assert call(state=None) == moe.MOE_EINVAL
+    assert call(out=S + 4) == moe.MOE_EINVAL
+    assert call(rows=0) == moe.MOE_EINVAL
+    assert call(kind=moe.LAYER_HASH, w=_weights(table=False)) == moe.MOE_EINVAL
+    assert call(out=FAKE + 4096 * 4) == moe.MOE_EOVERLAP              # inside state_in
+    assert call(ws=S + 64 * 1024) == moe.MOE_EOVERLAP                 # workspace inside state_out
+    assert call(wsb=1024) == moe.MOE_EWORKSPACE
+    assert call(ws=FAKE + (8 << 30) + 16) == moe.MOE_EWORKSPACE
+    assert call(rows=(1 << 24) + 1) == moe.MOE_EOVERFLOW
