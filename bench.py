@@ -46,7 +46,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def alg_bytes(kernel, cfg, U, R):
+def alg_bytes(kernel, cfg, U, R, hc=4):
     """Algorithmic HBM bytes of one launch: every touched weight once, plus
     activations in and out (U = distinct routed experts of the step; a
     routed (expert, row) pair per slot, R*K of them).  Launch names ending in
@@ -81,6 +81,13 @@ def alg_bytes(kernel, cfg, U, R):
         return U * H * I * wb + S * I * 2 + S * H * 2
     if kernel == "gemm_down_shared_reduce":  # shared expert + weighted reduce of d16
         return H * I * wb + R * I * 2 + S * H * 2 + R * H * 4 + S * 12
+    mw = (2 + hc) * hc  # hyper-connection wrapper: hc streams of H per row
+    if kernel == "hc_mix":           # state in, hc_fn once, partial sums out
+        return R * hc * H * 4 + mw * hc * H * 2 + R * (mw + 1) * 4 * ((hc * H + 1023) // 1024)
+    if kernel == "hc_pre":           # partial sums and state in; mixes, maps, FFN input out
+        return R * (mw + 1) * 4 * ((hc * H + 1023) // 1024) + R * hc * H * 4 + 2 * R * mw * 4 + R * H * 4
+    if kernel == "hc_post":          # state, maps and FFN output in; new state out
+        return 2 * R * hc * H * 4 + R * mw * 4 + R * H * 4
     return None
 
 
@@ -111,6 +118,10 @@ def step_bytes(cfg, U, R, fmt="bf16"):
     H, I, E = cfg.hidden, cfg.inter, cfg.experts
     return (U + 1) * EXPERT_BYTES(H, I, WEIGHT_BYTES[fmt]) + E * H * 2 + 2 * R * H * 4 + H * 4 + E * 4
 
+
+# the hyper-connection-wrapped layer (moe_ffn_forward_hc, hc streams), bf16
+HC_WORKLOADS = ("decode-r1-score", "prefill-r512-score")
+HC_STREAMS = 4
 
 SUB_WORKLOADS = ("decode-cohort-r4-hash", "prefill-r512-score", "prefill-r8192-score-skewed")
 # the same workloads with MXFP8 expert weights (moe_ffn_forward_mxfp8)
@@ -284,6 +295,60 @@ def time_workload(cfg, layers, steps, warmup, graph=False):
     return rec, gpu0
 
 
+def time_hc(cfg, layers, hc, steps, warmup, ffn_ms):
+    """The wrapped layer (moe_ffn_forward_hc) on the same layers: time per
+    step, the wrapper's kernels against their algorithmic bytes, and what
+    the wrapper adds to the bare layer's step."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_ffn_rmsnorm_amd import inputs as gen
+    from mixture_experts_ffn_rmsnorm_amd import moe
+
+    R, L = cfg.rows, len(layers)
+    dims = moe.dims_of(cfg)
+    h = gen.hc_inputs(cfg, hc)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    fn = t(h.hc_fn.view(np.int16)).view(torch.bfloat16)
+    sc, base = t(h.hc_scale), t(h.hc_base)
+    hw = moe.make_hc_weights(fn, sc, base, hc, h.iters)
+    state = t(h.state)
+    tok = t(layers[0][0].token_ids)
+    out = torch.empty_like(state)
+    ws = moe.alloc_hc_workspace(dims, hc, R)
+
+    def step(i):
+        moe.forward_hc(dims, state, tok, cfg.layer_kind, layers[i % L][2], hw, out, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    moe.stage_timing_begin()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    stages = moe.stage_timing_end()
+    kernels = {}
+    for name, (kms, n) in stages.items():
+        k = {"avg_us": kms * 1e3 / n, "launches": n}
+        if name.startswith("hc_"):
+            b = alg_bytes(name, cfg, 0, R, hc)
+            k["alg_bytes"] = b
+            k["hbm_frac"] = b / (k["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS
+        kernels[name] = k
+    wrapper_us = sum(k["avg_us"] for n, k in kernels.items() if n.startswith("hc_"))
+    log(f"{cfg.name} hc{hc}: {ms * 1e3:.1f} us per step ({ffn_ms * 1e3:.1f} bare), wrapper kernels {wrapper_us:.1f} us")
+    del state, out, ws
+    return {"rows": R, "hc": hc, "rows_per_s": R / (ms / 1e3), "ms_per_step": ms, "bare_ms_per_step": ffn_ms,
+            "added_us_per_step": (ms - ffn_ms) * 1e3, "wrapper_kernels_us": wrapper_us, "kernels": kernels,
+            "dtype": "f32" if R <= 4 else "f16", "weights": "bf16"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,7 +381,8 @@ def main():
     moe.lib()  # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
     cfg = gen.config(args.workload)
-    subs = [] if (args.only or cfg.hidden != 4096) else [gen.config(n) for n in SUB_WORKLOADS if n != cfg.name]
+    subs = [] if (args.only or cfg.hidden != 4096 or args.weights != "bf16") else \
+        [gen.config(n) for n in SUB_WORKLOADS if n != cfg.name]
     nl = lambda c: args.layers or (4 if c.rows <= 4 else 1)
     L = max([nl(cfg)] + [nl(c) for c in subs])
     log(f"workload {cfg.name} (+ {len(subs)} more): drawing {L} layers of weights on the GPU")
@@ -350,6 +416,13 @@ def main():
         res["workloads"][c.name] = r_c
         sub_gpu[c.name] = (lay_c[0], g_c)
         torch.cuda.empty_cache()
+    if subs:
+        for name in HC_WORKLOADS:
+            c = gen.config(name)
+            lay_c = bind_layers(c, big, nl(c))
+            base_ms = rec["ms_per_step"] if c.name == cfg.name else res["workloads"][c.name]["ms_per_step"]
+            res["workloads"][f"{c.name}-hc{HC_STREAMS}"] = time_hc(c, lay_c, HC_STREAMS, args.steps, args.warmup,
+                                                                    base_ms)
     mx_gpu = {}
     if subs:
         mx_cfgs = [gen.config(n) for n in MX_WORKLOADS]

@@ -25,6 +25,31 @@ namespace {
 
 constexpr int kHcThreads = 256;
 constexpr int kHcWaves = kHcThreads / kWave;
+
+// v moved across lanes inside each 16-lane row by a DPP control (all lanes
+// active): quad_perm [1,0,3,2] (0xB1) and [2,3,0,1] (0x4E) swap lane bit 0 /
+// bit 1, row_half_mirror (0x141) and row_mirror (0x140) reverse 8 / 16
+// lanes, row_ror:n (0x120 + n) rotates the row by n lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Sum over the 16 lanes of each row, in every lane of the row: after the
+// two quad swaps every lane holds its quad's sum, the half mirror adds the
+// other quad of its 8, the mirror the other 8 of its row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  return v + dpp<0x140>(v);
+}
+// Sum over the whole wave (the four rows added in order), wave-uniform.
+__device__ __forceinline__ float wave_total(float v) {
+  v = row16_sum(v);
+  const int b = __float_as_int(v);
+  return ((__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 32))) + __int_as_float(__builtin_amdgcn_readlane(b, 48));
+}
 static_assert(kHcSlice == 4 * kHcThreads, "four flattened inputs per thread");
 
 template <int HC>
@@ -66,7 +91,7 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
     if (r < nr) {  // block-uniform
 #pragma unroll
       for (int m = 0; m < V; ++m) {
-        const float v = wave_sum(acc[r][m]);
+        const float v = wave_total(acc[r][m]);
         if (lane == 0) s_part[wv][r * V + m] = v;
       }
     }
@@ -83,8 +108,10 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
 
 // One row's split, then its FFN input for 4 hidden values per thread.
 // Lane m of wave 0 adds mix m over the row's slices in order; lanes 0-15
-// normalise and split: lane 4j + i holds comb entry (j, i) through the Sinkhorn rounds
-// (row sums over the lanes of one j, column sums over the lanes of one i).
+// normalise and split: lane 4j + i holds comb entry (j, i) through the
+// Sinkhorn rounds (row sums over the lanes of one j, column sums over the
+// lanes of one i, by DPP moves; each division is a reciprocal and a
+// multiply, within 2 ulp).
 // Every hidden chunk of a row repeats the split; chunk 0 stores the mixes
 // and maps.
 template <int HC>
@@ -102,31 +129,33 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_pre(const HcArgs a) {
     s_sum[t] = v;
   }
   __syncthreads();
-  if (t < 16) {
-    const int j = t / 4, i = t % 4;
+  if (t < kWave) {  // wave 0 (every lane active for the DPP moves); lanes 0-15 keep the result
+    const int j = (t / 4) % 4, i = t % 4;
     float mix[V];  // entries t, t + 16, ... are this lane's to store
 #pragma unroll
     for (int m = 0; m < V; ++m) mix[m] = s_sum[m];
     const float rinv = 1.0f / sqrtf(mix[MW] / (float)(HC * a.H) + a.eps);
 #pragma unroll
     for (int m = 0; m < MW; ++m) mix[m] *= rinv;
-    const bool in = j < HC && i < HC;
+    const bool in = j < HC && i < HC && t < 16;
     if (in && i == 0) {  // pre_j and post_j
       s_map[j] = 1.0f / (1.0f + expf(-(a.scale[0] * mix[j] + a.base[j])));
       s_map[HC + j] = 2.0f / (1.0f + expf(-(a.scale[1] * mix[HC + j] + a.base[HC + j])));
     }
     float c = 0.f;
     if (in) c = expf(a.scale[2] * mix[2 * HC + j * HC + i] + a.base[2 * HC + j * HC + i]);
+    // rows: the 4 lanes of one j are one quad; columns: the 4 lanes of one
+    // i are 4 apart in the row, reached by rotating it by 4 and by 8
     for (int it = 0; it < a.iters; ++it) {
-      float rs = c + __shfl_xor(c, 1, kWave);
-      rs += __shfl_xor(rs, 2, kWave);
-      c = in ? c / rs : 0.f;
-      float cs = c + __shfl_xor(c, 4, kWave);
-      cs += __shfl_xor(cs, 8, kWave);
-      c = in ? c / cs : 0.f;
+      float rs = c + dpp<0xB1>(c);
+      rs += dpp<0x4E>(rs);
+      c = in ? c * __builtin_amdgcn_rcpf(rs) : 0.f;
+      float cs = c + dpp<0x124>(c);
+      cs += dpp<0x128>(cs);
+      c = in ? c * __builtin_amdgcn_rcpf(cs) : 0.f;
     }
     if (in) s_map[2 * HC + j * HC + i] = c;
-    if (blockIdx.y == 0) {
+    if (blockIdx.y == 0 && t < 16) {
 #pragma unroll
       for (int m = 0; m < MW; ++m)
         if (m % 16 == t) a.mixes[r * MW + m] = mix[m];

@@ -107,7 +107,7 @@ def launch_name(kernel: str) -> str | None:
     else:
         mx = False
         base = {"k_pre_norm": "pre_norm", "k_pre_router": "pre_router", "k_pre_sort": "pre_sort",
-                "k_route": "route"}.get(name)
+                "k_route": "route", "k_hc_mix": "hc_mix", "k_hc_pre": "hc_pre", "k_hc_post": "hc_post"}.get(name)
     if base is None:
         return None
     return base + "_mx" if mx else base
@@ -187,7 +187,7 @@ def cmd_stats(args, extra):
 
 # counters are collected on this library's kernels only (the weight
 # generation's torch kernels run unprofiled)
-KERNEL_REGEX = "k_(dec|pre|gemm|route)"
+KERNEL_REGEX = "k_(dec|pre|gemm|route|hc)"
 
 
 def _pmc_pass(counter, cmd, out_dir, include=None):

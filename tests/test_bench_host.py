@@ -71,6 +71,9 @@ def test_profiled_kernel_names_map_to_launch_names():
         "k_gemm<2, 2048, 4096, moe::(anonymous namespace)::GemmCfg<256, 4, 256, 2, 64, 2>, true>(moe::FwdArgs)":
             "gemm_down_shared_reduce_mx",
         "k_route(moe::RouteArgs)": "route",
+        "k_hc_mix<4>(moe::HcArgs)": "hc_mix",
+        "k_hc_pre<4>(moe::HcArgs)": "hc_pre",
+        "k_hc_post<2>(moe::HcArgs)": "hc_post",
     }
     for kernel, name in cases.items():
         assert profiling.launch_name(ns + kernel) == name, kernel
