@@ -51,10 +51,31 @@ __device__ __forceinline__ float load_wt(const float* p) {
 // Every store this thread issued has completed.
 __device__ __forceinline__ void sync_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
+// v moved across lanes inside each 16-lane row by a DPP control (every
+// lane of the wave active): quad_perm [1,0,3,2] (0xB1) and [2,3,0,1] (0x4E)
+// swap lane bit 0 / bit 1, row_half_mirror (0x141) and row_mirror (0x140)
+// reverse 8 / 16 lanes, row_ror:n (0x120 + n) rotates the row by n lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Sum over the 16 lanes of each row, in every lane of the row: after the
+// two quad swaps every lane holds its quad's sum, the half mirror adds the
+// other quad of its 8, the mirror the other 8 of its row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  return v + dpp_f32<0x140>(v);
+}
+// Sum over the wave (every lane active), the same in every lane: the rows'
+// sums read out and added in row order.  DPP moves and lane reads instead
+// of LDS-crossbar shuffles: a handful of cycles each.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v = row16_sum(v);
+  const int b = __float_as_int(v);
+  return ((__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 32))) + __int_as_float(__builtin_amdgcn_readlane(b, 48));
 }
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }

@@ -26,32 +26,6 @@ namespace {
 constexpr int kHcThreads = 256;
 constexpr int kHcWaves = kHcThreads / kWave;
 
-// v moved across lanes inside each 16-lane row by a DPP control (all lanes
-// active): quad_perm [1,0,3,2] (0xB1) and [2,3,0,1] (0x4E) swap lane bit 0 /
-// bit 1, row_half_mirror (0x141) and row_mirror (0x140) reverse 8 / 16
-// lanes, row_ror:n (0x120 + n) rotates the row by n lanes.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-// Sum over the 16 lanes of each row, in every lane of the row: after the
-// two quad swaps every lane holds its quad's sum, the half mirror adds the
-// other quad of its 8, the mirror the other 8 of its row.
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
-  return v + dpp<0x140>(v);
-}
-// Sum over the whole wave (the four rows added in order), wave-uniform.
-__device__ __forceinline__ float wave_total(float v) {
-  v = row16_sum(v);
-  const int b = __float_as_int(v);
-  return ((__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
-          __int_as_float(__builtin_amdgcn_readlane(b, 32))) + __int_as_float(__builtin_amdgcn_readlane(b, 48));
-}
-static_assert(kHcSlice == 4 * kHcThreads, "four flattened inputs per thread");
-
 template <int HC>
 __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
   constexpr int MW = (2 + HC) * HC, V = MW + 1;  // mixes, then the sum of squares
@@ -91,7 +65,7 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
     if (r < nr) {  // block-uniform
 #pragma unroll
       for (int m = 0; m < V; ++m) {
-        const float v = wave_total(acc[r][m]);
+        const float v = wave_sum(acc[r][m]);
         if (lane == 0) s_part[wv][r * V + m] = v;
       }
     }
@@ -147,11 +121,11 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_pre(const HcArgs a) {
     // rows: the 4 lanes of one j are one quad; columns: the 4 lanes of one
     // i are 4 apart in the row, reached by rotating it by 4 and by 8
     for (int it = 0; it < a.iters; ++it) {
-      float rs = c + dpp<0xB1>(c);
-      rs += dpp<0x4E>(rs);
+      float rs = c + dpp_f32<0xB1>(c);
+      rs += dpp_f32<0x4E>(rs);
       c = in ? c * __builtin_amdgcn_rcpf(rs) : 0.f;
-      float cs = c + dpp<0x124>(c);
-      cs += dpp<0x128>(cs);
+      float cs = c + dpp_f32<0x124>(c);
+      cs += dpp_f32<0x128>(cs);
       c = in ? c * __builtin_amdgcn_rcpf(cs) : 0.f;
     }
     if (in) s_map[2 * HC + j * HC + i] = c;
