@@ -659,27 +659,27 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
 // group, then in blocks of 4 row tiles x 8 column tiles, and handed out so
 // that each XCD takes a contiguous run of them: the tiles that share
 // activation tiles and weight slices run at the same time behind one L2.
-constexpr int kGT = 512;  // threads per GEMM block: 8 waves, 2 per SIMD
-constexpr int GWN = 4;    // waves along the B rows (2 x 4 wave grid)
 constexpr int kSlab = 64; // epilogue rows staged per pass
 
 // Tile configurations: BM tile rows (WM A fragments per wave), BROWS tile B
 // rows (WN B fragments per wave), k-tiles of BK held in LDS as BK/64 halves
-// of 64 k (one 128-byte row each), a ring of STAGES k-tiles.
+// of 64 k (one 128-byte row each), a ring of STAGES k-tiles, THREADS / 64
+// waves in a grid of (THREADS / 64 / GWN) x GWN.
 //   Big: 256 x 256, BK 64, 2 stages -- groups of many rows.
 //   Small: 64 x 128, BK 128, 3 stages -- groups of a few rows, where the
 //   kernel mostly streams weights: a lane fetches the two adjacent 128-byte
 //   lines of a weight row back to back, so each row is read 256 bytes at a
 //   time (DRAM page locality), and two k-tiles are in flight per compute
 //   unit.
-template <int BM_, int WM_, int BROWS_, int WN_, int BK_, int STAGES_>
+template <int BM_, int WM_, int BROWS_, int WN_, int BK_, int STAGES_, int GWN_, int THREADS_>
 struct GemmCfg {
   static constexpr int BM = BM_, WM = WM_, BROWS = BROWS_, WN = WN_, BK = BK_, kStages = STAGES_;
-  static_assert(BM == 2 * WM * 32 && BROWS == GWN * WN * 32, "2 x 4 wave grid, 32-row fragments");
+  static constexpr int GWN = GWN_, kGT = THREADS_, GWM = THREADS_ / 64 / GWN_;  // wave grid GWM x GWN
+  static_assert(BM == GWM * WM * 32 && BROWS == GWN * WN * 32, "wave grid of 32-row fragments");
   static_assert(BK % 64 == 0, "k-tiles of whole 64-k halves");
 };
-using GemmBig = GemmCfg<256, 4, 256, 2, 64, 2>;
-using GemmSmall = GemmCfg<64, 1, 128, 1, 128, 3>;
+using GemmBig = GemmCfg<256, 4, 256, 2, 64, 2, 4, 512>;
+using GemmSmall = GemmCfg<64, 1, 128, 1, 128, 3, 4, 512>;
 
 // output columns per block tile
 template <int MODE, class Cfg>
@@ -688,8 +688,9 @@ struct GemmShape {
 };
 
 template <int MODE, int KD, int ND, class Cfg, bool MX>
-__global__ __launch_bounds__(kGT, 1) void k_gemm(const FwdArgs a) {
+__global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
   constexpr int BM = Cfg::BM, WM = Cfg::WM, BROWS = Cfg::BROWS, WN = Cfg::WN, BK = Cfg::BK;
+  constexpr int kGT = Cfg::kGT, GWN = Cfg::GWN;
   constexpr int kStages = Cfg::kStages;
   constexpr int BN = GemmShape<MODE, Cfg>::BN;
   constexpr int NT = ND / BN;                // column tiles per group
@@ -1315,11 +1316,11 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   const bool small = (int64_t)a.R * a.K <= 32LL * a.E;
   err = launch(MX ? "gemm_gateup_swiglu_mx" : "gemm_gateup_swiglu",
                small ? (const void*)k_gemm<0, H, I, GemmSmall, MX> : (const void*)k_gemm<0, H, I, GemmBig, MX>,
-               dim3(grid), dim3(kGT), 0, s, &args);
+               dim3(grid), dim3(small ? GemmSmall::kGT : GemmBig::kGT), 0, s, &args);
   if (err != hipSuccess) return err;
   err = launch(MX ? "gemm_down_mx" : "gemm_down",
                small ? (const void*)k_gemm<1, I, H, GemmSmall, MX> : (const void*)k_gemm<1, I, H, GemmBig, MX>,
-               dim3(grid), dim3(kGT), 0, s, &args);
+               dim3(grid), dim3(small ? GemmSmall::kGT : GemmBig::kGT), 0, s, &args);
   if (err != hipSuccess) return err;
   // the shared down covers R rows only: small tiles when big ones would
   // leave compute units idle
@@ -1330,7 +1331,7 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   const int sh_grid = sh_tiles < grid ? (int)sh_tiles : grid;
   return launch(MX ? "gemm_down_shared_reduce_mx" : "gemm_down_shared_reduce",
                 sh_small ? (const void*)k_gemm<2, I, H, GemmSmall, MX> : (const void*)k_gemm<2, I, H, GemmBig, MX>,
-                dim3(sh_grid), dim3(kGT), 0, s, &args);
+                dim3(sh_grid), dim3(sh_small ? GemmSmall::kGT : GemmBig::kGT), 0, s, &args);
 }
 
 }  // namespace
