@@ -19,6 +19,11 @@ Recipe (per tensor an independent stream):
     E4M3 codes of N(0,1) * 8 samples (rounded to E4M3 by torch) and one
     E8M0 scale per 32 inputs drawn from 2^-10, 2^-9, 2^-8, from torch's
     generator with one seed per (tensor, expert) as above.
+  * Block-scaled 4-bit (MXFP4) expert weights: N(0, 1.5^2) samples rounded
+    to the nearest E2M1 magnitude (0, 0.5, 1, 1.5, 2, 3, 4, 6; ties to the
+    smaller), packed two per byte (lower input index in the low nibble), and
+    one E8M0 scale per 32 inputs drawn from 2^-8, 2^-7, 2^-6 (weights of
+    standard deviation 0.006-0.023), from torch's generator as above.
   * Hyper-connection wrapper (hc residual streams): the state is N(0,1) per
     stream (like x); hc_fn is bf16 N(0, 0.02) [(2+hc)*hc, hc*hidden] (mixes
     of standard deviation 0.02 * sqrt(hc*hidden), 2.6 at the full shape);
@@ -267,6 +272,50 @@ def mx_expert_weights(cfg: Config, device, layer: int = 0):
 
     def stack(tensor_id, out, inn):
         q = torch.empty((E, out, inn), dtype=torch.uint8, device=device)
+        s = torch.empty((E, out, inn // MX_BLOCK), dtype=torch.uint8, device=device)
+        for e in range(E):
+            q[e], s[e] = mat(tensor_id, e, out, inn)
+        return q, s
+
+    routed = (stack(_T_GATE, I, H), stack(_T_UP, I, H), stack(_T_DOWN, H, I))
+    shared = (mat(_T_SGATE, 0, I, H), mat(_T_SUP, 0, I, H), mat(_T_SDOWN, 0, H, I))
+    return routed, shared
+
+
+_T_MX4 = 30
+_E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _mx4_matrix(gen, out, inn, device):
+    """Packed E2M1 codes [out, inn/2] and E8M0 scales [out, inn/32]."""
+    import torch
+
+    v = torch.randn((out, inn), generator=gen, device=device, dtype=torch.float32).mul_(1.5)
+    mag = torch.tensor(_E2M1_MAG, device=device, dtype=torch.float32)
+    idx = (v.abs().unsqueeze(-1) - mag).abs().argmin(dim=-1).to(torch.uint8)  # first minimum: ties to the smaller
+    codes = idx | ((v < 0).to(torch.uint8) << 3)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    sc = torch.randint(119, 122, (out, inn // MX_BLOCK), generator=gen, device=device, dtype=torch.int32)
+    return packed.contiguous(), sc.to(torch.uint8)
+
+
+def mx4_expert_weights(cfg: Config, device, layer: int = 0):
+    """MXFP4 expert weights drawn on ``device``: ``(gate, up, down)`` and the
+    shared ``(gate, up, down)``, each a ``(packed codes uint8 [..., out,
+    in/2], scales uint8 [..., out, in/32])`` pair (routed: a leading expert
+    dimension).  One generator seed per (tensor, expert)."""
+    import torch
+
+    ls = cfg.param_seed + 7919 * layer
+    I, H, E = cfg.inter, cfg.hidden, cfg.experts
+    gen = torch.Generator(device=device)
+
+    def mat(tensor_id, e, out, inn):
+        gen.manual_seed((ls * 1_000_003 + (_T_MX4 + tensor_id) * 65_537 + e) & 0x7FFF_FFFF_FFFF_FFFF)
+        return _mx4_matrix(gen, out, inn, device)
+
+    def stack(tensor_id, out, inn):
+        q = torch.empty((E, out, inn // 2), dtype=torch.uint8, device=device)
         s = torch.empty((E, out, inn // MX_BLOCK), dtype=torch.uint8, device=device)
         for e in range(E):
             q[e], s[e] = mat(tensor_id, e, out, inn)

@@ -48,7 +48,8 @@ the design notes of the repository):
     activation stays in float64.
 
 Block-scaled weights: an expert matrix may be given as OCP MXFP8 codes and
-scales instead of bf16 bits; ``mx_dequant`` decodes it exactly (FP8 E4M3 and
+scales, or OCP MXFP4 packed codes and scales, instead of bf16 bits;
+``mx_dequant`` / ``mx4_dequant`` decode it exactly (FP8 E4M3, FP4 E2M1 and
 E8M0 values are all exact in float64) and the layer is then computed the
 same way.
 
@@ -123,11 +124,49 @@ def mx_dequant(codes, scales, block: int = MX_BLOCK) -> np.ndarray:
     return v * np.repeat(sc, block, axis=-1)
 
 
+# OCP MXFP4: FP4 E2M1 elements packed two per byte (the element of the lower
+# input index in the low nibble), one E8M0 scale per 32 elements as above.
+def e2m1_to_f64(nibbles) -> np.ndarray:
+    """OCP FP4 E2M1 codes (0..15) -> float64.  Bit 3 is the sign, bits 2..1
+    the exponent (bias 1), bit 0 the mantissa: exponent 0 encodes the
+    subnormals 0 and 0.5, so the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+    the format has no infinities and no NaN."""
+    c = np.asarray(nibbles, dtype=np.uint8).astype(np.int64)
+    sign, ex, man = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    mag = np.where(ex == 0, man * 0.5, (1.0 + man / 2.0) * np.exp2(ex - 1.0))
+    return np.where(sign == 1, -mag, mag)
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """Bytes ``[..., n/2]`` -> E2M1 codes ``[..., n]``: byte k holds elements
+    2k (low nibble) and 2k + 1 (high nibble)."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def mx4_dequant(packed, scales, block: int = MX_BLOCK) -> np.ndarray:
+    """Decode an MXFP4 matrix exactly: ``w[..., o, i] = e2m1(code i of row o)
+    * e8m0(scales[..., o, i // block])``."""
+    v = e2m1_to_f64(unpack_fp4(packed))
+    sc = e8m0_to_f64(scales)
+    assert sc.shape[-1] * block == v.shape[-1], "one scale per block of the input dimension"
+    return v * np.repeat(sc, block, axis=-1)
+
+
+MXFP4 = "mxfp4"  # tag of a (packed codes, scales, MXFP4) weight tuple
+
+
 def weight_f64(w) -> np.ndarray:
     """One weight matrix in float64: bf16 bit patterns (uint16) widened
-    exactly, an MX matrix given as ``(codes, scales)`` decoded exactly, or an
-    array of values taken as they are."""
+    exactly, an MXFP8 matrix given as ``(codes, scales)`` or an MXFP4 one as
+    ``(packed codes, scales, MXFP4)`` decoded exactly, or an array of values
+    taken as they are."""
     if isinstance(w, tuple):
+        if len(w) == 3 and w[2] == MXFP4:
+            return mx4_dequant(w[0], w[1])
         return mx_dequant(*w)
     w = np.asarray(w)
     return bf16_to_f64(w) if w.dtype == np.uint16 else w.astype(np.float64)

@@ -342,13 +342,72 @@ def check_mx_layer_equals_bf16_layer():
     assert np.array_equal(a, b) and np.abs(a).max() > 0
 
 
+def check_mx4_golden_codes():
+    """All 16 E2M1 codes against values worked by hand from the OCP MX
+    definitions (tests/golden/mx_codes.txt)."""
+    g = read_golden("mx_codes.txt")["e2m1"]
+    assert len(g) == 16
+    for key, (code, want) in g.items():
+        got = float(ref.e2m1_to_f64(np.array([int(code)], np.uint8))[0])
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (key, got, want)
+
+
+def check_mx4_packing_and_blocks():
+    """A hand-built 2 x 64 MXFP4 matrix (32 bytes a row): element 2k is the
+    low nibble of byte k, 2k + 1 the high one, and every element takes the
+    scale of its own 32-element block of its own row."""
+    q = np.zeros((2, 32), np.uint8)
+    q[0, 0] = 0x72       # elements 0, 1: 1 (0x2) and 6 (0x7)
+    q[0, 15] = 0x9A      # elements 30, 31: -1 (0xA) and -0.5 (0x9)
+    q[0, 16] = 0x03      # element 32: 1.5, first of the second block
+    q[1, 31] = 0xF0      # elements 62, 63: 0 and -6
+    sc = np.array([[127, 129], [0, 126]], np.uint8)   # 1, 4 ; 2^-127, 1/2
+    w = ref.mx4_dequant(q, sc)
+    want = np.zeros((2, 64))
+    want[0, 0], want[0, 1], want[0, 30], want[0, 31], want[0, 32] = 1.0, 6.0, -1.0, -0.5, 6.0
+    want[1, 63] = -3.0
+    assert np.array_equal(w, want) and np.signbit(w[1, 62]) == False  # noqa: E712
+
+
+def check_mx4_layer_equals_bf16_layer():
+    """A tiny layer with MXFP4 experts gives bitwise the output of the same
+    layer with bf16 experts holding the same values; the bf16 bits come from
+    the hand-worked E2M1 table of the golden file and torch (value * scale ->
+    bfloat16, exact here), not from the oracle's decoders."""
+    import torch
+
+    cfg = gen.config(0)
+    hi, _, _ = tiny_weights(cfg)
+    (G, U, D), (sg, su, sd) = gen.mx4_expert_weights(cfg, "cpu")
+    table = read_golden("mx_codes.txt")["e2m1"]
+    val = torch.tensor([table[f"n{i}"][1] for i in range(16)], dtype=torch.float32)
+
+    def bits(pair):
+        q, s = pair
+        codes = torch.stack([q & 15, q >> 4], dim=-1).flatten(-2).long()
+        v = val[codes]
+        scale = torch.exp2(s.to(torch.float32) - 127.0).repeat_interleave(gen.MX_BLOCK, dim=-1)
+        return gen.bf16_tensor_bits((v * scale).to(torch.bfloat16))
+
+    mx = lambda e: tuple(gen.mx_host((m[0][e], m[1][e])) + (ref.MXFP4,) for m in (G, U, D))
+    b16 = lambda e: tuple(bits((m[0][e], m[1][e])) for m in (G, U, D))
+    Wm = ref.Weights(hi.norm_w, hi.router, hi.sel_bias, None, mx,
+                     tuple(gen.mx_host(m) + (ref.MXFP4,) for m in (sg, su, sd)))
+    Wb = ref.Weights(hi.norm_w, hi.router, hi.sel_bias, None, b16, tuple(bits(m) for m in (sg, su, sd)))
+    x = np.random.default_rng(18).standard_normal((5, cfg.hidden))
+    a = ref.forward(x, None, ref.LAYER_SCORE, Wm, cfg.top_k, cfg.eps)["out"]
+    b = ref.forward(x, None, ref.LAYER_SCORE, Wb, cfg.top_k, cfg.eps)["out"]
+    assert np.array_equal(a, b) and np.abs(a).max() > 0
+
+
 ALL_CHECKS = [check_bf16_widening, check_matmul_triple_loop, check_micro_example, check_topk_rank_definition,
               check_topk_subset_enumeration, check_engineered_ties, check_weights_sum_to_one,
               check_hash_equals_score, check_zero_input_closed_form, check_rmsnorm_identities,
               check_scale_invariance, check_row_independence, check_expert_relabelling,
               check_identical_experts, check_invalid_masking, check_special_functions,
               check_mx_golden_codes, check_mx_against_torch, check_mx_block_broadcast,
-              check_mx_layer_equals_bf16_layer]
+              check_mx_layer_equals_bf16_layer, check_mx4_golden_codes, check_mx4_packing_and_blocks,
+              check_mx4_layer_equals_bf16_layer]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -357,6 +416,8 @@ def test_pin(check):
 
 
 # ------------------------------------------------- planted mistakes (CPU) ---
+_E2M1 = ref.e2m1_to_f64  # the unpatched decoder, for the mutants built on it
+
 def _mut_eps_outside(x, g, eps):
     x = np.asarray(x, np.float64)
     return x / (np.sqrt(np.mean(x * x, -1, keepdims=True)) + eps) * np.asarray(g, np.float64)
@@ -461,6 +522,32 @@ def _mut_e4m3_unsigned(codes):
     return np.abs(_orig_e4m3(codes))
 
 
+def _mut_e2m1_bias2(nibbles):
+    c = np.asarray(nibbles, dtype=np.uint8).astype(np.int64)
+    sign, ex, man = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    mag = np.where(ex == 0, man * 0.25, (1.0 + man / 2.0) * np.exp2(ex - 2.0))
+    return np.where(sign == 1, -mag, mag)
+
+
+def _mut_e2m1_no_subnormal(nibbles):
+    c = np.asarray(nibbles, dtype=np.uint8).astype(np.int64)
+    sign, ex, man = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    mag = (1.0 + man / 2.0) * np.exp2(ex - 1.0)
+    return np.where(sign == 1, -mag, mag)
+
+
+def _mut_e2m1_unsigned(nibbles):
+    return np.abs(_E2M1(nibbles))
+
+
+def _mut_fp4_high_nibble_first(packed):
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b >> 4
+    out[..., 1::2] = b & 15
+    return out
+
+
 def _mut_mx_block_64(codes, scales, block=32):
     v = ref.e4m3_to_f64(codes)
     sc = ref.e8m0_to_f64(scales)
@@ -485,6 +572,10 @@ MUTANTS = {
     "e4m3_subnormals_as_normals": ("e4m3_to_f64", _mut_e4m3_no_subnormals),
     "e4m3_sign_dropped": ("e4m3_to_f64", _mut_e4m3_unsigned),
     "e8m0_bias_128": ("e8m0_to_f64", _mut_e8m0_bias_128),
+    "e2m1_exponent_bias_2": ("e2m1_to_f64", _mut_e2m1_bias2),
+    "e2m1_subnormal_as_normal": ("e2m1_to_f64", _mut_e2m1_no_subnormal),
+    "e2m1_sign_dropped": ("e2m1_to_f64", _mut_e2m1_unsigned),
+    "fp4_high_nibble_first": ("unpack_fp4", _mut_fp4_high_nibble_first),
     "mx_blocks_of_64": ("mx_dequant", _mut_mx_block_64),
     "mx_scale_per_column_block": ("mx_dequant", _mut_mx_scale_per_column),
     "rmsnorm_eps_outside_root": ("rms_norm", _mut_eps_outside),
