@@ -38,7 +38,7 @@ METRIC = "MoE-layer rows/sec at 1/4/512/8192 rows; HBM GB/s and MFMA % of peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix cores
 # bytes per expert weight: bf16, or an MXFP8 code plus 1/32 of its block's E8M0 scale
-WEIGHT_BYTES = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32}
+WEIGHT_BYTES = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32, "mxfp4": 0.5 + 1.0 / 32}
 EXPERT_BYTES = lambda H, I, wb=2.0: 3 * H * I * wb  # gate + up + down
 
 
@@ -53,7 +53,9 @@ def alg_bytes(kernel, cfg, U, R, hc=4):
     "_mx" read MXFP8 expert weights (the router stays bf16)."""
     H, I, E, K = cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
     wb = WEIGHT_BYTES["bf16"]
-    if kernel.endswith("_mx"):
+    if kernel.endswith("_mx4"):
+        kernel, wb = kernel[:-4], WEIGHT_BYTES["mxfp4"]
+    elif kernel.endswith("_mx"):
         kernel, wb = kernel[:-3], WEIGHT_BYTES["mxfp8"]
     x = R * H * 4
     S = R * K
@@ -92,8 +94,7 @@ def alg_bytes(kernel, cfg, U, R, hc=4):
 
 
 def alg_flops(kernel, cfg, R):
-    if kernel.endswith("_mx"):
-        kernel = kernel[:-3]
+    kernel = kernel[:-4] if kernel.endswith("_mx4") else kernel[:-3] if kernel.endswith("_mx") else kernel
     H, I, E, K = cfg.hidden, cfg.inter, cfg.experts, cfg.top_k
     S = R * K
     if kernel == "pre_router":       # hi and lo passes
@@ -126,6 +127,8 @@ HC_STREAMS = 4
 SUB_WORKLOADS = ("decode-cohort-r4-hash", "prefill-r512-score", "prefill-r8192-score-skewed")
 # the same workloads with MXFP8 expert weights (moe_ffn_forward_mxfp8)
 MX_WORKLOADS = ("decode-r1-score", "decode-cohort-r4-hash", "prefill-r512-score", "prefill-r8192-score-skewed")
+# and with MXFP4 expert weights (moe_ffn_forward_mxfp4)
+MX4_WORKLOADS = ("decode-r1-score", "decode-cohort-r4-hash", "prefill-r512-score", "prefill-r8192-score-skewed")
 
 
 def draw_layers(cfg, L):
@@ -140,14 +143,16 @@ def draw_layers(cfg, L):
     return out
 
 
-def draw_layers_mx(cfg, L):
-    """Device MXFP8 expert weights of L layers ((codes, scales) per matrix)."""
+def draw_layers_mx(cfg, L, fmt="mxfp8"):
+    """Device block-scaled expert weights of L layers ((codes, scales) per
+    matrix; MXFP8 codes, or MXFP4 codes packed two per byte)."""
     from mixture_experts_ffn_rmsnorm_amd import inputs as gen
 
+    draw = gen.mx4_expert_weights if fmt == "mxfp4" else gen.mx_expert_weights
     out = []
     for l in range(L):
-        out.append(gen.mx_expert_weights(cfg, "cuda", layer=l))
-        log(f"layer {l} MXFP8 weights ready")
+        out.append(draw(cfg, "cuda", layer=l))
+        log(f"layer {l} {fmt.upper()} weights ready")
     return out
 
 
@@ -176,7 +181,7 @@ def bind_layers(cfg, big, L, fmt="bf16"):
 def forward_fn(fmt):
     from mixture_experts_ffn_rmsnorm_amd import moe
 
-    return moe.forward if fmt == "bf16" else moe.forward_mxfp8
+    return {"bf16": moe.forward, "mxfp8": moe.forward_mxfp8, "mxfp4": moe.forward_mxfp4}[fmt]
 
 
 def time_workload(cfg, layers, steps, warmup, graph=False):
@@ -358,7 +363,7 @@ def main():
     ap.add_argument("--only", action="store_true",
                     help="time the named workload alone (no sub-records of the other full-size workloads)")
     ap.add_argument("--layers", type=int, default=None, help="distinct weight sets cycled (default 4 decode, 1 prefill)")
-    ap.add_argument("--weights", choices=("bf16", "mxfp8"), default="bf16",
+    ap.add_argument("--weights", choices=("bf16", "mxfp8", "mxfp4"), default="bf16",
                     help="expert weight format of the named workload (the headline is bf16)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the headline's oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -386,7 +391,7 @@ def main():
     nl = lambda c: args.layers or (4 if c.rows <= 4 else 1)
     L = max([nl(cfg)] + [nl(c) for c in subs])
     log(f"workload {cfg.name} (+ {len(subs)} more): drawing {L} layers of weights on the GPU")
-    big = draw_layers(cfg, L) if args.weights == "bf16" else draw_layers_mx(cfg, L)
+    big = draw_layers(cfg, L) if args.weights == "bf16" else draw_layers_mx(cfg, L, args.weights)
     layers = bind_layers(cfg, big, nl(cfg), args.weights)
     rec, gpu0 = time_workload(cfg, layers, args.steps, args.warmup, graph=args.graph and cfg.rows <= 4)
     R = cfg.rows
@@ -425,16 +430,18 @@ def main():
                                                                     base_ms)
     mx_gpu = {}
     if subs:
-        mx_cfgs = [gen.config(n) for n in MX_WORKLOADS]
-        if mx_cfgs:
-            big_mx = draw_layers_mx(cfg, max(nl(c) for c in mx_cfgs))
+        for fmt, names in (("mxfp8", MX_WORKLOADS), ("mxfp4", MX4_WORKLOADS)):
+            mx_cfgs = [gen.config(n) for n in names]
+            big_mx = draw_layers_mx(cfg, max(nl(c) for c in mx_cfgs), fmt)
             for c in mx_cfgs:
-                lay_c = bind_layers(c, big_mx, nl(c), "mxfp8")
+                lay_c = bind_layers(c, big_mx, nl(c), fmt)
                 r_c, g_c = time_workload(c, lay_c, args.steps, args.warmup, graph=args.graph and c.rows <= 4)
                 r_c["dtype"] = "f32" if c.rows <= 4 else "f16"
                 r_c["layer_kind"] = "hash" if c.layer_kind == 1 else "score"
-                res["workloads"][c.name + "-mxfp8"] = r_c
-                mx_gpu[c.name + "-mxfp8"] = (c, lay_c[0], g_c)
+                res["workloads"][f"{c.name}-{fmt}"] = r_c
+                mx_gpu[f"{c.name}-{fmt}"] = (c, lay_c[0], g_c)
+            del big_mx
+            torch.cuda.empty_cache()
     if not args.no_peaks:
         # the published peaks above are the roofline's; these are the same
         # two ceilings measured on this device, after the timed passes
@@ -511,8 +518,9 @@ def _oracle_weights(cfg, layer):
     if fmt == "bf16":
         host = gen.bf16_tensor_bits
         pick = lambda m, e: m[e]
-    else:  # MXFP8: (codes, scales) pairs
-        host = gen.mx_host
+    else:  # MXFP8 / MXFP4: (codes, scales) pairs, MXFP4 tagged for the oracle
+        tag = (ref.MXFP4,) if fmt == "mxfp4" else ()
+        host = lambda pair: gen.mx_host(pair) + tag
         pick = lambda m, e: (m[0][e], m[1][e])
 
     def expert(e):

@@ -226,6 +226,22 @@ int moe_ffn_forward_mxfp8(const moe_dims_t* d, const float* x, const int32_t* to
                           int layer_kind, const moe_mx_weights_t* w, float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* moe_ffn_forward with MXFP4 expert weights (OCP Microscaling MXFP4): the
+ * same moe_mx_weights_t, whose code arrays now hold FP4 E2M1 codes packed
+ * two per byte -- [out][in / 2] (routed: [experts][out][in / 2]), the
+ * element of the lower input index in the low nibble -- with the same E8M0
+ * scales, value = e2m1(code) * 2^(scale - 127) (E2M1: sign, 2 exponent bits
+ * of bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).  Same
+ * arguments, workspace, routing, status and reproducibility.  Reads about a
+ * quarter of the expert bytes of the bf16 layer.  Precision as
+ * moe_ffn_forward_mxfp8: rows <= 4 each weight exactly, f32 accumulation;
+ * rows > 4 each weight rounded to nearest even fp16 (exact for decoded
+ * magnitudes 2^-14 .. 65504), then the fp16 path.
+ * Errors: as moe_ffn_forward_mxfp8. */
+int moe_ffn_forward_mxfp4(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,
+                          int layer_kind, const moe_mx_weights_t* w, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* moe_ffn_forward without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Same arguments, kernels and

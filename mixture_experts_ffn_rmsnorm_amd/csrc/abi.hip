@@ -174,11 +174,11 @@ int check_forward_args(const moe_dims_t* d, const float* x, const int32_t* token
 
 // The forward with its intermediates carved from `workspace` (already
 // checked: at least L.total bytes, 256-byte aligned).  With `mx` the expert
-// matrices are the block-scaled ones there (w then supplies only the small
-// parameters).
+// matrices are the block-scaled ones there, in format `mx_format` (1 MXFP8,
+// 2 MXFP4; w then supplies only the small parameters).
 int forward_in(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
-               const moe_weights_t* w, const moe_mx_weights_t* mx, float* out, void* workspace, const Layout& L,
-               void* stream) {
+               const moe_weights_t* w, const moe_mx_weights_t* mx, int mx_format, float* out, void* workspace,
+               const Layout& L, void* stream) {
   char* ws = (char*)workspace;
   FwdArgs a;
   memset(&a, 0, sizeof(a));
@@ -204,7 +204,7 @@ int forward_in(const moe_dims_t* d, const float* x, const int32_t* token_ids, in
   a.down_sh = w->down_sh;
   if (mx) {
     a.gate = a.up = a.down = a.gate_sh = a.up_sh = a.down_sh = nullptr;
-    a.mx = 1;
+    a.mx = mx_format;
     a.gate_q = mx->gate_exps.codes;
     a.up_q = mx->up_exps.codes;
     a.down_q = mx->down_exps.codes;
@@ -322,7 +322,7 @@ int moe_ffn_forward(const moe_dims_t* d, const float* x, const int32_t* token_id
   const int rc = check_forward_args(d, x, token_ids, rows, layer_kind, w, out, &L);
   if (rc) return rc;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
-  return forward_in(d, x, token_ids, rows, layer_kind, w, nullptr, out, workspace, L, stream);
+  return forward_in(d, x, token_ids, rows, layer_kind, w, nullptr, 0, out, workspace, L, stream);
 }
 
 int moe_ffn_forward_noalloc(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows,
@@ -334,7 +334,7 @@ int moe_ffn_forward_noalloc(const moe_dims_t* d, const float* x, const int32_t* 
   void* ws = nullptr;
   rc = scratch_for((hipStream_t)stream, L.logits, &ws);  // the status block precedes the logits
   if (rc) return rc;
-  return forward_in(d, x, token_ids, rows, layer_kind, w, nullptr, out, ws, L, stream);
+  return forward_in(d, x, token_ids, rows, layer_kind, w, nullptr, 0, out, ws, L, stream);
 }
 
 int moe_ffn_forward_mxfp8(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
@@ -349,7 +349,22 @@ int moe_ffn_forward_mxfp8(const moe_dims_t* d, const float* x, const int32_t* to
   rc = check_forward_args(d, x, token_ids, rows, layer_kind, &common, out, &L);
   if (rc) return rc;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
-  return forward_in(d, x, token_ids, rows, layer_kind, &common, w, out, workspace, L, stream);
+  return forward_in(d, x, token_ids, rows, layer_kind, &common, w, 1, out, workspace, L, stream);
+}
+
+int moe_ffn_forward_mxfp4(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
+                          const moe_mx_weights_t* w, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  moe_weights_t common;
+  int rc = check_dims_rows(d, rows);
+  if (rc) return rc;
+  rc = check_mx_weights(w, &common);
+  if (rc) return rc;
+  Layout L;
+  rc = check_forward_args(d, x, token_ids, rows, layer_kind, &common, out, &L);
+  if (rc) return rc;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return MOE_EWORKSPACE;
+  return forward_in(d, x, token_ids, rows, layer_kind, &common, w, 2, out, workspace, L, stream);
 }
 
 int moe_route(const moe_dims_t* d, const float* logits, const int32_t* token_ids, int64_t rows, int layer_kind,
@@ -423,8 +438,8 @@ int moe_ffn_forward_hc(const moe_dims_t* d, const float* state_in, const int32_t
   a.out = state_out;
   hipStream_t s = (hipStream_t)stream;
   if (run_hc_pre(a, s) != hipSuccess) return MOE_EHIP;
-  rc = forward_in(d, a.ffn_in, token_ids, rows, layer_kind, w, nullptr, (float*)(ws + L.ffn_out), workspace, L.ffn,
-                  stream);
+  rc = forward_in(d, a.ffn_in, token_ids, rows, layer_kind, w, nullptr, 0, (float*)(ws + L.ffn_out), workspace,
+                  L.ffn, stream);
   if (rc) return rc;
   return run_hc_post(a, s) == hipSuccess ? MOE_OK : MOE_EHIP;
 }

@@ -49,12 +49,14 @@ constexpr int kSdRows = 16;
 // vs 213.6-216.0 us; 8-bit weights four rows 172.9 us with two rows in
 // flight vs 177.7 us with four (four in flight without pairs: 83 us at one
 // row).
-template <bool MX> constexpr int kNbuf = 2;
-template <bool MX> constexpr bool kPair = true;
+template <int MX> constexpr int kNbuf = 2;
+template <int MX> constexpr bool kPair = true;
 
-// An expert matrix [out][LEN] in either weight format: bf16 values, or
-// block-scaled 8-bit values (E4M3 codes [out][LEN] with one E8M0 scale per
-// 32 columns, [out][LEN/32]).  WRow is one row of it.
+// An expert matrix [out][LEN] in one of the weight formats MX: 0 bf16
+// values; 1 block-scaled 8-bit values (E4M3 codes [out][LEN], one E8M0
+// scale per 32 columns, [out][LEN/32]); 2 block-scaled 4-bit values (E2M1
+// codes packed two per byte, [out][LEN/2], the same scales).  WRow is one
+// row of it.
 struct WMat {
   const void* w;
   const uint8_t* s;  // MX only
@@ -63,16 +65,16 @@ struct WRow {
   const void* w;
   const uint8_t* s;
 };
-template <bool MX, int LEN>
+template <int MX, int LEN>
 __device__ __forceinline__ WRow wrow(const WMat& m, int64_t i) {
-  if constexpr (MX) return WRow{(const uint8_t*)m.w + i * LEN, m.s + i * (LEN / 32)};
+  if constexpr (MX) return WRow{(const uint8_t*)m.w + i * (MX == 2 ? LEN / 2 : LEN), m.s + i * (LEN / 32)};
   else return WRow{(const uint16_t*)m.w + i * LEN, nullptr};
 }
 // Expert e's matrix of `elems` values from the forward's arguments.
-template <bool MX>
+template <int MX>
 __device__ __forceinline__ WMat expert_mat(const uint16_t* bf, const uint8_t* q, const uint8_t* s, int64_t e,
                                            int64_t elems) {
-  if constexpr (MX) return WMat{q + e * elems, s + e * (elems / 32)};
+  if constexpr (MX) return WMat{q + e * (MX == 2 ? elems / 2 : elems), s + e * (elems / 32)};
   else return WMat{bf + e * elems, nullptr};
 }
 
@@ -88,11 +90,25 @@ __device__ __forceinline__ void unpack8_e4m3(const uint2& q, float* f) {
   const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)q.y, true);
   f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y; f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
 }
+// Eight E2M1 codes (the nibbles of q, lowest first) -> eight floats,
+// exactly (v_cvt_scalef32_pk_f32_fp4 with scale 1 converts the two codes
+// of one byte; each result pair is taken as one 64-bit value).
+__device__ __forceinline__ void unpack8_e2m1(uint32_t q, float* f) {
+  const uint64_t v0 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0));
+  const uint64_t v1 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1));
+  const uint64_t v2 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2));
+  const uint64_t v3 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3));
+  f[0] = __uint_as_float((uint32_t)v0); f[1] = __uint_as_float((uint32_t)(v0 >> 32));
+  f[2] = __uint_as_float((uint32_t)v1); f[3] = __uint_as_float((uint32_t)(v1 >> 32));
+  f[4] = __uint_as_float((uint32_t)v2); f[5] = __uint_as_float((uint32_t)(v2 >> 32));
+  f[6] = __uint_as_float((uint32_t)v3); f[7] = __uint_as_float((uint32_t)(v3 >> 32));
+}
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 load_stream8(const void* p) {
   const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
   return make_uint2(v.x, v.y);
 }
+__device__ __forceinline__ uint32_t load_stream4(const void* p) { return __builtin_nontemporal_load((const uint32_t*)p); }
 
 // One wavefront walks a sequence of whole weight rows (global) and dots each
 // with up to 4 f32 activation rows in LDS (row r at act + r*LEN).  Each row
@@ -116,19 +132,25 @@ __device__ __forceinline__ uint2 load_stream8(const void* p) {
 // from LDS serves both (with several activation rows and half-size 8-bit
 // weight rows the LDS reads, not the weight stream, bound the loop
 // otherwise).
-template <int LEN, int NBUF, bool MX, bool PAIR, class RowSrc, class Pre, class Sink>
+template <int LEN, int NBUF, int MX, bool PAIR, class RowSrc, class Pre, class Sink>
 __device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const float* act, int nr, Pre pre, Sink sink) {
   static_assert(LEN % 256 == 0, "row length must be a multiple of 256");
   static_assert(!PAIR || NBUF % 2 == 0, "pairs of rows in flight");
   constexpr int NCH = (LEN + 511) / 512;
   const int lane = threadIdx.x & (kWave - 1);
   const bool full = LEN % 512 == 0 || lane * 8 < LEN % 512;  // active in the last chunk
-  using Chunk = typename std::conditional<MX, uint2, uint4>::type;
+  using Chunk = typename std::conditional<MX == 2, uint32_t, typename std::conditional<MX == 1, uint2, uint4>::type>::type;
   Chunk q[NBUF][NCH];
   uint32_t sw[NBUF];  // MX: this lane's 4 scale bytes of the row
   auto load_row = [&](int b, int j) {
     const WRow src = rowsrc(j);
-    if constexpr (MX) {
+    if constexpr (MX == 2) {  // 4-bit codes: 4 bytes per lane and chunk
+      const uint8_t* p = (const uint8_t*)src.w + lane * 4;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        if (c < NCH - 1 || full) q[b][c] = load_stream4(p + c * 256);
+      sw[b] = lane * 4 < LEN / 32 ? *(const uint32_t*)(src.s + lane * 4) : 0u;
+    } else if constexpr (MX) {
       const uint8_t* p = (const uint8_t*)src.w + lane * 8;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
@@ -163,7 +185,8 @@ __device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const floa
         float f[NR][8];
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-          if constexpr (MX) unpack8_e4m3(q[b + i][c], f[i]);
+          if constexpr (MX == 2) unpack8_e2m1(q[b + i][c], f[i]);
+          else if constexpr (MX) unpack8_e4m3(q[b + i][c], f[i]);
           else unpack8(q[b + i][c], f[i]);
         }
 #pragma unroll
@@ -311,7 +334,7 @@ __device__ __forceinline__ void stage_rows(float* dst, const float* const (&src)
 // so the blocks working on one expert at the same time read neighbouring
 // rows; wave w streams gate_i then up_i for every fourth of them.  h32 rows
 // hout..hout+nr-1 receive silu(gate . x) * (up . x).
-template <int H, int I, int PAIRS, int NBUF, bool MX, bool PAIR, class Pre>
+template <int H, int I, int PAIRS, int NBUF, int MX, bool PAIR, class Pre>
 __device__ __forceinline__ void gateup_tile(const WMat& gm, const WMat& um, const float* xs, int nr, int x, int tiles,
                                             float* h32, int hout, Pre pre) {
   constexpr int W = kThreads / kWave, PPW = PAIRS / W;  // pairs per wave
@@ -726,7 +749,7 @@ __device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R) {
 // x + (i * mul + add) * stride, so concurrent blocks read neighbouring rows
 // (x, x + stride, ... for mul 1; every other one of them, from `add`, for
 // mul 2).  d32 rows ent..ent+nr-1 receive the results (written through).
-template <int H, int I, int ROWS, int NBUF, bool MX, bool PAIR, class Pre>
+template <int H, int I, int ROWS, int NBUF, int MX, bool PAIR, class Pre>
 __device__ __forceinline__ void down_tile(const WMat& wm, const float* hs, int nr, int x, int stride, int mul, int add,
                                           float* d32, int ent, Pre pre) {
   constexpr int W = kThreads / kWave, RPW = ROWS / W;  // rows per wave
@@ -764,7 +787,7 @@ __device__ __forceinline__ void down_tile(const WMat& wm, const float* hs, int n
 //   Shared gate/up block: RMSNorm into LDS, then 8 inter rows of the shared
 //   expert's SwiGLU output for every row; its streaming covers the router's
 //   latency and the routing.  The first of these blocks publishes xn.
-template <int H, int I, bool kRouterOnly, bool MX>
+template <int H, int I, bool kRouterOnly, int MX>
 __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [R][H]
   __shared__ int s_idx[kDecodeMaxSlots];
@@ -869,7 +892,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
 // x + H/16, ... of the shared expert's down projection -> d32 shared rows.
 // Gate/up block (u, x): inter rows x, x + I/16, ... of the plan's u-th
 // expert -> h32.
-template <int H, int I, bool MX>
+template <int H, int I, int MX>
 __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [nr][H] activations, or [R][I] shared h
   constexpr int nsd = H / kSdRows, gut = I / kGuRows;
@@ -906,7 +929,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
 // microseconds of work that every block repeats, against the
 // cross-workgroup round trips of a shared plan.  At full size this is 256 +
 // 6 * 128 blocks, one shared and three routed per compute unit.
-template <int H, int I, bool MX>
+template <int H, int I, int MX>
 __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [H] normalised row
   __shared__ int s_idx[kDecodeMaxSlots];
@@ -955,7 +978,7 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
 // output is bitwise reproducible.  No block waits for another.  Without
 // kShared and with no valid routed expert at all, the u = 0 blocks write
 // out = shared down.
-template <int H, int I, bool kShared, bool MX>
+template <int H, int I, bool kShared, int MX>
 __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   __shared__ float hs[kDecodeMaxRows * I];
   __shared__ int s_er[kDecodeMaxSlots];    // the plan's entry rows and weights, for the reduce
@@ -1034,7 +1057,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   a.out[(int64_t)r * H + h] = o;
 }
 
-template <int H, int I, bool MX>
+template <int H, int I, int MX>
 hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   static_assert(H / kDnRows <= kDecodeMaxTiles, "too many down tiles");
   FwdArgs args = a;
@@ -1043,30 +1066,34 @@ hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   if (a.R == 1) {
     // one row: router launch, then gate/up blocks that route for
     // themselves, then routed + shared down with the reduce
-    err = launch(MX ? "dec1_router_mx" : "dec1_router", (const void*)k_dec_head<H, I, true, MX>, dim3((a.E + 3) / 4),
+    err = launch(MX == 2 ? "dec1_router_mx4" : MX ? "dec1_router_mx" : "dec1_router", (const void*)k_dec_head<H, I, true, MX>, dim3((a.E + 3) / 4),
                  dim3(kThreads), (size_t)H * 4, s, &args);
     if (err != hipSuccess) return err;
-    err = launch(MX ? "dec1_gateup_mx" : "dec1_gateup", (const void*)k_dec1_gateup<H, I, MX>,
+    err = launch(MX == 2 ? "dec1_gateup_mx4" : MX ? "dec1_gateup_mx" : "dec1_gateup", (const void*)k_dec1_gateup<H, I, MX>,
                  dim3(I / kShRows + gmax * (I / kGuRows)), dim3(kThreads), (size_t)H * 4, s, &args);
     if (err != hipSuccess) return err;
-    return launch(MX ? "dec1_down_reduce_mx" : "dec1_down_reduce", (const void*)k_dec_down<H, I, true, MX>,
+    return launch(MX == 2 ? "dec1_down_reduce_mx4" : MX ? "dec1_down_reduce_mx" : "dec1_down_reduce", (const void*)k_dec_down<H, I, true, MX>,
                   dim3(H / kDnRows, gmax + 2), dim3(kThreads), 0, s, &args);
   }
-  err = launch(MX ? "dec_head_mx" : "dec_head", (const void*)k_dec_head<H, I, false, MX>,
+  err = launch(MX == 2 ? "dec_head_mx4" : MX ? "dec_head_mx" : "dec_head", (const void*)k_dec_head<H, I, false, MX>,
                dim3((a.E + 3) / 4 + I / kShRows), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  err = launch(MX ? "dec_gateup_mx" : "dec_gateup", (const void*)k_dec_gateup<H, I, MX>,
+  err = launch(MX == 2 ? "dec_gateup_mx4" : MX ? "dec_gateup_mx" : "dec_gateup", (const void*)k_dec_gateup<H, I, MX>,
                dim3(H / kSdRows + gmax * (I / kGuRows)), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  return launch(MX ? "dec_down_reduce_mx" : "dec_down_reduce", (const void*)k_dec_down<H, I, false, MX>,
+  return launch(MX == 2 ? "dec_down_reduce_mx4" : MX ? "dec_down_reduce_mx" : "dec_down_reduce", (const void*)k_dec_down<H, I, false, MX>,
                 dim3(H / kDnRows, gmax), dim3(kThreads), 0, s, &args);
 }
 
 }  // namespace
 
 hipError_t run_decode(const FwdArgs& a, hipStream_t s) {
-  if (a.H == 4096 && a.I == 2048) return a.mx ? run_decode_t<4096, 2048, true>(a, s) : run_decode_t<4096, 2048, false>(a, s);
-  if (a.H == 512 && a.I == 256) return a.mx ? run_decode_t<512, 256, true>(a, s) : run_decode_t<512, 256, false>(a, s);
+  if (a.H == 4096 && a.I == 2048)
+    return a.mx == 2 ? run_decode_t<4096, 2048, 2>(a, s)
+           : a.mx    ? run_decode_t<4096, 2048, 1>(a, s)
+                     : run_decode_t<4096, 2048, 0>(a, s);
+  if (a.H == 512 && a.I == 256)
+    return a.mx == 2 ? run_decode_t<512, 256, 2>(a, s) : a.mx ? run_decode_t<512, 256, 1>(a, s) : run_decode_t<512, 256, 0>(a, s);
   return hipErrorInvalidValue;
 }
 

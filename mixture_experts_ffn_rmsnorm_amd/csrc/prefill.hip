@@ -75,11 +75,14 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 
 // chunk swizzle of a 128-byte LDS row
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-// chunk swizzle of an 8-bit weight row in LDS: 8 chunks (one 128-byte row
-// per line) as above; 4 chunks (two 64-byte rows per line) by (row / 4) & 3,
+// chunk swizzle of a row of weight codes in LDS: 8 chunks (one 128-byte
+// row per line) as above; 4 chunks (two 64-byte rows per line) by
+// (row / 4) & 3; 2 chunks (four 32-byte rows per line) by (row / 8) & 1 --
 // so that 16 consecutive rows read at one chunk hit 16 distinct 16-byte bank
 // groups
-__device__ __forceinline__ int mxsw(int row, int cpr) { return cpr == 8 ? swz(row) : (row >> 2) & 3; }
+__device__ __forceinline__ int mxsw(int row, int cpr) {
+  return cpr == 8 ? swz(row) : cpr == 4 ? (row >> 2) & 3 : (row >> 3) & 1;
+}
 // dword swizzle of a scale row of `dpr` dwords: the rows that share a
 // 256-byte span rotate their dwords, so 32 consecutive rows reading one
 // dword hit 32 distinct banks
@@ -124,6 +127,18 @@ __device__ __forceinline__ uint4 fp8x8_to_f16x8(uint32_t lo, uint32_t hi, float 
   r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, scale, true));
   r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, scale, false));
   r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, scale, true));
+  return r;
+}
+
+// Eight E2M1 codes (the nibbles of w, lowest first) times `scale`, rounded
+// to nearest even fp16, in k order: v_cvt_scalef32_pk_f16_fp4 converts the
+// two codes of one byte; results taken as whole 32-bit words as above.
+__device__ __forceinline__ uint4 fp4x8_to_f16x8(uint32_t w, float scale) {
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3));
   return r;
 }
 
@@ -646,15 +661,18 @@ __global__ __launch_bounds__(kThreads) void k_pre_sort(const FwdArgs a) {
 // hit distinct LDS banks.  B stays bf16 in LDS and is converted to fp16
 // after the fragment read, interleaved with the MFMAs of the previous
 // k-step.
-// Block-scaled 8-bit weights (MX) travel the same way as 8-bit codes, a
+// Block-scaled weights (MX) travel the same way as codes: 8-bit (MXFP8), a
 // k-tile row of BK bytes (BK 128: one 128-byte row; BK 64: two rows per
-// 128-byte line, 16-byte chunks swizzled by (row / 4) & 3); each tile's
-// block scales (one byte per 32 inputs) land in LDS once per tile.  The k
-// order inside a pair of k-steps is permuted so that a lane's 16 codes of
-// the pair are contiguous and share one scale: k-step 2p + o takes k =
-// 32p + 16 * (lane / 32) + 8o + 0..7 (the A fragments follow the same map),
-// and one 16-byte read per pair feeds both steps through
-// v_cvt_scalef32_pk_f16_fp8.
+// 128-byte line, 16-byte chunks swizzled by (row / 4) & 3), or 4-bit
+// (MXFP4), BK / 2 bytes (two 64-byte rows per line; BK 64: four 32-byte
+// rows, chunks swizzled by (row / 8) & 1); each tile's block scales (one
+// byte per 32 inputs) land in LDS once per tile.  The k order inside a
+// group of k-steps is permuted so that a lane's codes of the group are one
+// 16-byte read under one scale: MXFP8, pairs -- k-step 2p + o takes k =
+// 32p + 16 * (lane / 32) + 8o + 0..7; MXFP4, quads -- k-step 4p + o takes
+// k = 64p + 32 * (lane / 32) + 8o + 0..7 (the A fragments follow the same
+// map).  v_cvt_scalef32_pk_f16_fp8 / _fp4 turn the codes into fp16 with
+// the scale.
 // The grid is persistent (one block per compute unit); tiles are ordered by
 // group, then in blocks of 4 row tiles x 8 column tiles, and handed out so
 // that each XCD takes a contiguous run of them: the tiles that share
@@ -687,7 +705,7 @@ struct GemmShape {
   static constexpr int BN = MODE == 0 ? Cfg::BROWS / 2 : Cfg::BROWS;
 };
 
-template <int MODE, int KD, int ND, class Cfg, bool MX>
+template <int MODE, int KD, int ND, class Cfg, int MX>
 __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
   constexpr int BM = Cfg::BM, WM = Cfg::WM, BROWS = Cfg::BROWS, WN = Cfg::WN, BK = Cfg::BK;
   constexpr int kGT = Cfg::kGT, GWN = Cfg::GWN;
@@ -703,7 +721,9 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
   constexpr int SLAB = kSlab * CPITCH * 4;
   // MX: the B tile holds BK bytes per row; with three stages they are
   // padded to a slab so that the epilogue can stage through one of them
-  constexpr int A_ST = NH * HA, B_ST = MX ? BROWS * BK : NH * HB;
+  constexpr int RB = MX == 2 ? BK / 2 : BK;  // MX: bytes of a k-tile row of codes
+  constexpr int KB = MX == 2 ? KD / 2 : KD;  // MX: bytes of a whole row of codes
+  constexpr int A_ST = NH * HA, B_ST = MX ? BROWS * RB : NH * HB;
   constexpr bool kPad = MX && kStages == 3 && MODE != 2 && A_ST + B_ST < SLAB;
   constexpr int ST = kPad ? (SLAB + 1023) / 1024 * 1024 : A_ST + B_ST;
   constexpr int AI = A_ST / 16 / kGT;  // A DMA instructions per thread per k-tile
@@ -714,8 +734,8 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
   static_assert(SLAB <= kStages * ST, "staging fits");
   static_assert(NK >= 2 && ND % BN == 0, "tiling");
   // MX B rows: RPL rows per 128-byte line, CPR 16-byte chunks per row
-  constexpr int RPL = MX ? 128 / BK : 1, CPR = MX ? BK / 16 : 8;
-  static_assert(!MX || ((BK == 64 || BK == 128) && BROWS % (8 * RPL) == 0), "MX B layout");
+  constexpr int RPL = MX ? 128 / RB : 1, CPR = MX ? RB / 16 : 8;
+  static_assert(!MX || ((RB == 32 || RB == 64 || RB == 128) && BROWS % (8 * RPL) == 0), "MX B layout");
   // MX block scales of the tile's B rows: SR bytes per row (DPR dwords),
   // dword w of row r stored at slot w ^ ssw(r); one buffer padded to whole
   // rounds of 4-byte DMA, SCI per thread
@@ -871,7 +891,7 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
       row = n0 + r;
     }
     const int64_t rows_before = sh ? 0 : (int64_t)g * ND;
-    return m + (rows_before + row) * (scales ? SR : KD);
+    return m + (rows_before + row) * (scales ? SR : KB);
   };
   // MX B DMA: instruction i of the wave fills 1024 bytes of the B tile,
   // lane l the 16-byte slot l & 7 of line (wave * BI + i) * 8 + l / 8: row
@@ -968,7 +988,7 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
           for (int h = 0; h < NH; ++h) dma16(asrc[i] + src * (BK * 2) + h * 128, base + a_wave + h * HA + i * 1024);
       if constexpr (MX) {
 #pragma unroll
-        for (int i = 0; i < BG; ++i) dma16(bsrc[i] + src * BK, base + b_wave + i * 1024);
+        for (int i = 0; i < BG; ++i) dma16(bsrc[i] + src * RB, base + b_wave + i * 1024);
       } else {
 #pragma unroll
         for (int i = 0; i < BG; ++i)
@@ -986,7 +1006,7 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
           for (int h = 0; h < NH; ++h) dma16(nasrc[i] + src * (BK * 2) + h * 128, base + a_wave + h * HA + i * 1024);
       if constexpr (MX) {
 #pragma unroll
-        for (int i = 0; i < BG; ++i) dma16(nbsrc[i] + src * BK, base + b_wave + i * 1024);
+        for (int i = 0; i < BG; ++i) dma16(nbsrc[i] + src * RB, base + b_wave + i * 1024);
       } else {
 #pragma unroll
         for (int i = 0; i < BG; ++i)
@@ -996,11 +1016,13 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
     };
     auto ring_buf = [&](int kt) { return kPre ? (off + kt) % kStages : kt % kStages; };
     // fragment reads of k-step `st` (16 k) of k-tile `kt` from ring buffer
-    // `buf`.  MX: the B codes of a step pair and their scale are read at its
-    // even step and kept for the odd one.
+    // `buf`.  MX: the B codes of a step pair (MXFP8) or quad (MXFP4) and
+    // their scale are read at its first step and kept for the others.
     auto read_step = [&](int buf, int st, half8 (&af)[WM], uint4 (&rb)[WN], float (&sc)[WN], int nv, int kt) {
       const unsigned char* As = s_ring + buf * ST + (st >> 2) * HA;
-      const int c = MX ? 4 * ((st >> 1) & 1) + 2 * (lane >> 5) + (st & 1) : 2 * (st & 3) + (lane >> 5);
+      const int c = MX == 2 ? 4 * (lane >> 5) + (st & 3)
+                    : MX    ? 4 * ((st >> 1) & 1) + 2 * (lane >> 5) + (st & 1)
+                            : 2 * (st & 3) + (lane >> 5);
 #pragma unroll
       for (int i = 0; i < WM; ++i)
         if (i < nv) af[i] = *(const half8*)(As + arow[i] * 128 + ((c ^ swz(arow[i])) << 4));
@@ -1008,14 +1030,15 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
         const unsigned char* Bs = s_ring + buf * ST + A_ST + (st >> 2) * HB;
 #pragma unroll
         for (int j = 0; j < WN; ++j) rb[j] = *(const uint4*)(Bs + brow[j] * 128 + ((c ^ swz(brow[j])) << 4));
-      } else if ((st & 1) == 0) {
+      } else if ((st & (MX == 2 ? 3 : 1)) == 0) {
         const unsigned char* Bs = s_ring + buf * ST + A_ST;
-        const int q = 2 * (st >> 1) + (lane >> 5);
-        const int b = kt * (BK / 32) + (st >> 1);  // 32-k block of the pair
+        const int q = MX == 2 ? 2 * (st >> 2) + (lane >> 5) : 2 * (st >> 1) + (lane >> 5);
+        // 32-k block of the lane's codes
+        const int b = kt * (BK / 32) + (MX == 2 ? 2 * (st >> 2) + (lane >> 5) : st >> 1);
         const unsigned char* Ss = s_scl + sb * SCL + (b & 3);
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
-          rb[j] = *(const uint4*)(Bs + (brow[j] / RPL) * 128 + (brow[j] % RPL) * BK + ((q ^ mxsw(brow[j], CPR)) << 4));
+          rb[j] = *(const uint4*)(Bs + (brow[j] / RPL) * 128 + (brow[j] % RPL) * RB + ((q ^ mxsw(brow[j], CPR)) << 4));
           sc[j] = e8m0_scale(Ss[brow[j] * SR + (((b >> 2) ^ ssw(brow[j], DPR)) << 2)]);
         }
       }
@@ -1023,8 +1046,14 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
     // B fragment j of k-step `st` in fp16
     auto conv1 = [&](int j, int st, const uint4 (&rb)[WN], const float (&sc)[WN], half8& out) {
       uint4 cv;
-      if constexpr (MX) cv = (st & 1) ? fp8x8_to_f16x8(rb[j].z, rb[j].w, sc[j]) : fp8x8_to_f16x8(rb[j].x, rb[j].y, sc[j]);
-      else cv = bf16x8_to_f16x8(rb[j]);
+      if constexpr (MX == 2) {
+        const int o = st & 3;
+        cv = fp4x8_to_f16x8(o == 0 ? rb[j].x : o == 1 ? rb[j].y : o == 2 ? rb[j].z : rb[j].w, sc[j]);
+      } else if constexpr (MX) {
+        cv = (st & 1) ? fp8x8_to_f16x8(rb[j].z, rb[j].w, sc[j]) : fp8x8_to_f16x8(rb[j].x, rb[j].y, sc[j]);
+      } else {
+        cv = bf16x8_to_f16x8(rb[j]);
+      }
       out = __builtin_bit_cast(half8, cv);
     };
 
@@ -1068,7 +1097,7 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
 #pragma unroll
       for (int st = 1; st < kStages; ++st) issue(st < NK ? st : NK - 1, st);
     }
-    // raw B fragments (MX: of the current step pair) and their scales
+    // raw B fragments (MX: of the current step pair or quad) and their scales
     uint4 rb[WN];
     float sc[WN];
     read_step(ring_buf(0), 0, af, rb, sc, NV, 0);
@@ -1293,7 +1322,7 @@ const void* router_fn() {
   else return (const void*)k_pre_router<H, E, 1>;
 }
 
-template <int H, int I, int E, bool MX>
+template <int H, int I, int E, int MX>
 hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   FwdArgs args = a;
   const int nb = (a.R + kRR - 1) / kRR;
@@ -1314,11 +1343,11 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   // groups of a few rows on average: the small row tile and the deeper ring
   const bool small = (int64_t)a.R * a.K <= 32LL * a.E;
-  err = launch(MX ? "gemm_gateup_swiglu_mx" : "gemm_gateup_swiglu",
+  err = launch(MX == 2 ? "gemm_gateup_swiglu_mx4" : MX ? "gemm_gateup_swiglu_mx" : "gemm_gateup_swiglu",
                small ? (const void*)k_gemm<0, H, I, GemmSmall, MX> : (const void*)k_gemm<0, H, I, GemmBig, MX>,
                dim3(grid), dim3(small ? GemmSmall::kGT : GemmBig::kGT), 0, s, &args);
   if (err != hipSuccess) return err;
-  err = launch(MX ? "gemm_down_mx" : "gemm_down",
+  err = launch(MX == 2 ? "gemm_down_mx4" : MX ? "gemm_down_mx" : "gemm_down",
                small ? (const void*)k_gemm<1, I, H, GemmSmall, MX> : (const void*)k_gemm<1, I, H, GemmBig, MX>,
                dim3(grid), dim3(small ? GemmSmall::kGT : GemmBig::kGT), 0, s, &args);
   if (err != hipSuccess) return err;
@@ -1329,7 +1358,7 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
   const int64_t sh_tiles =
       sh_small ? (a.R + GemmSmall::BM - 1) / GemmSmall::BM * (H / GemmShape<2, GemmSmall>::BN) : big_tiles;
   const int sh_grid = sh_tiles < grid ? (int)sh_tiles : grid;
-  return launch(MX ? "gemm_down_shared_reduce_mx" : "gemm_down_shared_reduce",
+  return launch(MX == 2 ? "gemm_down_shared_reduce_mx4" : MX ? "gemm_down_shared_reduce_mx" : "gemm_down_shared_reduce",
                 sh_small ? (const void*)k_gemm<2, I, H, GemmSmall, MX> : (const void*)k_gemm<2, I, H, GemmBig, MX>,
                 dim3(sh_grid), dim3(sh_small ? GemmSmall::kGT : GemmBig::kGT), 0, s, &args);
 }
@@ -1338,9 +1367,13 @@ hipError_t run_prefill_t(const FwdArgs& a, hipStream_t s) {
 
 hipError_t run_prefill(const FwdArgs& a, hipStream_t s) {
   if (a.H == 4096 && a.I == 2048 && a.E == 256)
-    return a.mx ? run_prefill_t<4096, 2048, 256, true>(a, s) : run_prefill_t<4096, 2048, 256, false>(a, s);
+    return a.mx == 2   ? run_prefill_t<4096, 2048, 256, 2>(a, s)
+           : a.mx == 1 ? run_prefill_t<4096, 2048, 256, 1>(a, s)
+                       : run_prefill_t<4096, 2048, 256, 0>(a, s);
   if (a.H == 512 && a.I == 256 && a.E == 32)
-    return a.mx ? run_prefill_t<512, 256, 32, true>(a, s) : run_prefill_t<512, 256, 32, false>(a, s);
+    return a.mx == 2   ? run_prefill_t<512, 256, 32, 2>(a, s)
+           : a.mx == 1 ? run_prefill_t<512, 256, 32, 1>(a, s)
+                       : run_prefill_t<512, 256, 32, 0>(a, s);
   return hipErrorInvalidValue;
 }
 

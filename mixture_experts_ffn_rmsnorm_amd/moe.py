@@ -19,7 +19,8 @@ LAYER_SCORE, LAYER_HASH = 0, 1
 FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY, FLAG_SYNC_TIMEOUT, FLAG_F16_RANGE = 1, 2, 4, 8
 
 # Function names the header declares (checked against the library's exports).
-EXPORTS = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp8", "moe_ffn_forward_noalloc",
+EXPORTS = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp8", "moe_ffn_forward_mxfp4",
+           "moe_ffn_forward_noalloc",
            "moe_ffn_hc_workspace_bytes", "moe_ffn_forward_hc", "moe_ffn_hc_view", "moe_route",
            "moe_ffn_routing_view", "moe_ffn_status", "moe_strerror", "moe_ffn_stage_timing_begin",
            "moe_ffn_stage_timing_end")
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(Dims), I64, ctypes.POINTER(SZ)]
         L.moe_ffn_forward.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, SZ, P]
         L.moe_ffn_forward_mxfp8.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(MxWeightsC), P, P, SZ,
+                                            P]
+        L.moe_ffn_forward_mxfp4.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(MxWeightsC), P, P, SZ,
                                             P]
         L.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P]
         L.moe_ffn_hc_workspace_bytes.argtypes = [ctypes.POINTER(Dims), I32, I64, ctypes.POINTER(SZ)]
@@ -149,6 +152,17 @@ def forward_mxfp8(dims: Dims, x, token_ids, layer_kind: int, weights: MxWeightsC
                                      ctypes.byref(weights), _ptr(out), _ptr(workspace), workspace.numel(),
                                      _stream(stream))
     _check(rc, "moe_ffn_forward_mxfp8")
+    return out
+
+
+def forward_mxfp4(dims: Dims, x, token_ids, layer_kind: int, weights: MxWeightsC, out, workspace, stream=None):
+    """``forward`` with MXFP4 expert weights (``make_mx_weights`` over packed
+    E2M1 codes); enqueue only."""
+    rows = x.shape[0]
+    rc = lib().moe_ffn_forward_mxfp4(ctypes.byref(dims), _ptr(x), _ptr(token_ids), rows, int(layer_kind),
+                                     ctypes.byref(weights), _ptr(out), _ptr(workspace), workspace.numel(),
+                                     _stream(stream))
+    _check(rc, "moe_ffn_forward_mxfp4")
     return out
 
 

@@ -92,7 +92,8 @@ def launch_name(kernel: str) -> str | None:
     template: block-scaled (MX) instances end in "_mx"; the one-row decode
     path's router-only head and shared-expert down are dec1_*."""
     name, args = _template(kernel)
-    mx = bool(args) and args[-1] == "true"
+    fmt = {"true": "_mx", "1": "_mx", "2": "_mx4"}.get(args[-1], "") if args else ""
+    mx = fmt != ""
     base = None
     if name == "k_dec_head" and len(args) == 4:
         base = "dec1_router" if args[2] == "true" else "dec_head"
@@ -110,7 +111,7 @@ def launch_name(kernel: str) -> str | None:
                 "k_route": "route", "k_hc_mix": "hc_mix", "k_hc_pre": "hc_pre", "k_hc_post": "hc_post"}.get(name)
     if base is None:
         return None
-    return base + "_mx" if mx else base
+    return base + fmt if mx else base
 
 
 def _run(cmd, log):
@@ -290,7 +291,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("what", choices=["stats", "traffic"])
     ap.add_argument("--workload", default="decode-r1-score")
-    ap.add_argument("--weights", choices=["bf16", "mxfp8"], default="bf16")
+    ap.add_argument("--weights", choices=["bf16", "mxfp8", "mxfp4"], default="bf16")
     ap.add_argument("--scratch", default="/tmp/moe_prof")
     ap.add_argument("--outdir", default=PROFILES, help="directory for the summaries (default profiles/)")
     argv = sys.argv[1:]

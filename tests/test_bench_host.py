@@ -50,25 +50,27 @@ def test_profiled_kernel_names_map_to_launch_names():
 
     ns = "void moe::(anonymous namespace)::"
     cases = {
-        "k_dec_head<4096, 2048, false, false>(moe::FwdArgs)": "dec_head",
-        "k_dec_head<4096, 2048, true, false>(moe::FwdArgs)": "dec1_router",
-        "k_dec_head<4096, 2048, true, true>(moe::FwdArgs)": "dec1_router_mx",
-        "k_dec_gateup<4096, 2048, false>(moe::FwdArgs)": "dec_gateup",
-        "k_dec_gateup<4096, 2048, true>(moe::FwdArgs)": "dec_gateup_mx",
-        "k_dec1_gateup<512, 256, false>(moe::FwdArgs)": "dec1_gateup",
-        "k_dec_down<4096, 2048, false, false>(moe::FwdArgs)": "dec_down_reduce",
-        "k_dec_down<512, 256, true, false>(moe::FwdArgs)": "dec1_down_reduce",
-        "k_dec_down<4096, 2048, true, true>(moe::FwdArgs)": "dec1_down_reduce_mx",
+        "k_dec_head<4096, 2048, false, 0>(moe::FwdArgs)": "dec_head",
+        "k_dec_head<4096, 2048, true, 0>(moe::FwdArgs)": "dec1_router",
+        "k_dec_head<4096, 2048, true, 1>(moe::FwdArgs)": "dec1_router_mx",
+        "k_dec_head<4096, 2048, true, 2>(moe::FwdArgs)": "dec1_router_mx4",
+        "k_dec_gateup<4096, 2048, 0>(moe::FwdArgs)": "dec_gateup",
+        "k_dec_gateup<4096, 2048, 1>(moe::FwdArgs)": "dec_gateup_mx",
+        "k_dec1_gateup<512, 256, 0>(moe::FwdArgs)": "dec1_gateup",
+        "k_dec1_gateup<4096, 2048, 2>(moe::FwdArgs)": "dec1_gateup_mx4",
+        "k_dec_down<4096, 2048, false, 0>(moe::FwdArgs)": "dec_down_reduce",
+        "k_dec_down<512, 256, true, 0>(moe::FwdArgs)": "dec1_down_reduce",
+        "k_dec_down<4096, 2048, true, 1>(moe::FwdArgs)": "dec1_down_reduce_mx",
         "k_pre_norm<4096>(moe::FwdArgs)": "pre_norm",
         "k_pre_router<4096, 256, 8>(moe::FwdArgs)": "pre_router",
         "k_pre_sort(moe::FwdArgs)": "pre_sort",
-        "k_gemm<0, 4096, 2048, moe::(anonymous namespace)::GemmCfg<64, 1, 128, 1, 128, 3>, false>(moe::FwdArgs)":
+        "k_gemm<0, 4096, 2048, moe::(anonymous namespace)::GemmCfg<64, 1, 128, 1, 128, 3, 4, 512>, 0>(moe::FwdArgs)":
             "gemm_gateup_swiglu",
-        "k_gemm<0, 4096, 2048, moe::(anonymous namespace)::GemmCfg<64, 1, 128, 1, 128, 3>, true>(moe::FwdArgs)":
+        "k_gemm<0, 4096, 2048, moe::(anonymous namespace)::GemmCfg<64, 1, 128, 1, 128, 3, 4, 512>, 1>(moe::FwdArgs)":
             "gemm_gateup_swiglu_mx",
-        "k_gemm<1, 2048, 4096, moe::(anonymous namespace)::GemmCfg<256, 4, 256, 2, 64, 2>, false>(moe::FwdArgs)":
+        "k_gemm<1, 2048, 4096, moe::(anonymous namespace)::GemmCfg<256, 4, 256, 2, 64, 2, 4, 512>, 0>(moe::FwdArgs)":
             "gemm_down",
-        "k_gemm<2, 2048, 4096, moe::(anonymous namespace)::GemmCfg<256, 4, 256, 2, 64, 2>, true>(moe::FwdArgs)":
+        "k_gemm<2, 2048, 4096, moe::(anonymous namespace)::GemmCfg<256, 4, 256, 2, 64, 2, 4, 512>, 1>(moe::FwdArgs)":
             "gemm_down_shared_reduce_mx",
         "k_route(moe::RouteArgs)": "route",
         "k_hc_mix<4>(moe::HcArgs)": "hc_mix",

@@ -18,28 +18,34 @@ pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarnin
 SCORE, HASH = ref.LAYER_SCORE, ref.LAYER_HASH
 
 
-class MxLayer:
-    """One layer with MXFP8 experts on the device, and the oracle's view of
-    the same codes and scales."""
+E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0)
 
-    def __init__(self, cfg: gen.Config, layer: int = 0):
+
+class MxLayer:
+    """One layer with block-scaled experts on the device (``fmt`` "mxfp8" or
+    "mxfp4"), and the oracle's view of the same codes and scales."""
+
+    def __init__(self, cfg: gen.Config, layer: int = 0, fmt: str = "mxfp8"):
         import torch
 
         self.cfg = cfg
+        self.fmt = fmt
+        tag = (ref.MXFP4,) if fmt == "mxfp4" else ()
         hi = gen.host_inputs(cfg, layer=layer)
         self.host = hi
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         self.norm_w, self.bias = t(hi.norm_w), t(hi.sel_bias)
         self.router = t(hi.router.view(np.int16)).view(torch.bfloat16)
         self.table = t(hi.tid2eid) if hi.tid2eid is not None else None
-        routed, shared = gen.mx_expert_weights(cfg, "cuda", layer)
+        draw = gen.mx4_expert_weights if fmt == "mxfp4" else gen.mx_expert_weights
+        routed, shared = draw(cfg, "cuda", layer)
         self.routed, self.shared = routed, shared
 
         def expert(e):  # fetched per call: the oracle asks once per expert
-            return tuple(gen.mx_host((m[0][e], m[1][e])) for m in self.routed)
+            return tuple(gen.mx_host((m[0][e], m[1][e])) + tag for m in self.routed)
 
         self.oracle_w = ref.Weights(hi.norm_w, hi.router, hi.sel_bias, hi.tid2eid, expert,
-                                    tuple(gen.mx_host(m) for m in shared))
+                                    tuple(gen.mx_host(m) + tag for m in shared))
         self.dims = moe.dims_of(cfg)
         self.cw = moe.make_mx_weights(self.norm_w, self.router, self.bias, self.table, *routed, *shared)
 
@@ -56,7 +62,7 @@ class MxLayer:
         tok = torch.from_numpy(np.ascontiguousarray(tok_np, dtype=np.int32)).cuda() if tok_np is not None else None
         out = torch.full((R, self.cfg.hidden), float("nan"), dtype=torch.float32, device="cuda")
         ws = moe.alloc_workspace(self.dims, R)
-        moe.forward_mxfp8(self.dims, x, tok, kind, self.cw, out, ws)
+        (moe.forward_mxfp4 if self.fmt == "mxfp4" else moe.forward_mxfp8)(self.dims, x, tok, kind, self.cw, out, ws)
         lg, idx, w = moe.routing_view(self.dims, R, ws)
         st = moe.status(ws)
         torch.cuda.synchronize()
@@ -69,7 +75,11 @@ class MxLayer:
 
         def b16(pair):
             q, s = pair
-            v = q.view(torch.float8_e4m3fn).to(torch.float32)
+            if self.fmt == "mxfp4":
+                codes = torch.stack([q & 15, q >> 4], dim=-1).flatten(-2).long()
+                v = torch.tensor(E2M1, device=q.device)[codes]
+            else:
+                v = q.view(torch.float8_e4m3fn).to(torch.float32)
             sc = torch.exp2(s.to(torch.float32) - 127.0).repeat_interleave(gen.MX_BLOCK, dim=-1)
             return (v * sc).to(torch.bfloat16)
 
@@ -243,3 +253,141 @@ def test_full_mx_prefill_8192_skewed():
     near = check_forward(lay, hi.x, None, SCORE, out, lg, idx, w)
     report_near_ties(f"mx {cfg.name}", near, cfg.rows)
     np.testing.assert_array_equal(out, lay.run(hi.x, None, SCORE)[0])
+
+
+# ------------------------------------------------------------- MXFP4 ---
+@pytest.fixture(scope="module")
+def tiny_mx4():
+    return MxLayer(gen.config(0), fmt="mxfp4")
+
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 4])
+@pytest.mark.parametrize("kind", [SCORE, HASH])
+def test_tiny_mx4_decode(tiny_mx4, rows, kind):
+    cfg = tiny_mx4.cfg
+    x = _x(cfg, rows, 400 + rows)
+    tok = _tok(cfg, rows, 410 + rows) if kind == HASH else None
+    out, lg, idx, w, st = tiny_mx4.run(x, tok, kind)
+    assert st == 0
+    check_forward(tiny_mx4, x, tok, kind, out, lg, idx, w, rel=1e-5, maxabs=5e-5)
+
+
+def test_tiny_mx4_matches_bf16_twin(tiny_mx4):
+    """E2M1 * 2^k fits bf16 exactly: the bf16 path on the same values agrees
+    to f32 rounding."""
+    import torch
+
+    cfg = tiny_mx4.cfg
+    twin = tiny_mx4.bf16_twin()
+    for rows in (1, 4):
+        x = _x(cfg, rows, 420 + rows)
+        out_mx = tiny_mx4.run(x, None, SCORE)[0]
+        xd = torch.from_numpy(x).cuda()
+        ob = torch.empty_like(xd)
+        moe.forward(tiny_mx4.dims, xd, None, SCORE, twin, ob, moe.alloc_workspace(tiny_mx4.dims, rows))
+        torch.cuda.synchronize()
+        check_output(out_mx, ob.cpu().numpy(), rel=1e-6, maxabs=1e-5, what=f"mx4 vs bf16 twin, {rows} rows")
+
+
+@pytest.mark.parametrize("rows", [3, 37])
+def test_tiny_mx4_special_scales(rows):
+    """Scale 255 (NaN) poisons exactly the rows routed to its expert; scale 0
+    (2^-127) makes its block vanish."""
+    lay = MxLayer(gen.config(0), layer=3, fmt="mxfp4")
+    cfg = lay.cfg
+    x = _x(cfg, rows, 430)
+    _, _, idx0, _, _ = lay.run(x, None, SCORE)
+    e_nan = int(idx0[0, 0])
+    e_zero = int(idx0[rows - 1, -1]) if int(idx0[rows - 1, -1]) != e_nan else int(idx0[rows - 1, 0])
+    lay.set_scale(0, e_nan, 5, 1, 255)
+    lay.set_scale(2, e_zero, 7, 0, 0)
+    out, lg, idx, w, st = lay.run(x, None, SCORE)
+    res = ref.forward(x, None, SCORE, lay.oracle_w, cfg.top_k, cfg.eps)
+    nan_rows = np.isnan(res["out"]).any(axis=1)
+    assert nan_rows[0] and not nan_rows.all()
+    np.testing.assert_array_equal(np.isnan(out).any(axis=1), nan_rows)
+    if rows > 4:
+        assert st & moe.FLAG_F16_RANGE
+    tol = 1e-5 if rows <= 4 else PREFILL_TOL
+    check_output(out[~nan_rows], res["out"][~nan_rows], rel=tol, maxabs=5 * tol, what="finite rows")
+
+
+@pytest.mark.parametrize("rows", [5, 37, 300])
+def test_tiny_mx4_prefill(tiny_mx4, rows):
+    """More than 4 rows: 4-bit B tiles (37 rows the small tile, 300 the big
+    one) converted to fp16 with their scales."""
+    cfg = tiny_mx4.cfg
+    x = _x(cfg, rows, 440 + rows)
+    out, lg, idx, w, st = tiny_mx4.run(x, None, SCORE)
+    assert st == 0
+    check_forward(tiny_mx4, x, None, SCORE, out, lg, idx, w, rel=PREFILL_TOL, maxabs=PREFILL_TOL * 5)
+    tok = _tok(cfg, rows, 445 + rows)
+    out, lg, idx, w, st = tiny_mx4.run(x, tok, HASH)
+    assert st == 0
+    check_forward(tiny_mx4, x, tok, HASH, out, lg, idx, w, rel=PREFILL_TOL, maxabs=PREFILL_TOL * 5)
+
+
+@pytest.mark.parametrize("rows", [37, 300])
+def test_tiny_mx4_prefill_matches_bf16_twin(tiny_mx4, rows):
+    """The same fp16 operands as the bf16 path on the same values; only the
+    k order inside the MFMAs differs."""
+    import torch
+
+    cfg = tiny_mx4.cfg
+    twin = tiny_mx4.bf16_twin()
+    x = _x(cfg, rows, 460 + rows)
+    out_mx = tiny_mx4.run(x, None, SCORE)[0]
+    xd = torch.from_numpy(x).cuda()
+    ob = torch.empty_like(xd)
+    moe.forward(tiny_mx4.dims, xd, None, SCORE, twin, ob, moe.alloc_workspace(tiny_mx4.dims, rows))
+    torch.cuda.synchronize()
+    check_output(out_mx, ob.cpu().numpy(), rel=1e-4, maxabs=5e-4, what=f"mx4 vs bf16 twin, {rows} rows")
+
+
+def test_full_mx4_prefill_512():
+    cfg = gen.config(3)
+    lay = MxLayer(cfg, fmt="mxfp4")
+    hi = lay.host
+    out, lg, idx, w, st = lay.run(hi.x, None, SCORE)
+    assert st == 0
+    near = check_forward(lay, hi.x, None, SCORE, out, lg, idx, w)
+    report_near_ties(f"mx4 {cfg.name}", near, cfg.rows)
+
+
+def test_full_mx4_prefill_8192_skewed():
+    cfg = gen.config(4)
+    lay = MxLayer(cfg, fmt="mxfp4")
+    hi = lay.host
+    out, lg, idx, w, st = lay.run(hi.x, None, SCORE)
+    assert st == 0
+    near = check_forward(lay, hi.x, None, SCORE, out, lg, idx, w)
+    report_near_ties(f"mx4 {cfg.name}", near, cfg.rows)
+    np.testing.assert_array_equal(out, lay.run(hi.x, None, SCORE)[0])
+
+
+@pytest.fixture(scope="module")
+def full_mx4():
+    return MxLayer(gen.config(1), fmt="mxfp4")
+
+
+def test_full_mx4_decode_one_row(full_mx4):
+    hi = full_mx4.host
+    out, lg, idx, w, st = full_mx4.run(hi.x, None, SCORE)
+    assert st == 0
+    check_forward(full_mx4, hi.x, None, SCORE, out, lg, idx, w, rel=1e-5, maxabs=5e-5)
+
+
+def test_full_mx4_decode_cohort():
+    lay = MxLayer(gen.config(2), fmt="mxfp4")
+    hi = lay.host
+    out, lg, idx, w, st = lay.run(hi.x, hi.token_ids, HASH)
+    assert st == 0
+    check_forward(lay, hi.x, hi.token_ids, HASH, out, lg, idx, w, rel=1e-5, maxabs=5e-5)
+
+
+@pytest.mark.parametrize("rows", [2, 3])
+def test_full_mx4_decode_ragged(full_mx4, rows):
+    x = _x(full_mx4.cfg, rows, 450 + rows)
+    out, lg, idx, w, st = full_mx4.run(x, None, SCORE)
+    near = check_forward(full_mx4, x, None, SCORE, out, lg, idx, w, rel=1e-5, maxabs=5e-5)
+    report_near_ties(f"mx4 {rows} rows", near, rows)
