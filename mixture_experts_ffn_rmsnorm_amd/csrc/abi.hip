@@ -176,9 +176,18 @@ int check_forward_args(const moe_dims_t* d, const float* x, const int32_t* token
 // checked: at least L.total bytes, 256-byte aligned).  With `mx` the expert
 // matrices are the block-scaled ones there, in format `mx_format` (1 MXFP8,
 // 2 MXFP4; w then supplies only the small parameters).
+// The hyper-connection post-mix folded into a decode call's reduce.
+struct HcPost {
+  int hc;
+  const float* state;
+  const float* maps;
+  float* x;  // the FFN input, stored for the view
+  float* out;
+};
+
 int forward_in(const moe_dims_t* d, const float* x, const int32_t* token_ids, int64_t rows, int layer_kind,
                const moe_weights_t* w, const moe_mx_weights_t* mx, int mx_format, float* out, void* workspace,
-               const Layout& L, void* stream) {
+               const Layout& L, void* stream, const HcPost* post = nullptr) {
   char* ws = (char*)workspace;
   FwdArgs a;
   memset(&a, 0, sizeof(a));
@@ -219,6 +228,13 @@ int forward_in(const moe_dims_t* d, const float* x, const int32_t* token_ids, in
     a.down_sh_s = mx->down_sh.scales;
   }
   a.out = out;
+  if (post) {
+    a.hc = post->hc;
+    a.hc_state = post->state;
+    a.hc_maps = post->maps;
+    a.hc_x = post->x;
+    a.hc_out = post->out;
+  }
   a.status = (uint32_t*)(ws + L.status);
   a.sync = (DecodeSync*)(ws + L.status + 64);  // both paths: the status block
   a.logits = (float*)(ws + L.logits);
@@ -436,11 +452,18 @@ int moe_ffn_forward_hc(const moe_dims_t* d, const float* state_in, const int32_t
   a.ffn_in = (float*)(ws + L.ffn_in);
   a.ffn_out = (float*)(ws + L.ffn_out);
   a.out = state_out;
+  // 1-4 rows: the mix launch's last block splits (its arrival count sits at
+  // a fixed place in the status block), the decode launches form the FFN
+  // input from the streams, and the decode reduce does the post-mix
+  const bool small = rows <= kDecodeMaxRows;
+  a.cnt = small ? (uint32_t*)(ws + L.ffn.status + 64 + offsetof(DecodeSync, hc_arrive)) : nullptr;
   hipStream_t s = (hipStream_t)stream;
   if (run_hc_pre(a, s) != hipSuccess) return MOE_EHIP;
+  const HcPost post{hw->hc, state_in, a.maps, a.ffn_in, state_out};
   rc = forward_in(d, a.ffn_in, token_ids, rows, layer_kind, w, nullptr, 0, (float*)(ws + L.ffn_out), workspace,
-                  L.ffn, stream);
+                  L.ffn, stream, small ? &post : nullptr);
   if (rc) return rc;
+  if (small) return MOE_OK;
   return run_hc_post(a, s) == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

@@ -243,21 +243,54 @@ __device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const floa
 // Every row's loads go out before the first reduction (one memory round
 // trip for the batch, not one per row), and the values stay in registers
 // for the scaled write.  The first floats of xs double as the cross-wave
-// reduction scratch.
+// reduction scratch.  With the hyper-connection wrapper folded in (a.hc >
+// 0) each row is formed from the streams, x[r] = sum_i pre[r][i] *
+// state[r][i] (i in order, from 0), and `store_x` stores it to a.hc_x.
 template <int H>
-__device__ __forceinline__ void norm_rows_to_lds(const float* __restrict__ x, const float* __restrict__ g, int R,
-                                                 float eps, float* xs) {
+__device__ __forceinline__ void norm_rows_to_lds(const FwdArgs& a, bool store_x, float* xs) {
+  const float* __restrict__ x = a.x;
+  const float* __restrict__ g = a.norm_w;
+  const int R = a.R;
+  const float eps = a.eps;
   const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
   constexpr int V = H / 4;                            // float4 per row
   constexpr int NPT = (V + kThreads - 1) / kThreads;  // float4 per thread and row
   float4 v[kDecodeMaxRows][NPT];
+  if (a.hc > 0) {
+    const int hc = a.hc, mw = (2 + hc) * hc;
+    float p[kDecodeMaxRows][kHcMax];
 #pragma unroll
-  for (int r = 0; r < kDecodeMaxRows; ++r)
+    for (int r = 0; r < kDecodeMaxRows; ++r)
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-      const int i = t + k * kThreads;
-      v[r][k] = (r < R && i < V) ? ((const float4*)(x + (int64_t)r * H))[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+      for (int i = 0; i < kHcMax; ++i) p[r][i] = (r < R && i < hc) ? a.hc_maps[r * mw + i] : 0.f;
+#pragma unroll
+    for (int r = 0; r < kDecodeMaxRows; ++r)
+#pragma unroll
+      for (int k = 0; k < NPT; ++k) {
+        const int idx = t + k * kThreads;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < R && idx < V) {
+#pragma unroll
+          for (int i = 0; i < kHcMax; ++i) {
+            if (i < hc) {
+              const float4 s = ((const float4*)(a.hc_state + ((int64_t)r * hc + i) * H))[idx];
+              o.x = fmaf(p[r][i], s.x, o.x); o.y = fmaf(p[r][i], s.y, o.y);
+              o.z = fmaf(p[r][i], s.z, o.z); o.w = fmaf(p[r][i], s.w, o.w);
+            }
+          }
+          if (store_x) ((float4*)(a.hc_x + (int64_t)r * H))[idx] = o;
+        }
+        v[r][k] = o;
+      }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kDecodeMaxRows; ++r)
+#pragma unroll
+      for (int k = 0; k < NPT; ++k) {
+        const int i = t + k * kThreads;
+        v[r][k] = (r < R && i < V) ? ((const float4*)(x + (int64_t)r * H))[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+  }
 #pragma unroll
   for (int r = 0; r < kDecodeMaxRows; ++r) {
     if (r < R) {
@@ -804,7 +837,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   if (!kRouterOnly && b >= nrb) {  // shared gate/up block
     const int x = b - nrb;
     auto stage = [&]() {
-      norm_rows_to_lds<H>(a.x, a.norm_w, R, a.eps, xs);
+      norm_rows_to_lds<H>(a, false, xs);
       if (x == 0)
         for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
     };
@@ -826,7 +859,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
     for (int c = 0; c < NCH; ++c)
       if (c < NCH - 1 || full) q[c] = load_stream(a.router + (int64_t)e * H + c * 512 + lane * 8);
   }
-  norm_rows_to_lds<H>(a.x, a.norm_w, R, a.eps, xs);
+  norm_rows_to_lds<H>(a, b == 0, xs);
   if (kRouterOnly && b == 0)  // the later launches stage the normalised row from xn
     for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
   if (e < E) {
@@ -1038,6 +1071,13 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   if (t >= R * kDnRows) return;
   const int r = t / kDnRows;
   const int h = x + (t % kDnRows) * dnt;
+  // hyper-connection post-mix: the row's old streams at h, requested first
+  float st[kHcMax];
+  if (a.hc > 0) {
+#pragma unroll
+    for (int i = 0; i < kHcMax; ++i)
+      if (i < a.hc) st[i] = a.hc_state[((int64_t)r * a.hc + i) * H + h];
+  }
   // written through by other blocks of this launch when kShared (the shared
   // half-blocks), so read past any stale cache line like the partials below
   const float sh = load_wt(&a.d32[(int64_t)(kDecodeMaxSlots + r) * H + h]);
@@ -1055,6 +1095,20 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   }
   o += sh;
   a.out[(int64_t)r * H + h] = o;
+  if (a.hc > 0) {  // new[r][j] = post_j * out + sum_i comb[j][i] * state_i, i in order
+    const int hc = a.hc, mw = (2 + hc) * hc;
+    const float* mp = a.hc_maps + (int64_t)r * mw;
+#pragma unroll
+    for (int j = 0; j < kHcMax; ++j) {
+      if (j < hc) {
+        float v = mp[hc + j] * o;
+#pragma unroll
+        for (int i = 0; i < kHcMax; ++i)
+          if (i < hc) v = fmaf(mp[2 * hc + j * hc + i], st[i], v);
+        a.hc_out[((int64_t)r * hc + j) * H + h] = v;
+      }
+    }
+  }
 }
 
 template <int H, int I, int MX>

@@ -9,12 +9,15 @@
 //
 //   k_hc_mix   one block per (row tile, slice of kHcSlice flattened inputs):
 //              the slice's dot products with every hc_fn row and its sum of
-//              squares
+//              squares; with 1-4 rows (one tile) the block that completes
+//              the arrival count adds the slices and splits every row (the
+//              decode launches then form the FFN input from the streams)
 //   k_hc_pre   per (row, hidden chunk): the row's slices added in order,
 //              normalised and split (pre and post by sigmoid, comb by exp
 //              and Sinkhorn rounds with one lane per (output, input) stream
 //              pair), then FFN input = sum_i pre_i * state_i
 //   k_hc_post  new_j = post_j * ffn_output + sum_i comb[j][i] * state_i
+//              (more than 4 rows; with 1-4 the decode reduce does it)
 //
 // Everything is f32 with sums in a fixed order (bitwise reproducible).
 #include "device.h"
@@ -25,6 +28,56 @@ namespace {
 
 constexpr int kHcThreads = 256;
 constexpr int kHcWaves = kHcThreads / kWave;
+
+// The split of up to kHcRows rows by one whole wave (every lane active for
+// the DPP moves): lane 16 * rr + 4j + i holds comb entry (j, i) of row rr
+// through the Sinkhorn rounds (row sums over the lanes of one j: a quad;
+// column sums over the lanes of one i: 4 apart, reached by rotating the
+// 16-lane row by 4 and by 8; each division a reciprocal and a multiply,
+// within 2 ulp).  sums[rr]: the row's mix sums, the sum of squares last.
+// Writes the maps of rows rr < nrr to maps[rr] (LDS) and, with `store`,
+// their mixes to a.mixes from row r0 on.
+template <int HC>
+__device__ __forceinline__ void split_rows(const HcArgs& a, const float (*sums)[(2 + HC) * HC + 1], int nrr,
+                                           int64_t r0, bool store, float (*maps)[(2 + HC) * HC]) {
+  constexpr int MW = (2 + HC) * HC;
+  const int lane = threadIdx.x % kWave, rr = lane / 16, j = (lane / 4) % 4, i = lane % 4;
+  const bool row_ok = rr < nrr;
+  const int rs = row_ok ? rr : 0;  // every lane reads a valid row
+  const float rinv = 1.0f / sqrtf(sums[rs][MW] / (float)(HC * a.H) + a.eps);
+  const bool in = row_ok && j < HC && i < HC;
+  if (in && i == 0) {  // pre_j and post_j
+    maps[rr][j] = 1.0f / (1.0f + expf(-(a.scale[0] * (sums[rs][j] * rinv) + a.base[j])));
+    maps[rr][HC + j] = 2.0f / (1.0f + expf(-(a.scale[1] * (sums[rs][HC + j] * rinv) + a.base[HC + j])));
+  }
+  float c = 0.f;
+  if (in) c = expf(a.scale[2] * (sums[rs][2 * HC + j * HC + i] * rinv) + a.base[2 * HC + j * HC + i]);
+  for (int it = 0; it < a.iters; ++it) {
+    float rsum = c + dpp_f32<0xB1>(c);
+    rsum += dpp_f32<0x4E>(rsum);
+    c = in ? c * __builtin_amdgcn_rcpf(rsum) : 0.f;
+    float csum = c + dpp_f32<0x124>(c);
+    csum += dpp_f32<0x128>(csum);
+    c = in ? c * __builtin_amdgcn_rcpf(csum) : 0.f;
+  }
+  if (in) maps[rr][2 * HC + j * HC + i] = c;
+  if (store && row_ok)
+    for (int m = lane % 16; m < MW; m += 16) a.mixes[(r0 + rr) * MW + m] = sums[rr][m] * rinv;
+}
+
+// FFN input of row r (maps in LDS) for hidden values h .. h+3
+template <int HC>
+__device__ __forceinline__ void pre_mix(const HcArgs& a, int64_t r, const float* map, int h) {
+  const float* st = a.state + r * HC * a.H + h;
+  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < HC; ++i) {
+    const float p = map[i];
+    const float4 s = *(const float4*)(st + (int64_t)i * a.H);
+    x.x = fmaf(p, s.x, x.x); x.y = fmaf(p, s.y, x.y); x.z = fmaf(p, s.z, x.z); x.w = fmaf(p, s.w, x.w);
+  }
+  *(float4*)(a.ffn_in + r * a.H + h) = x;
+}
 
 template <int HC>
 __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
@@ -76,79 +129,58 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
     float v = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < kHcWaves; ++w2) v += s_part[w2][q];
-    part[q] = v;
+    store_wt(&part[q], v);  // read by the last block below (1-4 rows) or the next launch
   }
+  if (!a.cnt) return;
+  // 1-4 rows (one tile): the block that completes the arrival count adds
+  // the slices in order and splits
+  sync_stores();
+  __syncthreads();
+  __shared__ int s_last;
+  if (t == 0) s_last = __hip_atomic_fetch_add(a.cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+                       (uint32_t)a.slices;
+  __syncthreads();
+  if (!s_last) return;
+  if (t == 0) *a.cnt = 0u;  // ready for the next call
+  __shared__ float s_sum[kHcRows][V];
+  __shared__ float s_map[kHcRows][MW];
+  for (int q = t; q < nr * V; q += kHcThreads) {
+    float v = 0.f;
+#pragma unroll 8
+    for (int64_t s2 = 0; s2 < a.slices; ++s2) v += load_wt(&a.partial[s2 * (kHcRows * V) + q]);
+    s_sum[q / V][q % V] = v;
+  }
+  __syncthreads();
+  if (wv == 0) split_rows<HC>(a, s_sum, nr, 0, true, s_map);
+  __syncthreads();
+  for (int q = t; q < nr * MW; q += kHcThreads) a.maps[q] = s_map[q / MW][q % MW];
 }
 
-// One row's split, then its FFN input for 4 hidden values per thread.
-// Lane m of wave 0 adds mix m over the row's slices in order; lanes 0-15
-// normalise and split: lane 4j + i holds comb entry (j, i) through the
-// Sinkhorn rounds (row sums over the lanes of one j, column sums over the
-// lanes of one i, by DPP moves; each division is a reciprocal and a
-// multiply, within 2 ulp).
-// Every hidden chunk of a row repeats the split; chunk 0 stores the mixes
+// More than 4 rows: one row's split, then its FFN input for 4 hidden values
+// per thread.  Lane m of wave 0 adds mix m over the row's slices in order;
+// every hidden chunk of a row repeats the split; chunk 0 stores the mixes
 // and maps.
 template <int HC>
 __global__ __launch_bounds__(kHcThreads) void k_hc_pre(const HcArgs a) {
   constexpr int MW = (2 + HC) * HC, V = MW + 1;
   const int64_t r = blockIdx.x;
   const int t = threadIdx.x;
-  __shared__ float s_map[MW];
-  __shared__ float s_sum[V];
+  __shared__ float s_map[1][MW];
+  __shared__ float s_sum[1][V];
   if (t < V) {  // mix t (t = MW: the sum of squares) over the slices, in order
     const float* part = a.partial + (r / kHcRows) * a.slices * (kHcRows * V) + (r % kHcRows) * V + t;
     float v = 0.f;
 #pragma unroll 8
     for (int64_t s2 = 0; s2 < a.slices; ++s2) v += part[s2 * (kHcRows * V)];
-    s_sum[t] = v;
+    s_sum[0][t] = v;
   }
   __syncthreads();
-  if (t < kWave) {  // wave 0 (every lane active for the DPP moves); lanes 0-15 keep the result
-    const int j = (t / 4) % 4, i = t % 4;
-    float mix[V];  // entries t, t + 16, ... are this lane's to store
-#pragma unroll
-    for (int m = 0; m < V; ++m) mix[m] = s_sum[m];
-    const float rinv = 1.0f / sqrtf(mix[MW] / (float)(HC * a.H) + a.eps);
-#pragma unroll
-    for (int m = 0; m < MW; ++m) mix[m] *= rinv;
-    const bool in = j < HC && i < HC && t < 16;
-    if (in && i == 0) {  // pre_j and post_j
-      s_map[j] = 1.0f / (1.0f + expf(-(a.scale[0] * mix[j] + a.base[j])));
-      s_map[HC + j] = 2.0f / (1.0f + expf(-(a.scale[1] * mix[HC + j] + a.base[HC + j])));
-    }
-    float c = 0.f;
-    if (in) c = expf(a.scale[2] * mix[2 * HC + j * HC + i] + a.base[2 * HC + j * HC + i]);
-    // rows: the 4 lanes of one j are one quad; columns: the 4 lanes of one
-    // i are 4 apart in the row, reached by rotating it by 4 and by 8
-    for (int it = 0; it < a.iters; ++it) {
-      float rs = c + dpp_f32<0xB1>(c);
-      rs += dpp_f32<0x4E>(rs);
-      c = in ? c * __builtin_amdgcn_rcpf(rs) : 0.f;
-      float cs = c + dpp_f32<0x124>(c);
-      cs += dpp_f32<0x128>(cs);
-      c = in ? c * __builtin_amdgcn_rcpf(cs) : 0.f;
-    }
-    if (in) s_map[2 * HC + j * HC + i] = c;
-    if (blockIdx.y == 0 && t < 16) {
-#pragma unroll
-      for (int m = 0; m < MW; ++m)
-        if (m % 16 == t) a.mixes[r * MW + m] = mix[m];
-    }
-  }
+  if (t < kWave) split_rows<HC>(a, s_sum, 1, r, blockIdx.y == 0, s_map);
   __syncthreads();
   if (blockIdx.y == 0)
-    for (int m = t; m < MW; m += kHcThreads) a.maps[r * MW + m] = s_map[m];
+    for (int m = t; m < MW; m += kHcThreads) a.maps[r * MW + m] = s_map[0][m];
   const int h = (blockIdx.y * kHcThreads + t) * 4;
-  if (h >= a.H) return;
-  const float* st = a.state + r * HC * a.H + h;
-  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int i = 0; i < HC; ++i) {
-    const float p = s_map[i];
-    const float4 s = *(const float4*)(st + (int64_t)i * a.H);
-    x.x = fmaf(p, s.x, x.x); x.y = fmaf(p, s.y, x.y); x.z = fmaf(p, s.z, x.z); x.w = fmaf(p, s.w, x.w);
-  }
-  *(float4*)(a.ffn_in + r * a.H + h) = x;
+  if (h < a.H) pre_mix<HC>(a, r, s_map[0], h);
 }
 
 // new state: 4 hidden values of every stream per thread
@@ -182,7 +214,7 @@ hipError_t run_hc_pre_t(const HcArgs& a, hipStream_t s) {
   hipError_t err = launch("hc_mix", (const void*)k_hc_mix<HC>,
                           dim3((unsigned)((a.R + kHcRows - 1) / kHcRows), (unsigned)a.slices), dim3(kHcThreads), 0, s,
                           &args);
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || a.cnt) return err;  // 1-4 rows: the mix launch has finished the prelude
   return launch("hc_pre", (const void*)k_hc_pre<HC>, dim3(a.R, (a.H / 4 + kHcThreads - 1) / kHcThreads),
                 dim3(kHcThreads), 0, s, &args);
 }

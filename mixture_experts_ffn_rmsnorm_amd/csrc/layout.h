@@ -43,7 +43,8 @@ struct DecodePlan {
 constexpr int kDecodeMaxTiles = 256;  // down column tiles (hidden/32) and shared gate/up tiles (inter/8)
 struct DecodeSync {
   uint32_t arrive;                       // router blocks of the current call that have written their logits
-  uint32_t pad[15];
+  uint32_t hc_arrive;                    // hyper-connection mix blocks of the current call (1-4 rows)
+  uint32_t pad[14];
   uint32_t tile_cnt[kDecodeMaxTiles];    // groups finished per down column tile
   // one-row path: each expert's ordered selection key and float64 sigmoid,
   // written by the router launch for the gate/up blocks that route
@@ -126,6 +127,7 @@ inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
 // tile and slice; the next launch adds them.
 constexpr int kHcMax = 4;       // streams
 constexpr int kHcRows = 4;      // rows per mix tile
+static_assert(kHcRows == kDecodeMaxRows, "a decode call is one mix tile");
 constexpr int kHcSlice = 1024;  // flattened state values per mix block
 struct HcLayout {
   Layout ffn;
