@@ -69,7 +69,7 @@ enum {
   MOE_FLAG_SYNC_TIMEOUT = 4u,    /* reserved, never set: no workgroup of
                                     any call waits for another (kept so the
                                     bit values stay stable)                 */
-  MOE_FLAG_F16_RANGE = 8u        /* calls of more than 4 rows only (the
+  MOE_FLAG_F16_RANGE = 8u,       /* calls of more than 4 rows only (the
                                     matrix-core path, whose operands are
                                     fp16): a router logit, SwiGLU output,
                                     routed down output or layer output was
@@ -78,6 +78,13 @@ enum {
                                     non-finite input; the output is not
                                     valid.  Calls of 1 to 4 rows compute in
                                     f32 and never set it                    */
+  MOE_FLAG_CHECK = 16u           /* checked build (libmoeffn_checked.so)
+                                    only: an index that an earlier step of
+                                    the call produced (a row list, a routing
+                                    plan entry, a slot position) failed its
+                                    bounds test where it was used; the access
+                                    was clamped, the output is not valid.
+                                    The default build never sets it         */
 };
 
 /* Layer dimensions.  ffn_forward.rs guards the native path with fixed

@@ -5,8 +5,11 @@
 Each ``csrc/*.hip`` compiles to an object under ``_build/`` in parallel, then
 everything links into ``mixture_experts_ffn_rmsnorm_amd/libmoeffn.so``;
 ``peaks/peaks.hip`` (the device-ceiling microbenchmarks) becomes
-``mixture_experts_ffn_rmsnorm_amd/libmoepeaks.so``.  The build always
-recompiles (it is the "does it build" check); loading code never builds.
+``mixture_experts_ffn_rmsnorm_amd/libmoepeaks.so``; the same sources built
+with ``-DMOE_CHECKED`` become ``libmoeffn_checked.so``, the checked build
+(bounds tests on the indices the call itself produces, reported through
+MOE_FLAG_CHECK).  The build always recompiles (it is the "does it build"
+check); loading code never builds.
 """
 
 from __future__ import annotations
@@ -24,6 +27,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoeffn.so")
+CHECKED_LIB = os.path.join(PKG, "libmoeffn_checked.so")
 PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
 PEAKS_LIB = os.path.join(PKG, "libmoepeaks.so")
 ARCH = os.environ.get("MOEFFN_ARCH", "gfx950")
@@ -39,9 +43,9 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, checked: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + (".checked.o" if checked else ".o"))
+    cmd = [HIPCC, *CFLAGS, *(["-DMOE_CHECKED"] if checked else []), "-c", src, "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{p.stderr}")
@@ -63,13 +67,15 @@ def _link(objs, lib: str) -> None:
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
-        objs = list(ex.map(_compile, srcs + [PEAKS_SRC]))
-    _link(objs[-1:], PEAKS_LIB)
-    objs = objs[:-1]
-    _link(objs, LIB)
+    jobs = [(s, False) for s in srcs] + [(PEAKS_SRC, False)] + [(s, True) for s in srcs]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    n = len(srcs)
+    _link(objs[n:n + 1], PEAKS_LIB)
+    _link(objs[:n], LIB)
+    _link(objs[n + 1:], CHECKED_LIB)
     if verbose:
-        print(f"built {LIB} and {PEAKS_LIB}")
+        print(f"built {LIB}, {CHECKED_LIB} and {PEAKS_LIB}")
     return LIB
 
 

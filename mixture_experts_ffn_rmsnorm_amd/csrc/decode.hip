@@ -759,11 +759,12 @@ __device__ __forceinline__ int plan_ngroups(const DecodePlan* P) {
   const int n = P->ngroups;
   return n < 0 ? 0 : (n > kDecodeMaxSlots ? kDecodeMaxSlots : n);
 }
-__device__ __forceinline__ PlanGroup plan_group(const DecodePlan* P, int u, int E) {
+__device__ __forceinline__ PlanGroup plan_group(const DecodePlan* P, int u, int E, uint32_t* status) {
   PlanGroup g;
   const int e = P->group_expert[u];
   g.expert = e < 0 ? 0 : (e >= E ? E - 1 : e);
   int b = P->group_begin[u], n = P->group_begin[u + 1];
+  check_index(status, e >= 0 && e < E && b >= 0 && n > b && n - b <= kDecodeMaxRows && n <= kDecodeMaxSlots);
   b = b < 0 ? 0 : (b > kDecodeMaxSlots - 1 ? kDecodeMaxSlots - 1 : b);
   n = n - b;  // n <= 0 (only from a corrupt plan) just means no rows
   n = n > kDecodeMaxRows ? kDecodeMaxRows : n;
@@ -772,8 +773,9 @@ __device__ __forceinline__ PlanGroup plan_group(const DecodePlan* P, int u, int 
   g.nr = n;
   return g;
 }
-__device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R) {
+__device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R, uint32_t* status) {
   const int r = P->entry_row[j];
+  check_index(status, r >= 0 && r < R);
   return r < 0 ? 0 : (r >= R ? R - 1 : r);
 }
 
@@ -942,10 +944,10 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
   const DecodePlan* P = a.plan;
   const int u = (b - nsd) / gut, x = (b - nsd) % gut;
   if (u >= plan_ngroups(P)) return;
-  const PlanGroup g = plan_group(P, u, a.E);
+  const PlanGroup g = plan_group(P, u, a.E, a.status);
   const float* src[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) src[j] = a.xn32 + (int64_t)plan_row(P, g.begin + (j < g.nr ? j : 0), a.R) * H;
+  for (int j = 0; j < 4; ++j) src[j] = a.xn32 + (int64_t)plan_row(P, g.begin + (j < g.nr ? j : 0), a.R, a.status) * H;
   gateup_tile<H, I, kGuRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.gate, a.gate_q, a.gate_s, g.expert, (int64_t)I * H),
                                     expert_mat<MX>(a.up, a.up_q, a.up_s, g.expert, (int64_t)I * H), xs, g.nr, x, gut,
                              a.h32, g.begin, [&]() { stage_rows<H>(xs, src, g.nr); });
@@ -989,7 +991,7 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
   __syncthreads();
   if (u == 0 && x == 0) publish_routing(a, s_idx, s_w, s_flags, &P);
   if (u >= plan_ngroups(&P)) return;
-  const PlanGroup g = plan_group(&P, u, a.E);
+  const PlanGroup g = plan_group(&P, u, a.E, a.status);
   const int nr = g.nr < a.R ? g.nr : a.R;  // LDS holds a.R rows
   gateup_tile<H, I, kGuRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.gate, a.gate_q, a.gate_s, g.expert, (int64_t)I * H),
                                     expert_mat<MX>(a.up, a.up_q, a.up_s, g.expert, (int64_t)I * H), xs, nr, x, gut,
@@ -1044,7 +1046,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
       });
     } else {
       if (u >= ng) return;
-      const PlanGroup g = plan_group(P, u, a.E);
+      const PlanGroup g = plan_group(P, u, a.E, a.status);
       const float* src[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;

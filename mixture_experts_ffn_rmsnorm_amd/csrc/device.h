@@ -48,6 +48,20 @@ __device__ __forceinline__ void store_wt(float* p, float v) {
 __device__ __forceinline__ float load_wt(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Checked build (MOE_CHECKED): an index produced by an earlier step of the
+// call is tested where it is used; a failed test sets MOE_FLAG_CHECK in the
+// status word, and the caller clamps the index as the default build does
+// (so nothing reads or writes out of bounds either way).  The default build
+// compiles the tests away.
+__device__ __forceinline__ void check_index(uint32_t* status, bool ok) {
+#ifdef MOE_CHECKED
+  if (!ok) atomicOr(status, (uint32_t)MOE_FLAG_CHECK);
+#else
+  (void)status;
+  (void)ok;
+#endif
+}
+
 // Every store this thread issued has completed.
 __device__ __forceinline__ void sync_stores() { __builtin_amdgcn_s_waitcnt(0); }
 

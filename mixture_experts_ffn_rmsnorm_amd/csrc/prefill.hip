@@ -856,8 +856,13 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
     const int row = (wv * AG + i) * 8 + (lane >> 3);
     const int m = (m0 + row < cntg) ? m0 + row : cntg - 1;
     int64_t r;
-    if (MODE == 0) r = g == E ? (int64_t)m : (int64_t)a.perm[(int64_t)g * R + m];
-    else r = (int64_t)s_rbase[g] + m;
+    if (MODE == 0) {
+      r = g == E ? (int64_t)m : (int64_t)a.perm[(int64_t)g * R + m];
+      check_index(a.status, r >= 0 && r < R);
+      r = r < 0 ? 0 : (r >= R ? R - 1 : r);
+    } else {
+      r = (int64_t)s_rbase[g] + m;
+    }
     return (MODE == 0 ? (const unsigned char*)a.xn16 : (const unsigned char*)a.h16) + r * (KD * 2) +
            (((wv * AG + i) & 1) ? chunk1 : chunk0);
   };
@@ -942,6 +947,8 @@ __global__ __launch_bounds__(Cfg::kGT, 1) void k_gemm(const FwdArgs a) {
           const int rank = a.slot_rank[r * K + k];
           if (e >= 0 && e < E && rank >= 0) {
             pos = s_rbase[e] + rank;
+            check_index(a.status, rank < s_cnt[e] && pos < s_rbase[E]);
+            pos = pos < s_rbase[E] ? pos : s_rbase[E] - 1;
             w = a.wts[r * K + k];
           }
         }

@@ -8,15 +8,18 @@ first use -- there is no fallback.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoeffn.so")
+# the checked build: the same library with bounds tests (MOE_FLAG_CHECK)
+CHECKED_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoeffn_checked.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EOVERFLOW, MOE_EWORKSPACE, MOE_EHIP, MOE_EOVERLAP, MOE_ESCRATCH = range(8)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 LAYER_SCORE, LAYER_HASH = 0, 1
-FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY, FLAG_SYNC_TIMEOUT, FLAG_F16_RANGE = 1, 2, 4, 8
+FLAG_BAD_TOKEN, FLAG_BAD_TABLE_ENTRY, FLAG_SYNC_TIMEOUT, FLAG_F16_RANGE, FLAG_CHECK = 1, 2, 4, 8, 16
 
 # Function names the header declares (checked against the library's exports).
 EXPORTS = ("moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_mxfp8", "moe_ffn_forward_mxfp4",
@@ -67,36 +70,54 @@ def lib() -> ctypes.CDLL:
     """Load the HIP library (once).  Raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -m mixture_experts_ffn_rmsnorm_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
-        L.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(Dims), I64, ctypes.POINTER(SZ)]
-        L.moe_ffn_forward.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, SZ, P]
-        L.moe_ffn_forward_mxfp8.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(MxWeightsC), P, P, SZ,
-                                            P]
-        L.moe_ffn_forward_mxfp4.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(MxWeightsC), P, P, SZ,
-                                            P]
-        L.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P]
-        L.moe_ffn_hc_workspace_bytes.argtypes = [ctypes.POINTER(Dims), I32, I64, ctypes.POINTER(SZ)]
-        L.moe_ffn_forward_hc.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC),
-                                         ctypes.POINTER(HcWeightsC), P, P, SZ, P]
-        L.moe_ffn_hc_view.argtypes = [ctypes.POINTER(Dims), I32, I64, P, SZ] + [ctypes.POINTER(P)] * 4
-        L.moe_route.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, P]
-        L.moe_ffn_routing_view.argtypes = [ctypes.POINTER(Dims), I64, P, SZ, ctypes.POINTER(P), ctypes.POINTER(P),
-                                           ctypes.POINTER(P)]
-        L.moe_ffn_status.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
-        L.moe_strerror.argtypes = [I32]
-        L.moe_strerror.restype = ctypes.c_char_p
-        L.moe_ffn_stage_timing_begin.argtypes = []
-        L.moe_ffn_stage_timing_end.argtypes = [I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
-                                               ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(I32)]
-        for n in EXPORTS:
-            if n != "moe_strerror":
-                getattr(L, n).restype = I32
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Route every call of this module to the library at ``path`` (e.g. the
+    checked build ``CHECKED_LIB_PATH``) inside the ``with`` block."""
+    global _lib
+    prev = _lib
+    _lib = load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def load(path: str) -> ctypes.CDLL:
+    """Load a build of the HIP library and declare its C signatures."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m mixture_experts_ffn_rmsnorm_amd.build`")
+    L = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    L.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(Dims), I64, ctypes.POINTER(SZ)]
+    L.moe_ffn_forward.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, SZ, P]
+    L.moe_ffn_forward_mxfp8.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(MxWeightsC), P, P, SZ,
+                                        P]
+    L.moe_ffn_forward_mxfp4.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(MxWeightsC), P, P, SZ,
+                                        P]
+    L.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P]
+    L.moe_ffn_hc_workspace_bytes.argtypes = [ctypes.POINTER(Dims), I32, I64, ctypes.POINTER(SZ)]
+    L.moe_ffn_forward_hc.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC),
+                                     ctypes.POINTER(HcWeightsC), P, P, SZ, P]
+    L.moe_ffn_hc_view.argtypes = [ctypes.POINTER(Dims), I32, I64, P, SZ] + [ctypes.POINTER(P)] * 4
+    L.moe_route.argtypes = [ctypes.POINTER(Dims), P, P, I64, I32, ctypes.POINTER(WeightsC), P, P, P]
+    L.moe_ffn_routing_view.argtypes = [ctypes.POINTER(Dims), I64, P, SZ, ctypes.POINTER(P), ctypes.POINTER(P),
+                                       ctypes.POINTER(P)]
+    L.moe_ffn_status.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
+    L.moe_strerror.argtypes = [I32]
+    L.moe_strerror.restype = ctypes.c_char_p
+    L.moe_ffn_stage_timing_begin.argtypes = []
+    L.moe_ffn_stage_timing_end.argtypes = [I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(I32)]
+    for n in EXPORTS:
+        if n != "moe_strerror":
+            getattr(L, n).restype = I32
+    return L
 
 
 def strerror(code: int) -> str:

@@ -407,3 +407,15 @@ def test_hc_forward_rejects_on_host():
     assert call(wsb=1024) == moe.MOE_EWORKSPACE
     assert call(ws=FAKE + (8 << 30) + 16) == moe.MOE_EWORKSPACE
     assert call(rows=(1 << 24) + 1) == moe.MOE_EOVERFLOW
+
+
+def test_checked_build_exports_the_same_functions():
+    """The checked build (bounds tests reported through MOE_FLAG_CHECK) is the
+    same C ABI."""
+    syms = []
+    for path in (moe.LIB_PATH, moe.CHECKED_LIB_PATH):
+        nm = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True)
+        syms.append(set(re.findall(r"\b(moe_\w+)\b", nm.stdout)))
+    assert syms[0] == syms[1] and set(moe.EXPORTS) <= syms[1]
+    L = moe.load(moe.CHECKED_LIB_PATH)
+    assert L.moe_strerror(moe.MOE_EINVAL) == moe.lib().moe_strerror(moe.MOE_EINVAL)
