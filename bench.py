@@ -270,8 +270,11 @@ def time_workload(cfg, layers, steps, warmup, graph=False):
     measured = profiling.read_traffic(profiling.profile_key(cfg.name, layers[0][3]))
     if measured and dom in measured:
         roof["traffic"] = measured[dom]
+    launch_bytes = []  # algorithmic bytes of each launch of a step
     for name, k in kernels.items():
         kb, kf = alg_bytes(name, cfg, u_mean, R), alg_flops(name, cfg, R)
+        if kb is not None:
+            launch_bytes += [kb] * max(1, round(k["launches"] / steps))
         secs = k["avg_us"] * 1e-6
         if kb is not None:
             k["hbm_frac"] = kb / secs / 1e9 / HBM_PEAK_GBPS
@@ -287,7 +290,7 @@ def time_workload(cfg, layers, steps, warmup, graph=False):
         "step_alg_bytes": sb, "step_hbm_GBps": sb / step_s / 1e9, "step_hbm_frac": sb / step_s / 1e9 / HBM_PEAK_GBPS,
         "step_alg_flops": sf, "step_TFLOPs": sf / step_s / 1e12,
         "step_mfma_frac": sf / step_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
-        "roofline": roof, "kernels": kernels,
+        "roofline": roof, "kernels": kernels, "launch_bytes": launch_bytes,
     }
     if graph:
         rec["graph"] = graph_chain(dims, cfg, layers, x, tok, ws, steps, ms_per_step)
@@ -365,6 +368,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="distinct weight sets cycled (default 4 decode, 1 prefill)")
     ap.add_argument("--weights", choices=("bf16", "mxfp8", "mxfp4"), default="bf16",
                     help="expert weight format of the named workload (the headline is bf16)")
+    ap.add_argument("--hc", type=int, default=0,
+                    help="also time the named workload wrapped by this many hyper-connection streams (bf16 only)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the headline's oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
@@ -376,6 +381,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if args.hc and (args.weights != "bf16" or not 1 <= args.hc <= 4):
+        print("--hc takes 1 to 4 streams around bf16 expert weights", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -410,6 +418,8 @@ def main():
               "step_mfma_frac", "status_flags", "kernels", "graph"):
         if k in rec:
             res[k] = rec[k]
+    if args.hc:
+        res["hc"] = time_hc(cfg, layers, args.hc, args.steps, args.warmup, rec["ms_per_step"])
     sub_gpu = {}
     if subs:
         res["workloads"] = {}
@@ -448,7 +458,10 @@ def main():
         from mixture_experts_ffn_rmsnorm_amd import device_peaks
 
         log("measuring device ceilings")
-        pk = device_peaks.measure()
+        pk = device_peaks.measure(read_sequence=rec["launch_bytes"])
+        if "read_floor_us" in pk:
+            # the step's event-timed latency against plain reads of its launches' bytes
+            pk["step_latency_over_read_floor"] = rec["latency_us"]["median"] / pk["read_floor_us"]
         roof = res["roofline"]
         top = pk["hbm_read_GBps"] if roof["unit"] == "GB/s" else pk["mfma_f16_TFLOPs"]
         pk["roofline_frac_of_measured"] = roof["achieved"] / top

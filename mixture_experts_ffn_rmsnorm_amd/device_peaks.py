@@ -11,6 +11,15 @@ matrix) that the roofline fractions are taken against.
 
 Each launch is timed with its own pair of HIP events on the current stream,
 after two untimed launches; a ceiling is the best launch.
+
+    read_floor_us    -- (optional) plain reads of a given list of byte
+                        counts, one launch each, back to back on one stream:
+                        the time the same reads take when every launch only
+                        reads (a launch's fixed ramp and tail included), the
+                        floor of a step that makes launches of those sizes.
+                        The windows rotate over the 2 GiB buffer, so no
+                        launch finds its bytes in the last-level cache; the
+                        median of the sequences.
 """
 
 from __future__ import annotations
@@ -58,7 +67,36 @@ def _timed(launch, reps: int) -> float:
     return min(a.elapsed_time(b) for a, b in ev)
 
 
-def measure(read_bytes: int = 2 << 30, reps: int = 10, mfma_iters: int = 8192) -> dict:
+def _read_floor(L, buf, read_bytes, sizes, sink, stream, reps=30):
+    """Median microseconds of plain reads of `sizes` bytes (one launch each,
+    back to back), or None if the windows do not fit the buffer often enough
+    to leave the last-level cache behind."""
+    import torch
+
+    sizes = [int(s) // 4096 * 4096 for s in sizes if s >= 4096]
+    total = sum(sizes)
+    nwin = read_bytes // total if total else 0
+    if nwin < 2 or nwin * total < (1 << 30):
+        return None
+    base = buf.data_ptr()
+    ev = []
+    for rep in range(reps + 2):
+        o = base + (rep % nwin) * total
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in sizes:
+            rc = L.moe_peaks_read(ctypes.c_void_p(o), s, ctypes.c_void_p(sink.data_ptr()), 2048, stream)
+            if rc != 0:
+                raise RuntimeError(f"moe_peaks_read: hip error {rc}")
+            o += s
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev[2:])
+    return us[len(us) // 2]
+
+
+def measure(read_bytes: int = 2 << 30, reps: int = 10, mfma_iters: int = 8192, read_sequence=None) -> dict:
     import torch
 
     L = lib()
@@ -84,10 +122,15 @@ def measure(read_bytes: int = 2 << 30, reps: int = 10, mfma_iters: int = 8192) -
 
     ms_read = _timed(read, reps)
     ms_mfma = _timed(mfma, reps)
+    floor = _read_floor(L, buf, read_bytes, read_sequence, sink, stream) if read_sequence else None
     waves = mblocks * L.moe_peaks_mfma_threads() // 64
     flops = waves * mfma_iters * L.moe_peaks_mfma_chains() * MFMA_FLOPS
     del buf
+    out = {}
+    if floor is not None:
+        out = {"read_floor_us": floor, "read_floor_launch_bytes": [int(b) for b in read_sequence]}
     return {
+        **out,
         "hbm_read_GBps": read_bytes / (ms_read * 1e-3) / 1e9,
         "mfma_f16_TFLOPs": flops / (ms_mfma * 1e-3) / 1e12,
         "compute_units": cus,

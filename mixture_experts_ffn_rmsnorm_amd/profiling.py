@@ -129,22 +129,29 @@ def _run(cmd, log):
     return rc, open(log + ".stdout").read()
 
 
-def _bench_cmd(workload, extra, weights="bf16"):
+def _bench_cmd(workload, extra, weights="bf16", hc=0):
     return ([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--only", "--weights", weights]
-            + list(extra))
+            + (["--hc", str(hc)] if hc else []) + list(extra))
 
 
-def profile_key(workload: str, weights: str = "bf16") -> str:
-    """File-name key of a workload's summaries: MXFP8 runs get "-mxfp8"."""
-    return workload if weights == "bf16" else f"{workload}-{weights}"
+def profile_key(workload: str, weights: str = "bf16", hc: int = 0) -> str:
+    """File-name key of a workload's summaries: block-scaled weights add
+    "-mxfp8" / "-mxfp4", the wrapped layer "-hc<streams>"."""
+    key = workload if weights == "bf16" else f"{workload}-{weights}"
+    return key + (f"-hc{hc}" if hc else "")
+
+
+def _opts(args) -> str:
+    """The format and wrapper options of a command line, as typed."""
+    return ("" if args.weights == "bf16" else f" --weights {args.weights}") + (f" --hc {args.hc}" if args.hc else "")
 
 
 def cmd_stats(args, extra):
-    key = profile_key(args.workload, args.weights)
+    key = profile_key(args.workload, args.weights, args.hc)
     out_dir = os.path.join(args.scratch, f"stats_{key}")
     os.makedirs(out_dir, exist_ok=True)
     prof = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d", out_dir, "-o", "run", "--"]
-    bench = _bench_cmd(args.workload, extra, args.weights)
+    bench = _bench_cmd(args.workload, extra, args.weights, args.hc)
     rc, stdout = _run(prof + bench, os.path.join(out_dir, "log.txt"))
     json_line = next((l for l in stdout.splitlines() if l.startswith("{")), None)
     if rc != 0 and json_line is None:
@@ -161,18 +168,17 @@ def cmd_stats(args, extra):
         rows.append((short_name(row["Name"]), launch_name(row["Name"]), int(row["Calls"]),
                      float(row["AverageNs"]) / 1e3, float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
     rows.sort(key=lambda t: -t[2] * t[3])
-    cmdline = "python3 -m mixture_experts_ffn_rmsnorm_amd.profiling stats --workload " + args.workload
-    if args.weights != "bf16":
-        cmdline += " --weights " + args.weights
+    cmdline = "python3 -m mixture_experts_ffn_rmsnorm_amd.profiling stats --workload " + args.workload + _opts(args)
     if extra:
         cmdline += " -- " + " ".join(shlex.quote(e) for e in extra)
     path = os.path.join(OUTDIR, f"kernels-{key}.md")
     with open(path, "w") as f:
-        f.write(f"# Kernel durations, workload {args.workload}, {args.weights} expert weights\n\n")
+        f.write(f"# Kernel durations, workload {args.workload}, {args.weights} expert weights"
+                + (f", wrapped by {args.hc} hyper-connection streams" if args.hc else "") + "\n\n")
         f.write("Command (from the repository root, on one MI355X):\n\n")
         f.write(f"    {cmdline}\n\nwhich runs\n\n    rocprofv3 --kernel-trace --stats --output-format csv "
                 f"-d <scratch> -o run -- python3 bench.py --workload {args.workload} --only --weights {args.weights}"
-                + ("" if not extra else " " + " ".join(extra)) + "\n\n")
+                + (f" --hc {args.hc}" if args.hc else "") + ("" if not extra else " " + " ".join(extra)) + "\n\n")
         f.write(f"Kernel sources digest: `{sources_digest()}`\n\n")
         f.write("rocprofv3 kernel statistics for this library's kernels (every call of the run: warm-up, "
                 "timed steps and the per-kernel event pass):\n\n")
@@ -213,9 +219,9 @@ def _pmc_pass(counter, cmd, out_dir, include=None):
 
 def cmd_traffic(args, extra):
     copy_cmd = [sys.executable, "-m", "mixture_experts_ffn_rmsnorm_amd.profiling", "child-copy"]
-    key = profile_key(args.workload, args.weights)
+    key = profile_key(args.workload, args.weights, args.hc)
     bench_args = ["--steps", "5", "--warmup", "2", "--layers", "1", "--no-cpu-baseline", "--no-peaks"]
-    bench = _bench_cmd(args.workload, bench_args, args.weights)
+    bench = _bench_cmd(args.workload, bench_args, args.weights, args.hc)
     res = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         copy = _pmc_pass(counter, copy_cmd, os.path.join(args.scratch, f"copy_{counter}"))
@@ -227,16 +233,17 @@ def cmd_traffic(args, extra):
     ffac, wfac = COPY_BYTES / (cf * 1024.0), COPY_BYTES / (cw * 1024.0)
     names = sorted(set(res["FETCH_SIZE"][1]) | set(res["WRITE_SIZE"][1]))
     path = os.path.join(OUTDIR, f"traffic-{key}.txt")
-    wopt = "" if args.weights == "bf16" else f" --weights {args.weights}"
+    wopt = _opts(args)
     with open(path, "w") as f:
         f.write(f"# HBM traffic per dispatch, workload {args.workload}, {args.weights} expert weights, "
-                "from rocprofv3 counters\n")
+                + (f"wrapped by {args.hc} hyper-connection streams, " if args.hc else "")
+                + "from rocprofv3 counters\n")
         f.write(f"# command: python3 -m mixture_experts_ffn_rmsnorm_amd.profiling traffic --workload {args.workload}"
                 f"{wopt}\n")
         f.write(f"# passes: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, with --kernel-include-regex "
                 f"'{KERNEL_REGEX}', each over\n")
         f.write(f"#   python3 bench.py --workload {args.workload} --only --weights {args.weights} "
-                + " ".join(bench_args) + "\n")
+                + (f"--hc {args.hc} " if args.hc else "") + " ".join(bench_args) + "\n")
         f.write("#   and over a 1 GiB device-to-device copy (calibration: factor = bytes / counter bytes)\n")
         f.write(f"sources_sha256: {sources_digest()}\n")
         f.write(f"copy_kernel: {short_name(cf_name)}\n")
@@ -292,6 +299,7 @@ def main():
     ap.add_argument("what", choices=["stats", "traffic"])
     ap.add_argument("--workload", default="decode-r1-score")
     ap.add_argument("--weights", choices=["bf16", "mxfp8", "mxfp4"], default="bf16")
+    ap.add_argument("--hc", type=int, default=0, help="profile the layer wrapped by this many streams")
     ap.add_argument("--scratch", default="/tmp/moe_prof")
     ap.add_argument("--outdir", default=PROFILES, help="directory for the summaries (default profiles/)")
     argv = sys.argv[1:]

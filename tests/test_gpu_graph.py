@@ -70,34 +70,37 @@ def test_graph_prefill_score(full):
     _replay_matches_eager(full, 300, ref.LAYER_SCORE, seeds=(21, 22, 23))
 
 
-def _two_layer_chain_on_one_workspace(lay0, lay1, rows, kind, seeds, rel, maxabs):
-    """Layers 0 and 1 chained (layer 1 reads layer 0's output) and captured
-    once in one graph, both calls on ONE workspace; replayed with new x and
+def _chain_on_one_workspace(lays, rows, kind, seeds, rel, maxabs):
+    """The layers chained (layer l+1 reads layer l's output) and captured
+    once in one graph, every call on ONE workspace; replayed with new x and
     token ids each time, with an eager call of the same row count on the
-    same workspace between replays.  Each replay's two outputs are checked
-    against the oracle (layer 1 against the oracle fed the GPU's layer-0
-    output), and bitwise against eager calls on fresh workspaces."""
+    same workspace between replays.  Each replay's outputs are checked
+    against the oracle layer by layer (layer l+1 against the oracle fed the
+    GPU's layer-l output), and bitwise against eager calls on fresh
+    workspaces."""
     import torch
 
     from tests.gpu_common import check_output
 
-    cfg = lay0.cfg
-    H, K = cfg.hidden, cfg.top_k
+    cfg = lays[0].cfg
+    H, K, L = cfg.hidden, cfg.top_k, len(lays)
     x = torch.empty((rows, H), dtype=torch.float32, device="cuda")
-    mid, out = torch.empty_like(x), torch.empty_like(x)
+    outs = [torch.empty_like(x) for _ in lays]
     tok = torch.zeros(rows, dtype=torch.int32, device="cuda")
-    ws = moe.alloc_workspace(lay0.dims, rows)
+    ws = moe.alloc_workspace(lays[0].dims, rows)
     x2, out2 = torch.empty_like(x), torch.empty_like(x)
 
     def chain():
-        moe.forward(lay0.dims, x, tok, kind, lay0.cw, mid, ws)
-        moe.forward(lay1.dims, mid, tok, kind, lay1.cw, out, ws)
+        src = x
+        for lay, dst in zip(lays, outs):
+            moe.forward(lay.dims, src, tok, kind, lay.cw, dst, ws)
+            src = dst
 
     rng = np.random.default_rng(seeds[0])
 
     def fill(dst_x):
         v = rng.standard_normal((rows, H)).astype(np.float32)
-        t = rng.integers(0, cfg.table_rows, rows).astype(np.int32)
+        t = rng.integers(0, max(cfg.table_rows, 1), rows).astype(np.int32)  # unused by score layers
         dst_x.copy_(torch.from_numpy(v))
         tok.copy_(torch.from_numpy(t))
         return v, t
@@ -114,27 +117,30 @@ def _two_layer_chain_on_one_workspace(lay0, lay1, rows, kind, seeds, rel, maxabs
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got_mid, got_out = mid.cpu().numpy(), out.cpu().numpy()
+        got = [o.cpu().numpy() for o in outs]
         assert moe.status(ws) == 0
         # the oracle, layer by layer
-        want_mid = ref.forward(xv, tv, kind, lay0.oracle_w, K, cfg.eps)["out"]
-        check_output(got_mid, want_mid, rel, maxabs, what=f"replay {i} layer 0")
-        want_out = ref.forward(got_mid, tv, kind, lay1.oracle_w, K, cfg.eps)["out"]
-        check_output(got_out, want_out, rel, maxabs, what=f"replay {i} layer 1")
+        src = xv
+        for l, lay in enumerate(lays):
+            want = ref.forward(src, tv, kind, lay.oracle_w, K, cfg.eps)["out"]
+            check_output(got[l], want, rel, maxabs, what=f"replay {i} layer {l}")
+            src = got[l]
         # bitwise against eager calls on fresh workspaces
-        e_mid, e_out = torch.empty_like(x), torch.empty_like(x)
-        moe.forward(lay0.dims, x, tok, kind, lay0.cw, e_mid, moe.alloc_workspace(lay0.dims, rows))
-        moe.forward(lay1.dims, e_mid, tok, kind, lay1.cw, e_out, moe.alloc_workspace(lay1.dims, rows))
-        torch.cuda.synchronize()
-        assert np.array_equal(e_mid.cpu().numpy(), got_mid) and np.array_equal(e_out.cpu().numpy(), got_out), \
-            f"replay {i}: differs from eager calls on fresh workspaces"
+        src = x
+        for l, lay in enumerate(lays):
+            e = torch.empty_like(x)
+            moe.forward(lay.dims, src, tok, kind, lay.cw, e, moe.alloc_workspace(lay.dims, rows))
+            torch.cuda.synchronize()
+            assert np.array_equal(e.cpu().numpy(), got[l]), \
+                f"replay {i} layer {l}: differs from eager calls on fresh workspaces"
+            src = e
         # an eager call on the shared workspace between replays
         x2v, t2v = xv[::-1].copy(), tv[::-1].copy()
         x2.copy_(torch.from_numpy(x2v))
         tok.copy_(torch.from_numpy(t2v))
-        moe.forward(lay1.dims, x2, tok, kind, lay1.cw, out2, ws)
+        moe.forward(lays[-1].dims, x2, tok, kind, lays[-1].cw, out2, ws)
         torch.cuda.synchronize()
-        want2 = ref.forward(x2v, t2v, kind, lay1.oracle_w, K, cfg.eps)["out"]
+        want2 = ref.forward(x2v, t2v, kind, lays[-1].oracle_w, K, cfg.eps)["out"]
         check_output(out2.cpu().numpy(), want2, rel, maxabs, what=f"eager call after replay {i}")
 
 
@@ -142,7 +148,7 @@ def test_graph_two_layers_one_workspace_tiny():
     cfg = gen.config(0)
     lay0, lay1 = Layer(cfg, layer=0), Layer(cfg, layer=1)
     for rows in (2, 4):
-        _two_layer_chain_on_one_workspace(lay0, lay1, rows, ref.LAYER_HASH, (61, 62, 63, 64), 1e-5, 5e-5)
+        _chain_on_one_workspace([lay0, lay1], rows, ref.LAYER_HASH, (61, 62, 63, 64), 1e-5, 5e-5)
 
 
 def test_graph_two_layers_one_workspace_full(full):
@@ -151,4 +157,23 @@ def test_graph_two_layers_one_workspace_full(full):
     cfg = gen.config(2)
     lay0 = Layer(cfg, share=full)
     lay1 = Layer(cfg, layer=1)
-    _two_layer_chain_on_one_workspace(lay0, lay1, 4, ref.LAYER_HASH, (71, 72, 73), 1e-5, 5e-5)
+    _chain_on_one_workspace([lay0, lay1], 4, ref.LAYER_HASH, (71, 72, 73), 1e-5, 5e-5)
+
+
+def test_graph_decode_four_layer_chain_one_row_full(full):
+    """The one-row decode pipeline: four consecutive score layers with
+    distinct weights, one workspace, one graph -- the pattern of a model's
+    decode step over its layers."""
+    cfg = gen.config(1)
+    lays = [full] + [Layer(cfg, layer=l) for l in (1, 2, 3)]
+    _chain_on_one_workspace(lays, 1, ref.LAYER_SCORE, (81, 82), 1e-5, 5e-5)
+
+
+def test_graph_decode_three_layer_chain_tiny_all_row_counts():
+    """Chains of three tiny score layers at every decode row count: one row
+    (the one-row path) and two to four (the counted-in routing), each chain
+    on one workspace."""
+    cfg = gen.config(0)
+    lays = [Layer(cfg, layer=l) for l in (0, 1, 2)]
+    for rows in (1, 2, 3, 4):
+        _chain_on_one_workspace(lays, rows, ref.LAYER_SCORE, (90 + rows, 95 + rows), 1e-5, 5e-5)
