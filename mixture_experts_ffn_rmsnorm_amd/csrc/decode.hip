@@ -256,6 +256,12 @@ __device__ __forceinline__ void norm_rows_to_lds(const FwdArgs& a, bool store_x,
   constexpr int V = H / 4;                            // float4 per row
   constexpr int NPT = (V + kThreads - 1) / kThreads;  // float4 per thread and row
   float4 v[kDecodeMaxRows][NPT];
+  float4 gg[NPT];  // the norm weight, requested with the rows
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    const int i = t + k * kThreads;
+    gg[k] = i < V ? ((const float4*)g)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   if (a.hc > 0) {
     const int hc = a.hc, mw = (2 + hc) * hc;
     float p[kDecodeMaxRows][kHcMax];
@@ -318,13 +324,12 @@ __device__ __forceinline__ void norm_rows_to_lds(const FwdArgs& a, bool store_x,
   for (int k = 0; k < NPT; ++k) {
     const int i = t + k * kThreads;
     if (i < V) {
-      const float4 gg = ((const float4*)g)[i];
 #pragma unroll
       for (int r = 0; r < kDecodeMaxRows; ++r) {
         if (r < R) {
           float4 o;
-          o.x = v[r][k].x * rs[r] * gg.x; o.y = v[r][k].y * rs[r] * gg.y;
-          o.z = v[r][k].z * rs[r] * gg.z; o.w = v[r][k].w * rs[r] * gg.w;
+          o.x = v[r][k].x * rs[r] * gg[k].x; o.y = v[r][k].y * rs[r] * gg[k].y;
+          o.z = v[r][k].z * rs[r] * gg[k].z; o.w = v[r][k].w * rs[r] * gg[k].w;
           ((float4*)(xs + r * H))[i] = o;
         }
       }
@@ -484,6 +489,39 @@ __device__ __forceinline__ void build_plan(const int* s_idx, const float* s_w, c
     P->ngroups = ngroups;
     P->nentries = nentries;
     P->group_begin[ngroups] = nentries;
+  }
+}
+
+// The plan of one row, in slot order: group g is the g-th valid slot (its
+// expert, one entry for row 0 with the slot's weight).  Two slots that name
+// one expert (only from a malformed hash table) stay two groups, each adding
+// its weight times that expert's output -- the sum over slots as defined.
+// A handful of wave-wide operations on wave 0 (lane k = slot k), no loops:
+// the routed gate/up blocks run it before their streams start.
+__device__ __forceinline__ void build_plan_one_row(const int* s_idx, const float* s_w, const unsigned char* s_valid,
+                                                   int K, int E, DecodePlan* P) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int e = -1;
+  float w = 0.f;
+  bool v = false;
+  if (lane < K) {
+    e = s_idx[lane];
+    w = s_w[lane];
+    v = s_valid[lane] && e >= 0 && e < E;
+  }
+  const uint64_t vm = __ballot(v);
+  const int gidx = __popcll(vm & ((1ull << lane) - 1ull));
+  const int n = __popcll(vm);
+  if (v) {
+    P->group_expert[gidx] = e;
+    P->group_begin[gidx] = gidx;
+    P->entry_row[gidx] = 0;
+    P->entry_w[gidx] = w;
+  }
+  if (lane == 0) {
+    P->ngroups = n;
+    P->nentries = n;
+    P->group_begin[n] = n;
   }
 }
 
@@ -856,6 +894,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   constexpr int NCH = (H + 511) / 512;
   const bool full = H % 512 == 0 || lane * 8 < H % 512;
   uint4 q[NCH];
+  // one row: the expert's selection bias, requested with its router row
+  const float bias_e = (kRouterOnly && e < E && lane == 0 && a.layer_kind != MOE_LAYER_HASH) ? a.bias[e] : 0.f;
   if (e < E) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
@@ -891,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
           if (kRouterOnly) {  // one row: what the gate/up blocks' routing needs of this expert
             a.logits[e] = v;
             sy->route_sig[e] = sigmoid_f64(v);
-            sy->route_key[e] = a.layer_kind == MOE_LAYER_HASH ? 0ull : ordered_key(score_key(v, a.bias[e]));
+            sy->route_key[e] = a.layer_kind == MOE_LAYER_HASH ? 0ull : ordered_key(score_key(v, bias_e));
           } else {
             store_wt(&a.logits[(int64_t)r * E + e], v);
           }
@@ -959,7 +999,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
 // has written the logits, each expert's selection key and sigmoid, and xn.
 // A routed block routes the row itself -- wave 0 reads the keys and
 // sigmoids and picks the slots with the head plan block's selection, then
-// builds the plan in LDS -- and streams the rows of the plan's u-th expert;
+// builds the slot-order plan in LDS -- and streams the rows of the plan's
+// u-th expert;
 // the u = 0, x = 0 block also publishes the routing and the plan.  No block waits for another: with one row the routing is a few
 // microseconds of work that every block repeats, against the
 // cross-workgroup round trips of a shared plan.  At full size this is 256 +
@@ -987,7 +1028,7 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
   const int u = (b - nsh) / gut, x = (b - nsh) % gut;
   route_one_row(a, s_idx, s_w, s_valid, s_flags);  // wave 0 (the row)
   __syncthreads();
-  if (threadIdx.x < kWave) build_plan(s_idx, s_w, s_valid, 1, a.K, a.E, &P);
+  if (threadIdx.x < kWave) build_plan_one_row(s_idx, s_w, s_valid, a.K, a.E, &P);
   __syncthreads();
   if (u == 0 && x == 0) publish_routing(a, s_idx, s_w, s_flags, &P);
   if (u >= plan_ngroups(&P)) return;
@@ -1009,7 +1050,8 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
 // tile_cnt[x].  The block that completes the count (every routed group of
 // the tile, and both shared halves, have written) forms, for those 32
 // columns, out[r] = sum over r's (expert, row) pairs in plan order (experts
-// ascending) of weight * down, then + shared down -- a fixed order, so the
+// ascending; slot order for one row) of weight * down, then + shared down --
+// a fixed order, so the
 // output is bitwise reproducible.  No block waits for another.  Without
 // kShared and with no valid routed expert at all, the u = 0 blocks write
 // out = shared down.
