@@ -442,6 +442,7 @@ int moe_ffn_forward_hc(const moe_dims_t* d, const float* state_in, const int32_t
   a.iters = hw->sinkhorn_iters;
   a.eps = d->eps;
   a.slices = L.slices;
+  a.slice_k = (int)L.slice_k;
   a.state = state_in;
   a.fn = hw->hc_fn;
   a.scale = hw->hc_scale;

@@ -7,9 +7,11 @@
 // input (dispatch_hc_pre); after it, dispatch_hc_post builds the new state.
 // The split, pre and post arithmetic is the reading stated in moe_ffn.h.
 //
-//   k_hc_mix   one block per (row tile, slice of kHcSlice flattened inputs):
+//   k_hc_mix   one block per (row tile, slice of slice_k flattened inputs):
 //              the slice's dot products with every hc_fn row and its sum of
-//              squares; with 1-4 rows (one tile) the block that completes
+//              squares, each thread adding its 4-input pieces of the slice
+//              in order before the wave-wide sums; with 1-4 rows (one tile,
+//              slices of 1024 inputs) the block that completes
 //              the arrival count adds the slices and splits every row (the
 //              decode launches then form the FFN input from the streams)
 //   k_hc_pre   per (row, hidden chunk): the row's slices added in order,
@@ -87,14 +89,16 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
   const int64_t r0 = (int64_t)tile * kHcRows;
   const int nr = a.R - r0 < kHcRows ? (int)(a.R - r0) : kHcRows;
   const int K = HC * a.H;
-  const int k = sl * kHcSlice + 4 * t;
+  const int kend = (sl + 1) * a.slice_k < K ? (sl + 1) * a.slice_k : K;
 
   float acc[kHcRows][V];
 #pragma unroll
   for (int r = 0; r < kHcRows; ++r)
 #pragma unroll
     for (int m = 0; m < V; ++m) acc[r][m] = 0.f;
-  if (k < K) {  // K is a multiple of 4
+  // the thread's pieces k, k + 4 * threads, ... of the slice, in order
+#pragma unroll 1
+  for (int k = sl * a.slice_k + 4 * t; k < kend; k += 4 * kHcThreads) {  // K is a multiple of 4
     float w[MW][4];
 #pragma unroll
     for (int m = 0; m < MW; ++m) {
@@ -105,21 +109,24 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
     for (int r = 0; r < kHcRows; ++r) {
       if (r < nr) {
         const float4 s = *(const float4*)(a.state + (r0 + r) * K + k);
-        acc[r][MW] = fmaf(s.x, s.x, fmaf(s.y, s.y, fmaf(s.z, s.z, s.w * s.w)));
+        acc[r][MW] = fmaf(s.x, s.x, fmaf(s.y, s.y, fmaf(s.z, s.z, fmaf(s.w, s.w, acc[r][MW]))));
 #pragma unroll
-        for (int m = 0; m < MW; ++m) acc[r][m] = fmaf(s.x, w[m][0], fmaf(s.y, w[m][1], fmaf(s.z, w[m][2], s.w * w[m][3])));
+        for (int m = 0; m < MW; ++m)
+          acc[r][m] = fmaf(s.x, w[m][0], fmaf(s.y, w[m][1], fmaf(s.z, w[m][2], fmaf(s.w, w[m][3], acc[r][m]))));
       }
     }
   }
-  // block sums: each wave, then the waves in order
-  __shared__ float s_part[kHcWaves][kHcRows * V];
+  // block sums: each 16-lane row of each wave by DPP moves (no lane reads),
+  // then the block's rows in order
+  constexpr int kRows16 = kHcWaves * (kWave / 16);
+  __shared__ float s_part[kRows16][kHcRows * V];
 #pragma unroll
   for (int r = 0; r < kHcRows; ++r) {
     if (r < nr) {  // block-uniform
 #pragma unroll
       for (int m = 0; m < V; ++m) {
-        const float v = wave_sum(acc[r][m]);
-        if (lane == 0) s_part[wv][r * V + m] = v;
+        const float v = row16_sum(acc[r][m]);
+        if ((lane & 15) == 0) s_part[wv * (kWave / 16) + lane / 16][r * V + m] = v;
       }
     }
   }
@@ -128,7 +135,7 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
   for (int q = t; q < nr * V; q += kHcThreads) {
     float v = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kHcWaves; ++w2) v += s_part[w2][q];
+    for (int w2 = 0; w2 < kRows16; ++w2) v += s_part[w2][q];
     store_wt(&part[q], v);  // read by the last block below (1-4 rows) or the next launch
   }
   if (!a.cnt) return;

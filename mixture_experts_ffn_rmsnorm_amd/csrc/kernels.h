@@ -81,6 +81,7 @@ struct HcArgs {
   int R, H, hc, iters;
   float eps;
   int64_t slices;
+  int slice_k;           // flattened inputs per slice (a multiple of 4 * threads)
   const float* state;    // [R][hc][H]
   const uint16_t* fn;    // bf16 [(2+hc)*hc][hc*H]
   const float* scale;    // [3]

@@ -123,15 +123,20 @@ inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
 
 // Hyper-connection wrapper (moe_ffn_forward_hc): the FFN's layout at offset
 // 0, then the wrapper's intermediates.  The mix launch works on tiles of
-// kHcRows rows x kHcSlice flattened inputs and leaves one partial sum per
-// tile and slice; the next launch adds them.
+// kHcRows rows x slice_k flattened inputs and leaves one partial sum per
+// tile and slice; the next launch adds them.  One tile (1-4 rows, a
+// latency-bound call) takes slices of kHcSlice inputs, one block each; more
+// tiles take fewer, wider slices -- as few as keep about kHcMixBlocks
+// blocks in the launch -- so that a thread adds more products between
+// wave-wide sums.
 constexpr int kHcMax = 4;       // streams
 constexpr int kHcRows = 4;      // rows per mix tile
 static_assert(kHcRows == kDecodeMaxRows, "a decode call is one mix tile");
-constexpr int kHcSlice = 1024;  // flattened state values per mix block
+constexpr int kHcSlice = 1024;  // flattened state values per mix block and pass (256 threads x 4)
+constexpr int kHcMixBlocks = 512;
 struct HcLayout {
   Layout ffn;
-  int64_t tiles, slices;
+  int64_t tiles, slices, slice_k;  // slice_k: flattened inputs per slice, a multiple of kHcSlice
   size_t mixes;    // f32 [R][(2+hc)*hc]
   size_t maps;     // f32 [R][(2+hc)*hc]  pre | post | comb (output stream, input stream)
   size_t ffn_in;   // f32 [R][H]
@@ -146,7 +151,11 @@ inline bool make_hc_layout(int64_t R, int H, int E, int K, int I, int hc, HcLayo
   const unsigned __int128 r = (unsigned __int128)R;
   const int mw = (2 + hc) * hc;
   L->tiles = (R + kHcRows - 1) / kHcRows;
-  L->slices = ((int64_t)hc * H + kHcSlice - 1) / kHcSlice;
+  const int64_t passes = ((int64_t)hc * H + kHcSlice - 1) / kHcSlice;  // kHcSlice-wide pieces of a row
+  int64_t want = L->tiles > 1 ? (kHcMixBlocks + L->tiles - 1) / L->tiles : passes;
+  want = want < 1 ? 1 : (want > passes ? passes : want);
+  L->slice_k = (passes + want - 1) / want * kHcSlice;
+  L->slices = ((int64_t)hc * H + L->slice_k - 1) / L->slice_k;
   unsigned __int128 off = L->ffn.total;
   auto take = [&](unsigned __int128 bytes) -> size_t {
     off = (off + 255) / 256 * 256;
