@@ -119,8 +119,11 @@ __device__ __forceinline__ uint32_t load_stream4(const void* p) { return __built
 // of a partial chunk (LEN not a multiple of 512) neither load nor add.  With
 // MX the row's scale bytes come with one 4-byte load per lane, and chunk c's
 // lane takes the scale of its 32-column block from the lane holding it
-// (columns c*512 + 8l.. lie in block 16c + l/4); the lane's 8-term partial
-// of the chunk is multiplied by it (a power of two: exact) and added.
+// (columns c*512 + 8l.. lie in block 16c + l/4, in scale dword 4c + r for
+// the lanes of 16-lane row r = l/16): lane 16r + p loads scale dword 4p + r,
+// so the dword a row needs for chunk c sits in its own lane c, broadcast
+// within the row by a DPP move; the lane's 8-term partial of the chunk is
+// multiplied by the scale (a power of two: exact) and added.
 // rowsrc(j) gives row j (WRow); pre() runs once after the first NBUF rows
 // are requested (staging the activations there overlaps it with the first
 // weight fetch; it must end with a barrier if it fills LDS); sink(j, part)
@@ -141,7 +144,9 @@ __device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const floa
   const bool full = LEN % 512 == 0 || lane * 8 < LEN % 512;  // active in the last chunk
   using Chunk = typename std::conditional<MX == 2, uint32_t, typename std::conditional<MX == 1, uint2, uint4>::type>::type;
   Chunk q[NBUF][NCH];
-  uint32_t sw[NBUF];  // MX: this lane's 4 scale bytes of the row
+  uint32_t sw[NBUF];  // MX: this lane's 4 scale bytes of the row (dword sdw)
+  static_assert(!MX || NCH <= 16, "one scale dword per lane of a 16-lane row and chunk");
+  const int sdw = 4 * (lane & 15) + (lane >> 4);
   auto load_row = [&](int b, int j) {
     const WRow src = rowsrc(j);
     if constexpr (MX == 2) {  // 4-bit codes: 4 bytes per lane and chunk
@@ -149,13 +154,13 @@ __device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const floa
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
         if (c < NCH - 1 || full) q[b][c] = load_stream4(p + c * 256);
-      sw[b] = lane * 4 < LEN / 32 ? *(const uint32_t*)(src.s + lane * 4) : 0u;
+      sw[b] = sdw * 4 < LEN / 32 ? *(const uint32_t*)(src.s + sdw * 4) : 0u;
     } else if constexpr (MX) {
       const uint8_t* p = (const uint8_t*)src.w + lane * 8;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
         if (c < NCH - 1 || full) q[b][c] = load_stream8(p + c * 512);
-      sw[b] = lane * 4 < LEN / 32 ? *(const uint32_t*)(src.s + lane * 4) : 0u;
+      sw[b] = sdw * 4 < LEN / 32 ? *(const uint32_t*)(src.s + sdw * 4) : 0u;
     } else {
       const uint16_t* p = (const uint16_t*)src.w + lane * 8;
 #pragma unroll
@@ -176,8 +181,8 @@ __device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const floa
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         sc[i] = 1.f;
-        if constexpr (MX) {  // every lane takes part in the shuffle
-          const uint32_t w = (uint32_t)__shfl((int)sw[b + i], c * 4 + (lane >> 4), kWave);
+        if constexpr (MX) {  // every lane takes part in the broadcast
+          const uint32_t w = row_bcast(sw[b + i], c);
           sc[i] = e8m0_f32((w >> (8 * ((lane >> 2) & 3))) & 255u);
         }
       }

@@ -73,6 +73,19 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
+// Lane c (0..15) of each 16-lane row, in every lane of that row (DPP
+// row_newbcast:c).  c must fold to a constant (an unrolled loop index).
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v, int c) {
+#define MOE_ROW_BCAST(n) \
+  case n: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + n, 0xF, 0xF, false);
+  switch (c) {
+    MOE_ROW_BCAST(0) MOE_ROW_BCAST(1) MOE_ROW_BCAST(2) MOE_ROW_BCAST(3) MOE_ROW_BCAST(4) MOE_ROW_BCAST(5)
+    MOE_ROW_BCAST(6) MOE_ROW_BCAST(7) MOE_ROW_BCAST(8) MOE_ROW_BCAST(9) MOE_ROW_BCAST(10) MOE_ROW_BCAST(11)
+    MOE_ROW_BCAST(12) MOE_ROW_BCAST(13) MOE_ROW_BCAST(14) default: break;
+  }
+#undef MOE_ROW_BCAST
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x15F, 0xF, 0xF, false);
+}
 // Sum over the 16 lanes of each row, in every lane of the row: after the
 // two quad swaps every lane holds its quad's sum, the half mirror adds the
 // other quad of its 8, the mirror the other 8 of its row.
