@@ -103,6 +103,32 @@ def test_tiny_duplicate_table_entries(tiny):
         check_forward(lay, x, tok, HASH, out, lg, idx, w)
 
 
+def _one_row_table_edge_cases(lay, x):
+    """One row through the one-row path (routing inside the routed gate/up
+    blocks, plan in slot order): a table row with two bad entries (the valid
+    slots compact into four groups), a row that names one expert three
+    times (each slot its own group, adding its own weight), and a token id
+    past the table."""
+    cfg = lay.cfg
+    table = lay.host.tid2eid.copy()
+    table[17, 2] = cfg.experts + 5
+    table[17, 4] = -1
+    table[5] = [3, 3, 7, 3, 9, 11]
+    lay.with_table(table)
+    for t, flags in ((17, moe.FLAG_BAD_TABLE_ENTRY), (5, 0), (cfg.table_rows, moe.FLAG_BAD_TOKEN)):
+        tok = np.array([t], dtype=np.int32)
+        out, lg, idx, w, st = lay.run(x, tok, HASH)
+        assert st == flags, f"token {t}: status {st:#x}, want {flags:#x}"
+        if t == 17:
+            assert idx[0, 2] == cfg.experts + 5 and idx[0, 4] == -1 and w[0, 2] == 0 and w[0, 4] == 0
+        check_forward(lay, x, tok, HASH, out, lg, idx, w)
+
+
+def test_tiny_one_row_table_edge_cases():
+    cfg = gen.config(0)
+    _one_row_table_edge_cases(Layer(cfg), _x(cfg, 1, seed=15))
+
+
 def test_tiny_hash_equals_score(tiny):
     cfg = tiny.cfg
     rows = 16
@@ -396,6 +422,11 @@ def test_full_decode_one_row_hash(full):
     out, lg, idx, w, st = lay.run(x, tok_bad, HASH)
     assert st == moe.FLAG_BAD_TOKEN and (idx == -1).all() and (w == 0).all()
     check_forward(lay, x, tok_bad, HASH, out, lg, idx, w)
+
+
+def test_full_decode_one_row_table_edge_cases(full):
+    cfg = gen.config(2)
+    _one_row_table_edge_cases(Layer(cfg, share=full), _x(cfg, 1, seed=93))
 
 
 def test_full_prefill_hash(full):
