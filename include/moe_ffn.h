@@ -330,7 +330,8 @@ int moe_ffn_hc_workspace_bytes(const moe_dims_t* d, int32_t hc, int64_t rows, si
  *              moe_ffn_forward, whose intermediates it holds)
  * Launches on `stream`: the mixes' partial sums, the split with the FFN
  * input, moe_ffn_forward on it (same precision, routing and status), the
- * new state.  The wrapper's arithmetic is f32, sums in a fixed order; the
+ * new state; with 1 to 4 rows the split, the FFN input and the new state
+ * are formed inside moe_ffn_forward's own launches.  The wrapper's arithmetic is f32, sums in a fixed order; the
  * result is bitwise reproducible.
  * Errors: those of moe_ffn_forward; MOE_EINVAL also for a missing or
  * misaligned hc array or a round count outside 1..MOE_HC_MAX_ITERS,

@@ -176,11 +176,18 @@ int check_forward_args(const moe_dims_t* d, const float* x, const int32_t* token
 // checked: at least L.total bytes, 256-byte aligned).  With `mx` the expert
 // matrices are the block-scaled ones there, in format `mx_format` (1 MXFP8,
 // 2 MXFP4; w then supplies only the small parameters).
-// The hyper-connection post-mix folded into a decode call's reduce.
+// The hyper-connection wrapper folded into a decode call: the split in the
+// head (from the mix launch's partials), the pre-mix in its staging, the
+// post-mix in the reduce.
 struct HcPost {
-  int hc;
+  int hc, iters;
+  int64_t slices;
   const float* state;
-  const float* maps;
+  const float* partial;
+  const float* scale;
+  const float* base;
+  float* mixes;
+  float* maps;
   float* x;  // the FFN input, stored for the view
   float* out;
 };
@@ -230,7 +237,13 @@ int forward_in(const moe_dims_t* d, const float* x, const int32_t* token_ids, in
   a.out = out;
   if (post) {
     a.hc = post->hc;
+    a.hc_iters = post->iters;
+    a.hc_slices = post->slices;
     a.hc_state = post->state;
+    a.hc_partial = post->partial;
+    a.hc_scale = post->scale;
+    a.hc_base = post->base;
+    a.hc_mixes = post->mixes;
     a.hc_maps = post->maps;
     a.hc_x = post->x;
     a.hc_out = post->out;
@@ -453,14 +466,14 @@ int moe_ffn_forward_hc(const moe_dims_t* d, const float* state_in, const int32_t
   a.ffn_in = (float*)(ws + L.ffn_in);
   a.ffn_out = (float*)(ws + L.ffn_out);
   a.out = state_out;
-  // 1-4 rows: the mix launch's last block splits (its arrival count sits at
-  // a fixed place in the status block), the decode launches form the FFN
-  // input from the streams, and the decode reduce does the post-mix
+  // 1-4 rows: the mix launch leaves its slice partials, the decode head
+  // splits and forms the FFN input from the streams, and the decode reduce
+  // does the post-mix
   const bool small = rows <= kDecodeMaxRows;
-  a.cnt = small ? (uint32_t*)(ws + L.ffn.status + 64 + offsetof(DecodeSync, hc_arrive)) : nullptr;
   hipStream_t s = (hipStream_t)stream;
   if (run_hc_pre(a, s) != hipSuccess) return MOE_EHIP;
-  const HcPost post{hw->hc, state_in, a.maps, a.ffn_in, state_out};
+  const HcPost post{hw->hc, a.iters, a.slices, state_in, a.partial, a.scale, a.base, a.mixes, a.maps, a.ffn_in,
+                    state_out};
   rc = forward_in(d, a.ffn_in, token_ids, rows, layer_kind, w, nullptr, 0, (float*)(ws + L.ffn_out), workspace,
                   L.ffn, stream, small ? &post : nullptr);
   if (rc) return rc;

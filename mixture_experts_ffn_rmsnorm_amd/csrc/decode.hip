@@ -31,6 +31,7 @@
 #include <type_traits>
 
 #include "device.h"
+#include "hc_split.h"
 #include "kernels.h"
 
 namespace moe {
@@ -249,9 +250,14 @@ __device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const floa
 // trip for the batch, not one per row), and the values stay in registers
 // for the scaled write.  The first floats of xs double as the cross-wave
 // reduction scratch.  With the hyper-connection wrapper folded in (a.hc >
-// 0) each row is formed from the streams, x[r] = sum_i pre[r][i] *
-// state[r][i] (i in order, from 0), and `store_x` stores it to a.hc_x.
-template <int H>
+// 0) wave 0 first adds the mix launch's slice partials of each (row, mix)
+// in slice order and splits them (hc_split.h); with `store_x` (block 0) the
+// mixes and maps are stored.  Each row is then formed from the streams,
+// x[r] = sum_i pre[r][i] * state[r][i] (i in order, from 0), and `store_x`
+// stores it to a.hc_x.  With MAXR = 1 (the one-row head) the streams'
+// values are requested with the partials, before the split, and wait in
+// registers; with more rows they are requested after it.
+template <int H, int MAXR = kDecodeMaxRows>
 __device__ __forceinline__ void norm_rows_to_lds(const FwdArgs& a, bool store_x, float* xs) {
   const float* __restrict__ x = a.x;
   const float* __restrict__ g = a.norm_w;
@@ -268,14 +274,47 @@ __device__ __forceinline__ void norm_rows_to_lds(const FwdArgs& a, bool store_x,
     gg[k] = i < V ? ((const float4*)g)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (a.hc > 0) {
-    const int hc = a.hc, mw = (2 + hc) * hc;
+    constexpr int MWX = (2 + kHcMax) * kHcMax;
+    __shared__ float s_hsum[kHcRows][MWX + 1];
+    __shared__ float s_hmap[kHcRows][MWX];
+    const int hc = a.hc, mw = (2 + hc) * hc, mv = mw + 1;
+    float4 sv[MAXR == 1 ? kHcMax : 1][NPT];  // one row: its streams, requested now
+    if constexpr (MAXR == 1) {
+#pragma unroll
+      for (int i = 0; i < kHcMax; ++i)
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+          const int idx = t + k * kThreads;
+          sv[i][k] = (i < hc && idx < V) ? ((const float4*)(a.hc_state + (int64_t)i * H))[idx]
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    if (wv == 0) {
+      // (row, value) pair q = r * mv + m over the slices, in slice order
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {  // R * mv <= 100 pairs
+        const int q = lane + kWave * u;
+        if (q < R * mv) {
+          float sum = 0.f;
+#pragma unroll 8
+          for (int64_t s2 = 0; s2 < a.hc_slices; ++s2) sum += a.hc_partial[s2 * (kHcRows * mv) + q];
+          s_hsum[q / mv][q % mv] = sum;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      hc_split_rows_n(hc, &s_hsum[0][0], MWX + 1, R, (float)(hc * H), eps, a.hc_scale, a.hc_base, a.hc_iters,
+                      &s_hmap[0][0], MWX, store_x ? a.hc_mixes : nullptr);
+    }
+    __syncthreads();
+    if (store_x)
+      for (int q = t; q < R * mw; q += kThreads) a.hc_maps[q] = s_hmap[q / mw][q % mw];
     float p[kDecodeMaxRows][kHcMax];
 #pragma unroll
     for (int r = 0; r < kDecodeMaxRows; ++r)
 #pragma unroll
-      for (int i = 0; i < kHcMax; ++i) p[r][i] = (r < R && i < hc) ? a.hc_maps[r * mw + i] : 0.f;
+      for (int i = 0; i < kHcMax; ++i) p[r][i] = (r < R && i < hc) ? s_hmap[r][i] : 0.f;
 #pragma unroll
-    for (int r = 0; r < kDecodeMaxRows; ++r)
+    for (int r = 0; r < MAXR; ++r)
 #pragma unroll
       for (int k = 0; k < NPT; ++k) {
         const int idx = t + k * kThreads;
@@ -284,7 +323,8 @@ __device__ __forceinline__ void norm_rows_to_lds(const FwdArgs& a, bool store_x,
 #pragma unroll
           for (int i = 0; i < kHcMax; ++i) {
             if (i < hc) {
-              const float4 s = ((const float4*)(a.hc_state + ((int64_t)r * hc + i) * H))[idx];
+              const float4 s = MAXR == 1 ? sv[MAXR == 1 ? i : 0][k]
+                                         : ((const float4*)(a.hc_state + ((int64_t)r * hc + i) * H))[idx];
               o.x = fmaf(p[r][i], s.x, o.x); o.y = fmaf(p[r][i], s.y, o.y);
               o.z = fmaf(p[r][i], s.z, o.z); o.w = fmaf(p[r][i], s.w, o.w);
             }
@@ -293,6 +333,10 @@ __device__ __forceinline__ void norm_rows_to_lds(const FwdArgs& a, bool store_x,
         }
         v[r][k] = o;
       }
+#pragma unroll
+    for (int r = MAXR; r < kDecodeMaxRows; ++r)
+#pragma unroll
+      for (int k = 0; k < NPT; ++k) v[r][k] = make_float4(0.f, 0.f, 0.f, 0.f);
   } else {
 #pragma unroll
     for (int r = 0; r < kDecodeMaxRows; ++r)
@@ -906,7 +950,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
     for (int c = 0; c < NCH; ++c)
       if (c < NCH - 1 || full) q[c] = load_stream(a.router + (int64_t)e * H + c * 512 + lane * 8);
   }
-  norm_rows_to_lds<H>(a, b == 0, xs);
+  norm_rows_to_lds<H, kRouterOnly ? 1 : kDecodeMaxRows>(a, b == 0, xs);
   if (kRouterOnly && b == 0)  // the later launches stage the normalised row from xn
     for (int i = threadIdx.x; i < R * H / 4; i += kThreads) ((float4*)a.xn32)[i] = ((const float4*)xs)[i];
   if (e < E) {

@@ -10,19 +10,18 @@
 //   k_hc_mix   one block per (row tile, slice of slice_k flattened inputs):
 //              the slice's dot products with every hc_fn row and its sum of
 //              squares, each thread adding its 4-input pieces of the slice
-//              in order before the wave-wide sums; with 1-4 rows (one tile,
-//              slices of 1024 inputs) the block that completes
-//              the arrival count adds the slices and splits every row (the
-//              decode launches then form the FFN input from the streams)
-//   k_hc_pre   per (row, hidden chunk): the row's slices added in order,
-//              normalised and split (pre and post by sigmoid, comb by exp
-//              and Sinkhorn rounds with one lane per (output, input) stream
-//              pair), then FFN input = sum_i pre_i * state_i
+//              in order before the wave-wide sums; one partial per (tile,
+//              slice).  With 1-4 rows (one tile, slices of 1024 inputs) the
+//              decode head adds the slices and splits (decode.hip).
+//   k_hc_pre   (more than 4 rows) per (row, hidden chunk): the row's slices
+//              added in order, normalised and split (hc_split.h), then FFN
+//              input = sum_i pre_i * state_i
 //   k_hc_post  new_j = post_j * ffn_output + sum_i comb[j][i] * state_i
 //              (more than 4 rows; with 1-4 the decode reduce does it)
 //
 // Everything is f32 with sums in a fixed order (bitwise reproducible).
 #include "device.h"
+#include "hc_split.h"
 #include "kernels.h"
 
 namespace moe {
@@ -30,42 +29,6 @@ namespace {
 
 constexpr int kHcThreads = 256;
 constexpr int kHcWaves = kHcThreads / kWave;
-
-// The split of up to kHcRows rows by one whole wave (every lane active for
-// the DPP moves): lane 16 * rr + 4j + i holds comb entry (j, i) of row rr
-// through the Sinkhorn rounds (row sums over the lanes of one j: a quad;
-// column sums over the lanes of one i: 4 apart, reached by rotating the
-// 16-lane row by 4 and by 8; each division a reciprocal and a multiply,
-// within 2 ulp).  sums[rr]: the row's mix sums, the sum of squares last.
-// Writes the maps of rows rr < nrr to maps[rr] (LDS) and, with `store`,
-// their mixes to a.mixes from row r0 on.
-template <int HC>
-__device__ __forceinline__ void split_rows(const HcArgs& a, const float (*sums)[(2 + HC) * HC + 1], int nrr,
-                                           int64_t r0, bool store, float (*maps)[(2 + HC) * HC]) {
-  constexpr int MW = (2 + HC) * HC;
-  const int lane = threadIdx.x % kWave, rr = lane / 16, j = (lane / 4) % 4, i = lane % 4;
-  const bool row_ok = rr < nrr;
-  const int rs = row_ok ? rr : 0;  // every lane reads a valid row
-  const float rinv = 1.0f / sqrtf(sums[rs][MW] / (float)(HC * a.H) + a.eps);
-  const bool in = row_ok && j < HC && i < HC;
-  if (in && i == 0) {  // pre_j and post_j
-    maps[rr][j] = 1.0f / (1.0f + expf(-(a.scale[0] * (sums[rs][j] * rinv) + a.base[j])));
-    maps[rr][HC + j] = 2.0f / (1.0f + expf(-(a.scale[1] * (sums[rs][HC + j] * rinv) + a.base[HC + j])));
-  }
-  float c = 0.f;
-  if (in) c = expf(a.scale[2] * (sums[rs][2 * HC + j * HC + i] * rinv) + a.base[2 * HC + j * HC + i]);
-  for (int it = 0; it < a.iters; ++it) {
-    float rsum = c + dpp_f32<0xB1>(c);
-    rsum += dpp_f32<0x4E>(rsum);
-    c = in ? c * __builtin_amdgcn_rcpf(rsum) : 0.f;
-    float csum = c + dpp_f32<0x124>(c);
-    csum += dpp_f32<0x128>(csum);
-    c = in ? c * __builtin_amdgcn_rcpf(csum) : 0.f;
-  }
-  if (in) maps[rr][2 * HC + j * HC + i] = c;
-  if (store && row_ok)
-    for (int m = lane % 16; m < MW; m += 16) a.mixes[(r0 + rr) * MW + m] = sums[rr][m] * rinv;
-}
 
 // FFN input of row r (maps in LDS) for hidden values h .. h+3
 template <int HC>
@@ -136,31 +99,8 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
     float v = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < kRows16; ++w2) v += s_part[w2][q];
-    store_wt(&part[q], v);  // read by the last block below (1-4 rows) or the next launch
+    part[q] = v;  // read by the next launch
   }
-  if (!a.cnt) return;
-  // 1-4 rows (one tile): the block that completes the arrival count adds
-  // the slices in order and splits
-  sync_stores();
-  __syncthreads();
-  __shared__ int s_last;
-  if (t == 0) s_last = __hip_atomic_fetch_add(a.cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
-                       (uint32_t)a.slices;
-  __syncthreads();
-  if (!s_last) return;
-  if (t == 0) *a.cnt = 0u;  // ready for the next call
-  __shared__ float s_sum[kHcRows][V];
-  __shared__ float s_map[kHcRows][MW];
-  for (int q = t; q < nr * V; q += kHcThreads) {
-    float v = 0.f;
-#pragma unroll 8
-    for (int64_t s2 = 0; s2 < a.slices; ++s2) v += load_wt(&a.partial[s2 * (kHcRows * V) + q]);
-    s_sum[q / V][q % V] = v;
-  }
-  __syncthreads();
-  if (wv == 0) split_rows<HC>(a, s_sum, nr, 0, true, s_map);
-  __syncthreads();
-  for (int q = t; q < nr * MW; q += kHcThreads) a.maps[q] = s_map[q / MW][q % MW];
 }
 
 // More than 4 rows: one row's split, then its FFN input for 4 hidden values
@@ -182,7 +122,9 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_pre(const HcArgs a) {
     s_sum[0][t] = v;
   }
   __syncthreads();
-  if (t < kWave) split_rows<HC>(a, s_sum, 1, r, blockIdx.y == 0, s_map);
+  if (t < kWave)
+    hc_split_rows<HC>(&s_sum[0][0], V, 1, (float)(HC * a.H), a.eps, a.scale, a.base, a.iters, &s_map[0][0], MW,
+                      blockIdx.y == 0 ? a.mixes + r * MW : nullptr);
   __syncthreads();
   if (blockIdx.y == 0)
     for (int m = t; m < MW; m += kHcThreads) a.maps[r * MW + m] = s_map[0][m];
@@ -221,7 +163,7 @@ hipError_t run_hc_pre_t(const HcArgs& a, hipStream_t s) {
   hipError_t err = launch("hc_mix", (const void*)k_hc_mix<HC>,
                           dim3((unsigned)((a.R + kHcRows - 1) / kHcRows), (unsigned)a.slices), dim3(kHcThreads), 0, s,
                           &args);
-  if (err != hipSuccess || a.cnt) return err;  // 1-4 rows: the mix launch has finished the prelude
+  if (err != hipSuccess || a.R <= kHcRows) return err;  // 1-4 rows: the decode head splits
   return launch("hc_pre", (const void*)k_hc_pre<HC>, dim3(a.R, (a.H / 4 + kHcThreads - 1) / kHcThreads),
                 dim3(kHcThreads), 0, s, &args);
 }

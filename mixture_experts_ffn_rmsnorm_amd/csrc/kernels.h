@@ -42,14 +42,20 @@ struct FwdArgs {
   const uint8_t *gate_s, *up_s, *down_s, *gate_sh_s, *up_sh_s, *down_sh_s;
   float* out;
   // hyper-connection wrapper folded into a decode call (hc > 0, 1-4 rows):
-  // the input row is x[r] = sum_i pre[r][i] * state[r][i] (router block 0
-  // stores it to hc_x), and the reduce writes
+  // every head block adds the mix launch's slice partials and splits (block
+  // 0 stores the mixes and maps), the input row is x[r] = sum_i pre[r][i] *
+  // state[r][i] (block 0 stores it to hc_x), and the reduce writes
   // new[r][j] = post[r][j] * out[r] + sum_i comb[r][j][i] * state[r][i]
-  int hc;
-  const float* hc_state;  // [R][hc][H]
-  const float* hc_maps;   // [R][(2+hc)*hc]: pre | post | comb
-  float* hc_x;            // [R][H]
-  float* hc_out;          // [R][hc][H]
+  int hc, hc_iters;
+  int64_t hc_slices;
+  const float* hc_state;    // [R][hc][H]
+  const float* hc_partial;  // [slices][4][(2+hc)*hc + 1] mix sums, then the sum of squares
+  const float* hc_scale;    // [3]
+  const float* hc_base;     // [(2+hc)*hc]
+  float* hc_mixes;          // [R][(2+hc)*hc]
+  float* hc_maps;           // [R][(2+hc)*hc]: pre | post | comb
+  float* hc_x;              // [R][H]
+  float* hc_out;            // [R][hc][H]
   // workspace pieces
   uint32_t* status;
   DecodeSync* sync;
@@ -89,13 +95,13 @@ struct HcArgs {
   float* mixes;          // [R][(2+hc)*hc]
   float* maps;           // [R][(2+hc)*hc]
   float* partial;
-  uint32_t* cnt;         // 1-4 rows: the mix blocks' arrival count (fixed offset, reset by the last)
   float* ffn_in;         // [R][H]
   const float* ffn_out;  // [R][H]
   float* out;            // [R][hc][H]
 };
-// before the FFN: the mixes, the split and the FFN input -- one launch for
-// 1-4 rows (the last mix block finishes), two for more
+// before the FFN: the mixes' slice partials -- and, with more than 4 rows,
+// the split and the FFN input in a second launch (1-4 rows: the decode head
+// splits and forms the input)
 hipError_t run_hc_pre(const HcArgs& a, hipStream_t s);
 // the new state (after the FFN)
 hipError_t run_hc_post(const HcArgs& a, hipStream_t s);

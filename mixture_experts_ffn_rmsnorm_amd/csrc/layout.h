@@ -43,8 +43,7 @@ struct DecodePlan {
 constexpr int kDecodeMaxTiles = 256;  // down column tiles (hidden/32) and shared gate/up tiles (inter/8)
 struct DecodeSync {
   uint32_t arrive;                       // router blocks of the current call that have written their logits
-  uint32_t hc_arrive;                    // hyper-connection mix blocks of the current call (1-4 rows)
-  uint32_t pad[14];
+  uint32_t pad[15];
   uint32_t tile_cnt[kDecodeMaxTiles];    // groups finished per down column tile
   // one-row path: each expert's ordered selection key and float64 sigmoid,
   // written by the router launch for the gate/up blocks that route
