@@ -456,6 +456,7 @@ int moe_ffn_forward_hc(const moe_dims_t* d, const float* state_in, const int32_t
   a.eps = d->eps;
   a.slices = L.slices;
   a.slice_k = (int)L.slice_k;
+  a.tile_rows = (int)L.tile_rows;
   a.state = state_in;
   a.fn = hw->hc_fn;
   a.scale = hw->hc_scale;

@@ -7,12 +7,13 @@
 // input (dispatch_hc_pre); after it, dispatch_hc_post builds the new state.
 // The split, pre and post arithmetic is the reading stated in moe_ffn.h.
 //
-//   k_hc_mix   one block per (row tile, slice of slice_k flattened inputs):
-//              the slice's dot products with every hc_fn row and its sum of
-//              squares, each thread adding its 4-input pieces of the slice
-//              in order before the wave-wide sums; one partial per (tile,
-//              slice).  With 1-4 rows (one tile, slices of 1024 inputs) the
-//              decode head adds the slices and splits (decode.hip).
+//   k_hc_mix   1-4 rows: one block per slice of 1024 flattened inputs: the
+//              slice's dot products with every hc_fn row and its sum of
+//              squares on the vector ALUs, then wave-wide sums; the decode
+//              head adds the slices and splits (decode.hip)
+//   k_hc_mix_mfma  more rows: one block per (32-row tile, slice): the same
+//              dot products as one 32 x 32 tile of bf16 MFMAs, the state
+//              split exactly into three bf16 terms
 //   k_hc_pre   (more than 4 rows) per (row, hidden chunk): the row's slices
 //              added in order, normalised and split (hc_split.h), then FFN
 //              input = sum_i pre_i * state_i
@@ -29,6 +30,7 @@ namespace {
 
 constexpr int kHcThreads = 256;
 constexpr int kHcWaves = kHcThreads / kWave;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // FFN input of row r (maps in LDS) for hidden values h .. h+3
 template <int HC>
@@ -103,6 +105,74 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_mix(const HcArgs a) {
   }
 }
 
+// More than 4 rows, on the matrix cores: one block per (32-row tile, slice
+// of slice_k flattened inputs), its 4 waves taking every 4th 16-input k-step
+// of the slice.  The slice's dot products are one 32 x 32 tile of
+// v_mfma_f32_32x32x16_bf16 (mix columns past (2+hc)*hc are zero): the f32
+// state is split exactly into three bf16 terms, hi + mid + lo (24
+// significant bits; each difference is exact in f32), each multiplied by
+// the bf16 hc_fn values as they are, f32 accumulation.  Lane l carries row
+// l % 32 of the state and mix l % 32 of hc_fn, inputs 8 * (l / 32) .. +7
+// of each k-step (the operand layout of the instruction); the sum of
+// squares comes from the same loads on the vector ALUs.  The block adds its
+// waves in order and leaves one partial per row; rows past the batch read
+// its last row and are never read back.
+template <int HC>
+__global__ __launch_bounds__(kHcThreads) void k_hc_mix_mfma(const HcArgs a) {
+  constexpr int MW = (2 + HC) * HC, V = MW + 1;
+  static_assert(MW <= 32, "the mixes fit one 32-column tile");
+  const int tile = blockIdx.x, sl = blockIdx.y;
+  const int t = threadIdx.x, wv = t / kWave, lane = t % kWave;
+  const int K = HC * a.H;
+  const int rl = lane % 32, half = lane / 32;
+  const int64_t r0 = (int64_t)tile * kHcMfmaRows;
+  const int64_t rg = r0 + rl < a.R ? r0 + rl : a.R - 1;
+  const float* srow = a.state + rg * K + 8 * half;
+  const bool mcol = rl < MW;
+  const uint16_t* frow = a.fn + (int64_t)(mcol ? rl : 0) * K + 8 * half;
+  const int kbeg = sl * a.slice_k;
+  const int kend = kbeg + a.slice_k < K ? kbeg + a.slice_k : K;
+  floatx16 acc = {};
+  float ss = 0.f;
+#pragma unroll 4
+  for (int k0 = kbeg + wv * 16; k0 + 16 <= kend; k0 += kHcWaves * 16) {
+    const float4 x0 = *(const float4*)(srow + k0), x1 = *(const float4*)(srow + k0 + 4);
+    const uint4 wq = mcol ? *(const uint4*)(frow + k0) : make_uint4(0u, 0u, 0u, 0u);
+    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    bf16x8 hi, mid, lo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = (__bf16)x[i];
+      const float d1 = x[i] - (float)h;
+      const __bf16 m = (__bf16)d1;
+      hi[i] = h;
+      mid[i] = m;
+      lo[i] = (__bf16)(d1 - (float)m);
+      ss = fmaf(x[i], x[i], ss);
+    }
+    const bf16x8 w = __builtin_bit_cast(bf16x8, wq);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, w, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mid, w, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, w, acc, 0, 0, 0);
+  }
+  // lane l holds mix l % 32 of rows 8 (v / 4) + 4 (l / 32) + v % 4
+  __shared__ float s_acc[kHcWaves][kHcMfmaRows][MW];
+  __shared__ float s_ss[kHcWaves][2][kHcMfmaRows];
+  if (mcol)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s_acc[wv][8 * (v / 4) + 4 * half + (v % 4)][rl] = acc[v];
+  s_ss[wv][half][rl] = ss;
+  __syncthreads();
+  float* part = a.partial + ((int64_t)tile * a.slices + sl) * (kHcMfmaRows * V);
+  for (int q = t; q < kHcMfmaRows * V; q += kHcThreads) {
+    const int rr = q / V, m = q % V;
+    float v = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kHcWaves; ++w2) v += m < MW ? s_acc[w2][rr][m] : s_ss[w2][0][rr] + s_ss[w2][1][rr];
+    part[q] = v;  // read by the next launch
+  }
+}
+
 // More than 4 rows: one row's split, then its FFN input for 4 hidden values
 // per thread.  Lane m of wave 0 adds mix m over the row's slices in order;
 // every hidden chunk of a row repeats the split; chunk 0 stores the mixes
@@ -115,10 +185,11 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_pre(const HcArgs a) {
   __shared__ float s_map[1][MW];
   __shared__ float s_sum[1][V];
   if (t < V) {  // mix t (t = MW: the sum of squares) over the slices, in order
-    const float* part = a.partial + (r / kHcRows) * a.slices * (kHcRows * V) + (r % kHcRows) * V + t;
+    const int tr = a.tile_rows;
+    const float* part = a.partial + (r / tr) * a.slices * (tr * V) + (r % tr) * V + t;
     float v = 0.f;
 #pragma unroll 8
-    for (int64_t s2 = 0; s2 < a.slices; ++s2) v += part[s2 * (kHcRows * V)];
+    for (int64_t s2 = 0; s2 < a.slices; ++s2) v += part[s2 * (tr * V)];
     s_sum[0][t] = v;
   }
   __syncthreads();
@@ -160,10 +231,11 @@ __global__ __launch_bounds__(kHcThreads) void k_hc_post(const HcArgs a) {
 template <int HC>
 hipError_t run_hc_pre_t(const HcArgs& a, hipStream_t s) {
   HcArgs args = a;
-  hipError_t err = launch("hc_mix", (const void*)k_hc_mix<HC>,
-                          dim3((unsigned)((a.R + kHcRows - 1) / kHcRows), (unsigned)a.slices), dim3(kHcThreads), 0, s,
-                          &args);
-  if (err != hipSuccess || a.R <= kHcRows) return err;  // 1-4 rows: the decode head splits
+  const bool small = a.R <= kHcRows;  // 1-4 rows: one tile on the vector ALUs; the decode head splits
+  hipError_t err = launch("hc_mix", small ? (const void*)k_hc_mix<HC> : (const void*)k_hc_mix_mfma<HC>,
+                          dim3((unsigned)((a.R + a.tile_rows - 1) / a.tile_rows), (unsigned)a.slices),
+                          dim3(kHcThreads), 0, s, &args);
+  if (err != hipSuccess || small) return err;
   return launch("hc_pre", (const void*)k_hc_pre<HC>, dim3(a.R, (a.H / 4 + kHcThreads - 1) / kHcThreads),
                 dim3(kHcThreads), 0, s, &args);
 }

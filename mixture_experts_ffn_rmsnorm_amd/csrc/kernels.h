@@ -87,7 +87,8 @@ struct HcArgs {
   int R, H, hc, iters;
   float eps;
   int64_t slices;
-  int slice_k;           // flattened inputs per slice (a multiple of 4 * threads)
+  int slice_k;           // flattened inputs per slice
+  int tile_rows;         // rows per mix tile: 4 (1-4 rows) or 32 (more, on the matrix cores)
   const float* state;    // [R][hc][H]
   const uint16_t* fn;    // bf16 [(2+hc)*hc][hc*H]
   const float* scale;    // [3]

@@ -122,25 +122,27 @@ inline bool make_layout(int64_t R, int H, int E, int K, int I, Layout* L) {
 
 // Hyper-connection wrapper (moe_ffn_forward_hc): the FFN's layout at offset
 // 0, then the wrapper's intermediates.  The mix launch works on tiles of
-// kHcRows rows x slice_k flattened inputs and leaves one partial sum per
-// tile and slice; the next launch adds them.  One tile (1-4 rows, a
-// latency-bound call) takes slices of kHcSlice inputs, one block each; more
-// tiles take fewer, wider slices -- as few as keep about kHcMixBlocks
-// blocks in the launch -- so that a thread adds more products between
-// wave-wide sums.
+// tile_rows rows x slice_k flattened inputs and leaves one partial sum per
+// tile, slice and row; the next launch adds them.  1-4 rows (one tile of
+// kHcRows, a latency-bound call on the vector ALUs) take slices of
+// kHcSlice inputs, one block each; more rows go to the matrix cores in
+// tiles of kHcMfmaRows rows, with slices of a multiple of kHcMfmaK inputs,
+// as few as keep about kHcMixBlocks blocks in the launch.
 constexpr int kHcMax = 4;       // streams
 constexpr int kHcRows = 4;      // rows per mix tile
 static_assert(kHcRows == kDecodeMaxRows, "a decode call is one mix tile");
-constexpr int kHcSlice = 1024;  // flattened state values per mix block and pass (256 threads x 4)
+constexpr int kHcSlice = 1024;   // flattened state values per mix block (1-4 rows: 256 threads x 4)
+constexpr int kHcMfmaRows = 32;  // rows per mix tile with more than 4 rows (one 32x32 MFMA tile)
+constexpr int kHcMfmaK = 64;     // slice granule with more than 4 rows (4 waves x 16 k)
 constexpr int kHcMixBlocks = 512;
 struct HcLayout {
   Layout ffn;
-  int64_t tiles, slices, slice_k;  // slice_k: flattened inputs per slice, a multiple of kHcSlice
+  int64_t tile_rows, tiles, slices, slice_k;  // slice_k: flattened inputs per slice
   size_t mixes;    // f32 [R][(2+hc)*hc]
   size_t maps;     // f32 [R][(2+hc)*hc]  pre | post | comb (output stream, input stream)
   size_t ffn_in;   // f32 [R][H]
   size_t ffn_out;  // f32 [R][H]
-  size_t partial;  // f32 [tiles][slices][kHcRows][(2+hc)*hc + 1]  partial dots, then the sum of squares
+  size_t partial;  // f32 [tiles][slices][tile_rows][(2+hc)*hc + 1]  partial dots, then the sum of squares
   size_t total;
 };
 
@@ -149,11 +151,13 @@ inline bool make_hc_layout(int64_t R, int H, int E, int K, int I, int hc, HcLayo
   const unsigned __int128 lim = (unsigned __int128)1 << 62;
   const unsigned __int128 r = (unsigned __int128)R;
   const int mw = (2 + hc) * hc;
-  L->tiles = (R + kHcRows - 1) / kHcRows;
-  const int64_t passes = ((int64_t)hc * H + kHcSlice - 1) / kHcSlice;  // kHcSlice-wide pieces of a row
-  int64_t want = L->tiles > 1 ? (kHcMixBlocks + L->tiles - 1) / L->tiles : passes;
+  L->tile_rows = R <= kHcRows ? kHcRows : kHcMfmaRows;
+  L->tiles = (R + L->tile_rows - 1) / L->tile_rows;
+  const int64_t gran = R <= kHcRows ? kHcSlice : kHcMfmaK;
+  const int64_t passes = ((int64_t)hc * H + gran - 1) / gran;  // granule-wide pieces of a row
+  int64_t want = R <= kHcRows ? passes : (kHcMixBlocks + L->tiles - 1) / L->tiles;
   want = want < 1 ? 1 : (want > passes ? passes : want);
-  L->slice_k = (passes + want - 1) / want * kHcSlice;
+  L->slice_k = (passes + want - 1) / want * gran;
   L->slices = ((int64_t)hc * H + L->slice_k - 1) / L->slice_k;
   unsigned __int128 off = L->ffn.total;
   auto take = [&](unsigned __int128 bytes) -> size_t {
@@ -166,7 +170,7 @@ inline bool make_hc_layout(int64_t R, int H, int E, int K, int I, int hc, HcLayo
   L->maps = take(r * mw * 4);
   L->ffn_in = take(r * H * 4);
   L->ffn_out = take(r * H * 4);
-  L->partial = take((unsigned __int128)L->tiles * L->slices * kHcRows * (mw + 1) * 4);
+  L->partial = take((unsigned __int128)L->tiles * L->slices * L->tile_rows * (mw + 1) * 4);
   off = (off + 255) / 256 * 256;
   if (off >= lim) return false;
   L->total = (size_t)off;

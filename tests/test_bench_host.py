@@ -74,6 +74,7 @@ def test_profiled_kernel_names_map_to_launch_names():
             "gemm_down_shared_reduce_mx",
         "k_route(moe::RouteArgs)": "route",
         "k_hc_mix<4>(moe::HcArgs)": "hc_mix",
+        "k_hc_mix_mfma<3>(moe::HcArgs)": "hc_mix",
         "k_hc_pre<4>(moe::HcArgs)": "hc_pre",
         "k_hc_post<2>(moe::HcArgs)": "hc_post",
     }
