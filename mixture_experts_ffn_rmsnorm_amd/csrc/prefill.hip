@@ -163,12 +163,6 @@ struct RowPick {
   uint32_t flags;
 };
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((int)(uint32_t)v, m, kWave);
-  const uint32_t hi = __shfl_xor((int)(uint32_t)(v >> 32), m, kWave);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // weights of the K picks: s_k = sigmoid(l_k) (0 if masked), w_k = s_k / sum
 // with the sum taken in slot order; lane `sub` holds slot sub's s
 __device__ __forceinline__ float weight_8(double s_mine, int K, int sub) {
@@ -180,6 +174,16 @@ __device__ __forceinline__ float weight_8(double s_mine, int K, int sub) {
     if (k < K) tot += sk;
   }
   return (sub < K && tot > 0.0) ? (float)(s_mine / tot) : 0.0f;
+}
+
+// (key, expert) of the lane DPP control CTRL selects, kept if it ranks first
+template <int CTRL>
+__device__ __forceinline__ void pick_best_dpp(uint64_t& bu, int& be) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)bu, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(bu >> 32), CTRL, 0xF, 0xF, false);
+  const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xF, 0xF, false);
+  const uint64_t ou = ((uint64_t)hi << 32) | lo;
+  if (ou > bu || (ou == bu && oe < be)) { bu = ou; be = oe; }
 }
 
 template <int EMAX>
@@ -195,17 +199,24 @@ __device__ __forceinline__ RowPick pick_score_8_t(const double* key, const float
 #pragma unroll
   for (int k = 0; k < kMaxTopK; ++k) {
     if (k >= K) break;
-    uint64_t bu = 0ull;
-    int be = 0x7fffffff;
+    // the lane's best: four independent chains (keys i = c, c + 4, ...;
+    // the first of equal keys kept), then the chains by (key, lower expert)
+    uint64_t cu[4] = {0ull, 0ull, 0ull, 0ull};
+    int ce[4] = {0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff};
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      if (u[i] > bu) { bu = u[i]; be = sub + 8 * i; }
+      if (u[i] > cu[i % 4]) { cu[i % 4] = u[i]; ce[i % 4] = sub + 8 * i; }
+    uint64_t bu = cu[0];
+    int be = ce[0];
 #pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {
-      const uint64_t ou = shfl_xor_u64(bu, m);
-      const int oe = __shfl_xor(be, m, kWave);
-      if (ou > bu || (ou == bu && oe < be)) { bu = ou; be = oe; }
-    }
+    for (int c = 1; c < 4; ++c)
+      if (cu[c] > bu || (cu[c] == bu && ce[c] < be)) { bu = cu[c]; be = ce[c]; }
+    // the 8 lanes' best, by DPP moves (lane pairs 1 apart, 2 apart, then
+    // the mirror of the 8); the order (key, then lower expert) is total, so
+    // every lane ends with the group's best
+    pick_best_dpp<0xB1>(bu, be);
+    pick_best_dpp<0x4E>(bu, be);
+    pick_best_dpp<0x141>(bu, be);
 #pragma unroll
     for (int i = 0; i < PER; ++i)
       if (sub + 8 * i == be) u[i] = 0ull;
@@ -343,6 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
   static_assert(NK >= 2, "router k loop");
   __shared__ __align__(16) unsigned char s_ring[NSTG * ST];
   __shared__ uint32_t s_mask[E];
+  __shared__ float s_bias[E];  // the selection bias, staged once (score layers)
   __shared__ uint32_t s_flags;
   __shared__ int s_last;
   float* s_logit = reinterpret_cast<float*>(s_ring);                 // [kRR][E] after the k loop
@@ -356,7 +368,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
   const int64_t r0 = rb * kRR;
   const int nrows = (int)((a.R - r0) < kRR ? (a.R - r0) : kRR);
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)s_ring;
-  for (int e = t; e < E; e += kThreads) s_mask[e] = 0;
+  for (int e = t; e < E; e += kThreads) {
+    s_mask[e] = 0;
+    s_bias[e] = a.layer_kind != MOE_LAYER_HASH && e < a.E ? a.bias[e] : 0.f;
+  }
   if (t == 0) s_flags = 0;
 
   // 1. logits[32][e0 .. e0+EL).  DMA: the hi and lo tiles take one
@@ -525,10 +540,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_pre_router(const FwdArgs a) {
   const bool score = a.layer_kind != MOE_LAYER_HASH;
   {
     bool bad = false;
+#pragma unroll 4
     for (int q = t; q < nrows * E; q += kThreads) {
       const float l = s_logit[q];
       bad |= !__builtin_isfinite(l);
-      if (score) s_key[q] = score_key(l, a.bias[q % E]);
+      if (score) s_key[q] = score_key(l, s_bias[q % E]);
     }
     if (bad) atomicOr(&s_flags, (uint32_t)MOE_FLAG_F16_RANGE);
     __syncthreads();
