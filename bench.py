@@ -558,7 +558,8 @@ def _threads():
 
 def _parity(cfg, hi, res, out_g, idx_g):
     """Agreement of the GPU's output and expert sets with the oracle's on the
-    rows of `res`: relL2, max-abs ratio, rows whose expert set matches, and
+    rows of `res`: relL2 (whole batch and worst row), max-abs ratio, rows
+    whose expert set matches, and
     rows whose oracle 6th and 7th selection keys lie within 1e-6 (where a
     set mismatch would be a float32 tie, not an error; hash layers select
     from the table and have none)."""
@@ -575,7 +576,9 @@ def _parity(cfg, hi, res, out_g, idx_g):
         keys = ref.sigmoid(res["logits"]) + np.asarray(hi.sel_bias, dtype=np.float64)
         top = -np.sort(-keys, axis=1)
         near = int(np.sum(top[:, cfg.top_k - 1] - top[:, cfg.top_k] < gap_tol))
+    row_rel = np.linalg.norm(out_g - ref_out, axis=1) / np.maximum(np.linalg.norm(ref_out, axis=1), 1e-300)
     return {"rows": n, "relL2": float(np.linalg.norm(out_g - ref_out) / max(np.linalg.norm(ref_out), 1e-300)),
+            "worst_row_relL2": float(row_rel.max()),
             "maxabs_ratio": float(np.abs(out_g - ref_out).max() / max(np.abs(ref_out).max(), 1e-300)),
             "index_match_rows": int(same), "near_tie_rows": near, "near_tie_gap": gap_tol}
 
