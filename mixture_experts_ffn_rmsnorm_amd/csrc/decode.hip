@@ -24,6 +24,10 @@
 //   k_dec_down<true>  routed down, plus the shared down in two half-blocks
 //                     per column tile, and the same reduce
 //
+// Inside the hyper-connection wrapper (hc > 0) every head block also adds
+// the mix launch's partial sums and splits them, forms each row from the
+// streams while staging it, and the reduce writes the new streams.
+//
 // Stage order follows forward_ffn_rows on the hf2q ffn_forward.rs page
 // (rms_norm -> MoE gate -> route -> sanitize -> routed/shared gate, up ->
 // swiglu -> routed/shared down -> weighted reduce); the page's rows*top_k

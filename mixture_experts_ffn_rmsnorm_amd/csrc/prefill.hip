@@ -20,8 +20,9 @@
 // page; its "slotted" indexed matmul over [rows, top_k] becomes the sort +
 // grouped GEMM here.
 //
-// Matrix-core precision: weights are bf16, or block-scaled 8-bit codes
-// (E4M3 with an E8M0 scale per 32 inputs, OCP MX); activations (xn, and the
+// Matrix-core precision: weights are bf16, or block-scaled 8-bit or 4-bit
+// codes (E4M3, or E2M1 two per byte, with an E8M0 scale per 32 inputs: OCP
+// MXFP8 / MXFP4); activations (xn, and the
 // SwiGLU output h) are rounded to fp16 and multiplied by the weights
 // converted to fp16 (bf16: exact for 2^-14 <= |w| <= 65504, within 2^-25
 // below; MX: the decoded value code * 2^(scale-127) rounded to nearest even
@@ -321,10 +322,12 @@ __global__ __launch_bounds__(kThreads) void k_pre_norm(const FwdArgs a) {
 //  2. With S > 1 a block writes its logit columns through to the workspace
 //     and counts itself in the group's arrival counter; the group's last
 //     block reads all E logits of its rows back and routes them.
-//  3. Selection keys sigmoid(l) + bias (float64) of all 32 x E logits, by all
-//     threads at once; then one wave per row picks its top-k (or looks up
-//     its hash row), and the block publishes, per expert, the 32-bit mask
-//     of its rows that chose the expert, which is all the sort needs.
+//  3. Selection keys sigmoid(l) + bias (float64; the bias staged in LDS) of
+//     all 32 x E logits, by all threads at once; then 8 lanes per row pick
+//     its top-k (each lane's best of its experts, the 8 lanes' best by DPP
+//     moves; or look up its hash row), and the block publishes, per expert,
+//     the 32-bit mask of its rows that chose the expert, which is all the
+//     sort needs.
 constexpr int kRK = 64;                 // k-tile (one 128-byte row per operand row)
 constexpr int kRBudget = 144 * 1024;    // LDS bytes of the router ring
 
