@@ -69,8 +69,8 @@ def alg_bytes(kernel, cfg, U, R, hc=4):
         return E * H * 2 + x + H * 4 + R * E * 4 + R * H * 4 + R * E * 16
     if kernel == "dec1_gateup":      # shared + routed gate/up, routing from the keys
         return (U + 1) * 2 * I * H * wb + R * E * 16 + R * H * 4 + (R * K + R) * I * 4 + R * K * 12
-    if kernel == "dec1_down_reduce":  # routed + shared down + weighted reduce
-        return (U + 1) * H * I * wb + (R * K + R) * I * 4 + (R * K + R) * 2 * H * 4 + R * H * 4
+    if kernel == "dec1_down_reduce":  # routed + shared down + weighted reduce, formed in place
+        return (U + 1) * H * I * wb + (R * K + R) * I * 4 + R * H * 4
     if kernel == "pre_norm":         # x in, xn16 + xlo16 out
         return x + 2 * R * H * 2
     if kernel == "pre_router":       # xn16 + xlo16 in, logits + routing out, router weights once

@@ -21,12 +21,14 @@
 //                     selection key and float64 sigmoid
 //   k_dec1_gateup     shared gate/up blocks, and routed gate/up blocks that
 //                     each route the row from those keys before streaming
-//   k_dec_down<true>  routed down, plus the shared down in two half-blocks
-//                     per column tile, and the same reduce
+//   k_dec1_down       output-stationary down: each block streams 8 hidden
+//                     rows of every matrix (the routed experts', then the
+//                     shared one's) and forms those outputs itself
 //
 // Inside the hyper-connection wrapper (hc > 0) every head block also adds
 // the mix launch's partial sums and splits them, forms each row from the
-// streams while staging it, and the reduce writes the new streams.
+// streams while staging it, and the block forming the output writes the new
+// streams.
 //
 // Stage order follows forward_ffn_rows on the hf2q ffn_forward.rs page
 // (rms_norm -> MoE gate -> route -> sanitize -> routed/shared gate, up ->
@@ -56,6 +58,12 @@ constexpr int kSdRows = 16;
 // row).
 template <int MX> constexpr int kNbuf = 2;
 template <int MX> constexpr bool kPair = true;
+// The one-row down launch keeps four rows (two pairs) in flight per wave
+// through a fully unrolled stream: it has half as many waves per compute
+// unit as the other launches (two blocks of 74 KB of LDS each).  Measured
+// against two rows: down 21.0 vs 22.5 us (bf16), 14.5-15.2 vs 15.1-15.4 us
+// (8-bit), 12.3-12.6 vs 12.7-12.9 us (4-bit).
+constexpr int kNbuf1Down = 4;
 
 // An expert matrix [out][LEN] in one of the weight formats MX: 0 bf16
 // values; 1 block-scaled 8-bit values (E4M3 codes [out][LEN], one E8M0
@@ -115,6 +123,15 @@ __device__ __forceinline__ uint2 load_stream8(const void* p) {
 }
 __device__ __forceinline__ uint32_t load_stream4(const void* p) { return __builtin_nontemporal_load((const uint32_t*)p); }
 
+// f(std::integral_constant<int, K>{}) for K = B .. E-1, in order.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // One wavefront walks a sequence of whole weight rows (global) and dots each
 // with up to 4 f32 activation rows in LDS (row r at act + r*LEN).  Each row
 // is read front to back as contiguous wave loads (1 KiB for bf16, 512 B for
@@ -139,9 +156,11 @@ __device__ __forceinline__ uint32_t load_stream4(const void* p) { return __built
 // With PAIR rows are multiplied two at a time, so each activation value read
 // from LDS serves both (with several activation rows and half-size 8-bit
 // weight rows the LDS reads, not the weight stream, bound the loop
-// otherwise).
-template <int LEN, int NBUF, int MX, bool PAIR, class RowSrc, class Pre, class Sink>
-__device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const float* act, int nr, Pre pre, Sink sink) {
+// otherwise).  actof(j) gives row j's activations (stream_rows: the same for
+// every row); with PAIR rows 2i and 2i + 1 must share them.
+template <int LEN, int NBUF, int MX, bool PAIR, int MAXROWS, class RowSrc, class ActOf, class Pre, class Sink>
+__device__ __forceinline__ void stream_rows_by(int nrows, RowSrc rowsrc, ActOf actof, int nr, Pre pre, Sink sink) {
+  constexpr bool TAIL = MAXROWS > 0;
   static_assert(LEN % 256 == 0, "row length must be a multiple of 256");
   static_assert(!PAIR || NBUF % 2 == 0, "pairs of rows in flight");
   constexpr int NCH = (LEN + 511) / 512;
@@ -174,8 +193,9 @@ __device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const floa
     }
   };
   // rows b .. b+NR-1 (NR = 1, or 2 with PAIR) against the activations
-  auto dot_rows = [&](int b, auto nr_c, float (&part)[2][4]) {
+  auto dot_rows = [&](int b, int j, auto nr_c, float (&part)[2][4]) {
     constexpr int NR = decltype(nr_c)::value;
+    const float* act = actof(j);
 #pragma unroll
     for (int i = 0; i < NR; ++i)
 #pragma unroll
@@ -219,34 +239,63 @@ __device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const floa
   constexpr int STEP = PAIR ? 2 : 1;
   using StepC = std::integral_constant<int, STEP>;
 #pragma unroll
-  for (int b = 0; b < NBUF; ++b) load_row(b, b);
+  for (int b = 0; b < NBUF; ++b) load_row(b, TAIL && b >= nrows ? nrows - 1 : b);
   pre();
-  // Steady state: every row of the group has a successor NBUF rows on, whose
-  // loads go out as soon as the row is multiplied.  The loads are
-  // unconditional, so the compiler's wait for each chunk counts exactly the
-  // loads issued after it, and NBUF rows stay in flight (a conditional
-  // refill makes every wait assume it did not happen, and each wave then
-  // also waits for the row it has just requested).
+  if constexpr (!TAIL) {
+    // Steady state: every row of the group has a successor NBUF rows on,
+    // whose loads go out as soon as the row is multiplied.  The loads are
+    // unconditional, so the compiler's wait for each chunk counts exactly
+    // the loads issued after it, and NBUF rows stay in flight (a conditional
+    // refill makes every wait assume it did not happen, and each wave then
+    // also waits for the row it has just requested).
 #pragma unroll 1
-  for (int j0 = 0; j0 + NBUF < nrows; j0 += NBUF) {
+    for (int j0 = 0; j0 + NBUF < nrows; j0 += NBUF) {
+#pragma unroll
+      for (int b = 0; b < NBUF; b += STEP) {
+        float part[2][4];
+        dot_rows(b, j0 + b, StepC{}, part);
+#pragma unroll
+        for (int i = 0; i < STEP; ++i) load_row(b + i, j0 + b + i + NBUF);
+#pragma unroll
+        for (int i = 0; i < STEP; ++i) sink(j0 + b + i, part[i]);
+      }
+    }
+    // last group: no further loads
 #pragma unroll
     for (int b = 0; b < NBUF; b += STEP) {
       float part[2][4];
-      dot_rows(b, StepC{}, part);
+      dot_rows(b, nrows - NBUF + b, StepC{}, part);
 #pragma unroll
-      for (int i = 0; i < STEP; ++i) load_row(b + i, j0 + b + i + NBUF);
-#pragma unroll
-      for (int i = 0; i < STEP; ++i) sink(j0 + b + i, part[i]);
+      for (int i = 0; i < STEP; ++i) sink(nrows - NBUF + b + i, part[i]);
     }
-  }
-  // last group: no further loads
+  } else {
+    // nrows (a multiple of STEP, at most MAXROWS) is dispatched to a fully
+    // unrolled stream: every slot is a fixed set of registers, so no value
+    // is copied between slots (a copy waits for every load in flight) and
+    // each wait counts exactly the rows requested after its own; NBUF rows
+    // stay in flight to the end.  The slots past nrows hold copies of its
+    // last row, unused.
+    static_for<1, MAXROWS / STEP + 1>([&](auto n_c) {
+      constexpr int NROWS = decltype(n_c)::value * STEP;
+      if (nrows != NROWS) return;
 #pragma unroll
-  for (int b = 0; b < NBUF; b += STEP) {
-    float part[2][4];
-    dot_rows(b, StepC{}, part);
+      for (int j = 0; j < NROWS; j += STEP) {
+        float part[2][4];
+        dot_rows(j % NBUF, j, StepC{}, part);
+        // the refill may not move above the products, whose registers it reuses
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + NBUF < NROWS)
 #pragma unroll
-    for (int i = 0; i < STEP; ++i) sink(nrows - NBUF + b + i, part[i]);
+          for (int i = 0; i < STEP; ++i) load_row((j + i) % NBUF, j + i + NBUF);
+#pragma unroll
+        for (int i = 0; i < STEP; ++i) sink(j + i, part[i]);
+      }
+    });
   }
+}
+template <int LEN, int NBUF, int MX, bool PAIR, class RowSrc, class Pre, class Sink>
+__device__ __forceinline__ void stream_rows(int nrows, RowSrc rowsrc, const float* act, int nr, Pre pre, Sink sink) {
+  stream_rows_by<LEN, NBUF, MX, PAIR, 0>(nrows, rowsrc, [act](int) { return act; }, nr, pre, sink);
 }
 
 // RMSNorm of R (<= 4) rows into LDS: xs[r*H + j] = x[r,j] * (mean x^2 + eps)^-1/2 * g[j].
@@ -872,18 +921,17 @@ __device__ __forceinline__ int plan_row(const DecodePlan* P, int j, int R, uint3
 
 // Down projection of ROWS hidden rows of one expert (wbase [H][I]) for the
 // nr activation rows staged in hs: the block's i-th row (i = wave + 4j) is
-// x + (i * mul + add) * stride, so concurrent blocks read neighbouring rows
-// (x, x + stride, ... for mul 1; every other one of them, from `add`, for
-// mul 2).  d32 rows ent..ent+nr-1 receive the results (written through).
+// x + i * stride, so concurrent blocks read neighbouring rows.  d32 rows
+// ent..ent+nr-1 receive the results (written through).
 template <int H, int I, int ROWS, int NBUF, int MX, bool PAIR, class Pre>
-__device__ __forceinline__ void down_tile(const WMat& wm, const float* hs, int nr, int x, int stride, int mul, int add,
-                                          float* d32, int ent, Pre pre) {
+__device__ __forceinline__ void down_tile(const WMat& wm, const float* hs, int nr, int x, int stride, float* d32,
+                                          int ent, Pre pre) {
   constexpr int W = kThreads / kWave, RPW = ROWS / W;  // rows per wave
   static_assert(RPW * 4 <= kWave && RPW % NBUF == 0, "one lane per result; whole row groups in flight");
   __shared__ float s_res[ROWS * 4];  // results wait here until the stream ends
   const int wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   float* res = s_res + wv * RPW * 4;
-  auto row_of = [&](int j) { return x + ((wv + j * W) * mul + add) * stride; };
+  auto row_of = [&](int j) { return x + (wv + j * W) * stride; };
   auto rowsrc = [&](int j) { return wrow<MX, I>(wm, row_of(j)); };
   auto sink = [&](int j, const float (&part)[4]) {
 #pragma unroll
@@ -1030,7 +1078,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_gateup(const FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(kDecodeMaxSlots + (j < a.R ? j : 0)) * I;
     down_tile<H, I, kSdRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down_sh, a.down_sh_q, a.down_sh_s, 0, (int64_t)H * I), xs, a.R, b,
-                                 H / kSdRows, 1, 0, a.d32, kDecodeMaxSlots,
+                                 H / kSdRows, a.d32, kDecodeMaxSlots,
                              [&]() { stage_rows<I>(xs, src, a.R); });
     return;
   }
@@ -1093,22 +1141,17 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Routed down + weighted reduce.  grid = (H/32, G) with G the most distinct
-// routed experts, plus two rows of shared-down blocks when kShared (the
-// one-row path, whose shared h is computed by the launch before).  Block
-// (x, u < G) computes hidden rows x, x + H/32, ... of the plan's u-th
-// expert's down projection for its rows and writes them through to d32;
-// shared block (x, G + h) computes every other one of those rows, from the
-// h-th, of the shared down projection.  Each then counts itself in
-// tile_cnt[x].  The block that completes the count (every routed group of
-// the tile, and both shared halves, have written) forms, for those 32
-// columns, out[r] = sum over r's (expert, row) pairs in plan order (experts
-// ascending; slot order for one row) of weight * down, then + shared down --
-// a fixed order, so the
-// output is bitwise reproducible.  No block waits for another.  Without
-// kShared and with no valid routed expert at all, the u = 0 blocks write
-// out = shared down.
-template <int H, int I, bool kShared, int MX>
+// Routed down + weighted reduce (2-4 rows).  grid = (H/32, G) with G the
+// most distinct routed experts.  Block (x, u) computes hidden rows x, x +
+// H/32, ... of the plan's u-th expert's down projection for its rows and
+// writes them through to d32, then counts itself in tile_cnt[x].  The block
+// that completes the count (every routed group of the tile has written)
+// forms, for those 32 columns, out[r] = sum over r's (expert, row) pairs in
+// plan order (experts ascending) of weight * down, then + the shared down
+// written by the gate/up launch -- a fixed order, so the output is bitwise
+// reproducible.  No block waits for another.  With no valid routed expert
+// at all, the u = 0 blocks write out = shared down.
+template <int H, int I, int MX>
 __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   __shared__ float hs[kDecodeMaxRows * I];
   __shared__ int s_er[kDecodeMaxSlots];    // the plan's entry rows and weights, for the reduce
@@ -1121,8 +1164,7 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   constexpr int dnt = H / kDnRows;
   int ne = P->nentries;
   ne = ne < 0 ? 0 : (ne > kDecodeMaxSlots ? kDecodeMaxSlots : ne);
-  const int G = kShared ? (int)gridDim.y - 2 : (int)gridDim.y;
-  const int expect = ng + (kShared ? 2 : 0);  // blocks that write into tile x
+  const int expect = ng;  // blocks that write into tile x
   auto stage_entries = [&]() {
     if (threadIdx.x < kDecodeMaxSlots) {
       s_er[threadIdx.x] = P->entry_row[threadIdx.x];
@@ -1130,27 +1172,16 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
     }
   };
   if (expect > 0) {
-    if (kShared && u >= G) {  // shared half-block
-      const float* src[4];
+    if (u >= ng) return;
+    const PlanGroup g = plan_group(P, u, a.E, a.status);
+    const float* src[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(kDecodeMaxSlots + (j < R ? j : 0)) * I;
-      down_tile<H, I, kDnRows / 2, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down_sh, a.down_sh_q, a.down_sh_s, 0, (int64_t)H * I), hs, R, x,
-                                       dnt, 2, u - G, a.d32, kDecodeMaxSlots, [&]() {
-        stage_entries();
-        stage_rows<I>(hs, src, R);  // ends with a barrier
-      });
-    } else {
-      if (u >= ng) return;
-      const PlanGroup g = plan_group(P, u, a.E, a.status);
-      const float* src[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
-      down_tile<H, I, kDnRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down, a.down_q, a.down_s, g.expert, (int64_t)H * I), hs, g.nr, x,
-                                   dnt, 1, 0, a.d32, g.begin, [&]() {
-        stage_entries();
-        stage_rows<I>(hs, src, g.nr);  // ends with a barrier
-      });
-    }
+    for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
+    down_tile<H, I, kDnRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down, a.down_q, a.down_s, g.expert, (int64_t)H * I), hs, g.nr, x,
+                                 dnt, a.d32, g.begin, [&]() {
+      stage_entries();
+      stage_rows<I>(hs, src, g.nr);  // ends with a barrier
+    });
     sync_stores();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1175,8 +1206,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
     for (int i = 0; i < kHcMax; ++i)
       if (i < a.hc) st[i] = a.hc_state[((int64_t)r * a.hc + i) * H + h];
   }
-  // written through by other blocks of this launch when kShared (the shared
-  // half-blocks), so read past any stale cache line like the partials below
+  // the shared expert's down rows, written through by the gate/up launch's
+  // blocks on every XCD: read past any stale cache line like the partials
   const float sh = load_wt(&a.d32[(int64_t)(kDecodeMaxSlots + r) * H + h]);
   float o = 0.f;
   if (ng > 0 && ne > 0) {
@@ -1208,6 +1239,104 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// One-row down + reduce, output-stationary: grid = H/8 blocks.  Block x owns
+// the hidden rows x + i*H/8, i = 0..7 (wave w: i = w and w + 4, so the
+// blocks running together read neighbouring rows of each matrix).  Every
+// wave reads the plan itself (its groups' experts and weights; with one row
+// group u holds entry u), the block stages group u's h vector (u in plan
+// order) and the shared expert's into LDS, and each wave then streams its
+// two rows of every matrix -- the plan's experts in order, then the shared
+// one; the two rows share the activation -- keeping the dot products in
+// LDS.  Thread i < 8 then forms out = sum over u of w_u * down_u, then +
+// shared down: the order of the tile reduce, from the same dot products, so
+// the result is the same bit for bit; the hyper-connection post-mix follows
+// (its state and maps staged with the h vectors).  No block waits for
+// another and nothing goes through the workspace.  At full size: 512
+// blocks, two per compute unit, each streaming 8 rows of every matrix.
+template <int H, int I, int MX>
+__global__ __launch_bounds__(kThreads) void k_dec1_down(const FwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float hs[];  // [ng + 1][I]
+  constexpr int W = kThreads / kWave, ROWS = 2 * W, stride = H / ROWS;
+  static_assert(H % ROWS == 0, "whole row groups");
+  __shared__ float s_res[(kMaxTopK + 1) * ROWS];
+  __shared__ float s_st[kHcMax * ROWS];
+  __shared__ float s_map[(2 + kHcMax) * kHcMax];
+  const DecodePlan* P = a.plan;
+  const int cap = a.K < a.E ? a.K : a.E;  // hs holds cap + 1 vectors
+  int ng = plan_ngroups(P);
+  check_index(a.status, ng <= cap);
+  ng = ng > cap ? cap : ng;  // <= kMaxTopK
+  // lane u < kMaxTopK of every wave holds group u's expert, entry and
+  // weight (clamped; read for every u, the plan's arrays being whole)
+  const int x = blockIdx.x, wv = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int ul = lane < kMaxTopK ? lane : 0;
+  int exv = P->group_expert[ul], ebv = P->group_begin[ul];
+  check_index(a.status, ul >= ng || (exv >= 0 && exv < a.E && ebv == ul && P->group_begin[ul + 1] == ul + 1));
+  exv = exv < 0 ? 0 : (exv >= a.E ? a.E - 1 : exv);
+  ebv = ebv < 0 ? 0 : (ebv >= kDecodeMaxSlots ? kDecodeMaxSlots - 1 : ebv);
+  const float ewv = P->entry_w[ebv];
+  const int64_t msz = (int64_t)H * I;
+  const WMat shm = expert_mat<MX>(a.down_sh, a.down_sh_q, a.down_sh_s, 0, msz);
+  auto rowsrc = [&](int j) {
+    const int m = j >> 1;
+    const int e = __builtin_amdgcn_readlane(exv, m < kMaxTopK ? m : 0);
+    const WMat wm = m < ng ? expert_mat<MX>(a.down, a.down_q, a.down_s, e, msz) : shm;
+    return wrow<MX, I>(wm, x + (wv + W * (j & 1)) * stride);
+  };
+  auto actof = [&](int j) { return (const float*)hs + (j >> 1) * I; };
+  auto sink = [&](int j, const float (&part)[4]) {
+    const float v = wave_sum(part[0]);
+    if (lane == 0) s_res[(j >> 1) * ROWS + wv + W * (j & 1)] = v;
+  };
+  const int hc = a.hc > kHcMax ? kHcMax : a.hc;
+  auto pre = [&]() {
+    // h vectors, global -> LDS directly (no registers held): group u's from
+    // its entry's row, then the shared expert's
+    constexpr int V = I / 4;  // float4 per vector
+    static_assert(V % kWave == 0, "whole waves per vector");
+    for (int m = 0; m <= ng; ++m) {
+      const int row = m < ng ? __builtin_amdgcn_readlane(ebv, m < kMaxTopK ? m : 0) : kDecodeMaxSlots;
+      const float* src = a.h32 + (int64_t)row * I;
+#pragma unroll
+      for (int k = 0; k < (V + kThreads - 1) / kThreads; ++k) {
+        const int i = threadIdx.x + k * kThreads;  // float4 index; i - lane: the wave's first
+        if (V % kThreads == 0 || i < V)
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 4 * i),
+                                           (__attribute__((address_space(3))) void*)(hs + m * I + 4 * (i - lane)), 16, 0, 0);
+      }
+    }
+    const int t = threadIdx.x;
+    if (hc > 0 && t < hc * ROWS) s_st[t] = a.hc_state[(int64_t)(t / ROWS) * H + x + (t % ROWS) * stride];
+    if (hc > 0 && t < (2 + hc) * hc) s_map[t] = a.hc_maps[t];
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
+    __syncthreads();
+  };
+  stream_rows_by<I, kNbuf1Down, MX, true, 2 * (kMaxTopK + 1)>(2 * (ng + 1), rowsrc, actof, 1, pre, sink);
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t >= ROWS) return;
+  const int h = x + t * stride;
+  float o = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMaxTopK; ++u)
+    if (u < ng) o = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ewv), u)), s_res[u * ROWS + t], o);
+  o += s_res[ng * ROWS + t];
+  a.out[h] = o;
+  if (hc > 0) {  // new[j] = post_j * out + sum_i comb[j][i] * state_i, i in order
+#pragma unroll
+    for (int j = 0; j < kHcMax; ++j) {
+      if (j < hc) {
+        float v = s_map[hc + j] * o;
+#pragma unroll
+        for (int i = 0; i < kHcMax; ++i)
+          if (i < hc) v = fmaf(s_map[2 * hc + j * hc + i], s_st[i * ROWS + t], v);
+        a.hc_out[(int64_t)j * H + h] = v;
+      }
+    }
+  }
+}
+
 template <int H, int I, int MX>
 hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   static_assert(H / kDnRows <= kDecodeMaxTiles, "too many down tiles");
@@ -1216,15 +1345,15 @@ hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   hipError_t err;
   if (a.R == 1) {
     // one row: router launch, then gate/up blocks that route for
-    // themselves, then routed + shared down with the reduce
+    // themselves, then the output-stationary down
     err = launch(MX == 2 ? "dec1_router_mx4" : MX ? "dec1_router_mx" : "dec1_router", (const void*)k_dec_head<H, I, true, MX>, dim3((a.E + 3) / 4),
                  dim3(kThreads), (size_t)H * 4, s, &args);
     if (err != hipSuccess) return err;
     err = launch(MX == 2 ? "dec1_gateup_mx4" : MX ? "dec1_gateup_mx" : "dec1_gateup", (const void*)k_dec1_gateup<H, I, MX>,
                  dim3(I / kShRows + gmax * (I / kGuRows)), dim3(kThreads), (size_t)H * 4, s, &args);
     if (err != hipSuccess) return err;
-    return launch(MX == 2 ? "dec1_down_reduce_mx4" : MX ? "dec1_down_reduce_mx" : "dec1_down_reduce", (const void*)k_dec_down<H, I, true, MX>,
-                  dim3(H / kDnRows, gmax + 2), dim3(kThreads), 0, s, &args);
+    return launch(MX == 2 ? "dec1_down_reduce_mx4" : MX ? "dec1_down_reduce_mx" : "dec1_down_reduce", (const void*)k_dec1_down<H, I, MX>,
+                  dim3(H / 8), dim3(kThreads), (size_t)(gmax + 1) * I * 4, s, &args);
   }
   err = launch(MX == 2 ? "dec_head_mx4" : MX ? "dec_head_mx" : "dec_head", (const void*)k_dec_head<H, I, false, MX>,
                dim3((a.E + 3) / 4 + I / kShRows), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
@@ -1232,7 +1361,7 @@ hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   err = launch(MX == 2 ? "dec_gateup_mx4" : MX ? "dec_gateup_mx" : "dec_gateup", (const void*)k_dec_gateup<H, I, MX>,
                dim3(H / kSdRows + gmax * (I / kGuRows)), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  return launch(MX == 2 ? "dec_down_reduce_mx4" : MX ? "dec_down_reduce_mx" : "dec_down_reduce", (const void*)k_dec_down<H, I, false, MX>,
+  return launch(MX == 2 ? "dec_down_reduce_mx4" : MX ? "dec_down_reduce_mx" : "dec_down_reduce", (const void*)k_dec_down<H, I, MX>,
                 dim3(H / kDnRows, gmax), dim3(kThreads), 0, s, &args);
 }
 

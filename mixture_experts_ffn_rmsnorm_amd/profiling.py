@@ -101,8 +101,10 @@ def launch_name(kernel: str) -> str | None:
         base = "dec_gateup"
     elif name == "k_dec1_gateup" and len(args) == 3:
         base = "dec1_gateup"
-    elif name == "k_dec_down" and len(args) == 4:
-        base = "dec1_down_reduce" if args[2] == "true" else "dec_down_reduce"
+    elif name == "k_dec_down" and len(args) == 3:
+        base = "dec_down_reduce"
+    elif name == "k_dec1_down" and len(args) == 3:
+        base = "dec1_down_reduce"
     elif name == "k_gemm" and len(args) == 5:
         base = {"0": "gemm_gateup_swiglu", "1": "gemm_down", "2": "gemm_down_shared_reduce"}.get(args[0])
     else:

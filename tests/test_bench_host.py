@@ -58,9 +58,11 @@ def test_profiled_kernel_names_map_to_launch_names():
         "k_dec_gateup<4096, 2048, 1>(moe::FwdArgs)": "dec_gateup_mx",
         "k_dec1_gateup<512, 256, 0>(moe::FwdArgs)": "dec1_gateup",
         "k_dec1_gateup<4096, 2048, 2>(moe::FwdArgs)": "dec1_gateup_mx4",
-        "k_dec_down<4096, 2048, false, 0>(moe::FwdArgs)": "dec_down_reduce",
-        "k_dec_down<512, 256, true, 0>(moe::FwdArgs)": "dec1_down_reduce",
-        "k_dec_down<4096, 2048, true, 1>(moe::FwdArgs)": "dec1_down_reduce_mx",
+        "k_dec_down<4096, 2048, 0>(moe::FwdArgs)": "dec_down_reduce",
+        "k_dec1_down<512, 256, 0>(moe::FwdArgs)": "dec1_down_reduce",
+        "k_dec1_down<4096, 2048, 1>(moe::FwdArgs)": "dec1_down_reduce_mx",
+        "k_dec1_down<4096, 2048, 2>(moe::FwdArgs)": "dec1_down_reduce_mx4",
+        "k_dec_down<512, 256, 2>(moe::FwdArgs)": "dec_down_reduce_mx4",
         "k_pre_norm<4096>(moe::FwdArgs)": "pre_norm",
         "k_pre_router<4096, 256, 8>(moe::FwdArgs)": "pre_router",
         "k_pre_sort(moe::FwdArgs)": "pre_sort",
