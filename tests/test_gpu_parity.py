@@ -129,6 +129,32 @@ def test_tiny_one_row_table_edge_cases():
     _one_row_table_edge_cases(Layer(cfg), _x(cfg, 1, seed=15))
 
 
+def _one_row_every_valid_count(lay, x):
+    """One row whose table row holds v valid experts for every v = 0..top_k
+    (the rest -1, at rotating positions): the one-row down streams 2(v+1)
+    weight rows per wave, each count its own unrolled code."""
+    cfg = lay.cfg
+    K = cfg.top_k
+    table = lay.host.tid2eid.copy()
+    for v in range(K + 1):
+        row = table[40 + v].copy()
+        for j in range(K - v):
+            row[(3 * v + j) % K] = -1
+        table[40 + v] = row
+    lay.with_table(table)
+    for v in range(K + 1):
+        tok = np.array([40 + v], dtype=np.int32)
+        out, lg, idx, w, st = lay.run(x, tok, HASH)
+        assert int((idx[0] >= 0).sum()) == v
+        assert st == (moe.FLAG_BAD_TABLE_ENTRY if v < K else 0), f"{v} valid: status {st:#x}"
+        check_forward(lay, x, tok, HASH, out, lg, idx, w)
+
+
+def test_tiny_one_row_every_valid_count():
+    cfg = gen.config(0)
+    _one_row_every_valid_count(Layer(cfg), _x(cfg, 1, seed=16))
+
+
 def test_tiny_hash_equals_score(tiny):
     cfg = tiny.cfg
     rows = 16
@@ -427,6 +453,11 @@ def test_full_decode_one_row_hash(full):
 def test_full_decode_one_row_table_edge_cases(full):
     cfg = gen.config(2)
     _one_row_table_edge_cases(Layer(cfg, share=full), _x(cfg, 1, seed=93))
+
+
+def test_full_decode_one_row_every_valid_count(full):
+    cfg = gen.config(2)
+    _one_row_every_valid_count(Layer(cfg, share=full), _x(cfg, 1, seed=94))
 
 
 def test_full_prefill_hash(full):
