@@ -63,8 +63,10 @@ def alg_bytes(kernel, cfg, U, R, hc=4):
         return E * H * 2 + 2 * I * H * wb + 2 * x + H * 4 + R * E * 12 + R * (H + I) * 4
     if kernel == "dec_gateup":       # shared down + routed gate/up
         return H * I * wb + U * 2 * I * H * wb + R * (I + H) * 4 + R * K * (H + I) * 4
-    if kernel == "dec_down_reduce":  # routed down + weighted reduce
-        return U * H * I * wb + R * K * (I + 2 * H) * 4 + R * H * 4 + x
+    if kernel == "dec_down":         # routed down: h in, per-entry partials out
+        return U * H * I * wb + R * K * (I + H) * 4
+    if kernel == "dec_reduce":       # partials and shared down in, out
+        return R * K * H * 4 + R * H * 4 + x
     if kernel == "dec1_router":      # one-row path: router, logits + keys + sigmoids + xn out
         return E * H * 2 + x + H * 4 + R * E * 4 + R * H * 4 + R * E * 16
     if kernel == "dec1_gateup":      # shared + routed gate/up, routing from the keys

@@ -11,9 +11,8 @@
 //   k_dec_gateup   the shared expert's down projection (first blocks), then
 //                  routed gate/up + SwiGLU, one (expert, 16 inter rows) tile
 //                  per block
-//   k_dec_down     routed down projections for 32 hidden rows per block; the
-//                  last block of each column tile forms out = sum of weight
-//                  * down + shared in a fixed order
+//   k_dec_down     routed down projections for 32 hidden rows per block
+//   k_dec_reduce   out = sum of weight * down + shared in a fixed order
 //
 // With one row the launches divide the work differently, and no workgroup
 // ever waits for another:
@@ -869,11 +868,10 @@ __device__ void route_batch(const FwdArgs& a, int* s_idx, float* s_w, unsigned c
 
 // Writes the block's routing (indices, weights, row flags, status word) and
 // the plan (from LDS) to the workspace for the later launches and the
-// caller, and clears the down launch's tile counters.
+// caller.
 __device__ void publish_routing(const FwdArgs& a, const int* s_idx, const float* s_w, const uint32_t* s_flags,
                                 const DecodePlan* P) {
   const int R = a.R;
-  DecodeSync* sy = a.sync;
   for (int s = threadIdx.x; s < R * a.K; s += kThreads) {
     a.idx[s] = s_idx[s];
     a.wts[s] = s_w[s];
@@ -884,7 +882,6 @@ __device__ void publish_routing(const FwdArgs& a, const int* s_idx, const float*
     for (int r = 0; r < R; ++r) f |= s_flags[r];
     a.status[0] = f;
   }
-  for (int i = threadIdx.x; i < kDecodeMaxTiles; i += kThreads) sy->tile_cnt[i] = 0;
   const int* ps = (const int*)P;
   int* pd = (int*)a.plan;
   for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += kThreads) pd[i] = ps[i];
@@ -956,8 +953,8 @@ __device__ __forceinline__ void down_tile(const WMat& wm, const float* hs, int n
 //   block that completes the count -- every logit is written by then --
 //   routes the batch (wave r row r), builds the plan
 //   of distinct (expert, row) pairs, publishes indices, weights, row flags,
-//   status and the plan, clears the down launch's tile counters and resets
-//   the count for the next call.  No workgroup waits for another.
+//   status and the plan, and resets the count for the next call.  No
+//   workgroup waits for another.
 //   Shared gate/up block: RMSNorm into LDS, then 8 inter rows of the shared
 //   expert's SwiGLU output for every row; its streaming covers the router's
 //   latency and the routing.  The first of these blocks publishes xn.
@@ -1141,64 +1138,44 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Routed down + weighted reduce (2-4 rows).  grid = (H/32, G) with G the
-// most distinct routed experts.  Block (x, u) computes hidden rows x, x +
-// H/32, ... of the plan's u-th expert's down projection for its rows and
-// writes them through to d32, then counts itself in tile_cnt[x].  The block
-// that completes the count (every routed group of the tile has written)
-// forms, for those 32 columns, out[r] = sum over r's (expert, row) pairs in
-// plan order (experts ascending) of weight * down, then + the shared down
-// written by the gate/up launch -- a fixed order, so the output is bitwise
-// reproducible.  No block waits for another.  With no valid routed expert
-// at all, the u = 0 blocks write out = shared down.
+// Routed down (2-4 rows).  grid = (H/32, G) with G the most distinct routed
+// experts.  Block (x, u) computes hidden rows x, x + H/32, ... of the plan's
+// u-th expert's down projection for its rows and writes them to d32 (the
+// entries' rows); blocks past the plan's groups return at once.  The
+// weighted reduce is the next launch: a block here ends with its stream,
+// with no wait for its stores and no count.
 template <int H, int I, int MX>
 __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   __shared__ float hs[kDecodeMaxRows * I];
-  __shared__ int s_er[kDecodeMaxSlots];    // the plan's entry rows and weights, for the reduce
+  const DecodePlan* P = a.plan;
+  const int u = blockIdx.y;
+  if (u >= plan_ngroups(P)) return;
+  const PlanGroup g = plan_group(P, u, a.E, a.status);
+  const float* src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
+  down_tile<H, I, kDnRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down, a.down_q, a.down_s, g.expert, (int64_t)H * I), hs, g.nr,
+                                                     blockIdx.x, H / kDnRows, a.d32, g.begin,
+                                                     [&]() { stage_rows<I>(hs, src, g.nr); });  // ends with a barrier
+}
+
+// Weighted reduce + shared (2-4 rows).  grid = R*H/256, thread -> (row r,
+// hidden h).  out[r][h] = sum over r's (expert, row) pairs in plan order
+// (experts ascending) of weight * down, then + the shared down written by
+// the gate/up launch -- a fixed order, so the output is bitwise
+// reproducible; with no valid routed expert, out = shared down.  The
+// hyper-connection post-mix follows.
+template <int H>
+__global__ __launch_bounds__(kThreads) void k_dec_reduce(const FwdArgs a) {
+  static_assert(H % kThreads == 0, "a block covers part of one row");
+  __shared__ int s_er[kDecodeMaxSlots];  // the plan's entry rows and weights
   __shared__ float s_ew[kDecodeMaxSlots];
-  __shared__ int s_last;
-  const int R = a.R;
   const DecodePlan* P = a.plan;
   const int ng = plan_ngroups(P);
-  const int x = blockIdx.x, u = blockIdx.y;
-  constexpr int dnt = H / kDnRows;
   int ne = P->nentries;
   ne = ne < 0 ? 0 : (ne > kDecodeMaxSlots ? kDecodeMaxSlots : ne);
-  const int expect = ng;  // blocks that write into tile x
-  auto stage_entries = [&]() {
-    if (threadIdx.x < kDecodeMaxSlots) {
-      s_er[threadIdx.x] = P->entry_row[threadIdx.x];
-      s_ew[threadIdx.x] = P->entry_w[threadIdx.x];
-    }
-  };
-  if (expect > 0) {
-    if (u >= ng) return;
-    const PlanGroup g = plan_group(P, u, a.E, a.status);
-    const float* src[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
-    down_tile<H, I, kDnRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down, a.down_q, a.down_s, g.expert, (int64_t)H * I), hs, g.nr, x,
-                                 dnt, a.d32, g.begin, [&]() {
-      stage_entries();
-      stage_rows<I>(hs, src, g.nr);  // ends with a barrier
-    });
-    sync_stores();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t prev =
-          __hip_atomic_fetch_add(&a.sync->tile_cnt[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = prev + 1 == (uint32_t)expect;
-    }
-    __syncthreads();
-    if (!s_last) return;
-  } else if (u != 0) {
-    return;
-  }
-  // reduce this tile: thread t -> (row r = t / 32, hidden row x + (t % 32) * H/32)
-  const int t = threadIdx.x;
-  if (t >= R * kDnRows) return;
-  const int r = t / kDnRows;
-  const int h = x + (t % kDnRows) * dnt;
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int r = (int)(t / H), h = (int)(t % H);
   // hyper-connection post-mix: the row's old streams at h, requested first
   float st[kHcMax];
   if (a.hc > 0) {
@@ -1206,17 +1183,22 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
     for (int i = 0; i < kHcMax; ++i)
       if (i < a.hc) st[i] = a.hc_state[((int64_t)r * a.hc + i) * H + h];
   }
-  // the shared expert's down rows, written through by the gate/up launch's
-  // blocks on every XCD: read past any stale cache line like the partials
+  // the down launch's partials and the shared expert's down rows were
+  // written by blocks on every XCD: read past any stale cache line
   const float sh = load_wt(&a.d32[(int64_t)(kDecodeMaxSlots + r) * H + h]);
-  float o = 0.f;
-  if (ng > 0 && ne > 0) {
-    // every entry's partial is requested at once (one memory round trip; the
-    // index is clamped, so the loads past ne re-read a valid row), then the
-    // row's own entries are added in plan order
-    float v[kDecodeMaxSlots];
+  // every entry's partial is requested at once (one memory round trip; the
+  // index is clamped, so the loads past ne re-read a valid row)
+  float v[kDecodeMaxSlots];
 #pragma unroll
-    for (int j = 0; j < kDecodeMaxSlots; ++j) v[j] = load_wt(&a.d32[(int64_t)(j < ne ? j : ne - 1) * H + h]);
+  for (int j = 0; j < kDecodeMaxSlots; ++j) v[j] = load_wt(&a.d32[(int64_t)(j < ne ? j : (ne > 0 ? ne - 1 : 0)) * H + h]);
+  if (threadIdx.x < kDecodeMaxSlots) {
+    s_er[threadIdx.x] = P->entry_row[threadIdx.x];
+    s_ew[threadIdx.x] = P->entry_w[threadIdx.x];
+  }
+  __syncthreads();
+  float o = 0.f;
+  if (ng > 0) {
+    // the row's own entries, in plan order
 #pragma unroll
     for (int j = 0; j < kDecodeMaxSlots; ++j)
       if (j < ne && s_er[j] == r) o = fmaf(s_ew[j], v[j], o);
@@ -1229,11 +1211,11 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < kHcMax; ++j) {
       if (j < hc) {
-        float v = mp[hc + j] * o;
+        float w = mp[hc + j] * o;
 #pragma unroll
         for (int i = 0; i < kHcMax; ++i)
-          if (i < hc) v = fmaf(mp[2 * hc + j * hc + i], st[i], v);
-        a.hc_out[((int64_t)r * hc + j) * H + h] = v;
+          if (i < hc) w = fmaf(mp[2 * hc + j * hc + i], st[i], w);
+        a.hc_out[((int64_t)r * hc + j) * H + h] = w;
       }
     }
   }
@@ -1339,7 +1321,6 @@ __global__ __launch_bounds__(kThreads) void k_dec1_down(const FwdArgs a) {
 
 template <int H, int I, int MX>
 hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
-  static_assert(H / kDnRows <= kDecodeMaxTiles, "too many down tiles");
   FwdArgs args = a;
   const int gmax = a.R * a.K < a.E ? a.R * a.K : a.E;
   hipError_t err;
@@ -1361,8 +1342,10 @@ hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
   err = launch(MX == 2 ? "dec_gateup_mx4" : MX ? "dec_gateup_mx" : "dec_gateup", (const void*)k_dec_gateup<H, I, MX>,
                dim3(H / kSdRows + gmax * (I / kGuRows)), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
-  return launch(MX == 2 ? "dec_down_reduce_mx4" : MX ? "dec_down_reduce_mx" : "dec_down_reduce", (const void*)k_dec_down<H, I, MX>,
-                dim3(H / kDnRows, gmax), dim3(kThreads), 0, s, &args);
+  err = launch(MX == 2 ? "dec_down_mx4" : MX ? "dec_down_mx" : "dec_down", (const void*)k_dec_down<H, I, MX>,
+               dim3(H / kDnRows, gmax), dim3(kThreads), 0, s, &args);
+  if (err != hipSuccess) return err;
+  return launch("dec_reduce", (const void*)k_dec_reduce<H>, dim3(a.R * H / kThreads), dim3(kThreads), 0, s, &args);
 }
 
 }  // namespace

@@ -36,15 +36,12 @@ struct DecodePlan {
   float entry_w[kDecodeMaxSlots];
 };
 
-// Cross-workgroup counters of the decode path, after the status word.  The
+// Cross-workgroup words of the decode path, after the status word.  The
 // arrival count starts every call at 0: the router block that completes it
-// resets it (the workspace is zero-filled before its first use); the tile
-// counters are cleared by the head launch for the down launch.
-constexpr int kDecodeMaxTiles = 256;  // down column tiles (hidden/32) and shared gate/up tiles (inter/8)
+// resets it (the workspace is zero-filled before its first use).
 struct DecodeSync {
   uint32_t arrive;                       // router blocks of the current call that have written their logits
   uint32_t pad[15];
-  uint32_t tile_cnt[kDecodeMaxTiles];    // groups finished per down column tile
   // one-row path: each expert's ordered selection key and float64 sigmoid,
   // written by the router launch for the gate/up blocks that route
   uint64_t route_key[kMaxExperts];

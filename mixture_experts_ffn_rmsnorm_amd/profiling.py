@@ -102,7 +102,7 @@ def launch_name(kernel: str) -> str | None:
     elif name == "k_dec1_gateup" and len(args) == 3:
         base = "dec1_gateup"
     elif name == "k_dec_down" and len(args) == 3:
-        base = "dec_down_reduce"
+        base = "dec_down"
     elif name == "k_dec1_down" and len(args) == 3:
         base = "dec1_down_reduce"
     elif name == "k_gemm" and len(args) == 5:
@@ -110,7 +110,7 @@ def launch_name(kernel: str) -> str | None:
     else:
         mx = False
         base = {"k_pre_norm": "pre_norm", "k_pre_router": "pre_router", "k_pre_sort": "pre_sort",
-                "k_route": "route", "k_hc_mix": "hc_mix", "k_hc_mix_mfma": "hc_mix", "k_hc_pre": "hc_pre", "k_hc_post": "hc_post"}.get(name)
+                "k_route": "route", "k_dec_reduce": "dec_reduce", "k_hc_mix": "hc_mix", "k_hc_mix_mfma": "hc_mix", "k_hc_pre": "hc_pre", "k_hc_post": "hc_post"}.get(name)
     if base is None:
         return None
     return base + fmt if mx else base

@@ -11,7 +11,7 @@ import bench
 from mixture_experts_ffn_rmsnorm_amd import inputs as gen
 
 PATHS = {
-    "decode, 2 to 4 rows": ("dec_head", "dec_gateup", "dec_down_reduce"),
+    "decode, 2 to 4 rows": ("dec_head", "dec_gateup", "dec_down", "dec_reduce"),
     "decode, 1 row": ("dec1_router", "dec1_gateup", "dec1_down_reduce"),
     "prefill": ("pre_norm", "pre_router", "pre_sort", "gemm_gateup_swiglu", "gemm_down",
                 "gemm_down_shared_reduce"),
@@ -58,11 +58,12 @@ def test_profiled_kernel_names_map_to_launch_names():
         "k_dec_gateup<4096, 2048, 1>(moe::FwdArgs)": "dec_gateup_mx",
         "k_dec1_gateup<512, 256, 0>(moe::FwdArgs)": "dec1_gateup",
         "k_dec1_gateup<4096, 2048, 2>(moe::FwdArgs)": "dec1_gateup_mx4",
-        "k_dec_down<4096, 2048, 0>(moe::FwdArgs)": "dec_down_reduce",
+        "k_dec_down<4096, 2048, 0>(moe::FwdArgs)": "dec_down",
+        "k_dec_reduce<4096>(moe::FwdArgs)": "dec_reduce",
         "k_dec1_down<512, 256, 0>(moe::FwdArgs)": "dec1_down_reduce",
         "k_dec1_down<4096, 2048, 1>(moe::FwdArgs)": "dec1_down_reduce_mx",
         "k_dec1_down<4096, 2048, 2>(moe::FwdArgs)": "dec1_down_reduce_mx4",
-        "k_dec_down<512, 256, 2>(moe::FwdArgs)": "dec_down_reduce_mx4",
+        "k_dec_down<512, 256, 2>(moe::FwdArgs)": "dec_down_mx4",
         "k_pre_norm<4096>(moe::FwdArgs)": "pre_norm",
         "k_pre_router<4096, 256, 8>(moe::FwdArgs)": "pre_router",
         "k_pre_sort(moe::FwdArgs)": "pre_sort",
