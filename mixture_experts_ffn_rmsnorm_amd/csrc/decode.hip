@@ -151,12 +151,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 // receives each lane's partial sums part[0..nr) of row j (reduce them with
 // wave_sum); it must not store to global memory: loads and stores share one
 // wait counter, and a store among the weight loads makes every later wait
-// drain them all.  nrows is a positive multiple of NBUF.
+// drain them all.
 // With PAIR rows are multiplied two at a time, so each activation value read
 // from LDS serves both (with several activation rows and half-size 8-bit
 // weight rows the LDS reads, not the weight stream, bound the loop
 // otherwise).  actof(j) gives row j's activations (stream_rows: the same for
 // every row); with PAIR rows 2i and 2i + 1 must share them.
+// MAXROWS 0: a rolled loop over groups of NBUF rows, nrows a positive
+// multiple of NBUF.  MAXROWS > 0: nrows is any positive multiple of the
+// pair size up to MAXROWS, each count its own fully unrolled stream.
 template <int LEN, int NBUF, int MX, bool PAIR, int MAXROWS, class RowSrc, class ActOf, class Pre, class Sink>
 __device__ __forceinline__ void stream_rows_by(int nrows, RowSrc rowsrc, ActOf actof, int nr, Pre pre, Sink sink) {
   constexpr bool TAIL = MAXROWS > 0;
@@ -1231,10 +1234,10 @@ __global__ __launch_bounds__(kThreads) void k_dec_reduce(const FwdArgs a) {
 // two rows of every matrix -- the plan's experts in order, then the shared
 // one; the two rows share the activation -- keeping the dot products in
 // LDS.  Thread i < 8 then forms out = sum over u of w_u * down_u, then +
-// shared down: the order of the tile reduce, from the same dot products, so
-// the result is the same bit for bit; the hyper-connection post-mix follows
-// (its state and maps staged with the h vectors).  No block waits for
-// another and nothing goes through the workspace.  At full size: 512
+// shared down -- the order of the reduce launch of two to four rows -- and
+// the hyper-connection post-mix follows (its state and maps staged with
+// the h vectors).  No block waits for another and nothing goes through the
+// workspace.  At full size: 512
 // blocks, two per compute unit, each streaming 8 rows of every matrix.
 template <int H, int I, int MX>
 __global__ __launch_bounds__(kThreads) void k_dec1_down(const FwdArgs a) {
