@@ -11,7 +11,7 @@
 //   k_dec_gateup   the shared expert's down projection (first blocks), then
 //                  routed gate/up + SwiGLU, one (expert, 16 inter rows) tile
 //                  per block
-//   k_dec_down     routed down projections for 32 hidden rows per block
+//   k_dec_down     routed down projections for 16 or 32 hidden rows per block
 //   k_dec_reduce   out = sum of weight * down + shared in a fixed order
 //
 // With one row the launches divide the work differently, and no workgroup
@@ -45,7 +45,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kGuRows = 16;     // inter rows per routed gate/up block (x2 matrices): 4 waves x 4
 constexpr int kShRows = 8;      // inter rows per shared gate/up block: 4 waves x 2
-constexpr int kDnRows = 32;     // hidden rows per down block: 4 waves x 8
+// hidden rows per down block of two to four rows: 4 waves x 4 (bf16,
+// 8-bit), 4 waves x 8 (4-bit, whose rows are a quarter of bf16's).  Four-row
+// down launch, 16 / 32 / 8 rows per block: bf16 60.4 / 62.7 / 63.6 us,
+// 8-bit 40.1 / 41.2 / 43.8 us, 4-bit 31.4 / 30.4 / 36.1 us.
+template <int MX> constexpr int kDnRows = MX == 2 ? 32 : 16;
 // hidden rows per shared-down block of the gate/up launch (4 waves x 4): its
 // H/16 blocks give every compute unit one of them besides its routed blocks
 constexpr int kSdRows = 16;
@@ -1141,12 +1145,12 @@ __global__ __launch_bounds__(kThreads) void k_dec1_gateup(const FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Routed down (2-4 rows).  grid = (H/32, G) with G the most distinct routed
-// experts.  Block (x, u) computes hidden rows x, x + H/32, ... of the plan's
-// u-th expert's down projection for its rows and writes them to d32 (the
-// entries' rows); blocks past the plan's groups return at once.  The
-// weighted reduce is the next launch: a block here ends with its stream,
-// with no wait for its stores and no count.
+// Routed down (2-4 rows).  grid = (H/D, G) with D = kDnRows and G the most
+// distinct routed experts.  Block (x, u) computes hidden rows x, x + H/D,
+// ... of the plan's u-th expert's down projection for its rows and writes
+// them to d32 (the entries' rows); blocks past the plan's groups return at
+// once.  The weighted reduce is the next launch: a block here ends with its
+// stream, with no wait for its stores and no count.
 template <int H, int I, int MX>
 __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   __shared__ float hs[kDecodeMaxRows * I];
@@ -1157,8 +1161,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_down(const FwdArgs a) {
   const float* src[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) src[j] = a.h32 + (int64_t)(g.begin + (j < g.nr ? j : 0)) * I;
-  down_tile<H, I, kDnRows, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down, a.down_q, a.down_s, g.expert, (int64_t)H * I), hs, g.nr,
-                                                     blockIdx.x, H / kDnRows, a.d32, g.begin,
+  down_tile<H, I, kDnRows<MX>, kNbuf<MX>, MX, kPair<MX>>(expert_mat<MX>(a.down, a.down_q, a.down_s, g.expert, (int64_t)H * I), hs,
+                                                         g.nr, blockIdx.x, H / kDnRows<MX>, a.d32, g.begin,
                                                      [&]() { stage_rows<I>(hs, src, g.nr); });  // ends with a barrier
 }
 
@@ -1346,7 +1350,7 @@ hipError_t run_decode_t(const FwdArgs& a, hipStream_t s) {
                dim3(H / kSdRows + gmax * (I / kGuRows)), dim3(kThreads), (size_t)a.R * H * 4, s, &args);
   if (err != hipSuccess) return err;
   err = launch(MX == 2 ? "dec_down_mx4" : MX ? "dec_down_mx" : "dec_down", (const void*)k_dec_down<H, I, MX>,
-               dim3(H / kDnRows, gmax), dim3(kThreads), 0, s, &args);
+               dim3(H / kDnRows<MX>, gmax), dim3(kThreads), 0, s, &args);
   if (err != hipSuccess) return err;
   return launch("dec_reduce", (const void*)k_dec_reduce<H>, dim3(a.R * H / kThreads), dim3(kThreads), 0, s, &args);
 }
