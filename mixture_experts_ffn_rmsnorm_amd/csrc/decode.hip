@@ -1045,8 +1045,8 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
     }
   }
   if (kRouterOnly) return;
-  // count in once the logits are written through (like the down launch's
-  // partials: no cache-wide fence); the last router block routes, reading
+  // count in once the logits are written through (a wait for the block's
+  // own stores, no cache-wide fence); the last router block routes, reading
   // them with write-through loads
   sync_stores();
   __syncthreads();

@@ -39,9 +39,10 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
 }
 
 // Write-through (agent-scope) store / load of one float: data that another
-// workgroup of the same kernel reads after a flag or counter says so.  The
-// writer waits for these stores to complete (sync_stores) before raising
-// the flag; the reader's loads bypass stale cache lines.
+// workgroup reads -- of the same kernel after a flag or counter says so (the
+// writer waits for these stores to complete, sync_stores, before raising
+// it), or of a later launch, on any XCD.  The reader's loads bypass stale
+// cache lines.
 __device__ __forceinline__ void store_wt(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
