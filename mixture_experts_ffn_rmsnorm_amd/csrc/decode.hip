@@ -965,6 +965,9 @@ __device__ __forceinline__ void down_tile(const WMat& wm, const float* hs, int n
 //   Shared gate/up block: RMSNorm into LDS, then 8 inter rows of the shared
 //   expert's SwiGLU output for every row; its streaming covers the router's
 //   latency and the routing.  The first of these blocks publishes xn.
+// kRouterOnly (one row): the router blocks alone, each wave also storing
+// its expert's selection key and sigmoid; without the wrapper every lane
+// dots its own columns in registers and the norm is applied to the sum.
 template <int H, int I, bool kRouterOnly, int MX>
 __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];  // [R][H]
@@ -1005,6 +1008,66 @@ __global__ __launch_bounds__(kThreads) void k_dec_head(const FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
       if (c < NCH - 1 || full) q[c] = load_stream(a.router + (int64_t)e * H + c * 512 + lane * 8);
+  }
+  if constexpr (kRouterOnly) {
+    if (a.hc == 0) {
+      // One row without the wrapper: logit = (sum_j W[e,j] x_j g_j) / rms(x).
+      // Every wave loads the row and the norm weight at its own lanes'
+      // columns (those of its router row), so the dot needs no LDS and no
+      // barrier; the sum of squares comes from the same values.  Block 0's
+      // wave 0 also stores xn = x / rms(x) * g for the later launches.
+      float xv[NCH][8], gv[NCH][8];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int col = c * 512 + lane * 8;
+        if (c < NCH - 1 || full) {
+          const float4 x0 = *(const float4*)(a.x + col), x1 = *(const float4*)(a.x + col + 4);
+          const float4 g0 = *(const float4*)(a.norm_w + col), g1 = *(const float4*)(a.norm_w + col + 4);
+          xv[c][0] = x0.x; xv[c][1] = x0.y; xv[c][2] = x0.z; xv[c][3] = x0.w;
+          xv[c][4] = x1.x; xv[c][5] = x1.y; xv[c][6] = x1.z; xv[c][7] = x1.w;
+          gv[c][0] = g0.x; gv[c][1] = g0.y; gv[c][2] = g0.z; gv[c][3] = g0.w;
+          gv[c][4] = g1.x; gv[c][5] = g1.y; gv[c][6] = g1.z; gv[c][7] = g1.w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xv[c][i] = gv[c][i] = 0.f;
+        }
+      }
+      float ss = 0.f, dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        float f[8];
+        unpack8(e < E && (c < NCH - 1 || full) ? q[c] : make_uint4(0u, 0u, 0u, 0u), f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ss = fmaf(xv[c][i], xv[c][i], ss);
+          dot = fmaf(f[i], xv[c][i] * gv[c][i], dot);
+        }
+      }
+      ss = wave_sum(ss);
+      dot = wave_sum(dot);
+      const float rs = 1.0f / sqrtf(ss / (float)H + a.eps);
+      if (b == 0 && wv == 0) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          if (c < NCH - 1 || full) {
+            float4 o0, o1;
+            o0.x = xv[c][0] * rs * gv[c][0]; o0.y = xv[c][1] * rs * gv[c][1];
+            o0.z = xv[c][2] * rs * gv[c][2]; o0.w = xv[c][3] * rs * gv[c][3];
+            o1.x = xv[c][4] * rs * gv[c][4]; o1.y = xv[c][5] * rs * gv[c][5];
+            o1.z = xv[c][6] * rs * gv[c][6]; o1.w = xv[c][7] * rs * gv[c][7];
+            *(float4*)(a.xn32 + c * 512 + lane * 8) = o0;
+            *(float4*)(a.xn32 + c * 512 + lane * 8 + 4) = o1;
+          }
+        }
+      }
+      if (e < E && lane == 0) {
+        const float v = dot * rs;
+        a.logits[e] = v;
+        sy->route_sig[e] = sigmoid_f64(v);
+        sy->route_key[e] = a.layer_kind == MOE_LAYER_HASH ? 0ull : ordered_key(score_key(v, bias_e));
+      }
+      return;
+    }
   }
   norm_rows_to_lds<H, kRouterOnly ? 1 : kDecodeMaxRows>(a, b == 0, xs);
   if (kRouterOnly && b == 0)  // the later launches stage the normalised row from xn
